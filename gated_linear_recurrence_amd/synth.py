@@ -1,0 +1,153 @@
+"""Seeded synthetic inputs shaped like RecurrentGemma's recurrent block.
+
+This module only draws random numbers; it holds none of the method's
+arithmetic.  The oracle tests, the GPU parity tests and the benchmark all take
+their inputs from here, so both sides of a comparison read the same bits.
+
+Storage form: fp32 tensors are ``float32`` arrays; bf16 tensors are ``uint16``
+arrays of raw bf16 bits, rounded from fp32 draws with round-to-nearest-even.
+Lambda and h0 are always ``float32``.
+
+Streams: every tensor has its own ``numpy.random.Generator(PCG64(...))``
+seeded by ``SeedSequence([seed, tensor_id, ...])``.  Activations (x, y) are
+drawn in blocks of 1024 tokens per sequence, each block from its own stream,
+so a time prefix of one sequence can be regenerated without the rest.
+
+The widths follow the RecurrentGemma pages (2B: width 2560 for both branches,
+conv kernel 4); the 9B width (4096, 16 heads of 256), the gate block sizes and
+the value distributions are those of the five workloads below.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+F32 = "f32"
+BF16 = "bf16"
+ACT_BLOCK = 1024  # tokens per activation stream block
+
+# tensor ids for SeedSequence (fixed order: Lambda, W_a, W_x, b_a, b_x, conv_w, conv_b, h0, x, y)
+_TID = {"lambda": 0, "wa": 1, "wx": 2, "ba": 3, "bx": 4, "conv_w": 5, "conv_b": 6, "h0": 7,
+        "x": 8, "y": 9}
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int            # sequences (decode: concurrent sequences N)
+    T: int            # tokens per sequence (decode: number of single-token steps)
+    D: int            # channels (RNN width)
+    H: int            # gate heads; block size bs = D // H
+    dtype: str        # storage type of activations and weights
+    sig_lo: float     # sigmoid(Lambda) ~ U[sig_lo, sig_hi]
+    sig_hi: float
+    h0_std: float     # 0 -> h0 = 0
+    seed: int
+    decode: bool = False
+
+    @property
+    def bs(self) -> int:
+        return self.D // self.H
+
+    @property
+    def w_std(self) -> float:
+        return 1.0 / math.sqrt(self.bs)
+
+
+WORKLOADS = {
+    w.name: w for w in [
+        Workload("tiny-fp32-B1-T256-D256-H2", 1, 256, 256, 2, F32, 0.9, 0.999, 0.0, 1000),
+        Workload("2b-prefill-B1-T2048-D2560-H10", 1, 2048, 2560, 10, BF16, 0.9, 0.999, 0.0, 1001),
+        Workload("2b-batched-B8-T8192-D2560-H10", 8, 8192, 2560, 10, BF16, 0.9, 0.999, 0.1, 1002),
+        Workload("2b-decode-N256-S1024-D2560-H10", 256, 1024, 2560, 10, BF16, 0.9, 0.999, 0.0, 1003,
+                 decode=True),
+        Workload("9b-long-B2-T65536-D4096-H16", 2, 65536, 4096, 16, BF16, 0.99, 0.9999, 0.0, 1004),
+    ]
+}
+TINY, PREFILL_2B, BATCHED_2B, DECODE_2B, LONG_9B = list(WORKLOADS)
+
+
+def round_bf16(a: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bits, round to nearest even (inputs are finite draws)."""
+    a = np.ascontiguousarray(a, np.float32)
+    bits = a.view(np.uint32).astype(np.uint64)
+    bits = (bits + 0x7FFF + ((bits >> 16) & 1)) >> 16
+    return bits.astype(np.uint16)
+
+
+def to_storage(a: np.ndarray, dtype: str) -> np.ndarray:
+    a = np.asarray(a, np.float32)
+    return round_bf16(a) if dtype == BF16 else np.ascontiguousarray(a)
+
+
+def _rng(*key) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(list(key))))
+
+
+def make_params(w: Workload, biases: bool = False, seed: int | None = None) -> dict:
+    """Parameters in storage form.
+
+    Lambda: s ~ U[sig_lo, sig_hi], Lambda = log(s / (1 - s)), so sigmoid(Lambda) = s.
+    W_a, W_x [H, bs, bs] ~ N(0, std 1/sqrt(bs)); conv_w [D, 4] ~ N(0, std 0.5).
+    biases=False: b_a = b_x = conv_b = 0 (the measured workloads);
+    biases=True:  b_a, b_x, conv_b ~ N(0, std 0.5) (extra parity coverage).
+    """
+    s0 = w.seed if seed is None else seed
+    D, H, bs = w.D, w.H, w.bs
+    s = _rng(s0, _TID["lambda"]).uniform(w.sig_lo, w.sig_hi, D)
+    lam = np.log(s / (1.0 - s)).astype(np.float32)
+    wa = _rng(s0, _TID["wa"]).standard_normal((H, bs, bs), dtype=np.float32) * np.float32(w.w_std)
+    wx = _rng(s0, _TID["wx"]).standard_normal((H, bs, bs), dtype=np.float32) * np.float32(w.w_std)
+    if biases:
+        ba = _rng(s0, _TID["ba"]).standard_normal(D, dtype=np.float32) * np.float32(0.5)
+        bx = _rng(s0, _TID["bx"]).standard_normal(D, dtype=np.float32) * np.float32(0.5)
+        cb = _rng(s0, _TID["conv_b"]).standard_normal(D, dtype=np.float32) * np.float32(0.5)
+    else:
+        ba = np.zeros(D, np.float32)
+        bx = np.zeros(D, np.float32)
+        cb = np.zeros(D, np.float32)
+    cw = _rng(s0, _TID["conv_w"]).standard_normal((D, 4), dtype=np.float32) * np.float32(0.5)
+    st = lambda a: to_storage(a, w.dtype)
+    return {"conv_w": st(cw), "conv_b": st(cb), "wa": st(wa), "ba": st(ba), "wx": st(wx),
+            "bx": st(bx), "lambda": lam}
+
+
+def make_h0(w: Workload, B: int | None = None, seed: int | None = None) -> np.ndarray | None:
+    """h0 [B, D] fp32 ~ N(0, h0_std), or None when the workload starts from zero."""
+    if w.h0_std == 0.0:
+        return None
+    s0 = w.seed if seed is None else seed
+    B = w.B if B is None else B
+    return _rng(s0, _TID["h0"]).standard_normal((B, w.D), dtype=np.float32) * np.float32(w.h0_std)
+
+
+def make_conv0(w: Workload, B: int, seed: int | None = None) -> np.ndarray:
+    """A random conv state [B, 3, D] ~ N(0, 1) in storage form (edge-case coverage only)."""
+    s0 = w.seed if seed is None else seed
+    return to_storage(_rng(s0, _TID["conv_b"], 77).standard_normal((B, 3, w.D), dtype=np.float32),
+                      w.dtype)
+
+
+def make_act(w: Workload, which: str, B: int | None = None, T: int | None = None,
+             seed: int | None = None) -> np.ndarray:
+    """x or y [B, T, D] ~ N(0, 1) in storage form; blocks of 1024 tokens per stream."""
+    assert which in ("x", "y")
+    s0 = w.seed if seed is None else seed
+    B = w.B if B is None else B
+    T = w.T if T is None else T
+    st_dtype = np.uint16 if w.dtype == BF16 else np.float32
+    out = np.empty((B, T, w.D), st_dtype)
+    for b in range(B):
+        for blk in range((T + ACT_BLOCK - 1) // ACT_BLOCK):
+            t0 = blk * ACT_BLOCK
+            n = min(ACT_BLOCK, T - t0)
+            a = _rng(s0, _TID[which], b, blk).standard_normal((ACT_BLOCK, w.D), dtype=np.float32)
+            out[b, t0:t0 + n] = to_storage(a[:n], w.dtype)
+    return out
+
+
+def small(w: Workload, B: int | None = None, T: int | None = None) -> Workload:
+    """The same distributions with other sizes (test cases)."""
+    return dataclasses.replace(w, B=w.B if B is None else B, T=w.T if T is None else T)

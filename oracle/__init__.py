@@ -1,0 +1,251 @@
+"""fp64 CPU oracle for the RG-LRU recurrent-block path -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The HIP library never calls it, and it
+shares no code with the HIP library: the arithmetic lives in
+``rglru_oracle.c`` (plain C, fp64, sequential per (sequence, head) unit);
+this module only compiles that file with gcc and marshals numpy arrays.
+
+Storage conventions (the same as the library's inputs):
+  * fp32 tensors are ``numpy.float32`` arrays;
+  * bf16 tensors are ``numpy.uint16`` arrays holding the raw bf16 bits;
+  * Lambda and h0 are always ``numpy.float32``.
+Outputs are ``numpy.float64``.
+
+What each function follows is stated in the C file's header; every function
+is pinned in ``tests/test_oracle_pins.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "rglru_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+F32 = 0
+BF16 = 1
+
+
+def build(src: str = _SRC, out: str = _LIB) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP).  Returns the library path."""
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", "-D_DEFAULT_SOURCE",
+           src, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def _needs_build() -> bool:
+    if not os.path.exists(_LIB):
+        return True
+    return os.path.getmtime(_LIB) < os.path.getmtime(_SRC)
+
+
+def load(path: str | None = None):
+    """Load (building first if needed) and return the ctypes library."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    with _lock:
+        if _lib is None:
+            if _needs_build():
+                build()
+            _lib = _bind(ctypes.CDLL(_LIB))
+    return _lib
+
+
+def _bind(lib):
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    lib.oracle_prefill_unit.argtypes = [I, I, I, I, I, I, I] + [P] * 14
+    lib.oracle_prefill_unit.restype = I
+    lib.oracle_prefill.argtypes = [I, I, I, I, I] + [P] * 14 + [I]
+    lib.oracle_prefill.restype = I
+    lib.oracle_decode_step.argtypes = [I, I, I, I] + [P] * 12
+    lib.oracle_decode_step.restype = I
+    lib.oracle_conv1d_state_update.argtypes = [I, I, I, I] + [P] * 5
+    lib.oracle_conv1d_state_update.restype = I
+    lib.oracle_gate_preacts.argtypes = [I, I, I, I] + [P] * 7
+    lib.oracle_gate_preacts.restype = I
+    lib.oracle_gelu_tanh.argtypes = [ctypes.c_double]
+    lib.oracle_gelu_tanh.restype = ctypes.c_double
+    lib.oracle_rglru_step.argtypes = [ctypes.c_double] * 5
+    lib.oracle_rglru_step.restype = ctypes.c_double
+    lib.oracle_max_threads.argtypes = []
+    lib.oracle_max_threads.restype = I
+    return lib
+
+
+def _dtype_code(arr: np.ndarray) -> int:
+    if arr.dtype == np.float32:
+        return F32
+    if arr.dtype == np.uint16:
+        return BF16
+    raise TypeError("storage arrays must be float32 or uint16 (bf16 bits), got %s" % arr.dtype)
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype=None):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if dtype is not None and a.dtype != dtype:
+        raise TypeError("expected %s, got %s" % (dtype, a.dtype))
+    return a
+
+
+class Params:
+    """The block's parameters in storage form (see module docstring)."""
+
+    def __init__(self, conv_w, conv_b, wa, ba, wx, bx, lam, n_heads):
+        self.conv_w = _c(conv_w)
+        self.dtype = _dtype_code(self.conv_w)
+        sd = self.conv_w.dtype
+        self.conv_b = _c(conv_b, sd)
+        self.wa = _c(wa, sd)
+        self.ba = _c(ba, sd)
+        self.wx = _c(wx, sd)
+        self.bx = _c(bx, sd)
+        self.lam = _c(lam, np.float32)
+        self.H = int(n_heads)
+        self.D = int(self.lam.shape[0])
+
+    def args(self):
+        return [_ptr(self.conv_w), _ptr(self.conv_b), _ptr(self.wa), _ptr(self.ba),
+                _ptr(self.wx), _ptr(self.bx), _ptr(self.lam)]
+
+
+def _check(st, what):
+    if st != 0:
+        raise ValueError("%s: oracle status %d" % (what, st))
+
+
+def prefill(p: Params, x, y, h0=None, conv0=None, nthreads: int = 0, lib=None):
+    """Full prefill.  x, y [B, T, D].  Returns (out [B,T,D], h_last [B,D], conv_last [B,3,D])."""
+    lib = lib or load()
+    x = _c(x, p.conv_w.dtype)
+    y = _c(y, p.conv_w.dtype)
+    B, T, D = x.shape
+    h0 = _c(h0, np.float32)
+    conv0 = _c(conv0, p.conv_w.dtype)
+    out = np.empty((B, T, D), np.float64)
+    h_last = np.empty((B, D), np.float64)
+    conv_last = np.empty((B, 3, D), np.float64)
+    cw, cb, wa, ba, wx, bx, lam = p.args()
+    st = lib.oracle_prefill(p.dtype, B, T, D, p.H, _ptr(x), _ptr(y), cw, cb, wa, ba, wx, bx, lam,
+                            _ptr(h0), _ptr(conv0), _ptr(out), _ptr(h_last), _ptr(conv_last),
+                            int(nthreads))
+    _check(st, "oracle_prefill")
+    return out, h_last, conv_last
+
+
+def prefill_unit(p: Params, x, y, b: int, hd: int, t_use: int, h0=None, conv0=None, lib=None):
+    """One (b, head) unit over the first t_use tokens.
+
+    Returns (out [t_use, bs], h_end [bs], conv_end [3, bs]) for channels
+    hd*bs .. hd*bs+bs-1.
+    """
+    lib = lib or load()
+    x = _c(x, p.conv_w.dtype)
+    y = _c(y, p.conv_w.dtype)
+    B, T, D = x.shape
+    bs = D // p.H
+    out = np.empty((t_use, bs), np.float64)
+    h_end = np.empty((bs,), np.float64)
+    conv_end = np.empty((3, bs), np.float64)
+    h0 = _c(h0, np.float32)
+    conv0 = _c(conv0, p.conv_w.dtype)
+    cw, cb, wa, ba, wx, bx, lam = p.args()
+    st = lib.oracle_prefill_unit(p.dtype, T, D, p.H, int(b), int(hd), int(t_use), _ptr(x),
+                                 _ptr(y), cw, cb, wa, ba, wx, bx, lam, _ptr(h0), _ptr(conv0),
+                                 _ptr(out), _ptr(h_end), _ptr(conv_end))
+    _check(st, "oracle_prefill_unit")
+    return out, h_end, conv_end
+
+
+def decode_step(p: Params, x_t, y_t, h, win, lib=None):
+    """One decode step.  x_t, y_t [N, D] (storage); h [N, D] and win [N, 3, D] fp64, updated in place.
+
+    Returns out_t [N, D] (fp64)."""
+    lib = lib or load()
+    x_t = _c(x_t, p.conv_w.dtype)
+    y_t = _c(y_t, p.conv_w.dtype)
+    N, D = x_t.shape
+    assert h.dtype == np.float64 and h.flags.c_contiguous and h.shape == (N, D)
+    assert win.dtype == np.float64 and win.flags.c_contiguous and win.shape == (N, 3, D)
+    out = np.empty((N, D), np.float64)
+    cw, cb, wa, ba, wx, bx, lam = p.args()
+    st = lib.oracle_decode_step(p.dtype, N, D, p.H, _ptr(x_t), _ptr(y_t), cw, cb, wa, ba, wx, bx,
+                                lam, _ptr(h), _ptr(win), _ptr(out))
+    _check(st, "oracle_decode_step")
+    return out
+
+
+def conv1d_state_update(conv_w, conv_b, x_new, win, want_out=True, lib=None):
+    """x_new [N, T_new, D] (storage); win [N, 3, D] fp64 updated in place.
+
+    Returns conv_out [N, T_new, D] fp64 (or None)."""
+    lib = lib or load()
+    conv_w = _c(conv_w)
+    dt = _dtype_code(conv_w)
+    x_new = _c(x_new, conv_w.dtype)
+    conv_b = _c(conv_b, conv_w.dtype)
+    N, T_new, D = x_new.shape
+    assert win.dtype == np.float64 and win.flags.c_contiguous and win.shape == (N, 3, D)
+    out = np.empty((N, T_new, D), np.float64) if want_out else None
+    st = lib.oracle_conv1d_state_update(dt, N, T_new, D, _ptr(x_new), _ptr(conv_w), _ptr(conv_b),
+                                        _ptr(win), _ptr(out))
+    _check(st, "oracle_conv1d_state_update")
+    return out
+
+
+def gate_preacts(wa, ba, wx, bx, u, n_heads: int, lib=None):
+    """Gate pre-activations.  u [n, D] fp64 -> (ra, ri) [n, D] fp64."""
+    lib = lib or load()
+    wa = _c(wa)
+    dt = _dtype_code(wa)
+    wx = _c(wx, wa.dtype)
+    ba = _c(ba, wa.dtype)
+    bx = _c(bx, wa.dtype)
+    u = _c(u, np.float64)
+    n, D = u.shape
+    ra = np.empty((n, D), np.float64)
+    ri = np.empty((n, D), np.float64)
+    st = lib.oracle_gate_preacts(dt, n, D, int(n_heads), _ptr(u), _ptr(wa), _ptr(ba), _ptr(wx),
+                                 _ptr(bx), _ptr(ra), _ptr(ri))
+    _check(st, "oracle_gate_preacts")
+    return ra, ri
+
+
+def gelu_tanh(yv: float, lib=None) -> float:
+    lib = lib or load()
+    return lib.oracle_gelu_tanh(float(yv))
+
+
+def rglru_step(lam: float, ra: float, ri: float, u: float, h_prev: float, lib=None) -> float:
+    lib = lib or load()
+    return lib.oracle_rglru_step(float(lam), float(ra), float(ri), float(u), float(h_prev))
+
+
+def max_threads(lib=None) -> int:
+    lib = lib or load()
+    return lib.oracle_max_threads()
+
+
+def widen_bf16(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bits to float32 (the oracle's own converter, in numpy)."""
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)

@@ -1,0 +1,347 @@
+/*
+ * rglru_oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, sequential fp64 reference for the recurrent-block
+ * temporal-mixing path of RecurrentGemma.  Only the tests, the smoke check
+ * and the CPU-baseline leg of the benchmark load this file.  It shares no
+ * code, header, table or constant with the HIP library.
+ *
+ * What it computes, per sequence b and head hd (heads are independent):
+ *
+ *   The pages ("Gemma 詳解：RecurrentGemma 架構", section
+ *   "含遞迴區塊的殘差區塊", and the module printout on that page) fix the
+ *   dataflow: two width-2560 branches; on one, a depthwise Conv1d with
+ *   kernel 4 (padding 3, groups = width, with bias) followed by the
+ *   RG-LRU; on the other, GELU with the tanh approximation
+ *   (PytorchGELUTanh); the two branches are multiplied elementwise.
+ *   The library's inputs are the two branch projections' outputs
+ *   x = linear_x(.) and y = linear_y(.).
+ *
+ *   The pages name the RG-LRU (section "模型寬度與 RNN 寬度": it keeps a
+ *   fixed-size state of RNN width) but print none of its arithmetic.  The
+ *   recurrence below is the RG-LRU of the Griffin paper (arXiv 2402.19427,
+ *   linked from the article "RecurrentGemma vs 传统LLM..."), restated:
+ *     r_t = sigmoid(W_a u_t + b_a), i_t = sigmoid(W_x u_t + b_x)
+ *     a_t = sigmoid(Lambda) ** (8 r_t)
+ *     h_t = a_t h_{t-1} + sqrt(1 - a_t^2) (i_t u_t)
+ *   with block-diagonal W_a, W_x (one bs x bs block per head).
+ *
+ * Readings where the pages are silent (each one is listed in the design doc):
+ *   - the gates read the RG-LRU input u_t (the conv output);
+ *   - the conv is causal: the first T of the T+3 padded outputs are kept,
+ *     tap j multiplies x_{t-3+j}, and the carried conv state holds the
+ *     last three conv inputs, oldest first (zeros when absent);
+ *   - gate block h is stored like a Linear weight, [out j][in k]:
+ *       pre[h*bs + j] = b[h*bs + j] + sum_k W[h][j][k] * u[h*bs + k];
+ *   - out_t = h_t * gelu_tanh(y_t); no resets; h0 = 0 when absent.
+ *
+ * Everything is evaluated literally in double precision.  Inputs stored as
+ * bf16 are widened exactly by placing the 16 bits in the top half of a
+ * float; fp32 inputs are widened exactly.
+ *
+ * Parity pins (tests/test_oracle_pins.py): every function here is pinned
+ * by closed forms, library routines or brute force; see that file.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_F32 0
+#define ORACLE_BF16 1
+
+/* Exact widening of one stored element to double. */
+static double widen(const void *base, size_t idx, int dtype) {
+    if (dtype == ORACLE_F32) return (double)((const float *)base)[idx];
+    uint32_t bits = (uint32_t)((const uint16_t *)base)[idx] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+static double sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
+
+/* GELU, tanh form (Hendrycks & Gimpel 2016): 0.5 y (1 + tanh(sqrt(2/pi) (y + 0.044715 y^3))). */
+double oracle_gelu_tanh(double y) {
+    const double k = sqrt(2.0 / 3.14159265358979323846);
+    return 0.5 * y * (1.0 + tanh(k * (y + 0.044715 * y * y * y)));
+}
+
+/* Parameters of one recurrent block (all pointers are host memory). */
+typedef struct {
+    int dtype;        /* storage type of x, y, conv state and all weights but Lambda */
+    int D, H, bs;     /* channels, gate heads, block size D/H */
+    const void *conv_w;   /* [D][4] */
+    const void *conv_b;   /* [D] or NULL */
+    const void *wa, *ba;  /* [H][bs][bs] ([out][in]), [D] or NULL */
+    const void *wx, *bx;
+    const float *lambda;  /* [D] */
+} prm_t;
+
+/* Causal depthwise conv, one channel, one step.  win[0..2] hold the three
+ * previous inputs, oldest first; tap j multiplies x_{t-3+j}. */
+static double conv_step(const prm_t *p, int c, double win[3], double xt) {
+    double acc = p->conv_b ? widen(p->conv_b, (size_t)c, p->dtype) : 0.0;
+    acc += widen(p->conv_w, (size_t)c * 4 + 0, p->dtype) * win[0];
+    acc += widen(p->conv_w, (size_t)c * 4 + 1, p->dtype) * win[1];
+    acc += widen(p->conv_w, (size_t)c * 4 + 2, p->dtype) * win[2];
+    acc += widen(p->conv_w, (size_t)c * 4 + 3, p->dtype) * xt;
+    win[0] = win[1];
+    win[1] = win[2];
+    win[2] = xt;
+    return acc;
+}
+
+/* Gate pre-activations of head hd for one token: u_head[bs] -> ra[bs], ri[bs]. */
+static void gate_preacts(const prm_t *p, int hd, const double *u_head, double *ra, double *ri) {
+    const int bs = p->bs;
+    for (int j = 0; j < bs; ++j) {
+        const size_t ch = (size_t)hd * bs + j;
+        double sa = p->ba ? widen(p->ba, ch, p->dtype) : 0.0;
+        double sx = p->bx ? widen(p->bx, ch, p->dtype) : 0.0;
+        for (int k = 0; k < bs; ++k) {
+            const size_t widx = ((size_t)hd * bs + j) * bs + k;
+            sa += widen(p->wa, widx, p->dtype) * u_head[k];
+            sx += widen(p->wx, widx, p->dtype) * u_head[k];
+        }
+        ra[j] = sa;
+        ri[j] = sx;
+    }
+}
+
+/* One RG-LRU step for one channel: returns the new state. */
+static double rglru_step(double lambda, double ra, double ri, double u, double h_prev) {
+    const double r = sigmoid(ra);
+    const double i = sigmoid(ri);
+    const double a = pow(sigmoid(lambda), 8.0 * r);
+    const double m = sqrt(1.0 - a * a);
+    return a * h_prev + m * (i * u);
+}
+
+/*
+ * The core loop: one (sequence, head) unit over n_tok tokens.
+ *   x_row(t), y_row(t): element c of token t is x[xoff + t*xstride + c].
+ *   h[bs], win[3][bs]: state in/out (fp64).
+ *   out[t*bs + c] receives h_t * gelu(y_t) for channel hd*bs + c.
+ */
+static void run_unit(const prm_t *p, int hd, int n_tok,
+                     const void *x, size_t xoff, size_t xstride,
+                     const void *y, size_t yoff, size_t ystride,
+                     double *h, double *win, double *out) {
+    const int bs = p->bs;
+    double *u = (double *)malloc(sizeof(double) * 3 * (size_t)bs);
+    double *ra = u + bs, *ri = u + 2 * bs;
+    for (int t = 0; t < n_tok; ++t) {
+        for (int c = 0; c < bs; ++c) {
+            const int ch = hd * bs + c;
+            double w3[3] = {win[0 * bs + c], win[1 * bs + c], win[2 * bs + c]};
+            const double xt = widen(x, xoff + (size_t)t * xstride + ch, p->dtype);
+            u[c] = conv_step(p, ch, w3, xt);
+            win[0 * bs + c] = w3[0];
+            win[1 * bs + c] = w3[1];
+            win[2 * bs + c] = w3[2];
+        }
+        gate_preacts(p, hd, u, ra, ri);
+        for (int c = 0; c < bs; ++c) {
+            const int ch = hd * bs + c;
+            h[c] = rglru_step((double)p->lambda[ch], ra[c], ri[c], u[c], h[c]);
+            const double yt = widen(y, yoff + (size_t)t * ystride + ch, p->dtype);
+            out[(size_t)t * bs + c] = h[c] * oracle_gelu_tanh(yt);
+        }
+    }
+    free(u);
+}
+
+static int make_prm(prm_t *p, int dtype, int D, int H, const void *conv_w, const void *conv_b,
+                    const void *wa, const void *ba, const void *wx, const void *bx,
+                    const float *lambda) {
+    if (D <= 0 || H <= 0 || D % H != 0) return 2;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return 3;
+    if (!conv_w || !wa || !wx || !lambda) return 1;
+    p->dtype = dtype;
+    p->D = D;
+    p->H = H;
+    p->bs = D / H;
+    p->conv_w = conv_w;
+    p->conv_b = conv_b;
+    p->wa = wa;
+    p->ba = ba;
+    p->wx = wx;
+    p->bx = bx;
+    p->lambda = lambda;
+    return 0;
+}
+
+/* Initial state of unit (b, hd): h from h0 (fp32) or zero, window from conv0 or zero. */
+static void init_state(const prm_t *p, int b, int hd, const float *h0, const void *conv0,
+                       double *h, double *win) {
+    const int bs = p->bs, D = p->D;
+    for (int c = 0; c < bs; ++c) {
+        const size_t ch = (size_t)hd * bs + c;
+        h[c] = h0 ? (double)h0[(size_t)b * D + ch] : 0.0;
+        for (int j = 0; j < 3; ++j)
+            win[j * bs + c] = conv0 ? widen(conv0, ((size_t)b * 3 + j) * D + ch, p->dtype) : 0.0;
+    }
+}
+
+/*
+ * Prefill of one (b, hd) unit over the first T_use tokens of x, y [B][T][D].
+ * out_unit [T_use][bs]; h_end [bs]; conv_end [3][bs] (state after T_use tokens).
+ */
+int oracle_prefill_unit(int dtype, int T, int D, int H, int b, int hd, int T_use,
+                        const void *x, const void *y, const void *conv_w, const void *conv_b,
+                        const void *wa, const void *ba, const void *wx, const void *bx,
+                        const float *lambda, const float *h0, const void *conv0,
+                        double *out_unit, double *h_end, double *conv_end) {
+    prm_t p;
+    int st = make_prm(&p, dtype, D, H, conv_w, conv_b, wa, ba, wx, bx, lambda);
+    if (st) return st;
+    if (T < 0 || T_use < 0 || T_use > T || hd < 0 || hd >= H || b < 0) return 2;
+    init_state(&p, b, hd, h0, conv0, h_end, conv_end);
+    run_unit(&p, hd, T_use, x, (size_t)b * T * D, (size_t)D, y, (size_t)b * T * D, (size_t)D,
+             h_end, conv_end, out_unit);
+    return 0;
+}
+
+/*
+ * Full prefill: x, y [B][T][D]; out [B][T][D], h_last [B][D], conv_last [B][3][D]
+ * (all outputs fp64).  Units (b, hd) run in parallel over nthreads threads.
+ */
+int oracle_prefill(int dtype, int B, int T, int D, int H, const void *x, const void *y,
+                   const void *conv_w, const void *conv_b, const void *wa, const void *ba,
+                   const void *wx, const void *bx, const float *lambda, const float *h0,
+                   const void *conv0, double *out, double *h_last, double *conv_last,
+                   int nthreads) {
+    prm_t p;
+    int st = make_prm(&p, dtype, D, H, conv_w, conv_b, wa, ba, wx, bx, lambda);
+    if (st) return st;
+    if (B < 1 || T < 0) return 2;
+    const int bs = p.bs;
+    const int n_units = B * H;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+    for (int unit = 0; unit < n_units; ++unit) {
+        const int b = unit / H, hd = unit % H;
+        double *h = (double *)malloc(sizeof(double) * 4 * (size_t)bs);
+        double *win = h + bs;
+        double *o = (double *)malloc(sizeof(double) * ((size_t)T * bs + 1));
+        init_state(&p, b, hd, h0, conv0, h, win);
+        run_unit(&p, hd, T, x, (size_t)b * T * D, (size_t)D, y, (size_t)b * T * D, (size_t)D, h,
+                 win, o);
+        for (int t = 0; t < T; ++t)
+            for (int c = 0; c < bs; ++c)
+                out[((size_t)b * T + t) * D + (size_t)hd * bs + c] = o[(size_t)t * bs + c];
+        for (int c = 0; c < bs; ++c) {
+            h_last[(size_t)b * D + (size_t)hd * bs + c] = h[c];
+            for (int j = 0; j < 3; ++j)
+                conv_last[((size_t)b * 3 + j) * D + (size_t)hd * bs + c] = win[j * bs + c];
+        }
+        free(o);
+        free(h);
+    }
+    return 0;
+}
+
+/*
+ * One decode step for N sequences: x_t, y_t [N][D] (storage dtype);
+ * h [N][D] and win [N][3][D] are fp64 state, updated in place; out_t [N][D].
+ * The body is the prefill loop with one token.
+ */
+int oracle_decode_step(int dtype, int N, int D, int H, const void *x_t, const void *y_t,
+                       const void *conv_w, const void *conv_b, const void *wa, const void *ba,
+                       const void *wx, const void *bx, const float *lambda, double *h,
+                       double *win, double *out_t) {
+    prm_t p;
+    int st = make_prm(&p, dtype, D, H, conv_w, conv_b, wa, ba, wx, bx, lambda);
+    if (st) return st;
+    if (N < 1) return 2;
+    const int bs = p.bs;
+    double *hu = (double *)malloc(sizeof(double) * 5 * (size_t)bs);
+    double *wu = hu + bs, *ou = hu + 4 * bs;
+    for (int n = 0; n < N; ++n) {
+        for (int hd = 0; hd < H; ++hd) {
+            for (int c = 0; c < bs; ++c) {
+                const size_t ch = (size_t)hd * bs + c;
+                hu[c] = h[(size_t)n * D + ch];
+                for (int j = 0; j < 3; ++j) wu[j * bs + c] = win[((size_t)n * 3 + j) * D + ch];
+            }
+            run_unit(&p, hd, 1, x_t, (size_t)n * D, 0, y_t, (size_t)n * D, 0, hu, wu, ou);
+            for (int c = 0; c < bs; ++c) {
+                const size_t ch = (size_t)hd * bs + c;
+                h[(size_t)n * D + ch] = hu[c];
+                for (int j = 0; j < 3; ++j) win[((size_t)n * 3 + j) * D + ch] = wu[j * bs + c];
+                out_t[(size_t)n * D + ch] = ou[c];
+            }
+        }
+    }
+    free(hu);
+    return 0;
+}
+
+/*
+ * Conv-state update: x_new [N][T_new][D] (storage dtype); win [N][3][D] fp64
+ * state updated in place to the last three inputs; conv_out [N][T_new][D]
+ * (fp64) receives the conv outputs (may be NULL).
+ */
+int oracle_conv1d_state_update(int dtype, int N, int T_new, int D, const void *x_new,
+                               const void *conv_w, const void *conv_b, double *win,
+                               double *conv_out) {
+    prm_t p;
+    memset(&p, 0, sizeof p);
+    if (N < 1 || T_new < 0 || D < 1) return 2;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return 3;
+    if (!conv_w || !x_new || !win) return 1;
+    p.dtype = dtype;
+    p.D = D;
+    p.conv_w = conv_w;
+    p.conv_b = conv_b;
+    for (int n = 0; n < N; ++n) {
+        for (int c = 0; c < D; ++c) {
+            double w3[3];
+            for (int j = 0; j < 3; ++j) w3[j] = win[((size_t)n * 3 + j) * D + c];
+            for (int t = 0; t < T_new; ++t) {
+                const double xt = widen(x_new, ((size_t)n * T_new + t) * D + c, dtype);
+                const double u = conv_step(&p, c, w3, xt);
+                if (conv_out) conv_out[((size_t)n * T_new + t) * D + c] = u;
+            }
+            for (int j = 0; j < 3; ++j) win[((size_t)n * 3 + j) * D + c] = w3[j];
+        }
+    }
+    return 0;
+}
+
+/* Gate pre-activations for n_tok tokens: u [n_tok][D] (fp64) -> ra, ri [n_tok][D]. */
+int oracle_gate_preacts(int dtype, int n_tok, int D, int H, const double *u, const void *wa,
+                        const void *ba, const void *wx, const void *bx, double *ra, double *ri) {
+    prm_t p;
+    static const float dummy_lambda = 0.0f;
+    static const float dummy_w = 0.0f;
+    int st = make_prm(&p, dtype, D, H, &dummy_w, NULL, wa, ba, wx, bx, &dummy_lambda);
+    if (st) return st;
+    for (int t = 0; t < n_tok; ++t)
+        for (int hd = 0; hd < H; ++hd)
+            gate_preacts(&p, hd, u + (size_t)t * D + (size_t)hd * p.bs,
+                         ra + (size_t)t * D + (size_t)hd * p.bs,
+                         ri + (size_t)t * D + (size_t)hd * p.bs);
+    return 0;
+}
+
+/* One RG-LRU step on plain doubles (exposed so the pins can probe it directly). */
+double oracle_rglru_step(double lambda, double ra, double ri, double u, double h_prev) {
+    return rglru_step(lambda, ra, ri, u, h_prev);
+}
+
+/* Number of OpenMP threads a parallel region would use (1 without OpenMP). */
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
