@@ -1,0 +1,208 @@
+#!/usr/bin/env python3
+"""Benchmark of the RG-LRU recurrent-block path on one MI355X.
+
+A step is one rglru_prefill call over the 2B-shaped batched workload (B=8, T=8192, D=2560,
+10 gate heads of 256, bf16 storage, fp32 state): conv, gates, scan, GELU merge and all
+stores, inputs resident in HBM.  Prints one JSON line.  Besides the headline prefill figure
+the line carries the dominant kernel's roofline, the oracle's CPU throughput on a bounded
+sample, the 2B single-sequence prefill and the decode step time (256 sequences, D=2560).
+
+  python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-extras]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from gated_linear_recurrence_amd import synth  # noqa: E402
+
+METRIC = "RG-LRU prefill tokens·channels/s + decode step µs; % of MI355X HBM peak"
+HBM_PEAK_GBS = 8000.0
+
+
+def algorithmic_bytes(w: synth.Workload, B: int, T: int, state: bool = True) -> int:
+    """Minimum HBM bytes of one prefill: x, y read and out written once, weights, state."""
+    e = 2 if w.dtype == synth.BF16 else 4
+    D, Hh, bs = w.D, w.H, w.bs
+    act = 3 * B * T * D * e
+    weights = 2 * Hh * bs * bs * e + D * 4 * e + D * 4  # gate blocks, conv taps, Lambda
+    st = (B * D * 4 * (2 if w.h0_std else 1) + B * 3 * D * e) if state else 0
+    return act + weights + st
+
+
+def decode_bytes(w: synth.Workload, N: int) -> int:
+    """HBM bytes of one decode step in the ABI's layout: x_t, y_t, out_t, h (r+w),
+    conv window (r+w), gate blocks, conv taps, Lambda."""
+    e = 2 if w.dtype == synth.BF16 else 4
+    D = w.D
+    return 3 * N * D * e + 2 * N * D * 4 + 2 * N * 3 * D * e + 2 * w.H * w.bs * w.bs * e + \
+        D * 4 * e + D * 4
+
+
+def _to_dev(a, torch):
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(a).cuda()
+
+
+def time_prefill(w, B, T, steps, warmup, torch, binding):
+    p = synth.make_params(w)
+    P = binding.Params(*[_to_dev(p[k], torch) for k in ("conv_w", "conv_b", "wa", "ba", "wx",
+                                                          "bx", "lambda")])
+    wb = synth.small(w, B=B, T=T)
+    x = _to_dev(synth.make_act(wb, "x"), torch)
+    y = _to_dev(synth.make_act(wb, "y"), torch)
+    h0 = _to_dev(synth.make_h0(wb), torch)
+    out = torch.empty_like(x)
+    hl = torch.empty((B, w.D), dtype=torch.float32, device="cuda")
+    cl = torch.empty((B, 3, w.D), dtype=x.dtype, device="cuda")
+    ws = binding.make_workspace(P, B, T)
+    for _ in range(warmup):
+        binding.rglru_prefill(P, x, y, h0, out=out, h_last=hl, conv_last=cl, workspace=ws)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        binding.rglru_prefill(P, x, y, h0, out=out, h_last=hl, conv_last=cl, workspace=ws)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    flags = ws.flags()
+    if flags:
+        raise RuntimeError("prefill workspace reported error flags %#x" % flags)
+    return ms
+
+
+def time_decode(w, N, steps, torch, binding):
+    p = synth.make_params(w)
+    P = binding.Params(*[_to_dev(p[k], torch) for k in ("conv_w", "conv_b", "wa", "ba", "wx",
+                                                          "bx", "lambda")])
+    wb = synth.small(w, B=N, T=steps)
+    x = _to_dev(synth.make_act(wb, "x"), torch)
+    y = _to_dev(synth.make_act(wb, "y"), torch)
+    h = torch.zeros((N, w.D), dtype=torch.float32, device="cuda")
+    cs = torch.zeros((N, 3, w.D), dtype=x.dtype, device="cuda")
+    outs = torch.empty_like(x)
+
+    def run():
+        for t in range(steps):
+            binding.rglru_decode_step(P, x[:, t], y[:, t], h, cs, out_t=outs[:, t])
+
+    run()  # warm-up
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    run()
+    e1.record()
+    torch.cuda.synchronize()
+    eager_us = e0.elapsed_time(e1) * 1e3 / steps
+    # the same loop captured once as a graph and replayed (no host launch cost per step)
+    graph_us = None
+    try:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            run()
+        torch.cuda.current_stream().wait_stream(s)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run()
+        g.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        graph_us = e0.elapsed_time(e1) * 1e3 / steps
+    except Exception as exc:  # graph capture is optional for the figure
+        print("decode graph capture skipped: %s" % exc, file=sys.stderr)
+    return eager_us, graph_us
+
+
+def cpu_baseline(w):
+    """The oracle on a bounded sample of the workload: all heads of the 8 sequences over the
+    first 2048 tokens (one OpenMP thread per (sequence, head) unit)."""
+    import oracle
+    B, T = w.B, min(w.T, 2048)
+    wb = synth.small(w, B=B, T=T)
+    p = synth.make_params(w)
+    x = synth.make_act(wb, "x")
+    y = synth.make_act(wb, "y")
+    h0 = synth.make_h0(wb)
+    P = oracle.Params(p["conv_w"], p["conv_b"], p["wa"], p["ba"], p["wx"], p["bx"], p["lambda"], w.H)
+    lib = oracle.load()
+    threads = min(lib.oracle_max_threads(), B * w.H)
+    t = time.perf_counter()
+    oracle.prefill(P, x, y, h0=h0, nthreads=threads, lib=lib)
+    dt = time.perf_counter() - t
+    return {"value": B * T * w.D / dt, "unit": "tokens·channels/s", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": "B=%d sequences x T=%d tokens x D=%d (all %d heads), fp64 sequential "
+                      "oracle, OpenMP over (sequence, head) units" % (B, T, w.D, w.H)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="prefill headline only")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d "
+              "requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gated_linear_recurrence_amd import binding
+    binding.load_library()
+    w = synth.WORKLOADS[synth.BATCHED_2B]
+    ms = time_prefill(w, w.B, w.T, args.steps, args.warmup, torch, binding)
+    tokch = w.B * w.T * w.D
+    nbytes = algorithmic_bytes(w, w.B, w.T)
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC, "value": tokch / (ms * 1e-3), "unit": "tokens·channels/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; x, y ~ N(0,1); random-init gate and conv weights)",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "D": w.D, "gate_heads": w.H,
+                   "block": w.bs, "state": "fp32", "h0_std": w.h0_std},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "prefill_kernel<256, bf16>", "algorithmic_bytes": nbytes},
+    }
+    if not args.no_extras:
+        w2 = synth.WORKLOADS[synth.PREFILL_2B]
+        ms2 = time_prefill(w2, w2.B, w2.T, max(args.steps, 50), args.warmup, torch, binding)
+        b2 = algorithmic_bytes(w2, w2.B, w2.T)
+        line["prefill_2b_single"] = {
+            "workload": w2.name, "ms": ms2, "tokens·channels/s": w2.B * w2.T * w2.D / (ms2 * 1e-3),
+            "algorithmic_GBs": b2 / (ms2 * 1e-3) / 1e9, "hbm_frac": b2 / (ms2 * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "note": "34 MB working set fits the 256 MB Infinity Cache; not flushed between reps"}
+        wd = synth.WORKLOADS[synth.DECODE_2B]
+        eager_us, graph_us = time_decode(wd, wd.B, wd.T, torch, binding)
+        db = decode_bytes(wd, wd.B)
+        best = graph_us if graph_us is not None else eager_us
+        line["decode"] = {"workload": wd.name, "us_per_step_graph": graph_us,
+                          "us_per_step_eager": eager_us, "bytes_per_step": db,
+                          "hbm_frac": db / (best * 1e-6) / 1e9 / HBM_PEAK_GBS}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

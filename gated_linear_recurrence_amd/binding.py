@@ -1,0 +1,244 @@
+"""ctypes binding of librglru.so (argument marshalling only).
+
+Every step of the path runs in the library's HIP kernels; this module checks
+tensor dtype/device/contiguity/shape, passes ``data_ptr()`` values and
+``torch.cuda.current_stream().cuda_stream``, and raises on a non-zero status.
+PyTorch supplies device memory and streams, nothing else.
+
+There is no fallback: if librglru.so is missing or fails to load, every call
+raises ``RuntimeError``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "librglru.so")
+
+RGLRU_F32 = 0
+RGLRU_BF16 = 1
+STATUS = {0: "RGLRU_OK", 1: "RGLRU_ERR_NULL", 2: "RGLRU_ERR_SHAPE", 3: "RGLRU_ERR_UNSUPPORTED",
+          4: "RGLRU_ERR_WORKSPACE", 5: "RGLRU_ERR_ALIAS", 6: "RGLRU_ERR_HIP"}
+EXPORTS = ["rglru_prefill_workspace_bytes", "rglru_prefill_workspace_init", "rglru_prefill",
+           "rglru_decode_step", "conv1d_state_update", "rglru_prefill_workspace_flags",
+           "rglru_status_string", "rglru_last_hip_error", "rglru_abi_version"]
+
+_lock = threading.Lock()
+_lib = None
+
+
+class RglruError(RuntimeError):
+    def __init__(self, status: int, where: str, hip_error: int = 0):
+        msg = "%s failed: %s" % (where, STATUS.get(status, status))
+        if status == 6:
+            msg += " (hipError %d)" % hip_error
+        super().__init__(msg)
+        self.status = status
+
+
+class rglru_params(ctypes.Structure):
+    _fields_ = [("D", ctypes.c_int32), ("n_heads", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("conv_w", ctypes.c_void_p), ("conv_b", ctypes.c_void_p),
+                ("gate_a_w", ctypes.c_void_p), ("gate_a_b", ctypes.c_void_p),
+                ("gate_x_w", ctypes.c_void_p), ("gate_x_b", ctypes.c_void_p),
+                ("lambda_", ctypes.c_void_p)]
+
+
+def load_library(path: str = LIB_PATH):
+    """Load librglru.so (no build, no fallback)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError("librglru.so not found at %s: build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`" % path)
+        lib = ctypes.CDLL(path)
+        P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        PP = ctypes.POINTER(rglru_params)
+        lib.rglru_prefill_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
+        lib.rglru_prefill_workspace_bytes.restype = SZ
+        lib.rglru_prefill_workspace_init.argtypes = [P, SZ, P]
+        lib.rglru_prefill_workspace_init.restype = ctypes.c_int
+        lib.rglru_prefill.argtypes = [PP, I32, I32, P, P, P, P, P, P, P, P, SZ, P]
+        lib.rglru_prefill.restype = ctypes.c_int
+        lib.rglru_decode_step.argtypes = [PP, I32, P, I64, P, I64, P, I64, P, P, P]
+        lib.rglru_decode_step.restype = ctypes.c_int
+        lib.conv1d_state_update.argtypes = [PP, I32, I32, P, P, P, P]
+        lib.conv1d_state_update.restype = ctypes.c_int
+        lib.rglru_prefill_workspace_flags.argtypes = [P, SZ, ctypes.POINTER(ctypes.c_uint32), P]
+        lib.rglru_prefill_workspace_flags.restype = ctypes.c_int
+        lib.rglru_status_string.argtypes = [ctypes.c_int]
+        lib.rglru_status_string.restype = ctypes.c_char_p
+        lib.rglru_last_hip_error.argtypes = []
+        lib.rglru_last_hip_error.restype = ctypes.c_int
+        lib.rglru_abi_version.argtypes = []
+        lib.rglru_abi_version.restype = ctypes.c_int
+        _lib = lib
+        return lib
+
+
+def _check(lib, st: int, where: str):
+    if st != 0:
+        raise RglruError(st, where, lib.rglru_last_hip_error() if st == 6 else 0)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(dt) -> int:
+    if dt == torch.bfloat16:
+        return RGLRU_BF16
+    if dt == torch.float32:
+        return RGLRU_F32
+    raise TypeError("storage dtype must be torch.bfloat16 or torch.float32, got %s" % dt)
+
+
+def _need(t, name, dtype, shape=None, device=None):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s: expected %s, got %s" % (name, dtype, t.dtype))
+    if device is not None and t.device != device:
+        raise ValueError("%s: expected device %s, got %s" % (name, device, t.device))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s: expected shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+class Params:
+    """Block parameters on one device (storage dtype bf16 or fp32; Lambda fp32).
+
+    conv_w [D, 4]; conv_b [D] or None; gate_a_w, gate_x_w [H, bs, bs] stored like Linear
+    weights ([out, in]); gate_a_b, gate_x_b [D] or None; lam [D] fp32.
+    """
+
+    def __init__(self, conv_w, conv_b, gate_a_w, gate_a_b, gate_x_w, gate_x_b, lam):
+        self.dtype = conv_w.dtype
+        self.code = _dtype_code(self.dtype)
+        self.device = conv_w.device
+        D = conv_w.shape[0]
+        H = gate_a_w.shape[0]
+        bs = gate_a_w.shape[1]
+        _need(conv_w, "conv_w", self.dtype, (D, 4), self.device)
+        _need(conv_b, "conv_b", self.dtype, (D,), self.device)
+        _need(gate_a_w, "gate_a_w", self.dtype, (H, bs, bs), self.device)
+        _need(gate_x_w, "gate_x_w", self.dtype, (H, bs, bs), self.device)
+        _need(gate_a_b, "gate_a_b", self.dtype, (D,), self.device)
+        _need(gate_x_b, "gate_x_b", self.dtype, (D,), self.device)
+        _need(lam, "lam", torch.float32, (D,), self.device)
+        if H * bs != D:
+            raise ValueError("gate blocks %d x %d do not tile D=%d" % (H, bs, D))
+        self.D, self.H, self.bs = D, H, bs
+        self.tensors = (conv_w, conv_b, gate_a_w, gate_a_b, gate_x_w, gate_x_b, lam)
+        self.c = rglru_params(D, H, self.code, *[t.data_ptr() if t is not None else None
+                                                 for t in self.tensors])
+
+
+def rglru_prefill_workspace_bytes(B: int, T: int, D: int, n_heads: int, dtype) -> int:
+    lib = load_library()
+    return int(lib.rglru_prefill_workspace_bytes(B, T, D, n_heads, _dtype_code(dtype)))
+
+
+def rglru_prefill_workspace_init(ws: torch.Tensor):
+    lib = load_library()
+    _check(lib, lib.rglru_prefill_workspace_init(_ptr(ws), ws.numel(), _stream()),
+           "rglru_prefill_workspace_init")
+
+
+class Workspace:
+    """A reusable prefill workspace (uint8 device tensor, initialised once)."""
+
+    def __init__(self, nbytes: int, device):
+        self.t = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+        rglru_prefill_workspace_init(self.t)
+
+    @property
+    def nbytes(self) -> int:
+        return self.t.numel()
+
+    def flags(self) -> int:
+        lib = load_library()
+        v = ctypes.c_uint32(0)
+        _check(lib, lib.rglru_prefill_workspace_flags(_ptr(self.t), self.t.numel(),
+                                                      ctypes.byref(v), _stream()),
+               "rglru_prefill_workspace_flags")
+        return int(v.value)
+
+
+def make_workspace(p: Params, B: int, T: int) -> Workspace:
+    return Workspace(rglru_prefill_workspace_bytes(B, T, p.D, p.H, p.dtype), p.device)
+
+
+def rglru_prefill(p: Params, x, y, h0=None, conv0=None, *, out=None, h_last=None, conv_last=None,
+                  workspace: Workspace | None = None, want_state: bool = True):
+    """out = prefill(x, y); returns (out, h_last, conv_last) (state tensors None if not wanted)."""
+    lib = load_library()
+    B, T, D = x.shape
+    _need(x, "x", p.dtype, (B, T, p.D), p.device)
+    _need(y, "y", p.dtype, (B, T, p.D), p.device)
+    _need(h0, "h0", torch.float32, (B, D), p.device)
+    _need(conv0, "conv0", p.dtype, (B, 3, D), p.device)
+    if out is None:
+        out = torch.empty_like(x)
+    _need(out, "out", p.dtype, (B, T, D), p.device)
+    if want_state:
+        if h_last is None:
+            h_last = torch.empty((B, D), dtype=torch.float32, device=p.device)
+        if conv_last is None:
+            conv_last = torch.empty((B, 3, D), dtype=p.dtype, device=p.device)
+    _need(h_last, "h_last", torch.float32, (B, D), p.device)
+    _need(conv_last, "conv_last", p.dtype, (B, 3, D), p.device)
+    if workspace is None:
+        workspace = make_workspace(p, B, T)
+    st = lib.rglru_prefill(ctypes.byref(p.c), B, T, _ptr(x), _ptr(y), _ptr(out), _ptr(h0),
+                           _ptr(h_last), _ptr(conv0), _ptr(conv_last), _ptr(workspace.t),
+                           workspace.nbytes, _stream())
+    _check(lib, st, "rglru_prefill")
+    return out, h_last, conv_last
+
+
+def rglru_decode_step(p: Params, x_t, y_t, h, conv_state, out_t=None):
+    """One token for N sequences.  x_t, y_t [N, D] (rows may be strided, e.g. x[:, t]);
+    h [N, D] fp32 and conv_state [N, 3, D] are updated in place.  Returns out_t [N, D]."""
+    lib = load_library()
+    N, D = x_t.shape
+    for t, name in ((x_t, "x_t"), (y_t, "y_t")):
+        if t.dtype != p.dtype or t.device != p.device or t.shape != (N, p.D) or t.stride(1) != 1:
+            raise ValueError("%s must be [N, D] %s rows with unit channel stride" % (name, p.dtype))
+    _need(h, "h", torch.float32, (N, D), p.device)
+    _need(conv_state, "conv_state", p.dtype, (N, 3, D), p.device)
+    if out_t is None:
+        out_t = torch.empty((N, D), dtype=p.dtype, device=p.device)
+    if out_t.shape != (N, D) or out_t.stride(1) != 1 or out_t.dtype != p.dtype:
+        raise ValueError("out_t must be [N, D] rows with unit channel stride")
+    st = lib.rglru_decode_step(ctypes.byref(p.c), N, _ptr(x_t), x_t.stride(0), _ptr(y_t),
+                               y_t.stride(0), _ptr(out_t), out_t.stride(0), _ptr(h),
+                               _ptr(conv_state), _stream())
+    _check(lib, st, "rglru_decode_step")
+    return out_t
+
+
+def conv1d_state_update(p: Params, x_new, conv_state, want_out: bool = True):
+    """x_new [N, T_new, D]; conv_state [N, 3, D] updated in place.  Returns conv_out or None."""
+    lib = load_library()
+    N, T_new, D = x_new.shape
+    _need(x_new, "x_new", p.dtype, (N, T_new, p.D), p.device)
+    _need(conv_state, "conv_state", p.dtype, (N, 3, D), p.device)
+    out = torch.empty_like(x_new) if want_out else None
+    st = lib.conv1d_state_update(ctypes.byref(p.c), N, T_new, _ptr(x_new), _ptr(conv_state),
+                                 _ptr(out), _stream())
+    _check(lib, st, "conv1d_state_update")
+    return out

@@ -1,0 +1,229 @@
+// C ABI of librglru.so: argument validation, workspace sizing and kernel launches.
+// Every check runs on the host before any HIP call; see include/rglru.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/rglru.h"
+#include "rglru_internal.h"
+
+using namespace rglru;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_fail(hipError_t e) {
+    g_last_hip_error = (int)e;
+    return RGLRU_ERR_HIP;
+}
+
+size_t elem_size(int dtype) { return dtype == RGLRU_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; }
+
+// [p, p + n) and [q, q + m) overlap (null or empty ranges never overlap)
+bool overlap(const void* p, size_t n, const void* q, size_t m) {
+    if (!p || !q || n == 0 || m == 0) return false;
+    const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
+    return a < b + m && b < a + n;
+}
+
+// Shared checks of the parameter struct.  Returns RGLRU_OK or an error status.
+int check_params(const rglru_params* p, bool need_gates) {
+    if (!p) return RGLRU_ERR_NULL;
+    if (p->dtype != RGLRU_F32 && p->dtype != RGLRU_BF16) return RGLRU_ERR_UNSUPPORTED;
+    if (p->D < 1 || p->n_heads < 1 || p->D % p->n_heads != 0) return RGLRU_ERR_SHAPE;
+    if (!p->conv_w) return RGLRU_ERR_NULL;
+    if (!aligned16(p->conv_w) || !aligned16(p->conv_b)) return RGLRU_ERR_UNSUPPORTED;
+    if (p->D % 8 != 0) return RGLRU_ERR_UNSUPPORTED;
+    if (need_gates) {
+        const int bs = p->D / p->n_heads;
+        if (bs != 128 && bs != 256) return RGLRU_ERR_UNSUPPORTED;
+        if (!p->gate_a_w || !p->gate_x_w || !p->lambda) return RGLRU_ERR_NULL;
+        if (!aligned16(p->gate_a_w) || !aligned16(p->gate_x_w) || !aligned16(p->gate_a_b) ||
+            !aligned16(p->gate_x_b) || !aligned16(p->lambda))
+            return RGLRU_ERR_UNSUPPORTED;
+    }
+    return RGLRU_OK;
+}
+
+size_t n_segments(int32_t T) { return T <= 0 ? 1 : ((size_t)T + kSeg - 1) / kSeg; }
+
+}  // namespace
+
+extern "C" {
+
+int rglru_abi_version(void) { return RGLRU_ABI_VERSION; }
+
+int rglru_last_hip_error(void) { return g_last_hip_error; }
+
+const char* rglru_status_string(int status) {
+    switch (status) {
+        case RGLRU_OK: return "ok";
+        case RGLRU_ERR_NULL: return "a required pointer is NULL";
+        case RGLRU_ERR_SHAPE: return "invalid shape";
+        case RGLRU_ERR_UNSUPPORTED: return "unsupported block size, dtype or alignment";
+        case RGLRU_ERR_WORKSPACE: return "workspace missing or too small";
+        case RGLRU_ERR_ALIAS: return "an output overlaps an input it may not alias";
+        case RGLRU_ERR_HIP: return "HIP call failed";
+        default: return "unknown status";
+    }
+}
+
+size_t rglru_prefill_workspace_bytes(int32_t B, int32_t T, int32_t D, int32_t n_heads,
+                                     int32_t dtype) {
+    if (B < 1 || T < 0 || D < 1 || n_heads < 1 || D % n_heads != 0) return 0;
+    if (dtype != RGLRU_F32 && dtype != RGLRU_BF16) return 0;
+    return kWsHeader + n_segments(T) * (size_t)B * (size_t)D * sizeof(unsigned long long);
+}
+
+int rglru_prefill_workspace_init(void* workspace, size_t ws_bytes, void* stream) {
+    if (!workspace) return RGLRU_ERR_NULL;
+    if (!aligned16(workspace)) return RGLRU_ERR_UNSUPPORTED;
+    if (ws_bytes < kWsHeader) return RGLRU_ERR_WORKSPACE;
+    hipError_t e = launch_workspace_init(workspace, ws_bytes, (hipStream_t)stream);
+    return e == hipSuccess ? RGLRU_OK : hip_fail(e);
+}
+
+int rglru_prefill(const rglru_params* p, int32_t B, int32_t T, const void* x, const void* y,
+                  void* out, const float* h0, float* h_last, const void* conv0, void* conv_last,
+                  void* workspace, size_t ws_bytes, void* stream) {
+    int st = check_params(p, true);
+    if (st != RGLRU_OK) return st;
+    if (B < 1 || T < 0) return RGLRU_ERR_SHAPE;
+    if (T > 0 && (!x || !y || !out)) return RGLRU_ERR_NULL;
+    if (!aligned16(x) || !aligned16(y) || !aligned16(out) || !aligned16(h0) ||
+        !aligned16(h_last) || !aligned16(conv0) || !aligned16(conv_last) || !aligned16(workspace))
+        return RGLRU_ERR_UNSUPPORTED;
+    const size_t es = elem_size(p->dtype);
+    const size_t n_act = (size_t)B * (size_t)T * (size_t)p->D * es;
+    const size_t n_h = (size_t)B * (size_t)p->D * sizeof(float);
+    const size_t n_c = (size_t)B * 3 * (size_t)p->D * es;
+    const size_t need = rglru_prefill_workspace_bytes(B, T, p->D, p->n_heads, p->dtype);
+    if (T > 0 && (!workspace || ws_bytes < need)) return RGLRU_ERR_WORKSPACE;
+    // outputs: out vs every input; state outputs may alias their own input exactly
+    if (overlap(out, n_act, x, n_act) || overlap(out, n_act, y, n_act) ||
+        overlap(out, n_act, h0, n_h) || overlap(out, n_act, h_last, n_h) ||
+        overlap(out, n_act, conv0, n_c) || overlap(out, n_act, conv_last, n_c))
+        return RGLRU_ERR_ALIAS;
+    if (overlap(h_last, n_h, x, n_act) || overlap(h_last, n_h, y, n_act) ||
+        overlap(h_last, n_h, conv0, n_c) || overlap(h_last, n_h, conv_last, n_c) ||
+        ((const void*)h_last != (const void*)h0 && overlap(h_last, n_h, h0, n_h)))
+        return RGLRU_ERR_ALIAS;
+    if (overlap(conv_last, n_c, x, n_act) || overlap(conv_last, n_c, y, n_act) ||
+        overlap(conv_last, n_c, h0, n_h) ||
+        (conv_last != conv0 && overlap(conv_last, n_c, conv0, n_c)))
+        return RGLRU_ERR_ALIAS;
+    if (T > 0) {
+        const void* ins[] = {x, y, out, h0, h_last, conv0, conv_last};
+        const size_t lens[] = {n_act, n_act, n_act, n_h, n_h, n_c, n_c};
+        for (int i = 0; i < 7; ++i)
+            if (overlap(workspace, need, ins[i], lens[i])) return RGLRU_ERR_ALIAS;
+    }
+
+    PrefillArgs a;
+    memset(&a, 0, sizeof a);
+    a.x = x; a.y = y; a.out = out;
+    a.conv_w = p->conv_w; a.conv_b = p->conv_b;
+    a.wa = p->gate_a_w; a.ba = p->gate_a_b; a.wx = p->gate_x_w; a.bx = p->gate_x_b;
+    a.lambda = p->lambda;
+    a.h0 = h0; a.h_last = h_last; a.conv0 = conv0; a.conv_last = conv_last;
+    a.B = B; a.T = T; a.D = p->D; a.H = p->n_heads;
+    hipError_t e;
+    if (T == 0) {
+        if (!h_last && !conv_last) return RGLRU_OK;
+        e = launch_prefill_empty(a, p->dtype, (hipStream_t)stream);
+        return e == hipSuccess ? RGLRU_OK : hip_fail(e);
+    }
+    const size_t S = n_segments(T);
+    const size_t units = S * (size_t)B * (size_t)p->n_heads;
+    if (units > 0x7fffffffu) return RGLRU_ERR_SHAPE;
+    a.S = (int)S;
+    a.n_units = (int)units;
+    a.header = static_cast<unsigned*>(workspace);
+    a.words = reinterpret_cast<unsigned long long*>(static_cast<char*>(workspace) + kWsHeader);
+    e = launch_prefill(a, p->dtype, p->D / p->n_heads, (hipStream_t)stream);
+    return e == hipSuccess ? RGLRU_OK : hip_fail(e);
+}
+
+int rglru_decode_step(const rglru_params* p, int32_t N, const void* x_t, int64_t ld_x,
+                      const void* y_t, int64_t ld_y, void* out_t, int64_t ld_out, float* h,
+                      void* conv_state, void* stream) {
+    int st = check_params(p, true);
+    if (st != RGLRU_OK) return st;
+    if (N < 1) return RGLRU_ERR_SHAPE;
+    if (!x_t || !y_t || !out_t || !h || !conv_state) return RGLRU_ERR_NULL;
+    const int64_t D = p->D;
+    if (ld_x == 0) ld_x = D;
+    if (ld_y == 0) ld_y = D;
+    if (ld_out == 0) ld_out = D;
+    if (ld_x < D || ld_y < D || ld_out < D) return RGLRU_ERR_SHAPE;
+    if (!aligned16(x_t) || !aligned16(y_t) || !aligned16(out_t) || !aligned16(h) ||
+        !aligned16(conv_state))
+        return RGLRU_ERR_UNSUPPORTED;
+    const size_t es = elem_size(p->dtype);
+    if ((ld_x * (int64_t)es) % 16 || (ld_y * (int64_t)es) % 16 || (ld_out * (int64_t)es) % 16)
+        return RGLRU_ERR_UNSUPPORTED;
+    const size_t sx = ((size_t)(N - 1) * (size_t)ld_x + (size_t)D) * es;
+    const size_t sy = ((size_t)(N - 1) * (size_t)ld_y + (size_t)D) * es;
+    const size_t so = ((size_t)(N - 1) * (size_t)ld_out + (size_t)D) * es;
+    const size_t sh = (size_t)N * (size_t)D * sizeof(float);
+    const size_t sc = (size_t)N * 3 * (size_t)D * es;
+    if (overlap(out_t, so, x_t, sx) || overlap(out_t, so, y_t, sy) || overlap(out_t, so, h, sh) ||
+        overlap(out_t, so, conv_state, sc) || overlap(h, sh, x_t, sx) || overlap(h, sh, y_t, sy) ||
+        overlap(h, sh, conv_state, sc) || overlap(conv_state, sc, x_t, sx) ||
+        overlap(conv_state, sc, y_t, sy))
+        return RGLRU_ERR_ALIAS;
+    DecodeArgs a;
+    memset(&a, 0, sizeof a);
+    a.x = x_t; a.y = y_t; a.out = out_t;
+    a.ld_x = ld_x; a.ld_y = ld_y; a.ld_out = ld_out;
+    a.conv_w = p->conv_w; a.conv_b = p->conv_b;
+    a.wa = p->gate_a_w; a.ba = p->gate_a_b; a.wx = p->gate_x_w; a.bx = p->gate_x_b;
+    a.lambda = p->lambda;
+    a.h = h; a.conv_state = conv_state;
+    a.N = N; a.D = p->D; a.H = p->n_heads;
+    hipError_t e = launch_decode(a, p->dtype, p->D / p->n_heads, (hipStream_t)stream);
+    return e == hipSuccess ? RGLRU_OK : hip_fail(e);
+}
+
+int conv1d_state_update(const rglru_params* p, int32_t N, int32_t T_new, const void* x_new,
+                        void* conv_state, void* conv_out, void* stream) {
+    int st = check_params(p, false);
+    if (st != RGLRU_OK) return st;
+    if (N < 1 || T_new < 0) return RGLRU_ERR_SHAPE;
+    if (!conv_state || (T_new > 0 && !x_new)) return RGLRU_ERR_NULL;
+    if (!aligned16(x_new) || !aligned16(conv_state) || !aligned16(conv_out))
+        return RGLRU_ERR_UNSUPPORTED;
+    const size_t es = elem_size(p->dtype);
+    const size_t sx = (size_t)N * (size_t)T_new * (size_t)p->D * es;
+    const size_t sc = (size_t)N * 3 * (size_t)p->D * es;
+    if (overlap(conv_out, sx, x_new, sx) || overlap(conv_out, sx, conv_state, sc) ||
+        overlap(conv_state, sc, x_new, sx))
+        return RGLRU_ERR_ALIAS;
+    if (T_new == 0) return RGLRU_OK;  // nothing to convolve; the window is unchanged
+    ConvArgs a;
+    a.x = x_new; a.conv_w = p->conv_w; a.conv_b = p->conv_b;
+    a.conv_state = conv_state; a.conv_out = conv_out;
+    a.N = N; a.T = T_new; a.D = p->D;
+    hipError_t e = launch_conv_update(a, p->dtype, (hipStream_t)stream);
+    return e == hipSuccess ? RGLRU_OK : hip_fail(e);
+}
+
+int rglru_prefill_workspace_flags(void* workspace, size_t ws_bytes, uint32_t* flags_out,
+                                  void* stream) {
+    if (!workspace || !flags_out) return RGLRU_ERR_NULL;
+    if (ws_bytes < kWsHeader) return RGLRU_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    uint32_t* hdr = static_cast<uint32_t*>(workspace);
+    static const uint32_t zero = 0;
+    hipError_t e = hipMemcpyAsync(flags_out, hdr + 1, sizeof(uint32_t), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e == hipSuccess) e = hipMemcpyAsync(hdr + 1, &zero, sizeof(uint32_t), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    return e == hipSuccess ? RGLRU_OK : hip_fail(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,275 @@
+// Decode step: one token for each of N sequences, updating the carried fp32 state h and the
+// three-token conv window in place (the fixed-size state that lets the recurrent block
+// generate sequences of any length: page "Gemma 詳解：RecurrentGemma 架構", sections
+// "模型寬度與 RNN 寬度" and "區域注意力視窗大小").
+//
+// Workgroup = (tile of 32 sequences, gate head).  The conv runs over [window, x_t] and shifts
+// the window; u goes to LDS; the gate projections of the 32 sequences are one 32-row MFMA
+// tile per wave (32 output channels); then h <- a h + sqrt(1-a^2) i u and
+// out = h * gelu_tanh(y_t).
+#include <type_traits>
+
+#include "rglru_device.h"
+#include "rglru_internal.h"
+
+namespace rglru {
+
+namespace {
+
+template <int BS, typename ST>
+__global__ void __launch_bounds__(2 * BS) decode_kernel(DecodeArgs a) {
+    using S = Store<ST>;
+    constexpr bool kBf = S::kBf16;
+    constexpr int kChunks = BS / 8;
+    constexpr int kGroups = (2 * BS) / kChunks;  // 16 sequence groups of 2
+    constexpr int kRow = kBf ? BS + 8 : BS + 4;
+    using L = typename std::conditional<kBf, uint16_t, float>::type;
+    __shared__ __attribute__((aligned(16))) L u_lds[32 * kRow];
+
+    const int tid = threadIdx.x;
+    const int n0 = blockIdx.x * 32;
+    const int head = blockIdx.y;
+    const int N = a.N;
+    const size_t D = (size_t)a.D;
+    ST* __restrict__ cs = static_cast<ST*>(a.conv_state);
+
+    // ---- conv over [window, x_t]; shift the window in place ----
+    {
+        const int cg = tid % kChunks, sg = tid / kChunks;
+        const size_t c0 = (size_t)head * BS + cg * 8;
+        const ST* cw = static_cast<const ST*>(a.conv_w) + c0 * 4;
+        float w[4][8];
+        {
+            float tmp[8];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                S::load8(cw + 8 * q, tmp);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) w[e & 3][2 * q + (e >> 2)] = tmp[e];
+            }
+        }
+        float cb[8];
+        if (a.conv_b) S::load8(static_cast<const ST*>(a.conv_b) + c0, cb);
+        else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) cb[e] = 0.0f;
+        }
+#pragma unroll
+        for (int k = 0; k < 32 / kGroups; ++k) {
+            const int m = sg * (32 / kGroups) + k;
+            const int n = n0 + m;
+            float u[8];
+            if (n < N) {
+                float s0[8], s1[8], s2[8], xt[8];
+                S::load8(cs + ((size_t)n * 3 + 0) * D + c0, s0);
+                S::load8(cs + ((size_t)n * 3 + 1) * D + c0, s1);
+                S::load8(cs + ((size_t)n * 3 + 2) * D + c0, s2);
+                S::load8(static_cast<const ST*>(a.x) + (size_t)n * a.ld_x + c0, xt);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float acc = __builtin_fmaf(w[0][e], s0[e], cb[e]);
+                    acc = __builtin_fmaf(w[1][e], s1[e], acc);
+                    acc = __builtin_fmaf(w[2][e], s2[e], acc);
+                    u[e] = __builtin_fmaf(w[3][e], xt[e], acc);
+                }
+                S::store8(cs + ((size_t)n * 3 + 0) * D + c0, s1);
+                S::store8(cs + ((size_t)n * 3 + 1) * D + c0, s2);
+                S::store8(cs + ((size_t)n * 3 + 2) * D + c0, xt);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) u[e] = 0.0f;
+            }
+            L* dst = u_lds + m * kRow + cg * 8;
+            if constexpr (kBf) {
+                *reinterpret_cast<uint4*>(dst) = make_uint4(pack2bf(u[0], u[1]), pack2bf(u[2], u[3]),
+                                                            pack2bf(u[4], u[5]), pack2bf(u[6], u[7]));
+            } else {
+                *reinterpret_cast<float4*>(dst) = make_float4(u[0], u[1], u[2], u[3]);
+                *reinterpret_cast<float4*>(dst + 4) = make_float4(u[4], u[5], u[6], u[7]);
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- gates: one 32x32 tile per gate per wave (rows = sequences) ----
+    const int wv = tid >> 6, lane = tid & 63, ln = lane & 31, kh = lane >> 5;
+    const int ncol = wv * 32 + ln;
+    const size_t ch = (size_t)head * BS + ncol;
+    f32x16 accA, accX;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) { accA[e] = 0.0f; accX[e] = 0.0f; }
+    {
+        const ST* war = static_cast<const ST*>(a.wa) + ((size_t)head * BS + ncol) * BS;
+        const ST* wxr = static_cast<const ST*>(a.wx) + ((size_t)head * BS + ncol) * BS;
+        if constexpr (kBf) {
+#pragma unroll
+            for (int q4 = 0; q4 < BS / 64; ++q4) {
+                const int kb = 64 * q4 + 32 * kh;
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const bf16x8 bA = *reinterpret_cast<const bf16x8*>(war + kb + 8 * s);
+                    const bf16x8 bX = *reinterpret_cast<const bf16x8*>(wxr + kb + 8 * s);
+                    const bf16x8 A = *reinterpret_cast<const bf16x8*>(u_lds + ln * kRow + kb + 8 * s);
+                    accA = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, bA, accA, 0, 0, 0);
+                    accX = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, bX, accX, 0, 0, 0);
+                }
+            }
+        } else {
+#pragma unroll 4
+            for (int k4 = 0; k4 < BS / 2; k4 += 4) {
+                const int kb = kh * (BS / 2) + k4;
+                const float4 bA = *reinterpret_cast<const float4*>(war + kb);
+                const float4 bX = *reinterpret_cast<const float4*>(wxr + kb);
+                const float4 A = *reinterpret_cast<const float4*>(u_lds + ln * kRow + kb);
+                const float a4[4] = {A.x, A.y, A.z, A.w};
+                const float ba4[4] = {bA.x, bA.y, bA.z, bA.w}, bx4[4] = {bX.x, bX.y, bX.z, bX.w};
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    accA = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[s], ba4[s], accA, 0, 0, 0);
+                    accX = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[s], bx4[s], accX, 0, 0, 0);
+                }
+            }
+        }
+    }
+
+    // ---- gate math, state update, output ----
+    const float lam = a.lambda[ch];
+    const float sp = softplus_neg(lam);
+    const float bia = a.ba ? S::get(static_cast<const ST*>(a.ba), ch) : 0.0f;
+    const float bix = a.bx ? S::get(static_cast<const ST*>(a.bx), ch) : 0.0f;
+    const float nba = -bia * kLog2e, nbx = -bix * kLog2e;
+    const float kc = -8.0f * sp * kLog2e, kcn = -8.0f * sp;
+    const ST* __restrict__ y = static_cast<const ST*>(a.y);
+    ST* __restrict__ out = static_cast<ST*>(a.out);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int m = mfma_d_row(lane, j);
+        const int n = n0 + m;
+        if (n >= N) continue;
+        float u;
+        if constexpr (kBf) u = bf2f(u_lds[m * kRow + ncol]);
+        else u = u_lds[m * kRow + ncol];
+        const GateOut g = kBf ? gate_fast(accA[j], accX[j], nba, nbx, kc, u)
+                              : gate_precise(accA[j], accX[j], bia, bix, kcn, u);
+        float* hp = a.h + (size_t)n * D + ch;
+        const float hn = __builtin_fmaf(g.a, *hp, g.v);
+        *hp = hn;
+        const float yf = S::get(y, (size_t)n * a.ld_y + ch);
+        const float gl = kBf ? gelu_fast(yf) : gelu_precise(yf);
+        S::put(out, (size_t)n * a.ld_out + ch, hn * gl);
+    }
+}
+
+// conv outputs for a block of 16 tokens of one (sequence, 8-channel chunk); reads the old window
+template <typename ST>
+__global__ void conv_out_kernel(ConvArgs a) {
+    using S = Store<ST>;
+    constexpr int kTB = 16;
+    const int chunks = a.D / 8;
+    const int tblocks = (a.T + kTB - 1) / kTB;
+    const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= (size_t)a.N * chunks * tblocks) return;
+    const int cg = (int)(gid % chunks);
+    const int tb = (int)((gid / chunks) % tblocks);
+    const int n = (int)(gid / ((size_t)chunks * tblocks));
+    const size_t D = (size_t)a.D, c0 = (size_t)cg * 8;
+    const ST* x = static_cast<const ST*>(a.x);
+    const ST* cs = static_cast<const ST*>(a.conv_state);
+    float w[4][8], cb[8];
+    {
+        float tmp[8];
+        const ST* cw = static_cast<const ST*>(a.conv_w) + c0 * 4;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            S::load8(cw + 8 * q, tmp);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) w[e & 3][2 * q + (e >> 2)] = tmp[e];
+        }
+    }
+    if (a.conv_b) S::load8(static_cast<const ST*>(a.conv_b) + c0, cb);
+    else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cb[e] = 0.0f;
+    }
+    float r0[8], r1[8], r2[8];
+    auto row = [&](int t, float (&v)[8]) {
+        if (t >= 0) S::load8(x + ((size_t)n * a.T + t) * D + c0, v);
+        else S::load8(cs + ((size_t)n * 3 + 3 + t) * D + c0, v);
+    };
+    const int tbeg = tb * kTB;
+    row(tbeg - 3, r0);
+    row(tbeg - 2, r1);
+    row(tbeg - 1, r2);
+    ST* o = static_cast<ST*>(a.conv_out);
+    for (int t = tbeg; t < min(a.T, tbeg + kTB); ++t) {
+        float xt[8], u[8];
+        row(t, xt);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float acc = __builtin_fmaf(w[0][e], r0[e], cb[e]);
+            acc = __builtin_fmaf(w[1][e], r1[e], acc);
+            acc = __builtin_fmaf(w[2][e], r2[e], acc);
+            u[e] = __builtin_fmaf(w[3][e], xt[e], acc);
+            r0[e] = r1[e];
+            r1[e] = r2[e];
+            r2[e] = xt[e];
+        }
+        S::store8(o + ((size_t)n * a.T + t) * D + c0, u);
+    }
+}
+
+// new window = the last three of [old window, x_new] (each element read and written by one thread)
+template <typename ST>
+__global__ void conv_state_kernel(ConvArgs a) {
+    using S = Store<ST>;
+    const int chunks = a.D / 8;
+    const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= (size_t)a.N * chunks) return;
+    const int cg = (int)(gid % chunks);
+    const int n = (int)(gid / chunks);
+    const size_t D = (size_t)a.D, c0 = (size_t)cg * 8;
+    ST* cs = static_cast<ST*>(a.conv_state);
+    const ST* x = static_cast<const ST*>(a.x);
+    float v[3][8];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        const int t = a.T - 3 + j;
+        if (t >= 0) S::load8(x + ((size_t)n * a.T + t) * D + c0, v[j]);
+        else S::load8(cs + ((size_t)n * 3 + 3 + t) * D + c0, v[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 3; ++j) S::store8(cs + ((size_t)n * 3 + j) * D + c0, v[j]);
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, int dtype, int bs, hipStream_t s) {
+    const dim3 grid((a.N + 31) / 32, a.H);
+    if (dtype == 1) {
+        if (bs == 256) hipLaunchKernelGGL((decode_kernel<256, uint16_t>), grid, dim3(512), 0, s, a);
+        else hipLaunchKernelGGL((decode_kernel<128, uint16_t>), grid, dim3(256), 0, s, a);
+    } else {
+        if (bs == 256) hipLaunchKernelGGL((decode_kernel<256, float>), grid, dim3(512), 0, s, a);
+        else hipLaunchKernelGGL((decode_kernel<128, float>), grid, dim3(256), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_conv_update(const ConvArgs& a, int dtype, hipStream_t s) {
+    const int chunks = a.D / 8;
+    if (a.conv_out != nullptr && a.T > 0) {
+        const size_t n = (size_t)a.N * chunks * ((a.T + 15) / 16);
+        const dim3 grid((unsigned)((n + 255) / 256));
+        if (dtype == 1) hipLaunchKernelGGL(conv_out_kernel<uint16_t>, grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL(conv_out_kernel<float>, grid, dim3(256), 0, s, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const size_t n = (size_t)a.N * chunks;
+    const dim3 grid((unsigned)((n + 255) / 256));
+    if (dtype == 1) hipLaunchKernelGGL(conv_state_kernel<uint16_t>, grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(conv_state_kernel<float>, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace rglru

@@ -1,0 +1,66 @@
+// Host-side declarations shared by the library's translation units (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rglru {
+
+constexpr int kSeg = 64;              // tokens per prefill time segment (one workgroup)
+constexpr size_t kWsHeader = 256;     // workspace header bytes (counters and error flags)
+
+struct PrefillArgs {
+    const void* x;
+    const void* y;
+    void* out;
+    const void* conv_w;
+    const void* conv_b;
+    const void* wa;
+    const void* ba;
+    const void* wx;
+    const void* bx;
+    const float* lambda;
+    const float* h0;
+    float* h_last;
+    const void* conv0;
+    void* conv_last;
+    unsigned long long* words;  // carry words [S][B][D]
+    unsigned* header;           // [0] ticket counter, [1] error flags, [2] finished workgroups
+    int B, T, D, H, S;
+    int n_units;                // S * B * H workgroups
+};
+
+struct DecodeArgs {
+    const void* x;
+    const void* y;
+    void* out;
+    long long ld_x, ld_y, ld_out;
+    const void* conv_w;
+    const void* conv_b;
+    const void* wa;
+    const void* ba;
+    const void* wx;
+    const void* bx;
+    const float* lambda;
+    float* h;
+    void* conv_state;
+    int N, D, H;
+};
+
+struct ConvArgs {
+    const void* x;       // [N][T][D]
+    const void* conv_w;
+    const void* conv_b;
+    void* conv_state;    // [N][3][D]
+    void* conv_out;      // [N][T][D] or null
+    int N, T, D;
+};
+
+hipError_t launch_prefill(const PrefillArgs& a, int dtype, int bs, hipStream_t s);
+hipError_t launch_prefill_empty(const PrefillArgs& a, int dtype, hipStream_t s);
+hipError_t launch_workspace_init(void* ws, size_t bytes, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, int dtype, int bs, hipStream_t s);
+hipError_t launch_conv_update(const ConvArgs& a, int dtype, hipStream_t s);
+
+}  // namespace rglru

@@ -1,0 +1,154 @@
+/*
+ * rglru.h -- C ABI of the MI355X (gfx950) RG-LRU recurrent-block library (librglru.so).
+ *
+ * The operation is the recurrent block's temporal-mixing path of RecurrentGemma, as laid
+ * out on the page "Gemma 詳解：RecurrentGemma 架構" (section "含遞迴區塊的殘差區塊" and the
+ * module printout): two width-D branches; on one, a depthwise Conv1d with kernel 4
+ * followed by the RG-LRU; on the other, GELU (tanh form); the branches are multiplied.
+ * The library starts from the two branch projections' outputs:
+ *
+ *   x = linear_x(.), y = linear_y(.)            [B][T][D]  (inputs of every call)
+ *   u_t   = conv_b + sum_{j=0..3} conv_w[:, j] * x_{t-3+j}     (causal, depthwise)
+ *   r_t   = sigmoid(blockdiag(W_a) u_t + b_a),  i_t = sigmoid(blockdiag(W_x) u_t + b_x)
+ *   a_t   = sigmoid(Lambda) ** (8 r_t)
+ *   h_t   = a_t * h_{t-1} + sqrt(1 - a_t^2) * (i_t * u_t)
+ *   out_t = h_t * gelu_tanh(y_t)
+ *
+ * The RG-LRU lines are the Griffin paper's definition (arXiv 2402.19427, linked from the
+ * article "RecurrentGemma vs 传统LLM..."); the pages name the unit and its fixed-size
+ * state ("模型寬度與 RNN 寬度") but print no formula.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless stated otherwise; the rglru_params struct itself
+ *     is host memory (read during the call only).
+ *   - Tensors are row-major and contiguous with the channel axis D innermost.
+ *   - The caller allocates and owns every buffer, including the prefill workspace.
+ *   - Calls are asynchronous on the caller's HIP stream (passed as void*, NULL = default
+ *     stream) and never synchronise the host.  Results are available after the stream
+ *     reaches them.
+ *   - Every call returns an rglru_status.  Arguments are validated on the host before any
+ *     HIP call; a failing call leaves every buffer untouched.  RGLRU_ERR_HIP means a launch
+ *     failed; the hipError_t is kept per thread (rglru_last_hip_error).  Faults inside a
+ *     kernel surface at the caller's next synchronisation.
+ *   - Results are deterministic: the same inputs give bitwise the same outputs (no float
+ *     atomics; carries are always folded in sequence order).
+ *   - Storage type `dtype` (RGLRU_F32 or RGLRU_BF16) applies to x, y, out, the conv state and
+ *     all weights except Lambda; Lambda and the recurrent state h are always fp32.
+ *   - Supported block sizes bs = D / n_heads: 128 and 256.  All pointers 16-byte aligned.
+ */
+#ifndef RGLRU_H
+#define RGLRU_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RGLRU_ABI_VERSION 1
+
+enum rglru_dtype { RGLRU_F32 = 0, RGLRU_BF16 = 1 };
+
+enum rglru_status {
+    RGLRU_OK = 0,
+    RGLRU_ERR_NULL = 1,        /* a required pointer is NULL */
+    RGLRU_ERR_SHAPE = 2,       /* B/N < 1, T < 0, D < 1, n_heads < 1, D % n_heads != 0, bad stride */
+    RGLRU_ERR_UNSUPPORTED = 3, /* bs not in {128, 256}, unknown dtype, pointer not 16-byte aligned */
+    RGLRU_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than rglru_prefill_workspace_bytes */
+    RGLRU_ERR_ALIAS = 5,       /* an output overlaps an input it may not alias */
+    RGLRU_ERR_HIP = 6          /* a HIP call failed; see rglru_last_hip_error() */
+};
+
+/*
+ * Parameters of one recurrent block (device pointers, storage type `dtype` unless noted).
+ *   conv_w   [D][4]      tap j multiplies x_{t-3+j}: the first T outputs of PyTorch's
+ *                        Conv1d(D, D, 4, padding=3, groups=D) weight [D][1][4], squeezed
+ *   conv_b   [D] or NULL (NULL = no bias)
+ *   gate_a_w [H][bs][bs] block h of the recurrence gate, stored like a Linear weight
+ *                        [out j][in k]: pre_a[h*bs+j] = b_a[h*bs+j] + sum_k W_a[h][j][k] u[h*bs+k]
+ *   gate_a_b [D] or NULL
+ *   gate_x_w [H][bs][bs] input gate, same layout;  gate_x_b [D] or NULL
+ *   lambda   [D] fp32    (always fp32)
+ */
+typedef struct rglru_params {
+    int32_t D;
+    int32_t n_heads;
+    int32_t dtype;
+    const void *conv_w;
+    const void *conv_b;
+    const void *gate_a_w;
+    const void *gate_a_b;
+    const void *gate_x_w;
+    const void *gate_x_b;
+    const float *lambda;
+} rglru_params;
+
+/*
+ * Bytes of device workspace rglru_prefill needs for this shape (0 on invalid shapes).
+ * The workspace holds the cross-workgroup carry words of the time-segmented scan.  Before
+ * its first use a workspace must be initialised once with rglru_prefill_workspace_init;
+ * every completed rglru_prefill leaves it initialised again, so it can be reused for any
+ * shape that fits.  Calls sharing one workspace must be ordered on one stream.
+ */
+size_t rglru_prefill_workspace_bytes(int32_t B, int32_t T, int32_t D, int32_t n_heads,
+                                     int32_t dtype);
+
+/* Initialise a workspace of ws_bytes bytes on `stream` (asynchronous). */
+int rglru_prefill_workspace_init(void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Prefill over T tokens (the time-chunked scan).
+ *   x, y      [B][T][D]  inputs (storage dtype)
+ *   out       [B][T][D]  h_t * gelu_tanh(y_t), rounded to the storage dtype (nearest-even)
+ *   h0        [B][D] fp32 initial state, or NULL for zeros
+ *   h_last    [B][D] fp32 state after token T-1, or NULL to skip
+ *   conv0     [B][3][D]  last three conv inputs before token 0, oldest first, or NULL (zeros)
+ *   conv_last [B][3][D]  last three conv inputs after the call, or NULL to skip
+ *   workspace, ws_bytes  caller-owned device scratch (see above)
+ * h0 == h_last and conv0 == conv_last (in place) are allowed; out must not overlap x or y.
+ * T = 0 is valid: h_last = h0 and conv_last = conv0 (or zeros).
+ */
+int rglru_prefill(const rglru_params *p, int32_t B, int32_t T, const void *x, const void *y,
+                  void *out, const float *h0, float *h_last, const void *conv0, void *conv_last,
+                  void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * One decode step for N sequences (one token each), updating the carried state in place.
+ *   x_t, y_t, out_t  [N][D] rows with element strides ld_x, ld_y, ld_out between rows
+ *                    (0 means D), so a slice [:, t] of an [N][T][D] tensor needs no copy
+ *   h                [N][D] fp32 state, read and written in place
+ *   conv_state       [N][3][D] last three conv inputs, oldest first, read and written in place
+ * out_t must not overlap x_t, y_t, h or conv_state.
+ */
+int rglru_decode_step(const rglru_params *p, int32_t N, const void *x_t, int64_t ld_x,
+                      const void *y_t, int64_t ld_y, void *out_t, int64_t ld_out, float *h,
+                      void *conv_state, void *stream);
+
+/*
+ * Conv-state update (the conv part of the path on its own).
+ *   x_new      [N][T_new][D] new conv inputs (storage dtype); T_new >= 0
+ *   conv_state [N][3][D]     updated in place to the last three inputs, oldest first
+ *   conv_out   [N][T_new][D] the conv outputs u_t (storage dtype, nearest-even), or NULL
+ * Only p->D, p->dtype, p->conv_w and p->conv_b are read.  conv_out must not overlap x_new.
+ */
+int conv1d_state_update(const rglru_params *p, int32_t N, int32_t T_new, const void *x_new,
+                        void *conv_state, void *conv_out, void *stream);
+
+/*
+ * Diagnostics of a prefill workspace: copies its error flags to *flags_out (0 = none) and
+ * clears them.  Synchronous (waits for `stream`).  Bit 0: a carry wait exceeded its bound
+ * (the affected outputs are NaN).
+ */
+int rglru_prefill_workspace_flags(void *workspace, size_t ws_bytes, uint32_t *flags_out,
+                                  void *stream);
+
+const char *rglru_status_string(int status);
+int rglru_last_hip_error(void); /* hipError_t of this thread's last failing HIP call */
+int rglru_abi_version(void);    /* RGLRU_ABI_VERSION */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RGLRU_H */
