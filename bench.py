@@ -152,6 +152,23 @@ def cpu_baseline(w):
                       "oracle, OpenMP over (sequence, head) units" % (B, T, w.D, w.H)}
 
 
+def copy_probe(torch, nbytes: int = 1 << 30, reps: int = 5):
+    """A plain copy of known size: reads and writes nbytes per launch."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    print(json.dumps({"copy_probe_bytes_each_way": nbytes, "ms": ms,
+                      "GBs_read_plus_write": 2 * nbytes / (ms * 1e-3) / 1e9}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -159,6 +176,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="prefill headline only")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="time a plain 1 GiB device-to-device copy instead (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d "
@@ -166,6 +185,9 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_probe:
+        copy_probe(torch)
+        return
     from gated_linear_recurrence_amd import binding
     binding.load_library()
     w = synth.WORKLOADS[synth.BATCHED_2B]

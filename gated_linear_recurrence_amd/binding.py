@@ -162,7 +162,7 @@ class Workspace:
     """A reusable prefill workspace (uint8 device tensor, initialised once)."""
 
     def __init__(self, nbytes: int, device):
-        self.t = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+        self.t = torch.empty(max(int(nbytes), 4096), dtype=torch.uint8, device=device)
         rglru_prefill_workspace_init(self.t)
 
     @property

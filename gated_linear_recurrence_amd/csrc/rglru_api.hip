@@ -41,6 +41,7 @@ int check_params(const rglru_params* p, bool need_gates) {
     if (need_gates) {
         const int bs = p->D / p->n_heads;
         if (bs != 128 && bs != 256) return RGLRU_ERR_UNSUPPORTED;
+        if (p->n_heads > kMaxHeads) return RGLRU_ERR_UNSUPPORTED;
         if (!p->gate_a_w || !p->gate_x_w || !p->lambda) return RGLRU_ERR_NULL;
         if (!aligned16(p->gate_a_w) || !aligned16(p->gate_x_w) || !aligned16(p->gate_a_b) ||
             !aligned16(p->gate_x_b) || !aligned16(p->lambda))

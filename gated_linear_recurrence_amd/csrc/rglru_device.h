@@ -93,6 +93,7 @@ __device__ __forceinline__ GateOut gate_fast(float sa, float sx, float nba, floa
     const float ei = __builtin_amdgcn_exp2f(__builtin_fmaf(sx, -kLog2e, nbx));
     const float i = __builtin_amdgcn_rcpf(1.0f + ei);
     const float a = __builtin_amdgcn_exp2f(kc * r);
+    // a <= 1 in exact arithmetic; the clamp guards the 1-ulp error of the hardware exp2
     const float m = __builtin_amdgcn_sqrtf(fmaxf(__builtin_fmaf(-a, a, 1.0f), 0.0f));
     return {a, m * (i * u)};
 }

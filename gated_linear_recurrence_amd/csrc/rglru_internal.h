@@ -8,7 +8,12 @@
 namespace rglru {
 
 constexpr int kSeg = 64;              // tokens per prefill time segment (one workgroup)
-constexpr size_t kWsHeader = 256;     // workspace header bytes (counters and error flags)
+constexpr size_t kWsHeader = 4096;    // workspace header bytes (counters and error flags)
+// header words: [0] error flags, [1] finished workgroups, [kTicketWord + h] ticket counter of head h
+constexpr int kErrWord = 0;
+constexpr int kDoneWord = 1;
+constexpr int kTicketWord = 16;
+constexpr int kMaxHeads = 2048 / 4 - kTicketWord;  // header bytes 2048.. hold a zero block
 
 struct PrefillArgs {
     const void* x;
@@ -26,9 +31,10 @@ struct PrefillArgs {
     const void* conv0;
     void* conv_last;
     unsigned long long* words;  // carry words [S][B][D]
-    unsigned* header;           // [0] ticket counter, [1] error flags, [2] finished workgroups
+    unsigned* header;           // see kErrWord, kDoneWord, kTicketWord
     int B, T, D, H, S;
-    int n_units;                // S * B * H workgroups
+    int n_units;                // S * B * H units (generic kernel: one workgroup each)
+    int wph;                    // persistent kernel: workgroups per head
 };
 
 struct DecodeArgs {

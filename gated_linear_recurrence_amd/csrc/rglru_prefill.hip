@@ -16,6 +16,7 @@
 //      segments; carries are always folded forward from an inclusive word, so the result
 //      does not depend on timing.
 //   5. fix-up h_t = b_t + p_t * carry, out_t = h_t * gelu_tanh(y_t), store.
+#include <atomic>
 #include <type_traits>
 
 #include "rglru_device.h"
@@ -48,18 +49,23 @@ __device__ __forceinline__ void st_word(unsigned long long* p, unsigned long lon
 }
 
 // Carry into segment `seg` (> 0) for one channel.  wself points at this segment's word;
-// the predecessor's word is wself - wstride.
-__device__ float look_back(unsigned long long* wself, size_t wstride, int seg, float A_seg,
-                           float B_seg, bool publish_aggregate, unsigned* header) {
-    const unsigned long long w1 = ld_word(wself - wstride);
+// the predecessor's word is wself - wstride and w1 is a value already read from it.  The
+// window is read before this segment's aggregate is published so that waiting for the reads
+// never waits for that store.
+__device__ float look_back(unsigned long long* wself, size_t wstride, int seg, unsigned long long w1,
+                           float A_seg, float B_seg, bool publish_aggregate, unsigned* header) {
     if (w_ready(w1) && w_inclusive(w1)) return w_B(w1);
-    if (publish_aggregate) st_word(wself, make_word(A_seg, B_seg, false));
     const int n = seg < kWindow ? seg : kWindow;
+    bool published = !publish_aggregate;
     for (unsigned it = 0;; ++it) {
         unsigned long long win[kWindow];
 #pragma unroll
         for (int k = 0; k < kWindow; ++k)
             win[k] = (k < n) ? ld_word(wself - (size_t)(k + 1) * wstride) : kNotReady;
+        if (!published) {
+            st_word(wself, make_word(A_seg, B_seg, false));
+            published = true;
+        }
         int kinc = -1;
         bool blocked = false;
 #pragma unroll
@@ -80,7 +86,7 @@ __device__ float look_back(unsigned long long* wself, size_t wstride, int seg, f
             return c;
         }
         if (it >= kSpinLimit) {
-            atomicOr(&header[1], 1u);
+            atomicOr(&header[kErrWord], 1u);
             return __builtin_nanf("");
         }
         __builtin_amdgcn_s_sleep(1);
@@ -129,8 +135,10 @@ __device__ __forceinline__ void finish_outputs(const f32x16 (&accB)[2], const f3
     }
 }
 
+// Generic kernel (fp32 and bf16 storage, exact-precision gate math for fp32); one ticket
+// counter over all units.  The bf16 storage path uses prefill_bf16_kernel below.
 template <int BS, typename ST>
-__global__ void __launch_bounds__(2 * BS, 2) prefill_kernel(PrefillArgs a) {
+__global__ void __launch_bounds__(2 * BS) prefill_kernel(PrefillArgs a) {
     using C = Cfg<BS, ST>;
     using S = Store<ST>;
     using L = typename C::Lds;
@@ -141,7 +149,7 @@ __global__ void __launch_bounds__(2 * BS, 2) prefill_kernel(PrefillArgs a) {
     __shared__ unsigned s_ticket;
 
     const int tid = threadIdx.x;
-    if (tid == 0) s_ticket = atomicAdd(&a.header[0], 1u);
+    if (tid == 0) s_ticket = atomicAdd(&a.header[kTicketWord], 1u);
     __syncthreads();
     const unsigned ticket = s_ticket;
     const int n_chains = a.B * a.H;
@@ -334,7 +342,8 @@ __global__ void __launch_bounds__(2 * BS, 2) prefill_kernel(PrefillArgs a) {
             if (seg == 0) {
                 carry = a.h0 ? a.h0[(size_t)b * D + ch] : 0.0f;
             } else {
-                carry = look_back(wself, wstride, seg, A_seg, B_seg, !last, a.header);
+                carry = look_back(wself, wstride, seg, ld_word(wself - wstride), A_seg, B_seg, !last,
+                                  a.header);
             }
             if (!last) st_word(wself, make_word(A_seg, __builtin_fmaf(A_seg, carry, B_seg), true));
             if (seg > 0) st_word(wself - wstride, kNotReady);  // retire the predecessor's word
@@ -377,10 +386,436 @@ __global__ void __launch_bounds__(2 * BS, 2) prefill_kernel(PrefillArgs a) {
 
     // the last workgroup to finish resets the counters for the next call on this workspace
     if (tid == 0) {
-        const unsigned done = atomicAdd(&a.header[2], 1u);
+        const unsigned done = atomicAdd(&a.header[kDoneWord], 1u);
         if (done == (unsigned)a.n_units - 1) {
-            atomicExch(&a.header[0], 0u);
-            atomicExch(&a.header[2], 0u);
+            atomicExch(&a.header[kTicketWord], 0u);
+            atomicExch(&a.header[kDoneWord], 0u);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// bf16 storage, persistent kernel (the measured path).
+//
+// One workgroup per CU, pinned to one gate head for its lifetime: each wave keeps the B
+// fragments of its 32 output channels of both gate blocks in VGPRs (128 registers), so the
+// gate weights are read once per workgroup instead of once per segment.  The workgroup walks
+// the head's segments in ticket order (segment-major over the batch) and pipelines them:
+//   iteration k:  [conv k: x_k (LDS) -> u (LDS)] [store out_{k-1}] [DMA x_{k+1}, y_{k+1}]
+//                 [MFMA k] [gate math + scan k] [carry k] [GELU merge k -> registers]
+// x and y reach LDS by direct global->LDS loads (global_load_lds_dwordx4) one segment ahead;
+// the outputs of segment k are stored during iteration k+1, after its conv, so no wait on
+// the memory counter ever waits for freshly issued stores.
+// Placement: the hardware deals workgroups to the 8 XCDs round-robin; consecutive slots of
+// one XCD are given to one head, so each XCD's L2 serves few heads.
+// ---------------------------------------------------------------------------------------
+typedef unsigned short ushort2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0xffffffff, 0x00020000);
+}
+
+__device__ __forceinline__ float dot2bf(uint32_t w, uint32_t x, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
+                                           __builtin_bit_cast(bf16x2, x), c, false);
+}
+
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
+
+#ifndef RGLRU_NT256
+#define RGLRU_NT256 1
+#endif
+constexpr int kSchedGroup = 4;  // elements the scheduler may interleave (bounds register use)
+
+template <int BS>
+struct PCfg {
+    static constexpr int kNT = BS == 256 ? RGLRU_NT256 : 1;  // 32-channel MFMA tiles per wave
+    static constexpr int kWaves = BS / (32 * kNT);      // 4 waves: one per SIMD
+    static constexpr int kThreads = 64 * kWaves;
+    static constexpr int kRow = BS + 8;                 // ubuf row stride (bf16 elements)
+    static constexpr int kRowB = BS * 2;                // bytes of one head's slice of a token row
+    static constexpr int kHalo = 16;                    // xbuf rows before the segment
+    static constexpr int kXRows = kSeg + kHalo;         // tokens t0-16 .. t0+63
+    static constexpr int kRowsPerInst = 1024 / kRowB;   // one DMA instruction moves 1 KB
+    static constexpr int kLanesPerRow = kRowB / 16;
+    static constexpr int kXInst = kXRows / kRowsPerInst / kWaves;
+    static constexpr int kYInst = kSeg / kRowsPerInst / kWaves;
+    static constexpr int kPairs = BS / 2;               // conv: channel pairs ...
+    static constexpr int kTokGroups = kThreads / kPairs;  // ... x token groups
+    static constexpr int kTok = kSeg / kTokGroups;
+    static constexpr int kKSteps = BS / 16;
+    static_assert(kXInst * kRowsPerInst * kWaves == kXRows, "x DMA tiling");
+    static_assert(kYInst * kRowsPerInst * kWaves == kSeg, "y DMA tiling");
+    static_assert(kTokGroups * kTok == kSeg, "conv tiling");
+};
+
+// Direct global->LDS copy of one segment's rows of one head: LDS row r receives token
+// t0 + first + r of the ticket's sequence, clamped to [0, T-1]; a ticket past the end copies
+// the last segment again (harmless).
+template <int BS, int kInst>
+__device__ __forceinline__ void dma_rows(const char* head_base, unsigned tk, unsigned n_tk, int B,
+                                         int T, int rowb, int first, int wv, int dma_r,
+                                         uint16_t* lds) {
+    using C = PCfg<BS>;
+    tk = min(tk, n_tk - 1);
+    const int t0 = (int)(tk / (unsigned)B) * kSeg;
+    const char* base = head_base + (size_t)(tk % (unsigned)B) * T * rowb;
+#pragma unroll
+    for (int q = 0; q < kInst; ++q) {
+        const int inst = wv * kInst + q;
+        const int tr = min(max(t0 + first + inst * C::kRowsPerInst + dma_r, 0), T - 1);
+        __builtin_amdgcn_global_load_lds(base + (size_t)tr * rowb, lds + inst * 512, 16, 0, 0);
+    }
+}
+
+// A copy of v that the compiler cannot see through: values derived from it inside the loop
+// are recomputed there instead of being kept live across it (the gate weights already occupy
+// half of the register file).
+__device__ __forceinline__ int opaque(int v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+template <int BS>
+__global__ void __launch_bounds__(PCfg<BS>::kThreads)
+prefill_bf16_kernel(PrefillArgs a) {
+    using C = PCfg<BS>;
+    constexpr int kNT = C::kNT;
+    constexpr int kRow = C::kRow;
+    __shared__ __attribute__((aligned(16))) uint16_t xbuf[C::kXRows * BS];
+    __shared__ __attribute__((aligned(16))) uint16_t ybuf[2][kSeg * BS];
+    __shared__ __attribute__((aligned(16))) uint16_t ubuf[kSeg * kRow];
+    __shared__ __attribute__((aligned(16))) uint4 conv_tab[BS / 2];   // taps of a channel pair
+    __shared__ __attribute__((aligned(8))) float2 convb_tab[BS / 2];  // biases of a channel pair
+    __shared__ __attribute__((aligned(16))) float4 gate_tab[BS];      // (nba, nbx, kc, 0) per channel
+    __shared__ unsigned s_tk[2];
+
+    const int tid0 = threadIdx.x;
+    const int wv = __builtin_amdgcn_readfirstlane(tid0 >> 6);
+    const int B = a.B, T = a.T;
+    const size_t D = (size_t)a.D;
+    const int rowb = (int)(D * 2);
+
+    // ---- placement: slot -> head ----
+    const unsigned G = gridDim.x, bid = blockIdx.x;
+    const unsigned xcd = bid & 7u, jx = bid >> 3, per = G >> 3, rem = G & 7u;
+    const unsigned slot = xcd * per + min(xcd, rem) + jx;
+    const int head = (int)(slot / (unsigned)a.wph);
+    unsigned* tctr = a.header + kTicketWord + head;
+    const unsigned n_tk = (unsigned)(B * a.S);
+
+    const uint16_t* __restrict__ x = static_cast<const uint16_t*>(a.x);
+    const uint16_t* __restrict__ y = static_cast<const uint16_t*>(a.y);
+
+    // ---- per-workgroup tables: conv taps and biases, gate constants of the head's channels ----
+    for (int i = tid0; i < BS / 2; i += C::kThreads) {
+        const size_t c0 = (size_t)head * BS + 2 * i;
+        conv_tab[i] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.conv_w) + c0 * 4);
+        float2 cb = make_float2(0.0f, 0.0f);
+        if (a.conv_b) {
+            const uint32_t bb = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.conv_b) + c0);
+            cb = make_float2(bf_lo(bb), bf_hi(bb));
+        }
+        convb_tab[i] = cb;
+    }
+    for (int i = tid0; i < BS; i += C::kThreads) {
+        const size_t chn = (size_t)head * BS + i;
+        const float sp = softplus_neg(a.lambda[chn]);
+        const float bia = a.ba ? bf2f(static_cast<const uint16_t*>(a.ba)[chn]) : 0.0f;
+        const float bix = a.bx ? bf2f(static_cast<const uint16_t*>(a.bx)[chn]) : 0.0f;
+        gate_tab[i] = make_float4(-bia * kLog2e, -bix * kLog2e, -8.0f * sp * kLog2e, 0.0f);
+    }
+    // gate weights of this wave's channels [cw0, cw0 + 32 kNT), held in registers throughout
+    const int cw0 = wv * 32 * kNT;
+    bf16x8 wA[kNT][C::kKSteps], wX[kNT][C::kKSteps];
+    {
+        const int lane = tid0 & 63, ln = lane & 31, kh = lane >> 5;
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) {
+            const size_t chn = (size_t)head * BS + cw0 + 32 * nt + ln;
+            const uint16_t* war = static_cast<const uint16_t*>(a.wa) + chn * BS;
+            const uint16_t* wxr = static_cast<const uint16_t*>(a.wx) + chn * BS;
+#pragma unroll
+            for (int kk = 0; kk < C::kKSteps; ++kk) {
+                // K order: lane half kh supplies elements [64 q + 32 kh + 8 s, +8) at step 4q + s
+                const int kb = 64 * (kk >> 2) + 32 * kh + 8 * (kk & 3);
+                wA[nt][kk] = *reinterpret_cast<const bf16x8*>(war + kb);
+                wX[nt][kk] = *reinterpret_cast<const bf16x8*>(wxr + kb);
+            }
+        }
+    }
+    const char* xseq = reinterpret_cast<const char*>(x + (size_t)head * BS);
+    const char* yseq = reinterpret_cast<const char*>(y + (size_t)head * BS);
+
+    // ---- prologue ----
+    if (tid0 == 0) {
+        s_tk[0] = atomicAdd(tctr, 1u);
+        s_tk[1] = atomicAdd(tctr, 1u);
+    }
+    __syncthreads();
+    unsigned cur = s_tk[0], nxt = s_tk[1];
+    {
+        const int lane = tid0 & 63;
+        const char* xh = xseq + 16 * (lane % C::kLanesPerRow);
+        const char* yh = yseq + 16 * (lane % C::kLanesPerRow);
+        dma_rows<BS, C::kXInst>(xh, cur, n_tk, B, T, rowb, -C::kHalo, wv, lane / C::kLanesPerRow, xbuf);
+        dma_rows<BS, C::kYInst>(yh, cur, n_tk, B, T, rowb, 0, wv, lane / C::kLanesPerRow, ybuf[0]);
+    }
+    wait_vmem_all();
+    unsigned it = 0;
+
+    while (cur < n_tk) {
+        const int tid = opaque(tid0);
+        const int lane = tid & 63, ln = lane & 31, kh = lane >> 5, hh = lane >> 5;
+        const int seg = (int)(cur / (unsigned)B), b = (int)(cur % (unsigned)B);
+        const int t0 = seg * kSeg;
+        const int nt_tok = min(kSeg, T - t0);
+        const bool last = (seg == a.S - 1);
+        const uint16_t* ycur = ybuf[it & 1];
+
+        // x and y of `cur` have landed: each wave waited for its own DMA (prologue or the
+        // previous iteration); the barrier covers every wave
+        __syncthreads();
+        if (it > 0) nxt = s_tk[0];  // grabbed during the previous iteration, published before the barrier
+        if (seg == 0) {
+            // tokens -3..-1 come from the carried conv state (or are zero), not from x
+            constexpr int kCh = BS / 8;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (tid < 3 * kCh && a.conv0 != nullptr)
+                v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.conv0) +
+                                                    ((size_t)b * 3 + tid / kCh) * D + (size_t)head * BS + (tid % kCh) * 8);
+            if (tid < 3 * kCh)
+                *reinterpret_cast<uint4*>(xbuf + (C::kHalo - 3 + tid / kCh) * BS + (tid % kCh) * 8) = v;
+            __syncthreads();
+        }
+
+        // ---------------- 1. conv -> u (bf16) in LDS ----------------
+        {
+            const int cp = tid % C::kPairs;
+            const int tg = __builtin_amdgcn_readfirstlane(tid / C::kPairs);
+            const uint4 wq = conv_tab[cp];
+            const float2 cb = convb_tab[cp];
+            const uint32_t* xw = reinterpret_cast<const uint32_t*>(xbuf);
+            uint32_t xr[C::kTok + 3];
+#pragma unroll
+            for (int k = 0; k < C::kTok + 3; ++k)
+                xr[k] = xw[(tg * C::kTok + C::kHalo - 3 + k) * C::kPairs + cp];
+            uint16_t* ucol = ubuf + 2 * cp;
+#pragma unroll
+            for (int k = 0; k < C::kTok; ++k) {
+                // (x_{t-3}, x_{t-2}) and (x_{t-1}, x_t) of each of the two channels
+                const uint32_t p0a = __builtin_amdgcn_perm(xr[k + 1], xr[k], 0x05040100u);
+                const uint32_t p0b = __builtin_amdgcn_perm(xr[k + 1], xr[k], 0x07060302u);
+                const uint32_t p2a = __builtin_amdgcn_perm(xr[k + 3], xr[k + 2], 0x05040100u);
+                const uint32_t p2b = __builtin_amdgcn_perm(xr[k + 3], xr[k + 2], 0x07060302u);
+                const float u0 = dot2bf(wq.y, p2a, dot2bf(wq.x, p0a, cb.x));
+                const float u1 = dot2bf(wq.w, p2b, dot2bf(wq.z, p0b, cb.y));
+                *reinterpret_cast<uint32_t*>(ucol + lds_row(tg * C::kTok + k) * kRow) = pack2bf(u0, u1);
+            }
+        }
+        // conv state after the last token: rows T-3..T-1 are in xbuf now; they are written
+        // after the carry wait, which orders the write after segment 0 read conv0 (in place)
+        uint4 cl_rows = make_uint4(0, 0, 0, 0);
+        constexpr int kClCh = BS / 8;
+        const bool cl_act = last && a.conv_last != nullptr && tid < 3 * kClCh;
+        if (cl_act)
+            cl_rows = *reinterpret_cast<const uint4*>(xbuf + (T - 3 + tid / kClCh - t0 + C::kHalo) * BS +
+                                                      (tid % kClCh) * 8);
+        __syncthreads();  // u complete; xbuf and ybuf[(it+1)&1] are free
+
+        // ---------------- prefetch the next segment ----------------
+        {
+            const char* xh = xseq + 16 * (lane % C::kLanesPerRow);
+            const char* yh = yseq + 16 * (lane % C::kLanesPerRow);
+            dma_rows<BS, C::kXInst>(xh, nxt, n_tk, B, T, rowb, -C::kHalo, wv, lane / C::kLanesPerRow, xbuf);
+            dma_rows<BS, C::kYInst>(yh, nxt, n_tk, B, T, rowb, 0, wv, lane / C::kLanesPerRow, ybuf[(it + 1) & 1]);
+        }
+        unsigned pending = 0;
+        if (tid == 0) pending = atomicAdd(tctr, 1u);  // ticket after next (published after a barrier)
+
+        // ---------------- 2.+3. gates on MFMA, gate math and local scan ----------------
+        // tile 0 (rows 0..31) on MFMA first; then tile 0's gate math element j is issued
+        // next to tile 1's MFMA step j, so the matrix core and the VALU work side by side
+        f32x16 accB[kNT][2], accP[kNT][2];
+        float psc[kNT], bsc[kNT];
+        {
+            const int atok = 32 * ((ln >> 2) & 1) + 4 * (ln >> 3) + (ln & 3);
+            const uint16_t* ap0 = ubuf + lds_row(atok) * kRow + 32 * kh;
+            const uint16_t* ap1 = ubuf + lds_row(atok + 16) * kRow + 32 * kh;
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    accB[nt][0][e] = 0.0f; accP[nt][0][e] = 0.0f; accB[nt][1][e] = 0.0f; accP[nt][1][e] = 0.0f;
+                }
+#pragma unroll
+            for (int kk = 0; kk < C::kKSteps; ++kk) {
+                const bf16x8 A = *reinterpret_cast<const bf16x8*>(ap0 + 64 * (kk >> 2) + 8 * (kk & 3));
+#pragma unroll
+                for (int nt = 0; nt < kNT; ++nt) {
+                    accB[nt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, wA[nt][kk], accB[nt][0], 0, 0, 0);
+                    accP[nt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, wX[nt][kk], accP[nt][0], 0, 0, 0);
+                }
+            }
+            float4 gc[kNT];
+            const uint16_t* ucol[kNT];
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) {
+                psc[nt] = 1.0f;
+                bsc[nt] = 0.0f;
+                gc[nt] = gate_tab[cw0 + 32 * nt + ln];
+                ucol[nt] = ubuf + 32 * hh * kRow + cw0 + 32 * nt + ln;
+            }
+            static_assert(C::kKSteps == 16 || C::kKSteps == 8, "interleave");
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                if (j < C::kKSteps) {
+                    const int kk = j;
+                    const bf16x8 A = *reinterpret_cast<const bf16x8*>(ap1 + 64 * (kk >> 2) + 8 * (kk & 3));
+#pragma unroll
+                    for (int nt = 0; nt < kNT; ++nt) {
+                        accB[nt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, wA[nt][kk], accB[nt][1], 0, 0, 0);
+                        accP[nt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, wX[nt][kk], accP[nt][1], 0, 0, 0);
+                    }
+                }
+#pragma unroll
+                for (int nt = 0; nt < kNT; ++nt) {
+                    const int row = 4 * ((j >> 2) ^ (3 * hh)) + (j & 3);
+                    const float u = bf2f(ucol[nt][row * kRow]);
+                    const GateOut g = gate_fast(accB[nt][0][j], accP[nt][0][j], gc[nt].x, gc[nt].y, gc[nt].z, u);
+                    bsc[nt] = __builtin_fmaf(g.a, bsc[nt], g.v);
+                    psc[nt] = psc[nt] * g.a;
+                    accB[nt][0][j] = bsc[nt];
+                    accP[nt][0][j] = psc[nt];
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+#pragma unroll
+                for (int nt = 0; nt < kNT; ++nt) {
+                    const int row = 16 + 4 * ((j >> 2) ^ (3 * hh)) + (j & 3);
+                    const float u = bf2f(ucol[nt][row * kRow]);
+                    const GateOut g = gate_fast(accB[nt][1][j], accP[nt][1][j], gc[nt].x, gc[nt].y, gc[nt].z, u);
+                    bsc[nt] = __builtin_fmaf(g.a, bsc[nt], g.v);
+                    psc[nt] = psc[nt] * g.a;
+                    accB[nt][1][j] = bsc[nt];
+                    accP[nt][1][j] = psc[nt];
+                }
+            }
+        }
+        // segment aggregates: low half-wave (tokens 0..31) then high half-wave (32..63)
+        float p_lo[kNT], b_lo[kNT], A_seg[kNT], B_seg[kNT];
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) {
+            const float p_o = __shfl_xor(psc[nt], 32), b_o = __shfl_xor(bsc[nt], 32);
+            p_lo[nt] = hh ? p_o : psc[nt];
+            b_lo[nt] = hh ? b_o : bsc[nt];
+            const float p_hi = hh ? psc[nt] : p_o, b_hi = hh ? bsc[nt] : b_o;
+            A_seg[nt] = p_lo[nt] * p_hi;
+            B_seg[nt] = __builtin_fmaf(p_hi, b_lo[nt], b_hi);
+        }
+
+        // ---------------- 4. carry: probe now, GELU while the probe is in flight ----------------
+        const bool lb_lane = (kNT == 2) || (hh == 0);
+        const int nt_lb = (kNT == 2) ? hh : 0;
+        const size_t chl = (size_t)head * BS + cw0 + 32 * nt_lb + ln;
+        const size_t wstride = (size_t)B * D;
+        unsigned long long* wself = a.words + (size_t)seg * wstride + (size_t)b * D + chl;
+        unsigned long long w1 = kNotReady;
+        float carry_mine = 0.0f;
+        if (lb_lane) {
+            if (seg > 0) w1 = ld_word(wself - wstride);
+            else if (a.h0 != nullptr) carry_mine = a.h0[(size_t)b * D + chl];
+        }
+        // y of this segment has been in LDS since the previous iteration: out_t = h_t g_t with
+        // h_t = b_t + p_t c, kept as (b_t g_t, p_t g_t) until the carry c is known
+        if (!last) {
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) {
+                const uint16_t* ycol = ycur + 32 * hh * BS + cw0 + 32 * nt + ln;
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        const float g = gelu_fast(bf2f(ycol[(16 * mt + j) * BS]));
+                        accB[nt][mt][j] *= g;
+                        accP[nt][mt][j] *= g;
+                    }
+                }
+            }
+        }
+        if (lb_lane) {
+            const float As = (kNT == 2 && hh) ? A_seg[kNT - 1] : A_seg[0];
+            const float Bs = (kNT == 2 && hh) ? B_seg[kNT - 1] : B_seg[0];
+            if (seg > 0) carry_mine = look_back(wself, wstride, seg, w1, As, Bs, !last, a.header);
+        }
+        // this wave's DMA of the next segment completes before the next iteration's barrier,
+        // and before the stores below are issued (so that wait never waits for them)
+        wait_vmem_all();
+        if (lb_lane) {
+            const float As = (kNT == 2 && hh) ? A_seg[kNT - 1] : A_seg[0];
+            const float Bs = (kNT == 2 && hh) ? B_seg[kNT - 1] : B_seg[0];
+            if (!last) st_word(wself, make_word(As, __builtin_fmaf(As, carry_mine, Bs), true));
+            if (seg > 0) st_word(wself - wstride, kNotReady);
+        }
+        float state_in[kNT];
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) {
+            const float c = __shfl(carry_mine, ln + 32 * (kNT == 2 ? nt : 0));
+            state_in[nt] = hh ? __builtin_fmaf(p_lo[nt], c, b_lo[nt]) : c;
+        }
+        if (cl_act)
+            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.conv_last) + ((size_t)b * 3 + tid / kClCh) * D +
+                                      (size_t)head * BS + (tid % kClCh) * 8) = cl_rows;
+
+        // ---------------- 5. fix-up and store ----------------
+        {
+            const __amdgpu_buffer_rsrc_t ro = make_rsrc(static_cast<uint16_t*>(a.out) + ((size_t)b * T + t0) * D);
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) {
+                const int chw = head * BS + cw0 + 32 * nt + ln;
+                const int voff = (32 * hh * (int)D + chw) * 2;
+                if (!last) {
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+                        for (int j = 0; j < 16; j += 2) {
+                            const float o0 = __builtin_fmaf(accP[nt][mt][j], state_in[nt], accB[nt][mt][j]);
+                            const float o1 = __builtin_fmaf(accP[nt][mt][j + 1], state_in[nt], accB[nt][mt][j + 1]);
+                            const uint32_t o01 = pack2bf(o0, o1);
+                            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)o01, ro, voff, (16 * mt + j) * rowb, 0);
+                            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(o01 >> 16), ro, voff, (16 * mt + j + 1) * rowb, 0);
+                        }
+                    }
+                } else {
+                    const uint16_t* ycol = ycur + 32 * hh * BS + cw0 + 32 * nt + ln;
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+                        for (int j = 0; j < 16; ++j) {
+                            const int tok = 32 * hh + 16 * mt + j;
+                            const float h = __builtin_fmaf(accP[nt][mt][j], state_in[nt], accB[nt][mt][j]);
+                            const float o = h * gelu_fast(bf2f(ycol[(16 * mt + j) * BS]));
+                            if (tok < nt_tok)
+                                __builtin_amdgcn_raw_buffer_store_b16(f2bf(o), ro, voff, (16 * mt + j) * rowb, 0);
+                            if (a.h_last != nullptr && t0 + tok == T - 1) a.h_last[(size_t)b * D + chw] = h;
+                        }
+                    }
+                }
+            }
+        }
+        if (tid == 0) s_tk[0] = pending;
+        cur = nxt;
+        ++it;
+    }
+
+    wait_vmem_all();  // no DMA into LDS may outlive the workgroup
+    if (tid0 == 0) {
+        const unsigned done = atomicAdd(&a.header[kDoneWord], 1u);
+        if (done == G - 1) {
+            for (int h = 0; h < a.H; ++h) atomicExch(&a.header[kTicketWord + h], 0u);
+            atomicExch(&a.header[kDoneWord], 0u);
         }
     }
 }
@@ -404,12 +839,33 @@ __global__ void workspace_init_kernel(unsigned long long* p, size_t n_words) {
 
 }  // namespace
 
-hipError_t launch_prefill(const PrefillArgs& a, int dtype, int bs, hipStream_t s) {
-    const dim3 grid(a.n_units);
+// Compute units of the current device (cached per device).
+static int device_cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+hipError_t launch_prefill(const PrefillArgs& a_in, int dtype, int bs, hipStream_t s) {
+    PrefillArgs a = a_in;
     if (dtype == 1) {
-        if (bs == 256) hipLaunchKernelGGL((prefill_kernel<256, uint16_t>), grid, dim3(512), 0, s, a);
-        else hipLaunchKernelGGL((prefill_kernel<128, uint16_t>), grid, dim3(256), 0, s, a);
+        // persistent: one workgroup per CU, the same number for every head
+        const int ncu = device_cu_count();
+        a.wph = ncu > a.H ? ncu / a.H : 1;
+        const dim3 grid(a.wph * a.H);
+        if (bs == 256)
+            hipLaunchKernelGGL((prefill_bf16_kernel<256>), grid, dim3(PCfg<256>::kThreads), 0, s, a);
+        else
+            hipLaunchKernelGGL((prefill_bf16_kernel<128>), grid, dim3(PCfg<128>::kThreads), 0, s, a);
     } else {
+        const dim3 grid(a.n_units);
         if (bs == 256) hipLaunchKernelGGL((prefill_kernel<256, float>), grid, dim3(512), 0, s, a);
         else hipLaunchKernelGGL((prefill_kernel<128, float>), grid, dim3(256), 0, s, a);
     }

@@ -64,9 +64,9 @@ def _prefill(lib, p, B=2, T=100, x=X, y=Y, out=OUT, h0=H0, hl=HL, c0=C0, cl=CL, 
 
 def test_workspace_bytes(lib):
     f = lib.rglru_prefill_workspace_bytes
-    assert f(8, 8192, 2560, 10, 1) == 256 + 128 * 8 * 2560 * 8
-    assert f(1, 1, 256, 2, 0) == 256 + 1 * 1 * 256 * 8
-    assert f(1, 0, 256, 2, 0) == 256 + 256 * 8
+    assert f(8, 8192, 2560, 10, 1) == 4096 + 128 * 8 * 2560 * 8
+    assert f(1, 1, 256, 2, 0) == 4096 + 1 * 1 * 256 * 8
+    assert f(1, 0, 256, 2, 0) == 4096 + 256 * 8
     assert f(0, 10, 256, 2, 0) == 0
     assert f(1, -1, 256, 2, 0) == 0
     assert f(1, 10, 255, 2, 0) == 0
