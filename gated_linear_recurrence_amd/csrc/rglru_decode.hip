@@ -160,6 +160,160 @@ __global__ void __launch_bounds__(2 * BS) decode_kernel(DecodeArgs a) {
     }
 }
 
+// bf16 storage: the same step with every long-latency load issued up front and none of
+// them under a branch.  A load guarded by `n < N` whose value is converted inside the guard
+// makes the compiler wait for it there, so each guarded load would cost a full memory round
+// trip; here rows past N are clamped to row N-1 (read, never written) and optional operands
+// are selected after an unconditional load.  Wave w (of BS/32) owns output channels
+// [32w, 32w+32) of the head: one 32x32 MFMA tile per gate, B fragments of all K steps in
+// 128 VGPRs.  Order of issue: conv window + x_t, gate weights, then (after the conv) h and y;
+// the conv waits only for the first group, the MFMAs for the second, the gate math for the third.
+template <int BS>
+__global__ void __launch_bounds__(2 * BS) decode_bf16_kernel(DecodeArgs a) {
+    constexpr int kThreads = 2 * BS;
+    constexpr int kChunks = BS / 8;              // 8-channel chunks of the head
+    constexpr int kGroups = kThreads / kChunks;  // 16 sequence groups
+    constexpr int kPer = 32 / kGroups;           // sequences per conv thread (2)
+    constexpr int kRow = BS + 8;
+    constexpr int kKSteps = BS / 16;
+    __shared__ __attribute__((aligned(16))) uint16_t u_lds[32 * kRow];
+
+    const int tid = threadIdx.x;
+    const int n0 = blockIdx.x * 32;
+    const int head = blockIdx.y;
+    const int N = a.N;
+    const size_t D = (size_t)a.D;
+    uint16_t* __restrict__ cs = static_cast<uint16_t*>(a.conv_state);
+    const uint16_t* __restrict__ xg = static_cast<const uint16_t*>(a.x);
+    const int wv = tid >> 6, lane = tid & 63, ln = lane & 31, kh = lane >> 5;
+
+    // ---- group 1: conv taps, bias, window and x_t of this thread's (sequence, chunk) pairs ----
+    const int cg = tid % kChunks, sg = tid / kChunks;
+    const size_t c0 = (size_t)head * BS + cg * 8;
+    const uint4* cwp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.conv_w) + c0 * 4);
+    const uint4 cw0 = cwp[0], cw1 = cwp[1], cw2 = cwp[2], cw3 = cwp[3];
+    const bool has_cb = a.conv_b != nullptr;
+    const uint4 cbv = *reinterpret_cast<const uint4*>(
+        has_cb ? static_cast<const uint16_t*>(a.conv_b) + c0 : static_cast<const uint16_t*>(a.conv_w) + c0 * 4);
+    uint4 s0[kPer], s1[kPer], s2[kPer], xt[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int n = min(n0 + sg * kPer + k, N - 1);
+        const uint16_t* row = cs + (size_t)n * 3 * D + c0;
+        s0[k] = *reinterpret_cast<const uint4*>(row);
+        s1[k] = *reinterpret_cast<const uint4*>(row + D);
+        s2[k] = *reinterpret_cast<const uint4*>(row + 2 * D);
+        xt[k] = *reinterpret_cast<const uint4*>(xg + (size_t)n * a.ld_x + c0);
+    }
+    // ---- group 2: gate weights of this wave's 32 output channels, all K steps, both gates ----
+    const int ncol = 32 * wv + ln;
+    const size_t chn = (size_t)head * BS + ncol;
+    bf16x8 wA[kKSteps], wX[kKSteps];
+    {
+        const uint16_t* war = static_cast<const uint16_t*>(a.wa) + chn * BS;
+        const uint16_t* wxr = static_cast<const uint16_t*>(a.wx) + chn * BS;
+#pragma unroll
+        for (int kk = 0; kk < kKSteps; ++kk) {
+            const int kb = 64 * (kk >> 2) + 32 * kh + 8 * (kk & 3);
+            wA[kk] = *reinterpret_cast<const bf16x8*>(war + kb);
+            wX[kk] = *reinterpret_cast<const bf16x8*>(wxr + kb);
+        }
+    }
+    // ---- conv over [window, x_t]; shift the window in place (rows n < N only) ----
+    {
+        float w[4][8], cb[8];
+        const uint32_t* q[4] = {&cw0.x, &cw1.x, &cw2.x, &cw3.x};
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                // taps of channel c0 + 2 qq + (e >> 2), tap e & 3
+                const uint32_t wd = q[qq][e >> 1];
+                w[e & 3][2 * qq + (e >> 2)] = (e & 1) ? bf_hi(wd) : bf_lo(wd);
+            }
+        const uint32_t* qb = &cbv.x;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cb[e] = has_cb ? ((e & 1) ? bf_hi(qb[e >> 1]) : bf_lo(qb[e >> 1])) : 0.0f;
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            const int m = sg * kPer + k;
+            const int n = n0 + m;
+            const uint32_t* q0 = &s0[k].x;
+            const uint32_t* q1 = &s1[k].x;
+            const uint32_t* q2 = &s2[k].x;
+            const uint32_t* q3 = &xt[k].x;
+            float u[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float v0 = (e & 1) ? bf_hi(q0[e >> 1]) : bf_lo(q0[e >> 1]);
+                const float v1 = (e & 1) ? bf_hi(q1[e >> 1]) : bf_lo(q1[e >> 1]);
+                const float v2 = (e & 1) ? bf_hi(q2[e >> 1]) : bf_lo(q2[e >> 1]);
+                const float v3 = (e & 1) ? bf_hi(q3[e >> 1]) : bf_lo(q3[e >> 1]);
+                float acc = __builtin_fmaf(w[0][e], v0, cb[e]);
+                acc = __builtin_fmaf(w[1][e], v1, acc);
+                acc = __builtin_fmaf(w[2][e], v2, acc);
+                u[e] = __builtin_fmaf(w[3][e], v3, acc);
+            }
+            *reinterpret_cast<uint4*>(u_lds + m * kRow + cg * 8) =
+                make_uint4(pack2bf(u[0], u[1]), pack2bf(u[2], u[3]), pack2bf(u[4], u[5]), pack2bf(u[6], u[7]));
+            if (n < N) {
+                uint16_t* row = cs + (size_t)n * 3 * D + c0;
+                *reinterpret_cast<uint4*>(row) = s1[k];
+                *reinterpret_cast<uint4*>(row + D) = s2[k];
+                *reinterpret_cast<uint4*>(row + 2 * D) = xt[k];
+            }
+        }
+    }
+    // ---- group 3 (issued once the conv registers are free; in flight during the MFMAs):
+    // h, y of this lane's 16 (sequence, channel) elements and the gate constants ----
+    float hv[16];
+    uint16_t yv[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int n = min(n0 + mfma_d_row(lane, j), N - 1);
+        hv[j] = a.h[(size_t)n * D + chn];
+        yv[j] = static_cast<const uint16_t*>(a.y)[(size_t)n * a.ld_y + chn];
+    }
+    const float lam = a.lambda[chn];
+    const uint16_t* bap = static_cast<const uint16_t*>(a.ba);
+    const uint16_t* bxp = static_cast<const uint16_t*>(a.bx);
+    const uint16_t bav = (bap ? bap : static_cast<const uint16_t*>(a.wa))[bap ? chn : 0];
+    const uint16_t bxv = (bxp ? bxp : static_cast<const uint16_t*>(a.wx))[bxp ? chn : 0];
+
+    __syncthreads();
+
+    // ---- gate pre-activations of the 32 sequences on MFMA ----
+    f32x16 accA, accX;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) { accA[e] = 0.0f; accX[e] = 0.0f; }
+#pragma unroll
+    for (int kk = 0; kk < kKSteps; ++kk) {
+        const int kb = 64 * (kk >> 2) + 32 * kh + 8 * (kk & 3);
+        const bf16x8 A = *reinterpret_cast<const bf16x8*>(u_lds + ln * kRow + kb);
+        accA = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, wA[kk], accA, 0, 0, 0);
+        accX = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, wX[kk], accX, 0, 0, 0);
+    }
+
+    // ---- gates, state update, output ----
+    const float nba = bap ? -bf2f(bav) * kLog2e : 0.0f;
+    const float nbx = bxp ? -bf2f(bxv) * kLog2e : 0.0f;
+    const float kc = -8.0f * softplus_neg(lam) * kLog2e;
+    uint16_t* __restrict__ out = static_cast<uint16_t*>(a.out);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int m = mfma_d_row(lane, j);
+        const int n = n0 + m;
+        const float u = bf2f(u_lds[m * kRow + ncol]);
+        const GateOut g = gate_fast(accA[j], accX[j], nba, nbx, kc, u);
+        const float hn = __builtin_fmaf(g.a, hv[j], g.v);
+        const float o = hn * gelu_fast(bf2f(yv[j]));
+        if (n < N) {
+            a.h[(size_t)n * D + chn] = hn;
+            out[(size_t)n * a.ld_out + chn] = f2bf(o);
+        }
+    }
+}
+
 // conv outputs for a block of 16 tokens of one (sequence, 8-channel chunk); reads the old window
 template <typename ST>
 __global__ void conv_out_kernel(ConvArgs a) {
@@ -246,8 +400,8 @@ __global__ void conv_state_kernel(ConvArgs a) {
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int bs, hipStream_t s) {
     const dim3 grid((a.N + 31) / 32, a.H);
     if (dtype == 1) {
-        if (bs == 256) hipLaunchKernelGGL((decode_kernel<256, uint16_t>), grid, dim3(512), 0, s, a);
-        else hipLaunchKernelGGL((decode_kernel<128, uint16_t>), grid, dim3(256), 0, s, a);
+        if (bs == 256) hipLaunchKernelGGL((decode_bf16_kernel<256>), grid, dim3(512), 0, s, a);
+        else hipLaunchKernelGGL((decode_bf16_kernel<128>), grid, dim3(256), 0, s, a);
     } else {
         if (bs == 256) hipLaunchKernelGGL((decode_kernel<256, float>), grid, dim3(512), 0, s, a);
         else hipLaunchKernelGGL((decode_kernel<128, float>), grid, dim3(256), 0, s, a);

@@ -175,6 +175,42 @@ def test_decode_fp32_against_oracle():
     np.testing.assert_array_equal(H.to_host(cs).astype(np.float64), rc)
 
 
+@pytest.mark.parametrize("D,nh,N", [(512, 2, 45), (384, 3, 33), (2560, 10, 70), (256, 1, 1)])
+def test_decode_bf16_ragged_against_oracle(D, nh, N):
+    """bf16 decode with biases, a carried state and N not a multiple of the 32-sequence tile,
+    for both gate block sizes (256 and 128): every element against the oracle, the conv window
+    bit-exact, and canary bands around h, the conv window and the outputs untouched."""
+    from gated_linear_recurrence_amd import binding
+    T = 12
+    w = synth.Workload("dec-ragged", N, T, D, nh, synth.BF16, 0.9, 0.999, 0.0, 21)
+    p = synth.make_params(w, biases=True)
+    x, y = synth.make_act(w, "x"), synth.make_act(w, "y")
+    P = H.dev_params(p, w.H)
+    xd, yd = H.to_dev(x), H.to_dev(y)
+    h0 = np.random.default_rng(5).normal(0, 0.5, (N, D)).astype(np.float32)
+    c0 = synth.make_conv0(w, N)
+    pad = 4096
+    hb = torch.full((N * D + 2 * pad,), float("nan"), device="cuda")
+    cb = torch.full((3 * N * D + 2 * pad,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ob = torch.full((N * T * D + 2 * pad,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    h = hb[pad:pad + N * D].view(N, D)
+    cs = cb[pad:pad + 3 * N * D].view(N, 3, D)
+    outs = ob[pad:pad + N * T * D].view(N, T, D)
+    h.copy_(H.to_dev(h0))
+    cs.copy_(H.to_dev(c0))
+    for t in range(T):
+        binding.rglru_decode_step(P, xd[:, t], yd[:, t], h, cs, out_t=outs[:, t])
+    torch.cuda.synchronize()
+    ro, rh, rc = H.oracle.prefill(H.oracle_params(p, w.H), x, y, h0=h0, conv0=c0)
+    e_out = H.rel_l2(outs.float().cpu().numpy(), ro)
+    e_h = H.rel_l2(h.cpu().numpy().astype(np.float64), rh)
+    print("decode bf16 D=%d H=%d N=%d rel-L2 out %.3e h %.3e" % (D, nh, N, e_out, e_h))
+    assert e_out <= H.TOL[synth.BF16] and e_h <= H.TOL[synth.BF16]
+    np.testing.assert_array_equal(H.wide(H.to_host(cs)), rc)
+    for t_, m in ((hb, N * D), (cb, 3 * N * D), (ob, N * T * D)):
+        assert torch.isnan(t_[:pad].float()).all() and torch.isnan(t_[pad + m:].float()).all()
+
+
 # ------------------------------------------------------------------------------------------
 # conv-state update
 # ------------------------------------------------------------------------------------------
