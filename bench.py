@@ -12,6 +12,8 @@ sample, the 2B single-sequence prefill and the decode step time (256 sequences, 
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import os
 import sys
@@ -26,6 +28,13 @@ from gated_linear_recurrence_amd import synth  # noqa: E402
 
 METRIC = "RG-LRU prefill tokens·channels/s + decode step µs; % of MI355X HBM peak"
 HBM_PEAK_GBS = 8000.0
+PREFILL_KERNEL = "prefill_bf16_kernel<256>"
+# sources that define the measured prefill kernel; counter summaries name their hash
+KERNEL_SOURCES = ["gated_linear_recurrence_amd/csrc/rglru_prefill.hip",
+                  "gated_linear_recurrence_amd/csrc/rglru_device.h",
+                  "gated_linear_recurrence_amd/csrc/rglru_internal.h",
+                  "gated_linear_recurrence_amd/build.py"]
+COUNTERS_JSON = os.path.join(ROOT, "profiles", "prefill_bf16_kernel-2b-batched-counters.json")
 
 
 def algorithmic_bytes(w: synth.Workload, B: int, T: int, state: bool = True) -> int:
@@ -131,25 +140,23 @@ def time_decode(w, N, steps, torch, binding):
 
 
 def cpu_baseline(w):
-    """The oracle on a bounded sample of the workload: all heads of the 8 sequences over the
-    first 2048 tokens (one OpenMP thread per (sequence, head) unit)."""
+    """The oracle on the whole headline workload (all 8 sequences x 8192 tokens x 10 heads),
+    one OpenMP thread per (sequence, head) unit; inputs are generated before the clock starts."""
     import oracle
-    B, T = w.B, min(w.T, 2048)
-    wb = synth.small(w, B=B, T=T)
+    x = synth.make_act(w, "x")
+    y = synth.make_act(w, "y")
+    h0 = synth.make_h0(w)
     p = synth.make_params(w)
-    x = synth.make_act(wb, "x")
-    y = synth.make_act(wb, "y")
-    h0 = synth.make_h0(wb)
     P = oracle.Params(p["conv_w"], p["conv_b"], p["wa"], p["ba"], p["wx"], p["bx"], p["lambda"], w.H)
     lib = oracle.load()
-    threads = min(lib.oracle_max_threads(), B * w.H)
+    threads = min(lib.oracle_max_threads(), w.B * w.H)
     t = time.perf_counter()
     oracle.prefill(P, x, y, h0=h0, nthreads=threads, lib=lib)
     dt = time.perf_counter() - t
-    return {"value": B * T * w.D / dt, "unit": "tokens·channels/s", "cores": threads,
+    return {"value": w.B * w.T * w.D / dt, "unit": "tokens·channels/s", "cores": threads,
             "kind": "oracle", "seconds": round(dt, 3),
-            "sample": "B=%d sequences x T=%d tokens x D=%d (all %d heads), fp64 sequential "
-                      "oracle, OpenMP over (sequence, head) units" % (B, T, w.D, w.H)}
+            "sample": "the whole workload: B=%d x T=%d x D=%d (all %d heads), fp64 sequential "
+                      "oracle, OpenMP over (sequence, head) units" % (w.B, w.T, w.D, w.H)}
 
 
 def copy_probe(torch, nbytes: int = 1 << 30, reps: int = 5):
@@ -169,6 +176,95 @@ def copy_probe(torch, nbytes: int = 1 << 30, reps: int = 5):
                       "GBs_read_plus_write": 2 * nbytes / (ms * 1e-3) / 1e9}), flush=True)
 
 
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read() + b"\0")
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the prefill kernel from the committed counter summary, or None
+    when the summary is missing or was taken on other kernel sources."""
+    try:
+        with open(COUNTERS_JSON) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return c.get("traffic_bytes_per_launch")
+
+
+def _rows(path):
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _mean_counter(path, name_part, counter, min_value=0.0):
+    vals = [float(r["Counter_Value"]) for r in _rows(path)
+            if name_part in r["Kernel_Name"] and r["Counter_Name"] == counter
+            and float(r["Counter_Value"]) >= min_value]
+    if not vals:
+        raise SystemExit("no %s rows for %r in %s" % (counter, name_part, path))
+    return sum(vals) / len(vals), len(vals)
+
+
+def counter_summary(args):
+    """Turn rocprofv3 CSV output into the committed summaries under profiles/."""
+    kt = _rows(args.kernel_stats)
+    pre = [r for r in kt if "prefill_bf16_kernel" in r["Name"]]
+    if not pre:
+        raise SystemExit("prefill_bf16_kernel not in %s" % args.kernel_stats)
+    r = pre[0]
+    f_kib, nf = _mean_counter(args.fetch, "prefill_bf16_kernel", "FETCH_SIZE")
+    w_kib, nw = _mean_counter(args.write, "prefill_bf16_kernel", "WRITE_SIZE")
+    # calibration: a plain copy of 1 GiB reads and writes 1 GiB per dispatch
+    cf_kib, _ = _mean_counter(args.copy_fetch, "copyBuffer", "FETCH_SIZE", 1e5)
+    cw_kib, _ = _mean_counter(args.copy_write, "copyBuffer", "WRITE_SIZE", 1e5)
+    gib_kib = float(1 << 20)
+    fs, ws = gib_kib / cf_kib, gib_kib / cw_kib
+    traffic = (f_kib * fs + w_kib * ws) * 1024.0
+    w = synth.WORKLOADS[synth.BATCHED_2B]
+    alg = algorithmic_bytes(w, w.B, w.T)
+    out = {
+        "kernel": PREFILL_KERNEL, "workload": w.name,
+        "kernel_source_hash": kernel_source_hash(),
+        "avg_duration_ns": float(r["AverageNs"]), "calls": int(r["Calls"]),
+        "fetch_kib_per_dispatch": f_kib, "write_kib_per_dispatch": w_kib,
+        "fetch_dispatches": nf, "write_dispatches": nw,
+        "copy_probe_fetch_kib_per_gib": cf_kib, "copy_probe_write_kib_per_gib": cw_kib,
+        "fetch_scale": fs, "write_scale": ws,
+        "traffic_bytes_per_launch": traffic, "algorithmic_bytes_per_launch": alg,
+        "traffic_over_algorithmic": traffic / alg,
+        "commands": args.commands,
+    }
+    with open(COUNTERS_JSON, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    txt = os.path.join(ROOT, "profiles", "prefill_bf16_kernel-2b-batched-kernel-trace.txt")
+    with open(txt, "w") as f:
+        f.write("rocprofv3 kernel statistics, prefill on 2b-batched-B8-T8192-D2560-H10 (bf16)\n")
+        f.write("kernel source hash %s\n\n" % out["kernel_source_hash"])
+        f.write("commands (from the repository root):\n")
+        for c in args.commands:
+            f.write("  %s\n" % c)
+        f.write("\n%-60s %6s %14s %14s %14s\n" % ("kernel", "calls", "avg ns", "min ns", "max ns"))
+        for row in kt:
+            f.write("%-60s %6s %14.0f %14.0f %14.0f\n" % (row["Name"][:60], row["Calls"],
+                    float(row["AverageNs"]), float(row["MinNs"]), float(row["MaxNs"])))
+        f.write("\nprefill_bf16_kernel per dispatch: FETCH_SIZE %.0f KiB (x%.3f), WRITE_SIZE %.0f KiB "
+                "(x%.3f)\n" % (f_kib, fs, w_kib, ws))
+        f.write("calibration (plain 1 GiB copy): FETCH_SIZE %.0f KiB, WRITE_SIZE %.0f KiB per GiB\n"
+                % (cf_kib, cw_kib))
+        f.write("HBM traffic per launch %.0f B = %.3f x algorithmic %d B\n"
+                % (traffic, traffic / alg, alg))
+        f.write("algorithmic GB/s at the profiled average duration: %.1f\n"
+                % (alg / (float(r["AverageNs"]) * 1e-9) / 1e9))
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -178,7 +274,18 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="prefill headline only")
     ap.add_argument("--copy-probe", action="store_true",
                     help="time a plain 1 GiB device-to-device copy instead (counter calibration)")
+    ap.add_argument("--counter-summary", action="store_true",
+                    help="write profiles/ summaries from rocprofv3 CSV output (no GPU)")
+    ap.add_argument("--kernel-stats")
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    ap.add_argument("--copy-fetch")
+    ap.add_argument("--copy-write")
+    ap.add_argument("--commands", nargs="*", default=[])
     args = ap.parse_args()
+    if args.counter_summary:
+        counter_summary(args)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d "
               "requested)" % args.gpus, file=sys.stderr)
@@ -203,8 +310,8 @@ def main():
         "config": {"workload": w.name, "B": w.B, "T": w.T, "D": w.D, "gate_heads": w.H,
                    "block": w.bs, "state": "fp32", "h0_std": w.h0_std},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "prefill_kernel<256, bf16>", "algorithmic_bytes": nbytes},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
+                     "kernel": PREFILL_KERNEL, "algorithmic_bytes": nbytes},
     }
     if not args.no_extras:
         w2 = synth.WORKLOADS[synth.PREFILL_2B]
