@@ -13,7 +13,8 @@ constexpr size_t kWsHeader = 4096;    // workspace header bytes (counters and er
 constexpr int kErrWord = 0;
 constexpr int kDoneWord = 1;
 constexpr int kTicketWord = 16;
-constexpr int kMaxHeads = 2048 / 4 - kTicketWord;  // header bytes 2048.. hold a zero block
+constexpr size_t kZeroBlock = 2048;  // header bytes [2048, 4096) stay zero: a zero source for copies
+constexpr int kMaxHeads = (int)(kZeroBlock / 4) - kTicketWord;
 
 struct PrefillArgs {
     const void* x;

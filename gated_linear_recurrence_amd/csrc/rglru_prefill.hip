@@ -53,7 +53,9 @@ __device__ __forceinline__ void st_word(unsigned long long* p, unsigned long lon
 // window is read before this segment's aggregate is published so that waiting for the reads
 // never waits for that store.
 __device__ float look_back(unsigned long long* wself, size_t wstride, int seg, unsigned long long w1,
-                           float A_seg, float B_seg, bool publish_aggregate, unsigned* header) {
+                           float A_seg, float B_seg, bool publish_aggregate, unsigned* header,
+                           bool& pred_inclusive) {
+    pred_inclusive = true;
     if (w_ready(w1) && w_inclusive(w1)) return w_B(w1);
     const int n = seg < kWindow ? seg : kWindow;
     bool published = !publish_aggregate;
@@ -83,6 +85,7 @@ __device__ float look_back(unsigned long long* wself, size_t wstride, int seg, u
                 if (k == kinc) c = w_B(win[k]);
                 else if (k < kinc) c = __builtin_fmaf(w_A(win[k]), c, w_B(win[k]));
             }
+            pred_inclusive = (kinc == 0);
             return c;
         }
         if (it >= kSpinLimit) {
@@ -91,6 +94,26 @@ __device__ float look_back(unsigned long long* wself, size_t wstride, int seg, u
         }
         __builtin_amdgcn_s_sleep(1);
     }
+}
+
+// Reset the predecessor's word for the next launch.  Only once its inclusive value has been
+// seen: a carry folded from its aggregate may have been found before the predecessor's own
+// inclusive store, and a reset issued earlier could land before that store and leave a stale
+// word behind.  The predecessor has started (ticket order) and finishes its look-back without
+// waiting on this unit, so the wait ends.
+__device__ void retire_word(unsigned long long* wprev, bool seen_inclusive, unsigned* header) {
+    if (!seen_inclusive) {
+        for (unsigned it = 0;; ++it) {
+            const unsigned long long w = ld_word(wprev);
+            if (w_ready(w) && w_inclusive(w)) break;
+            if (it >= kSpinLimit) {
+                atomicOr(&header[kErrWord], 2u);
+                return;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+    }
+    st_word(wprev, kNotReady);
 }
 
 // LDS row of token t (0..63): tokens 32..63 have row bits 2..3 flipped so that the MFMA
@@ -339,14 +362,15 @@ __global__ void __launch_bounds__(2 * BS) prefill_kernel(PrefillArgs a) {
         const size_t wstride = (size_t)a.B * D;
         unsigned long long* wself = a.words + (size_t)seg * wstride + (size_t)b * D + ch;
         if (hh == 0) {
+            bool pred_inc = true;
             if (seg == 0) {
                 carry = a.h0 ? a.h0[(size_t)b * D + ch] : 0.0f;
             } else {
                 carry = look_back(wself, wstride, seg, ld_word(wself - wstride), A_seg, B_seg, !last,
-                                  a.header);
+                                  a.header, pred_inc);
             }
             if (!last) st_word(wself, make_word(A_seg, __builtin_fmaf(A_seg, carry, B_seg), true));
-            if (seg > 0) st_word(wself - wstride, kNotReady);  // retire the predecessor's word
+            if (seg > 0) retire_word(wself - wstride, pred_inc, a.header);
         }
     }
     carry = __shfl(carry, ln);
@@ -397,20 +421,22 @@ __global__ void __launch_bounds__(2 * BS) prefill_kernel(PrefillArgs a) {
 // ---------------------------------------------------------------------------------------
 // bf16 storage, persistent kernel (the measured path).
 //
-// One workgroup per CU, pinned to one gate head for its lifetime: each wave keeps the B
-// fragments of its 32 output channels of both gate blocks in VGPRs (128 registers), so the
-// gate weights are read once per workgroup instead of once per segment.  The workgroup walks
-// the head's segments in ticket order (segment-major over the batch) and pipelines them:
-//   iteration k:  [conv k: x_k (LDS) -> u (LDS)] [store out_{k-1}] [DMA x_{k+1}, y_{k+1}]
-//                 [MFMA k] [gate math + scan k] [carry k] [GELU merge k -> registers]
-// x and y reach LDS by direct global->LDS loads (global_load_lds_dwordx4) one segment ahead;
-// the outputs of segment k are stored during iteration k+1, after its conv, so no wait on
-// the memory counter ever waits for freshly issued stores.
+// One workgroup per CU, pinned to one gate head for its lifetime: wave w keeps the MFMA B
+// fragments of output channels [32w, 32w+32) of both gate blocks in VGPRs (128 registers), so
+// the gate weights are read once per workgroup.  The workgroup walks the head's segments in
+// ticket order (segment-major over the batch), one segment ahead in the conv:
+//   iteration k: [MFMA tile 0 of segment k  | conv of segment k+1 -> u[(k+1)&1]]
+//                copies: x of segment k+2, y of segment k
+//                [MFMA tile 1 of segment k  | gate math + scan of tile 0] [gate math tile 1]
+//                wait for the copies; [carry probe | GELU merge] [look-back, publish]
+//                [fix-up -> LDS -> 16-byte stores] barrier
+// Every wave copies (global -> LDS, no VGPRs) exactly the x rows its conv lanes read and the y
+// rows its output lanes read, into regions of its own, so readiness is a wave-local wait and
+// the barrier only orders u (written by all waves, double-buffered).  Rows before token 0
+// come from the carried conv window (or a zero block) by the same copies.
 // Placement: the hardware deals workgroups to the 8 XCDs round-robin; consecutive slots of
 // one XCD are given to one head, so each XCD's L2 serves few heads.
 // ---------------------------------------------------------------------------------------
-typedef unsigned short ushort2v __attribute__((ext_vector_type(2)));
-
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0xffffffff, 0x00020000);
 }
@@ -421,50 +447,86 @@ __device__ __forceinline__ float dot2bf(uint32_t w, uint32_t x, float c) {
 }
 
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
+__device__ __forceinline__ void wait_lds_all() { __builtin_amdgcn_s_waitcnt(0xc07f); }   // lgkmcnt(0)
 
-#ifndef RGLRU_NT256
-#define RGLRU_NT256 1
-#endif
-constexpr int kSchedGroup = 4;  // elements the scheduler may interleave (bounds register use)
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() would also wait for every
+// outstanding global->LDS copy (its fence must cover their LDS writes); here each wave waits for
+// its own copies where it reads them, so the barrier only needs this wave's LDS accesses done.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <int BS>
 struct PCfg {
-    static constexpr int kNT = BS == 256 ? RGLRU_NT256 : 1;  // 32-channel MFMA tiles per wave
-    static constexpr int kWaves = BS / (32 * kNT);      // 4 waves: one per SIMD
+    static constexpr int kWaves = BS / 32;          // wave w: output channels 32w .. 32w+31
     static constexpr int kThreads = 64 * kWaves;
-    static constexpr int kRow = BS + 8;                 // ubuf row stride (bf16 elements)
-    static constexpr int kRowB = BS * 2;                // bytes of one head's slice of a token row
-    static constexpr int kHalo = 16;                    // xbuf rows before the segment
-    static constexpr int kXRows = kSeg + kHalo;         // tokens t0-16 .. t0+63
-    static constexpr int kRowsPerInst = 1024 / kRowB;   // one DMA instruction moves 1 KB
-    static constexpr int kLanesPerRow = kRowB / 16;
-    static constexpr int kXInst = kXRows / kRowsPerInst / kWaves;
-    static constexpr int kYInst = kSeg / kRowsPerInst / kWaves;
-    static constexpr int kPairs = BS / 2;               // conv: channel pairs ...
-    static constexpr int kTokGroups = kThreads / kPairs;  // ... x token groups
-    static constexpr int kTok = kSeg / kTokGroups;
+    static constexpr int kRow = BS + 8;             // u row stride (bf16 elements)
     static constexpr int kKSteps = BS / 16;
-    static_assert(kXInst * kRowsPerInst * kWaves == kXRows, "x DMA tiling");
-    static_assert(kYInst * kRowsPerInst * kWaves == kSeg, "y DMA tiling");
-    static_assert(kTokGroups * kTok == kSeg, "conv tiling");
+    // conv tile of a wave: 64 channel pairs (128 channels) x 16 tokens
+    static constexpr int kPairWaves = BS / 128;     // waves per token group
+    static constexpr int kTokGroups = kWaves / kPairWaves;
+    static constexpr int kTok = kSeg / kTokGroups;
+    static constexpr int kXRows = 20;               // tokens 16 tg - 3 .. 16 tg + 16 (one spare)
+    static constexpr int kXElems = kXRows * 128;
+    // y / output staging region of a wave: 64 rows x 32 channels; rows 32..63 start 64 bytes
+    // later so that the two half-waves' 2-byte accesses fall in different banks
+    static constexpr int kYElems = kSeg * 32 + 32;
+    static_assert(kTok == 16 && kKSteps * 16 == BS, "tiling");
 };
 
-// Direct global->LDS copy of one segment's rows of one head: LDS row r receives token
-// t0 + first + r of the ticket's sequence, clamped to [0, T-1]; a ticket past the end copies
-// the last segment again (harmless).
-template <int BS, int kInst>
-__device__ __forceinline__ void dma_rows(const char* head_base, unsigned tk, unsigned n_tk, int B,
-                                         int T, int rowb, int first, int wv, int dma_r,
-                                         uint16_t* lds) {
-    using C = PCfg<BS>;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int yrow(int r) { return r * 32 + ((r >> 5) << 5); }
+
+// Global -> LDS copies of one wave (buffer loads with the LDS bit: SGPR base, 32-bit lane
+// offsets, no VGPR data).  x: rows t0 + 16 tg - 3 + r (r = 0..19) of the wave's 128 channels
+// (16 lanes per 256-byte row, 4 rows per instruction); rows past T-1 repeat row T-1 (never
+// used); for segment 0 the rows before token 0 come from the conv window, read through a
+// resource of length 0 when there is none (out-of-range buffer reads return zeros).  A ticket
+// past the end copies the last ticket's rows again (harmless, never used).
+__device__ __forceinline__ void dma_x_rows(const PrefillArgs& a, int head, int bs, int pw, int tg,
+                                           unsigned tk, unsigned n_tk, int lane, uint16_t* dst) {
     tk = min(tk, n_tk - 1);
-    const int t0 = (int)(tk / (unsigned)B) * kSeg;
-    const char* base = head_base + (size_t)(tk % (unsigned)B) * T * rowb;
+    const int seg = (int)(tk / (unsigned)a.B), b = (int)(tk % (unsigned)a.B);
+    const int rowb = a.D * 2;
+    const int coff = (head * bs + 128 * pw + 8 * (lane & 15)) * 2;
+    const __amdgpu_buffer_rsrc_t rx =
+        make_rsrc(static_cast<const uint16_t*>(a.x) + (size_t)b * a.T * a.D);
+    const int tok0 = seg * kSeg + 16 * tg - 3 + (lane >> 4);
+    if (seg == 0 && tg == 0) {
+        // rows 0..2 of the first instruction are tokens -3..-1 (the resource is formed before the
+        // lane-divergent choice, from a pointer made visibly wave-uniform)
+        // (readfirstlane yields a signed int: both halves are widened as unsigned)
+        const uint64_t cp = reinterpret_cast<uint64_t>(a.conv0 ? a.conv0 : a.x);
+        const uint32_t c_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(cp >> 32));
+        const uint32_t c_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)cp);
+        const uint64_t cpu = ((uint64_t)c_hi << 32) | (uint64_t)c_lo;
+        const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+            reinterpret_cast<void*>(cpu), 0, a.conv0 ? 0xffffffffu : 0u, 0x00020000);
+        const bool from_x = (lane >> 4) == 3;
+        if (from_x) __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, dst, 16, coff, 0, 0, 0);
+        else __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, dst, 16, (((b * 3 + (lane >> 4)) * a.D) * 2) + coff, 0, 0, 0);
+    } else {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, dst, 16, min(tok0, a.T - 1) * rowb + coff, 0, 0, 0);
+    }
 #pragma unroll
-    for (int q = 0; q < kInst; ++q) {
-        const int inst = wv * kInst + q;
-        const int tr = min(max(t0 + first + inst * C::kRowsPerInst + dma_r, 0), T - 1);
-        __builtin_amdgcn_global_load_lds(base + (size_t)tr * rowb, lds + inst * 512, 16, 0, 0);
+    for (int q = 1; q < 5; ++q) {
+        const int tok = min(tok0 + 4 * q, a.T - 1);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, dst + q * 512, 16, tok * rowb + coff, 0, 0, 0);
+    }
+}
+
+// y: rows t0 .. t0+63 (clamped to T-1) of the wave's 32 channels (4 lanes per 64-byte row).
+__device__ __forceinline__ void dma_y_rows(const PrefillArgs& a, int head, int bs, int cw0,
+                                           unsigned tk, unsigned n_tk, int lane, uint16_t* dst) {
+    tk = min(tk, n_tk - 1);
+    const int seg = (int)(tk / (unsigned)a.B), b = (int)(tk % (unsigned)a.B);
+    const int rowb = a.D * 2;
+    const int coff = (head * bs + cw0 + 8 * (lane & 3)) * 2;
+    const __amdgpu_buffer_rsrc_t ry =
+        make_rsrc(static_cast<const uint16_t*>(a.y) + (size_t)b * a.T * a.D);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int tok = min(seg * kSeg + 16 * q + (lane >> 2), a.T - 1);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, dst + yrow(16 * q), 16, tok * rowb + coff, 0, 0, 0);
     }
 }
 
@@ -476,19 +538,32 @@ __device__ __forceinline__ int opaque(int v) {
     return v;
 }
 
+// The same for a wave-uniform value (kept in an SGPR).
+__device__ __forceinline__ int sopaque(int v) {
+    asm volatile("" : "+s"(v));
+    return v;
+}
+
 template <int BS>
 __global__ void __launch_bounds__(PCfg<BS>::kThreads)
 prefill_bf16_kernel(PrefillArgs a) {
     using C = PCfg<BS>;
-    constexpr int kNT = C::kNT;
     constexpr int kRow = C::kRow;
-    __shared__ __attribute__((aligned(16))) uint16_t xbuf[C::kXRows * BS];
-    __shared__ __attribute__((aligned(16))) uint16_t ybuf[2][kSeg * BS];
-    __shared__ __attribute__((aligned(16))) uint16_t ubuf[kSeg * kRow];
+    constexpr int kU = kSeg * kRow;  // elements of one u tile
+    // LDS.  In the loop every access is "flat array + one index formed once per iteration
+    // (opaque to the optimizer) + constants": the compiler then knows which array each access
+    // touches, and an LDS read never waits for a global->LDS copy into another array.  (Left to
+    // itself it splits addresses into long pointer chains and loses that knowledge, and then
+    // every LDS read waits for all copies in flight.)
+    __shared__ __attribute__((aligned(16))) uint16_t u_lds[2 * kU];                    // u tiles
+    __shared__ __attribute__((aligned(16))) uint16_t x_lds[C::kWaves * C::kXElems];    // x rows
+    __shared__ __attribute__((aligned(16))) uint16_t y_lds[C::kWaves * C::kYElems];    // y rows / out
     __shared__ __attribute__((aligned(16))) uint4 conv_tab[BS / 2];   // taps of a channel pair
     __shared__ __attribute__((aligned(8))) float2 convb_tab[BS / 2];  // biases of a channel pair
     __shared__ __attribute__((aligned(16))) float4 gate_tab[BS];      // (nba, nbx, kc, 0) per channel
-    __shared__ unsigned s_tk[2];
+    __shared__ unsigned s_tk[4];
+    const uint32_t* const x_lds32 = reinterpret_cast<const uint32_t*>(x_lds);
+    uint32_t* const u_lds32 = reinterpret_cast<uint32_t*>(u_lds);
 
     const int tid0 = threadIdx.x;
     const int wv = __builtin_amdgcn_readfirstlane(tid0 >> 6);
@@ -500,12 +575,16 @@ prefill_bf16_kernel(PrefillArgs a) {
     const unsigned G = gridDim.x, bid = blockIdx.x;
     const unsigned xcd = bid & 7u, jx = bid >> 3, per = G >> 3, rem = G & 7u;
     const unsigned slot = xcd * per + min(xcd, rem) + jx;
-    const int head = (int)(slot / (unsigned)a.wph);
-    unsigned* tctr = a.header + kTicketWord + head;
+    const int head_ = (int)(slot / (unsigned)a.wph);
+    unsigned* tctr = a.header + kTicketWord + head_;
     const unsigned n_tk = (unsigned)(B * a.S);
 
-    const uint16_t* __restrict__ x = static_cast<const uint16_t*>(a.x);
-    const uint16_t* __restrict__ y = static_cast<const uint16_t*>(a.y);
+    const int pw = wv % C::kPairWaves, tg = wv / C::kPairWaves;  // conv tile
+    const int cw0_ = 32 * wv;                                      // output channels
+    const int xw0_ = wv * C::kXElems, yw0_ = wv * C::kYElems;      // the wave's LDS regions
+    const int head = head_, cw0 = cw0_, xw0 = xw0_, yw0 = yw0_;
+    // conv rows of this wave's tokens 16 tg + k: lds_row(16 tg + k) = 16 tg + (k ^ 12 sw)
+    const int csw = 12 * ((tg >> 1) & 1);
 
     // ---- per-workgroup tables: conv taps and biases, gate constants of the head's channels ----
     for (int i = tid0; i < BS / 2; i += C::kThreads) {
@@ -525,292 +604,261 @@ prefill_bf16_kernel(PrefillArgs a) {
         const float bix = a.bx ? bf2f(static_cast<const uint16_t*>(a.bx)[chn]) : 0.0f;
         gate_tab[i] = make_float4(-bia * kLog2e, -bix * kLog2e, -8.0f * sp * kLog2e, 0.0f);
     }
-    // gate weights of this wave's channels [cw0, cw0 + 32 kNT), held in registers throughout
-    const int cw0 = wv * 32 * kNT;
-    bf16x8 wA[kNT][C::kKSteps], wX[kNT][C::kKSteps];
+    // gate weights of this wave's channels, held in registers throughout
+    bf16x8 wA[C::kKSteps], wX[C::kKSteps];
     {
         const int lane = tid0 & 63, ln = lane & 31, kh = lane >> 5;
+        const size_t chn = (size_t)head * BS + cw0 + ln;
+        const uint16_t* war = static_cast<const uint16_t*>(a.wa) + chn * BS;
+        const uint16_t* wxr = static_cast<const uint16_t*>(a.wx) + chn * BS;
 #pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) {
-            const size_t chn = (size_t)head * BS + cw0 + 32 * nt + ln;
-            const uint16_t* war = static_cast<const uint16_t*>(a.wa) + chn * BS;
-            const uint16_t* wxr = static_cast<const uint16_t*>(a.wx) + chn * BS;
-#pragma unroll
-            for (int kk = 0; kk < C::kKSteps; ++kk) {
-                // K order: lane half kh supplies elements [64 q + 32 kh + 8 s, +8) at step 4q + s
-                const int kb = 64 * (kk >> 2) + 32 * kh + 8 * (kk & 3);
-                wA[nt][kk] = *reinterpret_cast<const bf16x8*>(war + kb);
-                wX[nt][kk] = *reinterpret_cast<const bf16x8*>(wxr + kb);
-            }
+        for (int kk = 0; kk < C::kKSteps; ++kk) {
+            // K order: lane half kh supplies elements [64 q + 32 kh + 8 s, +8) at step 4q + s
+            const int kb = 64 * (kk >> 2) + 32 * kh + 8 * (kk & 3);
+            wA[kk] = *reinterpret_cast<const bf16x8*>(war + kb);
+            wX[kk] = *reinterpret_cast<const bf16x8*>(wxr + kb);
         }
     }
-    const char* xseq = reinterpret_cast<const char*>(x + (size_t)head * BS);
-    const char* yseq = reinterpret_cast<const char*>(y + (size_t)head * BS);
 
-    // ---- prologue ----
+    // ---- prologue: tickets for this workgroup's first three segments; conv of the first ----
     if (tid0 == 0) {
         s_tk[0] = atomicAdd(tctr, 1u);
         s_tk[1] = atomicAdd(tctr, 1u);
+        s_tk[2] = atomicAdd(tctr, 1u);
     }
-    __syncthreads();
-    unsigned cur = s_tk[0], nxt = s_tk[1];
+    __syncthreads();  // tables and tickets
+    // tickets are workgroup-uniform: kept in SGPRs (buffer resources are built from them)
+    unsigned cur = __builtin_amdgcn_readfirstlane(s_tk[0]);
+    unsigned n1 = __builtin_amdgcn_readfirstlane(s_tk[1]);
+    unsigned n2 = __builtin_amdgcn_readfirstlane(s_tk[2]);
     {
         const int lane = tid0 & 63;
-        const char* xh = xseq + 16 * (lane % C::kLanesPerRow);
-        const char* yh = yseq + 16 * (lane % C::kLanesPerRow);
-        dma_rows<BS, C::kXInst>(xh, cur, n_tk, B, T, rowb, -C::kHalo, wv, lane / C::kLanesPerRow, xbuf);
-        dma_rows<BS, C::kYInst>(yh, cur, n_tk, B, T, rowb, 0, wv, lane / C::kLanesPerRow, ybuf[0]);
+        dma_x_rows(a, head, BS, pw, tg, cur, n_tk, lane, x_lds + xw0);
+        wait_vmem_all();
+        const int cp = 64 * pw + lane;
+        const uint4 wq = conv_tab[cp];
+        const float2 cb = convb_tab[cp];
+#pragma unroll
+        for (int k = 0; k < C::kTok; ++k) {
+            const uint32_t* xw = x_lds32 + xw0 / 2 + lane;
+            const uint32_t x0 = xw[k * 64], x1 = xw[(k + 1) * 64], x2 = xw[(k + 2) * 64], x3 = xw[(k + 3) * 64];
+            const float u0 = dot2bf(wq.y, __builtin_amdgcn_perm(x3, x2, 0x05040100u),
+                                    dot2bf(wq.x, __builtin_amdgcn_perm(x1, x0, 0x05040100u), cb.x));
+            const float u1 = dot2bf(wq.w, __builtin_amdgcn_perm(x3, x2, 0x07060302u),
+                                    dot2bf(wq.z, __builtin_amdgcn_perm(x1, x0, 0x07060302u), cb.y));
+            u_lds32[(lds_row(tg * C::kTok + k) * kRow) / 2 + cp] = pack2bf(u0, u1);
+        }
+        wait_lds_all();
+        dma_x_rows(a, head, BS, pw, tg, n1, n_tk, lane, x_lds + xw0);
     }
+    unsigned pending = 0;  // taken once per iteration, published at the iteration's barrier
     wait_vmem_all();
+    lds_barrier();  // u of the first segment complete; every wave has read the ticket slots
     unsigned it = 0;
 
     while (cur < n_tk) {
+        // per-iteration copies of workgroup constants: values derived from them are formed
+        // here with scalar ops instead of being hoisted (and spilled) across the loop
+        const int xw0 = sopaque(xw0_), yw0 = sopaque(yw0_), cw0 = sopaque(cw0_), head = sopaque(head_);
         const int tid = opaque(tid0);
         const int lane = tid & 63, ln = lane & 31, kh = lane >> 5, hh = lane >> 5;
         const int seg = (int)(cur / (unsigned)B), b = (int)(cur % (unsigned)B);
         const int t0 = seg * kSeg;
         const int nt_tok = min(kSeg, T - t0);
         const bool last = (seg == a.S - 1);
-        const uint16_t* ycur = ybuf[it & 1];
+        const int ucur = sopaque((int)(it & 1) * kU), unxt = kU - ucur;  // u tiles of cur, n1
+        const int atok = 32 * ((ln >> 2) & 1) + 4 * (ln >> 3) + (ln & 3);
 
-        // x and y of `cur` have landed: each wave waited for its own DMA (prologue or the
-        // previous iteration); the barrier covers every wave
-        __syncthreads();
-        if (it > 0) nxt = s_tk[0];  // grabbed during the previous iteration, published before the barrier
-        if (seg == 0) {
-            // tokens -3..-1 come from the carried conv state (or are zero), not from x
-            constexpr int kCh = BS / 8;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (tid < 3 * kCh && a.conv0 != nullptr)
-                v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.conv0) +
-                                                    ((size_t)b * 3 + tid / kCh) * D + (size_t)head * BS + (tid % kCh) * 8);
-            if (tid < 3 * kCh)
-                *reinterpret_cast<uint4*>(xbuf + (C::kHalo - 3 + tid / kCh) * BS + (tid % kCh) * 8) = v;
-            __syncthreads();
+        // ------- 1. MFMA tile 0 (tokens 0..31) of `cur`, interleaved with the conv of `n1` -------
+        f32x16 accB[2], accP[2];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            accB[0][e] = 0.0f; accP[0][e] = 0.0f; accB[1][e] = 0.0f; accP[1][e] = 0.0f;
         }
-
-        // ---------------- 1. conv -> u (bf16) in LDS ----------------
         {
-            const int cp = tid % C::kPairs;
-            const int tg = __builtin_amdgcn_readfirstlane(tid / C::kPairs);
+            const int cp = 64 * pw + lane;
             const uint4 wq = conv_tab[cp];
             const float2 cb = convb_tab[cp];
-            const uint32_t* xw = reinterpret_cast<const uint32_t*>(xbuf);
+            const int ia0 = opaque(ucur + lds_row(atok) * kRow + 32 * kh);
+            const int ixr = opaque(xw0 / 2 + lane);
+            const int iuw = opaque((unxt + 16 * tg * kRow) / 2 + cp);
             uint32_t xr[C::kTok + 3];
 #pragma unroll
-            for (int k = 0; k < C::kTok + 3; ++k)
-                xr[k] = xw[(tg * C::kTok + C::kHalo - 3 + k) * C::kPairs + cp];
-            uint16_t* ucol = ubuf + 2 * cp;
-#pragma unroll
-            for (int k = 0; k < C::kTok; ++k) {
-                // (x_{t-3}, x_{t-2}) and (x_{t-1}, x_t) of each of the two channels
-                const uint32_t p0a = __builtin_amdgcn_perm(xr[k + 1], xr[k], 0x05040100u);
-                const uint32_t p0b = __builtin_amdgcn_perm(xr[k + 1], xr[k], 0x07060302u);
-                const uint32_t p2a = __builtin_amdgcn_perm(xr[k + 3], xr[k + 2], 0x05040100u);
-                const uint32_t p2b = __builtin_amdgcn_perm(xr[k + 3], xr[k + 2], 0x07060302u);
-                const float u0 = dot2bf(wq.y, p2a, dot2bf(wq.x, p0a, cb.x));
-                const float u1 = dot2bf(wq.w, p2b, dot2bf(wq.z, p0b, cb.y));
-                *reinterpret_cast<uint32_t*>(ucol + lds_row(tg * C::kTok + k) * kRow) = pack2bf(u0, u1);
-            }
-        }
-        // conv state after the last token: rows T-3..T-1 are in xbuf now; they are written
-        // after the carry wait, which orders the write after segment 0 read conv0 (in place)
-        uint4 cl_rows = make_uint4(0, 0, 0, 0);
-        constexpr int kClCh = BS / 8;
-        const bool cl_act = last && a.conv_last != nullptr && tid < 3 * kClCh;
-        if (cl_act)
-            cl_rows = *reinterpret_cast<const uint4*>(xbuf + (T - 3 + tid / kClCh - t0 + C::kHalo) * BS +
-                                                      (tid % kClCh) * 8);
-        __syncthreads();  // u complete; xbuf and ybuf[(it+1)&1] are free
-
-        // ---------------- prefetch the next segment ----------------
-        {
-            const char* xh = xseq + 16 * (lane % C::kLanesPerRow);
-            const char* yh = yseq + 16 * (lane % C::kLanesPerRow);
-            dma_rows<BS, C::kXInst>(xh, nxt, n_tk, B, T, rowb, -C::kHalo, wv, lane / C::kLanesPerRow, xbuf);
-            dma_rows<BS, C::kYInst>(yh, nxt, n_tk, B, T, rowb, 0, wv, lane / C::kLanesPerRow, ybuf[(it + 1) & 1]);
-        }
-        unsigned pending = 0;
-        if (tid == 0) pending = atomicAdd(tctr, 1u);  // ticket after next (published after a barrier)
-
-        // ---------------- 2.+3. gates on MFMA, gate math and local scan ----------------
-        // tile 0 (rows 0..31) on MFMA first; then tile 0's gate math element j is issued
-        // next to tile 1's MFMA step j, so the matrix core and the VALU work side by side
-        f32x16 accB[kNT][2], accP[kNT][2];
-        float psc[kNT], bsc[kNT];
-        {
-            const int atok = 32 * ((ln >> 2) & 1) + 4 * (ln >> 3) + (ln & 3);
-            const uint16_t* ap0 = ubuf + lds_row(atok) * kRow + 32 * kh;
-            const uint16_t* ap1 = ubuf + lds_row(atok + 16) * kRow + 32 * kh;
-#pragma unroll
-            for (int nt = 0; nt < kNT; ++nt)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    accB[nt][0][e] = 0.0f; accP[nt][0][e] = 0.0f; accB[nt][1][e] = 0.0f; accP[nt][1][e] = 0.0f;
-                }
+            for (int k = 0; k < C::kTok + 3; ++k) xr[k] = x_lds32[ixr + k * 64];
+            constexpr int kTokPerStep = C::kTok / C::kKSteps;  // conv tokens per MFMA k-step
 #pragma unroll
             for (int kk = 0; kk < C::kKSteps; ++kk) {
-                const bf16x8 A = *reinterpret_cast<const bf16x8*>(ap0 + 64 * (kk >> 2) + 8 * (kk & 3));
+                const bf16x8 A = *reinterpret_cast<const bf16x8*>(u_lds + ia0 + 64 * (kk >> 2) + 8 * (kk & 3));
+                accB[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, wA[kk], accB[0], 0, 0, 0);
+                accP[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, wX[kk], accP[0], 0, 0, 0);
 #pragma unroll
-                for (int nt = 0; nt < kNT; ++nt) {
-                    accB[nt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, wA[nt][kk], accB[nt][0], 0, 0, 0);
-                    accP[nt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, wX[nt][kk], accP[nt][0], 0, 0, 0);
+                for (int s2 = 0; s2 < kTokPerStep; ++s2) {
+                    const int k = kk * kTokPerStep + s2;
+                    // (x_{t-3}, x_{t-2}) and (x_{t-1}, x_t) of each of the two channels
+                    const uint32_t p0a = __builtin_amdgcn_perm(xr[k + 1], xr[k], 0x05040100u);
+                    const uint32_t p0b = __builtin_amdgcn_perm(xr[k + 1], xr[k], 0x07060302u);
+                    const uint32_t p2a = __builtin_amdgcn_perm(xr[k + 3], xr[k + 2], 0x05040100u);
+                    const uint32_t p2b = __builtin_amdgcn_perm(xr[k + 3], xr[k + 2], 0x07060302u);
+                    const float u0 = dot2bf(wq.y, p2a, dot2bf(wq.x, p0a, cb.x));
+                    const float u1 = dot2bf(wq.w, p2b, dot2bf(wq.z, p0b, cb.y));
+                    u_lds32[iuw + ((k ^ csw) * kRow) / 2] = pack2bf(u0, u1);
                 }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            float4 gc[kNT];
-            const uint16_t* ucol[kNT];
+        }
+        // Copies go out only here, after this iteration's last LDS store before the wait in
+        // step 4 (an LDS store issued while a global->LDS copy is in flight waits for the copy):
+        // the x rows of the segment after next (the conv's reads are complete) and this
+        // segment's y rows (the region's previous contents were stored out last iteration).
+        wait_lds_all();
+        dma_x_rows(a, head, BS, pw, tg, n2, n_tk, lane, x_lds + xw0);
+        dma_y_rows(a, head, BS, cw0, cur, n_tk, lane, y_lds + yw0);
+
+        // ------- 2.+3. tile 1 on MFMA next to tile 0's gate math; then tile 1's gate math -------
+        float psc = 1.0f, bsc = 0.0f;
+        {
+            const int ia1 = opaque(ucur + lds_row(atok + 16) * kRow + 32 * kh);
+            const float4 gc = gate_tab[cw0 + ln];
+            // u of (token 32 hh + 16 mt + j, channel cw0 + ln) is at row 32 hh + 16 mt + (j ^ 12 hh);
+            // with j = 4 g + m that is 32 hh + 16 mt + 4 g + m + hh (12 - 8 g): one base per g
+            int iub[4];
 #pragma unroll
-            for (int nt = 0; nt < kNT; ++nt) {
-                psc[nt] = 1.0f;
-                bsc[nt] = 0.0f;
-                gc[nt] = gate_tab[cw0 + 32 * nt + ln];
-                ucol[nt] = ubuf + 32 * hh * kRow + cw0 + 32 * nt + ln;
-            }
-            static_assert(C::kKSteps == 16 || C::kKSteps == 8, "interleave");
+            for (int g4 = 0; g4 < 4; ++g4) iub[g4] = opaque(ucur + (32 * hh + hh * (12 - 8 * g4)) * kRow + cw0 + ln);
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 if (j < C::kKSteps) {
-                    const int kk = j;
-                    const bf16x8 A = *reinterpret_cast<const bf16x8*>(ap1 + 64 * (kk >> 2) + 8 * (kk & 3));
-#pragma unroll
-                    for (int nt = 0; nt < kNT; ++nt) {
-                        accB[nt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, wA[nt][kk], accB[nt][1], 0, 0, 0);
-                        accP[nt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, wX[nt][kk], accP[nt][1], 0, 0, 0);
-                    }
+                    const bf16x8 A = *reinterpret_cast<const bf16x8*>(u_lds + ia1 + 64 * (j >> 2) + 8 * (j & 3));
+                    accB[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, wA[j], accB[1], 0, 0, 0);
+                    accP[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, wX[j], accP[1], 0, 0, 0);
                 }
-#pragma unroll
-                for (int nt = 0; nt < kNT; ++nt) {
-                    const int row = 4 * ((j >> 2) ^ (3 * hh)) + (j & 3);
-                    const float u = bf2f(ucol[nt][row * kRow]);
-                    const GateOut g = gate_fast(accB[nt][0][j], accP[nt][0][j], gc[nt].x, gc[nt].y, gc[nt].z, u);
-                    bsc[nt] = __builtin_fmaf(g.a, bsc[nt], g.v);
-                    psc[nt] = psc[nt] * g.a;
-                    accB[nt][0][j] = bsc[nt];
-                    accP[nt][0][j] = psc[nt];
-                }
+                const float u = bf2f(u_lds[iub[j >> 2] + j * kRow]);
+                const GateOut g = gate_fast(accB[0][j], accP[0][j], gc.x, gc.y, gc.z, u);
+                bsc = __builtin_fmaf(g.a, bsc, g.v);
+                psc = psc * g.a;
+                accB[0][j] = bsc;
+                accP[0][j] = psc;
                 __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
-#pragma unroll
-                for (int nt = 0; nt < kNT; ++nt) {
-                    const int row = 16 + 4 * ((j >> 2) ^ (3 * hh)) + (j & 3);
-                    const float u = bf2f(ucol[nt][row * kRow]);
-                    const GateOut g = gate_fast(accB[nt][1][j], accP[nt][1][j], gc[nt].x, gc[nt].y, gc[nt].z, u);
-                    bsc[nt] = __builtin_fmaf(g.a, bsc[nt], g.v);
-                    psc[nt] = psc[nt] * g.a;
-                    accB[nt][1][j] = bsc[nt];
-                    accP[nt][1][j] = psc[nt];
-                }
+                const float u = bf2f(u_lds[iub[j >> 2] + (16 + j) * kRow]);
+                const GateOut g = gate_fast(accB[1][j], accP[1][j], gc.x, gc.y, gc.z, u);
+                bsc = __builtin_fmaf(g.a, bsc, g.v);
+                psc = psc * g.a;
+                accB[1][j] = bsc;
+                accP[1][j] = psc;
             }
         }
-        // segment aggregates: low half-wave (tokens 0..31) then high half-wave (32..63)
-        float p_lo[kNT], b_lo[kNT], A_seg[kNT], B_seg[kNT];
-#pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) {
-            const float p_o = __shfl_xor(psc[nt], 32), b_o = __shfl_xor(bsc[nt], 32);
-            p_lo[nt] = hh ? p_o : psc[nt];
-            b_lo[nt] = hh ? b_o : bsc[nt];
-            const float p_hi = hh ? psc[nt] : p_o, b_hi = hh ? bsc[nt] : b_o;
-            A_seg[nt] = p_lo[nt] * p_hi;
-            B_seg[nt] = __builtin_fmaf(p_hi, b_lo[nt], b_hi);
-        }
-
-        // ---------------- 4. carry: probe now, GELU while the probe is in flight ----------------
-        const bool lb_lane = (kNT == 2) || (hh == 0);
-        const int nt_lb = (kNT == 2) ? hh : 0;
-        const size_t chl = (size_t)head * BS + cw0 + 32 * nt_lb + ln;
+        // segment aggregate: low half-wave (tokens 0..31) then high half-wave (32..63)
+        const float p_o = __shfl_xor(psc, 32), b_o = __shfl_xor(bsc, 32);
+        const float p_lo = hh ? p_o : psc, b_lo = hh ? b_o : bsc;
+        const float p_hi = hh ? psc : p_o, b_hi = hh ? bsc : b_o;
+        const float A_seg = p_lo * p_hi;
+        const float B_seg = __builtin_fmaf(p_hi, b_lo, b_hi);
+        const size_t chl = (size_t)head * BS + cw0 + ln;
         const size_t wstride = (size_t)B * D;
-        unsigned long long* wself = a.words + (size_t)seg * wstride + (size_t)b * D + chl;
+        unsigned long long* const wself = a.words + (size_t)seg * wstride + (size_t)b * D + chl;
+        unsigned long long* const wprev = wself - wstride;
+
+        // ------- 4. carry: y and the next x have landed; probe, then GELU while it is in flight -------
+        if (tid == 0) pending = atomicAdd(tctr, 1u);  // ticket three segments ahead
+        wait_vmem_all();
+        // the aggregate goes out now (after the wait, so that wait never includes this store):
+        // successors can fold it while this workgroup merges the GELU branch and looks back
+        if (hh == 0 && seg > 0 && !last) st_word(wself, make_word(A_seg, B_seg, false));
         unsigned long long w1 = kNotReady;
-        float carry_mine = 0.0f;
-        if (lb_lane) {
-            if (seg > 0) w1 = ld_word(wself - wstride);
-            else if (a.h0 != nullptr) carry_mine = a.h0[(size_t)b * D + chl];
+        float h0v = 0.0f;
+        if (hh == 0) {
+            if (seg > 0) w1 = ld_word(wprev);
+            else if (a.h0 != nullptr) h0v = a.h0[(size_t)b * D + chl];
         }
-        // y of this segment has been in LDS since the previous iteration: out_t = h_t g_t with
-        // h_t = b_t + p_t c, kept as (b_t g_t, p_t g_t) until the carry c is known
+        // out_t = h_t g_t with h_t = b_t + p_t c: kept as (b_t g_t, p_t g_t) until c is known
+        const int iy = opaque(yw0 + yrow(32 * hh) + ln);  // y / staging of (token 32 hh + r, this lane)
         if (!last) {
 #pragma unroll
-            for (int nt = 0; nt < kNT; ++nt) {
-                const uint16_t* ycol = ycur + 32 * hh * BS + cw0 + 32 * nt + ln;
+            for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
-                for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) {
-                        const float g = gelu_fast(bf2f(ycol[(16 * mt + j) * BS]));
-                        accB[nt][mt][j] *= g;
-                        accP[nt][mt][j] *= g;
-                    }
+                for (int j = 0; j < 16; ++j) {
+                    const float g = gelu_fast(bf2f(y_lds[iy + (16 * mt + j) * 32]));
+                    accB[mt][j] *= g;
+                    accP[mt][j] *= g;
                 }
             }
         }
-        if (lb_lane) {
-            const float As = (kNT == 2 && hh) ? A_seg[kNT - 1] : A_seg[0];
-            const float Bs = (kNT == 2 && hh) ? B_seg[kNT - 1] : B_seg[0];
-            if (seg > 0) carry_mine = look_back(wself, wstride, seg, w1, As, Bs, !last, a.header);
+        float carry = h0v;
+        bool pred_inc = true;
+        if (hh == 0 && seg > 0) carry = look_back(wself, wstride, seg, w1, A_seg, B_seg, false, a.header, pred_inc);
+        wait_vmem_all();  // the carry's loads (nothing else is outstanding): no wait after the stores
+        const unsigned long long winc = make_word(A_seg, __builtin_fmaf(A_seg, carry, B_seg), true);
+        if (hh == 0) {
+            if (!last) st_word(wself, winc);
+            if (seg > 0) retire_word(wprev, pred_inc, a.header);
         }
-        // this wave's DMA of the next segment completes before the next iteration's barrier,
-        // and before the stores below are issued (so that wait never waits for them)
-        wait_vmem_all();
-        if (lb_lane) {
-            const float As = (kNT == 2 && hh) ? A_seg[kNT - 1] : A_seg[0];
-            const float Bs = (kNT == 2 && hh) ? B_seg[kNT - 1] : B_seg[0];
-            if (!last) st_word(wself, make_word(As, __builtin_fmaf(As, carry_mine, Bs), true));
-            if (seg > 0) st_word(wself - wstride, kNotReady);
-        }
-        float state_in[kNT];
-#pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) {
-            const float c = __shfl(carry_mine, ln + 32 * (kNT == 2 ? nt : 0));
-            state_in[nt] = hh ? __builtin_fmaf(p_lo[nt], c, b_lo[nt]) : c;
-        }
-        if (cl_act)
-            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.conv_last) + ((size_t)b * 3 + tid / kClCh) * D +
-                                      (size_t)head * BS + (tid % kClCh) * 8) = cl_rows;
+        carry = __shfl(carry, ln);
+        const float state_in = hh ? __builtin_fmaf(p_lo, carry, b_lo) : carry;
 
-        // ---------------- 5. fix-up and store ----------------
-        {
-            const __amdgpu_buffer_rsrc_t ro = make_rsrc(static_cast<uint16_t*>(a.out) + ((size_t)b * T + t0) * D);
+        // ------- 5. fix-up into the wave's staging region (in place of y), then 16-byte stores -------
+        if (!last) {
 #pragma unroll
-            for (int nt = 0; nt < kNT; ++nt) {
-                const int chw = head * BS + cw0 + 32 * nt + ln;
-                const int voff = (32 * hh * (int)D + chw) * 2;
-                if (!last) {
+            for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
-                    for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-                        for (int j = 0; j < 16; j += 2) {
-                            const float o0 = __builtin_fmaf(accP[nt][mt][j], state_in[nt], accB[nt][mt][j]);
-                            const float o1 = __builtin_fmaf(accP[nt][mt][j + 1], state_in[nt], accB[nt][mt][j + 1]);
-                            const uint32_t o01 = pack2bf(o0, o1);
-                            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)o01, ro, voff, (16 * mt + j) * rowb, 0);
-                            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(o01 >> 16), ro, voff, (16 * mt + j + 1) * rowb, 0);
-                        }
-                    }
-                } else {
-                    const uint16_t* ycol = ycur + 32 * hh * BS + cw0 + 32 * nt + ln;
-#pragma unroll
-                    for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-                        for (int j = 0; j < 16; ++j) {
-                            const int tok = 32 * hh + 16 * mt + j;
-                            const float h = __builtin_fmaf(accP[nt][mt][j], state_in[nt], accB[nt][mt][j]);
-                            const float o = h * gelu_fast(bf2f(ycol[(16 * mt + j) * BS]));
-                            if (tok < nt_tok)
-                                __builtin_amdgcn_raw_buffer_store_b16(f2bf(o), ro, voff, (16 * mt + j) * rowb, 0);
-                            if (a.h_last != nullptr && t0 + tok == T - 1) a.h_last[(size_t)b * D + chw] = h;
-                        }
-                    }
+                for (int j = 0; j < 16; j += 2) {
+                    const float o0 = __builtin_fmaf(accP[mt][j], state_in, accB[mt][j]);
+                    const float o1 = __builtin_fmaf(accP[mt][j + 1], state_in, accB[mt][j + 1]);
+                    const uint32_t o01 = pack2bf(o0, o1);
+                    y_lds[iy + (16 * mt + j) * 32] = (uint16_t)o01;
+                    y_lds[iy + (16 * mt + j + 1) * 32] = (uint16_t)(o01 >> 16);
                 }
             }
+        } else {
+            // last segment: GELU here, h_last and the conv window after the last token
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int tok = 32 * hh + 16 * mt + j;
+                    const float h = __builtin_fmaf(accP[mt][j], state_in, accB[mt][j]);
+                    const float o = h * gelu_fast(bf2f(y_lds[iy + (16 * mt + j) * 32]));
+                    y_lds[iy + (16 * mt + j) * 32] = f2bf(o);
+                    if (a.h_last != nullptr && t0 + tok == T - 1) a.h_last[(size_t)b * D + chl] = h;
+                }
+            }
+            if (a.conv_last != nullptr && tg == 0 && lane < 48) {
+                // the last three inputs (oldest first); before token 0 they are the carried window
+                // (read here, after the carry wait, so an in-place window was read by segment 0 first)
+                const int rr = lane >> 4, tok = T - 3 + rr;
+                const size_t c = (size_t)head * BS + 128 * pw + 8 * (lane & 15);
+                uint4 v = make_uint4(0, 0, 0, 0);
+                if (tok >= 0)
+                    v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + ((size_t)b * T + tok) * D + c);
+                else if (a.conv0 != nullptr)
+                    v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.conv0) + ((size_t)b * 3 + 3 + tok) * D + c);
+                *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.conv_last) + ((size_t)b * 3 + rr) * D + c) = v;
+            }
         }
-        if (tid == 0) s_tk[0] = pending;
-        cur = nxt;
+        {
+            // rows of the staging region -> out (4 lanes per 64-byte row, 16 rows per step)
+            const __amdgpu_buffer_rsrc_t ro = make_rsrc(static_cast<uint16_t*>(a.out) + ((size_t)b * T + t0) * D);
+            const int voff = (int)((size_t)head * BS + cw0 + 8 * (lane & 3)) * 2;
+            const int iyr = opaque(yw0 + (lane >> 2) * 32 + 8 * (lane & 3));
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r = 16 * q + (lane >> 2);
+                const uint4 v = *reinterpret_cast<const uint4*>(y_lds + iyr + yrow(16 * q));
+                if (r < nt_tok)
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ro, voff + r * rowb, 0, 0);
+            }
+        }
+        if (tid == 0) s_tk[it & 3] = pending;
+        lds_barrier();  // u of n1 complete and u of cur no longer read; the ticket slot is visible
+        const unsigned n3 = __builtin_amdgcn_readfirstlane(s_tk[it & 3]);
+        cur = n1;
+        n1 = n2;
+        n2 = n3;
         ++it;
     }
 
-    wait_vmem_all();  // no DMA into LDS may outlive the workgroup
+    wait_vmem_all();  // no copy into LDS may outlive the workgroup
     if (tid0 == 0) {
         const unsigned done = atomicAdd(&a.header[kDoneWord], 1u);
         if (done == G - 1) {

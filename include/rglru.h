@@ -138,7 +138,9 @@ int conv1d_state_update(const rglru_params *p, int32_t N, int32_t T_new, const v
 /*
  * Diagnostics of a prefill workspace: copies its error flags to *flags_out (0 = none) and
  * clears them.  Synchronous (waits for `stream`).  Bit 0: a carry wait exceeded its bound
- * (the affected outputs are NaN).
+ * (the affected outputs are NaN).  Bit 1: a wait for a predecessor's inclusive word before
+ * resetting it exceeded its bound (results are correct, but the workspace may hold a stale
+ * word: initialise it again before reuse).
  */
 int rglru_prefill_workspace_flags(void *workspace, size_t ws_bytes, uint32_t *flags_out,
                                   void *stream);

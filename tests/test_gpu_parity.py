@@ -336,6 +336,32 @@ def test_deterministic_and_workspace_reuse():
     assert ws.flags() == 0
 
 
+@pytest.mark.parametrize("storage", [synth.BF16, synth.F32])
+def test_workspace_clean_after_launch(storage):
+    """After every launch each carry word is back to 'not ready' and the ticket counters are
+    zero, so a reused workspace starts clean (this checks the word reset protocol directly)."""
+    from gated_linear_recurrence_amd import binding
+    D, nh = (512, 2) if storage == synth.BF16 else (256, 2)
+    w = synth.Workload("wsclean", 4, 1000, D, nh, storage, 0.9, 0.999, 0.0, 12)
+    p = synth.make_params(w, biases=True)
+    x, y = synth.make_act(w, "x"), synth.make_act(w, "y")
+    P = H.dev_params(p, w.H)
+    xd, yd = H.to_dev(x), H.to_dev(y)
+    ws = binding.make_workspace(P, w.B, w.T)
+    ref, _, _ = binding.rglru_prefill(P, xd, yd)
+    for rep in range(6):
+        T = w.T if rep % 2 == 0 else 700
+        out, _, _ = binding.rglru_prefill(P, xd[:, :T].contiguous(), yd[:, :T].contiguous(),
+                                          workspace=ws)
+        torch.cuda.synchronize()
+        raw = ws.t.cpu().numpy()
+        assert (raw[4096:] == 0xFF).all(), "stale carry words after launch %d" % rep
+        assert (raw[:4096] == 0).all(), "header not clean after launch %d" % rep
+        if T == w.T:
+            assert torch.equal(out, ref)
+    assert ws.flags() == 0
+
+
 def test_outputs_stay_in_bounds():
     """Canary bands around out/h_last/conv_last are untouched; the workspace gets no errors."""
     from gated_linear_recurrence_amd import binding
