@@ -138,7 +138,7 @@ __global__ void __launch_bounds__(2 * BS) decode_kernel(DecodeArgs a) {
     const float bia = a.ba ? S::get(static_cast<const ST*>(a.ba), ch) : 0.0f;
     const float bix = a.bx ? S::get(static_cast<const ST*>(a.bx), ch) : 0.0f;
     const float nba = -bia * kLog2e, nbx = -bix * kLog2e;
-    const float kc = -8.0f * sp * kLog2e, kcn = -8.0f * sp;
+    const float ikc = gate_ikc(sp), kcn = -8.0f * sp;
     const ST* __restrict__ y = static_cast<const ST*>(a.y);
     ST* __restrict__ out = static_cast<ST*>(a.out);
 #pragma unroll
@@ -149,7 +149,7 @@ __global__ void __launch_bounds__(2 * BS) decode_kernel(DecodeArgs a) {
         float u;
         if constexpr (kBf) u = bf2f(u_lds[m * kRow + ncol]);
         else u = u_lds[m * kRow + ncol];
-        const GateOut g = kBf ? gate_fast(accA[j], accX[j], nba, nbx, kc, u)
+        const GateOut g = kBf ? gate_fast(accA[j], accX[j], nba, nbx, ikc, u)
                               : gate_precise(accA[j], accX[j], bia, bix, kcn, u);
         float* hp = a.h + (size_t)n * D + ch;
         const float hn = __builtin_fmaf(g.a, *hp, g.v);
@@ -179,8 +179,15 @@ __global__ void __launch_bounds__(2 * BS) decode_bf16_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t u_lds[32 * kRow];
 
     const int tid = threadIdx.x;
-    const int n0 = blockIdx.x * 32;
-    const int head = blockIdx.y;
+    // Placement: workgroups are dealt to the 8 XCDs round-robin.  Slots are numbered XCD by XCD
+    // and walked head-major over (head, tile), so the tiles of one head share an XCD and its
+    // gate weights are fetched into that XCD's L2 once per step.
+    const unsigned G = gridDim.x, bid = blockIdx.x;
+    const unsigned xcd = bid & 7u, jx = bid >> 3, per = G >> 3, rem = G & 7u;
+    const unsigned slot = xcd * per + min(xcd, rem) + jx;
+    const unsigned n_tiles = (unsigned)((a.N + 31) / 32);
+    const int head = (int)(slot / n_tiles);
+    const int n0 = (int)(slot % n_tiles) * 32;
     const int N = a.N;
     const size_t D = (size_t)a.D;
     uint16_t* __restrict__ cs = static_cast<uint16_t*>(a.conv_state);
@@ -297,14 +304,14 @@ __global__ void __launch_bounds__(2 * BS) decode_bf16_kernel(DecodeArgs a) {
     // ---- gates, state update, output ----
     const float nba = bap ? -bf2f(bav) * kLog2e : 0.0f;
     const float nbx = bxp ? -bf2f(bxv) * kLog2e : 0.0f;
-    const float kc = -8.0f * softplus_neg(lam) * kLog2e;
+    const float ikc = gate_ikc(softplus_neg(lam));
     uint16_t* __restrict__ out = static_cast<uint16_t*>(a.out);
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
         const int m = mfma_d_row(lane, j);
         const int n = n0 + m;
         const float u = bf2f(u_lds[m * kRow + ncol]);
-        const GateOut g = gate_fast(accA[j], accX[j], nba, nbx, kc, u);
+        const GateOut g = gate_fast(accA[j], accX[j], nba, nbx, ikc, u);
         const float hn = __builtin_fmaf(g.a, hv[j], g.v);
         const float o = hn * gelu_fast(bf2f(yv[j]));
         if (n < N) {
@@ -400,8 +407,9 @@ __global__ void conv_state_kernel(ConvArgs a) {
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int bs, hipStream_t s) {
     const dim3 grid((a.N + 31) / 32, a.H);
     if (dtype == 1) {
-        if (bs == 256) hipLaunchKernelGGL((decode_bf16_kernel<256>), grid, dim3(512), 0, s, a);
-        else hipLaunchKernelGGL((decode_bf16_kernel<128>), grid, dim3(256), 0, s, a);
+        const dim3 grid1((unsigned)(((a.N + 31) / 32) * a.H));  // (tile, head) placed per XCD
+        if (bs == 256) hipLaunchKernelGGL((decode_bf16_kernel<256>), grid1, dim3(512), 0, s, a);
+        else hipLaunchKernelGGL((decode_bf16_kernel<128>), grid1, dim3(256), 0, s, a);
     } else {
         if (bs == 256) hipLaunchKernelGGL((decode_kernel<256, float>), grid, dim3(512), 0, s, a);
         else hipLaunchKernelGGL((decode_kernel<128, float>), grid, dim3(256), 0, s, a);

@@ -73,12 +73,19 @@ __device__ __forceinline__ float softplus_neg(float lam) {
     return lam > 0.0f ? log1pf(expf(-lam)) : (-lam + log1pf(expf(lam)));
 }
 
+// 1 / kc for gate_fast, kc = -8 softplus(-Lambda) log2(e) <= 0; kc = -0 (a == 1 for every r)
+// maps to -FLT_MAX, which keeps (1 + er) * ikc free of 0 * inf.
+__device__ __forceinline__ float gate_ikc(float sp_neg) {
+    return fmaxf(1.0f / (-8.0f * sp_neg * kLog2e), -3.4028234663852886e38f);
+}
+
 // ---------------------------------------------------------------------------------------
 // RG-LRU gate arithmetic for one element (r, i, a and the gated input v = sqrt(1-a^2) i u)
 //
 // Fast form (bf16 storage): exp2/rcp/sqrt hardware approximations (about 1 ulp each).
 //   pre-activations arrive as MFMA sums without bias; nb = -bias * log2(e);
-//   kc = -8 softplus(-Lambda) log2(e), so log2(a) = kc * r.
+//   kc = -8 softplus(-Lambda) log2(e) (so log2(a) = kc * r) enters as ikc = 1 / kc: then
+//   kc * r = kc / (1 + er) = rcp((1 + er) * ikc), one reciprocal and no multiply.
 // Precise form (fp32 storage): library expf/expm1f and IEEE division; sqrt(1 - a^2) is
 //   computed as sqrt(-expm1(2 log a)) so it keeps full relative accuracy when a -> 1.
 // ---------------------------------------------------------------------------------------
@@ -86,13 +93,13 @@ struct GateOut {
     float a, v;
 };
 
-__device__ __forceinline__ GateOut gate_fast(float sa, float sx, float nba, float nbx, float kc,
+__device__ __forceinline__ GateOut gate_fast(float sa, float sx, float nba, float nbx, float ikc,
                                              float u) {
     const float er = __builtin_amdgcn_exp2f(__builtin_fmaf(sa, -kLog2e, nba));
-    const float r = __builtin_amdgcn_rcpf(1.0f + er);
     const float ei = __builtin_amdgcn_exp2f(__builtin_fmaf(sx, -kLog2e, nbx));
     const float i = __builtin_amdgcn_rcpf(1.0f + ei);
-    const float a = __builtin_amdgcn_exp2f(kc * r);
+    // r -> 0 (er -> inf) gives rcp(-inf) = -0 and a = 1
+    const float a = __builtin_amdgcn_exp2f(__builtin_amdgcn_rcpf(__builtin_fmaf(er, ikc, ikc)));
     // a <= 1 in exact arithmetic; the clamp guards the 1-ulp error of the hardware exp2
     const float m = __builtin_amdgcn_sqrtf(fmaxf(__builtin_fmaf(-a, a, 1.0f), 0.0f));
     return {a, m * (i * u)};

@@ -328,7 +328,7 @@ __global__ void __launch_bounds__(2 * BS) prefill_kernel(PrefillArgs a) {
         const float bia = a.ba ? S::get(static_cast<const ST*>(a.ba), ch) : 0.0f;
         const float bix = a.bx ? S::get(static_cast<const ST*>(a.bx), ch) : 0.0f;
         const float nba = -bia * kLog2e, nbx = -bix * kLog2e;
-        const float kc = -8.0f * sp * kLog2e;  // log2(a) = kc * r
+        const float ikc = gate_ikc(sp);        // log2(a) = kc * r, ikc = 1 / kc
         const float kcn = -8.0f * sp;          // ln(a) = kcn * r
         // LDS row of register j (tile mt): 32 hh + 16 mt + 4 ((j>>2) ^ 3 hh) + (j & 3)
         const L* ucol = u_lds + 32 * hh * kRow + ncol;
@@ -340,7 +340,7 @@ __global__ void __launch_bounds__(2 * BS) prefill_kernel(PrefillArgs a) {
                 float u;
                 if constexpr (kBf) u = bf2f(ucol[row * kRow]);
                 else u = ucol[row * kRow];
-                const GateOut g = kBf ? gate_fast(accB[mt][j], accP[mt][j], nba, nbx, kc, u)
+                const GateOut g = kBf ? gate_fast(accB[mt][j], accP[mt][j], nba, nbx, ikc, u)
                                       : gate_precise(accB[mt][j], accP[mt][j], bia, bix, kcn, u);
                 bsc = __builtin_fmaf(g.a, bsc, g.v);
                 psc = psc * g.a;
@@ -560,7 +560,7 @@ prefill_bf16_kernel(PrefillArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t y_lds[C::kWaves * C::kYElems];    // y rows / out
     __shared__ __attribute__((aligned(16))) uint4 conv_tab[BS / 2];   // taps of a channel pair
     __shared__ __attribute__((aligned(8))) float2 convb_tab[BS / 2];  // biases of a channel pair
-    __shared__ __attribute__((aligned(16))) float4 gate_tab[BS];      // (nba, nbx, kc, 0) per channel
+    __shared__ __attribute__((aligned(16))) float4 gate_tab[BS];      // (nba, nbx, 1/kc, 0) per channel
     __shared__ unsigned s_tk[4];
     const uint32_t* const x_lds32 = reinterpret_cast<const uint32_t*>(x_lds);
     uint32_t* const u_lds32 = reinterpret_cast<uint32_t*>(u_lds);
@@ -602,7 +602,7 @@ prefill_bf16_kernel(PrefillArgs a) {
         const float sp = softplus_neg(a.lambda[chn]);
         const float bia = a.ba ? bf2f(static_cast<const uint16_t*>(a.ba)[chn]) : 0.0f;
         const float bix = a.bx ? bf2f(static_cast<const uint16_t*>(a.bx)[chn]) : 0.0f;
-        gate_tab[i] = make_float4(-bia * kLog2e, -bix * kLog2e, -8.0f * sp * kLog2e, 0.0f);
+        gate_tab[i] = make_float4(-bia * kLog2e, -bix * kLog2e, gate_ikc(sp), 0.0f);
     }
     // gate weights of this wave's channels, held in registers throughout
     bf16x8 wA[C::kKSteps], wX[C::kKSteps];
