@@ -93,7 +93,7 @@ def time_prefill(w, B, T, steps, warmup, torch, binding):
     return ms
 
 
-def time_decode(w, N, steps, torch, binding):
+def time_decode(w, N, steps, torch, binding, split=True):
     p = synth.make_params(w)
     P = binding.Params(*[_to_dev(p[k], torch) for k in ("conv_w", "conv_b", "wa", "ba", "wx",
                                                           "bx", "lambda")])
@@ -104,9 +104,11 @@ def time_decode(w, N, steps, torch, binding):
     cs = torch.zeros((N, 3, w.D), dtype=x.dtype, device="cuda")
     outs = torch.empty_like(x)
 
+    ws = binding.make_decode_workspace(P, N) if split else None
+
     def run():
         for t in range(steps):
-            binding.rglru_decode_step(P, x[:, t], y[:, t], h, cs, out_t=outs[:, t])
+            binding.rglru_decode_step(P, x[:, t], y[:, t], h, cs, out_t=outs[:, t], workspace=ws)
 
     run()  # warm-up
     torch.cuda.synchronize()
@@ -322,11 +324,14 @@ def main():
             "algorithmic_GBs": b2 / (ms2 * 1e-3) / 1e9, "hbm_frac": b2 / (ms2 * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "note": "34 MB working set fits the 256 MB Infinity Cache; not flushed between reps"}
         wd = synth.WORKLOADS[synth.DECODE_2B]
-        eager_us, graph_us = time_decode(wd, wd.B, wd.T, torch, binding)
+        eager_us, graph_us = time_decode(wd, wd.B, wd.T, torch, binding, split=True)
+        f_eager, f_graph = time_decode(wd, wd.B, wd.T, torch, binding, split=False)
         db = decode_bytes(wd, wd.B)
         best = graph_us if graph_us is not None else eager_us
-        line["decode"] = {"workload": wd.name, "us_per_step_graph": graph_us,
-                          "us_per_step_eager": eager_us, "bytes_per_step": db,
+        line["decode"] = {"workload": wd.name, "form": "split (conv pass + gate pass, workspace)",
+                          "us_per_step_graph": graph_us, "us_per_step_eager": eager_us,
+                          "fused_us_per_step_graph": f_graph, "fused_us_per_step_eager": f_eager,
+                          "bytes_per_step": db,
                           "hbm_frac": db / (best * 1e-6) / 1e9 / HBM_PEAK_GBS}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)

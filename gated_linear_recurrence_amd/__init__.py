@@ -5,5 +5,6 @@ ctypes layer with the same names as the C ABI in ``include/rglru.h``.  ``synth``
 seeded synthetic inputs.
 """
 from .binding import (Params, RglruError, Workspace, conv1d_state_update, load_library,  # noqa: F401
-                      make_workspace, rglru_decode_step, rglru_prefill,
-                      rglru_prefill_workspace_bytes, rglru_prefill_workspace_init)
+                      make_decode_workspace, make_workspace, rglru_decode_step,
+                      rglru_decode_workspace_bytes, rglru_prefill, rglru_prefill_workspace_bytes,
+                      rglru_prefill_workspace_init)

@@ -24,8 +24,9 @@ RGLRU_BF16 = 1
 STATUS = {0: "RGLRU_OK", 1: "RGLRU_ERR_NULL", 2: "RGLRU_ERR_SHAPE", 3: "RGLRU_ERR_UNSUPPORTED",
           4: "RGLRU_ERR_WORKSPACE", 5: "RGLRU_ERR_ALIAS", 6: "RGLRU_ERR_HIP"}
 EXPORTS = ["rglru_prefill_workspace_bytes", "rglru_prefill_workspace_init", "rglru_prefill",
-           "rglru_decode_step", "conv1d_state_update", "rglru_prefill_workspace_flags",
-           "rglru_status_string", "rglru_last_hip_error", "rglru_abi_version"]
+           "rglru_decode_workspace_bytes", "rglru_decode_step", "conv1d_state_update",
+           "rglru_prefill_workspace_flags", "rglru_status_string", "rglru_last_hip_error",
+           "rglru_abi_version"]
 
 _lock = threading.Lock()
 _lib = None
@@ -66,7 +67,9 @@ def load_library(path: str = LIB_PATH):
         lib.rglru_prefill_workspace_init.restype = ctypes.c_int
         lib.rglru_prefill.argtypes = [PP, I32, I32, P, P, P, P, P, P, P, P, SZ, P]
         lib.rglru_prefill.restype = ctypes.c_int
-        lib.rglru_decode_step.argtypes = [PP, I32, P, I64, P, I64, P, I64, P, P, P]
+        lib.rglru_decode_workspace_bytes.argtypes = [I32, I32, I32]
+        lib.rglru_decode_workspace_bytes.restype = SZ
+        lib.rglru_decode_step.argtypes = [PP, I32, P, I64, P, I64, P, I64, P, P, P, SZ, P]
         lib.rglru_decode_step.restype = ctypes.c_int
         lib.conv1d_state_update.argtypes = [PP, I32, I32, P, P, P, P]
         lib.conv1d_state_update.restype = ctypes.c_int
@@ -210,9 +213,21 @@ def rglru_prefill(p: Params, x, y, h0=None, conv0=None, *, out=None, h_last=None
     return out, h_last, conv_last
 
 
-def rglru_decode_step(p: Params, x_t, y_t, h, conv_state, out_t=None):
+def rglru_decode_workspace_bytes(N: int, D: int, dtype) -> int:
+    lib = load_library()
+    return int(lib.rglru_decode_workspace_bytes(N, D, _dtype_code(dtype)))
+
+
+def make_decode_workspace(p: Params, N: int):
+    """Device buffer for the split decode step (uint8; needs no initialisation)."""
+    return torch.empty(max(rglru_decode_workspace_bytes(N, p.D, p.dtype), 16), dtype=torch.uint8,
+                       device=p.device)
+
+
+def rglru_decode_step(p: Params, x_t, y_t, h, conv_state, out_t=None, workspace=None):
     """One token for N sequences.  x_t, y_t [N, D] (rows may be strided, e.g. x[:, t]);
-    h [N, D] fp32 and conv_state [N, 3, D] are updated in place.  Returns out_t [N, D]."""
+    h [N, D] fp32 and conv_state [N, 3, D] are updated in place.  Returns out_t [N, D].
+    workspace: None (fused kernel) or a buffer from make_decode_workspace (split step)."""
     lib = load_library()
     N, D = x_t.shape
     for t, name in ((x_t, "x_t"), (y_t, "y_t")):
@@ -224,9 +239,12 @@ def rglru_decode_step(p: Params, x_t, y_t, h, conv_state, out_t=None):
         out_t = torch.empty((N, D), dtype=p.dtype, device=p.device)
     if out_t.shape != (N, D) or out_t.stride(1) != 1 or out_t.dtype != p.dtype:
         raise ValueError("out_t must be [N, D] rows with unit channel stride")
+    if workspace is not None and (workspace.device != p.device or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous buffer on %s" % p.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.rglru_decode_step(ctypes.byref(p.c), N, _ptr(x_t), x_t.stride(0), _ptr(y_t),
                                y_t.stride(0), _ptr(out_t), out_t.stride(0), _ptr(h),
-                               _ptr(conv_state), _stream())
+                               _ptr(conv_state), _ptr(workspace), ws_bytes, _stream())
     _check(lib, st, "rglru_decode_step")
     return out_t
 

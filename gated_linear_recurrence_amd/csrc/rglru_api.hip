@@ -149,9 +149,14 @@ int rglru_prefill(const rglru_params* p, int32_t B, int32_t T, const void* x, co
     return e == hipSuccess ? RGLRU_OK : hip_fail(e);
 }
 
+size_t rglru_decode_workspace_bytes(int32_t N, int32_t D, int32_t dtype) {
+    if (N < 1 || D < 1) return 0;
+    return (size_t)N * (size_t)D * elem_size(dtype);
+}
+
 int rglru_decode_step(const rglru_params* p, int32_t N, const void* x_t, int64_t ld_x,
                       const void* y_t, int64_t ld_y, void* out_t, int64_t ld_out, float* h,
-                      void* conv_state, void* stream) {
+                      void* conv_state, void* workspace, size_t ws_bytes, void* stream) {
     int st = check_params(p, true);
     if (st != RGLRU_OK) return st;
     if (N < 1) return RGLRU_ERR_SHAPE;
@@ -177,6 +182,15 @@ int rglru_decode_step(const rglru_params* p, int32_t N, const void* x_t, int64_t
         overlap(h, sh, conv_state, sc) || overlap(conv_state, sc, x_t, sx) ||
         overlap(conv_state, sc, y_t, sy))
         return RGLRU_ERR_ALIAS;
+    if (workspace != nullptr) {
+        const size_t need = rglru_decode_workspace_bytes(N, p->D, p->dtype);
+        if (ws_bytes < need) return RGLRU_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return RGLRU_ERR_UNSUPPORTED;
+        if (overlap(workspace, need, x_t, sx) || overlap(workspace, need, y_t, sy) ||
+            overlap(workspace, need, out_t, so) || overlap(workspace, need, h, sh) ||
+            overlap(workspace, need, conv_state, sc))
+            return RGLRU_ERR_ALIAS;
+    }
     DecodeArgs a;
     memset(&a, 0, sizeof a);
     a.x = x_t; a.y = y_t; a.out = out_t;
@@ -185,6 +199,7 @@ int rglru_decode_step(const rglru_params* p, int32_t N, const void* x_t, int64_t
     a.wa = p->gate_a_w; a.ba = p->gate_a_b; a.wx = p->gate_x_w; a.bx = p->gate_x_b;
     a.lambda = p->lambda;
     a.h = h; a.conv_state = conv_state;
+    a.u_ws = workspace;
     a.N = N; a.D = p->D; a.H = p->n_heads;
     hipError_t e = launch_decode(a, p->dtype, p->D / p->n_heads, (hipStream_t)stream);
     return e == hipSuccess ? RGLRU_OK : hip_fail(e);

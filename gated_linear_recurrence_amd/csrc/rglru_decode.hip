@@ -16,6 +16,12 @@ namespace rglru {
 
 namespace {
 
+typedef unsigned int u32x4d __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0xffffffff, 0x00020000);
+}
+
 template <int BS, typename ST>
 __global__ void __launch_bounds__(2 * BS) decode_kernel(DecodeArgs a) {
     using S = Store<ST>;
@@ -321,6 +327,202 @@ __global__ void __launch_bounds__(2 * BS) decode_bf16_kernel(DecodeArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// Split decode (used when the caller passes a workspace of N x D storage elements for u).
+// The fused kernel above must give each (32 sequences, head) workgroup all of the head's
+// gate weights (256 KB at bs = 256), pulled through one CU on every step; that bounds the
+// step.  Split in two passes, the work of a head spreads over bs/32 workgroups per 64
+// sequences, each pulling only its 32 channels' weights.
+// ---------------------------------------------------------------------------------------
+
+// Pass 1: u = conv([window, x_t]) for one (sequence, 8-channel chunk) per thread, written to
+// the workspace in the storage dtype (nearest-even, as the fused step rounds it), and the
+// window shifted in place.  Elementwise: no thread reads what another writes.
+template <typename ST>
+__global__ void __launch_bounds__(256) decode_conv_kernel(DecodeArgs a) {
+    using S = Store<ST>;
+    const int D8 = a.D >> 3;
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (size_t)a.N * (size_t)D8) return;
+    const size_t D = (size_t)a.D;
+    const size_t n = i / (size_t)D8, c0 = (i % (size_t)D8) * 8;
+    ST* cs = static_cast<ST*>(a.conv_state) + n * 3 * D + c0;
+    float s0[8], s1[8], s2[8], xt[8], w[32], cb[8];
+    S::load8(cs, s0);
+    S::load8(cs + D, s1);
+    S::load8(cs + 2 * D, s2);
+    S::load8(static_cast<const ST*>(a.x) + n * (size_t)a.ld_x + c0, xt);
+    const ST* cw = static_cast<const ST*>(a.conv_w) + c0 * 4;  // [channel][tap]
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        float t[8];
+        S::load8(cw + 8 * q, t);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[8 * q + e] = t[e];
+    }
+    if (a.conv_b) S::load8(static_cast<const ST*>(a.conv_b) + c0, cb);
+    else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cb[e] = 0.0f;
+    }
+    float u[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        // tap j multiplies x_{t-3+j}: the window holds x_{t-3}, x_{t-2}, x_{t-1}
+        float acc = __builtin_fmaf(w[4 * e + 0], s0[e], cb[e]);
+        acc = __builtin_fmaf(w[4 * e + 1], s1[e], acc);
+        acc = __builtin_fmaf(w[4 * e + 2], s2[e], acc);
+        u[e] = __builtin_fmaf(w[4 * e + 3], xt[e], acc);
+    }
+    S::store8(static_cast<ST*>(a.u_ws) + n * D + c0, u);
+    // the stored values round-trip exactly (bf16 -> fp32 -> bf16, fp32 -> fp32)
+    S::store8(cs, s1);
+    S::store8(cs + D, s2);
+    S::store8(cs + 2 * D, xt);
+}
+
+// Global -> LDS copy of 16 bytes per lane (buffer load with the LDS bit).
+__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, void* lds, int byte_off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, byte_off, 0, 0, 0);
+}
+
+// 16-byte store through a buffer resource.
+__device__ __forceinline__ void store16(uint4 v, __amdgpu_buffer_rsrc_t r, int byte_off) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4d, v), r, byte_off, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
+
+// Pass 2: gates, state update and output for one wave = (64 sequences, head, 32 output
+// channels): two 32-row MFMA tiles per gate over the u rows of its 64 sequences (all bs input
+// channels of the head).  The u rows, h and y reach LDS by buffer loads with the LDS bit (u
+// with 16-byte chunks swizzled per row so the A-fragment reads spread over the banks); the
+// gate weights of the 32 channels are in VGPRs; h and out go back through LDS as 16-byte rows.
+template <int BS>
+__global__ void __launch_bounds__(64) decode_gate_kernel(DecodeArgs a) {
+    constexpr int kKSteps = BS / 16;
+    constexpr int kChunks = BS / 8;             // 16-byte chunks per u row
+    constexpr int kRowsPerInst = 64 / kChunks;  // u rows per copy instruction
+    constexpr int kCB = BS / 32;                // 32-channel blocks per head
+    __shared__ __attribute__((aligned(16))) uint16_t u_lds[64 * BS];
+    __shared__ __attribute__((aligned(16))) float h_lds[64 * 32];
+    __shared__ __attribute__((aligned(16))) uint16_t y_lds[64 * 32];
+
+    const int lane = threadIdx.x, ln = lane & 31, kh = lane >> 5;
+    const int N = a.N;
+    const size_t D = (size_t)a.D;
+    // Placement: workgroups are dealt to the 8 XCDs round-robin; slots are numbered XCD by XCD
+    // and walked head-major, so the workgroups of one head share an XCD's L2.
+    const unsigned G = gridDim.x, bid = blockIdx.x;
+    const unsigned xcd = bid & 7u, jx = bid >> 3, per = G >> 3, rem = G & 7u;
+    const unsigned slot = xcd * per + min(xcd, rem) + jx;
+    const unsigned n_blocks = (unsigned)((N + 63) / 64);
+    const int head = (int)(slot / (n_blocks * kCB));
+    const unsigned rs = slot % (n_blocks * kCB);
+    const int n0 = (int)(rs / kCB) * 64;
+    const int cw0 = (int)(rs % kCB) * 32;
+    const size_t chn = (size_t)head * BS + cw0 + ln;  // this lane's output channel
+
+    // 1. gate weights of the 32 channels: B fragments of all K steps, both gates
+    bf16x8 wA[kKSteps], wX[kKSteps];
+    {
+        const uint16_t* war = static_cast<const uint16_t*>(a.wa) + chn * BS;
+        const uint16_t* wxr = static_cast<const uint16_t*>(a.wx) + chn * BS;
+#pragma unroll
+        for (int kk = 0; kk < kKSteps; ++kk) {
+            const int kb = 64 * (kk >> 2) + 32 * kh + 8 * (kk & 3);
+            wA[kk] = *reinterpret_cast<const bf16x8*>(war + kb);
+            wX[kk] = *reinterpret_cast<const bf16x8*>(wxr + kb);
+        }
+    }
+    // 2. copies into LDS (rows past N repeat row N-1; they are never stored)
+    {
+        const __amdgpu_buffer_rsrc_t ru =
+            make_rsrc(static_cast<const uint16_t*>(a.u_ws) + (size_t)head * BS);
+#pragma unroll
+        for (int i = 0; i < 64 / kRowsPerInst; ++i) {
+            const int row = kRowsPerInst * i + lane / kChunks;
+            const int chunk = (lane % kChunks) ^ (row & 15);  // LDS position p holds chunk p ^ (row & 15)
+            const int n = min(n0 + row, N - 1);
+            copy16_to_lds(ru, u_lds + i * 512, (int)(((size_t)n * D + chunk * 8) * 2));
+        }
+        const __amdgpu_buffer_rsrc_t rh = make_rsrc(a.h + (size_t)head * BS + cw0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int n = min(n0 + 8 * i + lane / 8, N - 1);
+            copy16_to_lds(rh, h_lds + i * 256, (int)(((size_t)n * D + 4 * (lane % 8)) * 4));
+        }
+        const __amdgpu_buffer_rsrc_t ry =
+            make_rsrc(static_cast<const uint16_t*>(a.y) + (size_t)head * BS + cw0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int n = min(n0 + 16 * i + lane / 4, N - 1);
+            copy16_to_lds(ry, y_lds + i * 512, (int)(((size_t)n * (size_t)a.ld_y + 8 * (lane % 4)) * 2));
+        }
+    }
+    const float lam = a.lambda[chn];
+    const uint16_t* bap = static_cast<const uint16_t*>(a.ba);
+    const uint16_t* bxp = static_cast<const uint16_t*>(a.bx);
+    const uint16_t bav = (bap ? bap : static_cast<const uint16_t*>(a.wa))[bap ? chn : 0];
+    const uint16_t bxv = (bxp ? bxp : static_cast<const uint16_t*>(a.wx))[bxp ? chn : 0];
+    wait_vmem_all();  // weights, copies and constants have landed
+
+    // 3. gate pre-activations: rows of tile mt are sequences n0 + 32 mt + (lane % 32)
+    f32x16 accA[2], accX[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) { accA[mt][e] = 0.0f; accX[mt][e] = 0.0f; }
+        const int m = 32 * mt + ln;
+#pragma unroll
+        for (int kk = 0; kk < kKSteps; ++kk) {
+            const int chunk = 8 * (kk >> 2) + 4 * kh + (kk & 3);
+            const bf16x8 A = *reinterpret_cast<const bf16x8*>(u_lds + m * BS + (chunk ^ (m & 15)) * 8);
+            accA[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, wA[kk], accA[mt], 0, 0, 0);
+            accX[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, wX[kk], accX[mt], 0, 0, 0);
+        }
+    }
+
+    // 4. gates, state update, output (into the LDS tiles in place)
+    const float nba = bap ? -bf2f(bav) * kLog2e : 0.0f;
+    const float nbx = bxp ? -bf2f(bxv) * kLog2e : 0.0f;
+    const float ikc = gate_ikc(softplus_neg(lam));
+    const int cu = cw0 + ln;  // channel within the head (u column)
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int m = 32 * mt + mfma_d_row(lane, j);
+            const float u = bf2f(u_lds[m * BS + (((cu >> 3) ^ (m & 15)) << 3) + (cu & 7)]);
+            const GateOut g = gate_fast(accA[mt][j], accX[mt][j], nba, nbx, ikc, u);
+            const float hn = __builtin_fmaf(g.a, h_lds[m * 32 + ln], g.v);
+            h_lds[m * 32 + ln] = hn;
+            y_lds[m * 32 + ln] = f2bf(hn * gelu_fast(bf2f(y_lds[m * 32 + ln])));
+        }
+    }
+
+    // 5. h and out back to memory, 16 bytes per lane, rows below N only
+    {
+        const __amdgpu_buffer_rsrc_t rh = make_rsrc(a.h + (size_t)head * BS + cw0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int row = 8 * i + lane / 8;
+            const uint4 v = *reinterpret_cast<const uint4*>(h_lds + row * 32 + 4 * (lane % 8));
+            if (n0 + row < N)
+                store16(v, rh, (int)(((size_t)(n0 + row) * D + 4 * (lane % 8)) * 4));
+        }
+        const __amdgpu_buffer_rsrc_t ro =
+            make_rsrc(static_cast<uint16_t*>(a.out) + (size_t)head * BS + cw0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * i + lane / 4;
+            const uint4 v = *reinterpret_cast<const uint4*>(y_lds + row * 32 + 8 * (lane % 4));
+            if (n0 + row < N)
+                store16(v, ro, (int)(((size_t)(n0 + row) * (size_t)a.ld_out + 8 * (lane % 4)) * 2));
+        }
+    }
+}
+
 // conv outputs for a block of 16 tokens of one (sequence, 8-channel chunk); reads the old window
 template <typename ST>
 __global__ void conv_out_kernel(ConvArgs a) {
@@ -406,7 +608,14 @@ __global__ void conv_state_kernel(ConvArgs a) {
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int bs, hipStream_t s) {
     const dim3 grid((a.N + 31) / 32, a.H);
-    if (dtype == 1) {
+    if (dtype == 1 && a.u_ws != nullptr) {
+        // split: conv pass over (sequence, 8-channel chunk), then the gate pass
+        const size_t nc = (size_t)a.N * (size_t)(a.D / 8);
+        hipLaunchKernelGGL(decode_conv_kernel<uint16_t>, dim3((unsigned)((nc + 255) / 256)), dim3(256), 0, s, a);
+        const unsigned g2 = (unsigned)(((a.N + 63) / 64) * a.H * (bs / 32));
+        if (bs == 256) hipLaunchKernelGGL((decode_gate_kernel<256>), dim3(g2), dim3(64), 0, s, a);
+        else hipLaunchKernelGGL((decode_gate_kernel<128>), dim3(g2), dim3(64), 0, s, a);
+    } else if (dtype == 1) {
         const dim3 grid1((unsigned)(((a.N + 31) / 32) * a.H));  // (tile, head) placed per XCD
         if (bs == 256) hipLaunchKernelGGL((decode_bf16_kernel<256>), grid1, dim3(512), 0, s, a);
         else hipLaunchKernelGGL((decode_bf16_kernel<128>), grid1, dim3(256), 0, s, a);

@@ -52,6 +52,7 @@ struct DecodeArgs {
     const float* lambda;
     float* h;
     void* conv_state;
+    void* u_ws;  // split decode: u [N][D] in the storage dtype, or NULL for the fused kernel
     int N, D, H;
 };
 

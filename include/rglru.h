@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define RGLRU_ABI_VERSION 1
+#define RGLRU_ABI_VERSION 2
 
 enum rglru_dtype { RGLRU_F32 = 0, RGLRU_BF16 = 1 };
 
@@ -114,16 +114,29 @@ int rglru_prefill(const rglru_params *p, int32_t B, int32_t T, const void *x, co
                   void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * Bytes of the optional decode workspace for N sequences: N * D storage elements that hold
+ * the conv outputs u_t between the two passes of the split step (16-byte aligned, contents
+ * need no initialisation and are not preserved between calls).
+ */
+size_t rglru_decode_workspace_bytes(int32_t N, int32_t D, int32_t dtype);
+
+/*
  * One decode step for N sequences (one token each), updating the carried state in place.
  *   x_t, y_t, out_t  [N][D] rows with element strides ld_x, ld_y, ld_out between rows
  *                    (0 means D), so a slice [:, t] of an [N][T][D] tensor needs no copy
  *   h                [N][D] fp32 state, read and written in place
  *   conv_state       [N][3][D] last three conv inputs, oldest first, read and written in place
+ *   workspace, ws_bytes  NULL/0: one fused kernel per (32 sequences, gate head).  Otherwise a
+ *                    device buffer of at least rglru_decode_workspace_bytes(N, D, dtype): with
+ *                    bf16 storage the step runs as two kernels (conv pass into the workspace,
+ *                    then a gate pass spread over 32-channel blocks), the faster form for
+ *                    large N; with fp32 storage the workspace is not used.  Results of the two
+ *                    forms are identical.  The workspace must not overlap any other argument.
  * out_t must not overlap x_t, y_t, h or conv_state.
  */
 int rglru_decode_step(const rglru_params *p, int32_t N, const void *x_t, int64_t ld_x,
                       const void *y_t, int64_t ld_y, void *out_t, int64_t ld_out, float *h,
-                      void *conv_state, void *stream);
+                      void *conv_state, void *workspace, size_t ws_bytes, void *stream);
 
 /*
  * Conv-state update (the conv part of the path on its own).

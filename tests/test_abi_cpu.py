@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.rglru_abi_version() == 1
+    assert lib.rglru_abi_version() == 2
     for st in range(7):
         assert lib.rglru_status_string(st)
     assert lib.rglru_status_string(99) == b"unknown status"
@@ -103,13 +103,27 @@ def test_prefill_validation(lib):
 def test_decode_validation(lib):
     p = _params()
     f = lib.rglru_decode_step
-    assert f(ctypes.byref(p), 0, X, 0, Y, 0, OUT, 0, H0, C0, None) == SHAPE
-    assert f(ctypes.byref(p), 4, None, 0, Y, 0, OUT, 0, H0, C0, None) == NULL
-    assert f(ctypes.byref(p), 4, X, 100, Y, 0, OUT, 0, H0, C0, None) == SHAPE    # ld_x < D
-    assert f(ctypes.byref(p), 4, X, 513, Y, 0, OUT, 0, H0, C0, None) == UNSUP    # row alignment
-    assert f(ctypes.byref(p), 4, X, 0, Y, 0, X, 0, H0, C0, None) == ALIAS
-    assert f(ctypes.byref(p), 4, X, 0, Y, 0, OUT, 0, X + 64, C0, None) == ALIAS
-    assert f(ctypes.byref(p), 4, X, 0, Y, 0, OUT, 0, H0, Y, None) == ALIAS
+    assert f(ctypes.byref(p), 0, X, 0, Y, 0, OUT, 0, H0, C0, None, 0, None) == SHAPE
+    assert f(ctypes.byref(p), 4, None, 0, Y, 0, OUT, 0, H0, C0, None, 0, None) == NULL
+    assert f(ctypes.byref(p), 4, X, 100, Y, 0, OUT, 0, H0, C0, None, 0, None) == SHAPE  # ld_x < D
+    assert f(ctypes.byref(p), 4, X, 513, Y, 0, OUT, 0, H0, C0, None, 0, None) == UNSUP  # row alignment
+    assert f(ctypes.byref(p), 4, X, 0, Y, 0, X, 0, H0, C0, None, 0, None) == ALIAS
+    assert f(ctypes.byref(p), 4, X, 0, Y, 0, OUT, 0, X + 64, C0, None, 0, None) == ALIAS
+    assert f(ctypes.byref(p), 4, X, 0, Y, 0, OUT, 0, H0, Y, None, 0, None) == ALIAS
+
+
+def test_decode_workspace_validation(lib):
+    p = _params()
+    f = lib.rglru_decode_step
+    need = lib.rglru_decode_workspace_bytes(4, 512, 1)
+    assert need == 4 * 512 * 2
+    assert lib.rglru_decode_workspace_bytes(4, 512, 0) == 4 * 512 * 4
+    assert lib.rglru_decode_workspace_bytes(0, 512, 1) == 0
+    assert f(ctypes.byref(p), 4, X, 0, Y, 0, OUT, 0, H0, C0, WSP, need - 2, None) == WS
+    assert f(ctypes.byref(p), 4, X, 0, Y, 0, OUT, 0, H0, C0, WSP + 8, need, None) == UNSUP
+    assert f(ctypes.byref(p), 4, X, 0, Y, 0, OUT, 0, H0, C0, OUT + 16, need, None) == ALIAS
+    assert f(ctypes.byref(p), 4, X, 0, Y, 0, OUT, 0, H0, C0, C0, need, None) == ALIAS
+    assert f(ctypes.byref(p), 4, X, 0, Y, 0, OUT, 0, H0, C0, H0 + 4096, need, None) == ALIAS
 
 
 def test_conv_update_validation(lib):

@@ -175,8 +175,9 @@ def test_decode_fp32_against_oracle():
     np.testing.assert_array_equal(H.to_host(cs).astype(np.float64), rc)
 
 
+@pytest.mark.parametrize("split", [False, True])
 @pytest.mark.parametrize("D,nh,N", [(512, 2, 45), (384, 3, 33), (2560, 10, 70), (256, 1, 1)])
-def test_decode_bf16_ragged_against_oracle(D, nh, N):
+def test_decode_bf16_ragged_against_oracle(D, nh, N, split):
     """bf16 decode with biases, a carried state and N not a multiple of the 32-sequence tile,
     for both gate block sizes (256 and 128): every element against the oracle, the conv window
     bit-exact, and canary bands around h, the conv window and the outputs untouched."""
@@ -198,17 +199,52 @@ def test_decode_bf16_ragged_against_oracle(D, nh, N):
     outs = ob[pad:pad + N * T * D].view(N, T, D)
     h.copy_(H.to_dev(h0))
     cs.copy_(H.to_dev(c0))
+    ws, wsb = None, None
+    if split:
+        need = binding.rglru_decode_workspace_bytes(N, D, torch.bfloat16)
+        wsb = torch.full((need + 2 * pad,), 0x5A, dtype=torch.uint8, device="cuda")
+        ws = wsb[pad:pad + need]
     for t in range(T):
-        binding.rglru_decode_step(P, xd[:, t], yd[:, t], h, cs, out_t=outs[:, t])
+        binding.rglru_decode_step(P, xd[:, t], yd[:, t], h, cs, out_t=outs[:, t], workspace=ws)
     torch.cuda.synchronize()
+    if split:
+        assert (wsb[:pad] == 0x5A).all() and (wsb[pad + need:] == 0x5A).all()
     ro, rh, rc = H.oracle.prefill(H.oracle_params(p, w.H), x, y, h0=h0, conv0=c0)
     e_out = H.rel_l2(outs.float().cpu().numpy(), ro)
     e_h = H.rel_l2(h.cpu().numpy().astype(np.float64), rh)
-    print("decode bf16 D=%d H=%d N=%d rel-L2 out %.3e h %.3e" % (D, nh, N, e_out, e_h))
+    print("decode bf16 D=%d H=%d N=%d split=%s rel-L2 out %.3e h %.3e" % (D, nh, N, split, e_out, e_h))
     assert e_out <= H.TOL[synth.BF16] and e_h <= H.TOL[synth.BF16]
     np.testing.assert_array_equal(H.wide(H.to_host(cs)), rc)
     for t_, m in ((hb, N * D), (cb, 3 * N * D), (ob, N * T * D)):
         assert torch.isnan(t_[:pad].float()).all() and torch.isnan(t_[pad + m:].float()).all()
+
+
+@pytest.mark.parametrize("D,nh,N", [(2560, 10, 256), (2560, 10, 100), (384, 3, 70), (512, 2, 1)])
+def test_decode_split_equals_fused(D, nh, N):
+    """The split step (conv pass into the workspace, then the gate pass) and the fused kernel
+    use the same arithmetic in the same order: outputs, h and the conv window are bit-identical
+    over several steps, with biases and a carried state."""
+    from gated_linear_recurrence_amd import binding
+    T = 6
+    w = synth.Workload("dec-split", N, T, D, nh, synth.BF16, 0.9, 0.999, 0.0, 23)
+    p = synth.make_params(w, biases=True)
+    x, y = synth.make_act(w, "x"), synth.make_act(w, "y")
+    P = H.dev_params(p, w.H)
+    xd, yd = H.to_dev(x), H.to_dev(y)
+    h0 = H.to_dev(np.random.default_rng(6).normal(0, 0.5, (N, D)).astype(np.float32))
+    c0 = H.to_dev(synth.make_conv0(w, N))
+    ws = binding.make_decode_workspace(P, N)
+    runs = []
+    for workspace in (None, ws):
+        h, cs = h0.clone(), c0.clone()
+        outs = torch.empty_like(xd)
+        for t in range(T):
+            binding.rglru_decode_step(P, xd[:, t], yd[:, t], h, cs, out_t=outs[:, t],
+                                      workspace=workspace)
+        runs.append((outs, h, cs))
+    torch.cuda.synchronize()
+    (o1, h1, c1), (o2, h2, c2) = runs
+    assert torch.equal(o1, o2) and torch.equal(h1, h2) and torch.equal(c1, c2)
 
 
 # ------------------------------------------------------------------------------------------
