@@ -335,9 +335,10 @@ __global__ void __launch_bounds__(2 * BS) decode_bf16_kernel(DecodeArgs a) {
 // sequences, each pulling only its 32 channels' weights.
 // ---------------------------------------------------------------------------------------
 
-// Pass 1: u = conv([window, x_t]) for one (sequence, 8-channel chunk) per thread, written to
-// the workspace in the storage dtype (nearest-even, as the fused step rounds it), and the
-// window shifted in place.  Elementwise: no thread reads what another writes.
+// Pass 1 of the split step: u = conv([window, x_t]) for one (sequence, 8-channel chunk) per
+// thread, written to the workspace in the storage dtype (nearest-even, as the fused step
+// rounds it), and the window shifted in place (elementwise: no thread reads what another
+// writes).
 template <typename ST>
 __global__ void __launch_bounds__(256) decode_conv_kernel(DecodeArgs a) {
     using S = Store<ST>;
@@ -375,7 +376,7 @@ __global__ void __launch_bounds__(256) decode_conv_kernel(DecodeArgs a) {
         u[e] = __builtin_fmaf(w[4 * e + 3], xt[e], acc);
     }
     S::store8(static_cast<ST*>(a.u_ws) + n * D + c0, u);
-    // the stored values round-trip exactly (bf16 -> fp32 -> bf16, fp32 -> fp32)
+    // the stored values round-trip exactly (bf16 -> fp32 -> bf16)
     S::store8(cs, s1);
     S::store8(cs + D, s2);
     S::store8(cs + 2 * D, xt);
@@ -386,33 +387,46 @@ __device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, void* ld
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, byte_off, 0, 0, 0);
 }
 
-// 16-byte store through a buffer resource.
-__device__ __forceinline__ void store16(uint4 v, __amdgpu_buffer_rsrc_t r, int byte_off) {
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4d, v), r, byte_off, 0, 0);
-}
-
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
 
-// Pass 2: gates, state update and output for one wave = (64 sequences, head, 32 output
-// channels): two 32-row MFMA tiles per gate over the u rows of its 64 sequences (all bs input
-// channels of the head).  The u rows, h and y reach LDS by buffer loads with the LDS bit (u
-// with 16-byte chunks swizzled per row so the A-fragment reads spread over the banks); the
-// gate weights of the 32 channels are in VGPRs; h and out go back through LDS as 16-byte rows.
-template <int BS>
-__global__ void __launch_bounds__(64) decode_gate_kernel(DecodeArgs a) {
-    constexpr int kKSteps = BS / 16;
-    constexpr int kChunks = BS / 8;             // 16-byte chunks per u row
-    constexpr int kRowsPerInst = 64 / kChunks;  // u rows per copy instruction
-    constexpr int kCB = BS / 32;                // 32-channel blocks per head
-    __shared__ __attribute__((aligned(16))) uint16_t u_lds[64 * BS];
-    __shared__ __attribute__((aligned(16))) float h_lds[64 * 32];
-    __shared__ __attribute__((aligned(16))) uint16_t y_lds[64 * 32];
+// LDS-only barrier: the compiler's __syncthreads would also wait for outstanding global loads.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-    const int lane = threadIdx.x, ln = lane & 31, kh = lane >> 5;
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Pass 2 of the split step.  Workgroup = (64 sequences, head, 32 output channels), 4 waves of
+// 16 sequences each.  The gate weights of the 32 channels (32 rows of each gate, all BS
+// inputs) are copied once into LDS and shared by the 4 waves.  Each wave forms the transposed
+// products gates^T = W u^T with 16x16x32 MFMAs: operand A = weight rows from LDS (16 channels),
+// operand B = the u rows of its 16 sequences loaded straight from the workspace into VGPRs, so
+// the result tile holds 4 consecutive channels of one sequence per lane; h, y and out then move
+// as 16- and 8-byte vectors with no LDS round trip.  The gate parameters of the 32 channels
+// (Lambda and the two biases) arrive in LDS with the weights; wave 0 turns them into the
+// per-channel constants (nb_a, nb_x, 1/kc) beside its MFMAs and shares them through LDS.
+template <int BS>
+__global__ void __launch_bounds__(256) decode_gate_kernel(DecodeArgs a) {
+    constexpr int kKSteps = BS / 32;        // K steps of 32 inputs
+    constexpr int kRowB = BS * 2;           // bytes of one weight row
+    constexpr int kCB = BS / 32;            // 32-channel blocks per head
+    constexpr int kDma = 64 * kRowB / 4096; // 1024-byte copies (16 bytes per lane) per wave
+    // rows 0..31: gate a weights of the 32 channels, rows 32..63: gate x.  The 16-byte chunk at
+    // position p of row r holds input chunk p ^ (r & 15), so the 16 rows read by one A fragment
+    // fall on distinct banks.
+    __shared__ __attribute__((aligned(16))) uint16_t w_lds[64 * BS];
+    __shared__ __attribute__((aligned(16))) float k_lds[3 * 32];  // nb_a, nb_x, 1/kc by channel
+    // Lambda (128 bytes), gate a bias, gate x bias (64 bytes each) of the 32 channels; each copy
+    // instruction fills 1024 bytes, the lanes past the data repeating it
+    __shared__ __attribute__((aligned(16))) unsigned char p_lds[3 * 1024];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, g = lane >> 4;
     const int N = a.N;
     const size_t D = (size_t)a.D;
     // Placement: workgroups are dealt to the 8 XCDs round-robin; slots are numbered XCD by XCD
-    // and walked head-major, so the workgroups of one head share an XCD's L2.
+    // and walked head-major, so the workgroups that share a head's weights share an XCD's L2.
     const unsigned G = gridDim.x, bid = blockIdx.x;
     const unsigned xcd = bid & 7u, jx = bid >> 3, per = G >> 3, rem = G & 7u;
     const unsigned slot = xcd * per + min(xcd, rem) + jx;
@@ -421,104 +435,105 @@ __global__ void __launch_bounds__(64) decode_gate_kernel(DecodeArgs a) {
     const unsigned rs = slot % (n_blocks * kCB);
     const int n0 = (int)(rs / kCB) * 64;
     const int cw0 = (int)(rs % kCB) * 32;
-    const size_t chn = (size_t)head * BS + cw0 + ln;  // this lane's output channel
+    const int nq = n0 + 16 * wv + l16;  // this lane's sequence
+    const bool live = nq < N;
+    const size_t ns = (size_t)min(nq, N - 1);  // rows past N repeat row N-1 and are not stored
+    const size_t cbase = (size_t)head * BS + cw0;
 
-    // 1. gate weights of the 32 channels: B fragments of all K steps, both gates
-    bf16x8 wA[kKSteps], wX[kKSteps];
+    // 0. gate parameters of the 32 channels -> LDS (wave 0; an absent bias is not copied)
+    if (wv == 0) {
+        copy16_to_lds(make_rsrc(a.lambda + cbase), p_lds, 16 * (lane & 7));
+        if (a.ba) copy16_to_lds(make_rsrc(static_cast<const uint16_t*>(a.ba) + cbase), p_lds + 1024, 16 * (lane & 3));
+        if (a.bx) copy16_to_lds(make_rsrc(static_cast<const uint16_t*>(a.bx) + cbase), p_lds + 2048, 16 * (lane & 3));
+    }
+
+    // 1. weights -> LDS; each copy instruction fills 1024 / kRowB whole rows of one gate
     {
-        const uint16_t* war = static_cast<const uint16_t*>(a.wa) + chn * BS;
-        const uint16_t* wxr = static_cast<const uint16_t*>(a.wx) + chn * BS;
+        const uint16_t* wa = static_cast<const uint16_t*>(a.wa) + cbase * BS;
+        const uint16_t* wx = static_cast<const uint16_t*>(a.wx) + cbase * BS;
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(wa), rx = make_rsrc(wx);
 #pragma unroll
-        for (int kk = 0; kk < kKSteps; ++kk) {
-            const int kb = 64 * (kk >> 2) + 32 * kh + 8 * (kk & 3);
-            wA[kk] = *reinterpret_cast<const bf16x8*>(war + kb);
-            wX[kk] = *reinterpret_cast<const bf16x8*>(wxr + kb);
+        for (int i = 0; i < kDma; ++i) {
+            const int blk = i * 4 + wv;                 // 1024-byte block of w_lds
+            const int o = blk * 1024 + lane * 16;       // this lane's LDS byte offset
+            const int r = o / kRowB, p = (o % kRowB) / 16;
+            const int off = ((r & 31) * BS + 8 * (p ^ (r & 15))) * 2;
+            copy16_to_lds(blk * 1024 < 32 * kRowB ? ra : rx, w_lds + blk * 512, off);
         }
     }
-    // 2. copies into LDS (rows past N repeat row N-1; they are never stored)
+    // 2. operand B: the u row of this lane's sequence, K-slice g of every K step
+    bf16x8 ub[kKSteps];
     {
-        const __amdgpu_buffer_rsrc_t ru =
-            make_rsrc(static_cast<const uint16_t*>(a.u_ws) + (size_t)head * BS);
+        const uint16_t* ur = static_cast<const uint16_t*>(a.u_ws) + ns * D + (size_t)head * BS + 8 * g;
 #pragma unroll
-        for (int i = 0; i < 64 / kRowsPerInst; ++i) {
-            const int row = kRowsPerInst * i + lane / kChunks;
-            const int chunk = (lane % kChunks) ^ (row & 15);  // LDS position p holds chunk p ^ (row & 15)
-            const int n = min(n0 + row, N - 1);
-            copy16_to_lds(ru, u_lds + i * 512, (int)(((size_t)n * D + chunk * 8) * 2));
-        }
-        const __amdgpu_buffer_rsrc_t rh = make_rsrc(a.h + (size_t)head * BS + cw0);
+        for (int s = 0; s < kKSteps; ++s) ub[s] = *reinterpret_cast<const bf16x8*>(ur + 32 * s);
+    }
+    // 3. elementwise operands of channels cbase + 16 t + 4 g + (0..3), t = 0, 1
+    float4 hv[2];
+    uint2 yv[2], uv[2];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int n = min(n0 + 8 * i + lane / 8, N - 1);
-            copy16_to_lds(rh, h_lds + i * 256, (int)(((size_t)n * D + 4 * (lane % 8)) * 4));
+    for (int t = 0; t < 2; ++t) {
+        const size_t c = cbase + 16 * t + 4 * g;
+        hv[t] = *reinterpret_cast<const float4*>(a.h + ns * D + c);
+        yv[t] = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.y) + ns * (size_t)a.ld_y + c);
+        uv[t] = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.u_ws) + ns * D + c);
+    }
+    wait_vmem_all();  // this wave's copies and loads have landed
+    lds_barrier();    // ... and every wave's copies
+
+    // 4. gate pre-activations: acc[q] rows = channels 16 (q & 1) + (0..15) of gate q >> 1,
+    //    columns = the wave's 16 sequences; lane holds rows 4 g + (0..3) of column l16
+    f32x4 acc[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < kKSteps; ++s) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r = 16 * q + l16;
+            const bf16x8 A = *reinterpret_cast<const bf16x8*>(w_lds + r * BS + 8 * ((4 * s + g) ^ l16));
+            acc[q] = mfma16(A, ub[s], acc[q]);
         }
-        const __amdgpu_buffer_rsrc_t ry =
-            make_rsrc(static_cast<const uint16_t*>(a.y) + (size_t)head * BS + cw0);
+    }
+
+    // gate constants of channel cbase + lane, as the fused step derives them (wave 0)
+    if (wv == 0 && lane < 32) {
+        const float lam = reinterpret_cast<const float*>(p_lds)[lane];
+        const uint16_t* pb = reinterpret_cast<const uint16_t*>(p_lds + 1024);
+        k_lds[lane] = a.ba ? -bf2f(pb[lane]) * kLog2e : 0.0f;
+        k_lds[32 + lane] = a.bx ? -bf2f(pb[512 + lane]) * kLog2e : 0.0f;
+        k_lds[64 + lane] = gate_ikc(softplus_neg(lam));
+    }
+    lds_barrier();
+    float4 ka[2], kx[2], kk[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        ka[t] = *reinterpret_cast<const float4*>(k_lds + 16 * t + 4 * g);
+        kx[t] = *reinterpret_cast<const float4*>(k_lds + 32 + 16 * t + 4 * g);
+        kk[t] = *reinterpret_cast<const float4*>(k_lds + 64 + 16 * t + 4 * g);
+    }
+
+    // 5. gates, state update, output
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const float ua[4] = {bf_lo(uv[t].x), bf_hi(uv[t].x), bf_lo(uv[t].y), bf_hi(uv[t].y)};
+        const float ya[4] = {bf_lo(yv[t].x), bf_hi(yv[t].x), bf_lo(yv[t].y), bf_hi(yv[t].y)};
+        const float hs[4] = {hv[t].x, hv[t].y, hv[t].z, hv[t].w};
+        const float nba[4] = {ka[t].x, ka[t].y, ka[t].z, ka[t].w};
+        const float nbx[4] = {kx[t].x, kx[t].y, kx[t].z, kx[t].w};
+        const float ikc[4] = {kk[t].x, kk[t].y, kk[t].z, kk[t].w};
+        float hn[4], o[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int n = min(n0 + 16 * i + lane / 4, N - 1);
-            copy16_to_lds(ry, y_lds + i * 512, (int)(((size_t)n * (size_t)a.ld_y + 8 * (lane % 4)) * 2));
+            const GateOut gt = gate_fast(acc[t][i], acc[2 + t][i], nba[i], nbx[i], ikc[i], ua[i]);
+            hn[i] = __builtin_fmaf(gt.a, hs[i], gt.v);
+            o[i] = hn[i] * gelu_fast(ya[i]);
         }
-    }
-    const float lam = a.lambda[chn];
-    const uint16_t* bap = static_cast<const uint16_t*>(a.ba);
-    const uint16_t* bxp = static_cast<const uint16_t*>(a.bx);
-    const uint16_t bav = (bap ? bap : static_cast<const uint16_t*>(a.wa))[bap ? chn : 0];
-    const uint16_t bxv = (bxp ? bxp : static_cast<const uint16_t*>(a.wx))[bxp ? chn : 0];
-    wait_vmem_all();  // weights, copies and constants have landed
-
-    // 3. gate pre-activations: rows of tile mt are sequences n0 + 32 mt + (lane % 32)
-    f32x16 accA[2], accX[2];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) { accA[mt][e] = 0.0f; accX[mt][e] = 0.0f; }
-        const int m = 32 * mt + ln;
-#pragma unroll
-        for (int kk = 0; kk < kKSteps; ++kk) {
-            const int chunk = 8 * (kk >> 2) + 4 * kh + (kk & 3);
-            const bf16x8 A = *reinterpret_cast<const bf16x8*>(u_lds + m * BS + (chunk ^ (m & 15)) * 8);
-            accA[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, wA[kk], accA[mt], 0, 0, 0);
-            accX[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, wX[kk], accX[mt], 0, 0, 0);
-        }
-    }
-
-    // 4. gates, state update, output (into the LDS tiles in place)
-    const float nba = bap ? -bf2f(bav) * kLog2e : 0.0f;
-    const float nbx = bxp ? -bf2f(bxv) * kLog2e : 0.0f;
-    const float ikc = gate_ikc(softplus_neg(lam));
-    const int cu = cw0 + ln;  // channel within the head (u column)
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int m = 32 * mt + mfma_d_row(lane, j);
-            const float u = bf2f(u_lds[m * BS + (((cu >> 3) ^ (m & 15)) << 3) + (cu & 7)]);
-            const GateOut g = gate_fast(accA[mt][j], accX[mt][j], nba, nbx, ikc, u);
-            const float hn = __builtin_fmaf(g.a, h_lds[m * 32 + ln], g.v);
-            h_lds[m * 32 + ln] = hn;
-            y_lds[m * 32 + ln] = f2bf(hn * gelu_fast(bf2f(y_lds[m * 32 + ln])));
-        }
-    }
-
-    // 5. h and out back to memory, 16 bytes per lane, rows below N only
-    {
-        const __amdgpu_buffer_rsrc_t rh = make_rsrc(a.h + (size_t)head * BS + cw0);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int row = 8 * i + lane / 8;
-            const uint4 v = *reinterpret_cast<const uint4*>(h_lds + row * 32 + 4 * (lane % 8));
-            if (n0 + row < N)
-                store16(v, rh, (int)(((size_t)(n0 + row) * D + 4 * (lane % 8)) * 4));
-        }
-        const __amdgpu_buffer_rsrc_t ro =
-            make_rsrc(static_cast<uint16_t*>(a.out) + (size_t)head * BS + cw0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = 16 * i + lane / 4;
-            const uint4 v = *reinterpret_cast<const uint4*>(y_lds + row * 32 + 8 * (lane % 4));
-            if (n0 + row < N)
-                store16(v, ro, (int)(((size_t)(n0 + row) * (size_t)a.ld_out + 8 * (lane % 4)) * 2));
+        if (live) {
+            const size_t c = cbase + 16 * t + 4 * g;
+            *reinterpret_cast<float4*>(a.h + ns * D + c) = make_float4(hn[0], hn[1], hn[2], hn[3]);
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + ns * (size_t)a.ld_out + c) =
+                make_uint2(pack2bf(o[0], o[1]), pack2bf(o[2], o[3]));
         }
     }
 }
@@ -613,8 +628,8 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, int bs, hipStream_t s) 
         const size_t nc = (size_t)a.N * (size_t)(a.D / 8);
         hipLaunchKernelGGL(decode_conv_kernel<uint16_t>, dim3((unsigned)((nc + 255) / 256)), dim3(256), 0, s, a);
         const unsigned g2 = (unsigned)(((a.N + 63) / 64) * a.H * (bs / 32));
-        if (bs == 256) hipLaunchKernelGGL((decode_gate_kernel<256>), dim3(g2), dim3(64), 0, s, a);
-        else hipLaunchKernelGGL((decode_gate_kernel<128>), dim3(g2), dim3(64), 0, s, a);
+        if (bs == 256) hipLaunchKernelGGL((decode_gate_kernel<256>), dim3(g2), dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((decode_gate_kernel<128>), dim3(g2), dim3(256), 0, s, a);
     } else if (dtype == 1) {
         const dim3 grid1((unsigned)(((a.N + 31) / 32) * a.H));  // (tile, head) placed per XCD
         if (bs == 256) hipLaunchKernelGGL((decode_bf16_kernel<256>), grid1, dim3(512), 0, s, a);

@@ -9,6 +9,7 @@ namespace rglru {
 typedef __bf16 bf16x8 __attribute__((__vector_size__(16)));
 typedef __bf16 bf16x2 __attribute__((__vector_size__(4)));
 typedef float f32x16 __attribute__((__vector_size__(64)));
+typedef float f32x4 __attribute__((__vector_size__(16)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 // GELU, tanh form (Hendrycks & Gimpel 2016): gelu(y) = 0.5 y (1 + tanh(k (y + 0.044715 y^3)))
@@ -68,9 +69,10 @@ template <> struct Store<uint16_t> {
 // ---------------------------------------------------------------------------------------
 // per-channel gate constants
 // ---------------------------------------------------------------------------------------
-// softplus(-L) = -log(sigmoid(L)), evaluated without cancellation for either sign of L.
+// softplus(-L) = -log(sigmoid(L)) = max(-L, 0) + log1p(exp(-|L|)): no cancellation for
+// either sign of L, and no branch.
 __device__ __forceinline__ float softplus_neg(float lam) {
-    return lam > 0.0f ? log1pf(expf(-lam)) : (-lam + log1pf(expf(lam)));
+    return fmaxf(-lam, 0.0f) + log1pf(expf(-fabsf(lam)));
 }
 
 // 1 / kc for gate_fast, kc = -8 softplus(-Lambda) log2(e) <= 0; kc = -0 (a == 1 for every r)

@@ -130,8 +130,10 @@ size_t rglru_decode_workspace_bytes(int32_t N, int32_t D, int32_t dtype);
  *                    device buffer of at least rglru_decode_workspace_bytes(N, D, dtype): with
  *                    bf16 storage the step runs as two kernels (conv pass into the workspace,
  *                    then a gate pass spread over 32-channel blocks), the faster form for
- *                    large N; with fp32 storage the workspace is not used.  Results of the two
- *                    forms are identical.  The workspace must not overlap any other argument.
+ *                    large N; with fp32 storage the workspace is not used.  The two forms
+ *                    leave identical conv windows; h and out agree to the rounding of the
+ *                    fp32 gate sums, which the two forms accumulate in different orders.
+ *                    The workspace must not overlap any other argument.
  * out_t must not overlap x_t, y_t, h or conv_state.
  */
 int rglru_decode_step(const rglru_params *p, int32_t N, const void *x_t, int64_t ld_x,

@@ -220,10 +220,12 @@ def test_decode_bf16_ragged_against_oracle(D, nh, N, split):
 
 
 @pytest.mark.parametrize("D,nh,N", [(2560, 10, 256), (2560, 10, 100), (384, 3, 70), (512, 2, 1)])
-def test_decode_split_equals_fused(D, nh, N):
+def test_decode_split_matches_fused(D, nh, N):
     """The split step (conv pass into the workspace, then the gate pass) and the fused kernel
-    use the same arithmetic in the same order: outputs, h and the conv window are bit-identical
-    over several steps, with biases and a carried state."""
+    compute the same expressions on the same bf16 operands; only the order in which the MFMA
+    tiles sum the K = block-width products differs (16x16x32 tiles against 32x32x16).  So over
+    several steps, with biases and a carried state: the conv window is bit-identical, h agrees
+    to fp32 rounding, and each output differs by at most one bf16 rounding step."""
     from gated_linear_recurrence_amd import binding
     T = 6
     w = synth.Workload("dec-split", N, T, D, nh, synth.BF16, 0.9, 0.999, 0.0, 23)
@@ -244,7 +246,12 @@ def test_decode_split_equals_fused(D, nh, N):
         runs.append((outs, h, cs))
     torch.cuda.synchronize()
     (o1, h1, c1), (o2, h2, c2) = runs
-    assert torch.equal(o1, o2) and torch.equal(h1, h2) and torch.equal(c1, c2)
+    assert torch.equal(c1, c2)
+    torch.testing.assert_close(h2, h1, rtol=1e-5, atol=1e-5)
+    a, b = o1.float(), o2.float()
+    # one bf16 step is 2^-8 of the leading power of two, at most 2^-7 of the value
+    assert bool(((a - b).abs() <= a.abs() * 2.0 ** -7 + 1e-6).all())
+    assert float((a != b).float().mean()) < 0.01
 
 
 # ------------------------------------------------------------------------------------------
