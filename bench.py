@@ -64,7 +64,28 @@ def _to_dev(a, torch):
     return torch.from_numpy(a).cuda()
 
 
-def time_prefill(w, B, T, steps, warmup, torch, binding):
+FLUSH_BYTES = 512 << 20  # twice the 256 MB Infinity Cache
+
+
+def flushed_median_ms(torch, call, reps):
+    """Median GPU time of call() when a FLUSH_BYTES write precedes each rep, so that the call's
+    working set is no longer held in the L2 or the Infinity Cache."""
+    buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    ev = []
+    for _ in range(reps):
+        buf.zero_()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        call()
+        e1.record()
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    del buf
+    return ms[len(ms) // 2]
+
+
+def time_prefill(w, B, T, steps, warmup, torch, binding, flush=False):
     p = synth.make_params(w)
     P = binding.Params(*[_to_dev(p[k], torch) for k in ("conv_w", "conv_b", "wa", "ba", "wx",
                                                           "bx", "lambda")])
@@ -79,6 +100,12 @@ def time_prefill(w, B, T, steps, warmup, torch, binding):
     for _ in range(warmup):
         binding.rglru_prefill(P, x, y, h0, out=out, h_last=hl, conv_last=cl, workspace=ws)
     torch.cuda.synchronize()
+    if flush:
+        ms = flushed_median_ms(torch, lambda: binding.rglru_prefill(
+            P, x, y, h0, out=out, h_last=hl, conv_last=cl, workspace=ws), steps)
+        if ws.flags():
+            raise RuntimeError("prefill workspace reported error flags %#x" % ws.flags())
+        return ms
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     start.record()
@@ -93,7 +120,9 @@ def time_prefill(w, B, T, steps, warmup, torch, binding):
     return ms
 
 
-def time_decode(w, N, steps, torch, binding, split=True):
+def time_decode(w, N, steps, torch, binding, split=True, flush=False):
+    """Per-step time of `steps` decode steps: (eager us, graph us), or with flush=True the median
+    of single steps each preceded by a cache-flushing write (eager, us)."""
     p = synth.make_params(w)
     P = binding.Params(*[_to_dev(p[k], torch) for k in ("conv_w", "conv_b", "wa", "ba", "wx",
                                                           "bx", "lambda")])
@@ -112,6 +141,14 @@ def time_decode(w, N, steps, torch, binding, split=True):
 
     run()  # warm-up
     torch.cuda.synchronize()
+    if flush:
+        t = [0]
+
+        def one():
+            k = t[0] % steps
+            binding.rglru_decode_step(P, x[:, k], y[:, k], h, cs, out_t=outs[:, k], workspace=ws)
+            t[0] += 1
+        return flushed_median_ms(torch, one, 25) * 1e3
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     run()
@@ -318,19 +355,24 @@ def main():
     if not args.no_extras:
         w2 = synth.WORKLOADS[synth.PREFILL_2B]
         ms2 = time_prefill(w2, w2.B, w2.T, max(args.steps, 50), args.warmup, torch, binding)
+        ms2f = time_prefill(w2, w2.B, w2.T, 25, args.warmup, torch, binding, flush=True)
         b2 = algorithmic_bytes(w2, w2.B, w2.T)
         line["prefill_2b_single"] = {
             "workload": w2.name, "ms": ms2, "tokens·channels/s": w2.B * w2.T * w2.D / (ms2 * 1e-3),
             "algorithmic_GBs": b2 / (ms2 * 1e-3) / 1e9, "hbm_frac": b2 / (ms2 * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "note": "34 MB working set fits the 256 MB Infinity Cache; not flushed between reps"}
+            "ms_flushed": ms2f, "hbm_frac_flushed": b2 / (ms2f * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "note": "34 MB working set fits the 256 MB Infinity Cache: 'ms' is back-to-back "
+                    "launches, 'ms_flushed' the median single launch after a 512 MB write"}
         wd = synth.WORKLOADS[synth.DECODE_2B]
         eager_us, graph_us = time_decode(wd, wd.B, wd.T, torch, binding, split=True)
         f_eager, f_graph = time_decode(wd, wd.B, wd.T, torch, binding, split=False)
+        flushed_us = time_decode(wd, wd.B, wd.T, torch, binding, split=True, flush=True)
         db = decode_bytes(wd, wd.B)
         best = graph_us if graph_us is not None else eager_us
         line["decode"] = {"workload": wd.name, "form": "split (conv pass + gate pass, workspace)",
                           "us_per_step_graph": graph_us, "us_per_step_eager": eager_us,
                           "fused_us_per_step_graph": f_graph, "fused_us_per_step_eager": f_eager,
+                          "us_per_step_flushed": flushed_us,
                           "bytes_per_step": db,
                           "hbm_frac": db / (best * 1e-6) / 1e9 / HBM_PEAK_GBS}
     if not args.no_cpu_baseline:

@@ -335,24 +335,22 @@ __global__ void __launch_bounds__(2 * BS) decode_bf16_kernel(DecodeArgs a) {
 // sequences, each pulling only its 32 channels' weights.
 // ---------------------------------------------------------------------------------------
 
-// Pass 1 of the split step: u = conv([window, x_t]) for one (sequence, 8-channel chunk) per
-// thread, written to the workspace in the storage dtype (nearest-even, as the fused step
-// rounds it), and the window shifted in place (elementwise: no thread reads what another
-// writes).
-template <typename ST>
+// Pass 1 of the split step: u = conv([window, x_t]) for one 8-channel chunk of NS sequences
+// per thread (the chunk's taps and bias are loaded once and applied to all NS), written to the
+// workspace in the storage dtype (nearest-even, as the fused step rounds it), and the window
+// shifted in place (elementwise: no thread reads what another writes).  Consecutive threads
+// take consecutive chunks, so each load instruction covers whole rows.
+template <typename ST, int NS>
 __global__ void __launch_bounds__(256) decode_conv_kernel(DecodeArgs a) {
     using S = Store<ST>;
-    const int D8 = a.D >> 3;
-    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= (size_t)a.N * (size_t)D8) return;
+    const unsigned D8 = (unsigned)a.D >> 3;
+    const unsigned groups = (unsigned)((a.N + NS - 1) / NS);
+    const unsigned i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= groups * D8) return;
     const size_t D = (size_t)a.D;
-    const size_t n = i / (size_t)D8, c0 = (i % (size_t)D8) * 8;
-    ST* cs = static_cast<ST*>(a.conv_state) + n * 3 * D + c0;
-    float s0[8], s1[8], s2[8], xt[8], w[32], cb[8];
-    S::load8(cs, s0);
-    S::load8(cs + D, s1);
-    S::load8(cs + 2 * D, s2);
-    S::load8(static_cast<const ST*>(a.x) + n * (size_t)a.ld_x + c0, xt);
+    const unsigned ng = i / D8;
+    const size_t c0 = (size_t)(i - ng * D8) * 8;
+    float w[32], cb[8];
     const ST* cw = static_cast<const ST*>(a.conv_w) + c0 * 4;  // [channel][tap]
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -366,20 +364,38 @@ __global__ void __launch_bounds__(256) decode_conv_kernel(DecodeArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) cb[e] = 0.0f;
     }
-    float u[8];
+    // rows past N repeat row N-1 and are not stored
+    float s0[NS][8], s1[NS][8], s2[NS][8], xt[NS][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        // tap j multiplies x_{t-3+j}: the window holds x_{t-3}, x_{t-2}, x_{t-1}
-        float acc = __builtin_fmaf(w[4 * e + 0], s0[e], cb[e]);
-        acc = __builtin_fmaf(w[4 * e + 1], s1[e], acc);
-        acc = __builtin_fmaf(w[4 * e + 2], s2[e], acc);
-        u[e] = __builtin_fmaf(w[4 * e + 3], xt[e], acc);
+    for (int k = 0; k < NS; ++k) {
+        const size_t n = (size_t)min((int)(ng * NS) + k, a.N - 1);
+        const ST* cs = static_cast<const ST*>(a.conv_state) + n * 3 * D + c0;
+        S::load8(cs, s0[k]);
+        S::load8(cs + D, s1[k]);
+        S::load8(cs + 2 * D, s2[k]);
+        S::load8(static_cast<const ST*>(a.x) + n * (size_t)a.ld_x + c0, xt[k]);
     }
-    S::store8(static_cast<ST*>(a.u_ws) + n * D + c0, u);
-    // the stored values round-trip exactly (bf16 -> fp32 -> bf16)
-    S::store8(cs, s1);
-    S::store8(cs + D, s2);
-    S::store8(cs + 2 * D, xt);
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+        const int nk = (int)(ng * NS) + k;
+        if (nk >= a.N) break;
+        const size_t n = (size_t)nk;
+        float u[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            // tap j multiplies x_{t-3+j}: the window holds x_{t-3}, x_{t-2}, x_{t-1}
+            float acc = __builtin_fmaf(w[4 * e + 0], s0[k][e], cb[e]);
+            acc = __builtin_fmaf(w[4 * e + 1], s1[k][e], acc);
+            acc = __builtin_fmaf(w[4 * e + 2], s2[k][e], acc);
+            u[e] = __builtin_fmaf(w[4 * e + 3], xt[k][e], acc);
+        }
+        S::store8(static_cast<ST*>(a.u_ws) + n * D + c0, u);
+        // the stored values round-trip exactly (bf16 -> fp32 -> bf16)
+        ST* cs = static_cast<ST*>(a.conv_state) + n * 3 * D + c0;
+        S::store8(cs, s1[k]);
+        S::store8(cs + D, s2[k]);
+        S::store8(cs + 2 * D, xt[k]);
+    }
 }
 
 // Global -> LDS copy of 16 bytes per lane (buffer load with the LDS bit).
@@ -621,12 +637,16 @@ __global__ void conv_state_kernel(ConvArgs a) {
 
 }  // namespace
 
+constexpr int kConvSeqs = 1;     // sequences per thread in the split step's conv pass
+constexpr int kConvBlock = 256;  // threads per workgroup of the conv pass
+
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int bs, hipStream_t s) {
     const dim3 grid((a.N + 31) / 32, a.H);
     if (dtype == 1 && a.u_ws != nullptr) {
         // split: conv pass over (sequence, 8-channel chunk), then the gate pass
-        const size_t nc = (size_t)a.N * (size_t)(a.D / 8);
-        hipLaunchKernelGGL(decode_conv_kernel<uint16_t>, dim3((unsigned)((nc + 255) / 256)), dim3(256), 0, s, a);
+        const size_t nc = (size_t)((a.N + kConvSeqs - 1) / kConvSeqs) * (size_t)(a.D / 8);
+        hipLaunchKernelGGL((decode_conv_kernel<uint16_t, kConvSeqs>),
+                           dim3((unsigned)((nc + kConvBlock - 1) / kConvBlock)), dim3(kConvBlock), 0, s, a);
         const unsigned g2 = (unsigned)(((a.N + 63) / 64) * a.H * (bs / 32));
         if (bs == 256) hipLaunchKernelGGL((decode_gate_kernel<256>), dim3(g2), dim3(256), 0, s, a);
         else hipLaunchKernelGGL((decode_gate_kernel<128>), dim3(g2), dim3(256), 0, s, a);

@@ -57,6 +57,9 @@ __device__ float look_back(unsigned long long* wself, size_t wstride, int seg, u
                            bool& pred_inclusive) {
     pred_inclusive = true;
     if (w_ready(w1) && w_inclusive(w1)) return w_B(w1);
+    // the stride goes through an opaque SGPR copy: the window offsets are then formed here with
+    // scalar ops, not hoisted out of the caller's loop (where they would be spilled to VGPR lanes)
+    asm volatile("" : "+s"(wstride));
     const int n = seg < kWindow ? seg : kWindow;
     bool published = !publish_aggregate;
     for (unsigned it = 0;; ++it) {
@@ -686,25 +689,32 @@ prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
             for (int k = 0; k < C::kTok + 3; ++k) xr[k] = x_lds32[ixr + k * 64];
             constexpr int kTokPerStep = C::kTok / C::kKSteps;  // conv tokens per MFMA k-step
+            // the row swizzle of this wave's tokens is a compile-time constant in each branch,
+            // so every u store has an immediate offset
+            auto tile0 = [&](auto sw) {
+                constexpr int kSw = decltype(sw)::value;
 #pragma unroll
-            for (int kk = 0; kk < C::kKSteps; ++kk) {
-                const bf16x8 A = *reinterpret_cast<const bf16x8*>(u_lds + ia0 + 64 * (kk >> 2) + 8 * (kk & 3));
-                accB[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, wA[kk], accB[0], 0, 0, 0);
-                accP[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, wX[kk], accP[0], 0, 0, 0);
+                for (int kk = 0; kk < C::kKSteps; ++kk) {
+                    const bf16x8 A = *reinterpret_cast<const bf16x8*>(u_lds + ia0 + 64 * (kk >> 2) + 8 * (kk & 3));
+                    accB[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, wA[kk], accB[0], 0, 0, 0);
+                    accP[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, wX[kk], accP[0], 0, 0, 0);
 #pragma unroll
-                for (int s2 = 0; s2 < kTokPerStep; ++s2) {
-                    const int k = kk * kTokPerStep + s2;
-                    // (x_{t-3}, x_{t-2}) and (x_{t-1}, x_t) of each of the two channels
-                    const uint32_t p0a = __builtin_amdgcn_perm(xr[k + 1], xr[k], 0x05040100u);
-                    const uint32_t p0b = __builtin_amdgcn_perm(xr[k + 1], xr[k], 0x07060302u);
-                    const uint32_t p2a = __builtin_amdgcn_perm(xr[k + 3], xr[k + 2], 0x05040100u);
-                    const uint32_t p2b = __builtin_amdgcn_perm(xr[k + 3], xr[k + 2], 0x07060302u);
-                    const float u0 = dot2bf(wq.y, p2a, dot2bf(wq.x, p0a, cb.x));
-                    const float u1 = dot2bf(wq.w, p2b, dot2bf(wq.z, p0b, cb.y));
-                    u_lds32[iuw + ((k ^ csw) * kRow) / 2] = pack2bf(u0, u1);
+                    for (int s2 = 0; s2 < kTokPerStep; ++s2) {
+                        const int k = kk * kTokPerStep + s2;
+                        // (x_{t-3}, x_{t-2}) and (x_{t-1}, x_t) of each of the two channels
+                        const uint32_t p0a = __builtin_amdgcn_perm(xr[k + 1], xr[k], 0x05040100u);
+                        const uint32_t p0b = __builtin_amdgcn_perm(xr[k + 1], xr[k], 0x07060302u);
+                        const uint32_t p2a = __builtin_amdgcn_perm(xr[k + 3], xr[k + 2], 0x05040100u);
+                        const uint32_t p2b = __builtin_amdgcn_perm(xr[k + 3], xr[k + 2], 0x07060302u);
+                        const float u0 = dot2bf(wq.y, p2a, dot2bf(wq.x, p0a, cb.x));
+                        const float u1 = dot2bf(wq.w, p2b, dot2bf(wq.z, p0b, cb.y));
+                        u_lds32[iuw + ((k ^ kSw) * kRow) / 2] = pack2bf(u0, u1);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            };
+            if (sopaque(csw) != 0) tile0(std::integral_constant<int, 12>{});
+            else tile0(std::integral_constant<int, 0>{});
         }
         // Copies go out only here, after this iteration's last LDS store before the wait in
         // step 4 (an LDS store issued while a global->LDS copy is in flight waits for the copy):
