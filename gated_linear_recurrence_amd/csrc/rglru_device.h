@@ -102,8 +102,10 @@ __device__ __forceinline__ GateOut gate_fast(float sa, float sx, float nba, floa
     const float i = __builtin_amdgcn_rcpf(1.0f + ei);
     // r -> 0 (er -> inf) gives rcp(-inf) = -0 and a = 1
     const float a = __builtin_amdgcn_exp2f(__builtin_amdgcn_rcpf(__builtin_fmaf(er, ikc, ikc)));
-    // a <= 1 in exact arithmetic; the clamp guards the 1-ulp error of the hardware exp2
-    const float m = __builtin_amdgcn_sqrtf(fmaxf(__builtin_fmaf(-a, a, 1.0f), 0.0f));
+    // a <= 1 in exact arithmetic; when the 1-ulp error of the hardware exp2 puts a just above
+    // 1, 1 - a^2 is a rounding-sized negative number and |1 - a^2| is as good an estimate of
+    // the true (tiny, non-negative) value as 0.  The absolute value is a free operand modifier.
+    const float m = __builtin_amdgcn_sqrtf(fabsf(__builtin_fmaf(-a, a, 1.0f)));
     return {a, m * (i * u)};
 }
 
