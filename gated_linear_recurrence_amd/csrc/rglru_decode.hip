@@ -412,9 +412,10 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Pass 2 of the split step.  Workgroup = (64 sequences, head, 32 output channels), 4 waves of
-// 16 sequences each.  The gate weights of the 32 channels (32 rows of each gate, all BS
-// inputs) are copied once into LDS and shared by the 4 waves.  Each wave forms the transposed
+// Pass 2 of the split step.  Workgroup = (16 W sequences, head, 32 output channels), W waves of
+// 16 sequences each (W = blockDim.x / 64, chosen at launch so that the busiest CU pulls the
+// fewest bytes).  The gate weights of the 32 channels (32 rows of each gate, all BS inputs)
+// are copied once into LDS and shared by the W waves.  Each wave forms the transposed
 // products gates^T = W u^T with 16x16x32 MFMAs: operand A = weight rows from LDS (16 channels),
 // operand B = the u rows of its 16 sequences loaded straight from the workspace into VGPRs, so
 // the result tile holds 4 consecutive channels of one sequence per lane; h, y and out then move
@@ -422,11 +423,11 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 // (Lambda and the two biases) arrive in LDS with the weights; wave 0 turns them into the
 // per-channel constants (nb_a, nb_x, 1/kc) beside its MFMAs and shares them through LDS.
 template <int BS>
-__global__ void __launch_bounds__(256) decode_gate_kernel(DecodeArgs a) {
-    constexpr int kKSteps = BS / 32;        // K steps of 32 inputs
-    constexpr int kRowB = BS * 2;           // bytes of one weight row
-    constexpr int kCB = BS / 32;            // 32-channel blocks per head
-    constexpr int kDma = 64 * kRowB / 4096; // 1024-byte copies (16 bytes per lane) per wave
+__global__ void __launch_bounds__(512) decode_gate_kernel(DecodeArgs a) {
+    constexpr int kKSteps = BS / 32;         // K steps of 32 inputs
+    constexpr int kRowB = BS * 2;            // bytes of one weight row
+    constexpr int kCB = BS / 32;             // 32-channel blocks per head
+    constexpr int kBlocks = 64 * kRowB / 1024;  // 1024-byte copies (16 bytes per lane) of the weights
     // rows 0..31: gate a weights of the 32 channels, rows 32..63: gate x.  The 16-byte chunk at
     // position p of row r holds input chunk p ^ (r & 15), so the 16 rows read by one A fragment
     // fall on distinct banks.
@@ -438,6 +439,7 @@ __global__ void __launch_bounds__(256) decode_gate_kernel(DecodeArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nw = (int)(blockDim.x >> 6);  // waves, 16 sequences each
     const int l16 = lane & 15, g = lane >> 4;
     const int N = a.N;
     const size_t D = (size_t)a.D;
@@ -446,11 +448,14 @@ __global__ void __launch_bounds__(256) decode_gate_kernel(DecodeArgs a) {
     const unsigned G = gridDim.x, bid = blockIdx.x;
     const unsigned xcd = bid & 7u, jx = bid >> 3, per = G >> 3, rem = G & 7u;
     const unsigned slot = xcd * per + min(xcd, rem) + jx;
-    const unsigned n_blocks = (unsigned)((N + 63) / 64);
+    const unsigned n_blocks = (unsigned)((N + 16 * nw - 1) / (16 * nw));
     const int head = (int)(slot / (n_blocks * kCB));
     const unsigned rs = slot % (n_blocks * kCB);
-    const int n0 = (int)(rs / kCB) * 64;
+    const int n0 = (int)(rs / kCB) * 16 * nw;
     const int cw0 = (int)(rs % kCB) * 32;
+    // a wave whose 16 sequences all lie past N loads and stores nothing (it still copies its
+    // share of the weights and meets both barriers); wave 0 is always live
+    const bool wave_live = n0 + 16 * wv < N;
     const int nq = n0 + 16 * wv + l16;  // this lane's sequence
     const bool live = nq < N;
     const size_t ns = (size_t)min(nq, N - 1);  // rows past N repeat row N-1 and are not stored
@@ -468,9 +473,7 @@ __global__ void __launch_bounds__(256) decode_gate_kernel(DecodeArgs a) {
         const uint16_t* wa = static_cast<const uint16_t*>(a.wa) + cbase * BS;
         const uint16_t* wx = static_cast<const uint16_t*>(a.wx) + cbase * BS;
         const __amdgpu_buffer_rsrc_t ra = make_rsrc(wa), rx = make_rsrc(wx);
-#pragma unroll
-        for (int i = 0; i < kDma; ++i) {
-            const int blk = i * 4 + wv;                 // 1024-byte block of w_lds
+        for (int blk = wv; blk < kBlocks; blk += nw) {  // 1024-byte block of w_lds
             const int o = blk * 1024 + lane * 16;       // this lane's LDS byte offset
             const int r = o / kRowB, p = (o % kRowB) / 16;
             const int off = ((r & 31) * BS + 8 * (p ^ (r & 15))) * 2;
@@ -479,20 +482,20 @@ __global__ void __launch_bounds__(256) decode_gate_kernel(DecodeArgs a) {
     }
     // 2. operand B: the u row of this lane's sequence, K-slice g of every K step
     bf16x8 ub[kKSteps];
-    {
+    float4 hv[2];
+    uint2 yv[2], uv[2];
+    if (wave_live) {
         const uint16_t* ur = static_cast<const uint16_t*>(a.u_ws) + ns * D + (size_t)head * BS + 8 * g;
 #pragma unroll
         for (int s = 0; s < kKSteps; ++s) ub[s] = *reinterpret_cast<const bf16x8*>(ur + 32 * s);
-    }
-    // 3. elementwise operands of channels cbase + 16 t + 4 g + (0..3), t = 0, 1
-    float4 hv[2];
-    uint2 yv[2], uv[2];
+        // 3. elementwise operands of channels cbase + 16 t + 4 g + (0..3), t = 0, 1
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const size_t c = cbase + 16 * t + 4 * g;
-        hv[t] = *reinterpret_cast<const float4*>(a.h + ns * D + c);
-        yv[t] = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.y) + ns * (size_t)a.ld_y + c);
-        uv[t] = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.u_ws) + ns * D + c);
+        for (int t = 0; t < 2; ++t) {
+            const size_t c = cbase + 16 * t + 4 * g;
+            hv[t] = *reinterpret_cast<const float4*>(a.h + ns * D + c);
+            yv[t] = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.y) + ns * (size_t)a.ld_y + c);
+            uv[t] = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.u_ws) + ns * D + c);
+        }
     }
     wait_vmem_all();  // this wave's copies and loads have landed
     lds_barrier();    // ... and every wave's copies
@@ -502,13 +505,15 @@ __global__ void __launch_bounds__(256) decode_gate_kernel(DecodeArgs a) {
     f32x4 acc[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    if (wave_live) {
 #pragma unroll
-    for (int s = 0; s < kKSteps; ++s) {
+        for (int s = 0; s < kKSteps; ++s) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int r = 16 * q + l16;
-            const bf16x8 A = *reinterpret_cast<const bf16x8*>(w_lds + r * BS + 8 * ((4 * s + g) ^ l16));
-            acc[q] = mfma16(A, ub[s], acc[q]);
+            for (int q = 0; q < 4; ++q) {
+                const int r = 16 * q + l16;
+                const bf16x8 A = *reinterpret_cast<const bf16x8*>(w_lds + r * BS + 8 * ((4 * s + g) ^ l16));
+                acc[q] = mfma16(A, ub[s], acc[q]);
+            }
         }
     }
 
@@ -520,7 +525,8 @@ __global__ void __launch_bounds__(256) decode_gate_kernel(DecodeArgs a) {
         k_lds[32 + lane] = a.bx ? -bf2f(pb[512 + lane]) * kLog2e : 0.0f;
         k_lds[64 + lane] = gate_ikc(softplus_neg(lam));
     }
-    lds_barrier();
+    lds_barrier();  // the last barrier
+    if (!wave_live) return;
     float4 ka[2], kx[2], kk[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -637,6 +643,27 @@ __global__ void conv_state_kernel(ConvArgs a) {
 
 }  // namespace
 
+// Waves (16 sequences each) per workgroup of the gate pass.  Each workgroup pulls one weight
+// slice (64 rows of bs inputs) and, per live wave, 16 u rows plus the wave's h, y and out
+// (about 14 bytes per element); the choice minimises the bytes of the busiest CU, i.e.
+// ceil(workgroups / CUs) times the bytes of one workgroup, preferring fewer waves on ties.
+static int gate_waves(int N, int H, int bs, int ncu) {
+    int best = 1;
+    double best_cost = 0.0;
+    for (int nw = 1; nw <= 8; ++nw) {
+        const long long blocks = (N + 16 * nw - 1) / (16 * nw);
+        const long long wgs = blocks * H * (bs / 32);
+        const int live = min(nw, (N + 15) / 16);
+        const double per_wg = 128.0 * bs + live * (32.0 * bs + 16.0 * 32.0 * 14.0);
+        const double cost = (double)((wgs + ncu - 1) / ncu) * per_wg;
+        if (nw == 1 || cost < best_cost) {
+            best = nw;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
+
 constexpr int kConvSeqs = 1;     // sequences per thread in the split step's conv pass
 constexpr int kConvBlock = 256;  // threads per workgroup of the conv pass
 
@@ -647,9 +674,10 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, int bs, hipStream_t s) 
         const size_t nc = (size_t)((a.N + kConvSeqs - 1) / kConvSeqs) * (size_t)(a.D / 8);
         hipLaunchKernelGGL((decode_conv_kernel<uint16_t, kConvSeqs>),
                            dim3((unsigned)((nc + kConvBlock - 1) / kConvBlock)), dim3(kConvBlock), 0, s, a);
-        const unsigned g2 = (unsigned)(((a.N + 63) / 64) * a.H * (bs / 32));
-        if (bs == 256) hipLaunchKernelGGL((decode_gate_kernel<256>), dim3(g2), dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((decode_gate_kernel<128>), dim3(g2), dim3(256), 0, s, a);
+        const int nw = gate_waves(a.N, a.H, bs, device_cu_count());
+        const unsigned g2 = (unsigned)(((a.N + 16 * nw - 1) / (16 * nw)) * a.H * (bs / 32));
+        if (bs == 256) hipLaunchKernelGGL((decode_gate_kernel<256>), dim3(g2), dim3(64 * nw), 0, s, a);
+        else hipLaunchKernelGGL((decode_gate_kernel<128>), dim3(g2), dim3(64 * nw), 0, s, a);
     } else if (dtype == 1) {
         const dim3 grid1((unsigned)(((a.N + 31) / 32) * a.H));  // (tile, head) placed per XCD
         if (bs == 256) hipLaunchKernelGGL((decode_bf16_kernel<256>), grid1, dim3(512), 0, s, a);

@@ -65,6 +65,7 @@ struct ConvArgs {
     int N, T, D;
 };
 
+int device_cu_count();  // compute units of the current device (cached)
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int bs, hipStream_t s);
 hipError_t launch_prefill_empty(const PrefillArgs& a, int dtype, hipStream_t s);
 hipError_t launch_workspace_init(void* ws, size_t bytes, hipStream_t s);

@@ -898,7 +898,7 @@ __global__ void workspace_init_kernel(unsigned long long* p, size_t n_words) {
 }  // namespace
 
 // Compute units of the current device (cached per device).
-static int device_cu_count() {
+int device_cu_count() {
     static std::atomic<int> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
