@@ -3,10 +3,14 @@
 // generate sequences of any length: page "Gemma 詳解：RecurrentGemma 架構", sections
 // "模型寬度與 RNN 寬度" and "區域注意力視窗大小").
 //
-// Workgroup = (tile of 32 sequences, gate head).  The conv runs over [window, x_t] and shifts
-// the window; u goes to LDS; the gate projections of the 32 sequences are one 32-row MFMA
-// tile per wave (32 output channels); then h <- a h + sqrt(1-a^2) i u and
-// out = h * gelu_tanh(y_t).
+// Two forms of the bf16 step compute the same expressions:
+//  - fused (no workspace): workgroup = (tile of 32 sequences, gate head).  The conv runs over
+//    [window, x_t] and shifts the window; u goes to LDS; the gate projections of the 32
+//    sequences are one 32-row MFMA tile per wave (32 output channels); then
+//    h <- a h + sqrt(1-a^2) i u and out = h * gelu_tanh(y_t).
+//  - split (with a workspace): a conv pass writes u and shifts the window, then a gate pass
+//    spreads each head's output channels over many workgroups (see the two kernels below).
+// fp32 storage uses the fused decomposition with precise gate math.
 #include <type_traits>
 
 #include "rglru_device.h"
@@ -15,8 +19,6 @@
 namespace rglru {
 
 namespace {
-
-typedef unsigned int u32x4d __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0xffffffff, 0x00020000);

@@ -85,6 +85,7 @@ typedef struct rglru_params {
 } rglru_params;
 
 /*
+ * Workspace management (no passage of the pages: these exist for the chunked scan's carries).
  * Bytes of device workspace rglru_prefill needs for this shape (0 on invalid shapes).
  * The workspace holds the cross-workgroup carry words of the time-segmented scan.  Before
  * its first use a workspace must be initialised once with rglru_prefill_workspace_init;
@@ -99,6 +100,8 @@ int rglru_prefill_workspace_init(void *workspace, size_t ws_bytes, void *stream)
 
 /*
  * Prefill over T tokens (the time-chunked scan).
+ * Operation: the whole block path above over a prompt, page "Gemma 詳解：RecurrentGemma 架構",
+ * section "含遞迴區塊的殘差區塊" (Conv1d -> RG-LRU branch times the GELU branch).
  *   x, y      [B][T][D]  inputs (storage dtype)
  *   out       [B][T][D]  h_t * gelu_tanh(y_t), rounded to the storage dtype (nearest-even)
  *   h0        [B][D] fp32 initial state, or NULL for zeros
@@ -122,6 +125,9 @@ size_t rglru_decode_workspace_bytes(int32_t N, int32_t D, int32_t dtype);
 
 /*
  * One decode step for N sequences (one token each), updating the carried state in place.
+ * Operation: the same path for a single token, carrying the fixed-size state (h and the conv
+ * window) that the page "Gemma 詳解：RecurrentGemma 架構" describes in sections
+ * "模型寬度與 RNN 寬度" and "區域注意力視窗大小".
  *   x_t, y_t, out_t  [N][D] rows with element strides ld_x, ld_y, ld_out between rows
  *                    (0 means D), so a slice [:, t] of an [N][T][D] tensor needs no copy
  *   h                [N][D] fp32 state, read and written in place
@@ -147,6 +153,8 @@ int rglru_decode_step(const rglru_params *p, int32_t N, const void *x_t, int64_t
  *   conv_out   [N][T_new][D] the conv outputs u_t (storage dtype, nearest-even), or NULL
  * Only p->D, p->dtype, p->conv_w and p->conv_b are read.  conv_out must not overlap x_new.
  */
+/* Operation: the depthwise Conv1d (kernel 4, padding 3, groups D) of the module printout on the
+ * page "Gemma 詳解：RecurrentGemma 架構", kept causal, and its three-token state. */
 int conv1d_state_update(const rglru_params *p, int32_t N, int32_t T_new, const void *x_new,
                         void *conv_state, void *conv_out, void *stream);
 
