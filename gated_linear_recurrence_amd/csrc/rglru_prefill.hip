@@ -624,16 +624,11 @@ prefill_bf16_kernel(PrefillArgs a) {
     }
 
     // ---- prologue: tickets for this workgroup's first three segments; conv of the first ----
-    if (tid0 == 0) {
-        s_tk[0] = atomicAdd(tctr, 1u);
-        s_tk[1] = atomicAdd(tctr, 1u);
-        s_tk[2] = atomicAdd(tctr, 1u);
-    }
-    __syncthreads();  // tables and tickets
+    if (tid0 == 0) s_tk[0] = atomicAdd(tctr, 1u);
+    __syncthreads();  // tables and the first ticket
     // tickets are workgroup-uniform: kept in SGPRs (buffer resources are built from them)
     unsigned cur = __builtin_amdgcn_readfirstlane(s_tk[0]);
-    unsigned n1 = __builtin_amdgcn_readfirstlane(s_tk[1]);
-    unsigned n2 = __builtin_amdgcn_readfirstlane(s_tk[2]);
+    unsigned n1, n2;
     {
         const int lane = tid0 & 63;
         dma_x_rows(a, head, BS, pw, tg, cur, n_tk, lane, x_lds + xw0);
@@ -651,7 +646,17 @@ prefill_bf16_kernel(PrefillArgs a) {
                                     dot2bf(wq.z, __builtin_amdgcn_perm(x1, x0, 0x07060302u), cb.y));
             u_lds32[(lds_row(tg * C::kTok + k) * kRow) / 2 + cp] = pack2bf(u0, u1);
         }
-        wait_lds_all();
+        // The next two tickets are taken only now, a conv after the first: by then every
+        // workgroup of the head has normally taken its first ticket, so a head with few
+        // segments spreads them over all its workgroups instead of three each to the first
+        // workgroups to arrive.  (No copy into LDS is in flight here.)
+        if (tid0 == 0) {
+            s_tk[1] = atomicAdd(tctr, 1u);
+            s_tk[2] = atomicAdd(tctr, 1u);
+        }
+        lds_barrier();  // the two tickets are visible; this wave's conv reads of x are complete
+        n1 = __builtin_amdgcn_readfirstlane(s_tk[1]);
+        n2 = __builtin_amdgcn_readfirstlane(s_tk[2]);
         dma_x_rows(a, head, BS, pw, tg, n1, n_tk, lane, x_lds + xw0);
     }
     unsigned pending = 0;  // taken once per iteration, published at the iteration's barrier
