@@ -20,6 +20,24 @@ namespace rglru {
 
 namespace {
 
+constexpr float kLn2 = 0.6931471805599453f;
+
+// softplus(-L) from hardware exp2/log2 (a few ulp; ~20 instructions instead of the library
+// expf/log1pf).  log1p(e) is formed as log(1 + e) * e / ((1 + e) - 1), which cancels the
+// rounding of 1 + e (Goldberg's correction), so small e keeps full relative accuracy.
+__device__ __forceinline__ float softplus_neg_fast(float lam) {
+    const float e = __builtin_amdgcn_exp2f(-fabsf(lam) * kLog2e);  // exp(-|L|) in (0, 1]
+    const float w = 1.0f + e;
+    const float d = w - 1.0f;
+    const float l1p = d == 0.0f ? e : __builtin_amdgcn_logf(w) * kLn2 * (e * __builtin_amdgcn_rcpf(d));
+    return fmaxf(-lam, 0.0f) + l1p;
+}
+
+// gate_ikc with the hardware reciprocal (1 ulp); rcp(-0) = -inf also maps to -FLT_MAX.
+__device__ __forceinline__ float gate_ikc_fast(float sp_neg) {
+    return fmaxf(__builtin_amdgcn_rcpf(-8.0f * sp_neg * kLog2e), -3.4028234663852886e38f);
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0xffffffff, 0x00020000);
 }
@@ -519,13 +537,15 @@ __global__ void __launch_bounds__(512) decode_gate_kernel(DecodeArgs a) {
         }
     }
 
-    // gate constants of channel cbase + lane, as the fused step derives them (wave 0)
+    // gate constants of channel cbase + lane (wave 0), from hardware exp2/log2/rcp: a few ulp
+    // from the library forms of the fused step, and short enough that the other waves hardly
+    // wait for them at the barrier below
     if (wv == 0 && lane < 32) {
         const float lam = reinterpret_cast<const float*>(p_lds)[lane];
         const uint16_t* pb = reinterpret_cast<const uint16_t*>(p_lds + 1024);
         k_lds[lane] = a.ba ? -bf2f(pb[lane]) * kLog2e : 0.0f;
         k_lds[32 + lane] = a.bx ? -bf2f(pb[512 + lane]) * kLog2e : 0.0f;
-        k_lds[64 + lane] = gate_ikc(softplus_neg(lam));
+        k_lds[64 + lane] = gate_ikc_fast(softplus_neg_fast(lam));
     }
     lds_barrier();  // the last barrier
     if (!wave_live) return;
