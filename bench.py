@@ -56,6 +56,33 @@ def decode_bytes(w: synth.Workload, N: int) -> int:
         D * 4 * e + D * 4
 
 
+def conv_update_bytes(w: synth.Workload, N: int, T: int) -> int:
+    """HBM bytes of one conv1d_state_update with outputs: x read and u written once, the
+    window read and written, the taps and bias."""
+    e = 2 if w.dtype == synth.BF16 else 4
+    return 2 * N * T * w.D * e + 2 * N * 3 * w.D * e + w.D * 5 * e
+
+
+def time_conv_update(w, steps, torch, binding):
+    """ms per conv1d_state_update (outputs for all T tokens, window update) on w's shape."""
+    p = synth.make_params(w)
+    P = binding.Params(*[_to_dev(p[k], torch) for k in ("conv_w", "conv_b", "wa", "ba", "wx",
+                                                          "bx", "lambda")])
+    x = _to_dev(synth.make_act(w, "x"), torch)
+    cs = torch.zeros((w.B, 3, w.D), dtype=x.dtype, device="cuda")
+    out = torch.empty_like(x)
+    for _ in range(2):
+        binding.conv1d_state_update(P, x, cs, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        binding.conv1d_state_update(P, x, cs, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def _to_dev(a, torch):
     if a is None:
         return None
@@ -375,6 +402,12 @@ def main():
                           "us_per_step_flushed": flushed_us,
                           "bytes_per_step": db,
                           "hbm_frac": db / (best * 1e-6) / 1e9 / HBM_PEAK_GBS}
+        msc = time_conv_update(w, max(args.steps, 10), torch, binding)
+        cb = conv_update_bytes(w, w.B, w.T)
+        line["conv1d_state_update"] = {
+            "workload": w.name + " (conv outputs for every token, window update)", "ms": msc,
+            "algorithmic_bytes": cb, "algorithmic_GBs": cb / (msc * 1e-3) / 1e9,
+            "hbm_frac": cb / (msc * 1e-3) / 1e9 / HBM_PEAK_GBS}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)

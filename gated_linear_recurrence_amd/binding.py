@@ -249,13 +249,17 @@ def rglru_decode_step(p: Params, x_t, y_t, h, conv_state, out_t=None, workspace=
     return out_t
 
 
-def conv1d_state_update(p: Params, x_new, conv_state, want_out: bool = True):
-    """x_new [N, T_new, D]; conv_state [N, 3, D] updated in place.  Returns conv_out or None."""
+def conv1d_state_update(p: Params, x_new, conv_state, want_out: bool = True, out=None):
+    """x_new [N, T_new, D]; conv_state [N, 3, D] updated in place.  Returns conv_out (written
+    into `out` when given) or None when want_out is False."""
     lib = load_library()
     N, T_new, D = x_new.shape
     _need(x_new, "x_new", p.dtype, (N, T_new, p.D), p.device)
     _need(conv_state, "conv_state", p.dtype, (N, 3, D), p.device)
-    out = torch.empty_like(x_new) if want_out else None
+    if out is not None:
+        _need(out, "out", p.dtype, (N, T_new, D), p.device)
+    elif want_out:
+        out = torch.empty_like(x_new)
     st = lib.conv1d_state_update(ctypes.byref(p.c), N, T_new, _ptr(x_new), _ptr(conv_state),
                                  _ptr(out), _stream())
     _check(lib, st, "conv1d_state_update")

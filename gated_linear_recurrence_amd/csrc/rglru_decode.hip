@@ -582,11 +582,18 @@ __global__ void __launch_bounds__(512) decode_gate_kernel(DecodeArgs a) {
     }
 }
 
-// conv outputs for a block of 16 tokens of one (sequence, 8-channel chunk); reads the old window
+// conv outputs for a block of kConvTB tokens of one (sequence, 8-channel chunk); reads the old
+// window.  All input rows of the block (3 before it, kConvTB in it) are loaded before any is
+// used, so a thread has one memory round trip, not one per token.
+template <typename ST> struct ConvBlock { static constexpr int kTB = 16; };  // bf16: 19 raw rows = 76 VGPRs
+template <> struct ConvBlock<float> { static constexpr int kTB = 8; };       // fp32: 11 raw rows = 88 VGPRs
+
 template <typename ST>
-__global__ void conv_out_kernel(ConvArgs a) {
+__global__ void __launch_bounds__(256) conv_out_kernel(ConvArgs a) {
     using S = Store<ST>;
-    constexpr int kTB = 16;
+    constexpr int kTB = ConvBlock<ST>::kTB;
+    constexpr int kRows = kTB + 3;
+    constexpr int kWords = 8 * (int)sizeof(ST) / 16;  // 16-byte words per 8-element row chunk
     const int chunks = a.D / 8;
     const int tblocks = (a.T + kTB - 1) / kTB;
     const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -597,6 +604,18 @@ __global__ void conv_out_kernel(ConvArgs a) {
     const size_t D = (size_t)a.D, c0 = (size_t)cg * 8;
     const ST* x = static_cast<const ST*>(a.x);
     const ST* cs = static_cast<const ST*>(a.conv_state);
+    const int tbeg = tb * kTB;
+    // rows tbeg-3 .. tbeg+kTB-1: before token 0 from the window, past T-1 the row T-1 again
+    // (those outputs are not stored)
+    uint4 raw[kRows][kWords];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+        const int t = tbeg - 3 + r;
+        const ST* src = t >= 0 ? x + ((size_t)n * a.T + min(t, a.T - 1)) * D + c0
+                               : cs + ((size_t)n * 3 + 3 + t) * D + c0;
+#pragma unroll
+        for (int q = 0; q < kWords; ++q) raw[r][q] = reinterpret_cast<const uint4*>(src)[q];
+    }
     float w[4][8], cb[8];
     {
         float tmp[8];
@@ -613,19 +632,16 @@ __global__ void conv_out_kernel(ConvArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) cb[e] = 0.0f;
     }
+    auto widen = [&](int r, float (&v)[8]) { S::load8(reinterpret_cast<const ST*>(&raw[r][0]), v); };
     float r0[8], r1[8], r2[8];
-    auto row = [&](int t, float (&v)[8]) {
-        if (t >= 0) S::load8(x + ((size_t)n * a.T + t) * D + c0, v);
-        else S::load8(cs + ((size_t)n * 3 + 3 + t) * D + c0, v);
-    };
-    const int tbeg = tb * kTB;
-    row(tbeg - 3, r0);
-    row(tbeg - 2, r1);
-    row(tbeg - 1, r2);
+    widen(0, r0);
+    widen(1, r1);
+    widen(2, r2);
     ST* o = static_cast<ST*>(a.conv_out);
-    for (int t = tbeg; t < min(a.T, tbeg + kTB); ++t) {
+#pragma unroll
+    for (int k = 0; k < kTB; ++k) {
         float xt[8], u[8];
-        row(t, xt);
+        widen(k + 3, xt);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             float acc = __builtin_fmaf(w[0][e], r0[e], cb[e]);
@@ -636,7 +652,7 @@ __global__ void conv_out_kernel(ConvArgs a) {
             r1[e] = r2[e];
             r2[e] = xt[e];
         }
-        S::store8(o + ((size_t)n * a.T + t) * D + c0, u);
+        if (tbeg + k < a.T) S::store8(o + ((size_t)n * a.T + tbeg + k) * D + c0, u);
     }
 }
 
@@ -714,7 +730,8 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, int bs, hipStream_t s) 
 hipError_t launch_conv_update(const ConvArgs& a, int dtype, hipStream_t s) {
     const int chunks = a.D / 8;
     if (a.conv_out != nullptr && a.T > 0) {
-        const size_t n = (size_t)a.N * chunks * ((a.T + 15) / 16);
+        const int tb = dtype == 1 ? ConvBlock<uint16_t>::kTB : ConvBlock<float>::kTB;
+        const size_t n = (size_t)a.N * chunks * ((a.T + tb - 1) / tb);
         const dim3 grid((unsigned)((n + 255) / 256));
         if (dtype == 1) hipLaunchKernelGGL(conv_out_kernel<uint16_t>, grid, dim3(256), 0, s, a);
         else hipLaunchKernelGGL(conv_out_kernel<float>, grid, dim3(256), 0, s, a);
