@@ -219,10 +219,17 @@ def cpu_baseline(w):
     t = time.perf_counter()
     oracle.prefill(P, x, y, h0=h0, nthreads=threads, lib=lib)
     dt = time.perf_counter() - t
+    # one thread on one sequence of the same workload (all heads)
+    t = time.perf_counter()
+    oracle.prefill(P, x[:1], y[:1], h0=None if h0 is None else h0[:1], nthreads=1, lib=lib)
+    dt1 = time.perf_counter() - t
     return {"value": w.B * w.T * w.D / dt, "unit": "tokens·channels/s", "cores": threads,
             "kind": "oracle", "seconds": round(dt, 3),
             "sample": "the whole workload: B=%d x T=%d x D=%d (all %d heads), fp64 sequential "
-                      "oracle, OpenMP over (sequence, head) units" % (w.B, w.T, w.D, w.H)}
+                      "oracle, OpenMP over (sequence, head) units" % (w.B, w.T, w.D, w.H),
+            "single_core": {"value": w.T * w.D / dt1, "seconds": round(dt1, 3),
+                            "sample": "sequence 0 only (T=%d x D=%d, all heads), one thread"
+                                      % (w.T, w.D)}}
 
 
 def copy_probe(torch, nbytes: int = 1 << 30, reps: int = 5):
