@@ -707,9 +707,12 @@ constexpr int kConvBlock = 256;  // threads per workgroup of the conv pass
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int bs, hipStream_t s) {
     const dim3 grid((a.N + 31) / 32, a.H);
-    if (dtype == 1 && a.u_ws != nullptr) {
+    // the split form's conv pass indexes (sequence, 8-channel chunk) pairs in 32 bits; beyond
+    // that (N * D / 8 >= 2^31, some 6.7 million sequences at D = 2560) the fused kernel runs
+    const size_t pairs = (size_t)((a.N + kConvSeqs - 1) / kConvSeqs) * (size_t)(a.D / 8);
+    if (dtype == 1 && a.u_ws != nullptr && pairs < ((size_t)1 << 31)) {
         // split: conv pass over (sequence, 8-channel chunk), then the gate pass
-        const size_t nc = (size_t)((a.N + kConvSeqs - 1) / kConvSeqs) * (size_t)(a.D / 8);
+        const size_t nc = pairs;
         hipLaunchKernelGGL((decode_conv_kernel<uint16_t, kConvSeqs>),
                            dim3((unsigned)((nc + kConvBlock - 1) / kConvBlock)), dim3(kConvBlock), 0, s, a);
         const int nw = gate_waves(a.N, a.H, bs, device_cu_count());

@@ -136,7 +136,8 @@ size_t rglru_decode_workspace_bytes(int32_t N, int32_t D, int32_t dtype);
  *                    device buffer of at least rglru_decode_workspace_bytes(N, D, dtype): with
  *                    bf16 storage the step runs as two kernels (conv pass into the workspace,
  *                    then a gate pass spread over 32-channel blocks), the faster form for
- *                    large N; with fp32 storage the workspace is not used.  The two forms
+ *                    large N (up to N * D / 8 < 2^31; beyond that the fused kernel runs);
+ *                    with fp32 storage the workspace is not used.  The two forms
  *                    leave identical conv windows; h and out agree to the rounding of the
  *                    fp32 gate sums, which the two forms accumulate in different orders.
  *                    The workspace must not overlap any other argument.
