@@ -99,6 +99,11 @@ int rglru_prefill(const rglru_params* p, int32_t B, int32_t T, const void* x, co
         !aligned16(h_last) || !aligned16(conv0) || !aligned16(conv_last) || !aligned16(workspace))
         return RGLRU_ERR_UNSUPPORTED;
     const size_t es = elem_size(p->dtype);
+    // the bf16 kernel addresses one sequence's rows, and the carried conv window of all
+    // sequences, with 32-bit byte offsets
+    if (p->dtype == RGLRU_BF16 && ((size_t)T * (size_t)p->D * es >= ((size_t)1 << 31) ||
+                                   (size_t)B * 3 * (size_t)p->D * es >= ((size_t)1 << 31)))
+        return RGLRU_ERR_UNSUPPORTED;
     const size_t n_act = (size_t)B * (size_t)T * (size_t)p->D * es;
     const size_t n_h = (size_t)B * (size_t)p->D * sizeof(float);
     const size_t n_c = (size_t)B * 3 * (size_t)p->D * es;

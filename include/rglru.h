@@ -54,7 +54,8 @@ enum rglru_status {
     RGLRU_OK = 0,
     RGLRU_ERR_NULL = 1,        /* a required pointer is NULL */
     RGLRU_ERR_SHAPE = 2,       /* B/N < 1, T < 0, D < 1, n_heads < 1, D % n_heads != 0, bad stride */
-    RGLRU_ERR_UNSUPPORTED = 3, /* bs not in {128, 256}, unknown dtype, pointer not 16-byte aligned */
+    RGLRU_ERR_UNSUPPORTED = 3, /* bs not in {128, 256}, unknown dtype, pointer not 16-byte aligned,
+                                  a bf16 prefill sequence (or conv window set) of 2 GiB or more */
     RGLRU_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than rglru_prefill_workspace_bytes */
     RGLRU_ERR_ALIAS = 5,       /* an output overlaps an input it may not alias */
     RGLRU_ERR_HIP = 6          /* a HIP call failed; see rglru_last_hip_error() */
@@ -111,6 +112,10 @@ int rglru_prefill_workspace_init(void *workspace, size_t ws_bytes, void *stream)
  *   workspace, ws_bytes  caller-owned device scratch (see above)
  * h0 == h_last and conv0 == conv_last (in place) are allowed; out must not overlap x or y.
  * T = 0 is valid: h_last = h0 and conv_last = conv0 (or zeros).
+ * With bf16 storage one sequence must stay below 2 GiB (T * D * 2 < 2^31, e.g. T < 262144 at
+ * D = 4096) and so must the conv windows of all B sequences (B * 3 * D * 2 < 2^31), else
+ * RGLRU_ERR_UNSUPPORTED; longer sequences are prefilled in pieces, carrying h and the conv
+ * window from one call to the next, and larger batches in several calls.
  */
 int rglru_prefill(const rglru_params *p, int32_t B, int32_t T, const void *x, const void *y,
                   void *out, const float *h0, float *h_last, const void *conv0, void *conv_last,

@@ -84,6 +84,11 @@ def test_prefill_validation(lib):
     assert _prefill(lib, _params(D=512, H=8)) == UNSUP        # bs = 64
     assert _prefill(lib, _params(dtype=5)) == UNSUP
     assert _prefill(lib, p, x=X + 2) == UNSUP                 # alignment
+    big = _params(D=4096, H=16)
+    assert _prefill(lib, big, B=1, T=262144) == UNSUP         # one bf16 sequence of 2 GiB
+    assert _prefill(lib, big, B=1, T=262143) != UNSUP         # just below (then other checks)
+    assert _prefill(lib, big, B=87382, T=1) == UNSUP          # conv windows of 2 GiB
+    assert _prefill(lib, big, B=87381, T=1) != UNSUP
     assert _prefill(lib, p, ws=None) == WS
     assert _prefill(lib, p, ws_bytes=1000) == WS
     assert _prefill(lib, p, out=X) == ALIAS
