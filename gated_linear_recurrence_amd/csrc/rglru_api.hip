@@ -156,7 +156,7 @@ int rglru_prefill(const rglru_params* p, int32_t B, int32_t T, const void* x, co
 
 size_t rglru_decode_workspace_bytes(int32_t N, int32_t D, int32_t dtype) {
     if (N < 1 || D < 1) return 0;
-    return (size_t)N * (size_t)D * elem_size(dtype);
+    return (size_t)((N + 15) / 16) * 16 * (size_t)D * elem_size(dtype);  // blocks of 16 sequences
 }
 
 int rglru_decode_step(const rglru_params* p, int32_t N, const void* x_t, int64_t ld_x,

@@ -355,11 +355,21 @@ __global__ void __launch_bounds__(2 * BS) decode_bf16_kernel(DecodeArgs a) {
 // sequences, each pulling only its 32 channels' weights.
 // ---------------------------------------------------------------------------------------
 
+// Workspace layout of u between the two passes of the split step: in the order the gate pass's
+// MFMA B operands read it.  For a block of 16 sequences, a head and a K step of 32 inputs, one
+// contiguous 1 KB block holds 64 lanes x 8 inputs: lane (g, l) = 16 g + l holds inputs
+// 32 s + 8 g .. + 7 of sequence 16 nb + l.  Offset (in elements) of sequence n, input chunk c0:
+__device__ __forceinline__ size_t u_frag_offset(size_t n, size_t c0, int bs, int H) {
+    const size_t head = c0 / (size_t)bs, k0 = c0 % (size_t)bs;
+    const size_t s = k0 / 32, g = (k0 % 32) / 8;
+    return ((((n / 16) * (size_t)H + head) * (size_t)(bs / 32) + s) * 64 + g * 16 + n % 16) * 8;
+}
+
 // Pass 1 of the split step: u = conv([window, x_t]) for one 8-channel chunk of NS sequences
 // per thread (the chunk's taps and bias are loaded once and applied to all NS), written to the
-// workspace in the storage dtype (nearest-even, as the fused step rounds it), and the window
-// shifted in place (elementwise: no thread reads what another writes).  Consecutive threads
-// take consecutive chunks, so each load instruction covers whole rows.
+// workspace in the storage dtype (nearest-even, as the fused step rounds it) in the order above,
+// and the window shifted in place (elementwise: no thread reads what another writes).
+// Consecutive threads take consecutive chunks, so each load instruction covers whole rows.
 template <typename ST, int NS>
 __global__ void __launch_bounds__(256) decode_conv_kernel(DecodeArgs a) {
     using S = Store<ST>;
@@ -409,7 +419,7 @@ __global__ void __launch_bounds__(256) decode_conv_kernel(DecodeArgs a) {
             acc = __builtin_fmaf(w[4 * e + 2], s2[k][e], acc);
             u[e] = __builtin_fmaf(w[4 * e + 3], xt[k][e], acc);
         }
-        S::store8(static_cast<ST*>(a.u_ws) + n * D + c0, u);
+        S::store8(static_cast<ST*>(a.u_ws) + u_frag_offset(n, c0, a.D / a.H, a.H), u);
         // the stored values round-trip exactly (bf16 -> fp32 -> bf16)
         ST* cs = static_cast<ST*>(a.conv_state) + n * 3 * D + c0;
         S::store8(cs, s1[k]);
@@ -505,16 +515,24 @@ __global__ void __launch_bounds__(512) decode_gate_kernel(DecodeArgs a) {
     float4 hv[2];
     uint2 yv[2], uv[2];
     if (wave_live) {
-        const uint16_t* ur = static_cast<const uint16_t*>(a.u_ws) + ns * D + (size_t)head * BS + 8 * g;
+        // one contiguous 1 KB block per K step (see u_frag_offset); this wave's 16 sequences are
+        // one block of 16
+        const uint16_t* ur = static_cast<const uint16_t*>(a.u_ws) +
+                             ((((size_t)(n0 / 16 + wv) * a.H + head) * kKSteps) * 64 + lane) * 8;
 #pragma unroll
-        for (int s = 0; s < kKSteps; ++s) ub[s] = *reinterpret_cast<const bf16x8*>(ur + 32 * s);
+        for (int s = 0; s < kKSteps; ++s) ub[s] = *reinterpret_cast<const bf16x8*>(ur + 512 * s);
         // 3. elementwise operands of channels cbase + 16 t + 4 g + (0..3), t = 0, 1
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const size_t c = cbase + 16 * t + 4 * g;
             hv[t] = *reinterpret_cast<const float4*>(a.h + ns * D + c);
             yv[t] = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.y) + ns * (size_t)a.ld_y + c);
-            uv[t] = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.u_ws) + ns * D + c);
+            // inputs cw0 + 16 t + 4 g .. + 3 of this lane's sequence: K step cw0 / 32 (the block the
+            // B operand of that step came from), lane group 2 t + g / 2, elements 4 (g & 1) ..
+            uv[t] = *reinterpret_cast<const uint2*>(
+                static_cast<const uint16_t*>(a.u_ws) +
+                ((((size_t)(n0 / 16 + wv) * a.H + head) * kKSteps + cw0 / 32) * 64 +
+                 (2 * t + (g >> 1)) * 16 + l16) * 8 + 4 * (g & 1));
         }
     }
     wait_vmem_all();  // this wave's copies and loads have landed

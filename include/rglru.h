@@ -122,9 +122,10 @@ int rglru_prefill(const rglru_params *p, int32_t B, int32_t T, const void *x, co
                   void *workspace, size_t ws_bytes, void *stream);
 
 /*
- * Bytes of the optional decode workspace for N sequences: N * D storage elements that hold
- * the conv outputs u_t between the two passes of the split step (16-byte aligned, contents
- * need no initialisation and are not preserved between calls).
+ * Bytes of the optional decode workspace for N sequences: 16 * ceil(N / 16) * D storage
+ * elements that hold the conv outputs u_t between the two passes of the split step, in blocks
+ * of 16 sequences (16-byte aligned, contents need no initialisation and are not preserved
+ * between calls).
  */
 size_t rglru_decode_workspace_bytes(int32_t N, int32_t D, int32_t dtype);
 

@@ -121,8 +121,9 @@ def test_decode_workspace_validation(lib):
     p = _params()
     f = lib.rglru_decode_step
     need = lib.rglru_decode_workspace_bytes(4, 512, 1)
-    assert need == 4 * 512 * 2
-    assert lib.rglru_decode_workspace_bytes(4, 512, 0) == 4 * 512 * 4
+    assert need == 16 * 512 * 2                    # sequences in blocks of 16
+    assert lib.rglru_decode_workspace_bytes(4, 512, 0) == 16 * 512 * 4
+    assert lib.rglru_decode_workspace_bytes(17, 512, 1) == 32 * 512 * 2
     assert lib.rglru_decode_workspace_bytes(0, 512, 1) == 0
     assert f(ctypes.byref(p), 4, X, 0, Y, 0, OUT, 0, H0, C0, WSP, need - 2, None) == WS
     assert f(ctypes.byref(p), 4, X, 0, Y, 0, OUT, 0, H0, C0, WSP + 8, need, None) == UNSUP
