@@ -463,6 +463,10 @@ __global__ void __launch_bounds__(512) decode_gate_kernel(DecodeArgs a) {
     // fall on distinct banks.
     __shared__ __attribute__((aligned(16))) uint16_t w_lds[64 * BS];
     __shared__ __attribute__((aligned(16))) float k_lds[3 * 32];  // nb_a, nb_x, 1/kc by channel
+    // h of each wave's 16 sequences x 32 channels, moved as whole 128-byte rows; the 16-byte
+    // chunk at position p of row r holds channels 4 (p ^ (r & 7)) .. + 3, so the MFMA-layout
+    // accesses below (16 rows, one chunk each) spread over the banks
+    __shared__ __attribute__((aligned(16))) float h_lds[8 * 16 * 32];
     // Lambda (128 bytes), gate a bias, gate x bias (64 bytes each) of the 32 channels; each copy
     // instruction fills 1024 bytes, the lanes past the data repeating it
     __shared__ __attribute__((aligned(16))) unsigned char p_lds[3 * 1024];
@@ -512,9 +516,18 @@ __global__ void __launch_bounds__(512) decode_gate_kernel(DecodeArgs a) {
     }
     // 2. operand B: the u row of this lane's sequence, K-slice g of every K step
     bf16x8 ub[kKSteps];
-    float4 hv[2];
     uint2 yv[2], uv[2];
+    float* const hw = h_lds + wv * 512;  // this wave's h rows
     if (wave_live) {
+        // h rows -> LDS, 8 rows per copy (rows past N repeat row N-1 and are not stored)
+        const __amdgpu_buffer_rsrc_t rh = make_rsrc(a.h + (size_t)(n0 + 16 * wv) * D + cbase);
+        const int last_row = N - 1 - (n0 + 16 * wv);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int r = 8 * q + (lane >> 3), pch = lane & 7;
+            const int off = (min(r, last_row) * (int)D + 4 * (pch ^ (r & 7))) * 4;
+            copy16_to_lds(rh, hw + 256 * q, off);
+        }
         // one contiguous 1 KB block per K step (see u_frag_offset); this wave's 16 sequences are
         // one block of 16
         const uint16_t* ur = static_cast<const uint16_t*>(a.u_ws) +
@@ -525,7 +538,6 @@ __global__ void __launch_bounds__(512) decode_gate_kernel(DecodeArgs a) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const size_t c = cbase + 16 * t + 4 * g;
-            hv[t] = *reinterpret_cast<const float4*>(a.h + ns * D + c);
             yv[t] = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.y) + ns * (size_t)a.ld_y + c);
             // inputs cw0 + 16 t + 4 g .. + 3 of this lane's sequence: K step cw0 / 32 (the block the
             // B operand of that step came from), lane group 2 t + g / 2, elements 4 (g & 1) ..
@@ -576,6 +588,10 @@ __global__ void __launch_bounds__(512) decode_gate_kernel(DecodeArgs a) {
     }
 
     // 5. gates, state update, output
+    float4* const hq = reinterpret_cast<float4*>(hw);
+    float4 hv[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) hv[t] = hq[l16 * 8 + ((4 * t + g) ^ (l16 & 7))];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         const float ua[4] = {bf_lo(uv[t].x), bf_hi(uv[t].x), bf_lo(uv[t].y), bf_hi(uv[t].y)};
@@ -591,12 +607,20 @@ __global__ void __launch_bounds__(512) decode_gate_kernel(DecodeArgs a) {
             hn[i] = __builtin_fmaf(gt.a, hs[i], gt.v);
             o[i] = hn[i] * gelu_fast(ya[i]);
         }
+        hq[l16 * 8 + ((4 * t + g) ^ (l16 & 7))] = make_float4(hn[0], hn[1], hn[2], hn[3]);
         if (live) {
             const size_t c = cbase + 16 * t + 4 * g;
-            *reinterpret_cast<float4*>(a.h + ns * D + c) = make_float4(hn[0], hn[1], hn[2], hn[3]);
             *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + ns * (size_t)a.ld_out + c) =
                 make_uint2(pack2bf(o[0], o[1]), pack2bf(o[2], o[3]));
         }
+    }
+    // new h back to memory as whole rows (the wave's own LDS region: its LDS accesses are in order)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int r = 8 * q + (lane >> 3), pch = lane & 7;
+        const float4 v = hq[r * 8 + pch];
+        if (n0 + 16 * wv + r < N)
+            *reinterpret_cast<float4*>(a.h + (size_t)(n0 + 16 * wv + r) * D + cbase + 4 * (pch ^ (r & 7))) = v;
     }
 }
 
