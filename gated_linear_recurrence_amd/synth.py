@@ -30,7 +30,9 @@ ACT_BLOCK = 1024  # tokens per activation stream block
 
 # tensor ids for SeedSequence (fixed order: Lambda, W_a, W_x, b_a, b_x, conv_w, conv_b, h0, x, y)
 _TID = {"lambda": 0, "wa": 1, "wx": 2, "ba": 3, "bx": 4, "conv_w": 5, "conv_b": 6, "h0": 7,
-        "x": 8, "y": 9}
+        "x": 8, "y": 9,
+        # the block's dense projections and its input (x_in feeds linear_x and linear_y)
+        "lx_w": 10, "lx_b": 11, "ly_w": 12, "ly_b": 13, "lo_w": 14, "lo_b": 15, "x_in": 16}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -151,3 +153,43 @@ def make_act(w: Workload, which: str, B: int | None = None, T: int | None = None
 def small(w: Workload, B: int | None = None, T: int | None = None) -> Workload:
     """The same distributions with other sizes (test cases)."""
     return dataclasses.replace(w, B=w.B if B is None else B, T=w.T if T is None else T)
+
+
+def make_proj(w: Workload, Dm: int | None = None, biases: bool = False,
+              seed: int | None = None) -> dict:
+    """The block's dense projections in storage form (Linear weights [out][in]).
+
+    linear_x, linear_y [D, Dm] ~ N(0, std 1/sqrt(Dm)) and linear_out [Dm, D] ~ N(0, std
+    1/sqrt(D)), so unit-variance block inputs give unit-variance branch inputs.
+    biases=False: zero biases (the measured workloads); True: N(0, std 0.1) (parity coverage).
+    """
+    s0 = w.seed if seed is None else seed
+    D = w.D
+    Dm = D if Dm is None else Dm
+    out = {}
+    for name, shape, fan_in in (("lx_w", (D, Dm), Dm), ("ly_w", (D, Dm), Dm), ("lo_w", (Dm, D), D)):
+        a = _rng(s0, _TID[name]).standard_normal(shape, dtype=np.float32)
+        out[name] = to_storage(a * np.float32(1.0 / math.sqrt(fan_in)), w.dtype)
+    for name, n in (("lx_b", D), ("ly_b", D), ("lo_b", Dm)):
+        a = (_rng(s0, _TID[name]).standard_normal(n, dtype=np.float32) * np.float32(0.1)
+             if biases else np.zeros(n, np.float32))
+        out[name] = to_storage(a, w.dtype)
+    return out
+
+
+def make_block_input(w: Workload, Dm: int | None = None, B: int | None = None,
+                     T: int | None = None, seed: int | None = None) -> np.ndarray:
+    """The block input x_in [B, T, Dm] ~ N(0, 1) in storage form; blocks of 1024 tokens."""
+    s0 = w.seed if seed is None else seed
+    Dm = w.D if Dm is None else Dm
+    B = w.B if B is None else B
+    T = w.T if T is None else T
+    st_dtype = np.uint16 if w.dtype == BF16 else np.float32
+    out = np.empty((B, T, Dm), st_dtype)
+    for b in range(B):
+        for blk in range((T + ACT_BLOCK - 1) // ACT_BLOCK):
+            t0 = blk * ACT_BLOCK
+            n = min(ACT_BLOCK, T - t0)
+            a = _rng(s0, _TID["x_in"], b, blk).standard_normal((ACT_BLOCK, Dm), dtype=np.float32)
+            out[b, t0:t0 + n] = to_storage(a[:n], w.dtype)
+    return out

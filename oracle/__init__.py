@@ -80,6 +80,10 @@ def _bind(lib):
     lib.oracle_gelu_tanh.restype = ctypes.c_double
     lib.oracle_rglru_step.argtypes = [ctypes.c_double] * 5
     lib.oracle_rglru_step.restype = ctypes.c_double
+    lib.oracle_linear.argtypes = [I, I, I, I] + [P] * 4
+    lib.oracle_linear.restype = I
+    lib.oracle_block_prefill.argtypes = [I, I, I, I, I, I] + [P] * 19 + [I]
+    lib.oracle_block_prefill.restype = I
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = I
     return lib
@@ -229,6 +233,61 @@ def gate_preacts(wa, ba, wx, bx, u, n_heads: int, lib=None):
                                  _ptr(bx), _ptr(ra), _ptr(ri))
     _check(st, "oracle_gate_preacts")
     return ra, ri
+
+
+class ProjParams:
+    """The block's dense projections in storage form: Linear weights [out][in], biases or None.
+
+    lx_w, ly_w [D, Dm] (linear_x, linear_y); lo_w [Dm, D] (linear_out)."""
+
+    def __init__(self, lx_w, lx_b, ly_w, ly_b, lo_w, lo_b):
+        self.lx_w = _c(lx_w)
+        sd = self.lx_w.dtype
+        self.lx_b = _c(lx_b, sd)
+        self.ly_w = _c(ly_w, sd)
+        self.ly_b = _c(ly_b, sd)
+        self.lo_w = _c(lo_w, sd)
+        self.lo_b = _c(lo_b, sd)
+        self.D, self.Dm = self.lx_w.shape
+
+    def args(self):
+        return [_ptr(self.lx_w), _ptr(self.lx_b), _ptr(self.ly_w), _ptr(self.ly_b),
+                _ptr(self.lo_w), _ptr(self.lo_b)]
+
+
+def linear(x, w, b=None, lib=None):
+    """One Linear layer: x [M, K] (storage), w [N, K], b [N] or None -> [M, N] fp64."""
+    lib = lib or load()
+    x = _c(x)
+    dt = _dtype_code(x)
+    w = _c(w, x.dtype)
+    b = _c(b, x.dtype)
+    M, K = x.shape
+    N = w.shape[0]
+    assert w.shape == (N, K)
+    out = np.empty((M, N), np.float64)
+    _check(lib.oracle_linear(dt, M, K, N, _ptr(x), _ptr(w), _ptr(b), _ptr(out)), "oracle_linear")
+    return out
+
+
+def block_prefill(p: Params, q: ProjParams, x_in, h0=None, conv0=None, nthreads: int = 0, lib=None):
+    """The recurrent block with its projections: x_in [B, T, Dm] (storage).
+
+    Returns (out [B,T,Dm], h_last [B,D], conv_last [B,3,D]), all fp64."""
+    lib = lib or load()
+    x_in = _c(x_in, p.conv_w.dtype)
+    B, T, Dm = x_in.shape
+    assert q.Dm == Dm and q.D == p.D
+    h0 = _c(h0, np.float32)
+    conv0 = _c(conv0, p.conv_w.dtype)
+    out = np.empty((B, T, Dm), np.float64)
+    h_last = np.empty((B, p.D), np.float64)
+    conv_last = np.empty((B, 3, p.D), np.float64)
+    st = lib.oracle_block_prefill(p.dtype, B, T, Dm, p.D, p.H, _ptr(x_in), *q.args(), *p.args(),
+                                  _ptr(h0), _ptr(conv0), _ptr(out), _ptr(h_last), _ptr(conv_last),
+                                  int(nthreads))
+    _check(st, "oracle_block_prefill")
+    return out, h_last, conv_last
 
 
 def gelu_tanh(yv: float, lib=None) -> float:

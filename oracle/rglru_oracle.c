@@ -39,6 +39,15 @@
  * bf16 are widened exactly by placing the 16 bits in the top half of a
  * float; fp32 inputs are widened exactly.
  *
+ * The dense projections around the path (same page and section, and the
+ * module printout: linear_x and linear_y, width 2560 -> 2560 with bias,
+ * both applied to the block input; linear_out, 2560 -> 2560 with bias,
+ * applied to the product of the two branches) are plain Linear layers:
+ *   out[n] = b[n] + sum_k W[n][k] in[k],   W stored [out][in].
+ * oracle_block_prefill composes them with the path:
+ *   out = linear_out( path( linear_x(x_in), linear_y(x_in) ) )
+ * with every intermediate kept in double precision.
+ *
  * Parity pins (tests/test_oracle_pins.py): every function here is pinned
  * by closed forms, library routines or brute force; see that file.
  */
@@ -53,9 +62,11 @@
 
 #define ORACLE_F32 0
 #define ORACLE_BF16 1
+#define ORACLE_F64 2 /* intermediates of the composed block only */
 
 /* Exact widening of one stored element to double. */
 static double widen(const void *base, size_t idx, int dtype) {
+    if (dtype == ORACLE_F64) return ((const double *)base)[idx];
     if (dtype == ORACLE_F32) return (double)((const float *)base)[idx];
     uint32_t bits = (uint32_t)((const uint16_t *)base)[idx] << 16;
     float f;
@@ -73,7 +84,8 @@ double oracle_gelu_tanh(double y) {
 
 /* Parameters of one recurrent block (all pointers are host memory). */
 typedef struct {
-    int dtype;        /* storage type of x, y, conv state and all weights but Lambda */
+    int dtype;        /* storage type of the conv state and all weights but Lambda */
+    int xdtype;       /* type of x and y: the storage type, or ORACLE_F64 inside the block */
     int D, H, bs;     /* channels, gate heads, block size D/H */
     const void *conv_w;   /* [D][4] */
     const void *conv_b;   /* [D] or NULL */
@@ -139,7 +151,7 @@ static void run_unit(const prm_t *p, int hd, int n_tok,
         for (int c = 0; c < bs; ++c) {
             const int ch = hd * bs + c;
             double w3[3] = {win[0 * bs + c], win[1 * bs + c], win[2 * bs + c]};
-            const double xt = widen(x, xoff + (size_t)t * xstride + ch, p->dtype);
+            const double xt = widen(x, xoff + (size_t)t * xstride + ch, p->xdtype);
             u[c] = conv_step(p, ch, w3, xt);
             win[0 * bs + c] = w3[0];
             win[1 * bs + c] = w3[1];
@@ -149,7 +161,7 @@ static void run_unit(const prm_t *p, int hd, int n_tok,
         for (int c = 0; c < bs; ++c) {
             const int ch = hd * bs + c;
             h[c] = rglru_step((double)p->lambda[ch], ra[c], ri[c], u[c], h[c]);
-            const double yt = widen(y, yoff + (size_t)t * ystride + ch, p->dtype);
+            const double yt = widen(y, yoff + (size_t)t * ystride + ch, p->xdtype);
             out[(size_t)t * bs + c] = h[c] * oracle_gelu_tanh(yt);
         }
     }
@@ -163,6 +175,7 @@ static int make_prm(prm_t *p, int dtype, int D, int H, const void *conv_w, const
     if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return 3;
     if (!conv_w || !wa || !wx || !lambda) return 1;
     p->dtype = dtype;
+    p->xdtype = dtype;
     p->D = D;
     p->H = H;
     p->bs = D / H;
@@ -211,15 +224,11 @@ int oracle_prefill_unit(int dtype, int T, int D, int H, int b, int hd, int T_use
  * Full prefill: x, y [B][T][D]; out [B][T][D], h_last [B][D], conv_last [B][3][D]
  * (all outputs fp64).  Units (b, hd) run in parallel over nthreads threads.
  */
-int oracle_prefill(int dtype, int B, int T, int D, int H, const void *x, const void *y,
-                   const void *conv_w, const void *conv_b, const void *wa, const void *ba,
-                   const void *wx, const void *bx, const float *lambda, const float *h0,
-                   const void *conv0, double *out, double *h_last, double *conv_last,
-                   int nthreads) {
-    prm_t p;
-    int st = make_prm(&p, dtype, D, H, conv_w, conv_b, wa, ba, wx, bx, lambda);
-    if (st) return st;
-    if (B < 1 || T < 0) return 2;
+static void prefill_all(const prm_t *pp, int B, int T, const void *x, const void *y,
+                        const float *h0, const void *conv0, double *out, double *h_last,
+                        double *conv_last, int nthreads) {
+    const prm_t p = *pp;
+    const int D = p.D, H = p.H;
     const int bs = p.bs;
     const int n_units = B * H;
 #ifdef _OPENMP
@@ -245,6 +254,83 @@ int oracle_prefill(int dtype, int B, int T, int D, int H, const void *x, const v
         free(o);
         free(h);
     }
+}
+
+int oracle_prefill(int dtype, int B, int T, int D, int H, const void *x, const void *y,
+                   const void *conv_w, const void *conv_b, const void *wa, const void *ba,
+                   const void *wx, const void *bx, const float *lambda, const float *h0,
+                   const void *conv0, double *out, double *h_last, double *conv_last,
+                   int nthreads) {
+    prm_t p;
+    int st = make_prm(&p, dtype, D, H, conv_w, conv_b, wa, ba, wx, bx, lambda);
+    if (st) return st;
+    if (B < 1 || T < 0) return 2;
+    prefill_all(&p, B, T, x, y, h0, conv0, out, h_last, conv_last, nthreads);
+    return 0;
+}
+
+/*
+ * A Linear layer over M rows: in [M][K] (type xdtype), W [N][K] ([out][in], storage type
+ * wdtype), b [N] or NULL; out [M][N] = b + in W^T, summed in k order in double precision.
+ */
+static void linear_rows(int M, int K, int N, const void *in, int xdtype, const void *w,
+                        const void *b, int wdtype, double *out) {
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+    for (int m = 0; m < M; ++m) {
+        for (int n = 0; n < N; ++n) {
+            double s = b ? widen(b, (size_t)n, wdtype) : 0.0;
+            for (int k = 0; k < K; ++k)
+                s += widen(w, (size_t)n * K + k, wdtype) * widen(in, (size_t)m * K + k, xdtype);
+            out[(size_t)m * N + n] = s;
+        }
+    }
+}
+
+/* One Linear layer: x [M][K] (storage dtype), W [N][K], b [N] or NULL -> out [M][N] fp64. */
+int oracle_linear(int dtype, int M, int K, int N, const void *x, const void *w, const void *b,
+                  double *out) {
+    if (M < 0 || K < 1 || N < 1) return 2;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return 3;
+    if (!x || !w || !out) return 1;
+    linear_rows(M, K, N, x, dtype, w, b, dtype, out);
+    return 0;
+}
+
+/*
+ * The whole recurrent block's temporal mixing over T tokens:
+ *   x_in [B][T][Dm] (storage) -> xb = linear_x(x_in), yb = linear_y(x_in)   [B][T][D] fp64
+ *   -> the path above (conv, RG-LRU, times GELU of yb)                      [B][T][D] fp64
+ *   -> out = linear_out(.)                                                  [B][T][Dm] fp64
+ * lx_w, ly_w [D][Dm]; lo_w [Dm][D]; biases [D], [D], [Dm] or NULL.  h_last [B][D] and
+ * conv_last [B][3][D] (fp64) are the path's final state; conv0 holds storage-type values.
+ */
+int oracle_block_prefill(int dtype, int B, int T, int Dm, int D, int H, const void *x_in,
+                         const void *lx_w, const void *lx_b, const void *ly_w, const void *ly_b,
+                         const void *lo_w, const void *lo_b, const void *conv_w,
+                         const void *conv_b, const void *wa, const void *ba, const void *wx,
+                         const void *bx, const float *lambda, const float *h0,
+                         const void *conv0, double *out, double *h_last, double *conv_last,
+                         int nthreads) {
+    prm_t p;
+    int st = make_prm(&p, dtype, D, H, conv_w, conv_b, wa, ba, wx, bx, lambda);
+    if (st) return st;
+    if (B < 1 || T < 0 || Dm < 1) return 2;
+    if (!x_in || !lx_w || !ly_w || !lo_w) return 1;
+    const size_t MD = (size_t)B * T * D;
+    double *xb = (double *)malloc(sizeof(double) * (3 * MD + 1));
+    if (!xb) return 1;
+    double *yb = xb + MD, *mg = yb + MD;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#endif
+    linear_rows(B * T, Dm, D, x_in, dtype, lx_w, lx_b, dtype, xb);
+    linear_rows(B * T, Dm, D, x_in, dtype, ly_w, ly_b, dtype, yb);
+    p.xdtype = ORACLE_F64;
+    prefill_all(&p, B, T, xb, yb, h0, conv0, mg, h_last, conv_last, nthreads);
+    linear_rows(B * T, D, Dm, mg, ORACLE_F64, lo_w, lo_b, dtype, out);
+    free(xb);
     return 0;
 }
 
@@ -298,6 +384,7 @@ int oracle_conv1d_state_update(int dtype, int N, int T_new, int D, const void *x
     if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return 3;
     if (!conv_w || !x_new || !win) return 1;
     p.dtype = dtype;
+    p.xdtype = dtype;
     p.D = D;
     p.conv_w = conv_w;
     p.conv_b = conv_b;

@@ -420,6 +420,120 @@ def _pin_empty_sequence(lib):
     np.testing.assert_array_equal(conv_last, c0)
 
 
+# ----------------------------------------------------------------------------------------------
+# the dense projections around the path (Linear layers) and the composed block
+# ----------------------------------------------------------------------------------------------
+def _shift(n):
+    """Cyclic shift as a Linear weight [out][in]: output j takes input (j + 1) mod n."""
+    w = np.zeros((n, n), np.float32)
+    w[np.arange(n), (np.arange(n) + 1) % n] = 1.0
+    return w
+
+
+def _pin_linear_library(lib):
+    """A Linear layer equals numpy's fp64 matmul x @ W^T + b (W stored [out][in])."""
+    rng = np.random.default_rng(71)
+    x = rng.standard_normal((6, 40)).astype(np.float32)
+    w = rng.standard_normal((24, 40)).astype(np.float32)
+    b = rng.standard_normal(24).astype(np.float32)
+    ref = x.astype(np.float64) @ w.astype(np.float64).T + b.astype(np.float64)
+    np.testing.assert_allclose(oracle.linear(x, w, b, lib=lib), ref, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(oracle.linear(x, w, None, lib=lib), ref - b, rtol=1e-13, atol=1e-13)
+    xb = synth.round_bf16(x)
+    wb = synth.round_bf16(w)
+    refb = _wide(xb) @ _wide(wb).T
+    np.testing.assert_allclose(oracle.linear(xb, wb, None, lib=lib), refb, rtol=1e-13, atol=1e-13)
+
+
+def _pin_linear_exact(lib):
+    """Exact special cases: identity, a cyclic shift (orientation), a zero weight (bias only)."""
+    x = np.arange(-12, 12, dtype=np.float32).reshape(3, 8) * 0.25
+    n = x.shape[1]
+    np.testing.assert_array_equal(oracle.linear(x, np.eye(n, dtype=np.float32), lib=lib), x)
+    np.testing.assert_array_equal(oracle.linear(x, _shift(n), lib=lib), np.roll(x, -1, axis=1))
+    b = np.linspace(-1, 1, 5).astype(np.float32)
+    np.testing.assert_array_equal(oracle.linear(x, np.zeros((5, n), np.float32), b, lib=lib),
+                                  np.broadcast_to(b.astype(np.float64), (3, 5)))
+
+
+def _proj(lx_w, ly_w, lo_w, lx_b=None, ly_b=None, lo_b=None):
+    return oracle.ProjParams(lx_w, lx_b, ly_w, ly_b, lo_w, lo_b)
+
+
+def _pin_block_composition(lib):
+    """With linear_x = I, linear_y = 2 I and linear_out = a cyclic shift plus a bias, the block
+    is exactly the path on (x, 2x), shifted, plus the bias."""
+    D, H, B, T = 16, 2, 2, 11
+    P = _P(_params(D, H, seed=81), H)
+    x, _ = _acts(B, T, D, seed=82)
+    h0 = np.random.default_rng(83).normal(0, 0.3, (B, D)).astype(np.float32)
+    c0 = np.random.default_rng(84).normal(0, 1.0, (B, 3, D)).astype(np.float32)
+    c = np.linspace(-2, 2, D).astype(np.float32)
+    q = _proj(np.eye(D, dtype=np.float32), 2 * np.eye(D, dtype=np.float32), _shift(D), lo_b=c)
+    out, h_last, conv_last = oracle.block_prefill(P, q, x, h0=h0, conv0=c0, lib=lib)
+    po, ph, pc = oracle.prefill(P, x, 2 * x, h0=h0, conv0=c0, lib=lib)
+    np.testing.assert_array_equal(out, np.roll(po, -1, axis=2) + c.astype(np.float64))
+    np.testing.assert_array_equal(h_last, ph)
+    np.testing.assert_array_equal(conv_last, pc)
+
+
+def _pin_block_rectangular(lib):
+    """Block width Dm != path width D, random small-integer projections (every intermediate of
+    the projections is exact in fp32): the block equals numpy's matmuls around the path."""
+    D, H, Dm, B, T = 16, 2, 24, 2, 9
+    rng = np.random.default_rng(91)
+    P = _P(_params(D, H, seed=92), H)
+    x = rng.integers(-2, 3, (B, T, Dm)).astype(np.float32)
+    lx_w = rng.integers(-1, 2, (D, Dm)).astype(np.float32)
+    ly_w = rng.integers(-1, 2, (D, Dm)).astype(np.float32) * 0.25
+    lo_w = rng.standard_normal((Dm, D)).astype(np.float32)
+    lx_b = rng.integers(-3, 4, D).astype(np.float32)
+    ly_b = rng.integers(-3, 4, D).astype(np.float32) * 0.5
+    lo_b = rng.standard_normal(Dm).astype(np.float32)
+    q = _proj(lx_w, ly_w, lo_w, lx_b, ly_b, lo_b)
+    out, h_last, conv_last = oracle.block_prefill(P, q, x, lib=lib)
+    xw = x.astype(np.float64)
+    xb = (xw @ lx_w.astype(np.float64).T + lx_b).astype(np.float32)
+    yb = (xw @ ly_w.astype(np.float64).T + ly_b).astype(np.float32)
+    po, ph, pc = oracle.prefill(P, xb, yb, lib=lib)
+    ref = po @ lo_w.astype(np.float64).T + lo_b.astype(np.float64)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(h_last, ph)
+    np.testing.assert_array_equal(conv_last, pc)
+
+
+def test_linear_matches_numpy(oracle_lib):
+    _pin_linear_library(oracle_lib)
+
+
+def test_linear_exact_cases(oracle_lib):
+    _pin_linear_exact(oracle_lib)
+
+
+def test_block_composition(oracle_lib):
+    _pin_block_composition(oracle_lib)
+
+
+def test_block_rectangular(oracle_lib):
+    _pin_block_rectangular(oracle_lib)
+
+
+def test_block_empty_sequence(oracle_lib):
+    D, H, Dm = 8, 2, 16
+    P = _P(_params(D, H, seed=95), H)
+    rng = np.random.default_rng(96)
+    q = _proj(rng.standard_normal((D, Dm)).astype(np.float32),
+              rng.standard_normal((D, Dm)).astype(np.float32),
+              rng.standard_normal((Dm, D)).astype(np.float32))
+    h0 = np.arange(2 * D, dtype=np.float32).reshape(2, D)
+    c0 = np.arange(2 * 3 * D, dtype=np.float32).reshape(2, 3, D)
+    out, h_last, conv_last = oracle.block_prefill(P, q, np.zeros((2, 0, Dm), np.float32), h0=h0,
+                                                  conv0=c0, lib=oracle_lib)
+    assert out.shape == (2, 0, Dm)
+    np.testing.assert_array_equal(h_last, h0)
+    np.testing.assert_array_equal(conv_last, c0)
+
+
 def test_decode_equals_prefill(oracle_lib):
     _pin_decode_equals_prefill(oracle_lib)
 
@@ -471,6 +585,7 @@ PINS = [
     _pin_gates_block_diagonal, _pin_step_exact_values, _pin_step_limits, _pin_gelu,
     _pin_geometric_series, _pin_decode_equals_prefill, _pin_causality_and_heads,
     _pin_unit_matches_full, _pin_empty_sequence,
+    _pin_linear_library, _pin_linear_exact, _pin_block_composition, _pin_block_rectangular,
 ]
 
 MUTANTS = {
@@ -497,6 +612,14 @@ MUTANTS = {
     "bf16 widening": ("uint32_t bits = (uint32_t)((const uint16_t *)base)[idx] << 16;",
                       "uint32_t bits = (uint32_t)((const uint16_t *)base)[idx] << 15;"),
     "h0 ignored": ("h[c] = h0 ? (double)h0[(size_t)b * D + ch] : 0.0;", "h[c] = 0.0;"),
+    "linear weight transposed": ("widen(w, (size_t)n * K + k, wdtype)", "widen(w, (size_t)k * N + n, wdtype)"),
+    "linear bias dropped": ("double s = b ? widen(b, (size_t)n, wdtype) : 0.0;", "double s = 0.0;"),
+    "linear input row": ("widen(in, (size_t)m * K + k, xdtype)", "widen(in, (size_t)k, xdtype)"),
+    "branches swapped": ("linear_rows(B * T, Dm, D, x_in, dtype, lx_w, lx_b, dtype, xb);",
+                         "linear_rows(B * T, Dm, D, x_in, dtype, ly_w, ly_b, dtype, xb);"),
+    "output projection skips the path": (
+        "linear_rows(B * T, D, Dm, mg, ORACLE_F64, lo_w, lo_b, dtype, out);",
+        "linear_rows(B * T, D, Dm, xb, ORACLE_F64, lo_w, lo_b, dtype, out);"),
 }
 
 
