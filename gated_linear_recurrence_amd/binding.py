@@ -26,7 +26,8 @@ STATUS = {0: "RGLRU_OK", 1: "RGLRU_ERR_NULL", 2: "RGLRU_ERR_SHAPE", 3: "RGLRU_ER
 EXPORTS = ["rglru_prefill_workspace_bytes", "rglru_prefill_workspace_init", "rglru_prefill",
            "rglru_decode_workspace_bytes", "rglru_decode_step", "conv1d_state_update",
            "rglru_prefill_workspace_flags", "rglru_status_string", "rglru_last_hip_error",
-           "rglru_abi_version"]
+           "rglru_abi_version", "rglru_linear", "rglru_block_prefill_workspace_bytes",
+           "rglru_block_prefill"]
 
 _lock = threading.Lock()
 _lib = None
@@ -47,6 +48,13 @@ class rglru_params(ctypes.Structure):
                 ("gate_a_w", ctypes.c_void_p), ("gate_a_b", ctypes.c_void_p),
                 ("gate_x_w", ctypes.c_void_p), ("gate_x_b", ctypes.c_void_p),
                 ("lambda_", ctypes.c_void_p)]
+
+
+class rglru_proj_params(ctypes.Structure):
+    _fields_ = [("D_model", ctypes.c_int32),
+                ("lin_x_w", ctypes.c_void_p), ("lin_x_b", ctypes.c_void_p),
+                ("lin_y_w", ctypes.c_void_p), ("lin_y_b", ctypes.c_void_p),
+                ("lin_out_w", ctypes.c_void_p), ("lin_out_b", ctypes.c_void_p)]
 
 
 def load_library(path: str = LIB_PATH):
@@ -79,6 +87,13 @@ def load_library(path: str = LIB_PATH):
         lib.rglru_status_string.restype = ctypes.c_char_p
         lib.rglru_last_hip_error.argtypes = []
         lib.rglru_last_hip_error.restype = ctypes.c_int
+        lib.rglru_linear.argtypes = [I32, I32, I32, P, P, P, P, P]
+        lib.rglru_linear.restype = ctypes.c_int
+        lib.rglru_block_prefill_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32]
+        lib.rglru_block_prefill_workspace_bytes.restype = SZ
+        lib.rglru_block_prefill.argtypes = [PP, ctypes.POINTER(rglru_proj_params), I32, I32, P, P,
+                                            P, P, P, P, P, SZ, P]
+        lib.rglru_block_prefill.restype = ctypes.c_int
         lib.rglru_abi_version.argtypes = []
         lib.rglru_abi_version.restype = ctypes.c_int
         _lib = lib
@@ -264,3 +279,84 @@ def conv1d_state_update(p: Params, x_new, conv_state, want_out: bool = True, out
                                  _ptr(out), _stream())
     _check(lib, st, "conv1d_state_update")
     return out
+
+
+def rglru_linear(x, w, b=None, out=None):
+    """One Linear layer (bf16): out [M, N] = x [M, K] @ w [N, K]^T + b [N]."""
+    lib = load_library()
+    M, K = x.shape
+    N = w.shape[0]
+    _need(x, "x", torch.bfloat16, (M, K))
+    _need(w, "w", torch.bfloat16, (N, K), x.device)
+    _need(b, "b", torch.bfloat16, (N,), x.device)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", torch.bfloat16, (M, N), x.device)
+    _check(lib, lib.rglru_linear(M, K, N, _ptr(x), _ptr(w), _ptr(b), _ptr(out), _stream()),
+           "rglru_linear")
+    return out
+
+
+class ProjParams:
+    """The block's dense projections on one device (bf16, Linear weights [out, in]).
+
+    lin_x_w, lin_y_w [D, D_model]; lin_out_w [D_model, D]; biases [D], [D], [D_model] or None.
+    """
+
+    def __init__(self, lin_x_w, lin_x_b, lin_y_w, lin_y_b, lin_out_w, lin_out_b):
+        D, Dm = lin_x_w.shape
+        dev = lin_x_w.device
+        _need(lin_x_w, "lin_x_w", torch.bfloat16, (D, Dm), dev)
+        _need(lin_y_w, "lin_y_w", torch.bfloat16, (D, Dm), dev)
+        _need(lin_out_w, "lin_out_w", torch.bfloat16, (Dm, D), dev)
+        _need(lin_x_b, "lin_x_b", torch.bfloat16, (D,), dev)
+        _need(lin_y_b, "lin_y_b", torch.bfloat16, (D,), dev)
+        _need(lin_out_b, "lin_out_b", torch.bfloat16, (Dm,), dev)
+        self.D, self.Dm, self.device = D, Dm, dev
+        self.tensors = (lin_x_w, lin_x_b, lin_y_w, lin_y_b, lin_out_w, lin_out_b)
+        self.c = rglru_proj_params(Dm, *[t.data_ptr() if t is not None else None
+                                         for t in self.tensors])
+
+
+def rglru_block_prefill_workspace_bytes(B: int, T: int, D: int, n_heads: int, D_model: int,
+                                        dtype) -> int:
+    lib = load_library()
+    return int(lib.rglru_block_prefill_workspace_bytes(B, T, D, n_heads, D_model,
+                                                       _dtype_code(dtype)))
+
+
+def make_block_workspace(p: Params, q: ProjParams, B: int, T: int) -> Workspace:
+    return Workspace(rglru_block_prefill_workspace_bytes(B, T, p.D, p.H, q.Dm, p.dtype), p.device)
+
+
+def rglru_block_prefill(p: Params, q: ProjParams, x_in, h0=None, conv0=None, *, out=None,
+                        h_last=None, conv_last=None, workspace: Workspace | None = None,
+                        want_state: bool = True):
+    """The whole temporal-mixing block: out [B, T, D_model] = linear_out(path(linear_x(x_in),
+    linear_y(x_in))).  Returns (out, h_last, conv_last)."""
+    lib = load_library()
+    B, T, Dm = x_in.shape
+    D = p.D
+    if q.D != D or q.Dm != Dm:
+        raise ValueError("projection shapes (%d, %d) do not match D=%d, D_model=%d"
+                         % (q.D, q.Dm, D, Dm))
+    _need(x_in, "x_in", p.dtype, (B, T, Dm), p.device)
+    _need(h0, "h0", torch.float32, (B, D), p.device)
+    _need(conv0, "conv0", p.dtype, (B, 3, D), p.device)
+    if out is None:
+        out = torch.empty_like(x_in)
+    _need(out, "out", p.dtype, (B, T, Dm), p.device)
+    if want_state:
+        if h_last is None:
+            h_last = torch.empty((B, D), dtype=torch.float32, device=p.device)
+        if conv_last is None:
+            conv_last = torch.empty((B, 3, D), dtype=p.dtype, device=p.device)
+    _need(h_last, "h_last", torch.float32, (B, D), p.device)
+    _need(conv_last, "conv_last", p.dtype, (B, 3, D), p.device)
+    if workspace is None:
+        workspace = make_block_workspace(p, q, B, T)
+    st = lib.rglru_block_prefill(ctypes.byref(p.c), ctypes.byref(q.c), B, T, _ptr(x_in), _ptr(out),
+                                 _ptr(h0), _ptr(h_last), _ptr(conv0), _ptr(conv_last),
+                                 _ptr(workspace.t), workspace.nbytes, _stream())
+    _check(lib, st, "rglru_block_prefill")
+    return out, h_last, conv_last

@@ -88,9 +88,14 @@ int rglru_prefill_workspace_init(void* workspace, size_t ws_bytes, void* stream)
     return e == hipSuccess ? RGLRU_OK : hip_fail(e);
 }
 
-int rglru_prefill(const rglru_params* p, int32_t B, int32_t T, const void* x, const void* y,
+}  // extern "C"
+
+namespace {
+
+// Every check rglru_prefill makes before it launches anything.
+int check_prefill(const rglru_params* p, int32_t B, int32_t T, const void* x, const void* y,
                   void* out, const float* h0, float* h_last, const void* conv0, void* conv_last,
-                  void* workspace, size_t ws_bytes, void* stream) {
+                  void* workspace, size_t ws_bytes) {
     int st = check_params(p, true);
     if (st != RGLRU_OK) return st;
     if (B < 1 || T < 0) return RGLRU_ERR_SHAPE;
@@ -128,6 +133,19 @@ int rglru_prefill(const rglru_params* p, int32_t B, int32_t T, const void* x, co
         for (int i = 0; i < 7; ++i)
             if (overlap(workspace, need, ins[i], lens[i])) return RGLRU_ERR_ALIAS;
     }
+    return RGLRU_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int rglru_prefill(const rglru_params* p, int32_t B, int32_t T, const void* x, const void* y,
+                  void* out, const float* h0, float* h_last, const void* conv0, void* conv_last,
+                  void* workspace, size_t ws_bytes, void* stream) {
+    const int st = check_prefill(p, B, T, x, y, out, h0, h_last, conv0, conv_last, workspace,
+                                 ws_bytes);
+    if (st != RGLRU_OK) return st;
 
     PrefillArgs a;
     memset(&a, 0, sizeof a);
@@ -230,6 +248,99 @@ int conv1d_state_update(const rglru_params* p, int32_t N, int32_t T_new, const v
     a.conv_state = conv_state; a.conv_out = conv_out;
     a.N = N; a.T = T_new; a.D = p->D;
     hipError_t e = launch_conv_update(a, p->dtype, (hipStream_t)stream);
+    return e == hipSuccess ? RGLRU_OK : hip_fail(e);
+}
+
+int rglru_linear(int32_t M, int32_t K, int32_t N, const void* x, const void* w, const void* b,
+                 void* out, void* stream) {
+    if (M < 0 || K < 1 || N < 1) return RGLRU_ERR_SHAPE;
+    if (K % 128 != 0 || N % 256 != 0 || K >= (1 << 22) || N >= (1 << 22))
+        return RGLRU_ERR_UNSUPPORTED;
+    if (!w || (M > 0 && (!x || !out))) return RGLRU_ERR_NULL;
+    if (!aligned16(x) || !aligned16(w) || !aligned16(b) || !aligned16(out))
+        return RGLRU_ERR_UNSUPPORTED;
+    const size_t nx = (size_t)M * K * 2, no = (size_t)M * N * 2;
+    if (overlap(out, no, x, nx) || overlap(out, no, w, (size_t)N * K * 2) ||
+        overlap(out, no, b, (size_t)N * 2))
+        return RGLRU_ERR_ALIAS;
+    if (M == 0) return RGLRU_OK;
+    ProjGemmArgs g;
+    memset(&g, 0, sizeof g);
+    g.A = x; g.W0 = w; g.b0 = b; g.C0 = out;
+    g.M = M; g.K = K; g.N0 = N; g.n_out = 1;
+    hipError_t e = launch_proj_gemm(g, (hipStream_t)stream);
+    return e == hipSuccess ? RGLRU_OK : hip_fail(e);
+}
+
+size_t rglru_block_prefill_workspace_bytes(int32_t B, int32_t T, int32_t D, int32_t n_heads,
+                                           int32_t D_model, int32_t dtype) {
+    const size_t pw = rglru_prefill_workspace_bytes(B, T, D, n_heads, dtype);
+    if (pw == 0 || D_model < 1) return 0;
+    const size_t act = ((size_t)B * (size_t)T * (size_t)D * elem_size(dtype) + 255) & ~(size_t)255;
+    return ((pw + 255) & ~(size_t)255) + 3 * act;
+}
+
+int rglru_block_prefill(const rglru_params* p, const rglru_proj_params* q, int32_t B, int32_t T,
+                        const void* x_in, void* out, const float* h0, float* h_last,
+                        const void* conv0, void* conv_last, void* workspace, size_t ws_bytes,
+                        void* stream) {
+    int st = check_params(p, true);
+    if (st != RGLRU_OK) return st;
+    if (!q) return RGLRU_ERR_NULL;
+    if (p->dtype != RGLRU_BF16) return RGLRU_ERR_UNSUPPORTED;
+    if (B < 1 || T < 0 || q->D_model < 1) return RGLRU_ERR_SHAPE;
+    const int D = p->D, Dm = q->D_model;
+    if (D % 256 != 0 || Dm % 256 != 0 || D >= (1 << 21) || Dm >= (1 << 21))
+        return RGLRU_ERR_UNSUPPORTED;
+    if (!q->lin_x_w || !q->lin_y_w || !q->lin_out_w) return RGLRU_ERR_NULL;
+    if (T > 0 && (!x_in || !out)) return RGLRU_ERR_NULL;
+    const void* ptrs[] = {q->lin_x_w, q->lin_x_b, q->lin_y_w, q->lin_y_b, q->lin_out_w,
+                          q->lin_out_b, x_in, out, workspace};
+    for (const void* ptr : ptrs)
+        if (!aligned16(ptr)) return RGLRU_ERR_UNSUPPORTED;
+    if ((size_t)B * (size_t)T >= ((size_t)1 << 31)) return RGLRU_ERR_SHAPE;
+    const size_t pw = rglru_prefill_workspace_bytes(B, T, D, p->n_heads, p->dtype);
+    const size_t need = rglru_block_prefill_workspace_bytes(B, T, D, p->n_heads, Dm, p->dtype);
+    if (T > 0 && (!workspace || ws_bytes < need)) return RGLRU_ERR_WORKSPACE;
+    const size_t n_io = (size_t)B * T * Dm * 2;
+    const size_t n_h = (size_t)B * D * sizeof(float), n_c = (size_t)B * 3 * D * 2;
+    if (overlap(out, n_io, x_in, n_io) || overlap(out, n_io, h0, n_h) ||
+        overlap(out, n_io, h_last, n_h) || overlap(out, n_io, conv0, n_c) ||
+        overlap(out, n_io, conv_last, n_c))
+        return RGLRU_ERR_ALIAS;
+    if (T > 0) {
+        const void* ins[] = {x_in, out, h0, h_last, conv0, conv_last, q->lin_x_w, q->lin_y_w,
+                             q->lin_out_w};
+        const size_t lens[] = {n_io, n_io, n_h, n_h, n_c, n_c, (size_t)D * Dm * 2,
+                               (size_t)D * Dm * 2, (size_t)D * Dm * 2};
+        for (int i = 0; i < 9; ++i)
+            if (overlap(workspace, need, ins[i], lens[i])) return RGLRU_ERR_ALIAS;
+    }
+    const size_t act = ((size_t)B * T * D * 2 + 255) & ~(size_t)255;
+    char* base = T > 0 ? static_cast<char*>(workspace) + ((pw + 255) & ~(size_t)255) : nullptr;
+    void* xb = base;
+    void* yb = T > 0 ? base + act : nullptr;
+    void* mg = T > 0 ? base + 2 * act : nullptr;
+    // the path's own checks, before anything is launched
+    st = check_prefill(p, B, T, xb, yb, mg, h0, h_last, conv0, conv_last, workspace, pw);
+    if (st != RGLRU_OK) return st;
+    if (T == 0)  // state pass-through only
+        return rglru_prefill(p, B, 0, nullptr, nullptr, nullptr, h0, h_last, conv0, conv_last,
+                             nullptr, 0, stream);
+
+    const int M = B * T;
+    ProjGemmArgs g;
+    memset(&g, 0, sizeof g);
+    g.A = x_in; g.W0 = q->lin_x_w; g.W1 = q->lin_y_w; g.b0 = q->lin_x_b; g.b1 = q->lin_y_b;
+    g.C0 = xb; g.C1 = yb; g.M = M; g.K = Dm; g.N0 = D; g.n_out = 2;
+    hipError_t e = launch_proj_gemm(g, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e);
+    st = rglru_prefill(p, B, T, xb, yb, mg, h0, h_last, conv0, conv_last, workspace, pw, stream);
+    if (st != RGLRU_OK) return st;
+    memset(&g, 0, sizeof g);
+    g.A = mg; g.W0 = q->lin_out_w; g.b0 = q->lin_out_b; g.C0 = out;
+    g.M = M; g.K = D; g.N0 = Dm; g.n_out = 1;
+    e = launch_proj_gemm(g, (hipStream_t)stream);
     return e == hipSuccess ? RGLRU_OK : hip_fail(e);
 }
 

@@ -65,11 +65,26 @@ struct ConvArgs {
     int N, T, D;
 };
 
+// One Linear layer (or the two branch projections side by side) as a bf16 GEMM:
+// C_o[m][n] = b_o[n] + sum_k A[m][k] W_o[n][k] for output o < n_out, each [M][N0].
+struct ProjGemmArgs {
+    const void* A;               // [M][K]
+    const void* W0;              // [N0][K]
+    const void* W1;              // [N0][K] (n_out == 2) or null
+    const void* b0;              // [N0] or null
+    const void* b1;
+    void* C0;                    // [M][N0]
+    void* C1;
+    int M, K, N0, n_out;         // N0 % 256 == 0, K % 128 == 0, 256 * N0 < 2^31
+    int ntm, ntn;                // set by the launcher
+};
+
 int device_cu_count();  // compute units of the current device (cached)
 hipError_t launch_prefill(const PrefillArgs& a, int dtype, int bs, hipStream_t s);
 hipError_t launch_prefill_empty(const PrefillArgs& a, int dtype, hipStream_t s);
 hipError_t launch_workspace_init(void* ws, size_t bytes, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int bs, hipStream_t s);
 hipError_t launch_conv_update(const ConvArgs& a, int dtype, hipStream_t s);
+hipError_t launch_proj_gemm(const ProjGemmArgs& a, hipStream_t s);
 
 }  // namespace rglru

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define RGLRU_ABI_VERSION 2
+#define RGLRU_ABI_VERSION 3
 
 enum rglru_dtype { RGLRU_F32 = 0, RGLRU_BF16 = 1 };
 
@@ -55,7 +55,8 @@ enum rglru_status {
     RGLRU_ERR_NULL = 1,        /* a required pointer is NULL */
     RGLRU_ERR_SHAPE = 2,       /* B/N < 1, T < 0, D < 1, n_heads < 1, D % n_heads != 0, bad stride */
     RGLRU_ERR_UNSUPPORTED = 3, /* bs not in {128, 256}, unknown dtype, pointer not 16-byte aligned,
-                                  a bf16 prefill sequence (or conv window set) of 2 GiB or more */
+                                  a bf16 prefill sequence (or conv window set) of 2 GiB or more,
+                                  projection widths outside the multiples stated below */
     RGLRU_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than rglru_prefill_workspace_bytes */
     RGLRU_ERR_ALIAS = 5,       /* an output overlaps an input it may not alias */
     RGLRU_ERR_HIP = 6          /* a HIP call failed; see rglru_last_hip_error() */
@@ -164,6 +165,61 @@ int rglru_decode_step(const rglru_params *p, int32_t N, const void *x_t, int64_t
  * page "Gemma 詳解：RecurrentGemma 架構", kept causal, and its three-token state. */
 int conv1d_state_update(const rglru_params *p, int32_t N, int32_t T_new, const void *x_new,
                         void *conv_state, void *conv_out, void *stream);
+
+/*
+ * The dense projections around the path, which make it the whole temporal-mixing block.
+ * Operation: the page "Gemma 詳解：RecurrentGemma 架構" (section "含遞迴區塊的殘差區塊" and the
+ * module printout) applies two Linear layers with bias, linear_x and linear_y, to the block
+ * input (width D_model) to form the two width-D branches, and a third, linear_out, to the
+ * product of the branches, back to width D_model.  Weights are stored like PyTorch Linear
+ * weights, [out][in].  bf16 storage only (operands bf16, fp32 accumulation, results rounded to
+ * bf16 nearest-even).
+ *   lin_x_w, lin_y_w  [D][D_model];  lin_x_b, lin_y_b  [D] or NULL (NULL = no bias)
+ *   lin_out_w         [D_model][D];  lin_out_b         [D_model] or NULL
+ */
+typedef struct rglru_proj_params {
+    int32_t D_model;
+    const void *lin_x_w;
+    const void *lin_x_b;
+    const void *lin_y_w;
+    const void *lin_y_b;
+    const void *lin_out_w;
+    const void *lin_out_b;
+} rglru_proj_params;
+
+/*
+ * One Linear layer on its own: out[m][n] = b[n] + sum_k x[m][k] w[n][k] (bf16 storage).
+ *   x [M][K], w [N][K] ([out][in]), b [N] or NULL, out [M][N]; M >= 0.
+ * K % 128 == 0, N % 256 == 0, K < 2^22 and N < 2^22, else RGLRU_ERR_UNSUPPORTED.  out must not
+ * overlap x, w or b.
+ */
+int rglru_linear(int32_t M, int32_t K, int32_t N, const void *x, const void *w, const void *b,
+                 void *out, void *stream);
+
+/*
+ * Bytes of device workspace rglru_block_prefill needs: a prefill workspace (see
+ * rglru_prefill_workspace_bytes) at offset 0, then room for the two branches and their
+ * product ([B][T][D] each).  Initialise it once with rglru_prefill_workspace_init(workspace,
+ * ws_bytes); every completed call leaves it initialised again.  0 on invalid shapes.
+ */
+size_t rglru_block_prefill_workspace_bytes(int32_t B, int32_t T, int32_t D, int32_t n_heads,
+                                           int32_t D_model, int32_t dtype);
+
+/*
+ * Prefill of the whole temporal-mixing block over T tokens:
+ *   out = linear_out( path( linear_x(x_in), linear_y(x_in) ) )
+ * where path is rglru_prefill's operation on the two branches.
+ *   x_in  [B][T][D_model] block input;  out [B][T][D_model] block output (bf16)
+ *   h0, h_last, conv0, conv_last  as for rglru_prefill (the conv window holds linear_x outputs)
+ *   workspace, ws_bytes  at least rglru_block_prefill_workspace_bytes(...), initialised once
+ * bf16 storage only; D % 256 == 0 and D_model % 256 == 0, else RGLRU_ERR_UNSUPPORTED (and the
+ * limits of rglru_prefill apply).  out must not overlap x_in, the state buffers or the
+ * workspace; the workspace must not overlap any other argument.
+ */
+int rglru_block_prefill(const rglru_params *p, const rglru_proj_params *q, int32_t B, int32_t T,
+                        const void *x_in, void *out, const float *h0, float *h_last,
+                        const void *conv0, void *conv_last, void *workspace, size_t ws_bytes,
+                        void *stream);
 
 /*
  * Diagnostics of a prefill workspace: copies its error flags to *flags_out (0 = none) and

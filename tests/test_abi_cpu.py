@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.rglru_abi_version() == 2
+    assert lib.rglru_abi_version() == 3
     for st in range(7):
         assert lib.rglru_status_string(st)
     assert lib.rglru_status_string(99) == b"unknown status"
@@ -141,3 +141,72 @@ def test_conv_update_validation(lib):
     assert f(ctypes.byref(p), 2, 4, X, C0, X, None) == ALIAS
     assert f(ctypes.byref(p), 2, 0, None, C0, None, None) == OK   # nothing to do
     assert f(ctypes.byref(_params(D=100, H=1)), 2, 4, X, C0, None, None) == UNSUP  # D % 8
+
+
+def test_linear_validation(lib):
+    f = lib.rglru_linear
+    W, B_ = 0x60000000, 0x70000000
+    assert f(-1, 128, 256, X, W, B_, OUT, None) == SHAPE
+    assert f(4, 0, 256, X, W, B_, OUT, None) == SHAPE
+    assert f(4, 100, 256, X, W, B_, OUT, None) == UNSUP       # K % 128
+    assert f(4, 128, 200, X, W, B_, OUT, None) == UNSUP       # N % 256
+    assert f(4, 1 << 22, 256, X, W, B_, OUT, None) == UNSUP   # K bound
+    assert f(4, 128, 256, None, W, B_, OUT, None) == NULL
+    assert f(4, 128, 256, X, None, B_, OUT, None) == NULL
+    assert f(4, 128, 256, X + 2, W, B_, OUT, None) == UNSUP   # alignment
+    assert f(4, 128, 256, X, W, B_, X + 64, None) == ALIAS
+    assert f(4, 128, 256, X, W, B_, W, None) == ALIAS
+    assert f(0, 128, 256, None, W, None, None, None) == OK     # nothing to do, no launch
+
+
+def _proj(Dm=512, base=0x90000000):
+    q = binding.rglru_proj_params()
+    q.D_model = Dm
+    q.lin_x_w, q.lin_x_b = base, base + 0x100000
+    q.lin_y_w, q.lin_y_b = base + 0x200000, base + 0x300000
+    q.lin_out_w, q.lin_out_b = base + 0x400000, base + 0x500000
+    return q
+
+
+def _block(lib, p, q, B=2, T=100, x=X, out=OUT, h0=H0, hl=HL, c0=C0, cl=CL, ws=WSP, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.rglru_block_prefill_workspace_bytes(B, T, p.D, p.n_heads, q.D_model, p.dtype)
+    return lib.rglru_block_prefill(ctypes.byref(p), ctypes.byref(q), B, T, x, out, h0, hl, c0, cl,
+                                   ws, ws_bytes, None)
+
+
+def test_block_workspace_bytes(lib):
+    f = lib.rglru_block_prefill_workspace_bytes
+    pw = lib.rglru_prefill_workspace_bytes(8, 8192, 2560, 10, 1)
+    assert f(8, 8192, 2560, 10, 2560, 1) == ((pw + 255) // 256) * 256 + 3 * 8 * 8192 * 2560 * 2
+    assert f(8, 8192, 2560, 10, 0, 1) == 0
+    assert f(0, 8192, 2560, 10, 2560, 1) == 0
+
+
+def test_block_validation(lib):
+    p, q = _params(), _proj()
+    assert lib.rglru_block_prefill(ctypes.byref(p), None, 2, 10, X, OUT, H0, HL, C0, CL, WSP,
+                                   1 << 30, None) == NULL
+    assert _block(lib, _params(dtype=0), q) == UNSUP          # bf16 only
+    assert _block(lib, _params(D=384, H=3), q) == UNSUP       # D % 256 (bs = 128 is fine)
+    assert _block(lib, p, _proj(Dm=300)) == UNSUP             # D_model % 256
+    assert _block(lib, p, _proj(Dm=0)) == SHAPE
+    assert _block(lib, p, q, B=0) == SHAPE
+    assert _block(lib, p, q, x=None) == NULL
+    r = _proj()
+    r.lin_out_w = None
+    assert _block(lib, p, r) == NULL
+    assert _block(lib, p, q, x=X + 2) == UNSUP
+    assert _block(lib, p, q, ws=None) == WS
+    assert _block(lib, p, q, ws_bytes=4096) == WS
+    assert _block(lib, p, q, out=X + 64) == ALIAS
+    assert _block(lib, p, q, out=H0) == ALIAS
+    assert _block(lib, p, q, ws=X) == ALIAS
+    assert _block(lib, p, q, ws=q.lin_y_w - 4096) == ALIAS
+    # the path's own checks run before anything is launched
+    assert _block(lib, p, q, hl=H0 + 16) == ALIAS
+    assert _block(lib, p, q, c0=C0 + 2) == UNSUP
+    big = _params(D=4096, H=16)
+    far = [k << 40 for k in range(1, 8)]   # buffers of several GiB that do not overlap
+    kw = dict(x=far[0], out=far[1], h0=far[2], hl=far[3], c0=far[4], cl=far[5], ws=far[6])
+    assert _block(lib, big, _proj(), B=1, T=262144, **kw) == UNSUP   # one bf16 branch of 2 GiB
