@@ -13,10 +13,12 @@
 // weight and write x, the others read linear_y's weight and write y.
 //
 // Workgroup tile 256 x 256, four waves of 128 x 128 (4 x 4 tiles of v_mfma_f32_32x32x16_bf16,
-// 256 fp32 accumulators per lane).  K advances in steps of 32 through a ring of four LDS stages
-// filled by buffer loads with the LDS bit (16 bytes per lane, straight into LDS), three steps
-// ahead of the MFMAs.  Each stage is its own LDS array: the compiler can then tell a stage being
-// read from the copies in flight into the others, and does not wait for those copies.
+// 256 fp32 accumulators per lane, in AGPRs).  K advances in steps of 64 through two LDS stages
+// filled by buffer loads with the LDS bit (16 bytes per lane, straight into LDS), one k-step
+// ahead of the MFMAs.  A k-step reads whole 128-byte lines of its 512 tile rows; with 32-byte
+// k-steps each line was fetched twice (the L1 cannot keep 512 lines between the halves).
+#include <type_traits>
+
 #include "rglru_device.h"
 #include "rglru_internal.h"
 
@@ -24,44 +26,97 @@ namespace rglru {
 namespace {
 
 typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBM = 256;                    // tile rows (M)
 constexpr int kBN = 256;                    // tile columns (N)
-constexpr int kBK = 32;                     // K per stage
+constexpr int kBK = 64;                     // K per stage
 constexpr int kThreads = 256;               // 4 waves, 2 x 2 over the tile
 constexpr int kChunks = kBK / 8;            // 16-byte chunks per tile row
 constexpr int kRowBytes = kBK * 2;
-constexpr int kTileBytes = kBM * kRowBytes;             // one operand, one stage: 16 KB
+constexpr int kTileBytes = kBM * kRowBytes;             // one operand, one stage: 32 KB
 constexpr int kCopiesPerWave = kTileBytes / 1024 / 4;   // 1 KB copies per wave, operand, stage
 constexpr int kGroupM = 8;                  // tile rows per group of the tile order
 static_assert(kBM == kBN, "both operands share the copy and fragment helpers");
-static_assert(kChunks == 4, "the chunk swizzle below is written for 64-byte rows");
+static_assert(kChunks == 8 && kCopiesPerWave == 8, "the swizzle and copies are for 128-byte rows");
+
+// Position of 16-byte chunk c of tile row r inside its 128-byte row.  A fragment read has 16
+// lanes on 16 consecutive rows at one chunk index; chunk c of row r goes to c ^ f(r) with
+// f(r) = (r ^ (r / 8)) % 8, which puts the 16 reads in 16 distinct 16-byte bank groups of a
+// 256-byte bank line (and any 8 consecutive rows in distinct groups of a 128-byte line).
+__device__ __forceinline__ int chunk_pos(int r, int c) { return c ^ ((r ^ (r >> 3)) & 7); }
+
+// Four global -> LDS copies of 1 KB (buffer_load_dwordx4 with the LDS bit: lane l's 16 bytes go
+// to LDS byte M0 + 16 l), to consecutive 1 KB destinations from lds_addr.
+//
+// Written as inline assembly on purpose: the compiler's wait insertion cannot tell the LDS
+// stages apart, and made the fragment reads after each refill wait for that refill to land (a
+// memory round trip per k-step).  Hidden from it, the copies are waited for only where the
+// kernel says so: each wave waits for its own copies (vmcnt) before the barrier that publishes
+// a stage, and no other vector-memory instruction runs while copies are in flight.  The block
+// has no output register (the data goes to LDS); it saves M0, steps it through the 1 KB
+// destinations (one wait state after each write before its use) and restores it.  The resource
+// words are not written by the VALU inside the loop; before the first copies the prologue
+// waits the 5 states a buffer instruction needs after a VALU write of its SGPRs
+// (guard_vmem_sgprs).
+__device__ __forceinline__ void copy4(const u32x4& rs, uint32_t lds_addr, const int (&off)[4]) {
+    uint32_t keep;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %5\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %6, 0 offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %6, 0 offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %3, %6, 0 offen lds\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %4, %6, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(keep)
+        : "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "s"(lds_addr), "s"(rs)
+        : "memory", "scc");
+}
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+// Half of one operand's copies of k-step kt into an LDS stage (this wave's copies 4 h .. 4 h + 3
+// of its 8).  Lane l of copy q fills LDS chunk p = 64 q + l of the stage (row p / 8, position
+// p % 8), so the global side reads the chunk that belongs there (the swizzle is its own
+// inverse).  Tile row r is global row min(r, rows - 1) relative to the resource base: rows past
+// a ragged M repeat the last row and their results are never stored.
+__device__ __forceinline__ void copy_half(const u32x4& rs, uint16_t* lds, int h, int wv,
+                                          int lane, int K, int rows, int kt) {
+    int off[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int p = (wv * kCopiesPerWave + 4 * h + j) * 64 + lane;
+        const int r = p / kChunks;
+        const int c = chunk_pos(r, p % kChunks);
+        off[j] = min(r, rows - 1) * K * 2 + kt * kRowBytes + 16 * c;
+    }
+    copy4(rs, lds_address(lds + (wv * kCopiesPerWave + 4 * h) * 512), off);
+}
+
+// Five wait states after the resource words were last written (they are built from
+// v_readfirstlane results: a buffer instruction reading SGPRs that the VALU wrote needs 5).
+__device__ __forceinline__ void guard_vmem_sgprs(const u32x4& a, const u32x4& b) {
+    asm volatile("s_nop 4" ::"s"(a), "s"(b));
+}
+
+// A buffer resource as four dwords (base, stride 0, byte range, format word) for the copies.
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
+    const uint64_t p = (uint64_t)(uintptr_t)base;
+    return u32x4{(uint32_t)p, (uint32_t)(p >> 32) & 0xffffu, bytes, 0x00020000u};
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_n(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
-}
-
-// Position of 16-byte chunk c of tile row r inside the row.  A ds_read_b128 serves 8 lanes
-// (8 consecutive rows, one chunk index) per pass; with 64-byte rows, rows r and r + 1 share a
-// 128-byte bank line, so chunk c of row r goes to c ^ ((r / 2) % 4): the 8 rows then cover all
-// 8 16-byte bank groups.
-__device__ __forceinline__ int chunk_pos(int r, int c) { return c ^ ((r >> 1) & 3); }
-
-// Copy k-step kt of one operand's 256 tile rows into an LDS stage.  Tile row r is global row
-// min(r, rows - 1) relative to the resource base: rows past a ragged M repeat the last row and
-// their results are never stored.  Each copy moves 1 KB: lane l of copy q fills LDS chunk
-// 64 q + l, so the global side picks the chunk that belongs there.
-__device__ __forceinline__ void copy_stage(__amdgpu_buffer_rsrc_t rs, uint16_t* lds, int wv,
-                                           int lane, int K, int rows, int kt) {
-#pragma unroll
-    for (int j = 0; j < kCopiesPerWave; ++j) {
-        const int q = wv * kCopiesPerWave + j;
-        const int p = q * 64 + lane;
-        const int r = p / kChunks;
-        const int c = chunk_pos(r, p % kChunks);   // the swizzle is its own inverse
-        const int off = min(r, rows - 1) * K * 2 + kt * kRowBytes + 16 * c;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds + q * 512, 16, off, 0, 0, 0);
-    }
 }
 
 // A or B fragment of the 32-row tile starting at row r0, K sub-step s (16 k): lane l supplies
@@ -72,23 +127,25 @@ __device__ __forceinline__ bf16x8 frag(const uint16_t* lds, int r0, int lane, in
     return *reinterpret_cast<const bf16x8*>(lds + r * kBK + 8 * chunk_pos(r, c));
 }
 
-__device__ __forceinline__ void mma_stage(const uint16_t* sa, const uint16_t* sb,
-                                          f32x16 (&acc)[4][4], int wm, int wn, int lane) {
+// The lane's fragments of one K sub-step: 4 A tiles (rows 128 wm + 32 i) and 4 weight tiles
+// (rows 128 wn + 32 j).
+__device__ __forceinline__ void load_frags(const uint16_t* sa, const uint16_t* sb, int s, int wm,
+                                          int wn, int lane, bf16x8 (&a)[4], bf16x8 (&b)[4]) {
 #pragma unroll
-    for (int s = 0; s < kBK / 16; ++s) {
-        bf16x8 a[4], b[4];
+    for (int i = 0; i < 4; ++i) a[i] = frag(sa, 128 * wm + 32 * i, lane, s);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = frag(sa, 128 * wm + 32 * i, lane, s);
+    for (int j = 0; j < 4; ++j) b[j] = frag(sb, 128 * wn + 32 * j, lane, s);
+}
+
+// 16 MFMAs of one K sub-step.  Weight rows are the MFMA's A operand: the result tile is C^T,
+// so each lane ends up with 4 consecutive output columns per register group (8-byte stores).
+__device__ __forceinline__ void mma(const bf16x8 (&a)[4], const bf16x8 (&b)[4],
+                                    f32x16 (&acc)[4][4]) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) b[j] = frag(sb, 128 * wn + 32 * j, lane, s);
-        // weight rows as the MFMA's A operand: the result tile is C^T, so each lane ends up
-        // with 4 consecutive output columns per register group (8-byte stores)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
-    }
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
 }
 
 // vmcnt(n) with the other counters left alone (gfx9 encoding: vmcnt bits 3:0 and 15:14)
@@ -117,10 +174,8 @@ __device__ __forceinline__ void tile_of(int bid, int ntm, int ntn, int& tm, int&
 }
 
 __global__ void __launch_bounds__(kThreads, 1) proj_gemm_kernel(ProjGemmArgs g) {
-    __shared__ __attribute__((aligned(16))) uint16_t a0[kBM * kBK], a1[kBM * kBK], a2[kBM * kBK],
-        a3[kBM * kBK];
-    __shared__ __attribute__((aligned(16))) uint16_t b0[kBN * kBK], b1[kBN * kBK], b2[kBN * kBK],
-        b3[kBN * kBK];
+    __shared__ __attribute__((aligned(16))) uint16_t a0[kBM * kBK], a1[kBM * kBK];
+    __shared__ __attribute__((aligned(16))) uint16_t b0[kBN * kBK], b1[kBN * kBK];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (the copies' LDS base)
@@ -137,9 +192,9 @@ __global__ void __launch_bounds__(kThreads, 1) proj_gemm_kernel(ProjGemmArgs g) 
     const int rows = min(g.M - m0, kBM);
     const uint16_t* A = static_cast<const uint16_t*>(g.A) + (size_t)m0 * K;
     const uint16_t* W = static_cast<const uint16_t*>(second ? g.W1 : g.W0) + (size_t)nl0 * K;
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc_n(A, (uint32_t)(rows * K * 2));
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc_n(W, (uint32_t)(kBN * K * 2));
-    const int KT = K / kBK;
+    const u32x4 ra = rsrc_words(A, (uint32_t)(rows * K * 2));
+    const u32x4 rb = rsrc_words(W, (uint32_t)(kBN * K * 2));
+    const int KT = K / kBK;                       // even, >= 2
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -149,44 +204,78 @@ __global__ void __launch_bounds__(kThreads, 1) proj_gemm_kernel(ProjGemmArgs g) 
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    // three k-steps in flight before the first MFMA
-    copy_stage(ra, a0, wv, lane, K, rows, 0);
-    copy_stage(rb, b0, wv, lane, K, kBN, 0);
-    if (KT > 1) {
-        copy_stage(ra, a1, wv, lane, K, rows, 1);
-        copy_stage(rb, b1, wv, lane, K, kBN, 1);
-    }
-    if (KT > 2) {
-        copy_stage(ra, a2, wv, lane, K, rows, 2);
-        copy_stage(rb, b2, wv, lane, K, kBN, 2);
-    }
+    constexpr int kPerStep = 2 * kCopiesPerWave;  // copies per wave per k-step
+    guard_vmem_sgprs(ra, rb);
+    copy_half(ra, a0, 0, wv, lane, K, rows, 0);
+    copy_half(ra, a0, 1, wv, lane, K, rows, 0);
+    copy_half(rb, b0, 0, wv, lane, K, kBN, 0);
+    copy_half(rb, b0, 1, wv, lane, K, kBN, 0);
+    copy_half(ra, a1, 0, wv, lane, K, rows, 1);
+    copy_half(ra, a1, 1, wv, lane, K, rows, 1);
+    copy_half(rb, b1, 0, wv, lane, K, kBN, 1);
+    copy_half(rb, b1, 1, wv, lane, K, kBN, 1);
+    wait_vmcnt<kPerStep>();
+    lds_sync();
+    bf16x8 fa[4], fb[4];                           // fragments of the current k-step's sub-step 0
+    load_frags(a0, b0, 0, wm, wn, lane, fa, fb);
 
-    // one k-step: wait for this wave's copies of stage kt (those of the next two steps may stay
-    // in flight), meet the other waves (their copies have landed, and nobody still reads the
-    // stage about to be refilled), refill it three steps ahead, then run the MFMAs
-    auto step = [&](int kt, const uint16_t* ca, const uint16_t* cb, uint16_t* na, uint16_t* nb) {
-        constexpr int kPerStep = 2 * kCopiesPerWave;
-        const int ahead = KT - 1 - kt;
-        if (ahead >= 2) wait_vmcnt<2 * kPerStep>();
-        else if (ahead == 1) wait_vmcnt<kPerStep>();
-        else wait_vmcnt<0>();
-        lds_sync();
-        if (kt + 3 < KT) {
-            copy_stage(ra, na, wv, lane, K, rows, kt + 3);
-            copy_stage(rb, nb, wv, lane, K, kBN, kt + 3);
+    // One k-step of four K sub-steps, fragments ping-ponging between two register sets (each
+    // sub-step's loads arrive under the previous sub-step's MFMAs).  After the third sub-step
+    // this wave waits for its copies of the next stage and meets the other waves: the next
+    // stage is then complete, and nobody reads the current one any more (its last fragments
+    // are in registers), so its refill (k-step kt + 2) is issued between the fourth sub-step's
+    // MFMAs, after the next k-step's first fragments.  F (compile time): kRefill | kNext.
+    // A runtime branch there made the compiler's LDS wait counts fall back to the shorter path.
+    constexpr int kRefill = 1, kNext = 2;
+    auto step = [&](auto flags, int kt, uint16_t* ca, uint16_t* cb, const uint16_t* xa,
+                    const uint16_t* xb) {
+        constexpr int F = decltype(flags)::value;
+        bf16x8 ga[4], gb[4];
+        load_frags(ca, cb, 1, wm, wn, lane, ga, gb);
+        mma(fa, fb, acc);
+        load_frags(ca, cb, 2, wm, wn, lane, fa, fb);
+        mma(ga, gb, acc);
+        load_frags(ca, cb, 3, wm, wn, lane, ga, gb);
+        mma(fa, fb, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr ((F & kNext) != 0) {
+            wait_vmcnt<0>();
+            lds_sync();
+            load_frags(xa, xb, 0, wm, wn, lane, fa, fb);
         }
-        mma_stage(ca, cb, acc, wm, wn, lane);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gb[j], ga[i], acc[i][j], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr ((F & kRefill) != 0) {
+                if (i < 2) copy_half(ra, ca, i, wv, lane, K, rows, kt + 2);
+                else copy_half(rb, cb, i - 2, wv, lane, K, kBN, kt + 2);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
-    // Step 0 runs before the loop, so the loop's first step reads stage 1: with stage 0 read
-    // right after the loop header, the compiler's tracking of copies into LDS loses track of
-    // which stage each copy targets and waits for all of them there (the just-issued refill
-    // included), a full memory round trip every fourth step.  KT % 4 == 0.
-    step(0, a0, b0, a3, b3);
-    for (int kt = 1; kt < KT; kt += 4) {
-        step(kt, a1, b1, a0, b0);
-        step(kt + 1, a2, b2, a1, b1);
-        step(kt + 2, a3, b3, a2, b2);
-        if (kt + 3 < KT) step(kt + 3, a0, b0, a3, b3);
+    using All = std::integral_constant<int, kRefill | kNext>;
+    using NextOnly = std::integral_constant<int, kNext>;
+    using Fin = std::integral_constant<int, 0>;
+    // The stage of k-step kt is kt % 2.  Step 0 runs before the loop, so the loop's first step
+    // reads stage 1 (with stage 0 read right after the loop header the compiler's wait
+    // accounting merged the paths into the loop conservatively).  The loop runs k-steps
+    // 1 .. KT - 4, each of which refills and has a next; the last three follow it.
+    if (KT == 2) {
+        step(NextOnly{}, 0, a0, b0, a1, b1);
+        step(Fin{}, 1, a1, b1, a0, b0);
+    } else {
+        step(All{}, 0, a0, b0, a1, b1);
+        for (int kt = 1; kt < KT - 3; kt += 2) {
+            step(All{}, kt, a1, b1, a0, b0);
+            step(All{}, kt + 1, a0, b0, a1, b1);
+        }
+        step(All{}, KT - 3, a1, b1, a0, b0);
+        step(NextOnly{}, KT - 2, a0, b0, a1, b1);
+        step(Fin{}, KT - 1, a1, b1, a0, b0);
     }
 
     // bias, round, store.  acc[i][j] is the transposed 32 x 32 tile: lane l holds output row
@@ -198,20 +287,17 @@ __global__ void __launch_bounds__(kThreads, 1) proj_gemm_kernel(ProjGemmArgs g) 
     const __amdgpu_buffer_rsrc_t rc = make_rsrc_n(C, (uint32_t)(rows * ldc * 2));
     const int ncol = 128 * wn + 4 * (lane >> 5);
     const int mrow = 128 * wm + (lane & 31);
-    uint2 bw[4][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j) {
+        uint2 bw[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            bw[j][q] = bias ? *reinterpret_cast<const uint2*>(bias + nl0 + ncol + 32 * j + 8 * q)
-                            : make_uint2(0u, 0u);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
+            bw[q] = bias ? *reinterpret_cast<const uint2*>(bias + nl0 + ncol + 32 * j + 8 * q)
+                         : make_uint2(0u, 0u);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int n = ncol + 32 * j + 8 * q;
-            const float bv[4] = {bf_lo(bw[j][q].x), bf_hi(bw[j][q].x), bf_lo(bw[j][q].y),
-                                 bf_hi(bw[j][q].y)};
+            const float bv[4] = {bf_lo(bw[q].x), bf_hi(bw[q].x), bf_lo(bw[q].y), bf_hi(bw[q].y)};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const f32x16& t = acc[i][j];
@@ -221,6 +307,7 @@ __global__ void __launch_bounds__(kThreads, 1) proj_gemm_kernel(ProjGemmArgs g) 
                 __builtin_amdgcn_raw_buffer_store_b64(v, rc, off, 0, 0);
             }
         }
+    }
 }
 
 }  // namespace
