@@ -148,6 +148,27 @@ __device__ __forceinline__ void mma(const bf16x8 (&a)[4], const bf16x8 (&b)[4],
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
 }
 
+// The 16 MFMAs of one K sub-step (fragments a, b) with the 8 fragment loads of the next
+// sub-step (from stage na/nb, sub-step ns, into a2/b2) placed one after each of the first 8
+// MFMAs, and an optional extra unit of work (the stage refill) after MFMAs 8..11.  The order is
+// pinned (sched_barrier): left free, the compiler moved the loads next to their first use and
+// waited for them there.
+template <typename Extra>
+__device__ __forceinline__ void mma_pipe(const bf16x8 (&a)[4], const bf16x8 (&b)[4],
+                                         f32x16 (&acc)[4][4], const uint16_t* na,
+                                         const uint16_t* nb, int ns, int wm, int wn, int lane,
+                                         bf16x8 (&a2)[4], bf16x8 (&b2)[4], Extra&& extra) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+        const int i = u >> 2, j = u & 3;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+        if (u < 4) a2[u] = frag(na, 128 * wm + 32 * u, lane, ns);
+        else if (u < 8) b2[u - 4] = frag(nb, 128 * wn + 32 * (u - 4), lane, ns);
+        else if (u < 12) extra(u - 8);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 // vmcnt(n) with the other counters left alone (gfx9 encoding: vmcnt bits 3:0 and 15:14)
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -230,31 +251,25 @@ __global__ void __launch_bounds__(kThreads, 1) proj_gemm_kernel(ProjGemmArgs g) 
     auto step = [&](auto flags, int kt, uint16_t* ca, uint16_t* cb, const uint16_t* xa,
                     const uint16_t* xb) {
         constexpr int F = decltype(flags)::value;
+        auto none = [](int) {};
         bf16x8 ga[4], gb[4];
-        load_frags(ca, cb, 1, wm, wn, lane, ga, gb);
-        mma(fa, fb, acc);
-        load_frags(ca, cb, 2, wm, wn, lane, fa, fb);
-        mma(ga, gb, acc);
-        load_frags(ca, cb, 3, wm, wn, lane, ga, gb);
-        mma(fa, fb, acc);
         __builtin_amdgcn_sched_barrier(0);
+        mma_pipe(fa, fb, acc, ca, cb, 1, wm, wn, lane, ga, gb, none);
+        mma_pipe(ga, gb, acc, ca, cb, 2, wm, wn, lane, fa, fb, none);
+        mma_pipe(fa, fb, acc, ca, cb, 3, wm, wn, lane, ga, gb, none);
         if constexpr ((F & kNext) != 0) {
             wait_vmcnt<0>();
             lds_sync();
-            load_frags(xa, xb, 0, wm, wn, lane, fa, fb);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gb[j], ga[i], acc[i][j], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
-            if constexpr ((F & kRefill) != 0) {
-                if (i < 2) copy_half(ra, ca, i, wv, lane, K, rows, kt + 2);
-                else copy_half(rb, cb, i - 2, wv, lane, K, kBN, kt + 2);
-            }
-            __builtin_amdgcn_sched_barrier(0);
+            auto refill = [&](int h) {
+                if constexpr ((F & kRefill) != 0) {
+                    if (h < 2) copy_half(ra, ca, h, wv, lane, K, rows, kt + 2);
+                    else copy_half(rb, cb, h - 2, wv, lane, K, kBN, kt + 2);
+                }
+            };
+            mma_pipe(ga, gb, acc, xa, xb, 0, wm, wn, lane, fa, fb, refill);
+        } else {
+            mma(ga, gb, acc);
         }
     };
     using All = std::integral_constant<int, kRefill | kNext>;
