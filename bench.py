@@ -5,7 +5,8 @@ A step is one rglru_prefill call over the 2B-shaped batched workload (B=8, T=819
 10 gate heads of 256, bf16 storage, fp32 state): conv, gates, scan, GELU merge and all
 stores, inputs resident in HBM.  Prints one JSON line.  Besides the headline prefill figure
 the line carries the dominant kernel's roofline, the oracle's CPU throughput on a bounded
-sample, the 2B single-sequence prefill and the decode step time (256 sequences, D=2560).
+sample, the 2B single-sequence prefill, the decode step time (256 sequences, D=2560), the
+conv-state update and the whole block with its dense projections.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-extras]
 """
@@ -203,6 +204,72 @@ def time_decode(w, N, steps, torch, binding, split=True, flush=False):
     except Exception as exc:  # graph capture is optional for the figure
         print("decode graph capture skipped: %s" % exc, file=sys.stderr)
     return eager_us, graph_us
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+
+
+def time_block(w, steps, warmup, torch, binding):
+    """The whole temporal-mixing block (linear_x | linear_y, the path, linear_out) at the
+    workload's shape, plus each projection GEMM on its own (rglru_linear) and, for context, the
+    same GEMMs through torch.nn.functional.linear (hipBLASLt)."""
+    p = synth.make_params(w)
+    q = synth.make_proj(w)
+    P = binding.Params(*[_to_dev(p[k], torch) for k in ("conv_w", "conv_b", "wa", "ba", "wx",
+                                                          "bx", "lambda")])
+    qd = {k: _to_dev(v, torch) for k, v in q.items()}
+    Q = binding.ProjParams(qd["lx_w"], qd["lx_b"], qd["ly_w"], qd["ly_b"], qd["lo_w"], qd["lo_b"])
+    x_in = _to_dev(synth.make_block_input(w), torch)
+    h0 = _to_dev(synth.make_h0(w), torch)
+    out = torch.empty_like(x_in)
+    hl = torch.empty((w.B, w.D), dtype=torch.float32, device="cuda")
+    cl = torch.empty((w.B, 3, w.D), dtype=x_in.dtype, device="cuda")
+    ws = binding.make_block_workspace(P, Q, w.B, w.T)
+
+    def timed(call, n):
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    ms_block = timed(lambda: binding.rglru_block_prefill(P, Q, x_in, h0, out=out, h_last=hl,
+                                                         conv_last=cl, workspace=ws), steps)
+    if ws.flags():
+        raise RuntimeError("block workspace reported error flags %#x" % ws.flags())
+    M = w.B * w.T
+    x2 = x_in.view(M, w.D)
+    w_in = torch.cat([qd["lx_w"], qd["ly_w"]], 0).contiguous()     # [2D, D_model]
+    b_in = torch.cat([qd["lx_b"], qd["ly_b"]], 0).contiguous()
+    y_in = torch.empty((M, 2 * w.D), dtype=x_in.dtype, device="cuda")
+    mg = out.view(M, w.D)                                          # any [M, D] bf16 operand
+    y_out = torch.empty((M, w.D), dtype=x_in.dtype, device="cuda")
+    gemms = {}
+    for name, (a, wt, b, o) in {"in_proj": (x2, w_in, b_in, y_in),
+                                "out_proj": (mg, qd["lo_w"], qd["lo_b"], y_out)}.items():
+        ms = timed(lambda: binding.rglru_linear(a, wt, b, out=o), steps)
+        ms_lib = timed(lambda: torch.nn.functional.linear(a, wt, b), steps)
+        fl = 2.0 * M * a.shape[1] * wt.shape[0]
+        gemms[name] = {"M": M, "K": a.shape[1], "N": wt.shape[0], "ms": ms,
+                       "tflops": fl / (ms * 1e-3) / 1e12,
+                       "mfma_frac": fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                       "hipblaslt_ms": ms_lib,
+                       "hipblaslt_tflops": fl / (ms_lib * 1e-3) / 1e12}
+    flops = 2.0 * M * w.D * (2 * w.D) + 2.0 * M * w.D * w.D
+    return {"workload": w.name + " (block input width 2560 = D)", "ms": ms_block,
+            "tokens/s": M / (ms_block * 1e-3),
+            "projection_tflop": flops / 1e12,
+            "roofline": {"bound": "mfma", "kernel": "proj_gemm_kernel (in_proj)",
+                         "achieved": gemms["in_proj"]["tflops"], "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s",
+                         "frac": gemms["in_proj"]["tflops"] / MFMA_BF16_PEAK_TFLOPS},
+            "gemms": gemms,
+            "note": "hipblaslt_* is torch.nn.functional.linear on the same operands, for context"}
 
 
 def cpu_baseline(w):
@@ -415,6 +482,7 @@ def main():
             "workload": w.name + " (conv outputs for every token, window update)", "ms": msc,
             "algorithmic_bytes": cb, "algorithmic_GBs": cb / (msc * 1e-3) / 1e9,
             "hbm_frac": cb / (msc * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        line["block_prefill"] = time_block(w, max(args.steps // 2, 5), args.warmup, torch, binding)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)
