@@ -84,6 +84,13 @@ def _bind(lib):
     lib.oracle_linear.restype = I
     lib.oracle_block_prefill.argtypes = [I, I, I, I, I, I] + [P] * 19 + [I]
     lib.oracle_block_prefill.restype = I
+    D_ = ctypes.c_double
+    lib.oracle_rope.argtypes = [I, I, P, D_, P]
+    lib.oracle_rope.restype = I
+    lib.oracle_local_mqa.argtypes = [I, I, I, I, P, P, P, P]
+    lib.oracle_local_mqa.restype = I
+    lib.oracle_local_attention_block.argtypes = [I, I, I, I, I, I, I, D_] + [P] * 7 + [I]
+    lib.oracle_local_attention_block.restype = I
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = I
     return lib
@@ -288,6 +295,51 @@ def block_prefill(p: Params, q: ProjParams, x_in, h0=None, conv0=None, nthreads:
                                   int(nthreads))
     _check(st, "oracle_block_prefill")
     return out, h_last, conv_last
+
+
+def rope(v, pos, base: float = 10000.0, lib=None):
+    """Rotary position embedding of head vectors v [n, dh] (fp64) at positions pos [n]."""
+    lib = lib or load()
+    v = np.array(v, np.float64, copy=True, order="C")
+    n, dh = v.shape
+    pos = _c(np.asarray(pos, np.float64), np.float64)
+    _check(lib.oracle_rope(n, dh, _ptr(pos), float(base), _ptr(v)), "oracle_rope")
+    return v
+
+
+def local_mqa(q, k, v, window: int, lib=None):
+    """Sliding-window MQA over one sequence: q [T, Hq, dh], k, v [T, dh] (fp64, positions
+    already encoded) -> o [T, Hq, dh]."""
+    lib = lib or load()
+    q = _c(np.asarray(q, np.float64), np.float64)
+    k = _c(np.asarray(k, np.float64), np.float64)
+    v = _c(np.asarray(v, np.float64), np.float64)
+    T, Hq, dh = q.shape
+    assert k.shape == (T, dh) and v.shape == (T, dh)
+    o = np.empty((T, Hq, dh), np.float64)
+    _check(lib.oracle_local_mqa(T, Hq, dh, int(window), _ptr(q), _ptr(k), _ptr(v), _ptr(o)),
+           "oracle_local_mqa")
+    return o
+
+
+def local_attention_block(x_in, wq, wk, wv, wo, bo, n_heads: int, window: int,
+                          base: float = 10000.0, nthreads: int = 0, lib=None):
+    """The local-attention block: x_in [B, T, Dm] (storage) -> out [B, T, Dm] (fp64).
+    wq [Hq*dh, Dm], wk, wv [dh, Dm], wo [Dm, Hq*dh] (storage, [out][in]), bo [Dm] or None."""
+    lib = lib or load()
+    x_in = _c(x_in)
+    dt = _dtype_code(x_in)
+    wq, wk, wv, wo = (_c(a, x_in.dtype) for a in (wq, wk, wv, wo))
+    bo = _c(bo, x_in.dtype)
+    B, T, Dm = x_in.shape
+    dh = wk.shape[0]
+    assert wq.shape == (n_heads * dh, Dm) and wv.shape == (dh, Dm) and wo.shape == (Dm, n_heads * dh)
+    out = np.empty((B, T, Dm), np.float64)
+    st = lib.oracle_local_attention_block(dt, B, T, Dm, int(n_heads), dh, int(window), float(base),
+                                          _ptr(x_in), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo),
+                                          _ptr(bo), _ptr(out), int(nthreads))
+    _check(st, "oracle_local_attention_block")
+    return out
 
 
 def gelu_tanh(yv: float, lib=None) -> float:

@@ -48,6 +48,9 @@
  *   out = linear_out( path( linear_x(x_in), linear_y(x_in) ) )
  * with every intermediate kept in double precision.
  *
+ * The file ends with the model's other temporal-mixing block, local sliding-window
+ * multi-query attention with rotary position embedding (see its section header).
+ *
  * Parity pins (tests/test_oracle_pins.py): every function here is pinned
  * by closed forms, library routines or brute force; see that file.
  */
@@ -431,4 +434,123 @@ int oracle_max_threads(void) {
 #else
     return 1;
 #endif
+}
+
+/* ======================================================================================
+ * Local sliding-window multi-query attention: the other temporal-mixing block of the same
+ * model (page "Gemma 詳解：RecurrentGemma 架構", section "含區域 MQA 的殘差區塊" and the
+ * printout's RecurrentGemmaSdpaAttention): q_proj (width -> Hq heads of dh, no bias),
+ * k_proj and v_proj (width -> one head of dh shared by all query heads, no bias), rotary
+ * position embedding on q and k "as in base Gemma", each position attending to a fixed window
+ * of past tokens (section "區域注意力視窗大小": 2k tokens), and o_proj (with bias).
+ *
+ * Readings (listed in the design doc):
+ *   - RoPE pairs dimension i with i + dh/2 (the rotate-half convention) and turns pair i by
+ *     pos * base^(-2 i / dh), base 10000, over the whole head; pos is the token's index in
+ *     its sequence, from 0;
+ *   - the window of W tokens is the current token and the W - 1 before it;
+ *   - scores are q.k / sqrt(dh), no soft-capping; softmax over the window.
+ * ====================================================================================== */
+
+/* RoPE of one head vector v[dh] at position pos, in place. */
+static void rope_head(double *v, int dh, double pos, double base) {
+    const int half = dh / 2;
+    for (int i = 0; i < half; ++i) {
+        const double theta = pos * pow(base, -2.0 * (double)i / (double)dh);
+        const double c = cos(theta), s = sin(theta);
+        const double a = v[i], b = v[i + half];
+        v[i] = a * c - b * s;
+        v[i + half] = b * c + a * s;
+    }
+}
+
+/* RoPE of n head vectors v[n][dh] at positions pos[n], in place. */
+int oracle_rope(int n, int dh, const double *pos, double base, double *v) {
+    if (n < 0 || dh < 2 || dh % 2 != 0) return 2;
+    for (int r = 0; r < n; ++r) rope_head(v + (size_t)r * dh, dh, pos[r], base);
+    return 0;
+}
+
+/* Attention of one query vector q[dh] over keys/values k, v [n][dh] (all in the window):
+ * o[dh] = sum_s softmax_s(q . k_s / sqrt(dh)) v_s. */
+static void attend_one(int n, int dh, const double *q, const double *k, const double *v,
+                       double *o, double *score) {
+    const double scale = 1.0 / sqrt((double)dh);
+    double mx = -INFINITY;
+    for (int s = 0; s < n; ++s) {
+        double d = 0.0;
+        for (int c = 0; c < dh; ++c) d += q[c] * k[(size_t)s * dh + c];
+        score[s] = d * scale;
+        if (score[s] > mx) mx = score[s];
+    }
+    double den = 0.0;
+    for (int s = 0; s < n; ++s) {
+        score[s] = exp(score[s] - mx);
+        den += score[s];
+    }
+    for (int c = 0; c < dh; ++c) o[c] = 0.0;
+    for (int s = 0; s < n; ++s)
+        for (int c = 0; c < dh; ++c) o[c] += (score[s] / den) * v[(size_t)s * dh + c];
+}
+
+/* Local MQA over one sequence of T tokens: q [T][Hq][dh], k, v [T][dh] (positions already
+ * encoded); o [T][Hq][dh].  Query t of every head attends to tokens max(0, t-W+1) .. t. */
+int oracle_local_mqa(int T, int Hq, int dh, int W, const double *q, const double *k,
+                     const double *v, double *o) {
+    if (T < 0 || Hq < 1 || dh < 1 || W < 1) return 2;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(dynamic, 16)
+#endif
+    for (int t = 0; t < T; ++t) {
+        double *score = (double *)malloc(sizeof(double) * ((size_t)W + 1));
+        const int s0 = t - W + 1 > 0 ? t - W + 1 : 0;
+        for (int h = 0; h < Hq; ++h)
+            attend_one(t - s0 + 1, dh, q + ((size_t)t * Hq + h) * dh, k + (size_t)s0 * dh,
+                       v + (size_t)s0 * dh, o + ((size_t)t * Hq + h) * dh, score);
+        free(score);
+    }
+    return 0;
+}
+
+/*
+ * The local-attention temporal-mixing block over B sequences of T tokens:
+ *   x_in [B][T][Dm] (storage) -> q = x Wq^T [.., Hq*dh], k = x Wk^T [.., dh], v = x Wv^T
+ *   (no biases) -> RoPE on q (each head) and k at positions 0 .. T-1 -> local MQA with window
+ *   W -> out = o Wo^T + bo  [B][T][Dm] (fp64).  Wq [Hq*dh][Dm], Wk, Wv [dh][Dm], Wo [Dm][Hq*dh].
+ */
+int oracle_local_attention_block(int dtype, int B, int T, int Dm, int Hq, int dh, int W,
+                                 double base, const void *x_in, const void *wq, const void *wk,
+                                 const void *wv, const void *wo, const void *bo, double *out,
+                                 int nthreads) {
+    if (B < 1 || T < 0 || Dm < 1 || Hq < 1 || dh < 2 || dh % 2 || W < 1) return 2;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return 3;
+    if (!x_in || !wq || !wk || !wv || !wo || !out) return 1;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#endif
+    const int DQ = Hq * dh;
+    const size_t M = (size_t)T;
+    double *q = (double *)malloc(sizeof(double) * (M * DQ + 1));
+    double *k = (double *)malloc(sizeof(double) * (M * dh + 1));
+    double *v = (double *)malloc(sizeof(double) * (M * dh + 1));
+    double *o = (double *)malloc(sizeof(double) * (M * DQ + 1));
+    if (!q || !k || !v || !o) return 1;
+    for (int b = 0; b < B; ++b) {
+        const size_t xoff = (size_t)b * T * Dm;
+        const void *xb = (const char *)x_in + xoff * (dtype == ORACLE_F32 ? 4 : 2);
+        linear_rows(T, Dm, DQ, xb, dtype, wq, NULL, dtype, q);
+        linear_rows(T, Dm, dh, xb, dtype, wk, NULL, dtype, k);
+        linear_rows(T, Dm, dh, xb, dtype, wv, NULL, dtype, v);
+        for (int t = 0; t < T; ++t) {
+            for (int h = 0; h < Hq; ++h) rope_head(q + ((size_t)t * Hq + h) * dh, dh, (double)t, base);
+            rope_head(k + (size_t)t * dh, dh, (double)t, base);
+        }
+        oracle_local_mqa(T, Hq, dh, W, q, k, v, o);
+        linear_rows(T, DQ, Dm, o, ORACLE_F64, wo, bo, dtype, out + xoff);
+    }
+    free(q);
+    free(k);
+    free(v);
+    free(o);
+    return 0;
 }

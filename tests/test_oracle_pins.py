@@ -534,6 +534,126 @@ def test_block_empty_sequence(oracle_lib):
     np.testing.assert_array_equal(conv_last, c0)
 
 
+# ----------------------------------------------------------------------------------------------
+# local sliding-window multi-query attention and the rotary position embedding
+# ----------------------------------------------------------------------------------------------
+def _pin_rope_complex(lib):
+    """RoPE turns the pair (v_i, v_{i+dh/2}) as the complex number v_i + j v_{i+dh/2} times
+    exp(j pos 10000^(-2i/dh)) (numpy's complex exponential, not the oracle's cos/sin loop)."""
+    rng = np.random.default_rng(101)
+    dh, half = 16, 8
+    v = rng.standard_normal((5, dh))
+    pos = np.array([0.0, 1.0, 7.0, 100.0, 2047.0])
+    z = (v[:, :half] + 1j * v[:, half:]) * np.exp(
+        1j * pos[:, None] * 10000.0 ** (-2.0 * np.arange(half) / dh))
+    ref = np.concatenate([z.real, z.imag], axis=1)
+    np.testing.assert_allclose(oracle.rope(v, pos, lib=lib), ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(oracle.rope(v[:1], [0.0], lib=lib), v[:1])
+
+
+def _pin_rope_relative(lib):
+    """After RoPE, q_m . k_n depends on m - n only."""
+    rng = np.random.default_rng(102)
+    q, k = rng.standard_normal((1, 32)), rng.standard_normal((1, 32))
+    d1 = float((oracle.rope(q, [10.0], lib=lib) @ oracle.rope(k, [3.0], lib=lib).T)[0, 0])
+    d2 = float((oracle.rope(q, [1007.0], lib=lib) @ oracle.rope(k, [1000.0], lib=lib).T)[0, 0])
+    assert abs(d1 - d2) < 1e-9 * (1.0 + abs(d1))
+    d3 = float((oracle.rope(q, [11.0], lib=lib) @ oracle.rope(k, [3.0], lib=lib).T)[0, 0])
+    assert abs(d3 - d1) > 1e-6
+
+
+def _pin_mqa_closed_forms(lib):
+    rng = np.random.default_rng(103)
+    T, Hq, dh, W = 12, 3, 8, 4
+    q = rng.standard_normal((T, Hq, dh))
+    k = rng.standard_normal((T, dh))
+    v = rng.standard_normal((T, dh))
+    # window 1: every query sees only its own token
+    np.testing.assert_array_equal(oracle.local_mqa(q, k, v, 1, lib=lib),
+                                  np.broadcast_to(v[:, None, :], (T, Hq, dh)))
+    # zero queries: equal weights over the window, so the mean of the window's values
+    o = oracle.local_mqa(np.zeros_like(q), k, v, W, lib=lib)
+    ref = np.stack([v[max(0, t - W + 1):t + 1].mean(0) for t in range(T)])
+    np.testing.assert_allclose(o[:, 1], ref, rtol=1e-13, atol=1e-13)
+    # two tokens: the newer one's weight is the logistic of the scaled score difference
+    q2 = rng.standard_normal((2, 1, dh))
+    o2 = oracle.local_mqa(q2, k[:2], v[:2], 2, lib=lib)
+    w1 = 1.0 / (1.0 + math.exp(-float(q2[1, 0] @ (k[1] - k[0])) / math.sqrt(dh)))
+    np.testing.assert_allclose(o2[1, 0], v[0] + w1 * (v[1] - v[0]), rtol=1e-12, atol=1e-12)
+
+
+def _pin_mqa_invariants(lib):
+    rng = np.random.default_rng(104)
+    T, Hq, dh, W = 20, 2, 8, 5
+    q = rng.standard_normal((T, Hq, dh))
+    k = rng.standard_normal((T, dh))
+    v = rng.standard_normal((T, dh))
+    o = oracle.local_mqa(q, k, v, W, lib=lib)
+    t0 = 9
+    # tokens after t0, and tokens older than its window, do not change o[t0]
+    for s_ in (t0 + 1, t0 - W):
+        k2, v2 = k.copy(), v.copy()
+        k2[s_] += 3.0
+        v2[s_] -= 2.0
+        np.testing.assert_array_equal(oracle.local_mqa(q, k2, v2, W, lib=lib)[t0], o[t0])
+    # the oldest token inside the window does
+    k3 = k.copy()
+    k3[t0 - W + 1] += 3.0
+    assert np.all(np.abs(oracle.local_mqa(q, k3, v, W, lib=lib)[t0] - o[t0]) > 0)
+    # a component shared by every key shifts all scores of a query alike: no change
+    u = rng.standard_normal(dh)
+    np.testing.assert_allclose(oracle.local_mqa(q, k + u, v, W, lib=lib), o, rtol=1e-11,
+                               atol=1e-12)
+    # the heads share keys and values: equal queries give equal outputs
+    q4 = q.copy()
+    q4[:, 1] = q4[:, 0]
+    o4 = oracle.local_mqa(q4, k, v, W, lib=lib)
+    np.testing.assert_array_equal(o4[:, 1], o4[:, 0])
+
+
+def _pin_attention_block_composition(lib):
+    """Two heads, block width != head width, small-integer projections (exact in fp32): the
+    block equals numpy's projections around the pinned RoPE and attention."""
+    rng = np.random.default_rng(105)
+    B, T, Dm, Hq, dh, W = 2, 11, 24, 2, 8, 4
+    x = rng.integers(-2, 3, (B, T, Dm)).astype(np.float32)
+    wq = rng.integers(-1, 2, (Hq * dh, Dm)).astype(np.float32)
+    wk = rng.integers(-1, 2, (dh, Dm)).astype(np.float32)
+    wv = rng.integers(-1, 2, (dh, Dm)).astype(np.float32)
+    wo = rng.standard_normal((Dm, Hq * dh)).astype(np.float32)
+    bo = rng.standard_normal(Dm).astype(np.float32)
+    out = oracle.local_attention_block(x, wq, wk, wv, wo, bo, Hq, W, lib=lib)
+    pos = np.arange(T, dtype=np.float64)
+    for b in range(B):
+        xb = x[b].astype(np.float64)
+        q = xb @ wq.astype(np.float64).T
+        k = oracle.rope(xb @ wk.astype(np.float64).T, pos, lib=lib)
+        v = xb @ wv.astype(np.float64).T
+        qr = np.stack([oracle.rope(q[:, h * dh:(h + 1) * dh], pos, lib=lib) for h in range(Hq)], 1)
+        o = oracle.local_mqa(qr, k, v, W, lib=lib).reshape(T, Hq * dh)
+        np.testing.assert_allclose(out[b], o @ wo.astype(np.float64).T + bo, rtol=1e-11, atol=1e-11)
+
+
+def test_rope_complex(oracle_lib):
+    _pin_rope_complex(oracle_lib)
+
+
+def test_rope_relative(oracle_lib):
+    _pin_rope_relative(oracle_lib)
+
+
+def test_mqa_closed_forms(oracle_lib):
+    _pin_mqa_closed_forms(oracle_lib)
+
+
+def test_mqa_invariants(oracle_lib):
+    _pin_mqa_invariants(oracle_lib)
+
+
+def test_attention_block_composition(oracle_lib):
+    _pin_attention_block_composition(oracle_lib)
+
+
 def test_decode_equals_prefill(oracle_lib):
     _pin_decode_equals_prefill(oracle_lib)
 
@@ -586,6 +706,8 @@ PINS = [
     _pin_geometric_series, _pin_decode_equals_prefill, _pin_causality_and_heads,
     _pin_unit_matches_full, _pin_empty_sequence,
     _pin_linear_library, _pin_linear_exact, _pin_block_composition, _pin_block_rectangular,
+    _pin_rope_complex, _pin_rope_relative, _pin_mqa_closed_forms, _pin_mqa_invariants,
+    _pin_attention_block_composition,
 ]
 
 MUTANTS = {
@@ -620,6 +742,18 @@ MUTANTS = {
     "output projection skips the path": (
         "linear_rows(B * T, D, Dm, mg, ORACLE_F64, lo_w, lo_b, dtype, out);",
         "linear_rows(B * T, D, Dm, xb, ORACLE_F64, lo_w, lo_b, dtype, out);"),
+    "rope pairs neighbours": ("const double a = v[i], b = v[i + half];",
+                              "const double a = v[2 * i], b = v[2 * i + 1];"),
+    "rope sign": ("v[i] = a * c - b * s;", "v[i] = a * c + b * s;"),
+    "rope frequency": ("pow(base, -2.0 * (double)i / (double)dh)",
+                       "pow(base, -1.0 * (double)i / (double)dh)"),
+    "rope position of k": ("rope_head(k + (size_t)t * dh, dh, (double)t, base);",
+                           "rope_head(k + (size_t)t * dh, dh, (double)(t + 1), base);"),
+    "window one too wide": ("const int s0 = t - W + 1 > 0 ? t - W + 1 : 0;",
+                            "const int s0 = t - W > 0 ? t - W : 0;"),
+    "scores not scaled": ("score[s] = d * scale;", "score[s] = d;"),
+    "output projection on q": ("linear_rows(T, DQ, Dm, o, ORACLE_F64, wo, bo, dtype, out + xoff);",
+                               "linear_rows(T, DQ, Dm, q, ORACLE_F64, wo, bo, dtype, out + xoff);"),
 }
 
 
