@@ -27,7 +27,8 @@ EXPORTS = ["rglru_prefill_workspace_bytes", "rglru_prefill_workspace_init", "rgl
            "rglru_decode_workspace_bytes", "rglru_decode_step", "conv1d_state_update",
            "rglru_prefill_workspace_flags", "rglru_status_string", "rglru_last_hip_error",
            "rglru_abi_version", "rglru_linear", "rglru_block_prefill_workspace_bytes",
-           "rglru_block_prefill"]
+           "rglru_block_prefill", "rglru_local_attention_workspace_bytes", "rglru_local_attention",
+           "rglru_local_attention_block_workspace_bytes", "rglru_local_attention_block"]
 
 _lock = threading.Lock()
 _lib = None
@@ -55,6 +56,14 @@ class rglru_proj_params(ctypes.Structure):
                 ("lin_x_w", ctypes.c_void_p), ("lin_x_b", ctypes.c_void_p),
                 ("lin_y_w", ctypes.c_void_p), ("lin_y_b", ctypes.c_void_p),
                 ("lin_out_w", ctypes.c_void_p), ("lin_out_b", ctypes.c_void_p)]
+
+
+class rglru_attn_params(ctypes.Structure):
+    _fields_ = [("D_model", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("rope_base", ctypes.c_float),
+                ("q_w", ctypes.c_void_p), ("k_w", ctypes.c_void_p), ("v_w", ctypes.c_void_p),
+                ("o_w", ctypes.c_void_p), ("o_b", ctypes.c_void_p)]
 
 
 def load_library(path: str = LIB_PATH):
@@ -94,6 +103,16 @@ def load_library(path: str = LIB_PATH):
         lib.rglru_block_prefill.argtypes = [PP, ctypes.POINTER(rglru_proj_params), I32, I32, P, P,
                                             P, P, P, P, P, SZ, P]
         lib.rglru_block_prefill.restype = ctypes.c_int
+        lib.rglru_local_attention_workspace_bytes.argtypes = [I32, I32, I32]
+        lib.rglru_local_attention_workspace_bytes.restype = SZ
+        lib.rglru_local_attention.argtypes = [I32, I32, I32, I32, ctypes.c_float, P, P, P, P, P,
+                                              SZ, P]
+        lib.rglru_local_attention.restype = ctypes.c_int
+        AP = ctypes.POINTER(rglru_attn_params)
+        lib.rglru_local_attention_block_workspace_bytes.argtypes = [AP, I32, I32]
+        lib.rglru_local_attention_block_workspace_bytes.restype = SZ
+        lib.rglru_local_attention_block.argtypes = [AP, I32, I32, P, P, P, SZ, P]
+        lib.rglru_local_attention_block.restype = ctypes.c_int
         lib.rglru_abi_version.argtypes = []
         lib.rglru_abi_version.restype = ctypes.c_int
         _lib = lib
@@ -360,3 +379,96 @@ def rglru_block_prefill(p: Params, q: ProjParams, x_in, h0=None, conv0=None, *, 
                                  _ptr(workspace.t), workspace.nbytes, _stream())
     _check(lib, st, "rglru_block_prefill")
     return out, h_last, conv_last
+
+
+# ------------------------------------------------------------------------------------------
+# local sliding-window multi-query attention
+# ------------------------------------------------------------------------------------------
+ATTN_HEAD_DIM = 256
+
+
+class DeviceBuffer:
+    """Scratch device memory for one call (uint8 tensor); needs no initialisation."""
+
+    def __init__(self, nbytes: int, device):
+        self.t = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+    @property
+    def nbytes(self) -> int:
+        return self.t.numel()
+
+
+def rglru_local_attention_workspace_bytes(B: int, T: int, n_heads: int) -> int:
+    return int(load_library().rglru_local_attention_workspace_bytes(B, T, n_heads))
+
+
+def rglru_local_attention(q, k, v, window: int, rope_base: float = 10000.0, *, out=None,
+                          workspace: DeviceBuffer | None = None):
+    """Sliding-window MQA with RoPE (bf16): q [B, T, Hq, 256], k, v [B, T, 256] (before RoPE)
+    -> o [B, T, Hq, 256]."""
+    lib = load_library()
+    B, T, Hq, dh = q.shape
+    dev = q.device
+    _need(q, "q", torch.bfloat16, (B, T, Hq, ATTN_HEAD_DIM))
+    _need(k, "k", torch.bfloat16, (B, T, ATTN_HEAD_DIM), dev)
+    _need(v, "v", torch.bfloat16, (B, T, ATTN_HEAD_DIM), dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, (B, T, Hq, ATTN_HEAD_DIM), dev)
+    if workspace is None:
+        workspace = DeviceBuffer(rglru_local_attention_workspace_bytes(B, T, Hq), dev)
+    st = lib.rglru_local_attention(B, T, Hq, int(window), float(rope_base), _ptr(q), _ptr(k),
+                                   _ptr(v), _ptr(out), _ptr(workspace.t), workspace.nbytes,
+                                   _stream())
+    _check(lib, st, "rglru_local_attention")
+    return out
+
+
+class AttnParams:
+    """The local-attention block's weights on one device (bf16, Linear weights [out, in]).
+
+    q_w [n_heads * 256, D_model]; k_w, v_w [256, D_model]; o_w [D_model, n_heads * 256];
+    o_b [D_model] or None.
+    """
+
+    def __init__(self, q_w, k_w, v_w, o_w, o_b, n_heads: int, window: int,
+                 rope_base: float = 10000.0):
+        HD, Dm = q_w.shape
+        dev = q_w.device
+        if HD != n_heads * ATTN_HEAD_DIM:
+            raise ValueError("q_w has %d rows, expected n_heads * 256 = %d"
+                             % (HD, n_heads * ATTN_HEAD_DIM))
+        _need(q_w, "q_w", torch.bfloat16, (HD, Dm), dev)
+        _need(k_w, "k_w", torch.bfloat16, (ATTN_HEAD_DIM, Dm), dev)
+        _need(v_w, "v_w", torch.bfloat16, (ATTN_HEAD_DIM, Dm), dev)
+        _need(o_w, "o_w", torch.bfloat16, (Dm, HD), dev)
+        _need(o_b, "o_b", torch.bfloat16, (Dm,), dev)
+        self.Dm, self.H, self.window, self.device = Dm, n_heads, window, dev
+        self.tensors = (q_w, k_w, v_w, o_w, o_b)
+        self.c = rglru_attn_params(Dm, n_heads, ATTN_HEAD_DIM, int(window), float(rope_base),
+                                   *[t.data_ptr() if t is not None else None
+                                     for t in self.tensors])
+
+
+def rglru_local_attention_block_workspace_bytes(a: AttnParams, B: int, T: int) -> int:
+    return int(load_library().rglru_local_attention_block_workspace_bytes(ctypes.byref(a.c), B, T))
+
+
+def rglru_local_attention_block(a: AttnParams, x_in, *, out=None,
+                                workspace: DeviceBuffer | None = None):
+    """The whole local-attention block: out [B, T, D_model] = o_proj(attention(q_proj(x_in),
+    k_proj(x_in), v_proj(x_in)))."""
+    lib = load_library()
+    B, T, Dm = x_in.shape
+    if Dm != a.Dm:
+        raise ValueError("x_in width %d does not match D_model=%d" % (Dm, a.Dm))
+    _need(x_in, "x_in", torch.bfloat16, (B, T, Dm), a.device)
+    if out is None:
+        out = torch.empty_like(x_in)
+    _need(out, "out", torch.bfloat16, (B, T, Dm), a.device)
+    if workspace is None:
+        workspace = DeviceBuffer(rglru_local_attention_block_workspace_bytes(a, B, T), a.device)
+    st = lib.rglru_local_attention_block(ctypes.byref(a.c), B, T, _ptr(x_in), _ptr(out),
+                                         _ptr(workspace.t), workspace.nbytes, _stream())
+    _check(lib, st, "rglru_local_attention_block")
+    return out

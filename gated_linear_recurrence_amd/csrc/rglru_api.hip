@@ -2,6 +2,7 @@
 // Every check runs on the host before any HIP call; see include/rglru.h for the contract.
 #include <hip/hip_runtime.h>
 
+#include <math.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -20,6 +21,10 @@ int hip_fail(hipError_t e) {
 }
 
 size_t elem_size(int dtype) { return dtype == RGLRU_BF16 ? 2 : 4; }
+
+size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+constexpr int kAttnDh = 256;  // the attention's head width
 
 bool aligned16(const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; }
 
@@ -266,8 +271,8 @@ int rglru_linear(int32_t M, int32_t K, int32_t N, const void* x, const void* w, 
     if (M == 0) return RGLRU_OK;
     ProjGemmArgs g;
     memset(&g, 0, sizeof g);
-    g.A = x; g.W0 = w; g.b0 = b; g.C0 = out;
-    g.M = M; g.K = K; g.N0 = N; g.n_out = 1;
+    g.A = x; g.W[0] = w; g.b[0] = b; g.C[0] = out;
+    g.M = M; g.K = K; g.Nw[0] = N; g.nseg = 1;
     hipError_t e = launch_proj_gemm(g, (hipStream_t)stream);
     return e == hipSuccess ? RGLRU_OK : hip_fail(e);
 }
@@ -331,15 +336,133 @@ int rglru_block_prefill(const rglru_params* p, const rglru_proj_params* q, int32
     const int M = B * T;
     ProjGemmArgs g;
     memset(&g, 0, sizeof g);
-    g.A = x_in; g.W0 = q->lin_x_w; g.W1 = q->lin_y_w; g.b0 = q->lin_x_b; g.b1 = q->lin_y_b;
-    g.C0 = xb; g.C1 = yb; g.M = M; g.K = Dm; g.N0 = D; g.n_out = 2;
+    g.A = x_in; g.W[0] = q->lin_x_w; g.W[1] = q->lin_y_w; g.b[0] = q->lin_x_b; g.b[1] = q->lin_y_b;
+    g.C[0] = xb; g.C[1] = yb; g.M = M; g.K = Dm; g.Nw[0] = D; g.Nw[1] = D; g.nseg = 2;
     hipError_t e = launch_proj_gemm(g, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e);
     st = rglru_prefill(p, B, T, xb, yb, mg, h0, h_last, conv0, conv_last, workspace, pw, stream);
     if (st != RGLRU_OK) return st;
     memset(&g, 0, sizeof g);
-    g.A = mg; g.W0 = q->lin_out_w; g.b0 = q->lin_out_b; g.C0 = out;
-    g.M = M; g.K = D; g.N0 = Dm; g.n_out = 1;
+    g.A = mg; g.W[0] = q->lin_out_w; g.b[0] = q->lin_out_b; g.C[0] = out;
+    g.M = M; g.K = D; g.Nw[0] = Dm; g.nseg = 1;
+    e = launch_proj_gemm(g, (hipStream_t)stream);
+    return e == hipSuccess ? RGLRU_OK : hip_fail(e);
+}
+
+// ------------------------------------------------------------------------------------------
+// local sliding-window multi-query attention
+// ------------------------------------------------------------------------------------------
+size_t rglru_local_attention_workspace_bytes(int32_t B, int32_t T, int32_t n_heads) {
+    if (B < 1 || T < 0 || n_heads < 1) return 0;
+    const size_t M = (size_t)B * (size_t)T, T4 = ((size_t)T + 3) / 4;
+    return round256(M * n_heads * kAttnDh * 2) + round256(M * kAttnDh * 2) +
+           round256((size_t)B * T4 * kAttnDh * 4 * 2);
+}
+
+int rglru_local_attention(int32_t B, int32_t T, int32_t n_heads, int32_t window, float rope_base,
+                          const void* q, const void* k, const void* v, void* o, void* workspace,
+                          size_t ws_bytes, void* stream) {
+    if (B < 1 || T < 0 || n_heads < 1 || n_heads > 64 || window < 1 || !(rope_base > 1.0f) ||
+        !(rope_base < INFINITY))
+        return RGLRU_ERR_SHAPE;
+    const long long T4 = ((long long)T + 3) / 4;
+    if (T >= (1 << 22) || (long long)B * 4 * T4 >= (1LL << 24) ||
+        (long long)B * n_heads * (((long long)T + 127) / 128) >= (1LL << 24))
+        return RGLRU_ERR_UNSUPPORTED;
+    if (T > 0 && (!q || !k || !v || !o)) return RGLRU_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(workspace))
+        return RGLRU_ERR_UNSUPPORTED;
+    const size_t M = (size_t)B * T;
+    const size_t nq = M * n_heads * kAttnDh * 2, nk = M * kAttnDh * 2;
+    const size_t need = rglru_local_attention_workspace_bytes(B, T, n_heads);
+    if (T > 0 && (!workspace || ws_bytes < need)) return RGLRU_ERR_WORKSPACE;
+    if (overlap(o, nq, q, nq) || overlap(o, nq, k, nk) || overlap(o, nq, v, nk))
+        return RGLRU_ERR_ALIAS;
+    if (T > 0 && (overlap(workspace, need, q, nq) || overlap(workspace, need, k, nk) ||
+                  overlap(workspace, need, v, nk) || overlap(workspace, need, o, nq)))
+        return RGLRU_ERR_ALIAS;
+    if (T == 0) return RGLRU_OK;
+    AttnArgs a;
+    a.q = q; a.k = k; a.v = v; a.o = o;
+    char* ws = static_cast<char*>(workspace);
+    a.qr = ws;
+    a.kr = ws + round256(nq);
+    a.v4 = ws + round256(nq) + round256(nk);
+    a.B = B; a.T = T; a.Hq = n_heads; a.W = window; a.T4 = (int)T4; a.rope_base = rope_base;
+    hipError_t e = launch_attention(a, (hipStream_t)stream);
+    return e == hipSuccess ? RGLRU_OK : hip_fail(e);
+}
+
+size_t rglru_local_attention_block_workspace_bytes(const rglru_attn_params* a, int32_t B,
+                                                   int32_t T) {
+    if (!a || B < 1 || T < 0 || a->n_heads < 1) return 0;
+    const size_t M = (size_t)B * (size_t)T;
+    const size_t nq = round256(M * a->n_heads * kAttnDh * 2), nk = round256(M * kAttnDh * 2);
+    // q, k, v (projections), the attention output, then the attention's own workspace
+    return 2 * nq + 2 * nk + rglru_local_attention_workspace_bytes(B, T, a->n_heads);
+}
+
+int rglru_local_attention_block(const rglru_attn_params* a, int32_t B, int32_t T,
+                                const void* x_in, void* out, void* workspace, size_t ws_bytes,
+                                void* stream) {
+    if (!a) return RGLRU_ERR_NULL;
+    if (a->head_dim != kAttnDh) return RGLRU_ERR_UNSUPPORTED;
+    if (B < 1 || T < 0 || a->D_model < 1 || a->n_heads < 1 || a->n_heads > 64 || a->window < 1 ||
+        !(a->rope_base > 1.0f) || !(a->rope_base < INFINITY))
+        return RGLRU_ERR_SHAPE;
+    const int Dm = a->D_model, Hq = a->n_heads;
+    if (Dm % 256 != 0 || Dm >= (1 << 21)) return RGLRU_ERR_UNSUPPORTED;
+    if (!a->q_w || !a->k_w || !a->v_w || !a->o_w) return RGLRU_ERR_NULL;
+    if (T > 0 && (!x_in || !out)) return RGLRU_ERR_NULL;
+    const void* ptrs[] = {a->q_w, a->k_w, a->v_w, a->o_w, a->o_b, x_in, out, workspace};
+    for (const void* ptr : ptrs)
+        if (!aligned16(ptr)) return RGLRU_ERR_UNSUPPORTED;
+    const size_t M = (size_t)B * T;
+    const size_t need = rglru_local_attention_block_workspace_bytes(a, B, T);
+    if (T > 0 && (!workspace || ws_bytes < need)) return RGLRU_ERR_WORKSPACE;
+    const size_t n_io = M * Dm * 2, HD = (size_t)Hq * kAttnDh;
+    const size_t ins_len[] = {n_io, HD * Dm * 2, (size_t)kAttnDh * Dm * 2,
+                              (size_t)kAttnDh * Dm * 2, HD * Dm * 2, (size_t)Dm * 2};
+    const void* ins[] = {x_in, a->q_w, a->k_w, a->v_w, a->o_w, a->o_b};
+    for (int i = 0; i < 6; ++i)
+        if (overlap(out, n_io, ins[i], ins_len[i])) return RGLRU_ERR_ALIAS;
+    if (T > 0) {
+        if (overlap(workspace, need, out, n_io)) return RGLRU_ERR_ALIAS;
+        for (int i = 0; i < 6; ++i)
+            if (overlap(workspace, need, ins[i], ins_len[i])) return RGLRU_ERR_ALIAS;
+    }
+    const size_t nq = round256(M * HD * 2), nk = round256(M * kAttnDh * 2);
+    char* ws = static_cast<char*>(workspace);
+    void* qb = T > 0 ? ws : nullptr;
+    void* kb = T > 0 ? ws + nq : nullptr;
+    void* vb = T > 0 ? ws + nq + nk : nullptr;
+    void* ob = T > 0 ? ws + nq + 2 * nk : nullptr;
+    void* aw = T > 0 ? ws + 2 * nq + 2 * nk : nullptr;
+    const size_t aw_bytes = rglru_local_attention_workspace_bytes(B, T, Hq);
+    // the attention's own checks, before anything is launched
+    int st = rglru_local_attention(B, 0, Hq, a->window, a->rope_base, qb, kb, vb, ob, aw,
+                                   aw_bytes, stream);
+    if (st != RGLRU_OK) return st;
+    const long long T4 = ((long long)T + 3) / 4;
+    if (T >= (1 << 22) || (long long)B * 4 * T4 >= (1LL << 24) ||
+        (long long)B * Hq * (((long long)T + 127) / 128) >= (1LL << 24) ||
+        M >= ((size_t)1 << 31))
+        return RGLRU_ERR_UNSUPPORTED;
+    if (T == 0) return RGLRU_OK;
+
+    ProjGemmArgs g;
+    memset(&g, 0, sizeof g);
+    g.A = x_in; g.W[0] = a->q_w; g.W[1] = a->k_w; g.W[2] = a->v_w;
+    g.C[0] = qb; g.C[1] = kb; g.C[2] = vb;
+    g.M = (int)M; g.K = Dm; g.Nw[0] = (int)HD; g.Nw[1] = kAttnDh; g.Nw[2] = kAttnDh; g.nseg = 3;
+    hipError_t e = launch_proj_gemm(g, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e);
+    st = rglru_local_attention(B, T, Hq, a->window, a->rope_base, qb, kb, vb, ob, aw, aw_bytes,
+                               stream);
+    if (st != RGLRU_OK) return st;
+    memset(&g, 0, sizeof g);
+    g.A = ob; g.W[0] = a->o_w; g.b[0] = a->o_b; g.C[0] = out;
+    g.M = (int)M; g.K = (int)HD; g.Nw[0] = Dm; g.nseg = 1;
     e = launch_proj_gemm(g, (hipStream_t)stream);
     return e == hipSuccess ? RGLRU_OK : hip_fail(e);
 }

@@ -1,0 +1,270 @@
+// Local sliding-window multi-query attention, for gfx950 (CDNA4): the model's other
+// temporal-mixing block.  The page "Gemma 詳解：RecurrentGemma 架構" (section "含區域 MQA 的殘差
+// 區塊" and the printout's RecurrentGemmaSdpaAttention) gives Hq query heads of dh = 256
+// sharing one key/value head (multi-query attention), rotary position embedding on q and k as in
+// base Gemma, and attention restricted to a fixed window of past tokens (section "區域注意力視窗
+// 大小": 2k).  Here query t attends to tokens t - W + 1 .. t:
+//
+//   o[t, h] = sum_s softmax_s(q[t, h] . k[s] / sqrt(dh)) v[s]
+//
+// after RoPE turns each pair (x_i, x_{i + dh/2}) of q and k by t * base^(-2 i / dh).
+//
+// Two kernels:
+//   attn_prep_kernel  RoPE on q and k (angles in fp64), and v regrouped in fours of keys,
+//                     [B][T/4][dh][4], the order in which the P.V MFMA reads it;
+//   attn_fwd_kernel   one workgroup per (sequence, head, 128 queries); each wave holds 32
+//                     queries.  Scores are formed transposed, S^T = K Q^T (keys x queries), so a
+//                     lane owns one query: the softmax runs within the lane (and its partner
+//                     lane, which holds the query's other 16 keys).  The v_mfma_f32_32x32x16_bf16
+//                     result puts keys 8 g + 4 (l / 32) + i in register 4 g + i; taking registers
+//                     8 k .. 8 k + 7 as the K slice of the next MFMA, the probabilities feed
+//                     O^T += V^T P^T straight from registers, with V read as two groups of four
+//                     keys per lane.  Keys arrive in tiles of 32 (K 16 KB, V 16 KB) through two
+//                     LDS stages, copied by LDS-DMA one tile ahead.  The online softmax
+//                     keeps a reference maximum per query and rescales the output only when a
+//                     tile's maximum exceeds it by 2^8 (in exp2 units); the normaliser uses the
+//                     same reference, so the result is exact, and rescaling is rare.
+#include <math.h>
+
+#include "rglru_device.h"
+#include "rglru_internal.h"
+#include "rglru_lds_copy.h"
+
+namespace rglru {
+namespace {
+
+constexpr int kDh = 256;       // head dimension
+constexpr int kQB = 128;       // queries per workgroup (4 waves of 32)
+constexpr int kKB = 32;        // keys per tile
+constexpr int kAttnThreads = 256;
+constexpr float kRescale = 8.0f;  // exp2 units: rescale when a tile maximum exceeds the reference by 2^8
+
+// ---------------------------------------------------------------------------------------
+// prep: one workgroup per token row t in [0, 4 ceil(T / 4)) of one sequence
+// ---------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) attn_prep_kernel(AttnArgs a) {
+    const int rows = 4 * a.T4;
+    const int b = blockIdx.x / rows, t = blockIdx.x % rows;
+    const int tid = threadIdx.x;
+    const bool valid = t < a.T;
+    const size_t m = (size_t)b * a.T + (valid ? t : 0);
+    // v, regrouped: v4[b][t / 4][d][t % 4]; rows past T are zero (their weight is 0, but a
+    // non-finite value times 0 would not be)
+    const uint16_t* v = static_cast<const uint16_t*>(a.v);
+    uint16_t* v4 = static_cast<uint16_t*>(a.v4);
+    v4[(((size_t)b * a.T4 + t / 4) * kDh + tid) * 4 + (t & 3)] = valid ? v[m * kDh + tid] : 0;
+    if (!valid) return;
+    // RoPE: pair i of a head, (x_i, x_{i+128}), turned by t * base^(-2 i / 256)
+    const int HD = a.Hq * kDh;
+    const uint16_t* q = static_cast<const uint16_t*>(a.q) + m * HD;
+    const uint16_t* k = static_cast<const uint16_t*>(a.k) + m * kDh;
+    uint16_t* qr = static_cast<uint16_t*>(a.qr) + m * HD;
+    uint16_t* kr = static_cast<uint16_t*>(a.kr) + m * kDh;
+    // the angle depends on (t, i) only: thread tid turns pair i = tid % 128 of heads
+    // tid / 128, tid / 128 + 2, ... (the key head counted as head Hq)
+    const int i = tid % (kDh / 2);
+    const double ang = (double)t * exp2(-2.0 * (double)i / (double)kDh * log2((double)a.rope_base));
+    double sn_d, cs_d;
+    sincos(ang, &sn_d, &cs_d);
+    const float sn = (float)sn_d, cs = (float)cs_d;
+    for (int h = tid / (kDh / 2); h <= a.Hq; h += 2) {
+        const uint16_t* src = h < a.Hq ? q + h * kDh : k;
+        uint16_t* dst = h < a.Hq ? qr + h * kDh : kr;
+        const float x0 = bf2f(src[i]), x1 = bf2f(src[i + kDh / 2]);
+        dst[i] = f2bf(x0 * cs - x1 * sn);
+        dst[i + kDh / 2] = f2bf(x1 * cs + x0 * sn);
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// attention
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// One K/V tile of 32 keys, copied straight into an LDS stage: each wave issues 8 copies of
+// 1 KB, 4 of K and 4 of V, lane l of copy i filling stage chunk p = 64 (4 wave + i) + l.
+//   K stage: [key][32 chunks of 8 dims]; chunk c of key r sits at position c ^ (r % 16), so the
+//   16 lanes of a fragment read (16 keys, one chunk index) hit 16 distinct bank groups.
+//   V stage: 8 groups of 4 keys x 256 dims x 4 keys, a contiguous 16 KB slice of v4.
+// Keys past T repeat the last key (finite; their weight is 0).  rk / rv address one sequence's
+// k and v4.
+__device__ __forceinline__ void copy_tile(const u32x4& rk, const u32x4& rv, uint16_t* kl,
+                                          uint16_t* vl, int T, int T4, int kt, int wv, int lane) {
+    int ok[4], ov[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int p = (4 * wv + i) * 64 + lane;
+        const int key = p >> 5, pos = p & 31;
+        const int c = pos ^ (key & 15);
+        ok[i] = (min(kt * kKB + key, T - 1) * kDh + c * 8) * 2;
+        const int g = min(kt * (kKB / 4) + (p >> 7), T4 - 1);
+        ov[i] = (g * (kDh * 4) + (p & 127) * 8) * 2;
+    }
+    copy4(rk, lds_address(kl + 4 * wv * 512), ok);
+    copy4(rv, lds_address(vl + 4 * wv * 512), ov);
+}
+
+// Four consecutive bf16 keys of one dimension (8 bytes) from a V stage.
+__device__ __forceinline__ uint2 v_quad(const uint16_t* vl, int g, int d) {
+    return *reinterpret_cast<const uint2*>(vl + (g * kDh + d) * 4);
+}
+
+__global__ void __launch_bounds__(kAttnThreads, 1) attn_fwd_kernel(AttnArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t k0[kKB * kDh], k1[kKB * kDh];
+    __shared__ __attribute__((aligned(16))) uint16_t v0[kKB * kDh], v1[kKB * kDh];
+
+    const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nqb = (a.T + kQB - 1) / kQB;
+    const int qb = blockIdx.x % nqb;
+    const int bh = blockIdx.x / nqb;
+    const int h = bh % a.Hq, b = bh / a.Hq;
+    const int q0 = qb * kQB;
+    const int t0w = q0 + 32 * wv;                  // this wave's first query
+    const int tq = t0w + (lane & 31);              // this lane's query
+    const int W = a.W, T = a.T;
+
+    // Q fragments (B operand of S^T = K Q^T): query tq, dims 16 kk + 8 hl .. + 7
+    bf16x8 qf[16];
+    {
+        const uint16_t* qrow = static_cast<const uint16_t*>(a.qr) +
+                               ((size_t)b * T + min(tq, T - 1)) * ((size_t)a.Hq * kDh) + h * kDh;
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk)
+            qf[kk] = *reinterpret_cast<const bf16x8*>(qrow + 16 * kk + 8 * hl);
+    }
+
+    f32x16 oacc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[j][e] = 0.0f;
+    float mref = -1e30f;                            // reference maximum (exp2 units)
+    float lsum = 0.0f;                              // this lane's share of the normaliser
+    const float sc = kLog2e * 0.0625f;              // log2(e) / sqrt(256)
+
+    const int klo = max(0, q0 - W + 1);
+    const int khi = min(T - 1, q0 + kQB - 1);
+    const int ktlo = klo / kKB, kthi = khi / kKB;
+
+    const uint16_t* kseq = static_cast<const uint16_t*>(a.kr) + (size_t)b * T * kDh;
+    const uint16_t* vseq = static_cast<const uint16_t*>(a.v4) + (size_t)b * a.T4 * (kDh * 4);
+    const u32x4 rk = rsrc_words(kseq, (uint32_t)T * kDh * 2);
+    const u32x4 rv = rsrc_words(vseq, (uint32_t)a.T4 * kDh * 4 * 2);
+    guard_vmem_sgprs(rk, rv);
+    // Q fragments are loaded (and waited for) before the first copy: from here on the copies
+    // are this wave's only vector-memory instructions until the stores at the end.
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    copy_tile(rk, rv, k0, v0, T, a.T4, ktlo, wv, lane);
+
+    for (int kt = ktlo; kt <= kthi; ++kt) {
+        const bool odd = ((kt - ktlo) & 1) != 0;
+        uint16_t* kc = odd ? k1 : k0;
+        uint16_t* vc = odd ? v1 : v0;
+        // this wave's copies of tile kt (the only ones in flight) have landed; after the barrier
+        // every wave's have, and every wave is done with tile kt - 1, whose stage takes kt + 1
+        wait_vmcnt<0>();
+        lds_sync();
+        if (kt + 1 <= kthi) copy_tile(rk, rv, odd ? k0 : k1, odd ? v0 : v1, T, a.T4, kt + 1, wv, lane);
+        const int key0 = kt * kKB;
+        // does any key of this tile fall in any window of this wave's queries?
+        const bool live = key0 <= t0w + 31 && key0 + kKB - 1 > t0w - W;
+        if (live) {
+            f32x16 s;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) s[e] = 0.0f;
+            const int kr_ = lane & 31;
+            // fragment reads in groups of four, so that at most eight are in flight (left
+            // free, the compiler hoisted all of them and ran out of registers)
+#pragma unroll
+            for (int kk = 0; kk < 16; ++kk) {
+                const int pos = (2 * kk + hl) ^ (kr_ & 15);
+                const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kc + kr_ * kDh + pos * 8);
+                s = mfma32(kf, qf[kk], s);
+                if ((kk & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+            }
+            // scale; mask only on tiles that cross a window edge or the sequence end
+            const bool edge = key0 + kKB - 1 > t0w || key0 <= t0w + 31 - W || key0 + kKB > T;
+            float x[16];
+            float tmax = -INFINITY;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                float v = s[e] * sc;
+                if (edge) {
+                    const int key = key0 + mfma_d_row(lane, e);
+                    if (key > tq || key <= tq - W || key >= T) v = -INFINITY;
+                }
+                x[e] = v;
+                tmax = fmaxf(tmax, v);
+            }
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            const bool need = tmax > mref + kRescale;
+            if (__any(need)) {
+                const float al = need ? __builtin_amdgcn_exp2f(mref - tmax) : 1.0f;
+                if (need) mref = tmax;
+                lsum *= al;
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) oacc[j][e] *= al;
+            }
+            float p[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                p[e] = __builtin_amdgcn_exp2f(x[e] - mref);
+                lsum += p[e];
+            }
+            bf16x8 pf[2];
+#pragma unroll
+            for (int kq = 0; kq < 2; ++kq)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) pf[kq][i] = (__bf16)p[8 * kq + i];
+            // O^T[j] += V^T P^T: dims 32 j + l % 32; keys 16 kq + 4 hl + {0..3} and {8..11}
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int d = 32 * j + (lane & 31);
+#pragma unroll
+                for (int kq = 0; kq < 2; ++kq) {
+                    const uint2 lo = v_quad(vc, 4 * kq + hl, d);
+                    const uint2 hi = v_quad(vc, 4 * kq + hl + 2, d);
+                    const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+                    oacc[j] = mfma32(vf, pf[kq], oacc[j]);
+                }
+                if ((j & 1) == 1) __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+
+    // normalise and store: O^T tile j, register 4 g + i -> dim 32 j + 8 g + 4 hl + i
+    const float lt = lsum + __shfl_xor(lsum, 32);
+    const float inv = 1.0f / lt;
+    if (tq < T) {
+        uint16_t* orow = static_cast<uint16_t*>(a.o) + ((size_t)b * T + tq) * ((size_t)a.Hq * kDh) +
+                         h * kDh;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d = 32 * j + 8 * g + 4 * hl;
+                *reinterpret_cast<uint2*>(orow + d) =
+                    make_uint2(pack2bf(oacc[j][4 * g] * inv, oacc[j][4 * g + 1] * inv),
+                               pack2bf(oacc[j][4 * g + 2] * inv, oacc[j][4 * g + 3] * inv));
+            }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
+    if (a.T == 0) return hipSuccess;
+    hipLaunchKernelGGL(attn_prep_kernel, dim3((unsigned)(a.B * 4 * a.T4)), dim3(256), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long long blocks = (long long)a.B * a.Hq * ((a.T + kQB - 1) / kQB);
+    hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)blocks), dim3(kAttnThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace rglru

@@ -65,18 +65,31 @@ struct ConvArgs {
     int N, T, D;
 };
 
-// One Linear layer (or the two branch projections side by side) as a bf16 GEMM:
-// C_o[m][n] = b_o[n] + sum_k A[m][k] W_o[n][k] for output o < n_out, each [M][N0].
+// One Linear layer, or up to three side by side over the same input (the block's branch
+// projections; the attention block's q, k and v), as a bf16 GEMM: output segment o has width
+// Nw[o] and C_o[m][n] = b_o[n] + sum_k A[m][k] W_o[n][k], each C_o [M][Nw[o]].
 struct ProjGemmArgs {
     const void* A;               // [M][K]
-    const void* W0;              // [N0][K]
-    const void* W1;              // [N0][K] (n_out == 2) or null
-    const void* b0;              // [N0] or null
-    const void* b1;
-    void* C0;                    // [M][N0]
-    void* C1;
-    int M, K, N0, n_out;         // N0 % 256 == 0, K % 128 == 0, 256 * N0 < 2^31
+    const void* W[3];            // [Nw[o]][K]
+    const void* b[3];            // [Nw[o]] or null
+    void* C[3];                  // [M][Nw[o]]
+    int Nw[3];                   // multiples of 256 (unused segments 0)
+    int nseg;                    // 1 .. 3
+    int M, K;                    // K % 128 == 0, 256 * Nw < 2^31
     int ntm, ntn;                // set by the launcher
+};
+
+// Local sliding-window multi-query attention (head dim 256).
+struct AttnArgs {
+    const void* q;       // [B][T][Hq * 256] before RoPE
+    const void* k;       // [B][T][256]
+    const void* v;       // [B][T][256]
+    void* qr;            // workspace: q after RoPE
+    void* kr;            // workspace: k after RoPE
+    void* v4;            // workspace: v regrouped [B][T4][256][4]
+    void* o;             // [B][T][Hq * 256]
+    int B, T, Hq, W, T4; // T4 = ceil(T / 4)
+    float rope_base;
 };
 
 int device_cu_count();  // compute units of the current device (cached)
@@ -86,5 +99,6 @@ hipError_t launch_workspace_init(void* ws, size_t bytes, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int bs, hipStream_t s);
 hipError_t launch_conv_update(const ConvArgs& a, int dtype, hipStream_t s);
 hipError_t launch_proj_gemm(const ProjGemmArgs& a, hipStream_t s);
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 
 }  // namespace rglru

@@ -10,7 +10,8 @@
 //
 // Here: bf16 operands, fp32 accumulation on MFMA, bf16 results (round to nearest even).  The
 // two branch projections run as one GEMM with N = 2 D: output tiles left of D read linear_x's
-// weight and write x, the others read linear_y's weight and write y.
+// weight and write x, the others read linear_y's weight and write y (up to three such output
+// segments; the attention block's q, k and v are another use).
 //
 // Workgroup tile 256 x 256, four waves of 128 x 128 (4 x 4 tiles of v_mfma_f32_32x32x16_bf16,
 // 256 fp32 accumulators per lane, in AGPRs).  K advances in steps of 64 through two LDS stages
@@ -21,12 +22,12 @@
 
 #include "rglru_device.h"
 #include "rglru_internal.h"
+#include "rglru_lds_copy.h"
 
 namespace rglru {
 namespace {
 
 typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBM = 256;                    // tile rows (M)
 constexpr int kBN = 256;                    // tile columns (N)
@@ -46,45 +47,6 @@ static_assert(kChunks == 8 && kCopiesPerWave == 8, "the swizzle and copies are f
 // 256-byte bank line (and any 8 consecutive rows in distinct groups of a 128-byte line).
 __device__ __forceinline__ int chunk_pos(int r, int c) { return c ^ ((r ^ (r >> 3)) & 7); }
 
-// Four global -> LDS copies of 1 KB (buffer_load_dwordx4 with the LDS bit: lane l's 16 bytes go
-// to LDS byte M0 + 16 l), to consecutive 1 KB destinations from lds_addr.
-//
-// Written as inline assembly on purpose: the compiler's wait insertion cannot tell the LDS
-// stages apart, and made the fragment reads after each refill wait for that refill to land (a
-// memory round trip per k-step).  Hidden from it, the copies are waited for only where the
-// kernel says so: each wave waits for its own copies (vmcnt) before the barrier that publishes
-// a stage, and no other vector-memory instruction runs while copies are in flight.  The block
-// has no output register (the data goes to LDS); it saves M0, steps it through the 1 KB
-// destinations (one wait state after each write before its use) and restores it.  The resource
-// words are not written by the VALU inside the loop; before the first copies the prologue
-// waits the 5 states a buffer instruction needs after a VALU write of its SGPRs
-// (guard_vmem_sgprs).
-__device__ __forceinline__ void copy4(const u32x4& rs, uint32_t lds_addr, const int (&off)[4]) {
-    uint32_t keep;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %5\n\t"
-        "s_nop 0\n\t"
-        "buffer_load_dwordx4 %1, %6, 0 offen lds\n\t"
-        "s_add_u32 m0, m0, 0x400\n\t"
-        "s_nop 0\n\t"
-        "buffer_load_dwordx4 %2, %6, 0 offen lds\n\t"
-        "s_add_u32 m0, m0, 0x400\n\t"
-        "s_nop 0\n\t"
-        "buffer_load_dwordx4 %3, %6, 0 offen lds\n\t"
-        "s_add_u32 m0, m0, 0x400\n\t"
-        "s_nop 0\n\t"
-        "buffer_load_dwordx4 %4, %6, 0 offen lds\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(keep)
-        : "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "s"(lds_addr), "s"(rs)
-        : "memory", "scc");
-}
-
-__device__ __forceinline__ uint32_t lds_address(const void* p) {
-    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
-}
-
 // Half of one operand's copies of k-step kt into an LDS stage (this wave's copies 4 h .. 4 h + 3
 // of its 8).  Lane l of copy q fills LDS chunk p = 64 q + l of the stage (row p / 8, position
 // p % 8), so the global side reads the chunk that belongs there (the swizzle is its own
@@ -101,18 +63,6 @@ __device__ __forceinline__ void copy_half(const u32x4& rs, uint16_t* lds, int h,
         off[j] = min(r, rows - 1) * K * 2 + kt * kRowBytes + 16 * c;
     }
     copy4(rs, lds_address(lds + (wv * kCopiesPerWave + 4 * h) * 512), off);
-}
-
-// Five wait states after the resource words were last written (they are built from
-// v_readfirstlane results: a buffer instruction reading SGPRs that the VALU wrote needs 5).
-__device__ __forceinline__ void guard_vmem_sgprs(const u32x4& a, const u32x4& b) {
-    asm volatile("s_nop 4" ::"s"(a), "s"(b));
-}
-
-// A buffer resource as four dwords (base, stride 0, byte range, format word) for the copies.
-__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
-    const uint64_t p = (uint64_t)(uintptr_t)base;
-    return u32x4{(uint32_t)p, (uint32_t)(p >> 32) & 0xffffu, bytes, 0x00020000u};
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_n(const void* base, uint32_t bytes) {
@@ -169,16 +119,6 @@ __device__ __forceinline__ void mma_pipe(const bf16x8 (&a)[4], const bf16x8 (&b)
     }
 }
 
-// vmcnt(n) with the other counters left alone (gfx9 encoding: vmcnt bits 3:0 and 15:14)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
-}
-
-// Barrier over LDS accesses (each wave has waited for its own copies before it arrives).
-__device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
 // Workgroup -> output tile.  Workgroups go to the 8 XCDs round-robin; each XCD is given one
 // contiguous range of the tile order, and the tile order walks groups of kGroupM tile rows
 // column by column, so the ~32 workgroups an XCD runs at once share A rows and W rows in its L2.
@@ -207,12 +147,13 @@ __global__ void __launch_bounds__(kThreads, 1) proj_gemm_kernel(ProjGemmArgs g) 
     // built from it must sit in scalar registers
     const int m0 = __builtin_amdgcn_readfirstlane(tm) * kBM;
     const int n0 = __builtin_amdgcn_readfirstlane(tn) * kBN;
-    const bool second = n0 >= g.N0;               // the y half of the branch projections
-    const int nl0 = second ? n0 - g.N0 : n0;
+    // output segment of this tile (segment widths are multiples of the tile width)
+    const int seg = n0 < g.Nw[0] ? 0 : (n0 < g.Nw[0] + g.Nw[1] ? 1 : 2);
+    const int nl0 = n0 - (seg > 0 ? g.Nw[0] : 0) - (seg > 1 ? g.Nw[1] : 0);
     const int K = g.K;
     const int rows = min(g.M - m0, kBM);
     const uint16_t* A = static_cast<const uint16_t*>(g.A) + (size_t)m0 * K;
-    const uint16_t* W = static_cast<const uint16_t*>(second ? g.W1 : g.W0) + (size_t)nl0 * K;
+    const uint16_t* W = static_cast<const uint16_t*>(g.W[seg]) + (size_t)nl0 * K;
     const u32x4 ra = rsrc_words(A, (uint32_t)(rows * K * 2));
     const u32x4 rb = rsrc_words(W, (uint32_t)(kBN * K * 2));
     const int KT = K / kBK;                       // even, >= 2
@@ -296,9 +237,9 @@ __global__ void __launch_bounds__(kThreads, 1) proj_gemm_kernel(ProjGemmArgs g) 
     // bias, round, store.  acc[i][j] is the transposed 32 x 32 tile: lane l holds output row
     // 32 i + l % 32 and, in registers 4 q .. 4 q + 3, output columns 32 j + 8 q + 4 (l / 32) + 0..3.
     // The buffer's range ends at the last valid row, so stores of rows past a ragged M are dropped.
-    const uint16_t* bias = static_cast<const uint16_t*>(second ? g.b1 : g.b0);
-    const int ldc = g.N0;
-    uint16_t* C = static_cast<uint16_t*>(second ? g.C1 : g.C0) + (size_t)m0 * ldc + nl0;
+    const uint16_t* bias = static_cast<const uint16_t*>(g.b[seg]);
+    const int ldc = g.Nw[seg];
+    uint16_t* C = static_cast<uint16_t*>(g.C[seg]) + (size_t)m0 * ldc + nl0;
     const __amdgpu_buffer_rsrc_t rc = make_rsrc_n(C, (uint32_t)(rows * ldc * 2));
     const int ncol = 128 * wn + 4 * (lane >> 5);
     const int mrow = 128 * wm + (lane & 31);
@@ -330,7 +271,7 @@ __global__ void __launch_bounds__(kThreads, 1) proj_gemm_kernel(ProjGemmArgs g) 
 hipError_t launch_proj_gemm(const ProjGemmArgs& a_in, hipStream_t s) {
     ProjGemmArgs a = a_in;
     a.ntm = (a.M + kBM - 1) / kBM;
-    a.ntn = a.n_out * a.N0 / kBN;
+    a.ntn = (a.Nw[0] + a.Nw[1] + a.Nw[2]) / kBN;
     const long long tiles = (long long)a.ntm * a.ntn;
     if (tiles <= 0) return hipSuccess;
     hipLaunchKernelGGL(proj_gemm_kernel, dim3((unsigned)tiles), dim3(kThreads), 0, s, a);

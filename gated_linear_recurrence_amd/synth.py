@@ -32,7 +32,16 @@ ACT_BLOCK = 1024  # tokens per activation stream block
 _TID = {"lambda": 0, "wa": 1, "wx": 2, "ba": 3, "bx": 4, "conv_w": 5, "conv_b": 6, "h0": 7,
         "x": 8, "y": 9,
         # the block's dense projections and its input (x_in feeds linear_x and linear_y)
-        "lx_w": 10, "lx_b": 11, "ly_w": 12, "ly_b": 13, "lo_w": 14, "lo_b": 15, "x_in": 16}
+        "lx_w": 10, "lx_b": 11, "ly_w": 12, "ly_b": 13, "lo_w": 14, "lo_b": 15, "x_in": 16,
+        # the local-attention block's projections and the attention's own inputs
+        "q_w": 17, "k_w": 18, "v_w": 19, "o_w": 20, "o_b": 21, "q": 22, "k": 23, "v": 24}
+
+# local attention of the 2B model: 10 query heads of width 256 sharing one key/value head,
+# a window of 2048 tokens, RoPE base 10000
+ATTN_HEAD_DIM = 256
+ATTN_HEADS_2B = 10
+ATTN_WINDOW = 2048
+ROPE_BASE = 10000.0
 
 
 @dataclasses.dataclass(frozen=True)
@@ -193,3 +202,47 @@ def make_block_input(w: Workload, Dm: int | None = None, B: int | None = None,
             a = _rng(s0, _TID["x_in"], b, blk).standard_normal((ACT_BLOCK, Dm), dtype=np.float32)
             out[b, t0:t0 + n] = to_storage(a[:n], w.dtype)
     return out
+
+
+def make_attn(w: Workload, Dm: int | None = None, n_heads: int = ATTN_HEADS_2B,
+              bias: bool = False, seed: int | None = None) -> dict:
+    """The local-attention block's projections in storage form (Linear weights [out][in]).
+
+    q_w [n_heads*256, Dm], k_w, v_w [256, Dm] ~ N(0, std 1/sqrt(Dm)); o_w [Dm, n_heads*256] ~
+    N(0, std 1/sqrt(n_heads*256)); o_b zero, or N(0, std 0.1) with bias=True.
+    """
+    s0 = w.seed if seed is None else seed
+    Dm = w.D if Dm is None else Dm
+    HD = n_heads * ATTN_HEAD_DIM
+    out = {}
+    for name, shape, fan_in in (("q_w", (HD, Dm), Dm), ("k_w", (ATTN_HEAD_DIM, Dm), Dm),
+                                ("v_w", (ATTN_HEAD_DIM, Dm), Dm), ("o_w", (Dm, HD), HD)):
+        a = _rng(s0, _TID[name]).standard_normal(shape, dtype=np.float32)
+        out[name] = to_storage(a * np.float32(1.0 / math.sqrt(fan_in)), w.dtype)
+    a = (_rng(s0, _TID["o_b"]).standard_normal(Dm, dtype=np.float32) * np.float32(0.1)
+         if bias else np.zeros(Dm, np.float32))
+    out["o_b"] = to_storage(a, w.dtype)
+    return out
+
+
+def make_qkv(w: Workload, n_heads: int = ATTN_HEADS_2B, B: int | None = None,
+             T: int | None = None, seed: int | None = None):
+    """The attention's inputs before RoPE, ~ N(0, 1) in storage form, blocks of 1024 tokens:
+    q [B, T, n_heads, 256], k and v [B, T, 256]."""
+    s0 = w.seed if seed is None else seed
+    B = w.B if B is None else B
+    T = w.T if T is None else T
+    st_dtype = np.uint16 if w.dtype == BF16 else np.float32
+    res = []
+    for name, tail in (("q", (n_heads, ATTN_HEAD_DIM)), ("k", (ATTN_HEAD_DIM,)),
+                       ("v", (ATTN_HEAD_DIM,))):
+        out = np.empty((B, T) + tail, st_dtype)
+        for b in range(B):
+            for blk in range((T + ACT_BLOCK - 1) // ACT_BLOCK):
+                t0 = blk * ACT_BLOCK
+                n = min(ACT_BLOCK, T - t0)
+                a = _rng(s0, _TID[name], b, blk).standard_normal((ACT_BLOCK,) + tail,
+                                                                 dtype=np.float32)
+                out[b, t0:t0 + n] = to_storage(a[:n], w.dtype)
+        res.append(out)
+    return tuple(res)

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define RGLRU_ABI_VERSION 3
+#define RGLRU_ABI_VERSION 4
 
 enum rglru_dtype { RGLRU_F32 = 0, RGLRU_BF16 = 1 };
 
@@ -220,6 +220,63 @@ int rglru_block_prefill(const rglru_params *p, const rglru_proj_params *q, int32
                         const void *x_in, void *out, const float *h0, float *h_last,
                         const void *conv0, void *conv_last, void *workspace, size_t ws_bytes,
                         void *stream);
+
+/*
+ * Local sliding-window multi-query attention, the model's other temporal-mixing block.
+ * Operation: the page "Gemma 詳解：RecurrentGemma 架構" (section "含區域 MQA 的殘差區塊", the
+ * module printout's RecurrentGemmaSdpaAttention, and section "區域注意力視窗大小") gives n_heads
+ * query heads of width 256 sharing one key/value head, rotary position embedding on q and k,
+ * and attention limited to a window of recent tokens.  Query t attends to tokens
+ * max(0, t - window + 1) .. t of its own sequence:
+ *   q', k'   = RoPE(q, t), RoPE(k, t): each pair (x_i, x_{i+128}) of a head is turned by the angle
+ *              t * rope_base^(-2 i / 256), i = 0..127, positions t = 0..T-1 within each call
+ *   o[t, h]  = sum_s softmax_s(q'[t, h] . k'[s] / 16) v[s]
+ * bf16 storage only (fp32 scores and softmax, probabilities rounded to bf16 for the P.V
+ * product, output rounded to bf16 nearest-even).
+ *   q  [B][T][n_heads][256],  k, v  [B][T][256]   (before RoPE)
+ *   o  [B][T][n_heads][256]
+ *   workspace, ws_bytes  at least rglru_local_attention_workspace_bytes(B, T, n_heads); no
+ *                        initialisation needed
+ * B >= 1, T >= 0, 1 <= n_heads <= 64, window >= 1 and rope_base > 1, else RGLRU_ERR_SHAPE.
+ * T < 2^22, B * 4 * ceil(T / 4) < 2^24 and B * n_heads * ceil(T / 128) < 2^24 (launch sizes),
+ * else RGLRU_ERR_UNSUPPORTED.  o must not overlap q, k or v; the workspace must not overlap any
+ * other argument.  T = 0 launches nothing.
+ */
+size_t rglru_local_attention_workspace_bytes(int32_t B, int32_t T, int32_t n_heads);
+int rglru_local_attention(int32_t B, int32_t T, int32_t n_heads, int32_t window, float rope_base,
+                          const void *q, const void *k, const void *v, void *o, void *workspace,
+                          size_t ws_bytes, void *stream);
+
+/*
+ * The whole local-attention block: the projections of the page's printout (q_proj, k_proj and
+ * v_proj without bias, o_proj with bias) around rglru_local_attention:
+ *   q = x_in q_w^T,  k = x_in k_w^T,  v = x_in v_w^T,  out = attention(q, k, v) o_w^T + o_b
+ * Weights are stored like PyTorch Linear weights, [out][in], bf16:
+ *   q_w [n_heads * 256][D_model],  k_w, v_w [256][D_model],  o_w [D_model][n_heads * 256],
+ *   o_b [D_model] or NULL.
+ * head_dim must be 256 and D_model % 256 == 0, else RGLRU_ERR_UNSUPPORTED; the limits of
+ * rglru_local_attention apply.
+ *   x_in, out  [B][T][D_model];  out must not overlap x_in, the weights or the workspace
+ *   workspace, ws_bytes  at least rglru_local_attention_block_workspace_bytes(...)
+ */
+typedef struct rglru_attn_params {
+    int32_t D_model;
+    int32_t n_heads;
+    int32_t head_dim;
+    int32_t window;
+    float rope_base;
+    const void *q_w;
+    const void *k_w;
+    const void *v_w;
+    const void *o_w;
+    const void *o_b;
+} rglru_attn_params;
+
+size_t rglru_local_attention_block_workspace_bytes(const rglru_attn_params *a, int32_t B,
+                                                   int32_t T);
+int rglru_local_attention_block(const rglru_attn_params *a, int32_t B, int32_t T,
+                                const void *x_in, void *out, void *workspace, size_t ws_bytes,
+                                void *stream);
 
 /*
  * Diagnostics of a prefill workspace: copies its error flags to *flags_out (0 = none) and

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.rglru_abi_version() == 3
+    assert lib.rglru_abi_version() == 4
     for st in range(7):
         assert lib.rglru_status_string(st)
     assert lib.rglru_status_string(99) == b"unknown status"
@@ -210,3 +210,91 @@ def test_block_validation(lib):
     far = [k << 40 for k in range(1, 8)]   # buffers of several GiB that do not overlap
     kw = dict(x=far[0], out=far[1], h0=far[2], hl=far[3], c0=far[4], cl=far[5], ws=far[6])
     assert _block(lib, big, _proj(), B=1, T=262144, **kw) == UNSUP   # one bf16 branch of 2 GiB
+
+
+# ------------------------------------------------------------------------------------------
+# local attention
+# ------------------------------------------------------------------------------------------
+AQ, AK, AV, AO, AW = (0x100000000 * k for k in range(1, 6))
+
+
+def _attn(lib, B=2, T=300, Hq=4, window=64, base=10000.0, q=AQ, k=AK, v=AV, o=AO, ws=AW,
+          ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.rglru_local_attention_workspace_bytes(B, T, Hq)
+    return lib.rglru_local_attention(B, T, Hq, window, base, q, k, v, o, ws, ws_bytes, None)
+
+
+def test_attention_workspace_bytes(lib):
+    f = lib.rglru_local_attention_workspace_bytes
+    # q, k after RoPE, then v regrouped in fours of keys (padded to a multiple of 4 tokens)
+    assert f(2, 300, 4) == 2 * 300 * 4 * 512 + 2 * 300 * 512 + 2 * 75 * 2048
+    assert f(1, 5, 1) == 5 * 512 + 5 * 512 + 2 * 2048
+    assert f(1, 0, 3) == 0
+    assert f(0, 5, 1) == 0 and f(1, -1, 1) == 0 and f(1, 5, 0) == 0
+
+
+def test_attention_validation(lib):
+    # every call here fails validation (or has T = 0), so nothing is launched
+    assert _attn(lib, B=0) == SHAPE
+    assert _attn(lib, T=-1) == SHAPE
+    assert _attn(lib, Hq=0) == SHAPE and _attn(lib, Hq=65) == SHAPE
+    assert _attn(lib, window=0) == SHAPE
+    assert _attn(lib, base=1.0) == SHAPE and _attn(lib, base=float("nan")) == SHAPE
+    assert _attn(lib, base=float("inf")) == SHAPE
+    assert _attn(lib, T=1 << 22) == UNSUP                       # one sequence's k past 2 GiB
+    assert _attn(lib, B=1 << 12, T=1 << 12) == UNSUP            # too many token rows per launch
+    assert _attn(lib, q=None) == NULL and _attn(lib, o=None) == NULL
+    assert _attn(lib, T=0, q=None, k=None, v=None, o=None, ws=None, ws_bytes=0) == OK
+    assert _attn(lib, k=AK + 8) == UNSUP
+    assert _attn(lib, ws=None) == WS
+    assert _attn(lib, ws_bytes=lib.rglru_local_attention_workspace_bytes(2, 300, 4) - 1) == WS
+    assert _attn(lib, o=AQ + 512) == ALIAS                       # o overlaps q
+    assert _attn(lib, v=AO + 2 * 300 * 4 * 512 - 16) == ALIAS    # v's start inside o
+    assert _attn(lib, ws=AV + 1024) == ALIAS                     # workspace overlaps v
+
+
+def _attn_params(Dm=512, Hq=2, dh=256, window=64, base=10000.0, b=True):
+    a = binding.rglru_attn_params()
+    a.D_model, a.n_heads, a.head_dim, a.window, a.rope_base = Dm, Hq, dh, window, base
+    a.q_w, a.k_w, a.v_w, a.o_w = (0x200000000 + k * 0x1000000 for k in range(4))
+    a.o_b = 0x200000000 + 4 * 0x1000000 if b else None
+    return a
+
+
+def _attn_block(lib, a, B=2, T=100, x=AQ, out=AO, ws=AW, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.rglru_local_attention_block_workspace_bytes(ctypes.byref(a), B, T)
+    return lib.rglru_local_attention_block(ctypes.byref(a), B, T, x, out, ws, ws_bytes, None)
+
+
+def test_attention_block_workspace_bytes(lib):
+    a = _attn_params(Hq=3)
+    f = lib.rglru_local_attention_block_workspace_bytes
+    core = lib.rglru_local_attention_workspace_bytes(2, 100, 3)
+    # q and the attention output [M][Hq][256], k and v [M][256], then the attention's workspace
+    assert f(ctypes.byref(a), 2, 100) == 2 * (200 * 3 * 512) + 2 * (200 * 512) + core
+    assert f(None, 2, 100) == 0 and f(ctypes.byref(a), 0, 100) == 0
+
+
+def test_attention_block_validation(lib):
+    # every call here fails validation (or has T = 0), so nothing is launched
+    assert lib.rglru_local_attention_block(None, 1, 1, AQ, AO, AW, 1 << 30, None) == NULL
+    assert _attn_block(lib, _attn_params(dh=128)) == UNSUP
+    assert _attn_block(lib, _attn_params(Dm=384)) == UNSUP
+    assert _attn_block(lib, _attn_params(Hq=0)) == SHAPE
+    assert _attn_block(lib, _attn_params(window=0)) == SHAPE
+    assert _attn_block(lib, _attn_params(), B=0) == SHAPE
+    a = _attn_params()
+    a.k_w = None
+    assert _attn_block(lib, a) == NULL
+    a = _attn_params()
+    a.o_b = a.o_b + 4
+    assert _attn_block(lib, a) == UNSUP
+    assert _attn_block(lib, _attn_params(), x=None) == NULL
+    assert _attn_block(lib, _attn_params(), T=0, x=None, out=None, ws=None, ws_bytes=0) == OK
+    assert _attn_block(lib, _attn_params(), ws=None) == WS
+    assert _attn_block(lib, _attn_params(), out=AQ + 1024) == ALIAS     # out overlaps x_in
+    a = _attn_params()
+    assert _attn_block(lib, a, out=a.o_w) == ALIAS                      # out overlaps o_w
+    assert _attn_block(lib, a, ws=a.q_w) == ALIAS                       # workspace overlaps q_w
