@@ -79,6 +79,18 @@ __global__ void __launch_bounds__(256) attn_prep_kernel(AttnArgs a) {
 // ---------------------------------------------------------------------------------------
 // attention
 // ---------------------------------------------------------------------------------------
+// x *= f for a value held in an accumulation register.  Written out so that the output
+// accumulators stay in AGPRs across the key loop: left to itself, the compiler moved all of them
+// to VGPRs and back on every tile for the sake of this rarely taken multiply.
+__device__ __forceinline__ void scale_acc(float& x, float f) {
+    float t;
+    asm volatile("v_accvgpr_read_b32 %1, %0\n\t"
+                 "v_mul_f32 %1, %1, %2\n\t"
+                 "v_accvgpr_write_b32 %0, %1"
+                 : "+a"(x), "=&v"(t)
+                 : "v"(f));
+}
+
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -148,6 +160,10 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_fwd_kernel(AttnArgs a) {
     const int klo = max(0, q0 - W + 1);
     const int khi = min(T - 1, q0 + kQB - 1);
     const int ktlo = klo / kKB, kthi = khi / kKB;
+    // this wave's live tiles, kta .. ktb: those holding a key of some query's window, keys
+    // t0w - W + 1 .. t0w + 31 (none for a wave past the end of the sequence)
+    const int ktb = t0w < T ? min(kthi, t0w / kKB) : ktlo - 1;
+    const int kta = max(ktlo, max(0, t0w - W + 1) / kKB);
 
     const uint16_t* kseq = static_cast<const uint16_t*>(a.kr) + (size_t)b * T * kDh;
     const uint16_t* vseq = static_cast<const uint16_t*>(a.v4) + (size_t)b * a.T4 * (kDh * 4);
@@ -159,83 +175,96 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_fwd_kernel(AttnArgs a) {
     __builtin_amdgcn_s_waitcnt(0x0f70);
     copy_tile(rk, rv, k0, v0, T, a.T4, ktlo, wv, lane);
 
-    for (int kt = ktlo; kt <= kthi; ++kt) {
-        const bool odd = ((kt - ktlo) & 1) != 0;
-        uint16_t* kc = odd ? k1 : k0;
-        uint16_t* vc = odd ? v1 : v0;
-        // this wave's copies of tile kt (the only ones in flight) have landed; after the barrier
-        // every wave's have, and every wave is done with tile kt - 1, whose stage takes kt + 1
+    // One step per key tile, the same count on every wave: this wave's copies of tile kt (the
+    // only ones in flight) have landed; after the barrier every wave's have, and every wave is
+    // done with tile kt - 1, whose stage takes kt + 1.
+    auto advance = [&](int kt) {
         wait_vmcnt<0>();
         lds_sync();
-        if (kt + 1 <= kthi) copy_tile(rk, rv, odd ? k0 : k1, odd ? v0 : v1, T, a.T4, kt + 1, wv, lane);
+        if (kt + 1 <= kthi) {
+            const bool odd = ((kt - ktlo) & 1) != 0;
+            copy_tile(rk, rv, odd ? k0 : k1, odd ? v0 : v1, T, a.T4, kt + 1, wv, lane);
+        }
+    };
+    // The three loops keep the tile computation free of a skip branch: with one, the
+    // compiler carried the output accumulators through VGPRs and copied all of them on every
+    // tile.
+    int kt = ktlo;
+    for (; kt < kta; ++kt) advance(kt);
+    for (; kt <= ktb; ++kt) {
+        advance(kt);
+        const bool odd = ((kt - ktlo) & 1) != 0;
+        const uint16_t* kc = odd ? k1 : k0;
+        const uint16_t* vc = odd ? v1 : v0;
         const int key0 = kt * kKB;
-        // does any key of this tile fall in any window of this wave's queries?
-        const bool live = key0 <= t0w + 31 && key0 + kKB - 1 > t0w - W;
-        if (live) {
-            f32x16 s;
+        f32x16 s;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) s[e] = 0.0f;
-            const int kr_ = lane & 31;
-            // fragment reads in groups of four, so that at most eight are in flight (left
-            // free, the compiler hoisted all of them and ran out of registers)
+        for (int e = 0; e < 16; ++e) s[e] = 0.0f;
+        const int kr_ = lane & 31;
+        // fragment reads in groups of four, so that at most eight are in flight (left free,
+        // the compiler hoisted all of them and ran out of registers)
 #pragma unroll
-            for (int kk = 0; kk < 16; ++kk) {
-                const int pos = (2 * kk + hl) ^ (kr_ & 15);
-                const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kc + kr_ * kDh + pos * 8);
-                s = mfma32(kf, qf[kk], s);
-                if ((kk & 3) == 3) __builtin_amdgcn_sched_barrier(0);
-            }
-            // scale; mask only on tiles that cross a window edge or the sequence end
-            const bool edge = key0 + kKB - 1 > t0w || key0 <= t0w + 31 - W || key0 + kKB > T;
-            float x[16];
-            float tmax = -INFINITY;
+        for (int kk = 0; kk < 16; ++kk) {
+            const int pos = (2 * kk + hl) ^ (kr_ & 15);
+            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kc + kr_ * kDh + pos * 8);
+            s = mfma32(kf, qf[kk], s);
+            if ((kk & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+        }
+        float x[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x[e] = s[e] * sc;
+        // mask only on tiles that cross a window edge or the sequence end
+        if (key0 + kKB - 1 > t0w || key0 <= t0w + 31 - W || key0 + kKB > T) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                float v = s[e] * sc;
-                if (edge) {
-                    const int key = key0 + mfma_d_row(lane, e);
-                    if (key > tq || key <= tq - W || key >= T) v = -INFINITY;
-                }
-                x[e] = v;
-                tmax = fmaxf(tmax, v);
-            }
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-            const bool need = tmax > mref + kRescale;
-            if (__any(need)) {
-                const float al = need ? __builtin_amdgcn_exp2f(mref - tmax) : 1.0f;
-                if (need) mref = tmax;
-                lsum *= al;
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) oacc[j][e] *= al;
-            }
-            float p[16];
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                p[e] = __builtin_amdgcn_exp2f(x[e] - mref);
-                lsum += p[e];
-            }
-            bf16x8 pf[2];
-#pragma unroll
-            for (int kq = 0; kq < 2; ++kq)
-#pragma unroll
-                for (int i = 0; i < 8; ++i) pf[kq][i] = (__bf16)p[8 * kq + i];
-            // O^T[j] += V^T P^T: dims 32 j + l % 32; keys 16 kq + 4 hl + {0..3} and {8..11}
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int d = 32 * j + (lane & 31);
-#pragma unroll
-                for (int kq = 0; kq < 2; ++kq) {
-                    const uint2 lo = v_quad(vc, 4 * kq + hl, d);
-                    const uint2 hi = v_quad(vc, 4 * kq + hl + 2, d);
-                    const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-                    oacc[j] = mfma32(vf, pf[kq], oacc[j]);
-                }
-                if ((j & 1) == 1) __builtin_amdgcn_sched_barrier(0);
+                const int key = key0 + mfma_d_row(lane, e);
+                x[e] = (key > tq || key <= tq - W || key >= T) ? -INFINITY : x[e];
             }
         }
+        float tmax = x[0];
+#pragma unroll
+        for (int e = 1; e < 16; ++e) tmax = fmaxf(tmax, x[e]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        const bool need = tmax > mref + kRescale;
+        if (__any(need)) {
+            const float al = need ? __builtin_amdgcn_exp2f(mref - tmax) : 1.0f;
+            if (need) mref = tmax;
+            lsum *= al;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    float y = oacc[j][e];
+                    scale_acc(y, al);
+                    oacc[j][e] = y;
+                }
+        }
+        float p[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            p[e] = __builtin_amdgcn_exp2f(x[e] - mref);
+            lsum += p[e];
+        }
+        bf16x8 pf[2];
+#pragma unroll
+        for (int kq = 0; kq < 2; ++kq)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) pf[kq][i] = (__bf16)p[8 * kq + i];
+        // O^T[j] += V^T P^T: dims 32 j + l % 32; keys 16 kq + 4 hl + {0..3} and {8..11}
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int d = 32 * j + (lane & 31);
+#pragma unroll
+            for (int kq = 0; kq < 2; ++kq) {
+                const uint2 lo = v_quad(vc, 4 * kq + hl, d);
+                const uint2 hi = v_quad(vc, 4 * kq + hl + 2, d);
+                const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+                oacc[j] = mfma32(vf, pf[kq], oacc[j]);
+            }
+            if ((j & 1) == 1) __builtin_amdgcn_sched_barrier(0);
+        }
     }
+    for (; kt <= kthi; ++kt) advance(kt);
 
     // normalise and store: O^T tile j, register 4 g + i -> dim 32 j + 8 g + 4 hl + i
     const float lt = lsum + __shfl_xor(lsum, 32);
