@@ -28,7 +28,9 @@ EXPORTS = ["rglru_prefill_workspace_bytes", "rglru_prefill_workspace_init", "rgl
            "rglru_prefill_workspace_flags", "rglru_status_string", "rglru_last_hip_error",
            "rglru_abi_version", "rglru_linear", "rglru_block_prefill_workspace_bytes",
            "rglru_block_prefill", "rglru_local_attention_workspace_bytes", "rglru_local_attention",
-           "rglru_local_attention_block_workspace_bytes", "rglru_local_attention_block"]
+           "rglru_local_attention_block_workspace_bytes", "rglru_local_attention_block",
+           "rglru_local_attention_cache_bytes", "rglru_local_attention_decode_workspace_bytes",
+           "rglru_local_attention_decode"]
 
 _lock = threading.Lock()
 _lib = None
@@ -106,7 +108,14 @@ def load_library(path: str = LIB_PATH):
         lib.rglru_local_attention_workspace_bytes.argtypes = [I32, I32, I32]
         lib.rglru_local_attention_workspace_bytes.restype = SZ
         lib.rglru_local_attention.argtypes = [I32, I32, I32, I32, ctypes.c_float, P, P, P, P, P,
-                                              SZ, P]
+                                              P, P, SZ, P]
+        lib.rglru_local_attention_cache_bytes.argtypes = [I32, I32]
+        lib.rglru_local_attention_cache_bytes.restype = SZ
+        lib.rglru_local_attention_decode_workspace_bytes.argtypes = [I32, I32, I32]
+        lib.rglru_local_attention_decode_workspace_bytes.restype = SZ
+        lib.rglru_local_attention_decode.argtypes = [I32, I32, I32, ctypes.c_float, P, P, P, P, P,
+                                                     P, P, P, SZ, P]
+        lib.rglru_local_attention_decode.restype = ctypes.c_int
         lib.rglru_local_attention.restype = ctypes.c_int
         AP = ctypes.POINTER(rglru_attn_params)
         lib.rglru_local_attention_block_workspace_bytes.argtypes = [AP, I32, I32]
@@ -402,10 +411,23 @@ def rglru_local_attention_workspace_bytes(B: int, T: int, n_heads: int) -> int:
     return int(load_library().rglru_local_attention_workspace_bytes(B, T, n_heads))
 
 
+class AttnCache:
+    """The ring KV cache of the local attention for N sequences (two device buffers in the
+    library's tile layout; slot t % window holds position t)."""
+
+    def __init__(self, N: int, window: int, device):
+        nbytes = int(load_library().rglru_local_attention_cache_bytes(N, window))
+        if nbytes == 0:
+            raise ValueError("invalid cache shape N=%d window=%d" % (N, window))
+        self.N, self.window = N, window
+        self.k = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=device)
+        self.v = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=device)
+
+
 def rglru_local_attention(q, k, v, window: int, rope_base: float = 10000.0, *, out=None,
-                          workspace: DeviceBuffer | None = None):
+                          cache: AttnCache | None = None, workspace: DeviceBuffer | None = None):
     """Sliding-window MQA with RoPE (bf16): q [B, T, Hq, 256], k, v [B, T, 256] (before RoPE)
-    -> o [B, T, Hq, 256]."""
+    -> o [B, T, Hq, 256].  With a cache, the last `window` positions are written into it."""
     lib = load_library()
     B, T, Hq, dh = q.shape
     dev = q.device
@@ -417,10 +439,45 @@ def rglru_local_attention(q, k, v, window: int, rope_base: float = 10000.0, *, o
     _need(out, "out", torch.bfloat16, (B, T, Hq, ATTN_HEAD_DIM), dev)
     if workspace is None:
         workspace = DeviceBuffer(rglru_local_attention_workspace_bytes(B, T, Hq), dev)
+    if cache is not None and (cache.N != B or cache.window != window):
+        raise ValueError("cache is for N=%d window=%d" % (cache.N, cache.window))
+    kc = _ptr(cache.k) if cache is not None else None
+    vc = _ptr(cache.v) if cache is not None else None
     st = lib.rglru_local_attention(B, T, Hq, int(window), float(rope_base), _ptr(q), _ptr(k),
-                                   _ptr(v), _ptr(out), _ptr(workspace.t), workspace.nbytes,
+                                   _ptr(v), _ptr(out), kc, vc, _ptr(workspace.t), workspace.nbytes,
                                    _stream())
     _check(lib, st, "rglru_local_attention")
+    return out
+
+
+def rglru_local_attention_decode_workspace_bytes(N: int, n_heads: int, window: int) -> int:
+    return int(load_library().rglru_local_attention_decode_workspace_bytes(N, n_heads, window))
+
+
+def rglru_local_attention_decode(pos, q, k, v, cache: AttnCache, rope_base: float = 10000.0, *,
+                                 out=None, workspace: DeviceBuffer | None = None):
+    """One decode step: pos [N] int32 (device), q [N, Hq, 256], k, v [N, 256] (before RoPE);
+    writes position pos[n] into the cache and returns o [N, Hq, 256]."""
+    lib = load_library()
+    N, Hq, _ = q.shape
+    dev = q.device
+    _need(pos, "pos", torch.int32, (N,), dev)
+    _need(q, "q", torch.bfloat16, (N, Hq, ATTN_HEAD_DIM))
+    _need(k, "k", torch.bfloat16, (N, ATTN_HEAD_DIM), dev)
+    _need(v, "v", torch.bfloat16, (N, ATTN_HEAD_DIM), dev)
+    if cache.N != N:
+        raise ValueError("cache is for N=%d, got %d sequences" % (cache.N, N))
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, (N, Hq, ATTN_HEAD_DIM), dev)
+    if workspace is None:
+        workspace = DeviceBuffer(rglru_local_attention_decode_workspace_bytes(N, Hq, cache.window),
+                                 dev)
+    st = lib.rglru_local_attention_decode(N, Hq, cache.window, float(rope_base), _ptr(pos),
+                                          _ptr(q), _ptr(k), _ptr(v), _ptr(cache.k), _ptr(cache.v),
+                                          _ptr(out), _ptr(workspace.t), workspace.nbytes,
+                                          _stream())
+    _check(lib, st, "rglru_local_attention_decode")
     return out
 
 

@@ -359,9 +359,14 @@ size_t rglru_local_attention_workspace_bytes(int32_t B, int32_t T, int32_t n_hea
            round256((size_t)B * T4 * kAttnDh * 4 * 2);
 }
 
+size_t rglru_local_attention_cache_bytes(int32_t N, int32_t window) {
+    if (N < 1 || window < 1 || window >= (1 << 22)) return 0;
+    return (size_t)N * (size_t)((window + 31) / 32) * 32 * kAttnDh * 2;
+}
+
 int rglru_local_attention(int32_t B, int32_t T, int32_t n_heads, int32_t window, float rope_base,
-                          const void* q, const void* k, const void* v, void* o, void* workspace,
-                          size_t ws_bytes, void* stream) {
+                          const void* q, const void* k, const void* v, void* o, void* kcache,
+                          void* vcache, void* workspace, size_t ws_bytes, void* stream) {
     if (B < 1 || T < 0 || n_heads < 1 || n_heads > 64 || window < 1 || !(rope_base > 1.0f) ||
         !(rope_base < INFINITY))
         return RGLRU_ERR_SHAPE;
@@ -369,27 +374,82 @@ int rglru_local_attention(int32_t B, int32_t T, int32_t n_heads, int32_t window,
     if (T >= (1 << 22) || (long long)B * 4 * T4 >= (1LL << 24) ||
         (long long)B * n_heads * (((long long)T + 127) / 128) >= (1LL << 24))
         return RGLRU_ERR_UNSUPPORTED;
+    if (window >= (1 << 22)) return RGLRU_ERR_UNSUPPORTED;
     if (T > 0 && (!q || !k || !v || !o)) return RGLRU_ERR_NULL;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(workspace))
+    if ((kcache == nullptr) != (vcache == nullptr)) return RGLRU_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(workspace) ||
+        !aligned16(kcache) || !aligned16(vcache))
         return RGLRU_ERR_UNSUPPORTED;
     const size_t M = (size_t)B * T;
     const size_t nq = M * n_heads * kAttnDh * 2, nk = M * kAttnDh * 2;
+    const size_t nc = kcache ? rglru_local_attention_cache_bytes(B, window) : 0;
     const size_t need = rglru_local_attention_workspace_bytes(B, T, n_heads);
     if (T > 0 && (!workspace || ws_bytes < need)) return RGLRU_ERR_WORKSPACE;
-    if (overlap(o, nq, q, nq) || overlap(o, nq, k, nk) || overlap(o, nq, v, nk))
-        return RGLRU_ERR_ALIAS;
-    if (T > 0 && (overlap(workspace, need, q, nq) || overlap(workspace, need, k, nk) ||
-                  overlap(workspace, need, v, nk) || overlap(workspace, need, o, nq)))
-        return RGLRU_ERR_ALIAS;
+    const void* outs[] = {o, kcache, vcache};
+    const size_t outn[] = {nq, nc, nc};
+    const void* ins[] = {q, k, v};
+    const size_t inn[] = {nq, nk, nk};
+    for (int i = 0; i < 3; ++i) {
+        for (int j = 0; j < 3; ++j)
+            if (overlap(outs[i], outn[i], ins[j], inn[j])) return RGLRU_ERR_ALIAS;
+        for (int j = i + 1; j < 3; ++j)
+            if (overlap(outs[i], outn[i], outs[j], outn[j])) return RGLRU_ERR_ALIAS;
+    }
+    if (T > 0)
+        for (int i = 0; i < 3; ++i)
+            if (overlap(workspace, need, outs[i], outn[i]) || overlap(workspace, need, ins[i], inn[i]))
+                return RGLRU_ERR_ALIAS;
     if (T == 0) return RGLRU_OK;
     AttnArgs a;
-    a.q = q; a.k = k; a.v = v; a.o = o;
+    a.q = q; a.k = k; a.v = v; a.o = o; a.kc = kcache; a.vc = vcache;
+    a.Wc = (window + 31) / 32 * 32;
     char* ws = static_cast<char*>(workspace);
     a.qr = ws;
     a.kr = ws + round256(nq);
     a.v4 = ws + round256(nq) + round256(nk);
     a.B = B; a.T = T; a.Hq = n_heads; a.W = window; a.T4 = (int)T4; a.rope_base = rope_base;
     hipError_t e = launch_attention(a, (hipStream_t)stream);
+    return e == hipSuccess ? RGLRU_OK : hip_fail(e);
+}
+
+size_t rglru_local_attention_decode_workspace_bytes(int32_t N, int32_t n_heads, int32_t window) {
+    if (N < 1 || n_heads < 1 || window < 1 || window >= (1 << 22)) return 0;
+    const size_t nsplit = ((size_t)window + kAttnDecSlotsPerSplit - 1) / kAttnDecSlotsPerSplit;
+    return round256((size_t)N * n_heads * kAttnDh * 2) +
+           (size_t)N * nsplit * n_heads * (2 + kAttnDh) * sizeof(float);
+}
+
+int rglru_local_attention_decode(int32_t N, int32_t n_heads, int32_t window, float rope_base,
+                                 const int32_t* pos, const void* q, const void* k, const void* v,
+                                 void* kcache, void* vcache, void* o, void* workspace,
+                                 size_t ws_bytes, void* stream) {
+    if (N < 1 || n_heads < 1 || n_heads > 16 || window < 1 || !(rope_base > 1.0f) ||
+        !(rope_base < INFINITY))
+        return RGLRU_ERR_SHAPE;
+    const long long nsplit = ((long long)window + kAttnDecSlotsPerSplit - 1) / kAttnDecSlotsPerSplit;
+    if (window >= (1 << 22) || (long long)N * nsplit >= (1LL << 24)) return RGLRU_ERR_UNSUPPORTED;
+    if (!pos || !q || !k || !v || !kcache || !vcache || !o) return RGLRU_ERR_NULL;
+    const void* ptrs[] = {pos, q, k, v, kcache, vcache, o, workspace};
+    for (const void* ptr : ptrs)
+        if (!aligned16(ptr)) return RGLRU_ERR_UNSUPPORTED;
+    const size_t need = rglru_local_attention_decode_workspace_bytes(N, n_heads, window);
+    if (!workspace || ws_bytes < need) return RGLRU_ERR_WORKSPACE;
+    const size_t nq = (size_t)N * n_heads * kAttnDh * 2, nk = (size_t)N * kAttnDh * 2;
+    const size_t nc = rglru_local_attention_cache_bytes(N, window);
+    const void* all[] = {kcache, vcache, o, workspace, pos, q, k, v};
+    const size_t len[] = {nc, nc, nq, need, (size_t)N * 4, nq, nk, nk};
+    // the four written buffers overlap nothing; the read-only inputs may overlap each other
+    for (int i = 0; i < 4; ++i)
+        for (int j = i + 1; j < 8; ++j)
+            if (overlap(all[i], len[i], all[j], len[j])) return RGLRU_ERR_ALIAS;
+    AttnDecodeArgs a;
+    a.pos = pos; a.q = q; a.k = k; a.v = v; a.kc = kcache; a.vc = vcache; a.o = o;
+    a.qr = workspace;
+    a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                      round256((size_t)N * n_heads * kAttnDh * 2));
+    a.N = N; a.Hq = n_heads; a.W = window; a.Wc = (window + 31) / 32 * 32; a.nsplit = (int)nsplit;
+    a.rope_base = rope_base;
+    hipError_t e = launch_attention_decode(a, (hipStream_t)stream);
     return e == hipSuccess ? RGLRU_OK : hip_fail(e);
 }
 
@@ -440,8 +500,8 @@ int rglru_local_attention_block(const rglru_attn_params* a, int32_t B, int32_t T
     void* aw = T > 0 ? ws + 2 * nq + 2 * nk : nullptr;
     const size_t aw_bytes = rglru_local_attention_workspace_bytes(B, T, Hq);
     // the attention's own checks, before anything is launched
-    int st = rglru_local_attention(B, 0, Hq, a->window, a->rope_base, qb, kb, vb, ob, aw,
-                                   aw_bytes, stream);
+    int st = rglru_local_attention(B, 0, Hq, a->window, a->rope_base, qb, kb, vb, ob, nullptr,
+                                   nullptr, aw, aw_bytes, stream);
     if (st != RGLRU_OK) return st;
     const long long T4 = ((long long)T + 3) / 4;
     if (T >= (1 << 22) || (long long)B * 4 * T4 >= (1LL << 24) ||
@@ -457,8 +517,8 @@ int rglru_local_attention_block(const rglru_attn_params* a, int32_t B, int32_t T
     g.M = (int)M; g.K = Dm; g.Nw[0] = (int)HD; g.Nw[1] = kAttnDh; g.Nw[2] = kAttnDh; g.nseg = 3;
     hipError_t e = launch_proj_gemm(g, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e);
-    st = rglru_local_attention(B, T, Hq, a->window, a->rope_base, qb, kb, vb, ob, aw, aw_bytes,
-                               stream);
+    st = rglru_local_attention(B, T, Hq, a->window, a->rope_base, qb, kb, vb, ob, nullptr, nullptr,
+                               aw, aw_bytes, stream);
     if (st != RGLRU_OK) return st;
     memset(&g, 0, sizeof g);
     g.A = ob; g.W[0] = a->o_w; g.b[0] = a->o_b; g.C[0] = out;

@@ -40,6 +40,27 @@ constexpr int kAttnThreads = 256;
 constexpr float kRescale = 8.0f;  // exp2 units: rescale when a tile maximum exceeds the reference by 2^8
 
 // ---------------------------------------------------------------------------------------
+// Ring KV cache for decoding.  Per sequence, Wc / 32 tiles of 32 slots x 256 dims (16 KB of K and
+// 16 KB of V each); slot t % W holds position t.  Within a tile both are stored in the operand
+// order of v_mfma_f32_16x16x32_bf16 (lane l supplies row l % 16 and K-slice l / 16 of 8), so
+// that one fragment of a wave is 1 KB of contiguous memory:
+//   K, the A operand of S^T = K Q^T (rows: slots, K: dims), fragment (half, kk) for slots
+//   16 half .. + 15 and dims 32 kk .. + 31;
+//   V, the A operand of O^T = V^T P^T (rows: dims, K: slots), fragment jd for dims 16 jd .. + 15;
+//   lane group g = l / 16 holds slots 4 g .. 4 g + 3 and 16 + 4 g .. 16 + 4 g + 3, the slots whose
+//   scores the same lane holds in the two S^T results (rows 4 g + i of each).
+// ---------------------------------------------------------------------------------------
+constexpr int kTileElems = 32 * kDh;   // elements of one cache tile (K or V)
+
+__device__ __forceinline__ int kc_index(int r, int d) {  // slot r of a tile, dim d
+    return ((((r >> 4) * 8 + (d >> 5)) * 4 + ((d & 31) >> 3)) * 16 + (r & 15)) * 8 + (d & 7);
+}
+__device__ __forceinline__ int vc_index(int r, int d) {
+    const int rr = r & 15;
+    return (((d >> 4) * 4 + (rr >> 2)) * 16 + (d & 15)) * 8 + (rr & 3) + 4 * (r >> 4);
+}
+
+// ---------------------------------------------------------------------------------------
 // prep: one workgroup per token row t in [0, 4 ceil(T / 4)) of one sequence
 // ---------------------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) attn_prep_kernel(AttnArgs a) {
@@ -54,6 +75,12 @@ __global__ void __launch_bounds__(256) attn_prep_kernel(AttnArgs a) {
     uint16_t* v4 = static_cast<uint16_t*>(a.v4);
     v4[(((size_t)b * a.T4 + t / 4) * kDh + tid) * 4 + (t & 3)] = valid ? v[m * kDh + tid] : 0;
     if (!valid) return;
+    // the last W positions also go to the ring cache, if one is given
+    const bool to_cache = a.kc != nullptr && t >= a.T - a.W;
+    const int slot = t % a.W;
+    const size_t ctile = ((size_t)b * (a.Wc / 32) + slot / 32) * kTileElems;
+    if (to_cache)
+        static_cast<uint16_t*>(a.vc)[ctile + vc_index(slot & 31, tid)] = v[m * kDh + tid];
     // RoPE: pair i of a head, (x_i, x_{i+128}), turned by t * base^(-2 i / 256)
     const int HD = a.Hq * kDh;
     const uint16_t* q = static_cast<const uint16_t*>(a.q) + m * HD;
@@ -71,8 +98,14 @@ __global__ void __launch_bounds__(256) attn_prep_kernel(AttnArgs a) {
         const uint16_t* src = h < a.Hq ? q + h * kDh : k;
         uint16_t* dst = h < a.Hq ? qr + h * kDh : kr;
         const float x0 = bf2f(src[i]), x1 = bf2f(src[i + kDh / 2]);
-        dst[i] = f2bf(x0 * cs - x1 * sn);
-        dst[i + kDh / 2] = f2bf(x1 * cs + x0 * sn);
+        const uint16_t r0 = f2bf(x0 * cs - x1 * sn), r1 = f2bf(x1 * cs + x0 * sn);
+        dst[i] = r0;
+        dst[i + kDh / 2] = r1;
+        if (h == a.Hq && to_cache) {
+            uint16_t* kc = static_cast<uint16_t*>(a.kc) + ctile;
+            kc[kc_index(slot & 31, i)] = r0;
+            kc[kc_index(slot & 31, i + kDh / 2)] = r1;
+        }
     }
 }
 
@@ -284,7 +317,221 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_fwd_kernel(AttnArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// decode: one new token per sequence
+// ---------------------------------------------------------------------------------------
+// RoPE of the new token's q and k at its position; k and v go to cache slot pos % W.
+__global__ void __launch_bounds__(256) attn_dec_prep_kernel(AttnDecodeArgs a) {
+    const int n = blockIdx.x, tid = threadIdx.x;
+    const int t = a.pos[n];
+    if (t < 0) return;
+    const int slot = t % a.W;
+    const size_t ctile = ((size_t)n * (a.Wc / 32) + slot / 32) * kTileElems;
+    static_cast<uint16_t*>(a.vc)[ctile + vc_index(slot & 31, tid)] =
+        static_cast<const uint16_t*>(a.v)[(size_t)n * kDh + tid];
+    const int i = tid % (kDh / 2);
+    const double ang = (double)t * exp2(-2.0 * (double)i / (double)kDh * log2((double)a.rope_base));
+    double sn_d, cs_d;
+    sincos(ang, &sn_d, &cs_d);
+    const float sn = (float)sn_d, cs = (float)cs_d;
+    for (int h = tid / (kDh / 2); h <= a.Hq; h += 2) {
+        const uint16_t* src = h < a.Hq
+            ? static_cast<const uint16_t*>(a.q) + ((size_t)n * a.Hq + h) * kDh
+            : static_cast<const uint16_t*>(a.k) + (size_t)n * kDh;
+        const float x0 = bf2f(src[i]), x1 = bf2f(src[i + kDh / 2]);
+        const uint16_t r0 = f2bf(x0 * cs - x1 * sn), r1 = f2bf(x1 * cs + x0 * sn);
+        if (h < a.Hq) {
+            uint16_t* dst = static_cast<uint16_t*>(a.qr) + ((size_t)n * a.Hq + h) * kDh;
+            dst[i] = r0;
+            dst[i + kDh / 2] = r1;
+        } else {
+            uint16_t* kc = static_cast<uint16_t*>(a.kc) + ctile;
+            kc[kc_index(slot & 31, i)] = r0;
+            kc[kc_index(slot & 31, i + kDh / 2)] = r1;
+        }
+    }
+}
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// One workgroup per (sequence, 512 cache slots): each wave takes four 32-slot tiles (tile
+// 16 sp + 4 i + wave), heads as the 16 columns of S^T = K Q^T and O^T = V^T P^T, and a softmax
+// per head over its tiles; the four waves are merged through LDS into one partial result
+// (reference maximum M, normaliser L, unnormalised output O) per head.  Only slots below
+// min(pos + 1, W) hold positions of the window; the others are masked, and their V entries
+// zeroed (a slot never written may hold any bits).
+constexpr int kDecPad = 260;   // LDS row pitch (floats) of the per-wave outputs
+__global__ void __launch_bounds__(256, 2) attn_dec_kernel(AttnDecodeArgs a) {
+    __shared__ __attribute__((aligned(16))) float ow[4][16][kDecPad];
+    __shared__ float wm[4][16], wl[4][16];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = blockIdx.x / a.nsplit, sp = blockIdx.x % a.nsplit;
+    const int col = lane & 15, g = lane >> 4;
+    const int t = a.pos[n];
+    const int nvalid = t < 0 ? 0 : min(t + 1, a.W);
+
+    bf16x8 qf[8];
+    {
+        const uint16_t* qrow = static_cast<const uint16_t*>(a.qr) +
+                               ((size_t)n * a.Hq + min(col, a.Hq - 1)) * kDh;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            qf[kk] = *reinterpret_cast<const bf16x8*>(qrow + 32 * kk + 8 * g);
+            if (col >= a.Hq) qf[kk] = bf16x8{};
+        }
+    }
+    f32x4 oacc[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) oacc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    const float sc = kLog2e * 0.0625f;
+    const uint16_t* kseq = static_cast<const uint16_t*>(a.kc) + (size_t)n * (a.Wc / 32) * kTileElems;
+    const uint16_t* vseq = static_cast<const uint16_t*>(a.vc) + (size_t)n * (a.Wc / 32) * kTileElems;
+
+    int ntile = 0;   // this wave's tiles holding a slot of the window (a prefix of its four)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ntile += ((sp * 16 + 4 * i + wv) * 32 < nvalid) ? 1 : 0;
+
+    // Pass 1: scores of the wave's tiles, kept in registers, and their exact maximum per head
+    // (no running rescale: branches stay around loads and scores, never around accumulation).
+    // xs[i][m]: tile i, slot 4 g + m (m < 4) or 16 + 4 g + m - 4, the order of the P^T operand.
+    float xs[4][8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int tile = sp * 16 + 4 * i + wv, s0 = tile * 32;
+        if (i < ntile) {
+            const uint16_t* kt = kseq + (size_t)tile * kTileElems;
+            bf16x8 kf[16];
+#pragma unroll
+            for (int f = 0; f < 16; ++f)
+                kf[f] = *reinterpret_cast<const bf16x8*>(kt + (f * 64 + lane) * 8);
+            f32x4 sa = {0.0f, 0.0f, 0.0f, 0.0f}, sb = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+                sa = mfma16(kf[kk], qf[kk], sa);
+                sb = mfma16(kf[8 + kk], qf[kk], sb);
+            }
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                xs[i][m] = sa[m] * sc;
+                xs[i][4 + m] = sb[m] * sc;
+            }
+            if (s0 + 32 > nvalid) {
+#pragma unroll
+                for (int m = 0; m < 8; ++m)
+                    if (s0 + (m < 4 ? 4 * g + m : 16 + 4 * g + m - 4) >= nvalid) xs[i][m] = -INFINITY;
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < 8; ++m) xs[i][m] = -INFINITY;
+        }
+#pragma unroll
+        for (int m = 0; m < 8; ++m) mx = fmaxf(mx, xs[i][m]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mref = fmaxf(mx, -1e30f);   // a wave without tiles keeps a finite reference
+    float lsum = 0.0f;
+
+    // Pass 2: O^T += V^T P^T over the same tiles; a tile past the window contributes zeros
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int tile = sp * 16 + 4 * i + wv, s0 = tile * 32;
+        bf16x8 vf[16];
+        if (i < ntile) {
+            const uint16_t* vt = vseq + (size_t)tile * kTileElems;
+#pragma unroll
+            for (int f = 0; f < 16; ++f)
+                vf[f] = *reinterpret_cast<const bf16x8*>(vt + (f * 64 + lane) * 8);
+            if (s0 + 32 > nvalid) {
+#pragma unroll
+                for (int m = 0; m < 8; ++m) {
+                    const bool dead = s0 + (m < 4 ? 4 * g + m : 16 + 4 * g + m - 4) >= nvalid;
+#pragma unroll
+                    for (int f = 0; f < 16; ++f) vf[f][m] = dead ? (__bf16)0.0f : vf[f][m];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int f = 0; f < 16; ++f) vf[f] = bf16x8{};
+        }
+        bf16x8 pf;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const float p = __builtin_amdgcn_exp2f(xs[i][m] - mref);
+            lsum += p;
+            pf[m] = (__bf16)p;
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) oacc[j] = mfma16(vf[j], pf, oacc[j]);
+    }
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+    // O^T fragment j: column col, dims 16 j + 4 g + e
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+        *reinterpret_cast<f32x4*>(&ow[wv][col][16 * j + 4 * g]) = oacc[j];
+    if (g == 0) {
+        wm[wv][col] = mref;
+        wl[wv][col] = lsum;
+    }
+    __syncthreads();
+    float* prow = a.part + ((size_t)n * a.nsplit + sp) * a.Hq * (2 + kDh);
+    const int d = tid;
+    for (int h = 0; h < a.Hq; ++h) {
+        const float M = fmaxf(fmaxf(wm[0][h], wm[1][h]), fmaxf(wm[2][h], wm[3][h]));
+        float L = 0.0f, O = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float f = __builtin_amdgcn_exp2f(wm[w][h] - M);
+            L += f * wl[w][h];
+            O += f * ow[w][h][d];
+        }
+        prow[(size_t)h * (2 + kDh) + 2 + d] = O;
+        if (d == 0) {
+            prow[(size_t)h * (2 + kDh)] = M;
+            prow[(size_t)h * (2 + kDh) + 1] = L;
+        }
+    }
+}
+
+// o[n][h] = sum over splits of 2^(M_s - M) O_s / sum of 2^(M_s - M) L_s, in split order.
+__global__ void __launch_bounds__(256) attn_dec_combine_kernel(AttnDecodeArgs a) {
+    const int n = blockIdx.x / a.Hq, h = blockIdx.x % a.Hq, d = threadIdx.x;
+    uint16_t* orow = static_cast<uint16_t*>(a.o) + ((size_t)n * a.Hq + h) * kDh;
+    if (a.pos[n] < 0) {
+        orow[d] = 0;
+        return;
+    }
+    const float* p0 = a.part + ((size_t)n * a.nsplit * a.Hq + h) * (2 + kDh);
+    const size_t stride = (size_t)a.Hq * (2 + kDh);
+    float M = -INFINITY;
+    for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, p0[s * stride]);
+    float L = 0.0f, O = 0.0f;
+    for (int s = 0; s < a.nsplit; ++s) {
+        const float f = __builtin_amdgcn_exp2f(p0[s * stride] - M);
+        L += f * p0[s * stride + 1];
+        O += f * p0[s * stride + 2 + d];
+    }
+    orow[d] = f2bf(O / L);
+}
+
 }  // namespace
+
+hipError_t launch_attention_decode(const AttnDecodeArgs& a, hipStream_t s) {
+    if (a.N == 0) return hipSuccess;
+    hipLaunchKernelGGL(attn_dec_prep_kernel, dim3((unsigned)a.N), dim3(256), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(attn_dec_kernel, dim3((unsigned)(a.N * a.nsplit)), dim3(256), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(attn_dec_combine_kernel, dim3((unsigned)(a.N * a.Hq)), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     if (a.T == 0) return hipSuccess;

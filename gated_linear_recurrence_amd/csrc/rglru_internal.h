@@ -88,7 +88,25 @@ struct AttnArgs {
     void* kr;            // workspace: k after RoPE
     void* v4;            // workspace: v regrouped [B][T4][256][4]
     void* o;             // [B][T][Hq * 256]
+    void* kc;            // optional ring caches [B][Wc / 32][16 KB] (NULL: not filled)
+    void* vc;
     int B, T, Hq, W, T4; // T4 = ceil(T / 4)
+    int Wc;              // cache slots per sequence, W rounded up to 32
+    float rope_base;
+};
+
+// One decode step of local attention for N sequences.
+struct AttnDecodeArgs {
+    const int* pos;      // [N] position of the new token (device)
+    const void* q;       // [N][Hq * 256] before RoPE
+    const void* k;       // [N][256]
+    const void* v;       // [N][256]
+    void* kc;            // ring caches [N][Wc / 32][16 KB]
+    void* vc;
+    void* qr;            // workspace: q after RoPE [N][Hq][256]
+    float* part;         // workspace: partial results [N][nsplit][Hq][2 + 256]
+    void* o;             // [N][Hq * 256]
+    int N, Hq, W, Wc, nsplit;
     float rope_base;
 };
 
@@ -100,5 +118,7 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, int bs, hipStream_t s);
 hipError_t launch_conv_update(const ConvArgs& a, int dtype, hipStream_t s);
 hipError_t launch_proj_gemm(const ProjGemmArgs& a, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attention_decode(const AttnDecodeArgs& a, hipStream_t s);
+constexpr int kAttnDecSlotsPerSplit = 512;  // cache slots per decode workgroup
 
 }  // namespace rglru

@@ -235,17 +235,57 @@ int rglru_block_prefill(const rglru_params *p, const rglru_proj_params *q, int32
  * product, output rounded to bf16 nearest-even).
  *   q  [B][T][n_heads][256],  k, v  [B][T][256]   (before RoPE)
  *   o  [B][T][n_heads][256]
+ *   kcache, vcache       optional ring caches for decoding (both or neither; NULL: not filled),
+ *                        rglru_local_attention_cache_bytes(B, window) bytes each: the call writes
+ *                        positions max(0, T - window) .. T-1 into them (see the decode step)
  *   workspace, ws_bytes  at least rglru_local_attention_workspace_bytes(B, T, n_heads); no
  *                        initialisation needed
  * B >= 1, T >= 0, 1 <= n_heads <= 64, window >= 1 and rope_base > 1, else RGLRU_ERR_SHAPE.
  * T < 2^22, B * 4 * ceil(T / 4) < 2^24 and B * n_heads * ceil(T / 128) < 2^24 (launch sizes),
- * else RGLRU_ERR_UNSUPPORTED.  o must not overlap q, k or v; the workspace must not overlap any
- * other argument.  T = 0 launches nothing.
+ * else RGLRU_ERR_UNSUPPORTED.  o and the caches must not overlap q, k, v or each other; the
+ * workspace must not overlap any other argument.  T = 0 launches nothing.
  */
 size_t rglru_local_attention_workspace_bytes(int32_t B, int32_t T, int32_t n_heads);
 int rglru_local_attention(int32_t B, int32_t T, int32_t n_heads, int32_t window, float rope_base,
-                          const void *q, const void *k, const void *v, void *o, void *workspace,
-                          size_t ws_bytes, void *stream);
+                          const void *q, const void *k, const void *v, void *o, void *kcache,
+                          void *vcache, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Ring KV cache of the local attention, for decoding: per sequence, Wc = 32 * ceil(window / 32)
+ * slots of one key (after RoPE) and one value; slot t % window holds position t.  The slots are
+ * grouped in tiles of 32 (16 KB of keys, 16 KB of values, bf16), each stored in the operand
+ * order of the decode kernel's matrix instructions: within tile s / 32, slot r = s % 32 and
+ * dimension d sit at element
+ *   keys:    (((r / 16) * 8 + d / 32) * 4 + (d % 32) / 8) * 16 + r % 16) * 8 + d % 8
+ *   values:  ((d / 16) * 4 + (r % 16) / 4) * 16 + d % 16) * 8 + r % 4 + 4 * (r / 16)
+ * Bytes of one cache (keys or values) for N sequences; 0 on invalid arguments.  Slots that hold
+ * no position of the current window are never read as values (their contents do not matter).
+ */
+size_t rglru_local_attention_cache_bytes(int32_t N, int32_t window);
+
+/*
+ * Decode step of the local attention: one new token for each of N sequences, at its own position.
+ * Operation: as rglru_local_attention for the new token, which attends to positions
+ * max(0, t - window + 1) .. t of its sequence, taken from the ring cache.
+ *   pos               [N] int32 (device): the new token's position t >= 0 (a negative position
+ *                     leaves that sequence's cache as it is and gives o = 0)
+ *   q [N][n_heads][256], k, v [N][256]   the new token's q, k, v before RoPE
+ *   kcache, vcache    rglru_local_attention_cache_bytes(N, window) bytes each, holding positions
+ *                     max(0, t - window + 1) .. t - 1 (from rglru_local_attention or earlier
+ *                     steps); the call writes position t into slot t % window
+ *   o [N][n_heads][256]
+ *   workspace, ws_bytes  at least rglru_local_attention_decode_workspace_bytes(N, n_heads,
+ *                        window); no initialisation needed
+ * N >= 1, 1 <= n_heads <= 16, window >= 1 and rope_base > 1, else RGLRU_ERR_SHAPE; window < 2^22
+ * and N * ceil(window / 512) < 2^24, else RGLRU_ERR_UNSUPPORTED.  No argument may overlap
+ * another (q, k and v may overlap each other).  Deterministic: the window is split in fixed
+ * chunks of 512 slots whose partial results are combined in chunk order.
+ */
+size_t rglru_local_attention_decode_workspace_bytes(int32_t N, int32_t n_heads, int32_t window);
+int rglru_local_attention_decode(int32_t N, int32_t n_heads, int32_t window, float rope_base,
+                                 const int32_t *pos, const void *q, const void *k, const void *v,
+                                 void *kcache, void *vcache, void *o, void *workspace,
+                                 size_t ws_bytes, void *stream);
 
 /*
  * The whole local-attention block: the projections of the page's printout (q_proj, k_proj and

@@ -219,10 +219,11 @@ AQ, AK, AV, AO, AW = (0x100000000 * k for k in range(1, 6))
 
 
 def _attn(lib, B=2, T=300, Hq=4, window=64, base=10000.0, q=AQ, k=AK, v=AV, o=AO, ws=AW,
-          ws_bytes=None):
+          ws_bytes=None, kc=None, vc=None):
     if ws_bytes is None:
         ws_bytes = lib.rglru_local_attention_workspace_bytes(B, T, Hq)
-    return lib.rglru_local_attention(B, T, Hq, window, base, q, k, v, o, ws, ws_bytes, None)
+    return lib.rglru_local_attention(B, T, Hq, window, base, q, k, v, o, kc, vc, ws, ws_bytes,
+                                     None)
 
 
 def test_attention_workspace_bytes(lib):
@@ -252,6 +253,55 @@ def test_attention_validation(lib):
     assert _attn(lib, o=AQ + 512) == ALIAS                       # o overlaps q
     assert _attn(lib, v=AO + 2 * 300 * 4 * 512 - 16) == ALIAS    # v's start inside o
     assert _attn(lib, ws=AV + 1024) == ALIAS                     # workspace overlaps v
+    KC, VC = 0x700000000, 0x780000000
+    assert _attn(lib, kc=KC) == NULL                             # one cache without the other
+    assert _attn(lib, kc=KC + 8, vc=VC) == UNSUP
+    assert _attn(lib, kc=AV, vc=VC) == ALIAS                     # a cache overlaps v
+    assert _attn(lib, kc=KC, vc=KC + 4096) == ALIAS              # the caches overlap
+    assert _attn(lib, window=1 << 22, kc=KC, vc=VC) == UNSUP
+
+
+def test_attention_cache_and_decode_sizes(lib):
+    # per sequence: ceil(window / 32) tiles of 32 slots x 256 dims, bf16
+    assert lib.rglru_local_attention_cache_bytes(3, 2048) == 3 * 2048 * 512
+    assert lib.rglru_local_attention_cache_bytes(1, 33) == 64 * 512
+    assert lib.rglru_local_attention_cache_bytes(0, 64) == 0
+    assert lib.rglru_local_attention_cache_bytes(1, 0) == 0
+    f = lib.rglru_local_attention_decode_workspace_bytes
+    # q after RoPE, then per 512-slot split and head: max, normaliser and 256 outputs (fp32)
+    assert f(256, 10, 2048) == 256 * 10 * 512 + 256 * 4 * 10 * 258 * 4
+    assert f(1, 1, 1) == 512 + 258 * 4
+    assert f(0, 1, 64) == 0 and f(1, 0, 64) == 0
+
+
+DP, DQ, DK, DV, DKC, DVC, DO, DW = (0x1000000000 + k * 0x10000000 for k in range(8))
+
+
+def _dec(lib, N=4, Hq=10, window=2048, base=10000.0, pos=DP, q=DQ, k=DK, v=DV, kc=DKC, vc=DVC,
+         o=DO, ws=DW, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.rglru_local_attention_decode_workspace_bytes(N, Hq, window)
+    return lib.rglru_local_attention_decode(N, Hq, window, base, pos, q, k, v, kc, vc, o, ws,
+                                            ws_bytes, None)
+
+
+def test_attention_decode_validation(lib):
+    # every call here fails validation, so nothing is launched
+    assert _dec(lib, N=0) == SHAPE
+    assert _dec(lib, Hq=0) == SHAPE and _dec(lib, Hq=17) == SHAPE
+    assert _dec(lib, window=0) == SHAPE and _dec(lib, base=0.5) == SHAPE
+    assert _dec(lib, window=1 << 22) == UNSUP
+    assert _dec(lib, N=1 << 22, window=2048, ws_bytes=1 << 40) == UNSUP   # grid too large
+    for name in ("pos", "q", "k", "v", "kc", "vc", "o"):
+        assert _dec(lib, **{name: None}) == NULL, name
+    assert _dec(lib, pos=DP + 4) == UNSUP
+    assert _dec(lib, ws=None) == WS
+    assert _dec(lib, ws_bytes=lib.rglru_local_attention_decode_workspace_bytes(4, 10, 2048) - 4) == WS
+    assert _dec(lib, o=DQ) == ALIAS                  # output over q
+    assert _dec(lib, kc=DV) == ALIAS                 # cache over v
+    assert _dec(lib, vc=DKC + 4096) == ALIAS         # the caches overlap
+    assert _dec(lib, ws=DO) == ALIAS                 # workspace over the output
+    assert _dec(lib, pos=DKC) == ALIAS               # positions inside a cache
 
 
 def _attn_params(Dm=512, Hq=2, dh=256, window=64, base=10000.0, b=True):

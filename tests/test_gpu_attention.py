@@ -197,3 +197,103 @@ def test_attention_block_2b_batched_full_size_sampled():
               % (b, t_use, e))
         assert e <= H.TOL[synth.BF16]
     assert bool(torch.isfinite(out.float()).all())
+
+
+# ------------------------------------------------------------------------------------------
+# decode with the ring KV cache
+# ------------------------------------------------------------------------------------------
+def _decode_run(N, Hq, W, T0, steps, pause=None, seed=0):
+    """Prefill T0 tokens of N sequences into the cache (none when T0 = 0), then decode `steps`
+    tokens; sequence n skips the steps listed in pause.get(n, ()) (position -1: no cache write,
+    o = 0), so positions become ragged.  Returns the per-step outputs with each sequence's
+    positions, and the whole sequences' inputs for the oracle."""
+    from gated_linear_recurrence_amd import binding
+    total = T0 + steps
+    q, k, v = _inputs(N, total, Hq, 1.0, seed)
+    cache = binding.AttnCache(N, W, "cuda")
+    if T0 > 0:
+        binding.rglru_local_attention(H.to_dev(q[:, :T0]), H.to_dev(k[:, :T0]),
+                                      H.to_dev(v[:, :T0]), W, cache=cache)
+    nxt = [T0] * N          # next position of each sequence
+    outs = []
+    pause = pause or {}
+    for j in range(steps):
+        pos = np.array([-1 if j in pause.get(n, ()) else nxt[n] for n in range(N)], np.int32)
+        idx = np.maximum(pos, 0)
+        qs = np.stack([q[n, idx[n]] for n in range(N)])
+        ks = np.stack([k[n, idx[n]] for n in range(N)])
+        vs = np.stack([v[n, idx[n]] for n in range(N)])
+        o = binding.rglru_local_attention_decode(torch.as_tensor(pos, device="cuda"), H.to_dev(qs),
+                                                 H.to_dev(ks), H.to_dev(vs), cache)
+        outs.append((pos, H.wide(H.to_host(o))))
+        for n in range(N):
+            nxt[n] += pos[n] >= 0
+    torch.cuda.synchronize()
+    return outs, (q, k, v)
+
+
+def _check_decode(outs, inputs, W, label):
+    q, k, v = inputs
+    N = q.shape[0]
+    refs = [_oracle_seq(q[n], k[n], v[n], W) for n in range(N)]
+    got, ref = [], []
+    for pos, o in outs:
+        for n in range(N):
+            if pos[n] < 0:
+                assert not o[n].any(), "a paused sequence must give zeros"
+            else:
+                got.append(o[n])
+                ref.append(refs[n][pos[n]])
+    _compare(np.stack(got), np.stack(ref), label)
+
+
+@pytest.mark.parametrize("N,Hq,W,T0,steps", [
+    (3, 10, 64, 50, 40),      # the ring wraps during decoding; window not a multiple of 512
+    (2, 4, 2048, 2040, 20),   # the 2B window, crossed at position 2048
+    (2, 16, 100, 0, 45),      # from an empty cache, 16 heads, window not a multiple of 32
+    (1, 1, 1, 5, 6),          # window 1
+])
+def test_attention_decode_matches_oracle(N, Hq, W, T0, steps):
+    outs, inputs = _decode_run(N, Hq, W, T0, steps, seed=N * 100 + W + T0)
+    _check_decode(outs, inputs, W, "decode N=%d Hq=%d W=%d from %d, %d steps" % (N, Hq, W, T0, steps))
+
+
+def test_attention_decode_ragged_positions():
+    """Sequences at different positions in one call: sequence 1 pauses for five steps (position
+    -1 leaves its cache alone and gives zeros), sequence 2 for one."""
+    outs, inputs = _decode_run(3, 10, 48, 30, 30, pause={1: range(8, 13), 2: (0,)}, seed=5)
+    _check_decode(outs, inputs, 48, "decode with ragged positions")
+
+
+def test_attention_prefill_fills_cache_past_window():
+    """A prefill longer than the window leaves the last `window` positions in the cache; the
+    next decode step sees exactly those."""
+    outs, inputs = _decode_run(2, 10, 128, 300, 3, seed=9)
+    _check_decode(outs, inputs, 128, "decode after a prefill past the window")
+
+
+def test_attention_decode_full_size_sampled():
+    """One decode step of the 2B attention for 256 sequences at window 2048, with the ring
+    wrapped (prefill of 2100 tokens); sampled sequences and heads against the oracle on their
+    2048-token windows."""
+    from gated_linear_recurrence_amd import binding
+    N, Hq, W, T0 = 256, synth.ATTN_HEADS_2B, synth.ATTN_WINDOW, 2100
+    g = torch.Generator(device="cuda").manual_seed(21)
+    qd = torch.randn((N, T0 + 1, Hq, DH), generator=g, device="cuda").to(torch.bfloat16)
+    kd = torch.randn((N, T0 + 1, DH), generator=g, device="cuda").to(torch.bfloat16)
+    vd = torch.randn((N, T0 + 1, DH), generator=g, device="cuda").to(torch.bfloat16)
+    cache = binding.AttnCache(N, W, "cuda")
+    binding.rglru_local_attention(qd[:, :T0].contiguous(), kd[:, :T0].contiguous(),
+                                  vd[:, :T0].contiguous(), W, cache=cache)
+    pos = torch.full((N,), T0, dtype=torch.int32, device="cuda")
+    o = binding.rglru_local_attention_decode(pos, qd[:, T0].contiguous(), kd[:, T0].contiguous(),
+                                             vd[:, T0].contiguous(), cache)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o.float()).all())
+    s0 = T0 - W + 1
+    for n in (0, 137, N - 1):
+        for h in (0, Hq - 1):
+            ref = _oracle_seq(H.to_host(qd[n, s0:, h:h + 1]), H.to_host(kd[n, s0:]),
+                              H.to_host(vd[n, s0:]), W, t0=s0)[-1:]
+            _compare(H.wide(H.to_host(o[n:n + 1, h:h + 1])), ref,
+                     "decode full size, sequence %d, head %d" % (n, h))
