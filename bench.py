@@ -272,6 +272,97 @@ def time_block(w, steps, warmup, torch, binding):
             "note": "hipblaslt_* is torch.nn.functional.linear on the same operands, for context"}
 
 
+def attention_flops(B: int, T: int, Hq: int, W: int) -> float:
+    """Algorithmic flops of local attention: per (query, head, key in its window) a 256-long dot
+    product and a 256-long update, 4 * 256 flops."""
+    keys = sum(min(t + 1, W) for t in range(T))
+    return 4.0 * synth.ATTN_HEAD_DIM * keys * B * Hq
+
+
+def time_attention(w, steps, warmup, torch, binding):
+    """Local sliding-window MQA (the model's other temporal-mixing block) at the batched 2B
+    shape: the attention alone (RoPE prep + flash kernel), the block with its projections, and
+    a decode step for 256 sequences with a full 2048-slot ring cache."""
+    Hq, W = synth.ATTN_HEADS_2B, synth.ATTN_WINDOW
+
+    def timed(call, n):
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    q, k, v = (_to_dev(a, torch) for a in synth.make_qkv(w, Hq))
+    o = torch.empty_like(q)
+    ws = binding.DeviceBuffer(binding.rglru_local_attention_workspace_bytes(w.B, w.T, Hq), "cuda")
+    ms = timed(lambda: binding.rglru_local_attention(q, k, v, W, out=o, workspace=ws), steps)
+    fl = attention_flops(w.B, w.T, Hq, W)
+    tf = fl / (ms * 1e-3) / 1e12
+    # torch's scaled_dot_product_attention with the same band as a boolean mask, one sequence
+    # (the shared key/value head expanded to the ten query heads), for context
+    i = torch.arange(w.T, device="cuda")
+    band = (i[None, :] <= i[:, None]) & (i[None, :] > i[:, None] - W)
+    qq = q[:1].transpose(1, 2).contiguous()
+    kk = k[:1, :, None].expand(1, w.T, Hq, 256).transpose(1, 2).contiguous()
+    vv = v[:1, :, None].expand(1, w.T, Hq, 256).transpose(1, 2).contiguous()
+    ms_sdpa = timed(lambda: torch.nn.functional.scaled_dot_product_attention(
+        qq, kk, vv, attn_mask=band), max(steps // 4, 2))
+    del qq, kk, vv, band
+
+    a = synth.make_attn(w)
+    ad = {n: _to_dev(t, torch) for n, t in a.items()}
+    A = binding.AttnParams(ad["q_w"], ad["k_w"], ad["v_w"], ad["o_w"], ad["o_b"], Hq, W)
+    x_in = _to_dev(synth.make_block_input(w), torch)
+    out = torch.empty_like(x_in)
+    wsb = binding.DeviceBuffer(binding.rglru_local_attention_block_workspace_bytes(A, w.B, w.T),
+                               "cuda")
+    ms_block = timed(lambda: binding.rglru_local_attention_block(A, x_in, out=out, workspace=wsb),
+                     max(steps // 2, 3))
+    M, Dm, HD = w.B * w.T, w.D, Hq * synth.ATTN_HEAD_DIM
+    fl_proj = 2.0 * M * Dm * (HD + 2 * synth.ATTN_HEAD_DIM) + 2.0 * M * HD * Dm
+    del x_in, out, wsb, q, k, v, o, ws
+
+    N, pos0 = 256, 5000
+    cache = binding.AttnCache(N, W, "cuda")
+    cache.k.normal_()
+    cache.v.normal_()
+    g = torch.Generator(device="cuda").manual_seed(w.seed)
+    qd = torch.randn((N, Hq, 256), generator=g, device="cuda").to(torch.bfloat16)
+    kd = torch.randn((N, 256), generator=g, device="cuda").to(torch.bfloat16)
+    vd = torch.randn((N, 256), generator=g, device="cuda").to(torch.bfloat16)
+    pos = torch.full((N,), pos0, dtype=torch.int32, device="cuda")
+    od = torch.empty_like(qd)
+    wsd = binding.DeviceBuffer(binding.rglru_local_attention_decode_workspace_bytes(N, Hq, W),
+                               "cuda")
+    us_dec = 1e3 * timed(lambda: binding.rglru_local_attention_decode(
+        pos, qd, kd, vd, cache, out=od, workspace=wsd), max(steps, 20))
+    dec_bytes = 2 * N * W * 256 * 2 + 2 * N * Hq * 256 * 2 + 2 * N * 256 * 2 * 2
+    return {
+        "workload": "%s shape: %d x %d tokens, %d query heads x 256 sharing one key/value head, "
+                    "window %d, RoPE base %g" % (w.name, w.B, w.T, Hq, W, synth.ROPE_BASE),
+        "ms": ms, "tflop": fl / 1e12, "tflops": tf,
+        "roofline": {"bound": "mfma", "kernel": "attn_prep_kernel + attn_fwd_kernel (whole call)",
+                     "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tf / MFMA_BF16_PEAK_TFLOPS},
+        "torch_sdpa_band_mask_ms_per_sequence": ms_sdpa,
+        "torch_sdpa_band_mask_ms_x_sequences": ms_sdpa * w.B,
+        "block_ms": ms_block, "block_tokens/s": M / (ms_block * 1e-3),
+        "block_projection_tflop": fl_proj / 1e12,
+        "decode": {"sequences": N, "position": pos0, "window": W, "us_per_step": us_dec,
+                   "bytes_per_step": dec_bytes,
+                   "roofline": {"bound": "hbm", "kernel": "attn_dec_kernel (whole step)",
+                                "achieved": dec_bytes / (us_dec * 1e-6) / 1e9,
+                                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": dec_bytes / (us_dec * 1e-6) / 1e9 / HBM_PEAK_GBS}},
+        "note": "torch_sdpa_* is torch.nn.functional.scaled_dot_product_attention with the "
+                "window as a boolean mask, for context"}
+
+
 def cpu_baseline(w):
     """The oracle on the whole headline workload (all 8 sequences x 8192 tokens x 10 heads),
     one OpenMP thread per (sequence, head) unit; inputs are generated before the clock starts."""
@@ -483,6 +574,8 @@ def main():
             "algorithmic_bytes": cb, "algorithmic_GBs": cb / (msc * 1e-3) / 1e9,
             "hbm_frac": cb / (msc * 1e-3) / 1e9 / HBM_PEAK_GBS}
         line["block_prefill"] = time_block(w, max(args.steps // 2, 5), args.warmup, torch, binding)
+        line["local_attention"] = time_attention(w, max(args.steps // 2, 5), args.warmup, torch,
+                                                 binding)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)

@@ -1,15 +1,15 @@
 // Local sliding-window multi-query attention, for gfx950 (CDNA4): the model's other
 // temporal-mixing block.  The page "Gemma 詳解：RecurrentGemma 架構" (section "含區域 MQA 的殘差
 // 區塊" and the printout's RecurrentGemmaSdpaAttention) gives Hq query heads of dh = 256
-// sharing one key/value head (multi-query attention), rotary position embedding on q and k as in
-// base Gemma, and attention restricted to a fixed window of past tokens (section "區域注意力視窗
-// 大小": 2k).  Here query t attends to tokens t - W + 1 .. t:
+// sharing one key/value head (multi-query attention), rotary position embedding on q and k
+// following the base Gemma model, and attention restricted to a fixed window of past tokens
+// (section "區域注意力視窗大小": 2k).  Here query t attends to tokens t - W + 1 .. t:
 //
 //   o[t, h] = sum_s softmax_s(q[t, h] . k[s] / sqrt(dh)) v[s]
 //
 // after RoPE turns each pair (x_i, x_{i + dh/2}) of q and k by t * base^(-2 i / dh).
 //
-// Two kernels:
+// Prefill, two kernels (decode, with a ring KV cache, is further down):
 //   attn_prep_kernel  RoPE on q and k (angles in fp64), and v regrouped in fours of keys,
 //                     [B][T/4][dh][4], the order in which the P.V MFMA reads it;
 //   attn_fwd_kernel   one workgroup per (sequence, head, 128 queries); each wave holds 32

@@ -441,8 +441,8 @@ int oracle_max_threads(void) {
  * model (page "Gemma 詳解：RecurrentGemma 架構", section "含區域 MQA 的殘差區塊" and the
  * printout's RecurrentGemmaSdpaAttention): q_proj (width -> Hq heads of dh, no bias),
  * k_proj and v_proj (width -> one head of dh shared by all query heads, no bias), rotary
- * position embedding on q and k "as in base Gemma", each position attending to a fixed window
- * of past tokens (section "區域注意力視窗大小": 2k tokens), and o_proj (with bias).
+ * position embedding on q and k following the base Gemma model, each position attending to a
+ * fixed window of past tokens (section "區域注意力視窗大小": 2k tokens), and o_proj (with bias).
  *
  * Readings (listed in the design doc):
  *   - RoPE pairs dimension i with i + dh/2 (the rotate-half convention) and turns pair i by
