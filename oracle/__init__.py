@@ -32,6 +32,7 @@ _lib = None
 
 F32 = 0
 BF16 = 1
+F64 = 2   # fp64 intermediates (inputs of a block inside a residual layer)
 
 
 def build(src: str = _SRC, out: str = _LIB) -> str:
@@ -82,15 +83,19 @@ def _bind(lib):
     lib.oracle_rglru_step.restype = ctypes.c_double
     lib.oracle_linear.argtypes = [I, I, I, I] + [P] * 4
     lib.oracle_linear.restype = I
-    lib.oracle_block_prefill.argtypes = [I, I, I, I, I, I] + [P] * 19 + [I]
+    lib.oracle_block_prefill.argtypes = [I, I, I, I, I, I, I] + [P] * 19 + [I]
     lib.oracle_block_prefill.restype = I
     D_ = ctypes.c_double
     lib.oracle_rope.argtypes = [I, I, P, D_, P]
     lib.oracle_rope.restype = I
     lib.oracle_local_mqa.argtypes = [I, I, I, I, P, P, P, P]
     lib.oracle_local_mqa.restype = I
-    lib.oracle_local_attention_block.argtypes = [I, I, I, I, I, I, I, D_] + [P] * 7 + [I]
+    lib.oracle_local_attention_block.argtypes = [I, I, I, I, I, I, I, I, D_] + [P] * 7 + [I]
     lib.oracle_local_attention_block.restype = I
+    lib.oracle_rmsnorm.argtypes = [I, I, I, I, P, P, D_, P]
+    lib.oracle_rmsnorm.restype = I
+    lib.oracle_mlp.argtypes = [I, I, I, I, I] + [P] * 8 + [I]
+    lib.oracle_mlp.restype = I
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = I
     return lib
@@ -278,11 +283,15 @@ def linear(x, w, b=None, lib=None):
 
 
 def block_prefill(p: Params, q: ProjParams, x_in, h0=None, conv0=None, nthreads: int = 0, lib=None):
-    """The recurrent block with its projections: x_in [B, T, Dm] (storage).
+    """The recurrent block with its projections: x_in [B, T, Dm] (storage, or fp64 as inside a
+    residual layer).
 
     Returns (out [B,T,Dm], h_last [B,D], conv_last [B,3,D]), all fp64."""
     lib = lib or load()
-    x_in = _c(x_in, p.conv_w.dtype)
+    x_in = _c(x_in)
+    if x_in.dtype != np.float64:
+        _c(x_in, p.conv_w.dtype)
+    xdt = F64 if x_in.dtype == np.float64 else p.dtype
     B, T, Dm = x_in.shape
     assert q.Dm == Dm and q.D == p.D
     h0 = _c(h0, np.float32)
@@ -290,7 +299,8 @@ def block_prefill(p: Params, q: ProjParams, x_in, h0=None, conv0=None, nthreads:
     out = np.empty((B, T, Dm), np.float64)
     h_last = np.empty((B, p.D), np.float64)
     conv_last = np.empty((B, 3, p.D), np.float64)
-    st = lib.oracle_block_prefill(p.dtype, B, T, Dm, p.D, p.H, _ptr(x_in), *q.args(), *p.args(),
+    st = lib.oracle_block_prefill(p.dtype, xdt, B, T, Dm, p.D, p.H, _ptr(x_in), *q.args(),
+                                  *p.args(),
                                   _ptr(h0), _ptr(conv0), _ptr(out), _ptr(h_last), _ptr(conv_last),
                                   int(nthreads))
     _check(st, "oracle_block_prefill")
@@ -324,22 +334,85 @@ def local_mqa(q, k, v, window: int, lib=None):
 
 def local_attention_block(x_in, wq, wk, wv, wo, bo, n_heads: int, window: int,
                           base: float = 10000.0, nthreads: int = 0, lib=None):
-    """The local-attention block: x_in [B, T, Dm] (storage) -> out [B, T, Dm] (fp64).
+    """The local-attention block: x_in [B, T, Dm] (storage, or fp64 as inside a residual layer)
+    -> out [B, T, Dm] (fp64).
     wq [Hq*dh, Dm], wk, wv [dh, Dm], wo [Dm, Hq*dh] (storage, [out][in]), bo [Dm] or None."""
     lib = lib or load()
     x_in = _c(x_in)
-    dt = _dtype_code(x_in)
-    wq, wk, wv, wo = (_c(a, x_in.dtype) for a in (wq, wk, wv, wo))
-    bo = _c(bo, x_in.dtype)
+    wq = _c(wq)
+    dt = _dtype_code(wq)
+    xdt = F64 if x_in.dtype == np.float64 else _dtype_code(x_in)
+    if xdt != F64 and xdt != dt:
+        raise TypeError("x_in must be fp64 or the weights' storage type")
+    wk, wv, wo = (_c(a, wq.dtype) for a in (wk, wv, wo))
+    bo = _c(bo, wq.dtype)
     B, T, Dm = x_in.shape
     dh = wk.shape[0]
     assert wq.shape == (n_heads * dh, Dm) and wv.shape == (dh, Dm) and wo.shape == (Dm, n_heads * dh)
     out = np.empty((B, T, Dm), np.float64)
-    st = lib.oracle_local_attention_block(dt, B, T, Dm, int(n_heads), dh, int(window), float(base),
+    st = lib.oracle_local_attention_block(dt, xdt, B, T, Dm, int(n_heads), dh, int(window),
+                                          float(base),
                                           _ptr(x_in), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo),
                                           _ptr(bo), _ptr(out), int(nthreads))
     _check(st, "oracle_local_attention_block")
     return out
+
+
+def rmsnorm(x, g, eps: float = 1e-6, lib=None):
+    """RMSNorm over the last axis: x [..., D] (storage or fp64), g [D] (storage) -> fp64."""
+    lib = lib or load()
+    x = _c(x)
+    g = _c(g)
+    D = x.shape[-1]
+    assert g.shape == (D,)
+    rows = x.size // D if D else 0
+    xdt = F64 if x.dtype == np.float64 else _dtype_code(x)
+    out = np.empty(x.shape, np.float64)
+    _check(lib.oracle_rmsnorm(xdt, _dtype_code(g), rows, D, _ptr(x), _ptr(g), float(eps),
+                              _ptr(out)), "oracle_rmsnorm")
+    return out
+
+
+class MlpParams:
+    """The gated MLP in storage form: gate_w, up_w [F, Dm], down_w [Dm, F] ([out][in]); biases
+    [F], [F], [Dm] or None."""
+
+    def __init__(self, gate_w, gate_b, up_w, up_b, down_w, down_b):
+        self.gate_w = _c(gate_w)
+        sd = self.gate_w.dtype
+        self.gate_b, self.up_w, self.up_b = _c(gate_b, sd), _c(up_w, sd), _c(up_b, sd)
+        self.down_w, self.down_b = _c(down_w, sd), _c(down_b, sd)
+        self.F, self.Dm = self.gate_w.shape
+        assert self.up_w.shape == (self.F, self.Dm) and self.down_w.shape == (self.Dm, self.F)
+
+    def args(self):
+        return [_ptr(a) for a in (self.gate_w, self.gate_b, self.up_w, self.up_b, self.down_w,
+                                  self.down_b)]
+
+
+def mlp(m: MlpParams, x, nthreads: int = 0, lib=None):
+    """The gated MLP: x [..., Dm] (storage or fp64) -> down(gelu_tanh(gate(x)) * up(x)), fp64."""
+    lib = lib or load()
+    x = _c(x)
+    assert x.shape[-1] == m.Dm
+    rows = x.size // m.Dm
+    xdt = F64 if x.dtype == np.float64 else _dtype_code(x)
+    out = np.empty(x.shape, np.float64)
+    _check(lib.oracle_mlp(xdt, _dtype_code(m.gate_w), rows, m.Dm, m.F, _ptr(x), *m.args(),
+                          _ptr(out), int(nthreads)), "oracle_mlp")
+    return out
+
+
+def residual_layer(x_in, temporal, g1, g2, m: MlpParams, eps: float = 1e-6, lib=None):
+    """One residual layer of the model (pre-norm, two residual additions):
+        h = x + temporal(RMSNorm_1(x)),   out = h + MLP(RMSNorm_2(h))
+    x_in [B, T, Dm] (storage); temporal maps an fp64 [B, T, Dm] array to fp64 [B, T, Dm] (the
+    recurrent block or the local-attention block); g1, g2 [Dm] (storage).  Returns
+    (out, h) in fp64."""
+    x = widen_bf16(x_in).astype(np.float64) if np.asarray(x_in).dtype == np.uint16 \
+        else np.asarray(x_in, np.float64)
+    h = x + temporal(rmsnorm(x_in, g1, eps, lib=lib))
+    return h + mlp(m, rmsnorm(h, g2, eps, lib=lib), lib=lib), h
 
 
 def gelu_tanh(yv: float, lib=None) -> float:

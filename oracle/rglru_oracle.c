@@ -303,13 +303,15 @@ int oracle_linear(int dtype, int M, int K, int N, const void *x, const void *w, 
 
 /*
  * The whole recurrent block's temporal mixing over T tokens:
- *   x_in [B][T][Dm] (storage) -> xb = linear_x(x_in), yb = linear_y(x_in)   [B][T][D] fp64
+ *   x_in [B][T][Dm] (type xdtype: the storage type, or fp64 inside a residual layer)
+ *   -> xb = linear_x(x_in), yb = linear_y(x_in)                             [B][T][D] fp64
  *   -> the path above (conv, RG-LRU, times GELU of yb)                      [B][T][D] fp64
  *   -> out = linear_out(.)                                                  [B][T][Dm] fp64
  * lx_w, ly_w [D][Dm]; lo_w [Dm][D]; biases [D], [D], [Dm] or NULL.  h_last [B][D] and
  * conv_last [B][3][D] (fp64) are the path's final state; conv0 holds storage-type values.
  */
-int oracle_block_prefill(int dtype, int B, int T, int Dm, int D, int H, const void *x_in,
+int oracle_block_prefill(int dtype, int xdtype, int B, int T, int Dm, int D, int H,
+                         const void *x_in,
                          const void *lx_w, const void *lx_b, const void *ly_w, const void *ly_b,
                          const void *lo_w, const void *lo_b, const void *conv_w,
                          const void *conv_b, const void *wa, const void *ba, const void *wx,
@@ -320,6 +322,7 @@ int oracle_block_prefill(int dtype, int B, int T, int Dm, int D, int H, const vo
     int st = make_prm(&p, dtype, D, H, conv_w, conv_b, wa, ba, wx, bx, lambda);
     if (st) return st;
     if (B < 1 || T < 0 || Dm < 1) return 2;
+    if (xdtype != dtype && xdtype != ORACLE_F64) return 3;
     if (!x_in || !lx_w || !ly_w || !lo_w) return 1;
     const size_t MD = (size_t)B * T * D;
     double *xb = (double *)malloc(sizeof(double) * (3 * MD + 1));
@@ -328,8 +331,8 @@ int oracle_block_prefill(int dtype, int B, int T, int Dm, int D, int H, const vo
 #ifdef _OPENMP
     if (nthreads > 0) omp_set_num_threads(nthreads);
 #endif
-    linear_rows(B * T, Dm, D, x_in, dtype, lx_w, lx_b, dtype, xb);
-    linear_rows(B * T, Dm, D, x_in, dtype, ly_w, ly_b, dtype, yb);
+    linear_rows(B * T, Dm, D, x_in, xdtype, lx_w, lx_b, dtype, xb);
+    linear_rows(B * T, Dm, D, x_in, xdtype, ly_w, ly_b, dtype, yb);
     p.xdtype = ORACLE_F64;
     prefill_all(&p, B, T, xb, yb, h0, conv0, mg, h_last, conv_last, nthreads);
     linear_rows(B * T, D, Dm, mg, ORACLE_F64, lo_w, lo_b, dtype, out);
@@ -514,16 +517,17 @@ int oracle_local_mqa(int T, int Hq, int dh, int W, const double *q, const double
 
 /*
  * The local-attention temporal-mixing block over B sequences of T tokens:
- *   x_in [B][T][Dm] (storage) -> q = x Wq^T [.., Hq*dh], k = x Wk^T [.., dh], v = x Wv^T
+ *   x_in [B][T][Dm] (type xdtype: storage, or fp64 inside a residual layer) -> q = x Wq^T [.., Hq*dh], k = x Wk^T [.., dh], v = x Wv^T
  *   (no biases) -> RoPE on q (each head) and k at positions 0 .. T-1 -> local MQA with window
  *   W -> out = o Wo^T + bo  [B][T][Dm] (fp64).  Wq [Hq*dh][Dm], Wk, Wv [dh][Dm], Wo [Dm][Hq*dh].
  */
-int oracle_local_attention_block(int dtype, int B, int T, int Dm, int Hq, int dh, int W,
-                                 double base, const void *x_in, const void *wq, const void *wk,
-                                 const void *wv, const void *wo, const void *bo, double *out,
-                                 int nthreads) {
+int oracle_local_attention_block(int dtype, int xdtype, int B, int T, int Dm, int Hq, int dh,
+                                 int W, double base, const void *x_in, const void *wq,
+                                 const void *wk, const void *wv, const void *wo, const void *bo,
+                                 double *out, int nthreads) {
     if (B < 1 || T < 0 || Dm < 1 || Hq < 1 || dh < 2 || dh % 2 || W < 1) return 2;
     if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return 3;
+    if (xdtype != dtype && xdtype != ORACLE_F64) return 3;
     if (!x_in || !wq || !wk || !wv || !wo || !out) return 1;
 #ifdef _OPENMP
     if (nthreads > 0) omp_set_num_threads(nthreads);
@@ -537,10 +541,11 @@ int oracle_local_attention_block(int dtype, int B, int T, int Dm, int Hq, int dh
     if (!q || !k || !v || !o) return 1;
     for (int b = 0; b < B; ++b) {
         const size_t xoff = (size_t)b * T * Dm;
-        const void *xb = (const char *)x_in + xoff * (dtype == ORACLE_F32 ? 4 : 2);
-        linear_rows(T, Dm, DQ, xb, dtype, wq, NULL, dtype, q);
-        linear_rows(T, Dm, dh, xb, dtype, wk, NULL, dtype, k);
-        linear_rows(T, Dm, dh, xb, dtype, wv, NULL, dtype, v);
+        const size_t xes = xdtype == ORACLE_F64 ? 8 : (xdtype == ORACLE_F32 ? 4 : 2);
+        const void *xb = (const char *)x_in + xoff * xes;
+        linear_rows(T, Dm, DQ, xb, xdtype, wq, NULL, dtype, q);
+        linear_rows(T, Dm, dh, xb, xdtype, wk, NULL, dtype, k);
+        linear_rows(T, Dm, dh, xb, xdtype, wv, NULL, dtype, v);
         for (int t = 0; t < T; ++t) {
             for (int h = 0; h < Hq; ++h) rope_head(q + ((size_t)t * Hq + h) * dh, dh, (double)t, base);
             rope_head(k + (size_t)t * dh, dh, (double)t, base);
@@ -552,5 +557,61 @@ int oracle_local_attention_block(int dtype, int B, int T, int Dm, int Hq, int dh
     free(k);
     free(v);
     free(o);
+    return 0;
+}
+
+/* ======================================================================================
+ * The residual layer's other parts: the page "Gemma 詳解：RecurrentGemma 架構" (module
+ * printout; sections "含遞迴區塊的殘差區塊" and "含區域 MQA 的殘差區塊") puts an RMSNorm
+ * (temporal_pre_norm) before the temporal-mixing block and another (channel_pre_norm) before
+ * the MLP, whose gate_proj and up_proj (width -> 3 x width, with bias), GELU-tanh act_fn and
+ * down_proj (back to the width, with bias) follow the base Gemma feed-forward layer.
+ *
+ * Readings (listed in the design doc):
+ *   - RMSNorm(x) = x / sqrt(mean_d x_d^2 + eps) * g, with g the per-channel scale (models that
+ *     store w with g = 1 + w pass 1 + w); eps is an argument (1e-6 in the tests);
+ *   - MLP(x) = down_proj(gelu_tanh(gate_proj(x)) * up_proj(x)): the activation is applied to
+ *     the gate branch only;
+ *   - the layer is pre-norm with two residual additions:
+ *       h = x + temporal(RMSNorm_1(x)),  out = h + MLP(RMSNorm_2(h)).
+ * ====================================================================================== */
+
+/* RMSNorm over rows of D: x [rows][D] (type xdtype), g [D] (type wdtype) -> out fp64. */
+int oracle_rmsnorm(int xdtype, int wdtype, int rows, int D, const void *x, const void *g,
+                   double eps, double *out) {
+    if (rows < 0 || D < 1 || !(eps >= 0.0)) return 2;
+    if (!x || !g || !out) return 1;
+    for (int r = 0; r < rows; ++r) {
+        double ss = 0.0;
+        for (int d = 0; d < D; ++d) {
+            const double v = widen(x, (size_t)r * D + d, xdtype);
+            ss += v * v;
+        }
+        const double inv = 1.0 / sqrt(ss / (double)D + eps);
+        for (int d = 0; d < D; ++d)
+            out[(size_t)r * D + d] = widen(x, (size_t)r * D + d, xdtype) * inv * widen(g, d, wdtype);
+    }
+    return 0;
+}
+
+/* The gated MLP over rows: x [rows][Dm] (type xdtype); gate_w, up_w [F][Dm], down_w [Dm][F]
+ * ([out][in], type wdtype); biases [F], [F], [Dm] or NULL -> out [rows][Dm] fp64. */
+int oracle_mlp(int xdtype, int wdtype, int rows, int Dm, int F, const void *x, const void *gw,
+               const void *gb, const void *uw, const void *ub, const void *dw, const void *db,
+               double *out, int nthreads) {
+    if (rows < 0 || Dm < 1 || F < 1) return 2;
+    if (!x || !gw || !uw || !dw || !out) return 1;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#endif
+    const size_t n = (size_t)rows * F;
+    double *gt = (double *)malloc(sizeof(double) * (2 * n + 1));
+    if (!gt) return 1;
+    double *up = gt + n;
+    linear_rows(rows, Dm, F, x, xdtype, gw, gb, wdtype, gt);
+    linear_rows(rows, Dm, F, x, xdtype, uw, ub, wdtype, up);
+    for (size_t i = 0; i < n; ++i) gt[i] = oracle_gelu_tanh(gt[i]) * up[i];
+    linear_rows(rows, F, Dm, gt, ORACLE_F64, dw, db, wdtype, out);
+    free(gt);
     return 0;
 }

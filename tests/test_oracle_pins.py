@@ -698,6 +698,113 @@ def test_variance_is_sane():
 
 
 # ----------------------------------------------------------------------------------------------
+# the residual layer: RMSNorm, gated MLP, composition
+# ----------------------------------------------------------------------------------------------
+def _pin_rmsnorm_closed_forms(lib):
+    """RMSNorm against closed forms (eps = 0 unless stated):
+    - alternating +a, -a: the root mean square is |a|, so the output is +-g exactly;
+    - one nonzero entry v of D: the root mean square is |v| / sqrt(D), so that entry becomes
+      sign(v) sqrt(D) g_j and the rest stay 0;
+    - a constant row c with eps: c / sqrt(c^2 + eps) g (0.5 and eps 0.25 give g / sqrt(2));
+    - scaling a row by a power of two changes nothing, and with g = 1 the output's mean square
+      is 1; bf16 inputs give the same as their exact fp64 values."""
+    D = 8
+    g = np.array([1.0, 2.0, 0.5, -1.0, 3.0, 1.5, 0.25, 4.0], np.float32)
+    x = np.array([[3.0, -3.0] * 4, [-0.5, 0.5] * 4])
+    out = oracle.rmsnorm(x, g, 0.0, lib=lib)
+    assert np.array_equal(out, np.sign(x) * g.astype(np.float64))
+    x = np.zeros((1, D))
+    x[0, 5] = -7.0
+    out = oracle.rmsnorm(x, g, 0.0, lib=lib)
+    want = np.zeros((1, D))
+    want[0, 5] = -np.sqrt(D) * 1.5
+    assert np.allclose(out, want, rtol=1e-15, atol=0)
+    out = oracle.rmsnorm(np.full((1, D), 0.5), g, 0.25, lib=lib)
+    assert np.allclose(out, g / np.sqrt(2.0), rtol=1e-15, atol=0)
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((5, 64))
+    ones = np.ones(64, np.float32)
+    a = oracle.rmsnorm(x, ones, 0.0, lib=lib)
+    b = oracle.rmsnorm(x * 4.0, ones, 0.0, lib=lib)
+    assert np.array_equal(a, b)
+    assert np.allclose((a * a).mean(axis=1), 1.0, rtol=1e-13, atol=0)
+    xb = synth.round_bf16(x.astype(np.float32))
+    assert np.array_equal(oracle.rmsnorm(xb, ones, 1e-6, lib=lib),
+                          oracle.rmsnorm(oracle.widen_bf16(xb).astype(np.float64), ones, 1e-6,
+                                         lib=lib))
+
+
+def _pin_mlp_integer_exact(lib):
+    """The gated MLP on integers where GELU-tanh is exactly the identity (pre-activations of 10
+    or more: tanh rounds to 1 in fp64, which the pin checks first): then
+    out = b_d + W_d ((W_g x + b_g) * (W_u x + b_u)) exactly, against numpy's integer matmul.
+    The up branch takes small values of both signs, on which GELU is far from the identity.
+    With the up branch zero, the output is the down bias alone."""
+    assert oracle.gelu_tanh(10.0, lib=lib) == 10.0 and oracle.gelu_tanh(17.0, lib=lib) == 17.0
+    rng = np.random.default_rng(4)
+    rows, Dm, F = 6, 8, 12
+    x = rng.integers(0, 3, (rows, Dm)).astype(np.float32)
+    wg = rng.integers(0, 2, (F, Dm)).astype(np.float32)
+    bg = np.full(F, 10.0, np.float32)
+    wu = rng.integers(-2, 3, (F, Dm)).astype(np.float32)
+    bu = rng.integers(-3, 4, F).astype(np.float32)
+    wd = rng.integers(-2, 3, (Dm, F)).astype(np.float32)
+    bd = rng.integers(-5, 6, Dm).astype(np.float32)
+    m = oracle.MlpParams(wg, bg, wu, bu, wd, bd)
+    out = oracle.mlp(m, x, lib=lib)
+    xi = x.astype(np.int64)
+    gate = xi @ wg.astype(np.int64).T + bg.astype(np.int64)
+    up = xi @ wu.astype(np.int64).T + bu.astype(np.int64)
+    assert gate.min() >= 10 and up.min() < 0 < up.max()
+    want = (gate * up) @ wd.astype(np.int64).T + bd.astype(np.int64)
+    assert np.array_equal(out, want.astype(np.float64))
+    z = oracle.MlpParams(wg, bg, np.zeros_like(wu), np.zeros_like(bu), wd, bd)
+    assert np.array_equal(oracle.mlp(z, x, lib=lib), np.broadcast_to(bd.astype(np.float64), x.shape))
+
+
+def _pin_residual_layer_composition(lib):
+    """The residual layer around a temporal block whose output is known exactly: with the
+    recurrent block's linear_out weights zero and its bias c, the block gives c for every token,
+    so h = x + c exactly, and out must be h + MLP(RMSNorm_2(h)) with the pinned MLP and RMSNorm
+    applied to that h (not to x).  The same holds for the local-attention block with o_proj
+    zero.  The blocks also take fp64 inputs (as inside the layer) exactly like storage ones."""
+    rng = np.random.default_rng(6)
+    w = synth.small(synth.WORKLOADS[synth.TINY], B=2, T=9)
+    Dm, F = 256, 64
+    p = synth.make_params(w, biases=True)
+    q = synth.make_proj(w, Dm=Dm, biases=True)
+    c = rng.standard_normal(Dm).astype(np.float32)
+    P = oracle.Params(p["conv_w"], p["conv_b"], p["wa"], p["ba"], p["wx"], p["bx"], p["lambda"], w.H)
+    Qz = oracle.ProjParams(q["lx_w"], q["lx_b"], q["ly_w"], q["ly_b"], np.zeros_like(q["lo_w"]), c)
+    x = rng.standard_normal((2, 9, Dm)).astype(np.float32)
+    g1 = (1.0 + 0.1 * rng.standard_normal(Dm)).astype(np.float32)
+    g2 = (1.0 + 0.1 * rng.standard_normal(Dm)).astype(np.float32)
+    m = oracle.MlpParams(*(rng.standard_normal(s).astype(np.float32) / 8
+                           for s in ((F, Dm), F, (F, Dm), F, (Dm, F), Dm)))
+    out, h = oracle.residual_layer(x, lambda xn: oracle.block_prefill(P, Qz, xn, lib=lib)[0],
+                                   g1, g2, m, lib=lib)
+    hw = x.astype(np.float64) + c.astype(np.float64)
+    assert np.array_equal(h, hw)
+    assert np.array_equal(out, hw + oracle.mlp(m, oracle.rmsnorm(hw, g2, lib=lib), lib=lib))
+    # the attention block with o_proj zero and bias c
+    Hq, dh = 1, 16
+    wq, wk, wv = (rng.standard_normal((n, Dm)).astype(np.float32) / 16 for n in (Hq * dh, dh, dh))
+    out2, h2 = oracle.residual_layer(
+        x, lambda xn: oracle.local_attention_block(xn, wq, wk, wv, np.zeros((Dm, Hq * dh), np.float32),
+                                                   c, Hq, 4, lib=lib), g1, g2, m, lib=lib)
+    assert np.array_equal(h2, hw) and np.array_equal(out2, out)
+    # fp64 inputs to the blocks equal their storage inputs
+    Q = oracle.ProjParams(q["lx_w"], q["lx_b"], q["ly_w"], q["ly_b"], q["lo_w"], q["lo_b"])
+    a = oracle.block_prefill(P, Q, x, lib=lib)[0]
+    b = oracle.block_prefill(P, Q, x.astype(np.float64), lib=lib)[0]
+    assert np.array_equal(a, b)
+    wo = rng.standard_normal((Dm, Hq * dh)).astype(np.float32) / 4
+    a = oracle.local_attention_block(x, wq, wk, wv, wo, c, Hq, 4, lib=lib)
+    b = oracle.local_attention_block(x.astype(np.float64), wq, wk, wv, wo, c, Hq, 4, lib=lib)
+    assert np.array_equal(a, b)
+
+
+# ----------------------------------------------------------------------------------------------
 # planted mistakes: each plausible error in the oracle must fail at least one pin
 # ----------------------------------------------------------------------------------------------
 PINS = [
@@ -708,6 +815,7 @@ PINS = [
     _pin_linear_library, _pin_linear_exact, _pin_block_composition, _pin_block_rectangular,
     _pin_rope_complex, _pin_rope_relative, _pin_mqa_closed_forms, _pin_mqa_invariants,
     _pin_attention_block_composition,
+    _pin_rmsnorm_closed_forms, _pin_mlp_integer_exact, _pin_residual_layer_composition,
 ]
 
 MUTANTS = {
@@ -737,8 +845,8 @@ MUTANTS = {
     "linear weight transposed": ("widen(w, (size_t)n * K + k, wdtype)", "widen(w, (size_t)k * N + n, wdtype)"),
     "linear bias dropped": ("double s = b ? widen(b, (size_t)n, wdtype) : 0.0;", "double s = 0.0;"),
     "linear input row": ("widen(in, (size_t)m * K + k, xdtype)", "widen(in, (size_t)k, xdtype)"),
-    "branches swapped": ("linear_rows(B * T, Dm, D, x_in, dtype, lx_w, lx_b, dtype, xb);",
-                         "linear_rows(B * T, Dm, D, x_in, dtype, ly_w, ly_b, dtype, xb);"),
+    "branches swapped": ("linear_rows(B * T, Dm, D, x_in, xdtype, lx_w, lx_b, dtype, xb);",
+                         "linear_rows(B * T, Dm, D, x_in, xdtype, ly_w, ly_b, dtype, xb);"),
     "output projection skips the path": (
         "linear_rows(B * T, D, Dm, mg, ORACLE_F64, lo_w, lo_b, dtype, out);",
         "linear_rows(B * T, D, Dm, xb, ORACLE_F64, lo_w, lo_b, dtype, out);"),
@@ -754,6 +862,17 @@ MUTANTS = {
     "scores not scaled": ("score[s] = d * scale;", "score[s] = d;"),
     "output projection on q": ("linear_rows(T, DQ, Dm, o, ORACLE_F64, wo, bo, dtype, out + xoff);",
                                "linear_rows(T, DQ, Dm, q, ORACLE_F64, wo, bo, dtype, out + xoff);"),
+    "rmsnorm sum instead of mean": ("sqrt(ss / (double)D + eps)", "sqrt(ss + eps)"),
+    "rmsnorm eps outside the root": ("1.0 / sqrt(ss / (double)D + eps)", "1.0 / (sqrt(ss / (double)D) + eps)"),
+    "rmsnorm scale dropped": ("* inv * widen(g, d, wdtype)", "* inv"),
+    "mlp activation on the up branch": ("gt[i] = oracle_gelu_tanh(gt[i]) * up[i];",
+                                        "gt[i] = gt[i] * oracle_gelu_tanh(up[i]);"),
+    "mlp up branch dropped": ("gt[i] = oracle_gelu_tanh(gt[i]) * up[i];",
+                              "gt[i] = oracle_gelu_tanh(gt[i]);"),
+    "mlp down bias dropped": ("linear_rows(rows, F, Dm, gt, ORACLE_F64, dw, db, wdtype, out);",
+                              "linear_rows(rows, F, Dm, gt, ORACLE_F64, dw, NULL, wdtype, out);"),
+    "block input type ignored": ("linear_rows(T, Dm, DQ, xb, xdtype, wq, NULL, dtype, q);",
+                                 "linear_rows(T, Dm, DQ, xb, dtype, wq, NULL, dtype, q);"),
 }
 
 
