@@ -30,7 +30,9 @@ EXPORTS = ["rglru_prefill_workspace_bytes", "rglru_prefill_workspace_init", "rgl
            "rglru_block_prefill", "rglru_local_attention_workspace_bytes", "rglru_local_attention",
            "rglru_local_attention_block_workspace_bytes", "rglru_local_attention_block",
            "rglru_local_attention_cache_bytes", "rglru_local_attention_decode_workspace_bytes",
-           "rglru_local_attention_decode"]
+           "rglru_local_attention_decode", "rglru_rmsnorm", "rglru_mlp_workspace_bytes",
+           "rglru_mlp", "rglru_recurrent_layer_workspace_bytes", "rglru_recurrent_layer_prefill",
+           "rglru_attention_layer_workspace_bytes", "rglru_attention_layer_prefill"]
 
 _lock = threading.Lock()
 _lib = None
@@ -66,6 +68,18 @@ class rglru_attn_params(ctypes.Structure):
                 ("rope_base", ctypes.c_float),
                 ("q_w", ctypes.c_void_p), ("k_w", ctypes.c_void_p), ("v_w", ctypes.c_void_p),
                 ("o_w", ctypes.c_void_p), ("o_b", ctypes.c_void_p)]
+
+
+class rglru_norm_params(ctypes.Structure):
+    _fields_ = [("temporal_scale", ctypes.c_void_p), ("channel_scale", ctypes.c_void_p),
+                ("eps", ctypes.c_float)]
+
+
+class rglru_mlp_params(ctypes.Structure):
+    _fields_ = [("D_model", ctypes.c_int32), ("F", ctypes.c_int32),
+                ("gate_w", ctypes.c_void_p), ("gate_b", ctypes.c_void_p),
+                ("up_w", ctypes.c_void_p), ("up_b", ctypes.c_void_p),
+                ("down_w", ctypes.c_void_p), ("down_b", ctypes.c_void_p)]
 
 
 def load_library(path: str = LIB_PATH):
@@ -122,6 +136,22 @@ def load_library(path: str = LIB_PATH):
         lib.rglru_local_attention_block_workspace_bytes.restype = SZ
         lib.rglru_local_attention_block.argtypes = [AP, I32, I32, P, P, P, SZ, P]
         lib.rglru_local_attention_block.restype = ctypes.c_int
+        NP, MP = ctypes.POINTER(rglru_norm_params), ctypes.POINTER(rglru_mlp_params)
+        lib.rglru_rmsnorm.argtypes = [I32, I32, P, P, P, ctypes.c_float, P, P, P]
+        lib.rglru_rmsnorm.restype = ctypes.c_int
+        lib.rglru_mlp_workspace_bytes.argtypes = [I32, I32]
+        lib.rglru_mlp_workspace_bytes.restype = SZ
+        lib.rglru_mlp.argtypes = [MP, I32, P, P, P, SZ, P]
+        lib.rglru_mlp.restype = ctypes.c_int
+        lib.rglru_recurrent_layer_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32]
+        lib.rglru_recurrent_layer_workspace_bytes.restype = SZ
+        lib.rglru_recurrent_layer_prefill.argtypes = [PP, ctypes.POINTER(rglru_proj_params), NP, MP,
+                                                      I32, I32, P, P, P, P, P, P, P, SZ, P]
+        lib.rglru_recurrent_layer_prefill.restype = ctypes.c_int
+        lib.rglru_attention_layer_workspace_bytes.argtypes = [AP, I32, I32, I32]
+        lib.rglru_attention_layer_workspace_bytes.restype = SZ
+        lib.rglru_attention_layer_prefill.argtypes = [AP, NP, MP, I32, I32, P, P, P, P, P, SZ, P]
+        lib.rglru_attention_layer_prefill.restype = ctypes.c_int
         lib.rglru_abi_version.argtypes = []
         lib.rglru_abi_version.restype = ctypes.c_int
         _lib = lib
@@ -528,4 +558,133 @@ def rglru_local_attention_block(a: AttnParams, x_in, *, out=None,
     st = lib.rglru_local_attention_block(ctypes.byref(a.c), B, T, _ptr(x_in), _ptr(out),
                                          _ptr(workspace.t), workspace.nbytes, _stream())
     _check(lib, st, "rglru_local_attention_block")
+    return out
+
+
+# ------------------------------------------------------------------------------------------
+# the residual layer
+# ------------------------------------------------------------------------------------------
+class NormParams:
+    """The layer's two RMSNorm scales ([D_model] bf16 each) and eps."""
+
+    def __init__(self, temporal_scale, channel_scale, eps: float = 1e-6):
+        Dm = temporal_scale.shape[0]
+        dev = temporal_scale.device
+        _need(temporal_scale, "temporal_scale", torch.bfloat16, (Dm,), dev)
+        _need(channel_scale, "channel_scale", torch.bfloat16, (Dm,), dev)
+        self.Dm, self.device = Dm, dev
+        self.tensors = (temporal_scale, channel_scale)
+        self.c = rglru_norm_params(temporal_scale.data_ptr(), channel_scale.data_ptr(), float(eps))
+
+
+class MlpParams:
+    """The MLP (bf16, Linear weights [out, in]): gate_w, up_w [F, D_model], down_w [D_model, F];
+    biases [F], [F], [D_model] or None."""
+
+    def __init__(self, gate_w, gate_b, up_w, up_b, down_w, down_b):
+        F, Dm = gate_w.shape
+        dev = gate_w.device
+        _need(gate_w, "gate_w", torch.bfloat16, (F, Dm), dev)
+        _need(up_w, "up_w", torch.bfloat16, (F, Dm), dev)
+        _need(down_w, "down_w", torch.bfloat16, (Dm, F), dev)
+        _need(gate_b, "gate_b", torch.bfloat16, (F,), dev)
+        _need(up_b, "up_b", torch.bfloat16, (F,), dev)
+        _need(down_b, "down_b", torch.bfloat16, (Dm,), dev)
+        self.F, self.Dm, self.device = F, Dm, dev
+        self.tensors = (gate_w, gate_b, up_w, up_b, down_w, down_b)
+        self.c = rglru_mlp_params(Dm, F, *[t.data_ptr() if t is not None else None
+                                           for t in self.tensors])
+
+
+def rglru_rmsnorm(x, scale=None, residual=None, eps: float = 1e-6, *, want_norm: bool = True,
+                  want_h: bool = False, out=None, h_out=None):
+    """h = x (+ residual) and RMSNorm(h) * scale over the last axis (bf16).  Returns
+    (out, h_out) with None for what was not asked for."""
+    lib = load_library()
+    D = x.shape[-1]
+    M = x.numel() // D if D else 0
+    _need(x, "x", torch.bfloat16)
+    _need(residual, "residual", torch.bfloat16, tuple(x.shape), x.device)
+    _need(scale, "scale", torch.bfloat16, (D,), x.device)
+    if want_norm and out is None:
+        out = torch.empty_like(x)
+    if want_h and h_out is None:
+        h_out = torch.empty_like(x)
+    _need(out, "out", torch.bfloat16, tuple(x.shape), x.device)
+    _need(h_out, "h_out", torch.bfloat16, tuple(x.shape), x.device)
+    st = lib.rglru_rmsnorm(M, D, _ptr(x), _ptr(residual), _ptr(scale), float(eps), _ptr(h_out),
+                           _ptr(out), _stream())
+    _check(lib, st, "rglru_rmsnorm")
+    return out, h_out
+
+
+def rglru_mlp(m: MlpParams, x, *, out=None, workspace: DeviceBuffer | None = None):
+    """The gated MLP over the rows of x [..., D_model] (bf16)."""
+    lib = load_library()
+    M = x.numel() // m.Dm
+    _need(x, "x", torch.bfloat16, None, m.device)
+    if x.shape[-1] != m.Dm:
+        raise ValueError("x width %d, MLP width %d" % (x.shape[-1], m.Dm))
+    if out is None:
+        out = torch.empty_like(x)
+    _need(out, "out", torch.bfloat16, tuple(x.shape), m.device)
+    if workspace is None:
+        workspace = DeviceBuffer(int(lib.rglru_mlp_workspace_bytes(M, m.F)), m.device)
+    st = lib.rglru_mlp(ctypes.byref(m.c), M, _ptr(x), _ptr(out), _ptr(workspace.t),
+                       workspace.nbytes, _stream())
+    _check(lib, st, "rglru_mlp")
+    return out
+
+
+def make_recurrent_layer_workspace(p: Params, q: ProjParams, m: MlpParams, B: int,
+                                   T: int) -> Workspace:
+    lib = load_library()
+    return Workspace(int(lib.rglru_recurrent_layer_workspace_bytes(B, T, p.D, p.H, q.Dm, m.F)),
+                     p.device)
+
+
+def rglru_recurrent_layer_prefill(p: Params, q: ProjParams, n: NormParams, m: MlpParams, x_in,
+                                  h0=None, conv0=None, *, out=None, h_last=None, conv_last=None,
+                                  workspace: Workspace | None = None):
+    """The residual layer around the recurrent block.  Returns (out, h_last, conv_last)."""
+    lib = load_library()
+    B, T, Dm = x_in.shape
+    _need(x_in, "x_in", torch.bfloat16, (B, T, q.Dm), p.device)
+    _need(h0, "h0", torch.float32, (B, p.D), p.device)
+    _need(conv0, "conv0", torch.bfloat16, (B, 3, p.D), p.device)
+    if out is None:
+        out = torch.empty_like(x_in)
+    if h_last is None:
+        h_last = torch.empty((B, p.D), dtype=torch.float32, device=p.device)
+    if conv_last is None:
+        conv_last = torch.empty((B, 3, p.D), dtype=torch.bfloat16, device=p.device)
+    if workspace is None:
+        workspace = make_recurrent_layer_workspace(p, q, m, B, T)
+    st = lib.rglru_recurrent_layer_prefill(ctypes.byref(p.c), ctypes.byref(q.c), ctypes.byref(n.c),
+                                           ctypes.byref(m.c), B, T, _ptr(x_in), _ptr(out),
+                                           _ptr(h0), _ptr(h_last), _ptr(conv0), _ptr(conv_last),
+                                           _ptr(workspace.t), workspace.nbytes, _stream())
+    _check(lib, st, "rglru_recurrent_layer_prefill")
+    return out, h_last, conv_last
+
+
+def rglru_attention_layer_prefill(a: AttnParams, n: NormParams, m: MlpParams, x_in, *,
+                                  cache: AttnCache | None = None, out=None,
+                                  workspace: DeviceBuffer | None = None):
+    """The residual layer around the local-attention block (optionally filling a ring cache)."""
+    lib = load_library()
+    B, T, Dm = x_in.shape
+    _need(x_in, "x_in", torch.bfloat16, (B, T, a.Dm), a.device)
+    if out is None:
+        out = torch.empty_like(x_in)
+    if workspace is None:
+        workspace = DeviceBuffer(int(lib.rglru_attention_layer_workspace_bytes(
+            ctypes.byref(a.c), B, T, m.F)), a.device)
+    if cache is not None and (cache.N != B or cache.window != a.window):
+        raise ValueError("cache is for N=%d window=%d" % (cache.N, cache.window))
+    st = lib.rglru_attention_layer_prefill(
+        ctypes.byref(a.c), ctypes.byref(n.c), ctypes.byref(m.c), B, T, _ptr(x_in), _ptr(out),
+        _ptr(cache.k) if cache is not None else None, _ptr(cache.v) if cache is not None else None,
+        _ptr(workspace.t), workspace.nbytes, _stream())
+    _check(lib, st, "rglru_attention_layer_prefill")
     return out

@@ -285,10 +285,15 @@ size_t rglru_block_prefill_workspace_bytes(int32_t B, int32_t T, int32_t D, int3
     return ((pw + 255) & ~(size_t)255) + 3 * act;
 }
 
-int rglru_block_prefill(const rglru_params* p, const rglru_proj_params* q, int32_t B, int32_t T,
-                        const void* x_in, void* out, const float* h0, float* h_last,
-                        const void* conv0, void* conv_last, void* workspace, size_t ws_bytes,
-                        void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The recurrent block: every check runs first; with launch = false nothing else happens.
+int block_prefill_impl(const rglru_params* p, const rglru_proj_params* q, int32_t B, int32_t T,
+                       const void* x_in, void* out, const float* h0, float* h_last,
+                       const void* conv0, void* conv_last, void* workspace, size_t ws_bytes,
+                       void* stream, bool launch) {
     int st = check_params(p, true);
     if (st != RGLRU_OK) return st;
     if (!q) return RGLRU_ERR_NULL;
@@ -328,7 +333,7 @@ int rglru_block_prefill(const rglru_params* p, const rglru_proj_params* q, int32
     void* mg = T > 0 ? base + 2 * act : nullptr;
     // the path's own checks, before anything is launched
     st = check_prefill(p, B, T, xb, yb, mg, h0, h_last, conv0, conv_last, workspace, pw);
-    if (st != RGLRU_OK) return st;
+    if (st != RGLRU_OK || !launch) return st;
     if (T == 0)  // state pass-through only
         return rglru_prefill(p, B, 0, nullptr, nullptr, nullptr, h0, h_last, conv0, conv_last,
                              nullptr, 0, stream);
@@ -347,6 +352,18 @@ int rglru_block_prefill(const rglru_params* p, const rglru_proj_params* q, int32
     g.M = M; g.K = D; g.Nw[0] = Dm; g.nseg = 1;
     e = launch_proj_gemm(g, (hipStream_t)stream);
     return e == hipSuccess ? RGLRU_OK : hip_fail(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int rglru_block_prefill(const rglru_params* p, const rglru_proj_params* q, int32_t B, int32_t T,
+                        const void* x_in, void* out, const float* h0, float* h_last,
+                        const void* conv0, void* conv_last, void* workspace, size_t ws_bytes,
+                        void* stream) {
+    return block_prefill_impl(p, q, B, T, x_in, out, h0, h_last, conv0, conv_last, workspace,
+                              ws_bytes, stream, true);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -462,9 +479,15 @@ size_t rglru_local_attention_block_workspace_bytes(const rglru_attn_params* a, i
     return 2 * nq + 2 * nk + rglru_local_attention_workspace_bytes(B, T, a->n_heads);
 }
 
-int rglru_local_attention_block(const rglru_attn_params* a, int32_t B, int32_t T,
-                                const void* x_in, void* out, void* workspace, size_t ws_bytes,
-                                void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The local-attention block (optionally filling the ring caches): every check runs first; with
+// launch = false nothing else happens.
+int attn_block_impl(const rglru_attn_params* a, int32_t B, int32_t T, const void* x_in, void* out,
+                    void* kcache, void* vcache, void* workspace, size_t ws_bytes, void* stream,
+                    bool launch) {
     if (!a) return RGLRU_ERR_NULL;
     if (a->head_dim != kAttnDh) return RGLRU_ERR_UNSUPPORTED;
     if (B < 1 || T < 0 || a->D_model < 1 || a->n_heads < 1 || a->n_heads > 64 || a->window < 1 ||
@@ -500,15 +523,25 @@ int rglru_local_attention_block(const rglru_attn_params* a, int32_t B, int32_t T
     void* aw = T > 0 ? ws + 2 * nq + 2 * nk : nullptr;
     const size_t aw_bytes = rglru_local_attention_workspace_bytes(B, T, Hq);
     // the attention's own checks, before anything is launched
-    int st = rglru_local_attention(B, 0, Hq, a->window, a->rope_base, qb, kb, vb, ob, nullptr,
-                                   nullptr, aw, aw_bytes, stream);
+    int st = rglru_local_attention(B, 0, Hq, a->window, a->rope_base, qb, kb, vb, ob, kcache,
+                                   vcache, aw, aw_bytes, stream);
     if (st != RGLRU_OK) return st;
     const long long T4 = ((long long)T + 3) / 4;
     if (T >= (1 << 22) || (long long)B * 4 * T4 >= (1LL << 24) ||
         (long long)B * Hq * (((long long)T + 127) / 128) >= (1LL << 24) ||
         M >= ((size_t)1 << 31))
         return RGLRU_ERR_UNSUPPORTED;
-    if (T == 0) return RGLRU_OK;
+    if (kcache) {
+        const size_t nc = rglru_local_attention_cache_bytes(B, a->window);
+        if (overlap(kcache, nc, x_in, n_io) || overlap(vcache, nc, x_in, n_io) ||
+            overlap(kcache, nc, out, n_io) || overlap(vcache, nc, out, n_io) ||
+            (T > 0 && (overlap(kcache, nc, workspace, need) || overlap(vcache, nc, workspace, need))))
+            return RGLRU_ERR_ALIAS;
+        for (int i = 1; i < 6; ++i)
+            if (overlap(kcache, nc, ins[i], ins_len[i]) || overlap(vcache, nc, ins[i], ins_len[i]))
+                return RGLRU_ERR_ALIAS;
+    }
+    if (T == 0 || !launch) return RGLRU_OK;
 
     ProjGemmArgs g;
     memset(&g, 0, sizeof g);
@@ -517,7 +550,7 @@ int rglru_local_attention_block(const rglru_attn_params* a, int32_t B, int32_t T
     g.M = (int)M; g.K = Dm; g.Nw[0] = (int)HD; g.Nw[1] = kAttnDh; g.Nw[2] = kAttnDh; g.nseg = 3;
     hipError_t e = launch_proj_gemm(g, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e);
-    st = rglru_local_attention(B, T, Hq, a->window, a->rope_base, qb, kb, vb, ob, nullptr, nullptr,
+    st = rglru_local_attention(B, T, Hq, a->window, a->rope_base, qb, kb, vb, ob, kcache, vcache,
                                aw, aw_bytes, stream);
     if (st != RGLRU_OK) return st;
     memset(&g, 0, sizeof g);
@@ -525,6 +558,16 @@ int rglru_local_attention_block(const rglru_attn_params* a, int32_t B, int32_t T
     g.M = (int)M; g.K = (int)HD; g.Nw[0] = Dm; g.nseg = 1;
     e = launch_proj_gemm(g, (hipStream_t)stream);
     return e == hipSuccess ? RGLRU_OK : hip_fail(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int rglru_local_attention_block(const rglru_attn_params* a, int32_t B, int32_t T,
+                                const void* x_in, void* out, void* workspace, size_t ws_bytes,
+                                void* stream) {
+    return attn_block_impl(a, B, T, x_in, out, nullptr, nullptr, workspace, ws_bytes, stream, true);
 }
 
 int rglru_prefill_workspace_flags(void* workspace, size_t ws_bytes, uint32_t* flags_out,
@@ -539,6 +582,253 @@ int rglru_prefill_workspace_flags(void* workspace, size_t ws_bytes, uint32_t* fl
     if (e == hipSuccess) e = hipMemcpyAsync(hdr + 1, &zero, sizeof(uint32_t), hipMemcpyHostToDevice, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     return e == hipSuccess ? RGLRU_OK : hip_fail(e);
+}
+
+// ------------------------------------------------------------------------------------------
+// the residual layer: RMSNorm, MLP, and the two layers
+// ------------------------------------------------------------------------------------------
+int rglru_rmsnorm(int32_t M, int32_t D, const void* x, const void* residual, const void* scale,
+                  float eps, void* h_out, void* out, void* stream) {
+    if (M < 0 || D < 1 || !(eps >= 0.0f) || !(eps < INFINITY)) return RGLRU_ERR_SHAPE;
+    if (D % 8 != 0 || D > 8192 || (size_t)M * D >= ((size_t)1 << 40)) return RGLRU_ERR_UNSUPPORTED;
+    if (M > 0 && (!x || (!h_out && !out) || (out && !scale))) return RGLRU_ERR_NULL;
+    const void* ptrs[] = {x, residual, scale, h_out, out};
+    for (const void* ptr : ptrs)
+        if (!aligned16(ptr)) return RGLRU_ERR_UNSUPPORTED;
+    const size_t n = (size_t)M * D * 2;
+    if (overlap(out, n, x, n) || overlap(out, n, residual, n) || overlap(out, n, scale, D * 2) ||
+        overlap(out, n, h_out, n) || overlap(h_out, n, residual, n) ||
+        overlap(h_out, n, scale, D * 2) || (h_out != x && overlap(h_out, n, x, n)))
+        return RGLRU_ERR_ALIAS;
+    if (M == 0) return RGLRU_OK;
+    NormArgs a;
+    a.x = x; a.y = residual; a.g = scale; a.h = h_out; a.n = out; a.M = M; a.D = D; a.eps = eps;
+    hipError_t e = launch_add_rmsnorm(a, (hipStream_t)stream);
+    return e == hipSuccess ? RGLRU_OK : hip_fail(e);
+}
+
+size_t rglru_mlp_workspace_bytes(int32_t M, int32_t F) {
+    if (M < 0 || F < 1) return 0;
+    return 2 * round256((size_t)M * F * 2);
+}
+
+}  // extern "C"
+
+namespace {
+
+int check_mlp(const rglru_mlp_params* m, int Dm) {
+    if (!m) return RGLRU_ERR_NULL;
+    if (m->D_model != Dm || m->F < 1) return RGLRU_ERR_SHAPE;
+    if (m->F % 256 != 0 || m->F >= (1 << 21) || Dm % 256 != 0 || Dm >= (1 << 21))
+        return RGLRU_ERR_UNSUPPORTED;
+    if (!m->gate_w || !m->up_w || !m->down_w) return RGLRU_ERR_NULL;
+    const void* ptrs[] = {m->gate_w, m->gate_b, m->up_w, m->up_b, m->down_w, m->down_b};
+    for (const void* ptr : ptrs)
+        if (!aligned16(ptr)) return RGLRU_ERR_UNSUPPORTED;
+    return RGLRU_OK;
+}
+
+// the MLP's read-only operands, for overlap checks
+int mlp_operands(const rglru_mlp_params* m, const void** ptrs, size_t* lens) {
+    const size_t w = (size_t)m->F * m->D_model * 2;
+    const void* p[] = {m->gate_w, m->gate_b, m->up_w, m->up_b, m->down_w, m->down_b};
+    const size_t l[] = {w, (size_t)m->F * 2, w, (size_t)m->F * 2, w, (size_t)m->D_model * 2};
+    for (int i = 0; i < 6; ++i) {
+        ptrs[i] = p[i];
+        lens[i] = l[i];
+    }
+    return 6;
+}
+
+int check_norms(const rglru_norm_params* n, int Dm) {
+    if (!n) return RGLRU_ERR_NULL;
+    if (!n->temporal_scale || !n->channel_scale) return RGLRU_ERR_NULL;
+    if (!(n->eps >= 0.0f) || !(n->eps < INFINITY)) return RGLRU_ERR_SHAPE;
+    if (!aligned16(n->temporal_scale) || !aligned16(n->channel_scale) || Dm > 8192)
+        return RGLRU_ERR_UNSUPPORTED;
+    return RGLRU_OK;
+}
+
+hipError_t run_mlp(const rglru_mlp_params* m, int M, const void* x, void* out, void* ws,
+                   hipStream_t s) {
+    const size_t nf = (size_t)M * m->F;
+    void* G = ws;
+    void* U = static_cast<char*>(ws) + round256(nf * 2);
+    ProjGemmArgs g;
+    memset(&g, 0, sizeof g);
+    g.A = x; g.W[0] = m->gate_w; g.W[1] = m->up_w; g.b[0] = m->gate_b; g.b[1] = m->up_b;
+    g.C[0] = G; g.C[1] = U; g.M = M; g.K = m->D_model; g.Nw[0] = m->F; g.Nw[1] = m->F; g.nseg = 2;
+    hipError_t e = launch_proj_gemm(g, s);
+    if (e == hipSuccess) e = launch_geglu(G, U, nf, s);
+    if (e != hipSuccess) return e;
+    memset(&g, 0, sizeof g);
+    g.A = G; g.W[0] = m->down_w; g.b[0] = m->down_b; g.C[0] = out;
+    g.M = M; g.K = m->F; g.Nw[0] = m->D_model; g.nseg = 1;
+    return launch_proj_gemm(g, s);
+}
+
+// Layer workspace after the block's own part: xn / hn, the block output / the MLP output, h,
+// then the MLP's workspace.
+struct LayerBufs {
+    void *a, *b, *h, *mlp;
+};
+LayerBufs layer_bufs(void* workspace, size_t block_bytes, size_t M, int Dm) {
+    const size_t act = round256(M * Dm * 2);
+    char* base = static_cast<char*>(workspace) + round256(block_bytes);
+    return {base, base + act, base + 2 * act, base + 3 * act};
+}
+size_t layer_tail_bytes(size_t M, int Dm, int F) {
+    return 3 * round256(M * Dm * 2) + rglru_mlp_workspace_bytes((int32_t)M, F);
+}
+
+// Launches of the layer after validation: norm 1, the block (through `block`), h and norm 2,
+// the MLP, the final residual addition into out.
+template <class Block>
+int run_layer(const rglru_norm_params* nrm, const rglru_mlp_params* m, size_t M, int Dm,
+              const void* x_in, void* out, const LayerBufs& L, hipStream_t s, Block block) {
+    NormArgs na;
+    na.x = x_in; na.y = nullptr; na.g = nrm->temporal_scale; na.h = nullptr; na.n = L.a;
+    na.M = (int)M; na.D = Dm; na.eps = nrm->eps;
+    hipError_t e = launch_add_rmsnorm(na, s);
+    if (e != hipSuccess) return hip_fail(e);
+    int st = block();
+    if (st != RGLRU_OK) return st;
+    na.x = x_in; na.y = L.b; na.g = nrm->channel_scale; na.h = L.h; na.n = L.a;
+    e = launch_add_rmsnorm(na, s);
+    if (e == hipSuccess) e = run_mlp(m, (int)M, L.a, L.b, L.mlp, s);
+    if (e != hipSuccess) return hip_fail(e);
+    na.x = L.h; na.y = L.b; na.g = nullptr; na.h = out; na.n = nullptr;
+    e = launch_add_rmsnorm(na, s);
+    return e == hipSuccess ? RGLRU_OK : hip_fail(e);
+}
+
+// out and the workspace against everything else the layer reads or writes
+int check_layer_alias(const void* x_in, void* out, size_t n_io, void* ws, size_t need,
+                      const void* const* others, const size_t* olen, int nothers) {
+    if (overlap(out, n_io, x_in, n_io) || overlap(out, n_io, ws, need) ||
+        overlap(ws, need, x_in, n_io))
+        return RGLRU_ERR_ALIAS;
+    for (int i = 0; i < nothers; ++i)
+        if (overlap(out, n_io, others[i], olen[i]) || overlap(ws, need, others[i], olen[i]))
+            return RGLRU_ERR_ALIAS;
+    return RGLRU_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int rglru_mlp(const rglru_mlp_params* m, int32_t M, const void* x, void* out, void* workspace,
+              size_t ws_bytes, void* stream) {
+    if (!m) return RGLRU_ERR_NULL;
+    int st = check_mlp(m, m->D_model);
+    if (st != RGLRU_OK) return st;
+    if (M < 0) return RGLRU_ERR_SHAPE;
+    if (M > 0 && (!x || !out)) return RGLRU_ERR_NULL;
+    if (!aligned16(x) || !aligned16(out) || !aligned16(workspace)) return RGLRU_ERR_UNSUPPORTED;
+    const size_t need = rglru_mlp_workspace_bytes(M, m->F);
+    if (M > 0 && (!workspace || ws_bytes < need)) return RGLRU_ERR_WORKSPACE;
+    const size_t n_io = (size_t)M * m->D_model * 2;
+    const void* w[6];
+    size_t wl[6];
+    mlp_operands(m, w, wl);
+    if (M > 0 && check_layer_alias(x, out, n_io, workspace, need, w, wl, 6) != RGLRU_OK)
+        return RGLRU_ERR_ALIAS;
+    if (M == 0) return RGLRU_OK;
+    hipError_t e = run_mlp(m, M, x, out, workspace, (hipStream_t)stream);
+    return e == hipSuccess ? RGLRU_OK : hip_fail(e);
+}
+
+size_t rglru_recurrent_layer_workspace_bytes(int32_t B, int32_t T, int32_t D, int32_t n_heads,
+                                             int32_t D_model, int32_t F) {
+    const size_t bw = rglru_block_prefill_workspace_bytes(B, T, D, n_heads, D_model, RGLRU_BF16);
+    if (bw == 0 || F < 1) return 0;
+    return round256(bw) + layer_tail_bytes((size_t)B * T, D_model, F);
+}
+
+int rglru_recurrent_layer_prefill(const rglru_params* p, const rglru_proj_params* q,
+                                  const rglru_norm_params* nrm, const rglru_mlp_params* m,
+                                  int32_t B, int32_t T, const void* x_in, void* out,
+                                  const float* h0, float* h_last, const void* conv0,
+                                  void* conv_last, void* workspace, size_t ws_bytes,
+                                  void* stream) {
+    if (!p || !q) return RGLRU_ERR_NULL;
+    const int Dm = q->D_model;
+    int st = check_norms(nrm, Dm);
+    if (st == RGLRU_OK) st = check_mlp(m, Dm);
+    if (st != RGLRU_OK) return st;
+    if (B < 1 || T < 0) return RGLRU_ERR_SHAPE;
+    if (T > 0 && (!x_in || !out)) return RGLRU_ERR_NULL;
+    if (!aligned16(x_in) || !aligned16(out) || !aligned16(workspace)) return RGLRU_ERR_UNSUPPORTED;
+    const size_t M = (size_t)B * T;
+    const size_t bw = rglru_block_prefill_workspace_bytes(B, T, p->D, p->n_heads, Dm, RGLRU_BF16);
+    const size_t need = rglru_recurrent_layer_workspace_bytes(B, T, p->D, p->n_heads, Dm, m->F);
+    if (T > 0 && (bw == 0 || need == 0)) return RGLRU_ERR_SHAPE;
+    if (T > 0 && (!workspace || ws_bytes < need)) return RGLRU_ERR_WORKSPACE;
+    const LayerBufs L = layer_bufs(workspace, bw, M, Dm);
+    // the block's own checks on the buffers the layer hands it (nothing is launched yet)
+    st = block_prefill_impl(p, q, B, T, T > 0 ? L.a : nullptr, T > 0 ? L.b : nullptr, h0, h_last,
+                            conv0, conv_last, T > 0 ? workspace : nullptr, T > 0 ? bw : 0, stream,
+                            false);
+    if (st != RGLRU_OK) return st;
+    if (T == 0)   // state pass-through only
+        return block_prefill_impl(p, q, B, 0, nullptr, nullptr, h0, h_last, conv0, conv_last,
+                                  nullptr, 0, stream, true);
+    const size_t n_io = M * Dm * 2, n_h = (size_t)B * p->D * 4, n_c = (size_t)B * 3 * p->D * 2;
+    const size_t pw = (size_t)p->D * Dm * 2;
+    const void* others[16] = {h0, h_last, conv0, conv_last, nrm->temporal_scale,
+                              nrm->channel_scale, q->lin_x_w, q->lin_y_w, q->lin_out_w};
+    size_t olen[16] = {n_h, n_h, n_c, n_c, (size_t)Dm * 2, (size_t)Dm * 2, pw, pw, pw};
+    const int n = 9 + mlp_operands(m, others + 9, olen + 9);
+    if (check_layer_alias(x_in, out, n_io, workspace, need, others, olen, n) != RGLRU_OK)
+        return RGLRU_ERR_ALIAS;
+    return run_layer(nrm, m, M, Dm, x_in, out, L, (hipStream_t)stream, [&]() {
+        return block_prefill_impl(p, q, B, T, L.a, L.b, h0, h_last, conv0, conv_last, workspace,
+                                  bw, stream, true);
+    });
+}
+
+size_t rglru_attention_layer_workspace_bytes(const rglru_attn_params* a, int32_t B, int32_t T,
+                                             int32_t F) {
+    const size_t bw = rglru_local_attention_block_workspace_bytes(a, B, T);
+    if (bw == 0 || F < 1) return 0;
+    return round256(bw) + layer_tail_bytes((size_t)B * T, a->D_model, F);
+}
+
+int rglru_attention_layer_prefill(const rglru_attn_params* a, const rglru_norm_params* nrm,
+                                  const rglru_mlp_params* m, int32_t B, int32_t T,
+                                  const void* x_in, void* out, void* kcache, void* vcache,
+                                  void* workspace, size_t ws_bytes, void* stream) {
+    if (!a) return RGLRU_ERR_NULL;
+    const int Dm = a->D_model;
+    int st = check_norms(nrm, Dm);
+    if (st == RGLRU_OK) st = check_mlp(m, Dm);
+    if (st != RGLRU_OK) return st;
+    if (B < 1 || T < 0 || a->n_heads < 1) return RGLRU_ERR_SHAPE;
+    if (T > 0 && (!x_in || !out)) return RGLRU_ERR_NULL;
+    if (!aligned16(x_in) || !aligned16(out) || !aligned16(workspace)) return RGLRU_ERR_UNSUPPORTED;
+    const size_t M = (size_t)B * T;
+    const size_t bw = rglru_local_attention_block_workspace_bytes(a, B, T);
+    const size_t need = rglru_attention_layer_workspace_bytes(a, B, T, m->F);
+    if (T > 0 && (bw == 0 || need == 0)) return RGLRU_ERR_SHAPE;
+    if (T > 0 && (!workspace || ws_bytes < need)) return RGLRU_ERR_WORKSPACE;
+    const LayerBufs L = layer_bufs(workspace, bw, M, Dm);
+    st = attn_block_impl(a, B, T, T > 0 ? L.a : nullptr, T > 0 ? L.b : nullptr, kcache, vcache,
+                         T > 0 ? workspace : nullptr, T > 0 ? bw : 0, stream, false);
+    if (st != RGLRU_OK || T == 0) return st;
+    const size_t n_io = M * Dm * 2, HD = (size_t)a->n_heads * kAttnDh;
+    const size_t nc = kcache ? rglru_local_attention_cache_bytes(B, a->window) : 0;
+    const void* others[16] = {kcache, vcache, nrm->temporal_scale, nrm->channel_scale, a->q_w,
+                              a->k_w, a->v_w, a->o_w, a->o_b};
+    size_t olen[16] = {nc, nc, (size_t)Dm * 2, (size_t)Dm * 2, HD * Dm * 2,
+                       (size_t)kAttnDh * Dm * 2, (size_t)kAttnDh * Dm * 2, HD * Dm * 2,
+                       (size_t)Dm * 2};
+    const int n = 9 + mlp_operands(m, others + 9, olen + 9);
+    if (check_layer_alias(x_in, out, n_io, workspace, need, others, olen, n) != RGLRU_OK)
+        return RGLRU_ERR_ALIAS;
+    return run_layer(nrm, m, M, Dm, x_in, out, L, (hipStream_t)stream, [&]() {
+        return attn_block_impl(a, B, T, L.a, L.b, kcache, vcache, workspace, bw, stream, true);
+    });
 }
 
 }  // extern "C"

@@ -119,6 +119,19 @@ hipError_t launch_conv_update(const ConvArgs& a, int dtype, hipStream_t s);
 hipError_t launch_proj_gemm(const ProjGemmArgs& a, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attention_decode(const AttnDecodeArgs& a, hipStream_t s);
+
+// Residual-layer elementwise steps (bf16): h = x (+ y) and n = RMSNorm(h) * g over rows of D.
+struct NormArgs {
+    const void* x;       // [M][D]
+    const void* y;       // [M][D] or NULL
+    const void* g;       // [D] (needed when n is given)
+    void* h;             // [M][D] or NULL: x + y rounded to bf16
+    void* n;             // [M][D] or NULL
+    int M, D;            // D % 8 == 0, D <= 8192
+    float eps;
+};
+hipError_t launch_add_rmsnorm(const NormArgs& a, hipStream_t s);
+hipError_t launch_geglu(void* gate, const void* up, size_t n, hipStream_t s);  // n % 8 == 0
 constexpr int kAttnDecSlotsPerSplit = 512;  // cache slots per decode workgroup
 
 }  // namespace rglru

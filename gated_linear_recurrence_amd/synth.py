@@ -34,7 +34,13 @@ _TID = {"lambda": 0, "wa": 1, "wx": 2, "ba": 3, "bx": 4, "conv_w": 5, "conv_b": 
         # the block's dense projections and its input (x_in feeds linear_x and linear_y)
         "lx_w": 10, "lx_b": 11, "ly_w": 12, "ly_b": 13, "lo_w": 14, "lo_b": 15, "x_in": 16,
         # the local-attention block's projections and the attention's own inputs
-        "q_w": 17, "k_w": 18, "v_w": 19, "o_w": 20, "o_b": 21, "q": 22, "k": 23, "v": 24}
+        "q_w": 17, "k_w": 18, "v_w": 19, "o_w": 20, "o_b": 21, "q": 22, "k": 23, "v": 24,
+        # the residual layer: the two norm scales and the MLP
+        "norm_t": 25, "norm_c": 26, "gate_w": 27, "gate_b": 28, "up_w": 29, "up_b": 30,
+        "down_w": 31, "down_b": 32}
+
+MLP_EXPANSION = 3      # MLP width = 3 x model width (7680 at width 2560)
+NORM_EPS = 1e-6
 
 # local attention of the 2B model: 10 query heads of width 256 sharing one key/value head,
 # a window of 2048 tokens, RoPE base 10000
@@ -246,3 +252,26 @@ def make_qkv(w: Workload, n_heads: int = ATTN_HEADS_2B, B: int | None = None,
                 out[b, t0:t0 + n] = to_storage(a[:n], w.dtype)
         res.append(out)
     return tuple(res)
+
+
+def make_layer(w: Workload, Dm: int | None = None, F: int | None = None, biases: bool = False,
+               seed: int | None = None) -> dict:
+    """The residual layer's own weights in storage form: the two RMSNorm scales
+    (temporal_scale, channel_scale) ~ 1 + N(0, 0.1); the MLP's gate_w, up_w [F, Dm] ~
+    N(0, 1/sqrt(Dm)) and down_w [Dm, F] ~ N(0, 1/sqrt(F)); biases zero, or N(0, 0.1)."""
+    s0 = w.seed if seed is None else seed
+    Dm = w.D if Dm is None else Dm
+    F = MLP_EXPANSION * Dm if F is None else F
+    out = {}
+    for name in ("norm_t", "norm_c"):
+        a = 1.0 + _rng(s0, _TID[name]).standard_normal(Dm, dtype=np.float32) * np.float32(0.1)
+        out[name] = to_storage(a, w.dtype)
+    for name, shape, fan_in in (("gate_w", (F, Dm), Dm), ("up_w", (F, Dm), Dm),
+                                ("down_w", (Dm, F), F)):
+        a = _rng(s0, _TID[name]).standard_normal(shape, dtype=np.float32)
+        out[name] = to_storage(a * np.float32(1.0 / math.sqrt(fan_in)), w.dtype)
+    for name, n in (("gate_b", F), ("up_b", F), ("down_b", Dm)):
+        a = (_rng(s0, _TID[name]).standard_normal(n, dtype=np.float32) * np.float32(0.1)
+             if biases else np.zeros(n, np.float32))
+        out[name] = to_storage(a, w.dtype)
+    return out

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define RGLRU_ABI_VERSION 4
+#define RGLRU_ABI_VERSION 5
 
 enum rglru_dtype { RGLRU_F32 = 0, RGLRU_BF16 = 1 };
 
@@ -317,6 +317,80 @@ size_t rglru_local_attention_block_workspace_bytes(const rglru_attn_params *a, i
 int rglru_local_attention_block(const rglru_attn_params *a, int32_t B, int32_t T,
                                 const void *x_in, void *out, void *workspace, size_t ws_bytes,
                                 void *stream);
+
+/*
+ * The residual layer around a temporal-mixing block.  Operation: the page "Gemma 詳解：
+ * RecurrentGemma 架構" (module printout; sections "含遞迴區塊的殘差區塊" and "含區域 MQA 的殘差
+ * 區塊") wraps each block in a pre-norm residual layer with an MLP:
+ *   h   = x + temporal(RMSNorm_1(x))
+ *   out = h + down_proj(gelu_tanh(gate_proj(RMSNorm_2(h))) * up_proj(RMSNorm_2(h)))
+ *   RMSNorm(v) = v / sqrt(mean(v^2) + eps) * scale   (per row of D_model, fp32 arithmetic)
+ * scale is the per-channel multiplier itself (a model that stores w with multiplier 1 + w passes
+ * 1 + w).  bf16 storage only; like a bf16 model, every step's result is rounded to bf16 (RNE):
+ * the normalised rows, the block output, h, the MLP's gate, up and their product, its output.
+ */
+typedef struct rglru_norm_params {
+    const void *temporal_scale; /* [D_model], before the temporal block */
+    const void *channel_scale;  /* [D_model], before the MLP */
+    float eps;
+} rglru_norm_params;
+
+/* The MLP: gate_w, up_w [F][D_model], down_w [D_model][F] ([out][in]); biases [F], [F],
+ * [D_model] or NULL.  D_model % 256 == 0 and F % 256 == 0 (below 2^21), else
+ * RGLRU_ERR_UNSUPPORTED. */
+typedef struct rglru_mlp_params {
+    int32_t D_model;
+    int32_t F;
+    const void *gate_w;
+    const void *gate_b;
+    const void *up_w;
+    const void *up_b;
+    const void *down_w;
+    const void *down_b;
+} rglru_mlp_params;
+
+/*
+ * RMSNorm with an optional residual addition, over M rows of D (bf16):
+ *   h = x + residual (x alone when residual is NULL), rounded to bf16, written to h_out if given;
+ *   out = RMSNorm(h) * scale, written if out is given (scale is then required).
+ * M >= 0, D % 8 == 0 and D <= 8192 (else RGLRU_ERR_UNSUPPORTED), eps >= 0.  h_out and out must
+ * not overlap each other or the inputs, except that h_out may be x itself (in-place add).
+ */
+int rglru_rmsnorm(int32_t M, int32_t D, const void *x, const void *residual, const void *scale,
+                  float eps, void *h_out, void *out, void *stream);
+
+/* The MLP alone over M rows: out [M][D_model] = down(gelu_tanh(gate(x)) * up(x)), x [M][D_model].
+ * workspace: at least rglru_mlp_workspace_bytes(M, F) (gate and up outputs, [2][M][F] bf16). */
+size_t rglru_mlp_workspace_bytes(int32_t M, int32_t F);
+int rglru_mlp(const rglru_mlp_params *m, int32_t M, const void *x, void *out, void *workspace,
+              size_t ws_bytes, void *stream);
+
+/*
+ * The residual layer around the recurrent block (prefill over T tokens): temporal is
+ * rglru_block_prefill's operation (with its state arguments, as there).  x_in, out
+ * [B][T][D_model].  The workspace starts with the recurrent block's own workspace: initialise it
+ * once with rglru_prefill_workspace_init(workspace, ws_bytes).  out must not overlap x_in.
+ */
+size_t rglru_recurrent_layer_workspace_bytes(int32_t B, int32_t T, int32_t D, int32_t n_heads,
+                                             int32_t D_model, int32_t F);
+int rglru_recurrent_layer_prefill(const rglru_params *p, const rglru_proj_params *q,
+                                  const rglru_norm_params *nrm, const rglru_mlp_params *m,
+                                  int32_t B, int32_t T, const void *x_in, void *out,
+                                  const float *h0, float *h_last, const void *conv0,
+                                  void *conv_last, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * The residual layer around the local-attention block (prefill over T tokens): temporal is
+ * rglru_local_attention_block's operation; kcache, vcache (optional, as in
+ * rglru_local_attention) receive the last window positions for decoding.  out must not overlap
+ * x_in.  No initialisation of the workspace is needed.
+ */
+size_t rglru_attention_layer_workspace_bytes(const rglru_attn_params *a, int32_t B, int32_t T,
+                                             int32_t F);
+int rglru_attention_layer_prefill(const rglru_attn_params *a, const rglru_norm_params *nrm,
+                                  const rglru_mlp_params *m, int32_t B, int32_t T,
+                                  const void *x_in, void *out, void *kcache, void *vcache,
+                                  void *workspace, size_t ws_bytes, void *stream);
 
 /*
  * Diagnostics of a prefill workspace: copies its error flags to *flags_out (0 = none) and

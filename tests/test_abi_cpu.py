@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.rglru_abi_version() == 4
+    assert lib.rglru_abi_version() == 5
     for st in range(7):
         assert lib.rglru_status_string(st)
     assert lib.rglru_status_string(99) == b"unknown status"
@@ -348,3 +348,103 @@ def test_attention_block_validation(lib):
     a = _attn_params()
     assert _attn_block(lib, a, out=a.o_w) == ALIAS                      # out overlaps o_w
     assert _attn_block(lib, a, ws=a.q_w) == ALIAS                       # workspace overlaps q_w
+
+
+# ------------------------------------------------------------------------------------------
+# the residual layer (every call fails validation or has no rows, so nothing is launched)
+# ------------------------------------------------------------------------------------------
+NX, NR, NS, NH, NO = (0x2000000000 + k * 0x100000000 for k in range(5))
+
+
+def test_rmsnorm_validation(lib):
+    f = lib.rglru_rmsnorm
+    assert f(-1, 2560, NX, None, NS, 1e-6, None, NO, None) == SHAPE
+    assert f(10, 2560, NX, None, NS, -1.0, None, NO, None) == SHAPE
+    assert f(10, 2564, NX, None, NS, 1e-6, None, NO, None) == UNSUP      # D % 8
+    assert f(10, 8200, NX, None, NS, 1e-6, None, NO, None) == UNSUP      # D > 8192
+    assert f(10, 2560, None, None, NS, 1e-6, None, NO, None) == NULL
+    assert f(10, 2560, NX, None, NS, 1e-6, None, None, None) == NULL     # nothing to write
+    assert f(10, 2560, NX, None, None, 1e-6, None, NO, None) == NULL     # norm without scale
+    assert f(10, 2560, NX + 8, None, NS, 1e-6, None, NO, None) == UNSUP
+    assert f(10, 2560, NX, None, NS, 1e-6, None, NX + 512, None) == ALIAS
+    assert f(10, 2560, NX, NR, NS, 1e-6, NR, NO, None) == ALIAS          # h over the residual
+    assert f(10, 2560, NX, NR, NS, 1e-6, NH, NH + 1024, None) == ALIAS   # out over h
+    assert f(0, 2560, None, None, None, 1e-6, None, None, None) == OK
+
+
+def _mlp(Dm=512, F=768, b=True):
+    m = binding.rglru_mlp_params()
+    m.D_model, m.F = Dm, F
+    m.gate_w, m.up_w, m.down_w = (0x3000000000 + k * 0x10000000 for k in range(3))
+    if b:
+        m.gate_b, m.up_b, m.down_b = (0x3000000000 + k * 0x10000000 for k in range(3, 6))
+    return m
+
+
+def test_mlp_workspace_and_validation(lib):
+    assert lib.rglru_mlp_workspace_bytes(300, 768) == 2 * 300 * 768 * 2
+    assert lib.rglru_mlp_workspace_bytes(1, 256) == 2 * 512
+    assert lib.rglru_mlp_workspace_bytes(-1, 256) == 0 and lib.rglru_mlp_workspace_bytes(5, 0) == 0
+    ws = lib.rglru_mlp_workspace_bytes(300, 768)
+    f = lambda m, M=300, x=NX, o=NO, w=NH, n=ws: lib.rglru_mlp(ctypes.byref(m), M, x, o, w, n, None)
+    assert lib.rglru_mlp(None, 1, NX, NO, NH, ws, None) == NULL
+    assert f(_mlp(Dm=384)) == UNSUP and f(_mlp(F=700)) == UNSUP
+    m = _mlp()
+    m.up_w = None
+    assert f(m) == NULL
+    assert f(_mlp(), M=-1) == SHAPE
+    assert f(_mlp(), x=None) == NULL
+    assert f(_mlp(), n=ws - 1) == WS
+    assert f(_mlp(), o=NX + 256) == ALIAS                    # out over x
+    assert f(_mlp(), w=0x3000000000) == ALIAS                # workspace over gate_w
+    assert f(_mlp(), M=0, x=None, o=None, w=None, n=0) == OK
+
+
+def _norms(eps=1e-6):
+    n = binding.rglru_norm_params()
+    n.temporal_scale, n.channel_scale, n.eps = 0x3800000000, 0x3800010000, eps
+    return n
+
+
+def test_layer_workspace_bytes(lib):
+    B, T, D, H, Dm, F = 2, 100, 512, 2, 512, 768
+    act = 2 * 100 * 512 * 2
+    bw = lib.rglru_block_prefill_workspace_bytes(B, T, D, H, Dm, 1)
+    r256 = lambda v: (v + 255) // 256 * 256
+    assert lib.rglru_recurrent_layer_workspace_bytes(B, T, D, H, Dm, F) == \
+        r256(bw) + 3 * r256(act) + lib.rglru_mlp_workspace_bytes(B * T, F)
+    a = _attn_params(Dm=512, Hq=2)
+    aw = lib.rglru_local_attention_block_workspace_bytes(ctypes.byref(a), B, T)
+    assert lib.rglru_attention_layer_workspace_bytes(ctypes.byref(a), B, T, F) == \
+        r256(aw) + 3 * r256(act) + lib.rglru_mlp_workspace_bytes(B * T, F)
+    assert lib.rglru_recurrent_layer_workspace_bytes(B, T, D, H, Dm, 0) == 0
+
+
+def test_layer_validation(lib):
+    p = _params(D=512, H=2, dtype=1)
+    q = _proj(Dm=512)
+    a = _attn_params(Dm=512, Hq=2)
+    m, n = _mlp(Dm=512), _norms()
+    B, T = 2, 100
+    ws = lib.rglru_attention_layer_workspace_bytes(ctypes.byref(a), B, T, 768)
+    fa = lambda a=a, n=n, m=m, T=T, x=NX, o=NO, w=0x4000000000, nb=ws: \
+        lib.rglru_attention_layer_prefill(ctypes.byref(a), n if n is None else ctypes.byref(n),
+                                          ctypes.byref(m), B, T, x, o, None, None, w, nb, None)
+    assert fa(n=None) == NULL
+    assert fa(n=_norms(eps=-1.0)) == SHAPE
+    assert fa(m=_mlp(Dm=768)) == SHAPE                        # MLP width != D_model
+    assert fa(m=_mlp(Dm=512, F=700)) == UNSUP
+    assert fa(x=None) == NULL
+    assert fa(nb=ws - 1) == WS
+    assert fa(o=NX + 1024) == ALIAS                           # out over x_in
+    assert fa(w=0x3000000000) == ALIAS                        # workspace over the MLP weights
+    assert fa(a=_attn_params(Dm=512, Hq=2, dh=128)) == UNSUP  # the block's own checks
+    assert fa(T=0, x=None, o=None, w=None, nb=0) == OK
+    if q is not None:
+        wr = lib.rglru_recurrent_layer_workspace_bytes(B, T, 512, 2, 512, 768)
+        fr = lambda n=n, x=NX, o=NO, nb=wr: lib.rglru_recurrent_layer_prefill(
+            ctypes.byref(p), ctypes.byref(q), ctypes.byref(n), ctypes.byref(m), B, T, x, o,
+            None, None, None, None, 0x4000000000, nb, None)
+        assert fr(n=_norms(eps=float("nan"))) == SHAPE
+        assert fr(nb=wr - 1) == WS
+        assert fr(o=NX) == ALIAS

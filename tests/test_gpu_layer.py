@@ -1,0 +1,234 @@
+"""GPU parity of the residual layer (RMSNorm, gated MLP, both layers) through the C ABI against
+the fp64 oracle.
+
+Bars: the layer rounds each step's result to bf16 as a bf16 model does (normalised rows, block
+output, h, the MLP's gate, up, their product and its output) while the oracle keeps fp64, so
+outputs meet the bf16 bar, rel-L2 <= 2e-2; every row of an RMSNorm is also held to 2e-2, and
+h = x + residual to one bf16 rounding (2^-8 relative) of the exact sum.  Full-size layers are checked on time
+prefixes of sampled sequences (both layers are causal and their sequences independent).
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import pytest
+
+import helpers as H
+from gated_linear_recurrence_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from gated_linear_recurrence_amd import binding
+    binding.load_library()
+
+
+def _bf(a):
+    return synth.round_bf16(np.asarray(a, np.float32))
+
+
+@pytest.mark.parametrize("M,D,residual", [
+    (37, 2560, True),     # the 2B width, with the residual addition
+    (5, 8, False),        # one chunk per row, most lanes idle
+    (64, 8192, True),     # the widest row
+    (300, 512, False),
+])
+def test_rmsnorm_matches_oracle(M, D, residual):
+    from gated_linear_recurrence_amd import binding
+    rng = np.random.default_rng(M + D)
+    x = _bf(rng.standard_normal((M, D)) * 2)
+    r = _bf(rng.standard_normal((M, D))) if residual else None
+    g = _bf(1 + 0.1 * rng.standard_normal(D))
+    out, h = binding.rglru_rmsnorm(H.to_dev(x), H.to_dev(g), H.to_dev(r), 1e-6, want_h=True)
+    torch.cuda.synchronize()
+    exact = H.wide(x) + (H.wide(r) if residual else 0.0)
+    hg = H.wide(H.to_host(h))
+    assert np.all(np.abs(hg - exact) <= 2.0 ** -8 * np.abs(exact) + 1e-30)
+    ref = H.oracle.rmsnorm(exact, g, 1e-6)
+    got = H.wide(H.to_host(out))
+    e = H.rel_l2(got, ref)
+    rows = np.linalg.norm(got - ref, axis=1) / np.linalg.norm(ref, axis=1)
+    print("rmsnorm M=%d D=%d: rel-L2 %.3e, worst row %.3e" % (M, D, e, rows.max()))
+    assert e <= H.TOL[synth.BF16] and rows.max() <= H.TOL[synth.BF16]
+
+
+def test_rmsnorm_in_place_add_and_empty():
+    """h_out may be x itself (in-place residual addition); M = 0 launches nothing."""
+    from gated_linear_recurrence_amd import binding
+    rng = np.random.default_rng(2)
+    x = _bf(rng.standard_normal((20, 256)))
+    r = _bf(rng.standard_normal((20, 256)))
+    xd = H.to_dev(x)
+    binding.rglru_rmsnorm(xd, None, H.to_dev(r), want_norm=False, h_out=xd)
+    e = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    binding.rglru_rmsnorm(e, torch.ones(256, dtype=torch.bfloat16, device="cuda"))
+    torch.cuda.synchronize()
+    exact = H.wide(x) + H.wide(r)
+    assert np.all(np.abs(H.wide(H.to_host(xd)) - exact) <= 2.0 ** -8 * np.abs(exact) + 1e-30)
+
+
+def _mlp_dev(L):
+    from gated_linear_recurrence_amd import binding
+    return binding.MlpParams(*[H.to_dev(L[k]) for k in ("gate_w", "gate_b", "up_w", "up_b",
+                                                       "down_w", "down_b")])
+
+
+def _mlp_oracle(L):
+    return H.oracle.MlpParams(L["gate_w"], L["gate_b"], L["up_w"], L["up_b"], L["down_w"],
+                              L["down_b"])
+
+
+@pytest.mark.parametrize("M,Dm,F,biases", [
+    (300, 512, 768, True),     # ragged rows
+    (130, 2560, 7680, False),  # the 2B widths
+])
+def test_mlp_matches_oracle(M, Dm, F, biases):
+    from gated_linear_recurrence_amd import binding
+    w = synth.small(synth.WORKLOADS[synth.PREFILL_2B], B=1, T=M)
+    L = synth.make_layer(w, Dm=Dm, F=F, biases=biases)
+    x = synth.make_block_input(w, Dm=Dm, B=1, T=M)[0]
+    out = binding.rglru_mlp(_mlp_dev(L), H.to_dev(x))
+    torch.cuda.synchronize()
+    ref = H.oracle.mlp(_mlp_oracle(L), x)
+    e = H.rel_l2(H.wide(H.to_host(out)), ref)
+    print("mlp M=%d Dm=%d F=%d: rel-L2 %.3e" % (M, Dm, F, e))
+    assert e <= H.TOL[synth.BF16]
+
+
+# ------------------------------------------------------------------------------------------
+# the two layers
+# ------------------------------------------------------------------------------------------
+def _norms_dev(L):
+    from gated_linear_recurrence_amd import binding
+    return binding.NormParams(H.to_dev(L["norm_t"]), H.to_dev(L["norm_c"]), synth.NORM_EPS)
+
+
+def _run_recurrent_layer(w, p, q, L, x_in, h0, c0):
+    from gated_linear_recurrence_amd import binding
+    P = H.dev_params(p, w.H)
+    Q = binding.ProjParams(*[H.to_dev(q[k]) for k in ("lx_w", "lx_b", "ly_w", "ly_b",
+                                                      "lo_w", "lo_b")])
+    out, hl, cl = binding.rglru_recurrent_layer_prefill(P, Q, _norms_dev(L), _mlp_dev(L),
+                                                        H.to_dev(x_in), H.to_dev(h0), H.to_dev(c0))
+    torch.cuda.synchronize()
+    return out, hl, cl
+
+
+def _oracle_recurrent_layer(w, p, q, L, x_in, h0, c0):
+    Po = H.oracle_params(p, w.H)
+    Qo = H.oracle.ProjParams(q["lx_w"], q["lx_b"], q["ly_w"], q["ly_b"], q["lo_w"], q["lo_b"])
+    state = {}
+
+    def temporal(xn):
+        o, state["h"], state["c"] = H.oracle.block_prefill(Po, Qo, xn, h0=h0, conv0=c0)
+        return o
+
+    out, _ = H.oracle.residual_layer(x_in, temporal, L["norm_t"], L["norm_c"], _mlp_oracle(L),
+                                     synth.NORM_EPS)
+    return out, state["h"], state["c"]
+
+
+@pytest.mark.parametrize("D,nh,Dm,F,B,T,biases,state", [
+    (512, 2, 512, 768, 2, 150, True, 3),       # ragged rows (M = 300), with state
+    (2560, 10, 2560, 7680, 1, 96, False, None),  # the 2B widths
+])
+def test_recurrent_layer_matches_oracle(D, nh, Dm, F, B, T, biases, state):
+    w = dataclasses.replace(synth.small(synth.WORKLOADS[synth.PREFILL_2B], B=B, T=T), D=D, H=nh)
+    p = synth.make_params(w, biases=biases)
+    q = synth.make_proj(w, Dm=Dm, biases=biases)
+    L = synth.make_layer(w, Dm=Dm, F=F, biases=biases)
+    x_in = synth.make_block_input(w, Dm=Dm, B=B, T=T)
+    h0 = c0 = None
+    if state is not None:
+        h0 = np.random.default_rng(state).normal(0, 0.3, (B, D)).astype(np.float32)
+        c0 = synth.make_conv0(w, B)
+    out, hl, cl = _run_recurrent_layer(w, p, q, L, x_in, h0, c0)
+    ro, rh, rc = _oracle_recurrent_layer(w, p, q, L, x_in, h0, c0)
+    e = H.rel_l2(H.wide(H.to_host(out)), ro)
+    eh = H.rel_l2(H.to_host(hl).astype(np.float64), rh)
+    ec = H.rel_l2(H.wide(H.to_host(cl)), rc)
+    print("recurrent layer D=%d Dm=%d F=%d B=%d T=%d: rel-L2 out %.3e h_last %.3e conv %.3e"
+          % (D, Dm, F, B, T, e, eh, ec))
+    assert max(e, eh, ec) <= H.TOL[synth.BF16]
+
+
+def _run_attention_layer(a, L, x_in, Hq, W, cache=None):
+    from gated_linear_recurrence_amd import binding
+    A = binding.AttnParams(H.to_dev(a["q_w"]), H.to_dev(a["k_w"]), H.to_dev(a["v_w"]),
+                           H.to_dev(a["o_w"]), H.to_dev(a["o_b"]), Hq, W)
+    out = binding.rglru_attention_layer_prefill(A, _norms_dev(L), _mlp_dev(L), H.to_dev(x_in),
+                                                cache=cache)
+    torch.cuda.synchronize()
+    return out
+
+
+def _oracle_attention_layer(a, L, x_in, Hq, W):
+    out, _ = H.oracle.residual_layer(
+        x_in, lambda xn: H.oracle.local_attention_block(xn, a["q_w"], a["k_w"], a["v_w"],
+                                                        a["o_w"], a["o_b"], Hq, W,
+                                                        synth.ROPE_BASE),
+        L["norm_t"], L["norm_c"], _mlp_oracle(L), synth.NORM_EPS)
+    return out
+
+
+@pytest.mark.parametrize("Dm,Hq,F,B,T,W,biases", [
+    (512, 2, 512, 2, 200, 64, True),          # ragged rows, window edges
+    (2560, 10, 7680, 1, 130, 2048, False),    # the 2B widths and window
+])
+def test_attention_layer_matches_oracle(Dm, Hq, F, B, T, W, biases):
+    w = synth.small(synth.WORKLOADS[synth.PREFILL_2B], B=B, T=T)
+    a = synth.make_attn(w, Dm=Dm, n_heads=Hq, bias=biases)
+    L = synth.make_layer(w, Dm=Dm, F=F, biases=biases)
+    x_in = synth.make_block_input(w, Dm=Dm, B=B, T=T)
+    out = _run_attention_layer(a, L, x_in, Hq, W)
+    ref = _oracle_attention_layer(a, L, x_in, Hq, W)
+    e = H.rel_l2(H.wide(H.to_host(out)), ref)
+    print("attention layer Dm=%d Hq=%d F=%d B=%d T=%d W=%d: rel-L2 %.3e" % (Dm, Hq, F, B, T, W, e))
+    assert e <= H.TOL[synth.BF16]
+
+
+def test_layers_empty_sequence():
+    from gated_linear_recurrence_amd import binding
+    w = dataclasses.replace(synth.small(synth.WORKLOADS[synth.PREFILL_2B], B=2, T=0), D=512, H=2)
+    p, q = synth.make_params(w), synth.make_proj(w, Dm=256)
+    L = synth.make_layer(w, Dm=256, F=512)
+    h0 = np.random.default_rng(1).normal(0, 0.3, (2, 512)).astype(np.float32)
+    out, hl, _ = _run_recurrent_layer(w, p, q, L, np.zeros((2, 0, 256), np.uint16), h0, None)
+    assert tuple(out.shape) == (2, 0, 256)
+    np.testing.assert_array_equal(H.to_host(hl), h0)
+    a = synth.make_attn(w, Dm=256, n_heads=1)
+    out = _run_attention_layer(a, L, np.zeros((2, 0, 256), np.uint16), 1, 64)
+    assert tuple(out.shape) == (2, 0, 256)
+    del binding
+
+
+def test_layers_2b_batched_full_size_sampled():
+    """Both layers at the batched 2B size (8 x 8192 tokens, width 2560, MLP 7680); the oracle
+    checks the first 96 tokens of two sequences."""
+    w = synth.WORKLOADS[synth.BATCHED_2B]
+    x_in = synth.make_block_input(w)
+    L = synth.make_layer(w)
+    p, q = synth.make_params(w), synth.make_proj(w)
+    h0 = synth.make_h0(w)
+    out, _, _ = _run_recurrent_layer(w, p, q, L, x_in, h0, None)
+    a = synth.make_attn(w)
+    out_a = _run_attention_layer(a, L, x_in, synth.ATTN_HEADS_2B, synth.ATTN_WINDOW)
+    t_use = 96
+    for b in (0, w.B - 1):
+        ro, _, _ = _oracle_recurrent_layer(synth.small(w, B=1, T=t_use), p, q, L,
+                                           x_in[b:b + 1, :t_use], h0[b:b + 1], None)
+        e = H.rel_l2(H.wide(H.to_host(out[b:b + 1, :t_use])), ro)
+        ra = _oracle_attention_layer(a, L, x_in[b:b + 1, :t_use], synth.ATTN_HEADS_2B,
+                                     synth.ATTN_WINDOW)
+        ea = H.rel_l2(H.wide(H.to_host(out_a[b:b + 1, :t_use])), ra)
+        print("layers full size, sequence %d, first %d tokens: recurrent %.3e, attention %.3e"
+              % (b, t_use, e, ea))
+        assert e <= H.TOL[synth.BF16] and ea <= H.TOL[synth.BF16]
+    assert bool(torch.isfinite(out.float()).all()) and bool(torch.isfinite(out_a.float()).all())
