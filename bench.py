@@ -363,6 +363,195 @@ def time_attention(w, steps, warmup, torch, binding):
                 "window as a boolean mask, for context"}
 
 
+STACK_LAYERS = 26   # layers 0-1 recurrent, 2 attention, and so on (two recurrent to one attention)
+
+
+def _dev_randn(torch, g, shape, std):
+    return (torch.randn(shape, generator=g, device="cuda") * std).to(torch.bfloat16)
+
+
+def _stack_weights(torch, binding, w, g):
+    """Seeded random weights of one layer of each kind at the 2B widths, on the device."""
+    D, Dm, F, Hq = w.D, w.D, synth.MLP_EXPANSION * w.D, synth.ATTN_HEADS_2B
+    HD = Hq * synth.ATTN_HEAD_DIM
+
+    def norms():
+        return binding.NormParams(1 + _dev_randn(torch, g, (Dm,), 0.1),
+                                  1 + _dev_randn(torch, g, (Dm,), 0.1), synth.NORM_EPS)
+
+    def mlp():
+        return binding.MlpParams(_dev_randn(torch, g, (F, Dm), Dm ** -0.5), None,
+                                 _dev_randn(torch, g, (F, Dm), Dm ** -0.5), None,
+                                 _dev_randn(torch, g, (Dm, F), F ** -0.5), None)
+
+    def recurrent():
+        bs = D // w.H
+        lam = torch.log(torch.rand((D,), generator=g, device="cuda") * 0.099 + 0.9)
+        lam = lam - torch.log1p(-torch.exp(lam))          # sigmoid(Lambda) ~ U[0.9, 0.999]
+        P = binding.Params(_dev_randn(torch, g, (D, 4), 0.5), None,
+                           _dev_randn(torch, g, (w.H, bs, bs), bs ** -0.5), None,
+                           _dev_randn(torch, g, (w.H, bs, bs), bs ** -0.5), None,
+                           lam.float().contiguous())
+        Q = binding.ProjParams(_dev_randn(torch, g, (D, Dm), Dm ** -0.5), None,
+                               _dev_randn(torch, g, (D, Dm), Dm ** -0.5), None,
+                               _dev_randn(torch, g, (Dm, D), D ** -0.5), None)
+        return ("recurrent", P, Q, norms(), mlp())
+
+    def attention():
+        A = binding.AttnParams(_dev_randn(torch, g, (HD, Dm), Dm ** -0.5),
+                               _dev_randn(torch, g, (256, Dm), Dm ** -0.5),
+                               _dev_randn(torch, g, (256, Dm), Dm ** -0.5),
+                               _dev_randn(torch, g, (Dm, HD), HD ** -0.5), None, Hq,
+                               synth.ATTN_WINDOW)
+        return ("attention", A, None, norms(), mlp())
+
+    return [attention() if i % 3 == 2 else recurrent() for i in range(STACK_LAYERS)]
+
+
+def time_layers(w, steps, warmup, torch, binding):
+    """The residual layers at the batched 2B shape (width 2560, MLP 7680): each layer alone, the
+    MLP alone, and the 26-layer stack (two recurrent layers to one attention layer) on seeded
+    random weights: a prefill of the whole 8 x 8192-token batch, and decode steps for 256 and
+    for 1 sequences."""
+
+    def timed(call, n, warm=warmup):
+        for _ in range(warm):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    g = torch.Generator(device="cuda").manual_seed(w.seed + 7)
+    layers = _stack_weights(torch, binding, w, g)
+    B, T, Dm, D = w.B, w.T, w.D, w.D
+    F = synth.MLP_EXPANSION * Dm
+    M = B * T
+    x = _to_dev(synth.make_block_input(w), torch)
+    y = torch.empty_like(x)
+    _, P, Q, Nn, Mm = layers[0]
+    _, A, _, _, _ = layers[2]
+    ws_r = binding.make_recurrent_layer_workspace(P, Q, Mm, B, T)
+    ws_a = binding.DeviceBuffer(binding.load_library().rglru_attention_layer_workspace_bytes(
+        __import__("ctypes").byref(A.c), B, T, F), "cuda")
+    hl = torch.empty((B, D), dtype=torch.float32, device="cuda")
+    cl = torch.empty((B, 3, D), dtype=torch.bfloat16, device="cuda")
+
+    def rec_layer(P, Q, Nn, Mm, xi, yo):
+        binding.rglru_recurrent_layer_prefill(P, Q, Nn, Mm, xi, out=yo, h_last=hl, conv_last=cl,
+                                              workspace=ws_r)
+
+    def att_layer(A, Nn, Mm, xi, yo):
+        binding.rglru_attention_layer_prefill(A, Nn, Mm, xi, out=yo, workspace=ws_a)
+
+    n = max(steps // 4, 2)
+    ms_rec = timed(lambda: rec_layer(P, Q, Nn, Mm, x, y), n)
+    ms_att = timed(lambda: att_layer(A, layers[2][3], layers[2][4], x, y), n)
+    ws_m = binding.DeviceBuffer(binding.load_library().rglru_mlp_workspace_bytes(M, F), "cuda")
+    xm = x.view(M, Dm)
+    ms_mlp = timed(lambda: binding.rglru_mlp(Mm, xm, out=y.view(M, Dm), workspace=ws_m), n)
+    del ws_m
+    fl_mlp = 2.0 * M * Dm * F * 3
+    z = torch.empty_like(xm)
+    ms_norm = timed(lambda: binding.rglru_rmsnorm(xm, Nn.tensors[0], y.view(M, Dm), out=z),
+                    max(steps, 10))
+    del z
+    norm_bytes = 3 * M * Dm * 2
+
+    def stack_prefill():
+        xi, yo = x, y
+        for kind, Pa, Qa, Na, Ma in layers:
+            if kind == "recurrent":
+                rec_layer(Pa, Qa, Na, Ma, xi, yo)
+            else:
+                att_layer(Pa, Na, Ma, xi, yo)
+            xi, yo = yo, xi
+
+    ms_stack = timed(stack_prefill, 2, warm=1)
+    del ws_r, ws_a, hl, cl
+
+    def decode_stack(N):
+        xs = _dev_randn(torch, g, (N, Dm), 1.0)
+        ys = torch.empty_like(xs)
+        pos = torch.full((N,), 4096, dtype=torch.int32, device="cuda")
+        state = []
+        lib = binding.load_library()
+        import ctypes
+        for kind, Pa, Qa, Na, Ma in layers:
+            if kind == "recurrent":
+                state.append((torch.zeros((N, D), dtype=torch.float32, device="cuda"),
+                              _dev_randn(torch, g, (N, 3, D), 1.0),
+                              binding.DeviceBuffer(lib.rglru_recurrent_layer_decode_workspace_bytes(
+                                  N, D, Dm, F), "cuda")))
+            else:
+                c = binding.AttnCache(N, synth.ATTN_WINDOW, "cuda")
+                c.k.normal_(generator=g)
+                c.v.normal_(generator=g)
+                state.append((c, None, binding.DeviceBuffer(
+                    lib.rglru_attention_layer_decode_workspace_bytes(ctypes.byref(Pa.c), N, F),
+                    "cuda")))
+
+        def step():
+            xi, yo = xs, ys
+            for (kind, Pa, Qa, Na, Ma), (s0, s1, wsd) in zip(layers, state):
+                if kind == "recurrent":
+                    binding.rglru_recurrent_layer_decode(Pa, Qa, Na, Ma, xi, s0, s1, out=yo,
+                                                         workspace=wsd)
+                else:
+                    binding.rglru_attention_layer_decode(Pa, Na, Ma, pos, xi, s0, out=yo,
+                                                         workspace=wsd)
+                xi, yo = yo, xi
+
+        us = 1e3 * timed(step, max(steps // 2, 5), warm=2)
+        graph_us = None
+        try:
+            gr = torch.cuda.CUDAGraph()
+            st = torch.cuda.Stream()
+            st.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(st):
+                step()
+                torch.cuda.synchronize()
+                with torch.cuda.graph(gr, stream=st):
+                    step()
+            torch.cuda.current_stream().wait_stream(st)
+            graph_us = 1e3 * timed(gr.replay, max(steps // 2, 5), warm=2)
+        except Exception as ex:          # graph capture is an optimisation; eager stays valid
+            print("stack decode graph capture failed: %s" % ex, file=sys.stderr)
+        return us, graph_us
+
+    dec256, dec256_g = decode_stack(256)
+    dec1, dec1_g = decode_stack(1)
+    n_params = sum(sum(t.numel() for t in (l[1].tensors if hasattr(l[1], "tensors") else ())
+                       if t is not None) +
+                   sum(t.numel() for t in (l[2].tensors if l[2] is not None else ()) if t is not None) +
+                   sum(t.numel() for t in l[4].tensors if t is not None) for l in layers)
+    return {
+        "workload": "%s shape, width 2560, MLP 7680, residual layers with seeded random weights"
+                    % w.name,
+        "recurrent_layer_ms": ms_rec, "attention_layer_ms": ms_att,
+        "mlp": {"ms": ms_mlp, "tflops": fl_mlp / (ms_mlp * 1e-3) / 1e12,
+                "roofline": {"bound": "mfma", "achieved": fl_mlp / (ms_mlp * 1e-3) / 1e12,
+                             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                             "frac": fl_mlp / (ms_mlp * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}},
+        "add_rmsnorm": {"ms": ms_norm, "bytes": norm_bytes,
+                        "roofline": {"bound": "hbm",
+                                     "achieved": norm_bytes / (ms_norm * 1e-3) / 1e9,
+                                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                     "frac": norm_bytes / (ms_norm * 1e-3) / 1e9 / HBM_PEAK_GBS}},
+        "stack": {"layers": STACK_LAYERS, "pattern": "recurrent, recurrent, attention",
+                  "parameters": n_params,
+                  "prefill_ms": ms_stack, "prefill_tokens/s": M / (ms_stack * 1e-3),
+                  "decode_256_us_per_step": dec256, "decode_256_us_per_step_graph": dec256_g,
+                  "decode_1_us_per_step": dec1, "decode_1_us_per_step_graph": dec1_g,
+                  "note": "no embedding or final norm; decode at position 4096 with full "
+                          "attention windows; weight bytes per decode step %d"
+                          % (2 * n_params)}}
+
+
 def cpu_baseline(w):
     """The oracle on the whole headline workload (all 8 sequences x 8192 tokens x 10 heads),
     one OpenMP thread per (sequence, head) unit; inputs are generated before the clock starts."""
@@ -576,6 +765,7 @@ def main():
         line["block_prefill"] = time_block(w, max(args.steps // 2, 5), args.warmup, torch, binding)
         line["local_attention"] = time_attention(w, max(args.steps // 2, 5), args.warmup, torch,
                                                  binding)
+        line["residual_layers"] = time_layers(w, args.steps, args.warmup, torch, binding)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)

@@ -32,7 +32,9 @@ EXPORTS = ["rglru_prefill_workspace_bytes", "rglru_prefill_workspace_init", "rgl
            "rglru_local_attention_cache_bytes", "rglru_local_attention_decode_workspace_bytes",
            "rglru_local_attention_decode", "rglru_rmsnorm", "rglru_mlp_workspace_bytes",
            "rglru_mlp", "rglru_recurrent_layer_workspace_bytes", "rglru_recurrent_layer_prefill",
-           "rglru_attention_layer_workspace_bytes", "rglru_attention_layer_prefill"]
+           "rglru_attention_layer_workspace_bytes", "rglru_attention_layer_prefill",
+           "rglru_recurrent_layer_decode_workspace_bytes", "rglru_recurrent_layer_decode",
+           "rglru_attention_layer_decode_workspace_bytes", "rglru_attention_layer_decode"]
 
 _lock = threading.Lock()
 _lib = None
@@ -152,6 +154,15 @@ def load_library(path: str = LIB_PATH):
         lib.rglru_attention_layer_workspace_bytes.restype = SZ
         lib.rglru_attention_layer_prefill.argtypes = [AP, NP, MP, I32, I32, P, P, P, P, P, SZ, P]
         lib.rglru_attention_layer_prefill.restype = ctypes.c_int
+        lib.rglru_recurrent_layer_decode_workspace_bytes.argtypes = [I32, I32, I32, I32]
+        lib.rglru_recurrent_layer_decode_workspace_bytes.restype = SZ
+        lib.rglru_recurrent_layer_decode.argtypes = [PP, ctypes.POINTER(rglru_proj_params), NP, MP,
+                                                     I32, P, P, P, P, P, SZ, P]
+        lib.rglru_recurrent_layer_decode.restype = ctypes.c_int
+        lib.rglru_attention_layer_decode_workspace_bytes.argtypes = [AP, I32, I32]
+        lib.rglru_attention_layer_decode_workspace_bytes.restype = SZ
+        lib.rglru_attention_layer_decode.argtypes = [AP, NP, MP, I32, P, P, P, P, P, P, SZ, P]
+        lib.rglru_attention_layer_decode.restype = ctypes.c_int
         lib.rglru_abi_version.argtypes = []
         lib.rglru_abi_version.restype = ctypes.c_int
         _lib = lib
@@ -687,4 +698,47 @@ def rglru_attention_layer_prefill(a: AttnParams, n: NormParams, m: MlpParams, x_
         _ptr(cache.k) if cache is not None else None, _ptr(cache.v) if cache is not None else None,
         _ptr(workspace.t), workspace.nbytes, _stream())
     _check(lib, st, "rglru_attention_layer_prefill")
+    return out
+
+
+def rglru_recurrent_layer_decode(p: Params, q: ProjParams, n: NormParams, m: MlpParams, x_t, h,
+                                 conv_state, *, out=None, workspace: DeviceBuffer | None = None):
+    """One decode step of the residual layer around the recurrent block: x_t [N, D_model];
+    h [N, D] fp32 and conv_state [N, 3, D] are updated in place."""
+    lib = load_library()
+    N, Dm = x_t.shape
+    _need(x_t, "x_t", torch.bfloat16, (N, q.Dm), p.device)
+    _need(h, "h", torch.float32, (N, p.D), p.device)
+    _need(conv_state, "conv_state", torch.bfloat16, (N, 3, p.D), p.device)
+    if out is None:
+        out = torch.empty_like(x_t)
+    if workspace is None:
+        workspace = DeviceBuffer(int(lib.rglru_recurrent_layer_decode_workspace_bytes(
+            N, p.D, q.Dm, m.F)), p.device)
+    st = lib.rglru_recurrent_layer_decode(ctypes.byref(p.c), ctypes.byref(q.c), ctypes.byref(n.c),
+                                          ctypes.byref(m.c), N, _ptr(x_t), _ptr(out), _ptr(h),
+                                          _ptr(conv_state), _ptr(workspace.t), workspace.nbytes,
+                                          _stream())
+    _check(lib, st, "rglru_recurrent_layer_decode")
+    return out
+
+
+def rglru_attention_layer_decode(a: AttnParams, n: NormParams, m: MlpParams, pos, x_t,
+                                 cache: AttnCache, *, out=None,
+                                 workspace: DeviceBuffer | None = None):
+    """One decode step of the residual layer around the local-attention block."""
+    lib = load_library()
+    N, Dm = x_t.shape
+    _need(x_t, "x_t", torch.bfloat16, (N, a.Dm), a.device)
+    _need(pos, "pos", torch.int32, (N,), a.device)
+    if out is None:
+        out = torch.empty_like(x_t)
+    if workspace is None:
+        workspace = DeviceBuffer(int(lib.rglru_attention_layer_decode_workspace_bytes(
+            ctypes.byref(a.c), N, m.F)), a.device)
+    st = lib.rglru_attention_layer_decode(ctypes.byref(a.c), ctypes.byref(n.c), ctypes.byref(m.c),
+                                          N, _ptr(pos), _ptr(x_t), _ptr(out), _ptr(cache.k),
+                                          _ptr(cache.v), _ptr(workspace.t), workspace.nbytes,
+                                          _stream())
+    _check(lib, st, "rglru_attention_layer_decode")
     return out

@@ -2,6 +2,7 @@
 // Every check runs on the host before any HIP call; see include/rglru.h for the contract.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -182,9 +183,11 @@ size_t rglru_decode_workspace_bytes(int32_t N, int32_t D, int32_t dtype) {
     return (size_t)((N + 15) / 16) * 16 * (size_t)D * elem_size(dtype);  // blocks of 16 sequences
 }
 
-int rglru_decode_step(const rglru_params* p, int32_t N, const void* x_t, int64_t ld_x,
-                      const void* y_t, int64_t ld_y, void* out_t, int64_t ld_out, float* h,
-                      void* conv_state, void* workspace, size_t ws_bytes, void* stream) {
+// the decode step: every check runs first; with launch = false nothing else happens
+static int decode_step_impl(const rglru_params* p, int32_t N, const void* x_t, int64_t ld_x,
+                            const void* y_t, int64_t ld_y, void* out_t, int64_t ld_out, float* h,
+                            void* conv_state, void* workspace, size_t ws_bytes, void* stream,
+                            bool launch) {
     int st = check_params(p, true);
     if (st != RGLRU_OK) return st;
     if (N < 1) return RGLRU_ERR_SHAPE;
@@ -219,6 +222,7 @@ int rglru_decode_step(const rglru_params* p, int32_t N, const void* x_t, int64_t
             overlap(workspace, need, conv_state, sc))
             return RGLRU_ERR_ALIAS;
     }
+    if (!launch) return RGLRU_OK;
     DecodeArgs a;
     memset(&a, 0, sizeof a);
     a.x = x_t; a.y = y_t; a.out = out_t;
@@ -231,6 +235,13 @@ int rglru_decode_step(const rglru_params* p, int32_t N, const void* x_t, int64_t
     a.N = N; a.D = p->D; a.H = p->n_heads;
     hipError_t e = launch_decode(a, p->dtype, p->D / p->n_heads, (hipStream_t)stream);
     return e == hipSuccess ? RGLRU_OK : hip_fail(e);
+}
+
+int rglru_decode_step(const rglru_params* p, int32_t N, const void* x_t, int64_t ld_x,
+                      const void* y_t, int64_t ld_y, void* out_t, int64_t ld_out, float* h,
+                      void* conv_state, void* workspace, size_t ws_bytes, void* stream) {
+    return decode_step_impl(p, N, x_t, ld_x, y_t, ld_y, out_t, ld_out, h, conv_state, workspace,
+                            ws_bytes, stream, true);
 }
 
 int conv1d_state_update(const rglru_params* p, int32_t N, int32_t T_new, const void* x_new,
@@ -436,10 +447,11 @@ size_t rglru_local_attention_decode_workspace_bytes(int32_t N, int32_t n_heads, 
            (size_t)N * nsplit * n_heads * (2 + kAttnDh) * sizeof(float);
 }
 
-int rglru_local_attention_decode(int32_t N, int32_t n_heads, int32_t window, float rope_base,
-                                 const int32_t* pos, const void* q, const void* k, const void* v,
-                                 void* kcache, void* vcache, void* o, void* workspace,
-                                 size_t ws_bytes, void* stream) {
+// the attention decode step: every check runs first; with launch = false nothing else happens
+static int attn_decode_impl(int32_t N, int32_t n_heads, int32_t window, float rope_base,
+                            const int32_t* pos, const void* q, const void* k, const void* v,
+                            void* kcache, void* vcache, void* o, void* workspace, size_t ws_bytes,
+                            void* stream, bool launch) {
     if (N < 1 || n_heads < 1 || n_heads > 16 || window < 1 || !(rope_base > 1.0f) ||
         !(rope_base < INFINITY))
         return RGLRU_ERR_SHAPE;
@@ -459,6 +471,7 @@ int rglru_local_attention_decode(int32_t N, int32_t n_heads, int32_t window, flo
     for (int i = 0; i < 4; ++i)
         for (int j = i + 1; j < 8; ++j)
             if (overlap(all[i], len[i], all[j], len[j])) return RGLRU_ERR_ALIAS;
+    if (!launch) return RGLRU_OK;
     AttnDecodeArgs a;
     a.pos = pos; a.q = q; a.k = k; a.v = v; a.kc = kcache; a.vc = vcache; a.o = o;
     a.qr = workspace;
@@ -468,6 +481,14 @@ int rglru_local_attention_decode(int32_t N, int32_t n_heads, int32_t window, flo
     a.rope_base = rope_base;
     hipError_t e = launch_attention_decode(a, (hipStream_t)stream);
     return e == hipSuccess ? RGLRU_OK : hip_fail(e);
+}
+
+int rglru_local_attention_decode(int32_t N, int32_t n_heads, int32_t window, float rope_base,
+                                 const int32_t* pos, const void* q, const void* k, const void* v,
+                                 void* kcache, void* vcache, void* o, void* workspace,
+                                 size_t ws_bytes, void* stream) {
+    return attn_decode_impl(N, n_heads, window, rope_base, pos, q, k, v, kcache, vcache, o,
+                            workspace, ws_bytes, stream, true);
 }
 
 size_t rglru_local_attention_block_workspace_bytes(const rglru_attn_params* a, int32_t B,
@@ -650,7 +671,7 @@ int check_norms(const rglru_norm_params* n, int Dm) {
 }
 
 hipError_t run_mlp(const rglru_mlp_params* m, int M, const void* x, void* out, void* ws,
-                   hipStream_t s) {
+                   float* part, size_t part_bytes, hipStream_t s) {
     const size_t nf = (size_t)M * m->F;
     void* G = ws;
     void* U = static_cast<char*>(ws) + round256(nf * 2);
@@ -658,24 +679,35 @@ hipError_t run_mlp(const rglru_mlp_params* m, int M, const void* x, void* out, v
     memset(&g, 0, sizeof g);
     g.A = x; g.W[0] = m->gate_w; g.W[1] = m->up_w; g.b[0] = m->gate_b; g.b[1] = m->up_b;
     g.C[0] = G; g.C[1] = U; g.M = M; g.K = m->D_model; g.Nw[0] = m->F; g.Nw[1] = m->F; g.nseg = 2;
+    g.part = part; g.part_bytes = part_bytes;
     hipError_t e = launch_proj_gemm(g, s);
     if (e == hipSuccess) e = launch_geglu(G, U, nf, s);
     if (e != hipSuccess) return e;
     memset(&g, 0, sizeof g);
     g.A = G; g.W[0] = m->down_w; g.b[0] = m->down_b; g.C[0] = out;
     g.M = M; g.K = m->F; g.Nw[0] = m->D_model; g.nseg = 1;
+    g.part = part; g.part_bytes = part_bytes;
     return launch_proj_gemm(g, s);
 }
 
 // Layer workspace after the block's own part: xn / hn, the block output / the MLP output, h,
 // then the MLP's workspace.
+// Decode layers add fp32 partial sums for the GEMMs' split K at the end.
 struct LayerBufs {
     void *a, *b, *h, *mlp;
+    float* part;
+    size_t part_bytes;
 };
 LayerBufs layer_bufs(void* workspace, size_t block_bytes, size_t M, int Dm) {
     const size_t act = round256(M * Dm * 2);
     char* base = static_cast<char*>(workspace) + round256(block_bytes);
-    return {base, base + act, base + 2 * act, base + 3 * act};
+    return {base, base + act, base + 2 * act, base + 3 * act, nullptr, 0};
+}
+// the largest split-K partial buffer of a decode layer's GEMMs (M rows; N and K per GEMM)
+size_t decode_part_bytes(int M, const int (*nk)[2], int n) {
+    size_t b = 0;
+    for (int i = 0; i < n; ++i) b = std::max(b, proj_gemm_part_bytes(M, nk[i][0], nk[i][1]));
+    return round256(b);
 }
 size_t layer_tail_bytes(size_t M, int Dm, int F) {
     return 3 * round256(M * Dm * 2) + rglru_mlp_workspace_bytes((int32_t)M, F);
@@ -695,7 +727,7 @@ int run_layer(const rglru_norm_params* nrm, const rglru_mlp_params* m, size_t M,
     if (st != RGLRU_OK) return st;
     na.x = x_in; na.y = L.b; na.g = nrm->channel_scale; na.h = L.h; na.n = L.a;
     e = launch_add_rmsnorm(na, s);
-    if (e == hipSuccess) e = run_mlp(m, (int)M, L.a, L.b, L.mlp, s);
+    if (e == hipSuccess) e = run_mlp(m, (int)M, L.a, L.b, L.mlp, L.part, L.part_bytes, s);
     if (e != hipSuccess) return hip_fail(e);
     na.x = L.h; na.y = L.b; na.g = nullptr; na.h = out; na.n = nullptr;
     e = launch_add_rmsnorm(na, s);
@@ -711,6 +743,15 @@ int check_layer_alias(const void* x_in, void* out, size_t n_io, void* ws, size_t
     for (int i = 0; i < nothers; ++i)
         if (overlap(out, n_io, others[i], olen[i]) || overlap(ws, need, others[i], olen[i]))
             return RGLRU_ERR_ALIAS;
+    return RGLRU_OK;
+}
+
+// written state buffers (h, conv windows, ring caches) against the layer's read-only weights
+int check_state_alias(const void* const* wr, const size_t* wl, int nw, const void* const* rd,
+                      const size_t* rl, int nr) {
+    for (int i = 0; i < nw; ++i)
+        for (int j = 0; j < nr; ++j)
+            if (overlap(wr[i], wl[i], rd[j], rl[j])) return RGLRU_ERR_ALIAS;
     return RGLRU_OK;
 }
 
@@ -735,7 +776,7 @@ int rglru_mlp(const rglru_mlp_params* m, int32_t M, const void* x, void* out, vo
     if (M > 0 && check_layer_alias(x, out, n_io, workspace, need, w, wl, 6) != RGLRU_OK)
         return RGLRU_ERR_ALIAS;
     if (M == 0) return RGLRU_OK;
-    hipError_t e = run_mlp(m, M, x, out, workspace, (hipStream_t)stream);
+    hipError_t e = run_mlp(m, M, x, out, workspace, nullptr, 0, (hipStream_t)stream);
     return e == hipSuccess ? RGLRU_OK : hip_fail(e);
 }
 
@@ -780,7 +821,9 @@ int rglru_recurrent_layer_prefill(const rglru_params* p, const rglru_proj_params
                               nrm->channel_scale, q->lin_x_w, q->lin_y_w, q->lin_out_w};
     size_t olen[16] = {n_h, n_h, n_c, n_c, (size_t)Dm * 2, (size_t)Dm * 2, pw, pw, pw};
     const int n = 9 + mlp_operands(m, others + 9, olen + 9);
-    if (check_layer_alias(x_in, out, n_io, workspace, need, others, olen, n) != RGLRU_OK)
+    if (check_layer_alias(x_in, out, n_io, workspace, need, others, olen, n) != RGLRU_OK ||
+        check_state_alias(others + 1, olen + 1, 1, others + 4, olen + 4, n - 4) != RGLRU_OK ||
+        check_state_alias(others + 3, olen + 3, 1, others + 4, olen + 4, n - 4) != RGLRU_OK)
         return RGLRU_ERR_ALIAS;
     return run_layer(nrm, m, M, Dm, x_in, out, L, (hipStream_t)stream, [&]() {
         return block_prefill_impl(p, q, B, T, L.a, L.b, h0, h_last, conv0, conv_last, workspace,
@@ -824,10 +867,176 @@ int rglru_attention_layer_prefill(const rglru_attn_params* a, const rglru_norm_p
                        (size_t)kAttnDh * Dm * 2, (size_t)kAttnDh * Dm * 2, HD * Dm * 2,
                        (size_t)Dm * 2};
     const int n = 9 + mlp_operands(m, others + 9, olen + 9);
-    if (check_layer_alias(x_in, out, n_io, workspace, need, others, olen, n) != RGLRU_OK)
+    if (check_layer_alias(x_in, out, n_io, workspace, need, others, olen, n) != RGLRU_OK ||
+        check_state_alias(others, olen, 2, others + 2, olen + 2, n - 2) != RGLRU_OK)
         return RGLRU_ERR_ALIAS;
     return run_layer(nrm, m, M, Dm, x_in, out, L, (hipStream_t)stream, [&]() {
         return attn_block_impl(a, B, T, L.a, L.b, kcache, vcache, workspace, bw, stream, true);
+    });
+}
+
+// ------------------------------------------------------------------------------------------
+// decode steps of the two layers
+// ------------------------------------------------------------------------------------------
+// block part of the recurrent decode workspace: x and y branches, their product, the decode
+// step's own workspace
+static size_t rec_dec_block_bytes(size_t N, int D) {
+    return 3 * round256(N * D * 2) + round256(rglru_decode_workspace_bytes((int32_t)N, D,
+                                                                           RGLRU_BF16));
+}
+
+static size_t rec_dec_part_bytes(int N, int D, int Dm, int F) {
+    const int nk[4][2] = {{2 * D, Dm}, {Dm, D}, {2 * F, Dm}, {Dm, F}};
+    return decode_part_bytes(N, nk, 4);
+}
+
+size_t rglru_recurrent_layer_decode_workspace_bytes(int32_t N, int32_t D, int32_t D_model,
+                                                    int32_t F) {
+    if (N < 1 || D < 1 || D_model < 1 || F < 1) return 0;
+    return round256(rec_dec_block_bytes(N, D)) + layer_tail_bytes(N, D_model, F) +
+           rec_dec_part_bytes(N, D, D_model, F);
+}
+
+int rglru_recurrent_layer_decode(const rglru_params* p, const rglru_proj_params* q,
+                                 const rglru_norm_params* nrm, const rglru_mlp_params* m,
+                                 int32_t N, const void* x_t, void* out_t, float* h,
+                                 void* conv_state, void* workspace, size_t ws_bytes,
+                                 void* stream) {
+    int st = check_params(p, true);
+    if (st != RGLRU_OK) return st;
+    if (!q) return RGLRU_ERR_NULL;
+    const int Dm = q->D_model, D = p->D;
+    st = check_norms(nrm, Dm);
+    if (st == RGLRU_OK) st = check_mlp(m, Dm);
+    if (st != RGLRU_OK) return st;
+    if (p->dtype != RGLRU_BF16 || D % 256 != 0 || D >= (1 << 21)) return RGLRU_ERR_UNSUPPORTED;
+    if (N < 1) return RGLRU_ERR_SHAPE;
+    if (!q->lin_x_w || !q->lin_y_w || !q->lin_out_w || !x_t || !out_t) return RGLRU_ERR_NULL;
+    const void* ptrs[] = {q->lin_x_w, q->lin_x_b, q->lin_y_w, q->lin_y_b, q->lin_out_w,
+                          q->lin_out_b, x_t, out_t, workspace};
+    for (const void* ptr : ptrs)
+        if (!aligned16(ptr)) return RGLRU_ERR_UNSUPPORTED;
+    const size_t need = rglru_recurrent_layer_decode_workspace_bytes(N, D, Dm, m->F);
+    if (!workspace || ws_bytes < need) return RGLRU_ERR_WORKSPACE;
+    const size_t bb = rec_dec_block_bytes(N, D), act = round256((size_t)N * D * 2);
+    char* ws = static_cast<char*>(workspace);
+    void *xb = ws, *yb = ws + act, *mg = ws + 2 * act, *dws = ws + 3 * act;
+    const size_t dws_bytes = rglru_decode_workspace_bytes(N, D, RGLRU_BF16);
+    st = decode_step_impl(p, N, xb, D, yb, D, mg, D, h, conv_state, dws, dws_bytes, stream, false);
+    if (st != RGLRU_OK) return st;
+    const size_t n_io = (size_t)N * Dm * 2, pw = (size_t)D * Dm * 2;
+    const void* others[16] = {h, conv_state, nrm->temporal_scale, nrm->channel_scale,
+                              q->lin_x_w, q->lin_y_w, q->lin_out_w};
+    size_t olen[16] = {(size_t)N * D * 4, (size_t)N * 3 * D * 2, (size_t)Dm * 2, (size_t)Dm * 2,
+                       pw, pw, pw};
+    const int n = 7 + mlp_operands(m, others + 7, olen + 7);
+    if (check_layer_alias(x_t, out_t, n_io, workspace, need, others, olen, n) != RGLRU_OK ||
+        check_state_alias(others, olen, 2, others + 2, olen + 2, n - 2) != RGLRU_OK)
+        return RGLRU_ERR_ALIAS;
+    LayerBufs L = layer_bufs(workspace, bb, N, Dm);
+    L.part_bytes = rec_dec_part_bytes(N, D, Dm, m->F);
+    L.part = L.part_bytes ? reinterpret_cast<float*>(ws + need - L.part_bytes) : nullptr;
+    const hipStream_t s = (hipStream_t)stream;
+    return run_layer(nrm, m, N, Dm, x_t, out_t, L, s, [&]() {
+        ProjGemmArgs g;
+        memset(&g, 0, sizeof g);
+        g.A = L.a; g.W[0] = q->lin_x_w; g.W[1] = q->lin_y_w; g.b[0] = q->lin_x_b;
+        g.b[1] = q->lin_y_b; g.C[0] = xb; g.C[1] = yb; g.M = N; g.K = Dm; g.Nw[0] = D;
+        g.Nw[1] = D; g.nseg = 2; g.part = L.part; g.part_bytes = L.part_bytes;
+        hipError_t e = launch_proj_gemm(g, s);
+        if (e != hipSuccess) return hip_fail(e);
+        int r = decode_step_impl(p, N, xb, D, yb, D, mg, D, h, conv_state, dws, dws_bytes, stream,
+                                 true);
+        if (r != RGLRU_OK) return r;
+        memset(&g, 0, sizeof g);
+        g.A = mg; g.W[0] = q->lin_out_w; g.b[0] = q->lin_out_b; g.C[0] = L.b;
+        g.M = N; g.K = D; g.Nw[0] = Dm; g.nseg = 1; g.part = L.part; g.part_bytes = L.part_bytes;
+        e = launch_proj_gemm(g, s);
+        return e == hipSuccess ? RGLRU_OK : hip_fail(e);
+    });
+}
+
+// block part of the attention decode workspace: q, k, v, the attention output, the attention
+// decode's own workspace
+static size_t attn_dec_block_bytes(size_t N, int Hq, int W) {
+    return 2 * round256(N * Hq * kAttnDh * 2) + 2 * round256(N * kAttnDh * 2) +
+           round256(rglru_local_attention_decode_workspace_bytes((int32_t)N, Hq, W));
+}
+
+static size_t attn_dec_part_bytes(int N, int Hq, int Dm, int F) {
+    const int HD = Hq * kAttnDh;
+    const int nk[4][2] = {{HD + 2 * kAttnDh, Dm}, {Dm, HD}, {2 * F, Dm}, {Dm, F}};
+    return decode_part_bytes(N, nk, 4);
+}
+
+size_t rglru_attention_layer_decode_workspace_bytes(const rglru_attn_params* a, int32_t N,
+                                                    int32_t F) {
+    if (!a || N < 1 || F < 1 || a->n_heads < 1 || a->window < 1 || a->D_model < 1) return 0;
+    if (rglru_local_attention_decode_workspace_bytes(N, a->n_heads, a->window) == 0) return 0;
+    return round256(attn_dec_block_bytes(N, a->n_heads, a->window)) +
+           layer_tail_bytes(N, a->D_model, F) + attn_dec_part_bytes(N, a->n_heads, a->D_model, F);
+}
+
+int rglru_attention_layer_decode(const rglru_attn_params* a, const rglru_norm_params* nrm,
+                                 const rglru_mlp_params* m, int32_t N, const int32_t* pos,
+                                 const void* x_t, void* out_t, void* kcache, void* vcache,
+                                 void* workspace, size_t ws_bytes, void* stream) {
+    if (!a) return RGLRU_ERR_NULL;
+    const int Dm = a->D_model, Hq = a->n_heads;
+    int st = check_norms(nrm, Dm);
+    if (st == RGLRU_OK) st = check_mlp(m, Dm);
+    if (st != RGLRU_OK) return st;
+    if (a->head_dim != kAttnDh) return RGLRU_ERR_UNSUPPORTED;
+    if (N < 1 || Hq < 1 || Hq > 16 || a->window < 1) return RGLRU_ERR_SHAPE;
+    if (!a->q_w || !a->k_w || !a->v_w || !a->o_w || !x_t || !out_t) return RGLRU_ERR_NULL;
+    const void* ptrs[] = {a->q_w, a->k_w, a->v_w, a->o_w, a->o_b, x_t, out_t, workspace};
+    for (const void* ptr : ptrs)
+        if (!aligned16(ptr)) return RGLRU_ERR_UNSUPPORTED;
+    const size_t need = rglru_attention_layer_decode_workspace_bytes(a, N, m->F);
+    if (need == 0) return RGLRU_ERR_SHAPE;
+    if (!workspace || ws_bytes < need) return RGLRU_ERR_WORKSPACE;
+    const size_t HD = (size_t)Hq * kAttnDh;
+    const size_t nq = round256((size_t)N * HD * 2), nk = round256((size_t)N * kAttnDh * 2);
+    char* ws = static_cast<char*>(workspace);
+    void *qb = ws, *kb = ws + nq, *vb = ws + nq + nk, *ob = ws + nq + 2 * nk;
+    void* dws = ws + 2 * nq + 2 * nk;
+    const size_t dws_bytes = rglru_local_attention_decode_workspace_bytes(N, Hq, a->window);
+    st = attn_decode_impl(N, Hq, a->window, a->rope_base, pos, qb, kb, vb, kcache, vcache, ob, dws,
+                          dws_bytes, stream, false);
+    if (st != RGLRU_OK) return st;
+    const size_t n_io = (size_t)N * Dm * 2;
+    const size_t nc = rglru_local_attention_cache_bytes(N, a->window);
+    const void* others[16] = {pos, kcache, vcache, nrm->temporal_scale, nrm->channel_scale,
+                              a->q_w, a->k_w, a->v_w, a->o_w, a->o_b};
+    size_t olen[16] = {(size_t)N * 4, nc, nc, (size_t)Dm * 2, (size_t)Dm * 2, HD * Dm * 2,
+                       (size_t)kAttnDh * Dm * 2, (size_t)kAttnDh * Dm * 2, HD * Dm * 2,
+                       (size_t)Dm * 2};
+    const int n = 10 + mlp_operands(m, others + 10, olen + 10);
+    if (check_layer_alias(x_t, out_t, n_io, workspace, need, others, olen, n) != RGLRU_OK ||
+        check_state_alias(others + 1, olen + 1, 2, others + 3, olen + 3, n - 3) != RGLRU_OK)
+        return RGLRU_ERR_ALIAS;
+    LayerBufs L = layer_bufs(workspace, attn_dec_block_bytes(N, Hq, a->window), N, Dm);
+    L.part_bytes = attn_dec_part_bytes(N, Hq, Dm, m->F);
+    L.part = L.part_bytes ? reinterpret_cast<float*>(ws + need - L.part_bytes) : nullptr;
+    const hipStream_t s = (hipStream_t)stream;
+    return run_layer(nrm, m, N, Dm, x_t, out_t, L, s, [&]() {
+        ProjGemmArgs g;
+        memset(&g, 0, sizeof g);
+        g.A = L.a; g.W[0] = a->q_w; g.W[1] = a->k_w; g.W[2] = a->v_w;
+        g.C[0] = qb; g.C[1] = kb; g.C[2] = vb;
+        g.M = N; g.K = Dm; g.Nw[0] = (int)HD; g.Nw[1] = kAttnDh; g.Nw[2] = kAttnDh; g.nseg = 3;
+        g.part = L.part; g.part_bytes = L.part_bytes;
+        hipError_t e = launch_proj_gemm(g, s);
+        if (e != hipSuccess) return hip_fail(e);
+        int r = attn_decode_impl(N, Hq, a->window, a->rope_base, pos, qb, kb, vb, kcache, vcache,
+                                 ob, dws, dws_bytes, stream, true);
+        if (r != RGLRU_OK) return r;
+        memset(&g, 0, sizeof g);
+        g.A = ob; g.W[0] = a->o_w; g.b[0] = a->o_b; g.C[0] = L.b;
+        g.M = N; g.K = (int)HD; g.Nw[0] = Dm; g.nseg = 1;
+        g.part = L.part; g.part_bytes = L.part_bytes;
+        e = launch_proj_gemm(g, s);
+        return e == hipSuccess ? RGLRU_OK : hip_fail(e);
     });
 }
 

@@ -77,7 +77,14 @@ struct ProjGemmArgs {
     int nseg;                    // 1 .. 3
     int M, K;                    // K % 128 == 0, 256 * Nw < 2^31
     int ntm, ntn;                // set by the launcher
+    // split K (small M): with part given, the launcher may split K in up to part_bytes of fp32
+    // partial sums [ksplit][M][sum Nw], added in split order by a second kernel
+    float* part;
+    size_t part_bytes;
+    int ksplit;                  // set by the launcher
 };
+// fp32 partial-sum bytes the launcher would use for this shape with unlimited part_bytes
+size_t proj_gemm_part_bytes(int M, int Ntot, int K);
 
 // Local sliding-window multi-query attention (head dim 256).
 struct AttnArgs {

@@ -134,6 +134,7 @@ __device__ __forceinline__ void tile_of(int bid, int ntm, int ntn, int& tm, int&
     tn = r / gm;
 }
 
+template <bool kSplitK>
 __global__ void __launch_bounds__(kThreads, 1) proj_gemm_kernel(ProjGemmArgs g) {
     __shared__ __attribute__((aligned(16))) uint16_t a0[kBM * kBK], a1[kBM * kBK];
     __shared__ __attribute__((aligned(16))) uint16_t b0[kBN * kBK], b1[kBN * kBK];
@@ -142,7 +143,10 @@ __global__ void __launch_bounds__(kThreads, 1) proj_gemm_kernel(ProjGemmArgs g) 
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (the copies' LDS base)
     const int wm = wv >> 1, wn = wv & 1;
     int tm, tn;
-    tile_of(blockIdx.x, g.ntm, g.ntn, tm, tn);
+    // with K split, blocks tiles * ks .. tiles * (ks + 1) - 1 take split ks of every tile
+    const int tiles = g.ntm * g.ntn;
+    const int ks = kSplitK ? __builtin_amdgcn_readfirstlane((int)blockIdx.x / tiles) : 0;
+    tile_of((int)blockIdx.x - ks * tiles, g.ntm, g.ntn, tm, tn);
     // the divisions above run on the vector unit; the tile is uniform, and the buffer resources
     // built from it must sit in scalar registers
     const int m0 = __builtin_amdgcn_readfirstlane(tm) * kBM;
@@ -150,13 +154,16 @@ __global__ void __launch_bounds__(kThreads, 1) proj_gemm_kernel(ProjGemmArgs g) 
     // output segment of this tile (segment widths are multiples of the tile width)
     const int seg = n0 < g.Nw[0] ? 0 : (n0 < g.Nw[0] + g.Nw[1] ? 1 : 2);
     const int nl0 = n0 - (seg > 0 ? g.Nw[0] : 0) - (seg > 1 ? g.Nw[1] : 0);
-    const int K = g.K;
+    const int K = g.K;                            // row pitch of A and W
+    const int Ks = kSplitK ? K / g.ksplit : K;   // this block's share of K
+    const int k0 = ks * Ks;
     const int rows = min(g.M - m0, kBM);
-    const uint16_t* A = static_cast<const uint16_t*>(g.A) + (size_t)m0 * K;
-    const uint16_t* W = static_cast<const uint16_t*>(g.W[seg]) + (size_t)nl0 * K;
+    const uint16_t* A = static_cast<const uint16_t*>(g.A) + (size_t)m0 * K + k0;
+    const uint16_t* W = static_cast<const uint16_t*>(g.W[seg]) + (size_t)nl0 * K + k0;
+    // (the ranges run k0 elements past the last row's share; no access reaches that far)
     const u32x4 ra = rsrc_words(A, (uint32_t)(rows * K * 2));
     const u32x4 rb = rsrc_words(W, (uint32_t)(kBN * K * 2));
-    const int KT = K / kBK;                       // even, >= 2
+    const int KT = Ks / kBK;                      // even, >= 2
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -234,15 +241,35 @@ __global__ void __launch_bounds__(kThreads, 1) proj_gemm_kernel(ProjGemmArgs g) 
         step(Fin{}, KT - 1, a1, b1, a0, b0);
     }
 
-    // bias, round, store.  acc[i][j] is the transposed 32 x 32 tile: lane l holds output row
-    // 32 i + l % 32 and, in registers 4 q .. 4 q + 3, output columns 32 j + 8 q + 4 (l / 32) + 0..3.
-    // The buffer's range ends at the last valid row, so stores of rows past a ragged M are dropped.
+    // acc[i][j] is the transposed 32 x 32 tile: lane l holds output row 32 i + l % 32 and, in
+    // registers 4 q .. 4 q + 3, output columns 32 j + 8 q + 4 (l / 32) + 0..3.  Buffer ranges end at
+    // the last valid row, so stores of rows past a ragged M are dropped.
+    const int ncol = 128 * wn + 4 * (lane >> 5);
+    const int mrow = 128 * wm + (lane & 31);
+    if constexpr (kSplitK) {
+        // fp32 partial sums of this split, [ks][M][Ntot], four columns per 16-byte store
+        const int ntot = g.ntn * kBN;
+        float* P = g.part + ((size_t)ks * g.M + m0) * ntot + n0;
+        const __amdgpu_buffer_rsrc_t rp = make_rsrc_n(P, (uint32_t)(rows * ntot * 4));
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const f32x16& t = acc[i][j];
+                    const f32x4 v = {t[4 * q], t[4 * q + 1], t[4 * q + 2], t[4 * q + 3]};
+                    const int off = ((mrow + 32 * i) * ntot + ncol + 32 * j + 8 * q) * 4;
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rp, off,
+                                                           0, 0);
+                }
+        return;
+    }
+    // bias, round, store
     const uint16_t* bias = static_cast<const uint16_t*>(g.b[seg]);
     const int ldc = g.Nw[seg];
     uint16_t* C = static_cast<uint16_t*>(g.C[seg]) + (size_t)m0 * ldc + nl0;
     const __amdgpu_buffer_rsrc_t rc = make_rsrc_n(C, (uint32_t)(rows * ldc * 2));
-    const int ncol = 128 * wn + 4 * (lane >> 5);
-    const int mrow = 128 * wm + (lane & 31);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         uint2 bw[4];
@@ -266,7 +293,62 @@ __global__ void __launch_bounds__(kThreads, 1) proj_gemm_kernel(ProjGemmArgs g) 
     }
 }
 
+// C = bias + the sum of the K splits' partials, in split order; eight columns per thread (a
+// segment's columns are a multiple of the tile width, so eight never straddle two segments).
+__global__ void __launch_bounds__(256) proj_splitk_reduce_kernel(ProjGemmArgs g) {
+    const int ntot = g.ntn * kBN, n8 = ntot / 8;
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (size_t)g.M * n8) return;
+    const int m = (int)(i / n8), n = (int)(i % n8) * 8;
+    const int seg = n < g.Nw[0] ? 0 : (n < g.Nw[0] + g.Nw[1] ? 1 : 2);
+    const int nl = n - (seg > 0 ? g.Nw[0] : 0) - (seg > 1 ? g.Nw[1] : 0);
+    float v[8];
+    const uint16_t* bias = static_cast<const uint16_t*>(g.b[seg]);
+    if (bias) {
+        const uint4 b = *reinterpret_cast<const uint4*>(bias + nl);
+        const uint32_t w[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[2 * k] = bf_lo(w[k]);
+            v[2 * k + 1] = bf_hi(w[k]);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = 0.0f;
+    }
+    // the bias joins first: the partials are then added in split order, as one GEMM adds k-steps
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int s = 0; s < g.ksplit; ++s) {
+        const float4* p = reinterpret_cast<const float4*>(g.part + ((size_t)s * g.M + m) * ntot + n);
+        const float4 x = p[0], y = p[1];
+        acc[0] += x.x; acc[1] += x.y; acc[2] += x.z; acc[3] += x.w;
+        acc[4] += y.x; acc[5] += y.y; acc[6] += y.z; acc[7] += y.w;
+    }
+    uint16_t* C = static_cast<uint16_t*>(g.C[seg]) + (size_t)m * g.Nw[seg] + nl;
+    *reinterpret_cast<uint4*>(C) = make_uint4(pack2bf(acc[0] + v[0], acc[1] + v[1]),
+                                              pack2bf(acc[2] + v[2], acc[3] + v[3]),
+                                              pack2bf(acc[4] + v[4], acc[5] + v[5]),
+                                              pack2bf(acc[6] + v[6], acc[7] + v[7]));
+}
+
+// K splits for a shape: enough blocks to cover the chip (about 240) when the tiles alone do
+// not, each split a multiple of 128 of K.
+int choose_ksplit(int M, int Ntot, int K) {
+    const long long tiles = (long long)((M + kBM - 1) / kBM) * (Ntot / kBN);
+    if (tiles <= 0 || tiles >= 240) return 1;
+    const int want = (int)((240 + tiles - 1) / tiles), units = K / 128;
+    int best = 1;
+    for (int s = 1; s <= units && s <= want; ++s)
+        if (units % s == 0) best = s;
+    return best;
+}
+
 }  // namespace
+
+size_t proj_gemm_part_bytes(int M, int Ntot, int K) {
+    const int s = choose_ksplit(M, Ntot, K);
+    return s > 1 ? (size_t)s * M * Ntot * sizeof(float) : 0;
+}
 
 hipError_t launch_proj_gemm(const ProjGemmArgs& a_in, hipStream_t s) {
     ProjGemmArgs a = a_in;
@@ -274,7 +356,21 @@ hipError_t launch_proj_gemm(const ProjGemmArgs& a_in, hipStream_t s) {
     a.ntn = (a.Nw[0] + a.Nw[1] + a.Nw[2]) / kBN;
     const long long tiles = (long long)a.ntm * a.ntn;
     if (tiles <= 0) return hipSuccess;
-    hipLaunchKernelGGL(proj_gemm_kernel, dim3((unsigned)tiles), dim3(kThreads), 0, s, a);
+    a.ksplit = 1;
+    if (a.part) {
+        const int ks = choose_ksplit(a.M, a.ntn * kBN, a.K);
+        if (ks > 1 && (size_t)ks * a.M * a.ntn * kBN * sizeof(float) <= a.part_bytes) a.ksplit = ks;
+    }
+    if (a.ksplit > 1)
+        hipLaunchKernelGGL(proj_gemm_kernel<true>, dim3((unsigned)(tiles * a.ksplit)),
+                           dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL(proj_gemm_kernel<false>, dim3((unsigned)tiles), dim3(kThreads), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.ksplit == 1) return e;
+    const size_t n = (size_t)a.M * a.ntn * kBN / 8;
+    hipLaunchKernelGGL(proj_splitk_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                       s, a);
     return hipGetLastError();
 }
 

@@ -393,6 +393,34 @@ int rglru_attention_layer_prefill(const rglru_attn_params *a, const rglru_norm_p
                                   void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * Decode step of the residual layer around the recurrent block: one token for each of N
+ * sequences, the block's state carried in h [N][D] (fp32) and conv_state [N][3][D] (bf16) as in
+ * rglru_decode_step.  x_t, out_t [N][D_model] (bf16).  The projections run as GEMMs over the N
+ * rows.  workspace: at least rglru_recurrent_layer_decode_workspace_bytes(N, D, D_model, F), no
+ * initialisation needed.  out_t must not overlap x_t; nothing else may overlap.
+ */
+size_t rglru_recurrent_layer_decode_workspace_bytes(int32_t N, int32_t D, int32_t D_model,
+                                                    int32_t F);
+int rglru_recurrent_layer_decode(const rglru_params *p, const rglru_proj_params *q,
+                                 const rglru_norm_params *nrm, const rglru_mlp_params *m,
+                                 int32_t N, const void *x_t, void *out_t, float *h,
+                                 void *conv_state, void *workspace, size_t ws_bytes,
+                                 void *stream);
+
+/*
+ * Decode step of the residual layer around the local-attention block: one token for each of N
+ * sequences at positions pos [N] (device int32), with the ring caches of
+ * rglru_local_attention_decode (n_heads <= 16).  x_t, out_t [N][D_model].  workspace: at least
+ * rglru_attention_layer_decode_workspace_bytes(a, N, F), no initialisation needed.
+ */
+size_t rglru_attention_layer_decode_workspace_bytes(const rglru_attn_params *a, int32_t N,
+                                                    int32_t F);
+int rglru_attention_layer_decode(const rglru_attn_params *a, const rglru_norm_params *nrm,
+                                 const rglru_mlp_params *m, int32_t N, const int32_t *pos,
+                                 const void *x_t, void *out_t, void *kcache, void *vcache,
+                                 void *workspace, size_t ws_bytes, void *stream);
+
+/*
  * Diagnostics of a prefill workspace: copies its error flags to *flags_out (0 = none) and
  * clears them.  Synchronous (waits for `stream`).  Bit 0: a carry wait exceeded its bound
  * (the affected outputs are NaN).  Bit 1: a wait for a predecessor's inclusive word before

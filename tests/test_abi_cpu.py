@@ -448,3 +448,33 @@ def test_layer_validation(lib):
         assert fr(n=_norms(eps=float("nan"))) == SHAPE
         assert fr(nb=wr - 1) == WS
         assert fr(o=NX) == ALIAS
+
+
+def test_layer_decode_validation(lib):
+    p, q, m, n = _params(D=512, H=2, dtype=1), _proj(Dm=512), _mlp(Dm=512), _norms()
+    N = 4
+    wr = lib.rglru_recurrent_layer_decode_workspace_bytes(N, 512, 512, 768)
+    r256 = lambda v: (v + 255) // 256 * 256
+    base = r256(3 * r256(N * 512 * 2) + r256(lib.rglru_decode_workspace_bytes(N, 512, 1))) \
+        + 3 * r256(N * 512 * 2) + lib.rglru_mlp_workspace_bytes(N, 768)
+    # plus fp32 partial sums for the projections' split K: at most 4 splits of K = 512 for the
+    # widest GEMM (gate|up, 1536 columns) over N rows
+    assert base < wr <= base + r256(4 * N * 1536 * 4) and (wr - base) % 256 == 0
+    fr = lambda n=n, x=NX, o=NO, hh=NH, c=NR, nb=wr: lib.rglru_recurrent_layer_decode(
+        ctypes.byref(p), ctypes.byref(q), n if n is None else ctypes.byref(n), ctypes.byref(m),
+        N, x, o, hh, c, 0x4000000000, nb, None)
+    assert fr(n=None) == NULL
+    assert fr(hh=None) == NULL
+    assert fr(nb=wr - 1) == WS
+    assert fr(o=NX) == ALIAS
+    assert fr(c=0x3000000000) == ALIAS                       # conv state over gate_w
+    a = _attn_params(Dm=512, Hq=2, window=64)
+    wa = lib.rglru_attention_layer_decode_workspace_bytes(ctypes.byref(a), N, 768)
+    assert wa > 0 and lib.rglru_attention_layer_decode_workspace_bytes(ctypes.byref(a), 0, 768) == 0
+    fa = lambda a=a, pos=DP, o=NO, kc=DKC, vc=DVC, nb=wa: lib.rglru_attention_layer_decode(
+        ctypes.byref(a), ctypes.byref(n), ctypes.byref(m), N, pos, NX, o, kc, vc, 0x4000000000,
+        nb, None)
+    assert fa(pos=None) == NULL
+    assert fa(a=_attn_params(Dm=512, Hq=17)) == SHAPE           # decode takes 16 heads at most
+    assert fa(nb=wa - 1) == WS
+    assert fa(o=DKC) == ALIAS                                   # out over the key cache

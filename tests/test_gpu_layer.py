@@ -232,3 +232,66 @@ def test_layers_2b_batched_full_size_sampled():
               % (b, t_use, e, ea))
         assert e <= H.TOL[synth.BF16] and ea <= H.TOL[synth.BF16]
     assert bool(torch.isfinite(out.float()).all()) and bool(torch.isfinite(out_a.float()).all())
+
+
+# ------------------------------------------------------------------------------------------
+# decode steps of the layers: a prefill of T0 tokens, then single-token steps, must give the
+# oracle layer's rows over the whole sequence (the layers are causal)
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("D,nh,Dm,F,N,T0,steps", [
+    (512, 2, 512, 768, 3, 40, 6),
+    (2560, 10, 2560, 7680, 2, 20, 3),     # the 2B widths
+])
+def test_recurrent_layer_decode_continues_prefill(D, nh, Dm, F, N, T0, steps):
+    from gated_linear_recurrence_amd import binding
+    T = T0 + steps
+    w = dataclasses.replace(synth.small(synth.WORKLOADS[synth.PREFILL_2B], B=N, T=T), D=D, H=nh)
+    p, q = synth.make_params(w, biases=True), synth.make_proj(w, Dm=Dm, biases=True)
+    L = synth.make_layer(w, Dm=Dm, F=F, biases=True)
+    x_in = synth.make_block_input(w, Dm=Dm, B=N, T=T)
+    P = H.dev_params(p, w.H)
+    Q = binding.ProjParams(*[H.to_dev(q[k]) for k in ("lx_w", "lx_b", "ly_w", "ly_b",
+                                                      "lo_w", "lo_b")])
+    Nd, Md = _norms_dev(L), _mlp_dev(L)
+    _, h, conv = binding.rglru_recurrent_layer_prefill(P, Q, Nd, Md, H.to_dev(x_in[:, :T0]))
+    outs = []
+    for t in range(T0, T):
+        o = binding.rglru_recurrent_layer_decode(P, Q, Nd, Md, H.to_dev(x_in[:, t].copy()), h, conv)
+        outs.append(H.wide(H.to_host(o)))
+    torch.cuda.synchronize()
+    ref, _, _ = _oracle_recurrent_layer(w, p, q, L, x_in, None, None)
+    got = np.stack(outs, axis=1)
+    e = H.rel_l2(got, ref[:, T0:])
+    print("recurrent layer decode D=%d Dm=%d F=%d N=%d, %d steps after %d: rel-L2 %.3e"
+          % (D, Dm, F, N, steps, T0, e))
+    assert e <= H.TOL[synth.BF16]
+
+
+@pytest.mark.parametrize("Dm,Hq,F,N,W,T0,steps", [
+    (512, 2, 512, 3, 32, 40, 6),          # the ring wraps
+    (2560, 10, 7680, 2, 2048, 20, 3),     # the 2B widths and window
+])
+def test_attention_layer_decode_continues_prefill(Dm, Hq, F, N, W, T0, steps):
+    from gated_linear_recurrence_amd import binding
+    T = T0 + steps
+    w = synth.small(synth.WORKLOADS[synth.PREFILL_2B], B=N, T=T)
+    a = synth.make_attn(w, Dm=Dm, n_heads=Hq, bias=True)
+    L = synth.make_layer(w, Dm=Dm, F=F, biases=True)
+    x_in = synth.make_block_input(w, Dm=Dm, B=N, T=T)
+    A = binding.AttnParams(H.to_dev(a["q_w"]), H.to_dev(a["k_w"]), H.to_dev(a["v_w"]),
+                           H.to_dev(a["o_w"]), H.to_dev(a["o_b"]), Hq, W)
+    Nd, Md = _norms_dev(L), _mlp_dev(L)
+    cache = binding.AttnCache(N, W, "cuda")
+    binding.rglru_attention_layer_prefill(A, Nd, Md, H.to_dev(x_in[:, :T0]), cache=cache)
+    outs = []
+    for t in range(T0, T):
+        pos = torch.full((N,), t, dtype=torch.int32, device="cuda")
+        o = binding.rglru_attention_layer_decode(A, Nd, Md, pos, H.to_dev(x_in[:, t].copy()), cache)
+        outs.append(H.wide(H.to_host(o)))
+    torch.cuda.synchronize()
+    ref = _oracle_attention_layer(a, L, x_in, Hq, W)
+    got = np.stack(outs, axis=1)
+    e = H.rel_l2(got, ref[:, T0:])
+    print("attention layer decode Dm=%d Hq=%d F=%d N=%d W=%d, %d steps after %d: rel-L2 %.3e"
+          % (Dm, Hq, F, N, W, steps, T0, e))
+    assert e <= H.TOL[synth.BF16]
