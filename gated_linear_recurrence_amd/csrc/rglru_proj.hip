@@ -32,6 +32,7 @@ typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
 constexpr int kBM = 256;                    // tile rows (M)
 constexpr int kBN = 256;                    // tile columns (N)
 constexpr int kBK = 64;                     // K per stage
+constexpr int kSkinnyRows = 64;             // at most this many rows: skinny_gemm_kernel
 constexpr int kThreads = 256;               // 4 waves, 2 x 2 over the tile
 constexpr int kChunks = kBK / 8;            // 16-byte chunks per tile row
 constexpr int kRowBytes = kBK * 2;
@@ -331,6 +332,68 @@ __global__ void __launch_bounds__(256) proj_splitk_reduce_kernel(ProjGemmArgs g)
                                               pack2bf(acc[6] + v[6], acc[7] + v[7]));
 }
 
+// Few rows (decode: one row per sequence).  One workgroup per 16 output features: the weight
+// rows are the A operand of v_mfma_f32_16x16x32_bf16 (16 features x 32 k, each lane 16 bytes of
+// one row) and up to 64 input rows the B operand in blocks of 16 columns, so each weight byte
+// is read once and no MFMA work is spent on rows that do not exist.  The eight waves take an
+// eighth of K each, with eight weight loads in flight per wave (a few waves per CU must keep
+// enough bytes in flight to stream the weights); their tiles are added in wave order through
+// LDS.
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+constexpr int kSkinnyWaves = 8;
+template <int NB>   // blocks of 16 input rows: M <= 16 NB
+__global__ void __launch_bounds__(64 * kSkinnyWaves) skinny_gemm_kernel(ProjGemmArgs g) {
+    __shared__ f32x4 red[kSkinnyWaves][NB][64];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n0 = blockIdx.x * 16;
+    const int seg = n0 < g.Nw[0] ? 0 : (n0 < g.Nw[0] + g.Nw[1] ? 1 : 2);
+    const int nl0 = n0 - (seg > 0 ? g.Nw[0] : 0) - (seg > 1 ? g.Nw[1] : 0);
+    const int K = g.K, kq = K / kSkinnyWaves, g16 = lane >> 4;   // kq % 32 == 0
+    const uint16_t* W = static_cast<const uint16_t*>(g.W[seg]) + (size_t)(nl0 + (lane & 15)) * K;
+    const uint16_t* X = static_cast<const uint16_t*>(g.A);
+    int xr[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) xr[b] = min(16 * b + (lane & 15), g.M - 1);
+    f32x4 acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    const int kb = wv * kq + 8 * g16, ke = (wv + 1) * kq;
+#pragma unroll 8
+    for (int k = kb; k < ke; k += 32) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(W + k);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            // rows past M repeat the last row; their columns are never stored
+            const bf16x8 x = *reinterpret_cast<const bf16x8*>(X + (size_t)xr[b] * K + k);
+            acc[b] = mfma16(a, x, acc[b]);
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) red[wv][b][lane] = acc[b];
+    __syncthreads();
+    if (tid >= NB * 64) return;
+    // lane l of block b: input row 16 b + l % 16, features 4 (l / 16) .. + 3
+    const int b = tid >> 6, l = tid & 63, m = 16 * b + (l & 15);
+    if (m >= g.M) return;
+    f32x4 t = red[0][b][l];
+#pragma unroll
+    for (int w = 1; w < kSkinnyWaves; ++w) t += red[w][b][l];
+    const int n = nl0 + 4 * (l >> 4);
+    const uint16_t* bias = static_cast<const uint16_t*>(g.b[seg]);
+    float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (bias) {
+        const uint2 bw = *reinterpret_cast<const uint2*>(bias + n);
+        bv[0] = bf_lo(bw.x); bv[1] = bf_hi(bw.x); bv[2] = bf_lo(bw.y); bv[3] = bf_hi(bw.y);
+    }
+    uint16_t* C = static_cast<uint16_t*>(g.C[seg]) + (size_t)m * g.Nw[seg] + n;
+    *reinterpret_cast<uint2*>(C) = make_uint2(pack2bf(t[0] + bv[0], t[1] + bv[1]),
+                                              pack2bf(t[2] + bv[2], t[3] + bv[3]));
+}
+
 // K splits for a shape: enough blocks to cover the chip (about 240) when the tiles alone do
 // not, each split a multiple of 128 of K.
 int choose_ksplit(int M, int Ntot, int K) {
@@ -346,6 +409,7 @@ int choose_ksplit(int M, int Ntot, int K) {
 }  // namespace
 
 size_t proj_gemm_part_bytes(int M, int Ntot, int K) {
+    if (M <= kSkinnyRows && K % (32 * kSkinnyWaves) == 0) return 0;
     const int s = choose_ksplit(M, Ntot, K);
     return s > 1 ? (size_t)s * M * Ntot * sizeof(float) : 0;
 }
@@ -357,6 +421,17 @@ hipError_t launch_proj_gemm(const ProjGemmArgs& a_in, hipStream_t s) {
     const long long tiles = (long long)a.ntm * a.ntn;
     if (tiles <= 0) return hipSuccess;
     a.ksplit = 1;
+    // the skinny kernel's waves each take whole 32-wide steps of K: K % (32 * waves) == 0
+    if (a.M <= kSkinnyRows && a.K % (32 * kSkinnyWaves) == 0) {
+        const unsigned blocks = (unsigned)(a.ntn * kBN / 16);
+        switch ((a.M + 15) / 16) {
+            case 1: hipLaunchKernelGGL(skinny_gemm_kernel<1>, dim3(blocks), dim3(512), 0, s, a); break;
+            case 2: hipLaunchKernelGGL(skinny_gemm_kernel<2>, dim3(blocks), dim3(512), 0, s, a); break;
+            case 3: hipLaunchKernelGGL(skinny_gemm_kernel<3>, dim3(blocks), dim3(512), 0, s, a); break;
+            default: hipLaunchKernelGGL(skinny_gemm_kernel<4>, dim3(blocks), dim3(512), 0, s, a);
+        }
+        return hipGetLastError();
+    }
     if (a.part) {
         const int ks = choose_ksplit(a.M, a.ntn * kBN, a.K);
         if (ks > 1 && (size_t)ks * a.M * a.ntn * kBN * sizeof(float) <= a.part_bytes) a.ksplit = ks;

@@ -457,9 +457,10 @@ def test_layer_decode_validation(lib):
     r256 = lambda v: (v + 255) // 256 * 256
     base = r256(3 * r256(N * 512 * 2) + r256(lib.rglru_decode_workspace_bytes(N, 512, 1))) \
         + 3 * r256(N * 512 * 2) + lib.rglru_mlp_workspace_bytes(N, 768)
-    # plus fp32 partial sums for the projections' split K: at most 4 splits of K = 512 for the
+    # plus fp32 partial sums for the projections' split K (none at 64 rows or fewer, which take
+    # the skinny kernel): at most 4 splits of K = 512 for the
     # widest GEMM (gate|up, 1536 columns) over N rows
-    assert base < wr <= base + r256(4 * N * 1536 * 4) and (wr - base) % 256 == 0
+    assert base <= wr <= base + r256(4 * N * 1536 * 4) and (wr - base) % 256 == 0
     fr = lambda n=n, x=NX, o=NO, hh=NH, c=NR, nb=wr: lib.rglru_recurrent_layer_decode(
         ctypes.byref(p), ctypes.byref(q), n if n is None else ctypes.byref(n), ctypes.byref(m),
         N, x, o, hh, c, 0x4000000000, nb, None)
