@@ -92,6 +92,8 @@ def _bind(lib):
     lib.oracle_local_mqa.restype = I
     lib.oracle_local_attention_block.argtypes = [I, I, I, I, I, I, I, I, D_] + [P] * 7 + [I]
     lib.oracle_local_attention_block.restype = I
+    lib.oracle_prefill_backward.argtypes = [I, I, I, I, I] + [P] * 24
+    lib.oracle_prefill_backward.restype = I
     lib.oracle_rmsnorm.argtypes = [I, I, I, I, P, P, D_, P]
     lib.oracle_rmsnorm.restype = I
     lib.oracle_mlp.argtypes = [I, I, I, I, I] + [P] * 8 + [I]
@@ -305,6 +307,34 @@ def block_prefill(p: Params, q: ProjParams, x_in, h0=None, conv0=None, nthreads:
                                   int(nthreads))
     _check(st, "oracle_block_prefill")
     return out, h_last, conv_last
+
+
+def prefill_backward(p: Params, x, y, dout, h0=None, conv0=None, dh_last=None, lib=None) -> dict:
+    """Gradients of L = sum(dout * out) + sum(dh_last * h_last) for the path over x, y
+    [B, T, D] (storage), dout [B, T, D] and dh_last [B, D] (fp64 or None).  Returns a dict of
+    fp64 arrays: dx, dy, dconv_w [D,4], dconv_b, dwa, dwx [H,bs,bs], dba, dbx, dlambda [D],
+    dh0 [B,D], dconv0 [B,3,D]."""
+    lib = lib or load()
+    x = _c(x, p.conv_w.dtype)
+    y = _c(y, p.conv_w.dtype)
+    B, T, D = x.shape
+    h0 = _c(h0, np.float32)
+    conv0 = _c(conv0, p.conv_w.dtype)
+    dout = _c(np.asarray(dout, np.float64), np.float64)
+    dh_last = _c(np.asarray(dh_last, np.float64), np.float64) if dh_last is not None else None
+    bs = D // p.H
+    g = {"dx": np.empty((B, T, D)), "dy": np.empty((B, T, D)), "dconv_w": np.empty((D, 4)),
+         "dconv_b": np.empty(D), "dwa": np.empty((p.H, bs, bs)), "dba": np.empty(D),
+         "dwx": np.empty((p.H, bs, bs)), "dbx": np.empty(D), "dlambda": np.empty(D),
+         "dh0": np.empty((B, D)), "dconv0": np.empty((B, 3, D))}
+    cw, cb, wa, ba, wx, bx, lam = p.args()
+    st = lib.oracle_prefill_backward(p.dtype, B, T, D, p.H, _ptr(x), _ptr(y), cw, cb, wa, ba, wx,
+                                     bx, lam, _ptr(h0), _ptr(conv0), _ptr(dout), _ptr(dh_last),
+                                     *[_ptr(g[k]) for k in ("dx", "dy", "dconv_w", "dconv_b",
+                                                            "dwa", "dba", "dwx", "dbx", "dlambda",
+                                                            "dh0", "dconv0")])
+    _check(st, "oracle_prefill_backward")
+    return g
 
 
 def rope(v, pos, base: float = 10000.0, lib=None):

@@ -615,3 +615,149 @@ int oracle_mlp(int xdtype, int wdtype, int rows, int Dm, int F, const void *x, c
     free(gt);
     return 0;
 }
+
+/* ======================================================================================
+ * Backward pass of the path (for training).  The pages give no training detail; the
+ * gradients are those of the forward definition above, by the chain rule, for the loss
+ *   L = sum_t dout_t . out_t + dh_last . h_T-1
+ * (dh_last may be absent).  Per (sequence, head) the forward is re-run keeping u, r, i, a, m
+ * and h for every token; then time runs backwards:
+ *   dh_t   = dh_{t+1} a_{t+1} + dout_t gelu(y_t)            (carry of the state gradient)
+ *   dy_t   = dout_t h_t gelu'(y_t)
+ *   v_t    = m_t i_t u_t:   du += dh m i,  dm = dh i u,  di = dh m u
+ *   a_t    = sigma(L)^(8 r):  da = dh h_{t-1} - dm a / m,  dr = da a 8 log sigma(L),
+ *            dL += da a 8 r (1 - sigma(L))
+ *   r = sigma(W_a u + b_a), i = sigma(W_x u + b_x): dRpre = dr r (1 - r), dIpre = di i (1 - i),
+ *            du += W_a^T dRpre + W_x^T dIpre, dW += dRpre u^T, db += dRpre
+ *   u_t = conv_b + sum_j w_j x~_{t-3+j}:  dconv_b += du, dw_j += du x~_{t-3+j},
+ *            dx~_{t-3+j} += du w_j (the three positions before 0 are the conv0 window)
+ *   dh0 = the state gradient carried past t = 0.
+ * All outputs are fp64 and fully written (accumulated from zero).
+ * ====================================================================================== */
+static double gelu_tanh_grad(double y) {
+    const double k = sqrt(2.0 / 3.14159265358979323846);
+    const double z = k * (y + 0.044715 * y * y * y);
+    const double th = tanh(z);
+    return 0.5 * (1.0 + th) + 0.5 * y * (1.0 - th * th) * k * (1.0 + 3.0 * 0.044715 * y * y);
+}
+
+int oracle_prefill_backward(int dtype, int B, int T, int D, int H, const void *x, const void *y,
+                            const void *conv_w, const void *conv_b, const void *wa,
+                            const void *ba, const void *wx, const void *bx, const float *lambda,
+                            const float *h0, const void *conv0, const double *dout,
+                            const double *dh_last, double *dx, double *dy, double *dconv_w,
+                            double *dconv_b, double *dwa, double *dba, double *dwx, double *dbx,
+                            double *dlambda, double *dh0, double *dconv0) {
+    prm_t p;
+    int st = make_prm(&p, dtype, D, H, conv_w, conv_b, wa, ba, wx, bx, lambda);
+    if (st) return st;
+    if (B < 1 || T < 0) return 2;
+    if (!dout || !dx || !dy || !dconv_w || !dconv_b || !dwa || !dba || !dwx || !dbx ||
+        !dlambda || !dh0 || !dconv0)
+        return 1;
+    if (T > 0 && (!x || !y)) return 1;
+    const int bs = p.bs;
+    const size_t BTD = (size_t)B * T * D;
+    memset(dx, 0, sizeof(double) * BTD);
+    memset(dy, 0, sizeof(double) * BTD);
+    memset(dconv_w, 0, sizeof(double) * (size_t)D * 4);
+    memset(dconv_b, 0, sizeof(double) * (size_t)D);
+    memset(dwa, 0, sizeof(double) * (size_t)H * bs * bs);
+    memset(dwx, 0, sizeof(double) * (size_t)H * bs * bs);
+    memset(dba, 0, sizeof(double) * (size_t)D);
+    memset(dbx, 0, sizeof(double) * (size_t)D);
+    memset(dlambda, 0, sizeof(double) * (size_t)D);
+    memset(dconv0, 0, sizeof(double) * (size_t)B * 3 * D);
+    /* per-token values of one unit: window (3 per token), u, r, i, a, m, h, the two gate
+     * pre-activations; then the state gradient and three per-channel scratch rows */
+    const size_t per = (size_t)(T + 1) * bs;
+    double *xw = (double *)malloc(sizeof(double) * (11 * per + 4 * (size_t)bs + 1));
+    if (!xw) return 1;
+    double *u = xw + 3 * per, *r = u + per, *ig = r + per, *a = ig + per, *m = a + per;
+    double *h = m + per;            /* h[(t + 1) * bs + c], h[c] = h0 */
+    double *ra = h + per, *ri = ra + per;
+    double *dh = ri + per, *dra = dh + bs, *dia = dra + bs, *duv = dia + bs;
+    for (int b = 0; b < B; ++b) {
+        for (int hd = 0; hd < H; ++hd) {
+            double win[3 * 256];
+            if (bs > 256) {
+                free(xw);
+                return 3;
+            }
+            init_state(&p, b, hd, h0, conv0, h, win);   /* h[0..bs), win[j * bs + c] */
+            for (int t = 0; t < T; ++t) {
+                for (int c = 0; c < bs; ++c) {
+                    const size_t ch = (size_t)hd * bs + c;
+                    const double xt = widen(x, ((size_t)b * T + t) * D + ch, p.xdtype);
+                    double w3[3] = {win[c], win[bs + c], win[2 * bs + c]};
+                    xw[((size_t)t * bs + c) * 3 + 0] = w3[0];
+                    xw[((size_t)t * bs + c) * 3 + 1] = w3[1];
+                    xw[((size_t)t * bs + c) * 3 + 2] = w3[2];
+                    u[(size_t)t * bs + c] = conv_step(&p, (int)ch, w3, xt);
+                    win[c] = w3[0];
+                    win[bs + c] = w3[1];
+                    win[2 * bs + c] = w3[2];
+                }
+                gate_preacts(&p, hd, u + (size_t)t * bs, ra + (size_t)t * bs, ri + (size_t)t * bs);
+                for (int c = 0; c < bs; ++c) {
+                    const size_t k = (size_t)t * bs + c, ch = (size_t)hd * bs + c;
+                    r[k] = sigmoid(ra[k]);
+                    ig[k] = sigmoid(ri[k]);
+                    a[k] = pow(sigmoid((double)lambda[ch]), 8.0 * r[k]);
+                    m[k] = sqrt(1.0 - a[k] * a[k]);
+                    h[k + bs] = a[k] * h[k] + m[k] * (ig[k] * u[k]);
+                }
+            }
+            for (int c = 0; c < bs; ++c)
+                dh[c] = dh_last ? dh_last[(size_t)b * D + (size_t)hd * bs + c] : 0.0;
+            for (int t = T - 1; t >= 0; --t) {
+                for (int c = 0; c < bs; ++c) {
+                    const size_t k = (size_t)t * bs + c, ch = (size_t)hd * bs + c;
+                    const size_t o = ((size_t)b * T + t) * D + ch;
+                    const double yt = widen(y, o, p.xdtype);
+                    const double g = dh[c] + dout[o] * oracle_gelu_tanh(yt);
+                    dy[o] = dout[o] * h[k + bs] * gelu_tanh_grad(yt);
+                    duv[c] = g * m[k] * ig[k];
+                    const double dm = g * ig[k] * u[k];
+                    const double di = g * m[k] * u[k];
+                    const double da = g * h[k] - dm * a[k] / m[k];
+                    const double sg = sigmoid((double)lambda[ch]);
+                    dlambda[ch] += da * a[k] * 8.0 * r[k] * (1.0 - sg);
+                    const double dr = da * a[k] * 8.0 * log(sg);
+                    dra[c] = dr * r[k] * (1.0 - r[k]);
+                    dia[c] = di * ig[k] * (1.0 - ig[k]);
+                    dh[c] = g * a[k];
+                }
+                for (int j = 0; j < bs; ++j) {
+                    const size_t ch = (size_t)hd * bs + j;
+                    dba[ch] += dra[j];
+                    dbx[ch] += dia[j];
+                    for (int kk = 0; kk < bs; ++kk) {
+                        const size_t widx = ((size_t)hd * bs + j) * bs + kk;
+                        dwa[widx] += dra[j] * u[(size_t)t * bs + kk];
+                        dwx[widx] += dia[j] * u[(size_t)t * bs + kk];
+                        duv[kk] += widen(p.wa, widx, p.dtype) * dra[j] +
+                                   widen(p.wx, widx, p.dtype) * dia[j];
+                    }
+                }
+                for (int c = 0; c < bs; ++c) {
+                    const size_t ch = (size_t)hd * bs + c;
+                    const double du = duv[c];
+                    dconv_b[ch] += du;
+                    for (int j = 0; j < 4; ++j) {
+                        const double xv = j < 3 ? xw[((size_t)t * bs + c) * 3 + j]
+                                                : widen(x, ((size_t)b * T + t) * D + ch, p.xdtype);
+                        dconv_w[ch * 4 + j] += du * xv;
+                        const double gx = du * widen(p.conv_w, ch * 4 + j, p.dtype);
+                        const int pos = t - 3 + j;
+                        if (pos >= 0) dx[((size_t)b * T + pos) * D + ch] += gx;
+                        else dconv0[((size_t)b * 3 + (pos + 3)) * D + ch] += gx;
+                    }
+                }
+            }
+            for (int c = 0; c < bs; ++c) dh0[(size_t)b * D + (size_t)hd * bs + c] = dh[c];
+        }
+    }
+    free(xw);
+    return 0;
+}

@@ -805,6 +805,65 @@ def _pin_residual_layer_composition(lib):
 
 
 # ----------------------------------------------------------------------------------------------
+# backward pass of the path
+# ----------------------------------------------------------------------------------------------
+def _pin_backward_finite_differences(lib):
+    """The backward oracle against central differences of the (pinned) forward oracle, for
+    L = sum(dout * out) + sum(dh_last * h_last), on a tiny block (D = 8, two heads of 4, six
+    tokens, with state), at three sampled elements of each of the eleven inputs.  fp32
+    storage; the step is 1e-3 and the difference is divided by the exact step between the two
+    fp32 values, so the truncation error (~1e-7 relative) stays far below the bar (2e-5).
+    Also: the gradients are linear in (dout, dh_last), exactly so under doubling, and vanish
+    with them."""
+    rng = np.random.default_rng(11)
+    B, T, D, H = 2, 6, 8, 2
+    bs = D // H
+
+    def f(*s, sc=1.0):
+        return (rng.standard_normal(s) * sc).astype(np.float32)
+
+    lam = np.log(rng.uniform(0.9, 0.99, D) / (1 - rng.uniform(0.9, 0.99, D))).astype(np.float32)
+    ins = {"conv_w": f(D, 4, sc=0.5), "conv_b": f(D, sc=0.3), "wa": f(H, bs, bs, sc=0.5),
+           "ba": f(D, sc=0.3), "wx": f(H, bs, bs, sc=0.5), "bx": f(D, sc=0.3), "lambda": lam,
+           "x": f(B, T, D), "y": f(B, T, D), "h0": f(B, D, sc=0.3), "conv0": f(B, 3, D)}
+    dout = rng.standard_normal((B, T, D))
+    dhl = rng.standard_normal((B, D))
+
+    def params(v):
+        return oracle.Params(v["conv_w"], v["conv_b"], v["wa"], v["ba"], v["wx"], v["bx"],
+                             v["lambda"], H)
+
+    def loss(v):
+        o, hl, _ = oracle.prefill(params(v), v["x"], v["y"], h0=v["h0"], conv0=v["conv0"], lib=lib)
+        return float((o * dout).sum() + (hl * dhl).sum())
+
+    g = oracle.prefill_backward(params(ins), ins["x"], ins["y"], dout, h0=ins["h0"],
+                                conv0=ins["conv0"], dh_last=dhl, lib=lib)
+    names = {"conv_w": "dconv_w", "conv_b": "dconv_b", "wa": "dwa", "ba": "dba", "wx": "dwx",
+             "bx": "dbx", "lambda": "dlambda", "x": "dx", "y": "dy", "h0": "dh0",
+             "conv0": "dconv0"}
+    for name, gname in names.items():
+        a = ins[name]
+        for idx in [tuple(rng.integers(0, n) for n in a.shape) for _ in range(3)]:
+            vp = {k: v.copy() for k, v in ins.items()}
+            vm = {k: v.copy() for k, v in ins.items()}
+            vp[name][idx] += np.float32(1e-3)
+            vm[name][idx] -= np.float32(1e-3)
+            step = float(vp[name][idx]) - float(vm[name][idx])
+            fd = (loss(vp) - loss(vm)) / step
+            an = g[gname][idx]
+            assert abs(fd - an) <= 2e-5 * abs(an) + 1e-6, (name, idx, fd, an)
+    g2 = oracle.prefill_backward(params(ins), ins["x"], ins["y"], 2 * dout, h0=ins["h0"],
+                                 conv0=ins["conv0"], dh_last=2 * dhl, lib=lib)
+    for k in g:
+        assert np.array_equal(g2[k], 2 * g[k]), k
+    g0 = oracle.prefill_backward(params(ins), ins["x"], ins["y"], np.zeros_like(dout),
+                                 h0=ins["h0"], conv0=ins["conv0"], lib=lib)
+    for k in g0:
+        assert not np.any(g0[k]), k
+
+
+# ----------------------------------------------------------------------------------------------
 # planted mistakes: each plausible error in the oracle must fail at least one pin
 # ----------------------------------------------------------------------------------------------
 PINS = [
@@ -816,6 +875,7 @@ PINS = [
     _pin_rope_complex, _pin_rope_relative, _pin_mqa_closed_forms, _pin_mqa_invariants,
     _pin_attention_block_composition,
     _pin_rmsnorm_closed_forms, _pin_mlp_integer_exact, _pin_residual_layer_composition,
+    _pin_backward_finite_differences,
 ]
 
 MUTANTS = {
@@ -871,6 +931,16 @@ MUTANTS = {
                               "gt[i] = oracle_gelu_tanh(gt[i]);"),
     "mlp down bias dropped": ("linear_rows(rows, F, Dm, gt, ORACLE_F64, dw, db, wdtype, out);",
                               "linear_rows(rows, F, Dm, gt, ORACLE_F64, dw, NULL, wdtype, out);"),
+    "backward carry without the decay": ("dh[c] = g * a[k];", "dh[c] = g;"),
+    "backward drops the normaliser's decay term": ("const double da = g * h[k] - dm * a[k] / m[k];",
+                                                   "const double da = g * h[k];"),
+    "backward lambda factor": ("dlambda[ch] += da * a[k] * 8.0 * r[k] * (1.0 - sg);",
+                               "dlambda[ch] += da * a[k] * 8.0 * r[k] * sg;"),
+    "backward gate weights not transposed": (
+        "duv[kk] += widen(p.wa, widx, p.dtype) * dra[j] +",
+        "duv[kk] += widen(p.wa, ((size_t)hd * bs + kk) * bs + j, p.dtype) * dra[j] +"),
+    "backward conv position": ("const int pos = t - 3 + j;", "const int pos = t - j;"),
+    "backward gelu derivative": ("(1.0 + 3.0 * 0.044715 * y * y)", "(1.0 + 0.044715 * y * y)"),
     "block input type ignored": ("linear_rows(T, Dm, DQ, xb, xdtype, wq, NULL, dtype, q);",
                                  "linear_rows(T, Dm, DQ, xb, dtype, wq, NULL, dtype, q);"),
 }
