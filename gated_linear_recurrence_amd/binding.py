@@ -34,7 +34,8 @@ EXPORTS = ["rglru_prefill_workspace_bytes", "rglru_prefill_workspace_init", "rgl
            "rglru_mlp", "rglru_recurrent_layer_workspace_bytes", "rglru_recurrent_layer_prefill",
            "rglru_attention_layer_workspace_bytes", "rglru_attention_layer_prefill",
            "rglru_recurrent_layer_decode_workspace_bytes", "rglru_recurrent_layer_decode",
-           "rglru_attention_layer_decode_workspace_bytes", "rglru_attention_layer_decode"]
+           "rglru_attention_layer_decode_workspace_bytes", "rglru_attention_layer_decode",
+           "rglru_prefill_backward_workspace_bytes", "rglru_prefill_backward"]
 
 _lock = threading.Lock()
 _lib = None
@@ -163,6 +164,10 @@ def load_library(path: str = LIB_PATH):
         lib.rglru_attention_layer_decode_workspace_bytes.restype = SZ
         lib.rglru_attention_layer_decode.argtypes = [AP, NP, MP, I32, P, P, P, P, P, P, SZ, P]
         lib.rglru_attention_layer_decode.restype = ctypes.c_int
+        lib.rglru_prefill_backward_workspace_bytes.argtypes = [I32, I32, I32, I32]
+        lib.rglru_prefill_backward_workspace_bytes.restype = SZ
+        lib.rglru_prefill_backward.argtypes = [PP, I32, I32] + [P] * 18 + [SZ, P]
+        lib.rglru_prefill_backward.restype = ctypes.c_int
         lib.rglru_abi_version.argtypes = []
         lib.rglru_abi_version.restype = ctypes.c_int
         _lib = lib
@@ -742,3 +747,42 @@ def rglru_attention_layer_decode(a: AttnParams, n: NormParams, m: MlpParams, pos
                                           _stream())
     _check(lib, st, "rglru_attention_layer_decode")
     return out
+
+
+def rglru_prefill_backward_workspace_bytes(B: int, T: int, D: int, n_heads: int) -> int:
+    return int(load_library().rglru_prefill_backward_workspace_bytes(B, T, D, n_heads))
+
+
+BACKWARD_GRADS = ("dx", "dy", "dconv_w", "dconv_b", "dwa", "dba", "dwx", "dbx", "dlambda", "dh0",
+                  "dconv0")
+
+
+def rglru_prefill_backward(p: Params, x, y, dout, h0=None, conv0=None, dh_last=None, *,
+                           workspace: DeviceBuffer | None = None) -> dict:
+    """Gradients of sum(dout * out) + sum(dh_last * h_last) for rglru_prefill (bf16, block
+    size 256).  Returns a dict of tensors: dx, dy (bf16, like x); the rest fp32."""
+    lib = load_library()
+    B, T, D = x.shape
+    dev = p.device
+    _need(x, "x", torch.bfloat16, (B, T, p.D), dev)
+    _need(y, "y", torch.bfloat16, (B, T, p.D), dev)
+    _need(dout, "dout", torch.bfloat16, (B, T, p.D), dev)
+    _need(h0, "h0", torch.float32, (B, D), dev)
+    _need(conv0, "conv0", torch.bfloat16, (B, 3, D), dev)
+    _need(dh_last, "dh_last", torch.float32, (B, D), dev)
+    bs = D // p.H
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = {"dx": torch.empty_like(x), "dy": torch.empty_like(y),
+         "dconv_w": torch.empty((D, 4), **f32), "dconv_b": torch.empty((D,), **f32),
+         "dwa": torch.empty((p.H, bs, bs), **f32), "dba": torch.empty((D,), **f32),
+         "dwx": torch.empty((p.H, bs, bs), **f32), "dbx": torch.empty((D,), **f32),
+         "dlambda": torch.empty((D,), **f32), "dh0": torch.empty((B, D), **f32),
+         "dconv0": torch.empty((B, 3, D), **f32)}
+    if workspace is None:
+        workspace = DeviceBuffer(rglru_prefill_backward_workspace_bytes(B, T, D, p.H), dev)
+    st = lib.rglru_prefill_backward(ctypes.byref(p.c), B, T, _ptr(x), _ptr(y), _ptr(h0),
+                                    _ptr(conv0), _ptr(dout), _ptr(dh_last),
+                                    *[_ptr(g[k]) for k in BACKWARD_GRADS], _ptr(workspace.t),
+                                    workspace.nbytes, _stream())
+    _check(lib, st, "rglru_prefill_backward")
+    return g

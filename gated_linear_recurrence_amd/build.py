@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "librglru.so")
 SOURCES = ["rglru_api.hip", "rglru_prefill.hip", "rglru_decode.hip", "rglru_proj.hip",
-           "rglru_attention.hip", "rglru_layer.hip"]
+           "rglru_attention.hip", "rglru_layer.hip", "rglru_backward.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -1040,4 +1040,68 @@ int rglru_attention_layer_decode(const rglru_attn_params* a, const rglru_norm_pa
     });
 }
 
+// ------------------------------------------------------------------------------------------
+// backward pass of the path
+// ------------------------------------------------------------------------------------------
+static bool backward_shape_ok(int32_t B, int32_t T, int32_t D, int32_t n_heads) {
+    return B >= 1 && T >= 64 && n_heads >= 1 && D == 256 * n_heads && T % 64 == 0 &&
+           ((long long)B * T) % 256 == 0 && (long long)B * T < (1LL << 22) &&
+           (long long)B * (T / 64) * D < (1LL << 31);
+}
+
+size_t rglru_prefill_backward_workspace_bytes(int32_t B, int32_t T, int32_t D, int32_t n_heads) {
+    if (!backward_shape_ok(B, T, D, n_heads)) return 0;
+    return backward_workspace_bytes(B, T, D, n_heads);
+}
+
+int rglru_prefill_backward(const rglru_params* p, int32_t B, int32_t T, const void* x,
+                           const void* y, const float* h0, const void* conv0, const void* dout,
+                           const float* dh_last, void* dx, void* dy, float* dconv_w,
+                           float* dconv_b, float* dwa, float* dba, float* dwx, float* dbx,
+                           float* dlambda, float* dh0, float* dconv0, void* workspace,
+                           size_t ws_bytes, void* stream) {
+    int st = check_params(p, true);
+    if (st != RGLRU_OK) return st;
+    if (B < 1 || T < 0) return RGLRU_ERR_SHAPE;
+    if (p->dtype != RGLRU_BF16 || !backward_shape_ok(B, T, p->D, p->n_heads))
+        return RGLRU_ERR_UNSUPPORTED;
+    const void* outs[] = {dx, dy, dconv_w, dconv_b, dwa, dba, dwx, dbx, dlambda, dh0, dconv0};
+    if (!x || !y || !dout) return RGLRU_ERR_NULL;
+    for (const void* o : outs)
+        if (!o) return RGLRU_ERR_NULL;
+    const void* ins[] = {x, y, h0, conv0, dout, dh_last, p->conv_w, p->conv_b, p->gate_a_w,
+                         p->gate_a_b, p->gate_x_w, p->gate_x_b, p->lambda};
+    for (const void* q : ins)
+        if (!aligned16(q)) return RGLRU_ERR_UNSUPPORTED;
+    for (const void* o : outs)
+        if (!aligned16(o)) return RGLRU_ERR_UNSUPPORTED;
+    if (!aligned16(workspace)) return RGLRU_ERR_UNSUPPORTED;
+    const size_t need = rglru_prefill_backward_workspace_bytes(B, T, p->D, p->n_heads);
+    if (!workspace || ws_bytes < need) return RGLRU_ERR_WORKSPACE;
+    const size_t D = p->D, H = p->n_heads, bs = D / H;
+    const size_t act = (size_t)B * T * D * 2, st_b = (size_t)B * D * 4;
+    const size_t olen[] = {act, act, D * 16, D * 4, H * bs * bs * 4, D * 4, H * bs * bs * 4, D * 4,
+                           D * 4, st_b, (size_t)B * 3 * D * 4};
+    const size_t ilen[] = {act, act, st_b, (size_t)B * 3 * D * 2, act, st_b, D * 8, D * 2,
+                           H * bs * bs * 2, D * 2, H * bs * bs * 2, D * 2, D * 4};
+    for (int i = 0; i < 11; ++i) {
+        if (overlap(outs[i], olen[i], workspace, need)) return RGLRU_ERR_ALIAS;
+        for (int j = i + 1; j < 11; ++j)
+            if (overlap(outs[i], olen[i], outs[j], olen[j])) return RGLRU_ERR_ALIAS;
+        for (int j = 0; j < 13; ++j)
+            if (overlap(outs[i], olen[i], ins[j], ilen[j])) return RGLRU_ERR_ALIAS;
+    }
+    for (int j = 0; j < 13; ++j)
+        if (overlap(workspace, need, ins[j], ilen[j])) return RGLRU_ERR_ALIAS;
+    BwdArgs a;
+    a.x = x; a.y = y; a.dout = dout; a.h0 = h0; a.conv0 = conv0; a.dh_last = dh_last;
+    a.conv_w = p->conv_w; a.conv_b = p->conv_b; a.wa = p->gate_a_w; a.ba = p->gate_a_b;
+    a.wx = p->gate_x_w; a.bx = p->gate_x_b; a.lambda = p->lambda;
+    a.dx = dx; a.dy = dy; a.dconv_w = dconv_w; a.dconv_b = dconv_b; a.dwa = dwa; a.dba = dba;
+    a.dwx = dwx; a.dbx = dbx; a.dlambda = dlambda; a.dh0 = dh0; a.dconv0 = dconv0;
+    a.ws = workspace; a.B = B; a.T = T; a.D = (int)D; a.H = (int)H;
+    hipError_t e = launch_prefill_backward(a, (hipStream_t)stream);
+    return e == hipSuccess ? RGLRU_OK : hip_fail(e);
+}
+
 }  // extern "C"

@@ -82,6 +82,8 @@ struct ProjGemmArgs {
     float* part;
     size_t part_bytes;
     int ksplit;                  // set by the launcher
+    int c_f32;                   // split-K only: C[0] is fp32 (no rounding); the call fails
+                                 // unless the launcher splits K
 };
 // fp32 partial-sum bytes the launcher would use for this shape with unlimited part_bytes
 size_t proj_gemm_part_bytes(int M, int Ntot, int K);
@@ -138,6 +140,22 @@ struct NormArgs {
     float eps;
 };
 hipError_t launch_add_rmsnorm(const NormArgs& a, hipStream_t s);
+
+// Backward pass of the path (bf16 storage, block size 256, T % 64 == 0, B * T % 256 == 0).
+struct BwdArgs {
+    const void *x, *y, *dout;            // [B][T][D] bf16
+    const float* h0;                     // [B][D] or NULL
+    const void* conv0;                   // [B][3][D] bf16 or NULL
+    const float* dh_last;                // [B][D] or NULL
+    const void *conv_w, *conv_b, *wa, *ba, *wx, *bx;
+    const float* lambda;
+    void *dx, *dy;                       // [B][T][D] bf16
+    float *dconv_w, *dconv_b, *dwa, *dba, *dwx, *dbx, *dlambda, *dh0, *dconv0;
+    void* ws;                            // workspace (rglru_prefill_backward_workspace_bytes)
+    int B, T, D, H;
+};
+size_t backward_workspace_bytes(int B, int T, int D, int H);
+hipError_t launch_prefill_backward(const BwdArgs& a, hipStream_t s);
 hipError_t launch_geglu(void* gate, const void* up, size_t n, hipStream_t s);  // n % 8 == 0
 constexpr int kAttnDecSlotsPerSplit = 512;  // cache slots per decode workgroup
 

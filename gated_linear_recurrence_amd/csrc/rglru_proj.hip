@@ -325,6 +325,12 @@ __global__ void __launch_bounds__(256) proj_splitk_reduce_kernel(ProjGemmArgs g)
         acc[0] += x.x; acc[1] += x.y; acc[2] += x.z; acc[3] += x.w;
         acc[4] += y.x; acc[5] += y.y; acc[6] += y.z; acc[7] += y.w;
     }
+    if (g.c_f32) {
+        float4* Cf = reinterpret_cast<float4*>(static_cast<float*>(g.C[seg]) + (size_t)m * g.Nw[seg] + nl);
+        Cf[0] = make_float4(acc[0] + v[0], acc[1] + v[1], acc[2] + v[2], acc[3] + v[3]);
+        Cf[1] = make_float4(acc[4] + v[4], acc[5] + v[5], acc[6] + v[6], acc[7] + v[7]);
+        return;
+    }
     uint16_t* C = static_cast<uint16_t*>(g.C[seg]) + (size_t)m * g.Nw[seg] + nl;
     *reinterpret_cast<uint4*>(C) = make_uint4(pack2bf(acc[0] + v[0], acc[1] + v[1]),
                                               pack2bf(acc[2] + v[2], acc[3] + v[3]),
@@ -422,7 +428,7 @@ hipError_t launch_proj_gemm(const ProjGemmArgs& a_in, hipStream_t s) {
     if (tiles <= 0) return hipSuccess;
     a.ksplit = 1;
     // the skinny kernel's waves each take whole 32-wide steps of K: K % (32 * waves) == 0
-    if (a.M <= kSkinnyRows && a.K % (32 * kSkinnyWaves) == 0) {
+    if (!a.c_f32 && a.M <= kSkinnyRows && a.K % (32 * kSkinnyWaves) == 0) {
         const unsigned blocks = (unsigned)(a.ntn * kBN / 16);
         switch ((a.M + 15) / 16) {
             case 1: hipLaunchKernelGGL(skinny_gemm_kernel<1>, dim3(blocks), dim3(512), 0, s, a); break;
@@ -436,6 +442,7 @@ hipError_t launch_proj_gemm(const ProjGemmArgs& a_in, hipStream_t s) {
         const int ks = choose_ksplit(a.M, a.ntn * kBN, a.K);
         if (ks > 1 && (size_t)ks * a.M * a.ntn * kBN * sizeof(float) <= a.part_bytes) a.ksplit = ks;
     }
+    if (a.c_f32 && a.ksplit == 1) return hipErrorInvalidValue;   // fp32 output needs the split path
     if (a.ksplit > 1)
         hipLaunchKernelGGL(proj_gemm_kernel<true>, dim3((unsigned)(tiles * a.ksplit)),
                            dim3(kThreads), 0, s, a);

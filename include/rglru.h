@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define RGLRU_ABI_VERSION 5
+#define RGLRU_ABI_VERSION 6
 
 enum rglru_dtype { RGLRU_F32 = 0, RGLRU_BF16 = 1 };
 
@@ -419,6 +419,30 @@ int rglru_attention_layer_decode(const rglru_attn_params *a, const rglru_norm_pa
                                  const rglru_mlp_params *m, int32_t N, const int32_t *pos,
                                  const void *x_t, void *out_t, void *kcache, void *vcache,
                                  void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Backward pass of the path, for training: the gradients of
+ *   L = sum_t dout_t . out_t + dh_last . h_last
+ * with respect to every input of rglru_prefill (the pages give no training detail; these are the
+ * chain-rule gradients of the forward operation above).
+ *   x, y, dout     [B][T][D] (bf16);  h0 [B][D] fp32 or NULL;  conv0 [B][3][D] or NULL;
+ *   dh_last        [B][D] fp32 or NULL (NULL = 0)
+ *   dx, dy         [B][T][D] (bf16)
+ *   dconv_w [D][4], dconv_b [D], dwa and dwx [H][bs][bs], dba and dbx [D], dlambda [D],
+ *   dh0 [B][D], dconv0 [B][3][D]   all fp32, overwritten (not accumulated)
+ *   workspace      at least rglru_prefill_backward_workspace_bytes(B, T, D, n_heads); no
+ *                  initialisation needed
+ * bf16 storage, block size 256, T % 64 == 0 and B * T % 256 == 0 with B * T >= 256, else
+ * RGLRU_ERR_UNSUPPORTED.  Outputs must not overlap each other, the inputs or the workspace.
+ * Deterministic (sums over tokens are taken in a fixed order).
+ */
+size_t rglru_prefill_backward_workspace_bytes(int32_t B, int32_t T, int32_t D, int32_t n_heads);
+int rglru_prefill_backward(const rglru_params *p, int32_t B, int32_t T, const void *x,
+                           const void *y, const float *h0, const void *conv0, const void *dout,
+                           const float *dh_last, void *dx, void *dy, float *dconv_w,
+                           float *dconv_b, float *dwa, float *dba, float *dwx, float *dbx,
+                           float *dlambda, float *dh0, float *dconv0, void *workspace,
+                           size_t ws_bytes, void *stream);
 
 /*
  * Diagnostics of a prefill workspace: copies its error flags to *flags_out (0 = none) and

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.rglru_abi_version() == 5
+    assert lib.rglru_abi_version() == 6
     for st in range(7):
         assert lib.rglru_status_string(st)
     assert lib.rglru_status_string(99) == b"unknown status"
@@ -479,3 +479,28 @@ def test_layer_decode_validation(lib):
     assert fa(a=_attn_params(Dm=512, Hq=17)) == SHAPE           # decode takes 16 heads at most
     assert fa(nb=wa - 1) == WS
     assert fa(o=DKC) == ALIAS                                   # out over the key cache
+
+
+def test_backward_workspace_and_validation(lib):
+    f = lib.rglru_prefill_backward_workspace_bytes
+    assert f(2, 128, 512, 2) > 0 and f(8, 8192, 2560, 10) > 0
+    assert f(2, 100, 512, 2) == 0                      # T % 64
+    assert f(1, 64, 512, 2) == 0                       # B * T % 256
+    assert f(2, 128, 512, 4) == 0                      # block size 128
+    p = _params(D=512, H=2, dtype=1)
+    base = 0x5000000000
+    ptr = [base + k * 0x10000000 for k in range(20)]
+    ws = f(2, 128, 512, 2)
+
+    def call(p=p, B=2, T=128, x=ptr[0], y=ptr[1], dout=ptr[2], outs=None, w=ptr[19], n=ws):
+        o = outs or ptr[4:15]
+        return lib.rglru_prefill_backward(ctypes.byref(p), B, T, x, y, None, None, dout, None, *o,
+                                          w, n, None)
+    assert call(T=100) == UNSUP
+    assert call(p=_params(D=512, H=2, dtype=0)) == UNSUP   # fp32 storage
+    assert call(x=None) == NULL
+    assert call(outs=ptr[4:14] + [None]) == NULL
+    assert call(n=ws - 1) == WS
+    assert call(outs=ptr[4:14] + [ptr[0]]) == ALIAS        # dconv0 over x
+    assert call(outs=[ptr[4]] + [ptr[4] + 0x100] + ptr[6:15]) == ALIAS   # dx and dy overlap
+    assert call(w=ptr[1]) == ALIAS                          # workspace over y
