@@ -552,6 +552,40 @@ def time_layers(w, steps, warmup, torch, binding):
                           % (2 * n_params)}}
 
 
+def time_backward(w, steps, warmup, torch, binding):
+    """The path's backward pass (rglru_prefill_backward) over the batched 2B workload."""
+    p = synth.make_params(w)
+    P = binding.Params(*[_to_dev(p[k], torch) for k in ("conv_w", "conv_b", "wa", "ba", "wx",
+                                                          "bx", "lambda")])
+    x, y = _to_dev(synth.make_act(w, "x"), torch), _to_dev(synth.make_act(w, "y"), torch)
+    h0 = _to_dev(synth.make_h0(w), torch)
+    g = torch.Generator(device="cuda").manual_seed(w.seed + 11)
+    dout = torch.randn(tuple(x.shape), generator=g, device="cuda").to(torch.bfloat16)
+    ws = binding.DeviceBuffer(binding.rglru_prefill_backward_workspace_bytes(w.B, w.T, w.D, w.H),
+                              "cuda")
+    call = lambda: binding.rglru_prefill_backward(P, x, y, dout, h0, workspace=ws)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    n = w.B * w.T * w.D
+    byts = 10 * n               # x, y, dout read and dx, dy written, bf16
+    flops = 3 * 2 * 2.0 * w.B * w.T * w.D * w.bs   # three block-diagonal products, two gates
+    return {"workload": w.name, "ms": ms, "tokens·channels/s": n / (ms * 1e-3),
+            "algorithmic_bytes": byts, "algorithmic_flop": flops,
+            "roofline": {"bound": "hbm", "kernel": "whole backward call",
+                         "achieved": byts / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+            "mfma_frac": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "workspace_bytes": ws.nbytes}
+
+
 def cpu_baseline(w):
     """The oracle on the whole headline workload (all 8 sequences x 8192 tokens x 10 heads),
     one OpenMP thread per (sequence, head) unit; inputs are generated before the clock starts."""
@@ -766,6 +800,7 @@ def main():
         line["local_attention"] = time_attention(w, max(args.steps // 2, 5), args.warmup, torch,
                                                  binding)
         line["residual_layers"] = time_layers(w, args.steps, args.warmup, torch, binding)
+        line["backward"] = time_backward(w, max(args.steps // 4, 3), args.warmup, torch, binding)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)

@@ -1044,9 +1044,9 @@ int rglru_attention_layer_decode(const rglru_attn_params* a, const rglru_norm_pa
 // backward pass of the path
 // ------------------------------------------------------------------------------------------
 static bool backward_shape_ok(int32_t B, int32_t T, int32_t D, int32_t n_heads) {
-    return B >= 1 && T >= 64 && n_heads >= 1 && D == 256 * n_heads && T % 64 == 0 &&
+    return B >= 1 && T >= 32 && n_heads >= 1 && D == 256 * n_heads && T % 32 == 0 &&
            ((long long)B * T) % 256 == 0 && (long long)B * T < (1LL << 22) &&
-           (long long)B * (T / 64) * D < (1LL << 31);
+           (long long)B * (T / 32) * D < (1LL << 31);
 }
 
 size_t rglru_prefill_backward_workspace_bytes(int32_t B, int32_t T, int32_t D, int32_t n_heads) {

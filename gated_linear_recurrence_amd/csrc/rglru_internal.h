@@ -141,7 +141,7 @@ struct NormArgs {
 };
 hipError_t launch_add_rmsnorm(const NormArgs& a, hipStream_t s);
 
-// Backward pass of the path (bf16 storage, block size 256, T % 64 == 0, B * T % 256 == 0).
+// Backward pass of the path (bf16 storage, block size 256, T % 32 == 0, B * T % 256 == 0).
 struct BwdArgs {
     const void *x, *y, *dout;            // [B][T][D] bf16
     const float* h0;                     // [B][D] or NULL

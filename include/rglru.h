@@ -432,7 +432,7 @@ int rglru_attention_layer_decode(const rglru_attn_params *a, const rglru_norm_pa
  *   dh0 [B][D], dconv0 [B][3][D]   all fp32, overwritten (not accumulated)
  *   workspace      at least rglru_prefill_backward_workspace_bytes(B, T, D, n_heads); no
  *                  initialisation needed
- * bf16 storage, block size 256, T % 64 == 0 and B * T % 256 == 0 with B * T >= 256, else
+ * bf16 storage, block size 256, T % 32 == 0 and B * T % 256 == 0 with B * T >= 256, else
  * RGLRU_ERR_UNSUPPORTED.  Outputs must not overlap each other, the inputs or the workspace.
  * Deterministic (sums over tokens are taken in a fixed order).
  */
