@@ -9,8 +9,8 @@
 //   gates:      [Rpre | Ipre]_h = U_h [W_a[h]; W_x[h]]^T + b           (K = 256, two segments)
 //   input grad: dU_h = [dRpre | dIpre]_h [W_a[h]^T | W_x[h]^T]^T       (K = 512)
 //   weights:    [dW_a; dW_x]_h = [dRpre | dIpre]_h^T U_h                (K = B*T, split K, fp32)
-// The scans run per channel over chunks of 32 tokens: local aggregates, a sequential carry over
-// the chunks, then a pass that uses the carries (forward for h; the backward recurrence
+// The scans run per channel over chunks of 32 tokens: local aggregates of both directions in one
+// pass, sequential carries over the chunks, then a pass that uses the carries (forward for h; the backward recurrence
 //   dh_t = dout_t gelu(y_t) + a_{t+1} dh_{t+1}
 // in reverse, re-running the chunk's forward in registers to have h_{t-1}).
 #include <math.h>
@@ -30,7 +30,7 @@ constexpr int kChunk = 32;  // tokens per scan chunk (32: the gradient pass keep
 
 struct BwdBufs {
     uint16_t *U, *R, *I, *Wt, *dRI, *dRIt, *Ut, *dUg;
-    float *aggA, *aggB, *carry, *bP, *bQ, *cin, *duv, *plam, *pba, *pbx, *pconv, *dW, *part;
+    float *aggA, *aggB, *carry, *bQ, *cin, *duv, *plam, *pba, *pbx, *pconv, *dW, *part;
     size_t part_bytes;
 };
 
@@ -58,7 +58,6 @@ BwdBufs carve(void* ws, int B, int T, int D, int H, size_t* total) {
     b.aggA = reinterpret_cast<float*>(take(nc * 4));
     b.aggB = reinterpret_cast<float*>(take(nc * 4));
     b.carry = reinterpret_cast<float*>(take(nc * 4));
-    b.bP = reinterpret_cast<float*>(take(nc * 4));
     b.bQ = reinterpret_cast<float*>(take(nc * 4));
     b.cin = reinterpret_cast<float*>(take(nc * 4));
     b.duv = reinterpret_cast<float*>(take(MD * 4));
@@ -159,8 +158,11 @@ __device__ __forceinline__ Gate gate_of(float rp, float ip, float lsg) {
 }
 __device__ __forceinline__ float log_sigmoid(float lam) { return -log1pf(expf(-lam)); }
 
-// ---- forward chunk aggregates: (prod a, local h at the chunk end from 0) ------------------
-__global__ void __launch_bounds__(256) bwd_scan_agg_kernel(BwdArgs a, BwdBufs w) {
+// ---- chunk aggregates, both directions in one forward pass over the chunk -----------------
+// forward: h_end = A h_start + Bh with A = prod a, Bh the local state from 0;
+// reverse: c_start = A c_in + Q with c_t = a_t dh_t, dh_t = dout_t gelu(y_t) + c_{t+1}, i.e.
+// Q = sum_t (a_start ... a_t) dout_t gelu(y_t).
+__global__ void __launch_bounds__(256) bwd_chunk_agg_kernel(BwdArgs a, BwdBufs w) {
     const int nch = a.T / kChunk;
     const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
     if (idx >= (size_t)a.B * nch * a.D) return;
@@ -168,19 +170,24 @@ __global__ void __launch_bounds__(256) bwd_scan_agg_kernel(BwdArgs a, BwdBufs w)
     const size_t M = (size_t)a.B * a.T;
     const int h = d / kBs, k = d % kBs;
     const float lsg = log_sigmoid(a.lambda[d]);
-    float A = 1.0f, Bh = 0.0f;
+    const uint16_t* dout = static_cast<const uint16_t*>(a.dout);
+    const uint16_t* y = static_cast<const uint16_t*>(a.y);
+    float A = 1.0f, Bh = 0.0f, Q = 0.0f;
     for (int tt = 0; tt < kChunk; ++tt) {
         const size_t m = (size_t)b * a.T + c * kChunk + tt, e = hm(h, m, k, M);
         const Gate g = gate_of(bf2f(w.R[e]), bf2f(w.I[e]), lsg);
         A *= g.a;
         Bh = __builtin_fmaf(g.a, Bh, g.m * g.i * bf2f(w.U[e]));
+        Q = __builtin_fmaf(A, bf2f(dout[m * a.D + d]) * gelu_and_grad(bf2f(y[m * a.D + d])).x, Q);
     }
     w.aggA[idx] = A;
     w.aggB[idx] = Bh;
+    w.bQ[idx] = Q;
 }
 
-// ---- sequential carries over chunks: h entering each chunk ---------------------------------
-__global__ void __launch_bounds__(256) bwd_scan_carry_kernel(BwdArgs a, BwdBufs w) {
+// ---- sequential carries over the chunks: h entering each chunk (forward) and c entering it
+// from the right (reverse); the reverse carry past the first chunk is dh0 ----------------------
+__global__ void __launch_bounds__(256) bwd_carry_kernel(BwdArgs a, BwdBufs w) {
     const int nch = a.T / kChunk;
     const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
     if (idx >= (size_t)a.B * a.D) return;
@@ -191,42 +198,11 @@ __global__ void __launch_bounds__(256) bwd_scan_carry_kernel(BwdArgs a, BwdBufs 
         w.carry[e] = h;
         h = __builtin_fmaf(w.aggA[e], h, w.aggB[e]);
     }
-}
-
-// ---- backward chunk aggregates: c_start = P c_in + Q over the chunk in reverse -------------
-// (c_t = a_t dh_t is what token t passes to h_{t-1}; dh_t = dout_t gelu(y_t) + c_{t+1})
-__global__ void __launch_bounds__(256) bwd_rscan_agg_kernel(BwdArgs a, BwdBufs w) {
-    const int nch = a.T / kChunk;
-    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= (size_t)a.B * nch * a.D) return;
-    const int d = (int)(idx % a.D), c = (int)((idx / a.D) % nch), b = (int)(idx / ((size_t)nch * a.D));
-    const size_t M = (size_t)a.B * a.T;
-    const int h = d / kBs, k = d % kBs;
-    const float lsg = log_sigmoid(a.lambda[d]);
-    const uint16_t* dout = static_cast<const uint16_t*>(a.dout);
-    const uint16_t* y = static_cast<const uint16_t*>(a.y);
-    float P = 1.0f, Q = 0.0f;
-    for (int tt = kChunk - 1; tt >= 0; --tt) {
-        const size_t m = (size_t)b * a.T + c * kChunk + tt, e = hm(h, m, k, M);
-        const Gate g = gate_of(bf2f(w.R[e]), bf2f(w.I[e]), lsg);
-        const float gt = bf2f(dout[m * a.D + d]) * gelu_and_grad(bf2f(y[m * a.D + d])).x;
-        Q = g.a * (gt + Q);
-        P *= g.a;
-    }
-    w.bP[idx] = P;
-    w.bQ[idx] = Q;
-}
-
-__global__ void __launch_bounds__(256) bwd_rscan_carry_kernel(BwdArgs a, BwdBufs w) {
-    const int nch = a.T / kChunk;
-    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= (size_t)a.B * a.D) return;
-    const int d = (int)(idx % a.D), b = (int)(idx / a.D);
     float cc = a.dh_last ? a.dh_last[idx] : 0.0f;
     for (int c = nch - 1; c >= 0; --c) {
         const size_t e = ((size_t)b * nch + c) * a.D + d;
         w.cin[e] = cc;
-        cc = __builtin_fmaf(w.bP[e], cc, w.bQ[e]);
+        cc = __builtin_fmaf(w.aggA[e], cc, w.bQ[e]);
     }
     a.dh0[idx] = cc;
 }
@@ -469,10 +445,8 @@ hipError_t launch_prefill_backward(const BwdArgs& a, hipStream_t s) {
         g.Nw[0] = kBs; g.Nw[1] = kBs; g.nseg = 2; g.M = (int)M; g.K = kBs;
         if ((e = launch_proj_gemm(g, s)) != hipSuccess) return e;
     }
-    RG_LAUNCH(bwd_scan_agg_kernel, nlane);
-    RG_LAUNCH(bwd_scan_carry_kernel, (size_t)a.B * a.D);
-    RG_LAUNCH(bwd_rscan_agg_kernel, nlane);
-    RG_LAUNCH(bwd_rscan_carry_kernel, (size_t)a.B * a.D);
+    RG_LAUNCH(bwd_chunk_agg_kernel, nlane);
+    RG_LAUNCH(bwd_carry_kernel, (size_t)a.B * a.D);
     RG_LAUNCH(bwd_grad_kernel, nlane);
     for (int h = 0; h < a.H; ++h) {   // gradient of u through the gates
         ProjGemmArgs g;
