@@ -295,3 +295,74 @@ def test_attention_layer_decode_continues_prefill(Dm, Hq, F, N, W, T0, steps):
     print("attention layer decode Dm=%d Hq=%d F=%d N=%d W=%d, %d steps after %d: rel-L2 %.3e"
           % (Dm, Hq, F, N, W, steps, T0, e))
     assert e <= H.TOL[synth.BF16]
+
+
+def test_layer_decode_steps_replay_from_a_graph():
+    """Decode steps of both layers captured in one HIP graph and replayed three times (eager
+    work in between) give bitwise the eager steps' outputs and states."""
+    from gated_linear_recurrence_amd import binding
+    N, D, Dm, F, Hq, W = 3, 512, 512, 768, 2, 32
+    w = dataclasses.replace(synth.small(synth.WORKLOADS[synth.PREFILL_2B], B=N, T=8), D=D, H=2)
+    p, q = synth.make_params(w, biases=True), synth.make_proj(w, Dm=Dm, biases=True)
+    L = synth.make_layer(w, Dm=Dm, F=F, biases=True)
+    a = synth.make_attn(w, Dm=Dm, n_heads=Hq, bias=True)
+    P = H.dev_params(p, w.H)
+    Q = binding.ProjParams(*[H.to_dev(q[k]) for k in ("lx_w", "lx_b", "ly_w", "ly_b",
+                                                      "lo_w", "lo_b")])
+    A = binding.AttnParams(H.to_dev(a["q_w"]), H.to_dev(a["k_w"]), H.to_dev(a["v_w"]),
+                           H.to_dev(a["o_w"]), H.to_dev(a["o_b"]), Hq, W)
+    Nd, Md = _norms_dev(L), _mlp_dev(L)
+    lib = binding.load_library()
+    import ctypes
+    ws_r = binding.DeviceBuffer(lib.rglru_recurrent_layer_decode_workspace_bytes(N, D, Dm, F), "cuda")
+    ws_a = binding.DeviceBuffer(lib.rglru_attention_layer_decode_workspace_bytes(
+        ctypes.byref(A.c), N, F), "cuda")
+    g = torch.Generator(device="cuda").manual_seed(4)
+    x = torch.randn((N, Dm), generator=g, device="cuda").to(torch.bfloat16)
+    h0 = torch.randn((N, D), generator=g, device="cuda") * 0.3
+    c0 = torch.randn((N, 3, D), generator=g, device="cuda").to(torch.bfloat16)
+    cache0 = binding.AttnCache(N, W, "cuda")
+    cache0.k.normal_(generator=g)
+    cache0.v.normal_(generator=g)
+    # state and output buffers the graph owns
+    h, conv = h0.clone(), c0.clone()
+    cache = binding.AttnCache(N, W, "cuda")
+    pos = torch.full((N,), 40, dtype=torch.int32, device="cuda")
+    y1, y2 = torch.empty_like(x), torch.empty_like(x)
+
+    def step():
+        binding.rglru_recurrent_layer_decode(P, Q, Nd, Md, x, h, conv, out=y1, workspace=ws_r)
+        binding.rglru_attention_layer_decode(A, Nd, Md, pos, y1, cache, out=y2, workspace=ws_a)
+
+    def reset():
+        h.copy_(h0)
+        conv.copy_(c0)
+        cache.k.copy_(cache0.k)
+        cache.v.copy_(cache0.v)
+
+    reset()
+    eager = []
+    for _ in range(3):
+        step()
+        eager.append((y2.clone(), h.clone(), conv.clone(), cache.k.clone()))
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        reset()
+        step()                        # warm-up outside the capture
+        torch.cuda.synchronize()
+        with torch.cuda.graph(gr, stream=st):
+            step()
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    reset()
+    torch.cuda.synchronize()
+    for r in range(3):
+        gr.replay()
+        torch.cuda.synchronize()
+        got = (y2, h, conv, cache.k)
+        for i, (e, t) in enumerate(zip(eager[r], got)):
+            assert torch.equal(e, t), (r, i)
+        _ = (x.float() * 2).sum().item()   # eager work between replays
