@@ -338,13 +338,13 @@ __global__ void __launch_bounds__(256) proj_splitk_reduce_kernel(ProjGemmArgs g)
                                               pack2bf(acc[6] + v[6], acc[7] + v[7]));
 }
 
-// Few rows (decode: one row per sequence).  One workgroup per 16 output features: the weight
-// rows are the A operand of v_mfma_f32_16x16x32_bf16 (16 features x 32 k, each lane 16 bytes of
-// one row) and up to 64 input rows the B operand in blocks of 16 columns, so each weight byte
-// is read once and no MFMA work is spent on rows that do not exist.  The eight waves take an
-// eighth of K each, with eight weight loads in flight per wave (a few waves per CU must keep
-// enough bytes in flight to stream the weights); their tiles are added in wave order through
-// LDS.
+// Few rows (decode: one row per sequence), up to 64, where the row kernel below does not
+// apply.  One workgroup per 16 output features: the weight rows are the A operand of
+// v_mfma_f32_16x16x32_bf16 (16 features x 32 k, each lane 16 bytes of one row) and up to 64
+// input rows the B operand in blocks of 16 columns, so each weight byte is read once and no
+// MFMA work is spent on rows that do not exist.  The eight waves take an eighth of K each, with
+// eight weight loads in flight per wave (a few waves per CU must keep enough bytes in flight to
+// stream the weights); their tiles are added in wave order through LDS.
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -400,6 +400,59 @@ __global__ void __launch_bounds__(64 * kSkinnyWaves) skinny_gemm_kernel(ProjGemm
                                               pack2bf(t[2] + bv[2], t[3] + bv[3]));
 }
 
+// One to four rows with K % 512 == 0 (decode of one to four sequences).  One wave per output
+// feature: lane l takes the 16-byte pieces k = 512 c + 8 l of the feature's weight row, so every
+// load instruction reads 1 KB of one row contiguously (the MFMA kernel above reads 64 bytes of
+// each of 16 rows per instruction and streams the weights about 1.5x slower at these sizes).
+// Pairs of bf16 products accumulate in fp32 with v_dot2_f32_bf16; a butterfly over the wave
+// then adds the 64 lanes' sums, the same order for every feature and call.
+typedef __bf16 bf16v2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16v2, a),
+                                           __builtin_bit_cast(bf16v2, b), c, false);
+}
+
+constexpr int kRowsMax = 4;        // at most this many rows: gemv_rows_kernel
+constexpr int kRowsWaves = 4;      // features (waves) per workgroup
+template <int NB>   // input rows held per lane: M <= NB
+__global__ void __launch_bounds__(64 * kRowsWaves) gemv_rows_kernel(ProjGemmArgs g) {
+    const int lane = threadIdx.x & 63;
+    const int n = blockIdx.x * kRowsWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int seg = n < g.Nw[0] ? 0 : (n < g.Nw[0] + g.Nw[1] ? 1 : 2);
+    const int nl = n - (seg > 0 ? g.Nw[0] : 0) - (seg > 1 ? g.Nw[1] : 0);
+    const int K = g.K;
+    const uint16_t* w = static_cast<const uint16_t*>(g.W[seg]) + (size_t)nl * K + 8 * lane;
+    const uint16_t* x = static_cast<const uint16_t*>(g.A) + 8 * lane;
+    size_t xo[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) xo[b] = (size_t)min(b, g.M - 1) * K;   // rows past M repeat
+    float acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b] = 0.0f;
+#pragma unroll 4
+    for (int k = 0; k < K; k += 512) {
+        const uint4 wv = *reinterpret_cast<const uint4*>(w + k);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const uint4 xv = *reinterpret_cast<const uint4*>(x + xo[b] + k);
+            acc[b] = dot2(wv.x, xv.x, acc[b]);
+            acc[b] = dot2(wv.y, xv.y, acc[b]);
+            acc[b] = dot2(wv.z, xv.z, acc[b]);
+            acc[b] = dot2(wv.w, xv.w, acc[b]);
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) acc[b] += __shfl_xor(acc[b], o);
+    const uint16_t* bias = static_cast<const uint16_t*>(g.b[seg]);
+    const float bv = bias ? bf2f(bias[nl]) : 0.0f;
+    uint16_t* C = static_cast<uint16_t*>(g.C[seg]) + nl;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+        if (lane == b && b < g.M) C[(size_t)b * g.Nw[seg]] = f2bf(acc[b] + bv);
+}
+
 // K splits for a shape: enough blocks to cover the chip (about 240) when the tiles alone do
 // not, each split a multiple of 128 of K.
 int choose_ksplit(int M, int Ntot, int K) {
@@ -415,6 +468,7 @@ int choose_ksplit(int M, int Ntot, int K) {
 }  // namespace
 
 size_t proj_gemm_part_bytes(int M, int Ntot, int K) {
+    if (M <= kRowsMax && K % 512 == 0) return 0;
     if (M <= kSkinnyRows && K % (32 * kSkinnyWaves) == 0) return 0;
     const int s = choose_ksplit(M, Ntot, K);
     return s > 1 ? (size_t)s * M * Ntot * sizeof(float) : 0;
@@ -427,6 +481,15 @@ hipError_t launch_proj_gemm(const ProjGemmArgs& a_in, hipStream_t s) {
     const long long tiles = (long long)a.ntm * a.ntn;
     if (tiles <= 0) return hipSuccess;
     a.ksplit = 1;
+    if (!a.c_f32 && a.M <= kRowsMax && a.K % 512 == 0) {
+        const unsigned blocks = (unsigned)(a.ntn * kBN / kRowsWaves);
+        switch (a.M) {
+            case 1: hipLaunchKernelGGL(gemv_rows_kernel<1>, dim3(blocks), dim3(256), 0, s, a); break;
+            case 2: hipLaunchKernelGGL(gemv_rows_kernel<2>, dim3(blocks), dim3(256), 0, s, a); break;
+            default: hipLaunchKernelGGL(gemv_rows_kernel<4>, dim3(blocks), dim3(256), 0, s, a);
+        }
+        return hipGetLastError();
+    }
     // the skinny kernel's waves each take whole 32-wide steps of K: K % (32 * waves) == 0
     if (!a.c_f32 && a.M <= kSkinnyRows && a.K % (32 * kSkinnyWaves) == 0) {
         const unsigned blocks = (unsigned)(a.ntn * kBN / 16);

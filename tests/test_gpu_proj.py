@@ -54,6 +54,13 @@ def _check_linear(got_bits, ref, x_bits, w_bits, label):
     (300, 256, 512, True),        # ragged M: a full tile and a partial one
     (257, 2560, 2560, False),     # the 2B widths, one row past a tile
     (513, 384, 768, True),        # K = 384: a loop trip and a half over the stage ring
+    (1, 2560, 2560, True),        # decode of one sequence: the row kernel (M <= 4, K % 512 == 0)
+    (2, 7680, 512, False),        # row kernel, two rows, the MLP down projection's K
+    (3, 1024, 768, True),         # row kernel, a ragged row count (held as four)
+    (4, 512, 256, True),          # row kernel, one 512-wide step of K
+    (5, 512, 512, True),          # five rows: the MFMA skinny kernel
+    (4, 768, 512, True),          # K % 512 != 0: the MFMA skinny kernel
+    (64, 256, 256, False),        # the MFMA skinny kernel's largest row count
 ])
 def test_linear_matches_oracle(M, K, N, bias):
     from gated_linear_recurrence_amd import binding
