@@ -670,23 +670,30 @@ int check_norms(const rglru_norm_params* n, int Dm) {
     return RGLRU_OK;
 }
 
+// The MLP on M rows.  With the row kernel (one to four rows) the gating runs in the gate|up
+// launch's epilogue, and a residual, when given, is added in the down launch's epilogue
+// (*res_added tells the caller which happened).
 hipError_t run_mlp(const rglru_mlp_params* m, int M, const void* x, void* out, void* ws,
-                   float* part, size_t part_bytes, hipStream_t s) {
+                   float* part, size_t part_bytes, hipStream_t s,
+                   const void* residual = nullptr, bool* res_added = nullptr) {
     const size_t nf = (size_t)M * m->F;
     void* G = ws;
     void* U = static_cast<char*>(ws) + round256(nf * 2);
+    const bool gated = proj_gemm_rows(M, m->D_model);
     ProjGemmArgs g;
     memset(&g, 0, sizeof g);
     g.A = x; g.W[0] = m->gate_w; g.W[1] = m->up_w; g.b[0] = m->gate_b; g.b[1] = m->up_b;
     g.C[0] = G; g.C[1] = U; g.M = M; g.K = m->D_model; g.Nw[0] = m->F; g.Nw[1] = m->F; g.nseg = 2;
-    g.part = part; g.part_bytes = part_bytes;
+    g.part = part; g.part_bytes = part_bytes; g.gated = gated;
     hipError_t e = launch_proj_gemm(g, s);
-    if (e == hipSuccess) e = launch_geglu(G, U, nf, s);
+    if (e == hipSuccess && !gated) e = launch_geglu(G, U, nf, s);
     if (e != hipSuccess) return e;
+    const bool add = residual && proj_gemm_rows(M, m->F);
+    if (res_added) *res_added = add;
     memset(&g, 0, sizeof g);
     g.A = G; g.W[0] = m->down_w; g.b[0] = m->down_b; g.C[0] = out;
     g.M = M; g.K = m->F; g.Nw[0] = m->D_model; g.nseg = 1;
-    g.part = part; g.part_bytes = part_bytes;
+    g.part = part; g.part_bytes = part_bytes; g.R = add ? residual : nullptr;
     return launch_proj_gemm(g, s);
 }
 
@@ -714,7 +721,8 @@ size_t layer_tail_bytes(size_t M, int Dm, int F) {
 }
 
 // Launches of the layer after validation: norm 1, the block (through `block`), h and norm 2,
-// the MLP, the final residual addition into out.
+// the MLP into out, the final residual addition in place (done by the MLP's last launch when
+// that takes the row kernel).
 template <class Block>
 int run_layer(const rglru_norm_params* nrm, const rglru_mlp_params* m, size_t M, int Dm,
               const void* x_in, void* out, const LayerBufs& L, hipStream_t s, Block block) {
@@ -727,9 +735,12 @@ int run_layer(const rglru_norm_params* nrm, const rglru_mlp_params* m, size_t M,
     if (st != RGLRU_OK) return st;
     na.x = x_in; na.y = L.b; na.g = nrm->channel_scale; na.h = L.h; na.n = L.a;
     e = launch_add_rmsnorm(na, s);
-    if (e == hipSuccess) e = run_mlp(m, (int)M, L.a, L.b, L.mlp, L.part, L.part_bytes, s);
+    bool added = false;
+    if (e == hipSuccess)
+        e = run_mlp(m, (int)M, L.a, out, L.mlp, L.part, L.part_bytes, s, L.h, &added);
     if (e != hipSuccess) return hip_fail(e);
-    na.x = L.h; na.y = L.b; na.g = nullptr; na.h = out; na.n = nullptr;
+    if (added) return RGLRU_OK;
+    na.x = L.h; na.y = out; na.g = nullptr; na.h = out; na.n = nullptr;
     e = launch_add_rmsnorm(na, s);
     return e == hipSuccess ? RGLRU_OK : hip_fail(e);
 }

@@ -84,7 +84,13 @@ struct ProjGemmArgs {
     int ksplit;                  // set by the launcher
     int c_f32;                   // split-K only: C[0] is fp32 (no rounding); the call fails
                                  // unless the launcher splits K
+    // Row kernel only (proj_gemm_rows(M, K)); the call fails otherwise.
+    int gated;                   // two segments of equal width: C[0] = gelu_tanh(gate) * up,
+                                 // from the bf16-rounded segment outputs (C[1] unused)
+    const void* R;               // one segment: C = R + the rounded output, rounded again
 };
+// true when launch_proj_gemm takes the row kernel (which alone supports gated and R)
+bool proj_gemm_rows(int M, int K);
 // fp32 partial-sum bytes the launcher would use for this shape with unlimited part_bytes
 size_t proj_gemm_part_bytes(int M, int Ntot, int K);
 

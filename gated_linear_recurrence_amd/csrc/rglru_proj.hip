@@ -406,51 +406,80 @@ __global__ void __launch_bounds__(64 * kSkinnyWaves) skinny_gemm_kernel(ProjGemm
 // each of 16 rows per instruction and streams the weights about 1.5x slower at these sizes).
 // Pairs of bf16 products accumulate in fp32 with v_dot2_f32_bf16; a butterfly over the wave
 // then adds the 64 lanes' sums, the same order for every feature and call.
+//
+// Two epilogues serve the layer's MLP (page "Gemma 詳解：RecurrentGemma 架構", the MLP block of
+// the residual layers) without extra launches, with the roundings of the separate steps:
+//   kGated  the wave takes feature n of both segments (gate and up rows) and writes
+//           gelu_tanh(gate) * up, each rounded to bf16 first, as the gating step would;
+//   R       the final residual addition: C = R + the bf16 output, rounded again.
 typedef __bf16 bf16v2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16v2, a),
                                            __builtin_bit_cast(bf16v2, b), c, false);
 }
+__device__ __forceinline__ void dot8(const uint4& w, const uint4& x, float& acc) {
+    acc = dot2(w.x, x.x, acc);
+    acc = dot2(w.y, x.y, acc);
+    acc = dot2(w.z, x.z, acc);
+    acc = dot2(w.w, x.w, acc);
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
 
 constexpr int kRowsMax = 4;        // at most this many rows: gemv_rows_kernel
 constexpr int kRowsWaves = 4;      // features (waves) per workgroup
-template <int NB>   // input rows held per lane: M <= NB
+template <int NB, bool kGated>   // input rows held per lane: M <= NB
 __global__ void __launch_bounds__(64 * kRowsWaves) gemv_rows_kernel(ProjGemmArgs g) {
+    constexpr int NS = kGated ? 2 : 1;   // weight rows per wave
     const int lane = threadIdx.x & 63;
     const int n = blockIdx.x * kRowsWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int seg = n < g.Nw[0] ? 0 : (n < g.Nw[0] + g.Nw[1] ? 1 : 2);
+    const int seg = kGated ? 0 : (n < g.Nw[0] ? 0 : (n < g.Nw[0] + g.Nw[1] ? 1 : 2));
     const int nl = n - (seg > 0 ? g.Nw[0] : 0) - (seg > 1 ? g.Nw[1] : 0);
     const int K = g.K;
-    const uint16_t* w = static_cast<const uint16_t*>(g.W[seg]) + (size_t)nl * K + 8 * lane;
+    const uint16_t* w[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+        w[j] = static_cast<const uint16_t*>(g.W[seg + j]) + (size_t)nl * K + 8 * lane;
     const uint16_t* x = static_cast<const uint16_t*>(g.A) + 8 * lane;
     size_t xo[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) xo[b] = (size_t)min(b, g.M - 1) * K;   // rows past M repeat
-    float acc[NB];
+    float acc[NS][NB];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) acc[b] = 0.0f;
+    for (int j = 0; j < NS; ++j)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[j][b] = 0.0f;
 #pragma unroll 4
     for (int k = 0; k < K; k += 512) {
-        const uint4 wv = *reinterpret_cast<const uint4*>(w + k);
+        uint4 wv[NS];
+#pragma unroll
+        for (int j = 0; j < NS; ++j) wv[j] = *reinterpret_cast<const uint4*>(w[j] + k);
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             const uint4 xv = *reinterpret_cast<const uint4*>(x + xo[b] + k);
-            acc[b] = dot2(wv.x, xv.x, acc[b]);
-            acc[b] = dot2(wv.y, xv.y, acc[b]);
-            acc[b] = dot2(wv.z, xv.z, acc[b]);
-            acc[b] = dot2(wv.w, xv.w, acc[b]);
+#pragma unroll
+            for (int j = 0; j < NS; ++j) dot8(wv[j], xv, acc[j][b]);
         }
     }
+    float bv[NS];
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) acc[b] += __shfl_xor(acc[b], o);
-    const uint16_t* bias = static_cast<const uint16_t*>(g.b[seg]);
-    const float bv = bias ? bf2f(bias[nl]) : 0.0f;
+    for (int j = 0; j < NS; ++j) {
+        const uint16_t* bias = static_cast<const uint16_t*>(g.b[seg + j]);
+        bv[j] = bias ? bf2f(bias[nl]) : 0.0f;
+    }
+    const int ldc = kGated ? g.Nw[0] : g.Nw[seg];
     uint16_t* C = static_cast<uint16_t*>(g.C[seg]) + nl;
+    const uint16_t* R = static_cast<const uint16_t*>(g.R);
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
-        if (lane == b && b < g.M) C[(size_t)b * g.Nw[seg]] = f2bf(acc[b] + bv);
+    for (int b = 0; b < NB; ++b) {
+        float v = bf2f(f2bf(wave_sum(acc[0][b]) + bv[0]));
+        if (kGated) v = gelu_fast(v) * bf2f(f2bf(wave_sum(acc[1][b]) + bv[1]));
+        else if (R) v += bf2f(R[(size_t)min(b, g.M - 1) * ldc + nl]);
+        if (lane == b && b < g.M) C[(size_t)b * ldc] = f2bf(v);
+    }
 }
 
 // K splits for a shape: enough blocks to cover the chip (about 240) when the tiles alone do
@@ -467,8 +496,10 @@ int choose_ksplit(int M, int Ntot, int K) {
 
 }  // namespace
 
+bool proj_gemm_rows(int M, int K) { return M >= 1 && M <= kRowsMax && K % 512 == 0; }
+
 size_t proj_gemm_part_bytes(int M, int Ntot, int K) {
-    if (M <= kRowsMax && K % 512 == 0) return 0;
+    if (proj_gemm_rows(M, K)) return 0;
     if (M <= kSkinnyRows && K % (32 * kSkinnyWaves) == 0) return 0;
     const int s = choose_ksplit(M, Ntot, K);
     return s > 1 ? (size_t)s * M * Ntot * sizeof(float) : 0;
@@ -481,12 +512,24 @@ hipError_t launch_proj_gemm(const ProjGemmArgs& a_in, hipStream_t s) {
     const long long tiles = (long long)a.ntm * a.ntn;
     if (tiles <= 0) return hipSuccess;
     a.ksplit = 1;
-    if (!a.c_f32 && a.M <= kRowsMax && a.K % 512 == 0) {
-        const unsigned blocks = (unsigned)(a.ntn * kBN / kRowsWaves);
-        switch (a.M) {
-            case 1: hipLaunchKernelGGL(gemv_rows_kernel<1>, dim3(blocks), dim3(256), 0, s, a); break;
-            case 2: hipLaunchKernelGGL(gemv_rows_kernel<2>, dim3(blocks), dim3(256), 0, s, a); break;
-            default: hipLaunchKernelGGL(gemv_rows_kernel<4>, dim3(blocks), dim3(256), 0, s, a);
+    const bool rows = !a.c_f32 && proj_gemm_rows(a.M, a.K);
+    if (a.gated && !(rows && a.nseg == 2 && a.Nw[0] == a.Nw[1])) return hipErrorInvalidValue;
+    if (a.R && !(rows && a.nseg == 1)) return hipErrorInvalidValue;
+    if (rows) {
+        const unsigned blocks = (unsigned)((a.gated ? a.Nw[0] : a.ntn * kBN) / kRowsWaves);
+        const dim3 grid(blocks), blk(64 * kRowsWaves);
+        if (a.gated) {
+            switch (a.M) {
+                case 1: hipLaunchKernelGGL((gemv_rows_kernel<1, true>), grid, blk, 0, s, a); break;
+                case 2: hipLaunchKernelGGL((gemv_rows_kernel<2, true>), grid, blk, 0, s, a); break;
+                default: hipLaunchKernelGGL((gemv_rows_kernel<4, true>), grid, blk, 0, s, a);
+            }
+        } else {
+            switch (a.M) {
+                case 1: hipLaunchKernelGGL((gemv_rows_kernel<1, false>), grid, blk, 0, s, a); break;
+                case 2: hipLaunchKernelGGL((gemv_rows_kernel<2, false>), grid, blk, 0, s, a); break;
+                default: hipLaunchKernelGGL((gemv_rows_kernel<4, false>), grid, blk, 0, s, a);
+            }
         }
         return hipGetLastError();
     }

@@ -88,6 +88,8 @@ def _mlp_oracle(L):
 @pytest.mark.parametrize("M,Dm,F,biases", [
     (300, 512, 768, True),     # ragged rows
     (130, 2560, 7680, False),  # the 2B widths
+    (1, 2560, 7680, True),     # one row: gating in the gate|up row kernel's epilogue
+    (3, 512, 768, True),       # gated row kernel, then the down projection on the MFMA kernel
 ])
 def test_mlp_matches_oracle(M, Dm, F, biases):
     from gated_linear_recurrence_amd import binding
