@@ -442,7 +442,7 @@ int rglru_local_attention(int32_t B, int32_t T, int32_t n_heads, int32_t window,
 
 size_t rglru_local_attention_decode_workspace_bytes(int32_t N, int32_t n_heads, int32_t window) {
     if (N < 1 || n_heads < 1 || window < 1 || window >= (1 << 22)) return 0;
-    const size_t nsplit = ((size_t)window + kAttnDecSlotsPerSplit - 1) / kAttnDecSlotsPerSplit;
+    const size_t nsplit = (size_t)attn_dec_nsplit(N, window);
     return round256((size_t)N * n_heads * kAttnDh * 2) +
            (size_t)N * nsplit * n_heads * (2 + kAttnDh) * sizeof(float);
 }
@@ -455,7 +455,7 @@ static int attn_decode_impl(int32_t N, int32_t n_heads, int32_t window, float ro
     if (N < 1 || n_heads < 1 || n_heads > 16 || window < 1 || !(rope_base > 1.0f) ||
         !(rope_base < INFINITY))
         return RGLRU_ERR_SHAPE;
-    const long long nsplit = ((long long)window + kAttnDecSlotsPerSplit - 1) / kAttnDecSlotsPerSplit;
+    const long long nsplit = attn_dec_nsplit(N, window);
     if (window >= (1 << 22) || (long long)N * nsplit >= (1LL << 24)) return RGLRU_ERR_UNSUPPORTED;
     if (!pos || !q || !k || !v || !kcache || !vcache || !o) return RGLRU_ERR_NULL;
     const void* ptrs[] = {pos, q, k, v, kcache, vcache, o, workspace};
@@ -478,6 +478,7 @@ static int attn_decode_impl(int32_t N, int32_t n_heads, int32_t window, float ro
     a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                       round256((size_t)N * n_heads * kAttnDh * 2));
     a.N = N; a.Hq = n_heads; a.W = window; a.Wc = (window + 31) / 32 * 32; a.nsplit = (int)nsplit;
+    a.tpw = attn_dec_tiles_per_wave(N);
     a.rope_base = rope_base;
     hipError_t e = launch_attention_decode(a, (hipStream_t)stream);
     return e == hipSuccess ? RGLRU_OK : hip_fail(e);

@@ -356,8 +356,8 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// One workgroup per (sequence, 512 cache slots): each wave takes four 32-slot tiles (tile
-// 16 sp + 4 i + wave), heads as the 16 columns of S^T = K Q^T and O^T = V^T P^T, and a softmax
+// One workgroup per (sequence, 128 tpw cache slots): each wave takes tpw (1, 2 or 4) 32-slot tiles
+// (tile 4 tpw sp + 4 i + wave, i < tpw), heads as the 16 columns of S^T = K Q^T and O^T = V^T P^T, and a softmax
 // per head over its tiles; the four waves are merged through LDS into one partial result
 // (reference maximum M, normaliser L, unnormalised output O) per head.  Only slots below
 // min(pos + 1, W) hold positions of the window; the others are masked, and their V entries
@@ -390,9 +390,9 @@ __global__ void __launch_bounds__(256, 2) attn_dec_kernel(AttnDecodeArgs a) {
     const uint16_t* kseq = static_cast<const uint16_t*>(a.kc) + (size_t)n * (a.Wc / 32) * kTileElems;
     const uint16_t* vseq = static_cast<const uint16_t*>(a.vc) + (size_t)n * (a.Wc / 32) * kTileElems;
 
-    int ntile = 0;   // this wave's tiles holding a slot of the window (a prefix of its four)
+    int ntile = 0;   // this wave's tiles holding a slot of the window (a prefix of its tpw)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ntile += ((sp * 16 + 4 * i + wv) * 32 < nvalid) ? 1 : 0;
+    for (int i = 0; i < 4; ++i) ntile += (i < a.tpw && (sp * 4 * a.tpw + 4 * i + wv) * 32 < nvalid) ? 1 : 0;
 
     // Pass 1: scores of the wave's tiles, kept in registers, and their exact maximum per head
     // (no running rescale: branches stay around loads and scores, never around accumulation).
@@ -401,7 +401,7 @@ __global__ void __launch_bounds__(256, 2) attn_dec_kernel(AttnDecodeArgs a) {
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int tile = sp * 16 + 4 * i + wv, s0 = tile * 32;
+        const int tile = sp * 4 * a.tpw + 4 * i + wv, s0 = tile * 32;
         if (i < ntile) {
             const uint16_t* kt = kseq + (size_t)tile * kTileElems;
             bf16x8 kf[16];
@@ -439,7 +439,7 @@ __global__ void __launch_bounds__(256, 2) attn_dec_kernel(AttnDecodeArgs a) {
     // Pass 2: O^T += V^T P^T over the same tiles; a tile past the window contributes zeros
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int tile = sp * 16 + 4 * i + wv, s0 = tile * 32;
+        const int tile = sp * 4 * a.tpw + 4 * i + wv, s0 = tile * 32;
         bf16x8 vf[16];
         if (i < ntile) {
             const uint16_t* vt = vseq + (size_t)tile * kTileElems;

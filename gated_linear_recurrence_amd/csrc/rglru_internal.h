@@ -122,6 +122,7 @@ struct AttnDecodeArgs {
     float* part;         // workspace: partial results [N][nsplit][Hq][2 + 256]
     void* o;             // [N][Hq * 256]
     int N, Hq, W, Wc, nsplit;
+    int tpw;             // 32-slot tiles per wave (1, 2 or 4): 128 tpw slots per split
     float rope_base;
 };
 
@@ -163,6 +164,13 @@ struct BwdArgs {
 size_t backward_workspace_bytes(int B, int T, int D, int H);
 hipError_t launch_prefill_backward(const BwdArgs& a, hipStream_t s);
 hipError_t launch_geglu(void* gate, const void* up, size_t n, hipStream_t s);  // n % 8 == 0
-constexpr int kAttnDecSlotsPerSplit = 512;  // cache slots per decode workgroup
+// Decode attention: 32-slot tiles per wave (four waves per workgroup, so 128 tpw cache slots per
+// workgroup).  Four for batches of 64 or more; fewer for small batches, whose windows would
+// otherwise be read by only a few compute units.
+inline int attn_dec_tiles_per_wave(long long N) { return N >= 64 ? 4 : (N >= 16 ? 2 : 1); }
+inline long long attn_dec_nsplit(long long N, long long window) {
+    const long long slots = 128LL * attn_dec_tiles_per_wave(N);
+    return (window + slots - 1) / slots;
+}
 
 }  // namespace rglru

@@ -277,9 +277,10 @@ size_t rglru_local_attention_cache_bytes(int32_t N, int32_t window);
  *   workspace, ws_bytes  at least rglru_local_attention_decode_workspace_bytes(N, n_heads,
  *                        window); no initialisation needed
  * N >= 1, 1 <= n_heads <= 16, window >= 1 and rope_base > 1, else RGLRU_ERR_SHAPE; window < 2^22
- * and N * ceil(window / 512) < 2^24, else RGLRU_ERR_UNSUPPORTED.  No argument may overlap
- * another (q, k and v may overlap each other).  Deterministic: the window is split in fixed
- * chunks of 512 slots whose partial results are combined in chunk order.
+ * and N * ceil(window / S) < 2^24, else RGLRU_ERR_UNSUPPORTED, with S = 512 cache slots for
+ * N >= 64, 256 for 16 <= N < 64 and 128 below.  No argument may overlap another (q, k and v
+ * may overlap each other).  Deterministic: the window is split in fixed chunks of S slots whose
+ * partial results are combined in chunk order.
  */
 size_t rglru_local_attention_decode_workspace_bytes(int32_t N, int32_t n_heads, int32_t window);
 int rglru_local_attention_decode(int32_t N, int32_t n_heads, int32_t window, float rope_base,

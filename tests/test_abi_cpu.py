@@ -268,8 +268,12 @@ def test_attention_cache_and_decode_sizes(lib):
     assert lib.rglru_local_attention_cache_bytes(0, 64) == 0
     assert lib.rglru_local_attention_cache_bytes(1, 0) == 0
     f = lib.rglru_local_attention_decode_workspace_bytes
-    # q after RoPE, then per 512-slot split and head: max, normaliser and 256 outputs (fp32)
+    # q after RoPE, then per split and head: max, normaliser and 256 outputs (fp32); a split is
+    # 512 cache slots for N >= 64, 256 for 16 <= N < 64 and 128 below
     assert f(256, 10, 2048) == 256 * 10 * 512 + 256 * 4 * 10 * 258 * 4
+    assert f(64, 10, 2048) == 64 * 10 * 512 + 64 * 4 * 10 * 258 * 4
+    assert f(16, 10, 2048) == 16 * 10 * 512 + 16 * 8 * 10 * 258 * 4
+    assert f(1, 10, 2048) == 10 * 512 + 16 * 10 * 258 * 4
     assert f(1, 1, 1) == 512 + 258 * 4
     assert f(0, 1, 64) == 0 and f(1, 0, 64) == 0
 

@@ -251,6 +251,7 @@ def _check_decode(outs, inputs, W, label):
     (3, 10, 64, 50, 40),      # the ring wraps during decoding; window not a multiple of 512
     (2, 4, 2048, 2040, 20),   # the 2B window, crossed at position 2048
     (2, 16, 100, 0, 45),      # from an empty cache, 16 heads, window not a multiple of 32
+    (20, 4, 600, 590, 12),    # 16 <= N < 64: 256-slot splits, the last one ragged
     (1, 1, 1, 5, 6),          # window 1
 ])
 def test_attention_decode_matches_oracle(N, Hq, W, T0, steps):
