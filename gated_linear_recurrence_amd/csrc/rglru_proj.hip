@@ -317,7 +317,7 @@ __global__ void __launch_bounds__(256) proj_splitk_reduce_kernel(ProjGemmArgs g)
 #pragma unroll
         for (int k = 0; k < 8; ++k) v[k] = 0.0f;
     }
-    // the bias joins first: the partials are then added in split order, as one GEMM adds k-steps
+    // the partials are added in split order (as one GEMM adds its k-steps), then the bias
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int s = 0; s < g.ksplit; ++s) {
         const float4* p = reinterpret_cast<const float4*>(g.part + ((size_t)s * g.M + m) * ntot + n);
