@@ -765,7 +765,9 @@ def main():
                    "block": w.bs, "state": "fp32", "h0_std": w.h0_std},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
-                     "kernel": PREFILL_KERNEL, "algorithmic_bytes": nbytes},
+                     "kernel": PREFILL_KERNEL, "algorithmic_bytes": nbytes,
+                     "timed": "whole rglru_prefill calls on the launch stream (HIP events): the "
+                              "look-back reset kernel and the scan kernel"},
     }
     if not args.no_extras:
         w2 = synth.WORKLOADS[synth.PREFILL_2B]
@@ -778,6 +780,22 @@ def main():
             "ms_flushed": ms2f, "hbm_frac_flushed": b2 / (ms2f * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "note": "34 MB working set fits the 256 MB Infinity Cache: 'ms' is back-to-back "
                     "launches, 'ms_flushed' the median single launch after a 512 MB write"}
+        # the 9B-scale long-context prefill (B=2, T=65536, D=4096, 16 heads) and the tiny fp32
+        # block (B=1, T=256, D=256): same call, same roofline arithmetic
+        for key, wk, reps in (("prefill_9b_long", synth.WORKLOADS[synth.LONG_9B],
+                               max(args.steps // 2, 5)),
+                              ("prefill_tiny_fp32", synth.WORKLOADS[synth.TINY],
+                               max(args.steps, 50))):
+            msk = time_prefill(wk, wk.B, wk.T, reps, args.warmup, torch, binding)
+            bk = algorithmic_bytes(wk, wk.B, wk.T)
+            gbs = bk / (msk * 1e-3) / 1e9
+            line[key] = {
+                "workload": wk.name, "ms": msk,
+                "tokens·channels/s": wk.B * wk.T * wk.D / (msk * 1e-3),
+                "dtype": "bf16" if wk.dtype == synth.BF16 else "f32",
+                "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes": bk,
+                             "kernel": "one rglru_prefill call (look-back reset + scan kernel)"}}
         wd = synth.WORKLOADS[synth.DECODE_2B]
         eager_us, graph_us = time_decode(wd, wd.B, wd.T, torch, binding, split=True)
         f_eager, f_graph = time_decode(wd, wd.B, wd.T, torch, binding, split=False)

@@ -251,11 +251,11 @@ def rglru_prefill_workspace_init(ws: torch.Tensor):
 
 
 class Workspace:
-    """A reusable prefill workspace (uint8 device tensor, initialised once)."""
+    """A reusable prefill workspace (uint8 device tensor; the library prepares it at each call,
+    so its contents never matter)."""
 
     def __init__(self, nbytes: int, device):
         self.t = torch.empty(max(int(nbytes), 4096), dtype=torch.uint8, device=device)
-        rglru_prefill_workspace_init(self.t)
 
     @property
     def nbytes(self) -> int:

@@ -599,9 +599,9 @@ int rglru_prefill_workspace_flags(void* workspace, size_t ws_bytes, uint32_t* fl
     hipStream_t s = (hipStream_t)stream;
     uint32_t* hdr = static_cast<uint32_t*>(workspace);
     static const uint32_t zero = 0;
-    hipError_t e = hipMemcpyAsync(flags_out, hdr + 1, sizeof(uint32_t), hipMemcpyDeviceToHost, s);
+    hipError_t e = hipMemcpyAsync(flags_out, hdr + kErrWord, sizeof(uint32_t), hipMemcpyDeviceToHost, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
-    if (e == hipSuccess) e = hipMemcpyAsync(hdr + 1, &zero, sizeof(uint32_t), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(hdr + kErrWord, &zero, sizeof(uint32_t), hipMemcpyHostToDevice, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     return e == hipSuccess ? RGLRU_OK : hip_fail(e);
 }

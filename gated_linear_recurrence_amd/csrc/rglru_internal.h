@@ -9,11 +9,11 @@ namespace rglru {
 
 constexpr int kSeg = 64;              // tokens per prefill time segment (one workgroup)
 constexpr size_t kWsHeader = 4096;    // workspace header bytes (counters and error flags)
-// header words: [0] error flags, [1] finished workgroups, [kTicketWord + h] ticket counter of head h
+// header words: [0] error flags of the latest call, [kTicketWord + h] ticket counter of head h;
+// every prefill call clears the header and the carry words it uses before its scan kernel runs
 constexpr int kErrWord = 0;
-constexpr int kDoneWord = 1;
 constexpr int kTicketWord = 16;
-constexpr size_t kZeroBlock = 2048;  // header bytes [2048, 4096) stay zero: a zero source for copies
+constexpr size_t kZeroBlock = 2048;  // the ticket counters end before header byte 2048
 constexpr int kMaxHeads = (int)(kZeroBlock / 4) - kTicketWord;
 
 struct PrefillArgs {
@@ -32,7 +32,7 @@ struct PrefillArgs {
     const void* conv0;
     void* conv_last;
     unsigned long long* words;  // carry words [S][B][D]
-    unsigned* header;           // see kErrWord, kDoneWord, kTicketWord
+    unsigned* header;           // see kErrWord, kTicketWord
     int B, T, D, H, S;
     int n_units;                // S * B * H units (generic kernel: one workgroup each)
     int wph;                    // persistent kernel: workgroups per head

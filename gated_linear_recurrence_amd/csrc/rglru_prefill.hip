@@ -16,6 +16,7 @@
 //      segments; carries are always folded forward from an inclusive word, so the result
 //      does not depend on timing.
 //   5. fix-up h_t = b_t + p_t * carry, out_t = h_t * gelu_tanh(y_t), store.
+#include <algorithm>
 #include <atomic>
 #include <type_traits>
 
@@ -53,9 +54,7 @@ __device__ __forceinline__ void st_word(unsigned long long* p, unsigned long lon
 // window is read before this segment's aggregate is published so that waiting for the reads
 // never waits for that store.
 __device__ float look_back(unsigned long long* wself, size_t wstride, int seg, unsigned long long w1,
-                           float A_seg, float B_seg, bool publish_aggregate, unsigned* header,
-                           bool& pred_inclusive) {
-    pred_inclusive = true;
+                           float A_seg, float B_seg, bool publish_aggregate, unsigned* header) {
     if (w_ready(w1) && w_inclusive(w1)) return w_B(w1);
     // the stride goes through an opaque SGPR copy: the window offsets are then formed here with
     // scalar ops, not hoisted out of the caller's loop (where they would be spilled to VGPR lanes)
@@ -88,7 +87,6 @@ __device__ float look_back(unsigned long long* wself, size_t wstride, int seg, u
                 if (k == kinc) c = w_B(win[k]);
                 else if (k < kinc) c = __builtin_fmaf(w_A(win[k]), c, w_B(win[k]));
             }
-            pred_inclusive = (kinc == 0);
             return c;
         }
         if (it >= kSpinLimit) {
@@ -97,26 +95,6 @@ __device__ float look_back(unsigned long long* wself, size_t wstride, int seg, u
         }
         __builtin_amdgcn_s_sleep(1);
     }
-}
-
-// Reset the predecessor's word for the next launch.  Only once its inclusive value has been
-// seen: a carry folded from its aggregate may have been found before the predecessor's own
-// inclusive store, and a reset issued earlier could land before that store and leave a stale
-// word behind.  The predecessor has started (ticket order) and finishes its look-back without
-// waiting on this unit, so the wait ends.
-__device__ void retire_word(unsigned long long* wprev, bool seen_inclusive, unsigned* header) {
-    if (!seen_inclusive) {
-        for (unsigned it = 0;; ++it) {
-            const unsigned long long w = ld_word(wprev);
-            if (w_ready(w) && w_inclusive(w)) break;
-            if (it >= kSpinLimit) {
-                atomicOr(&header[kErrWord], 2u);
-                return;
-            }
-            __builtin_amdgcn_s_sleep(1);
-        }
-    }
-    st_word(wprev, kNotReady);
 }
 
 // LDS row of token t (0..63): tokens 32..63 have row bits 2..3 flipped so that the MFMA
@@ -365,15 +343,13 @@ __global__ void __launch_bounds__(2 * BS) prefill_kernel(PrefillArgs a) {
         const size_t wstride = (size_t)a.B * D;
         unsigned long long* wself = a.words + (size_t)seg * wstride + (size_t)b * D + ch;
         if (hh == 0) {
-            bool pred_inc = true;
             if (seg == 0) {
                 carry = a.h0 ? a.h0[(size_t)b * D + ch] : 0.0f;
             } else {
                 carry = look_back(wself, wstride, seg, ld_word(wself - wstride), A_seg, B_seg, !last,
-                                  a.header, pred_inc);
+                                  a.header);
             }
             if (!last) st_word(wself, make_word(A_seg, __builtin_fmaf(A_seg, carry, B_seg), true));
-            if (seg > 0) retire_word(wself - wstride, pred_inc, a.header);
         }
     }
     carry = __shfl(carry, ln);
@@ -408,15 +384,6 @@ __global__ void __launch_bounds__(2 * BS) prefill_kernel(PrefillArgs a) {
         if (act) {
             const size_t c0 = (size_t)head * BS + cg * 8;
             S::store8(static_cast<ST*>(a.conv_last) + ((size_t)b * 3 + jr) * D + c0, v);
-        }
-    }
-
-    // the last workgroup to finish resets the counters for the next call on this workspace
-    if (tid == 0) {
-        const unsigned done = atomicAdd(&a.header[kDoneWord], 1u);
-        if (done == (unsigned)a.n_units - 1) {
-            atomicExch(&a.header[kTicketWord], 0u);
-            atomicExch(&a.header[kDoneWord], 0u);
         }
     }
 }
@@ -801,14 +768,10 @@ prefill_bf16_kernel(PrefillArgs a) {
             }
         }
         float carry = h0v;
-        bool pred_inc = true;
-        if (hh == 0 && seg > 0) carry = look_back(wself, wstride, seg, w1, A_seg, B_seg, false, a.header, pred_inc);
+        if (hh == 0 && seg > 0) carry = look_back(wself, wstride, seg, w1, A_seg, B_seg, false, a.header);
         wait_vmem_all();  // the carry's loads (nothing else is outstanding): no wait after the stores
         const unsigned long long winc = make_word(A_seg, __builtin_fmaf(A_seg, carry, B_seg), true);
-        if (hh == 0) {
-            if (!last) st_word(wself, winc);
-            if (seg > 0) retire_word(wprev, pred_inc, a.header);
-        }
+        if (hh == 0 && !last) st_word(wself, winc);
         carry = __shfl(carry, ln);
         const float state_in = hh ? __builtin_fmaf(p_lo, carry, b_lo) : carry;
 
@@ -874,13 +837,6 @@ prefill_bf16_kernel(PrefillArgs a) {
     }
 
     wait_vmem_all();  // no copy into LDS may outlive the workgroup
-    if (tid0 == 0) {
-        const unsigned done = atomicAdd(&a.header[kDoneWord], 1u);
-        if (done == G - 1) {
-            for (int h = 0; h < a.H; ++h) atomicExch(&a.header[kTicketWord + h], 0u);
-            atomicExch(&a.header[kDoneWord], 0u);
-        }
-    }
 }
 
 // T = 0: state passes through (h_last = h0 or 0, conv_last = conv0 or 0).
@@ -898,6 +854,29 @@ __global__ void prefill_empty_kernel(PrefillArgs a) {
 __global__ void workspace_init_kernel(unsigned long long* p, size_t n_words) {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n_words) p[i] = (i < kWsHeader / 8) ? 0ull : kNotReady;
+}
+
+// The look-back state of one call, set up on the stream before the scan kernel: the header
+// (error flags, ticket counters, zero block) cleared, and every carry word the call can read
+// (segments 0 .. S-2; the last segment publishes none) set to "not ready" with 16-byte stores.
+// Whatever the buffer held before (a fresh allocation, another shape's words, a call that
+// stopped at a spin limit) is overwritten, so no call depends on an earlier one.
+__global__ void __launch_bounds__(256) ws_reset_kernel(unsigned* header, uint4* words, size_t n16) {
+    if (blockIdx.x == 0) {
+        for (int i = threadIdx.x; i < (int)(kWsHeader / 4); i += 256) header[i] = 0u;
+    }
+    const uint4 nr = make_uint4(~0u, ~0u, ~0u, ~0u);
+    const size_t stride = (size_t)gridDim.x * 256;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride) words[i] = nr;
+}
+
+hipError_t launch_ws_reset(const PrefillArgs& a, hipStream_t s) {
+    // words of segments 0 .. S-2, two per 16-byte store (B * D is even: D % 8 == 0)
+    const size_t n16 = (size_t)(a.S - 1) * (size_t)a.B * (size_t)a.D / 2;
+    const size_t blocks = std::min<size_t>(std::max<size_t>((n16 + 1023) / 1024, 1), 4096);
+    hipLaunchKernelGGL(ws_reset_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a.header,
+                       reinterpret_cast<uint4*>(a.words), n16);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -918,6 +897,8 @@ int device_cu_count() {
 
 hipError_t launch_prefill(const PrefillArgs& a_in, int dtype, int bs, hipStream_t s) {
     PrefillArgs a = a_in;
+    const hipError_t er = launch_ws_reset(a, s);
+    if (er != hipSuccess) return er;
     if (dtype == 1) {
         // persistent: one workgroup per CU, the same number for every head
         const int ncu = device_cu_count();

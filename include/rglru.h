@@ -88,16 +88,21 @@ typedef struct rglru_params {
 
 /*
  * Workspace management (no passage of the pages: these exist for the chunked scan's carries).
- * Bytes of device workspace rglru_prefill needs for this shape (0 on invalid shapes).
- * The workspace holds the cross-workgroup carry words of the time-segmented scan.  Before
- * its first use a workspace must be initialised once with rglru_prefill_workspace_init;
- * every completed rglru_prefill leaves it initialised again, so it can be reused for any
- * shape that fits.  Calls sharing one workspace must be ordered on one stream.
+ * Bytes of device workspace rglru_prefill needs for this shape (0 on invalid shapes):
+ * a 4096-byte header (error flags and ticket counters) and one 8-byte carry word per
+ * (64-token segment, sequence, channel).  The workspace needs no initialisation by the caller:
+ * every prefill call first clears the header and sets the carry words it will use to "not
+ * ready", on its own stream, with a fill kernel (no memset node, so the call may be captured
+ * in a graph).  Any contents are therefore fine, including a fresh allocation or a buffer left
+ * by a call of another shape.  The fill writes 8 * (ceil(T/64) - 1) * B * D bytes.
+ * Calls sharing one workspace must be ordered on one stream (concurrent calls race).
  */
 size_t rglru_prefill_workspace_bytes(int32_t B, int32_t T, int32_t D, int32_t n_heads,
                                      int32_t dtype);
 
-/* Initialise a workspace of ws_bytes bytes on `stream` (asynchronous). */
+/* Fills a whole workspace of ws_bytes bytes on `stream` (asynchronous): header zero, carry
+ * words "not ready".  Never required (every prefill call prepares the part it uses); kept so
+ * that callers of earlier versions of this header keep working. */
 int rglru_prefill_workspace_init(void *workspace, size_t ws_bytes, void *stream);
 
 /*
@@ -199,8 +204,8 @@ int rglru_linear(int32_t M, int32_t K, int32_t N, const void *x, const void *w, 
 /*
  * Bytes of device workspace rglru_block_prefill needs: a prefill workspace (see
  * rglru_prefill_workspace_bytes) at offset 0, then room for the two branches and their
- * product ([B][T][D] each).  Initialise it once with rglru_prefill_workspace_init(workspace,
- * ws_bytes); every completed call leaves it initialised again.  0 on invalid shapes.
+ * product ([B][T][D] each).  No initialisation is needed (the prefill part is prepared by every
+ * call, as for rglru_prefill).  0 on invalid shapes.
  */
 size_t rglru_block_prefill_workspace_bytes(int32_t B, int32_t T, int32_t D, int32_t n_heads,
                                            int32_t D_model, int32_t dtype);
@@ -211,7 +216,7 @@ size_t rglru_block_prefill_workspace_bytes(int32_t B, int32_t T, int32_t D, int3
  * where path is rglru_prefill's operation on the two branches.
  *   x_in  [B][T][D_model] block input;  out [B][T][D_model] block output (bf16)
  *   h0, h_last, conv0, conv_last  as for rglru_prefill (the conv window holds linear_x outputs)
- *   workspace, ws_bytes  at least rglru_block_prefill_workspace_bytes(...), initialised once
+ *   workspace, ws_bytes  at least rglru_block_prefill_workspace_bytes(...)
  * bf16 storage only; D % 256 == 0 and D_model % 256 == 0, else RGLRU_ERR_UNSUPPORTED (and the
  * limits of rglru_prefill apply).  out must not overlap x_in, the state buffers or the
  * workspace; the workspace must not overlap any other argument.
@@ -369,8 +374,8 @@ int rglru_mlp(const rglru_mlp_params *m, int32_t M, const void *x, void *out, vo
 /*
  * The residual layer around the recurrent block (prefill over T tokens): temporal is
  * rglru_block_prefill's operation (with its state arguments, as there).  x_in, out
- * [B][T][D_model].  The workspace starts with the recurrent block's own workspace: initialise it
- * once with rglru_prefill_workspace_init(workspace, ws_bytes).  out must not overlap x_in.
+ * [B][T][D_model].  The workspace starts with the recurrent block's own workspace; no
+ * initialisation is needed.  out must not overlap x_in.
  */
 size_t rglru_recurrent_layer_workspace_bytes(int32_t B, int32_t T, int32_t D, int32_t n_heads,
                                              int32_t D_model, int32_t F);
@@ -446,11 +451,10 @@ int rglru_prefill_backward(const rglru_params *p, int32_t B, int32_t T, const vo
                            size_t ws_bytes, void *stream);
 
 /*
- * Diagnostics of a prefill workspace: copies its error flags to *flags_out (0 = none) and
- * clears them.  Synchronous (waits for `stream`).  Bit 0: a carry wait exceeded its bound
- * (the affected outputs are NaN).  Bit 1: a wait for a predecessor's inclusive word before
- * resetting it exceeded its bound (results are correct, but the workspace may hold a stale
- * word: initialise it again before reuse).
+ * Diagnostics of a prefill workspace: copies the error flags of the latest prefill call on it
+ * to *flags_out (0 = none) and clears them.  Synchronous (waits for `stream`).  Bit 0: a carry
+ * wait exceeded its bound (the affected outputs are NaN).  The next prefill call clears the
+ * flags in any case.
  */
 int rglru_prefill_workspace_flags(void *workspace, size_t ws_bytes, uint32_t *flags_out,
                                   void *stream);

@@ -243,6 +243,8 @@ def test_layers_2b_batched_full_size_sampled():
 @pytest.mark.parametrize("D,nh,Dm,F,N,T0,steps", [
     (512, 2, 512, 768, 3, 40, 6),
     (2560, 10, 2560, 7680, 2, 20, 3),     # the 2B widths
+    (2560, 10, 2560, 7680, 1, 20, 3),     # one row: the row GEMV with the residual epilogue
+    (2560, 10, 2560, 7680, 4, 20, 3),     # four rows: the row GEMV's widest case
 ])
 def test_recurrent_layer_decode_continues_prefill(D, nh, Dm, F, N, T0, steps):
     from gated_linear_recurrence_amd import binding
@@ -272,6 +274,8 @@ def test_recurrent_layer_decode_continues_prefill(D, nh, Dm, F, N, T0, steps):
 @pytest.mark.parametrize("Dm,Hq,F,N,W,T0,steps", [
     (512, 2, 512, 3, 32, 40, 6),          # the ring wraps
     (2560, 10, 7680, 2, 2048, 20, 3),     # the 2B widths and window
+    (2560, 10, 7680, 1, 2048, 20, 3),     # one row
+    (2560, 10, 7680, 4, 2048, 20, 3),     # four rows
 ])
 def test_attention_layer_decode_continues_prefill(Dm, Hq, F, N, W, T0, steps):
     from gated_linear_recurrence_amd import binding
