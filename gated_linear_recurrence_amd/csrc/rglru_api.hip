@@ -83,7 +83,8 @@ size_t rglru_prefill_workspace_bytes(int32_t B, int32_t T, int32_t D, int32_t n_
                                      int32_t dtype) {
     if (B < 1 || T < 0 || D < 1 || n_heads < 1 || D % n_heads != 0) return 0;
     if (dtype != RGLRU_F32 && dtype != RGLRU_BF16) return 0;
-    return kWsHeader + n_segments(T) * (size_t)B * (size_t)D * sizeof(unsigned long long);
+    // carry words of every segment but the last (which publishes none)
+    return kWsHeader + (n_segments(T) - 1) * (size_t)B * (size_t)D * sizeof(unsigned long long);
 }
 
 int rglru_prefill_workspace_init(void* workspace, size_t ws_bytes, void* stream) {

@@ -90,7 +90,7 @@ typedef struct rglru_params {
  * Workspace management (no passage of the pages: these exist for the chunked scan's carries).
  * Bytes of device workspace rglru_prefill needs for this shape (0 on invalid shapes):
  * a 4096-byte header (error flags and ticket counters) and one 8-byte carry word per
- * (64-token segment, sequence, channel).  The workspace needs no initialisation by the caller:
+ * (64-token segment except the last, sequence, channel).  The workspace needs no initialisation by the caller:
  * every prefill call first clears the header and sets the carry words it will use to "not
  * ready", on its own stream, with a fill kernel (no memset node, so the call may be captured
  * in a graph).  Any contents are therefore fine, including a fresh allocation or a buffer left

@@ -64,9 +64,13 @@ def _prefill(lib, p, B=2, T=100, x=X, y=Y, out=OUT, h0=H0, hl=HL, c0=C0, cl=CL, 
 
 def test_workspace_bytes(lib):
     f = lib.rglru_prefill_workspace_bytes
-    assert f(8, 8192, 2560, 10, 1) == 4096 + 128 * 8 * 2560 * 8
-    assert f(1, 1, 256, 2, 0) == 4096 + 1 * 1 * 256 * 8
-    assert f(1, 0, 256, 2, 0) == 4096 + 256 * 8
+    # header plus one word per (segment but the last, sequence, channel)
+    assert f(8, 8192, 2560, 10, 1) == 4096 + 127 * 8 * 2560 * 8
+    assert f(2, 65536, 4096, 16, 1) == 4096 + 1023 * 2 * 4096 * 8
+    assert f(1, 65, 256, 2, 0) == 4096 + 1 * 1 * 256 * 8
+    assert f(1, 64, 256, 2, 0) == 4096
+    assert f(1, 1, 256, 2, 0) == 4096
+    assert f(1, 0, 256, 2, 0) == 4096
     assert f(0, 10, 256, 2, 0) == 0
     assert f(1, -1, 256, 2, 0) == 0
     assert f(1, 10, 255, 2, 0) == 0
