@@ -35,7 +35,9 @@ EXPORTS = ["rglru_prefill_workspace_bytes", "rglru_prefill_workspace_init", "rgl
            "rglru_attention_layer_workspace_bytes", "rglru_attention_layer_prefill",
            "rglru_recurrent_layer_decode_workspace_bytes", "rglru_recurrent_layer_decode",
            "rglru_attention_layer_decode_workspace_bytes", "rglru_attention_layer_decode",
-           "rglru_prefill_backward_workspace_bytes", "rglru_prefill_backward"]
+           "rglru_prefill_backward_workspace_bytes", "rglru_prefill_backward",
+           "rglru_prefill_noalloc"]
+PREFILL_NOALLOC_MAX_BYTES = 64 << 20  # RGLRU_PREFILL_NOALLOC_MAX_BYTES
 
 _lock = threading.Lock()
 _lib = None
@@ -103,6 +105,8 @@ def load_library(path: str = LIB_PATH):
         lib.rglru_prefill_workspace_init.restype = ctypes.c_int
         lib.rglru_prefill.argtypes = [PP, I32, I32, P, P, P, P, P, P, P, P, SZ, P]
         lib.rglru_prefill.restype = ctypes.c_int
+        lib.rglru_prefill_noalloc.argtypes = [PP, I32, I32, P, P, P, P, P, P, P, P]
+        lib.rglru_prefill_noalloc.restype = ctypes.c_int
         lib.rglru_decode_workspace_bytes.argtypes = [I32, I32, I32]
         lib.rglru_decode_workspace_bytes.restype = SZ
         lib.rglru_decode_step.argtypes = [PP, I32, P, I64, P, I64, P, I64, P, P, P, SZ, P]
@@ -299,6 +303,32 @@ def rglru_prefill(p: Params, x, y, h0=None, conv0=None, *, out=None, h_last=None
                            _ptr(h_last), _ptr(conv0), _ptr(conv_last), _ptr(workspace.t),
                            workspace.nbytes, _stream())
     _check(lib, st, "rglru_prefill")
+    return out, h_last, conv_last
+
+
+def rglru_prefill_noalloc(p: Params, x, y, h0=None, conv0=None, *, out=None, h_last=None,
+                          conv_last=None, want_state: bool = True):
+    """rglru_prefill without a workspace: the library's static scratch holds the look-back
+    state (no device allocation by the library; outputs are allocated here when not given)."""
+    lib = load_library()
+    B, T, D = x.shape
+    _need(x, "x", p.dtype, (B, T, p.D), p.device)
+    _need(y, "y", p.dtype, (B, T, p.D), p.device)
+    _need(h0, "h0", torch.float32, (B, D), p.device)
+    _need(conv0, "conv0", p.dtype, (B, 3, D), p.device)
+    if out is None:
+        out = torch.empty_like(x)
+    _need(out, "out", p.dtype, (B, T, D), p.device)
+    if want_state:
+        if h_last is None:
+            h_last = torch.empty((B, D), dtype=torch.float32, device=p.device)
+        if conv_last is None:
+            conv_last = torch.empty((B, 3, D), dtype=p.dtype, device=p.device)
+    _need(h_last, "h_last", torch.float32, (B, D), p.device)
+    _need(conv_last, "conv_last", p.dtype, (B, 3, D), p.device)
+    st = lib.rglru_prefill_noalloc(ctypes.byref(p.c), B, T, _ptr(x), _ptr(y), _ptr(out),
+                                   _ptr(h0), _ptr(h_last), _ptr(conv0), _ptr(conv_last), _stream())
+    _check(lib, st, "rglru_prefill_noalloc")
     return out, h_last, conv_last
 
 

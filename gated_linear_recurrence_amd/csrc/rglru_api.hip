@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -100,9 +102,11 @@ int rglru_prefill_workspace_init(void* workspace, size_t ws_bytes, void* stream)
 namespace {
 
 // Every check rglru_prefill makes before it launches anything.
+// static_ws: the look-back state lives in the library's static scratch (rglru_prefill_noalloc),
+// so the workspace arguments are not checked here.
 int check_prefill(const rglru_params* p, int32_t B, int32_t T, const void* x, const void* y,
                   void* out, const float* h0, float* h_last, const void* conv0, void* conv_last,
-                  void* workspace, size_t ws_bytes) {
+                  void* workspace, size_t ws_bytes, bool static_ws = false) {
     int st = check_params(p, true);
     if (st != RGLRU_OK) return st;
     if (B < 1 || T < 0) return RGLRU_ERR_SHAPE;
@@ -120,7 +124,7 @@ int check_prefill(const rglru_params* p, int32_t B, int32_t T, const void* x, co
     const size_t n_h = (size_t)B * (size_t)p->D * sizeof(float);
     const size_t n_c = (size_t)B * 3 * (size_t)p->D * es;
     const size_t need = rglru_prefill_workspace_bytes(B, T, p->D, p->n_heads, p->dtype);
-    if (T > 0 && (!workspace || ws_bytes < need)) return RGLRU_ERR_WORKSPACE;
+    if (!static_ws && T > 0 && (!workspace || ws_bytes < need)) return RGLRU_ERR_WORKSPACE;
     // outputs: out vs every input; state outputs may alias their own input exactly
     if (overlap(out, n_act, x, n_act) || overlap(out, n_act, y, n_act) ||
         overlap(out, n_act, h0, n_h) || overlap(out, n_act, h_last, n_h) ||
@@ -134,7 +138,7 @@ int check_prefill(const rglru_params* p, int32_t B, int32_t T, const void* x, co
         overlap(conv_last, n_c, h0, n_h) ||
         (conv_last != conv0 && overlap(conv_last, n_c, conv0, n_c)))
         return RGLRU_ERR_ALIAS;
-    if (T > 0) {
+    if (T > 0 && !static_ws) {
         const void* ins[] = {x, y, out, h0, h_last, conv0, conv_last};
         const size_t lens[] = {n_act, n_act, n_act, n_h, n_h, n_c, n_c};
         for (int i = 0; i < 7; ++i)
@@ -177,6 +181,67 @@ int rglru_prefill(const rglru_params* p, int32_t B, int32_t T, const void* x, co
     a.words = reinterpret_cast<unsigned long long*>(static_cast<char*>(workspace) + kWsHeader);
     e = launch_prefill(a, p->dtype, p->D / p->n_heads, (hipStream_t)stream);
     return e == hipSuccess ? RGLRU_OK : hip_fail(e);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------------------------------
+// Allocation-free prefill: the look-back state (header and carry words) lives in a static
+// device array instead of a caller workspace.  Each GPU holds its own copy of the array until
+// the process ends, and every call on a GPU shares it, so calls that overlap on one GPU race.
+// In host code `scratch` only names the symbol: its device address on the current GPU is
+// looked up once per device (hipGetSymbolAddress) and only that address reaches the kernels.
+// Every call sets up the part it uses on its stream (header cleared, carry words "not
+// ready"), so nothing depends on what an earlier call left there.
+// ------------------------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kScratchBytes = RGLRU_PREFILL_NOALLOC_MAX_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// Device address of `scratch` on the current device.
+int scratch_address(void** addr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dev < 0 || dev >= kMaxDevices) return RGLRU_ERR_UNSUPPORTED;
+    void* ptr = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (ptr == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        ptr = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (ptr == nullptr) {
+            e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return hip_fail(e);
+            if (ptr == nullptr) return hip_fail(hipErrorInvalidSymbol);
+            g_scratch_addr[dev].store(ptr, std::memory_order_release);
+        }
+    }
+    *addr = ptr;
+    return RGLRU_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int rglru_prefill_noalloc(const rglru_params* p, int32_t B, int32_t T, const void* x,
+                          const void* y, void* out, const float* h0, float* h_last,
+                          const void* conv0, void* conv_last, void* stream) {
+    int st = check_prefill(p, B, T, x, y, out, h0, h_last, conv0, conv_last, nullptr, 0, true);
+    if (st != RGLRU_OK) return st;
+    const size_t need = rglru_prefill_workspace_bytes(B, T, p->D, p->n_heads, p->dtype);
+    if (need > kScratchBytes) return RGLRU_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (T > 0) {
+        st = scratch_address(&ws);
+        if (st != RGLRU_OK) return st;
+    }
+    return rglru_prefill(p, B, T, x, y, out, h0, h_last, conv0, conv_last, ws,
+                         T > 0 ? kScratchBytes : 0, stream);
 }
 
 size_t rglru_decode_workspace_bytes(int32_t N, int32_t D, int32_t dtype) {

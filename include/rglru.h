@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define RGLRU_ABI_VERSION 6
+#define RGLRU_ABI_VERSION 7
 
 enum rglru_dtype { RGLRU_F32 = 0, RGLRU_BF16 = 1 };
 
@@ -126,6 +126,24 @@ int rglru_prefill_workspace_init(void *workspace, size_t ws_bytes, void *stream)
 int rglru_prefill(const rglru_params *p, int32_t B, int32_t T, const void *x, const void *y,
                   void *out, const float *h0, float *h_last, const void *conv0, void *conv_last,
                   void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Prefill without a workspace argument, for callers that cannot allocate device memory (code
+ * under graph capture, tight serving loops, harnesses that forbid allocation).  The same
+ * operation, kernels and results as rglru_prefill (bitwise), with the look-back state in a
+ * static device array of RGLRU_PREFILL_NOALLOC_MAX_BYTES bytes inside the library: every GPU
+ * the library runs on holds one copy until the process ends.  The call allocates nothing.
+ * A call whose rglru_prefill_workspace_bytes(B, T, D, n_heads, dtype) exceeds the maximum
+ * returns RGLRU_ERR_WORKSPACE before any HIP call (the maximum covers B = 2, T = 65536,
+ * D = 4096; longer inputs are prefilled in pieces, carrying h and the conv window).
+ * All calls on one GPU share the array: calls that may overlap in time on one GPU (different
+ * streams or threads) race and must be ordered by the caller.  The stream must belong to the
+ * current device.  Other arguments and errors as for rglru_prefill.
+ */
+#define RGLRU_PREFILL_NOALLOC_MAX_BYTES ((size_t)64 << 20)
+int rglru_prefill_noalloc(const rglru_params *p, int32_t B, int32_t T, const void *x,
+                          const void *y, void *out, const float *h0, float *h_last,
+                          const void *conv0, void *conv_last, void *stream);
 
 /*
  * Bytes of the optional decode workspace for N sequences: 16 * ceil(N / 16) * D storage

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.rglru_abi_version() == 6
+    assert lib.rglru_abi_version() == 7
     for st in range(7):
         assert lib.rglru_status_string(st)
     assert lib.rglru_status_string(99) == b"unknown status"
@@ -512,3 +512,32 @@ def test_backward_workspace_and_validation(lib):
     assert call(outs=ptr[4:14] + [ptr[0]]) == ALIAS        # dconv0 over x
     assert call(outs=[ptr[4]] + [ptr[4] + 0x100] + ptr[6:15]) == ALIAS   # dx and dy overlap
     assert call(w=ptr[1]) == ALIAS                          # workspace over y
+
+
+def _noalloc(lib, p, B, T, base=1 << 36, step=1 << 36, **kw):
+    ptr = {k: base + i * step for i, k in enumerate(("x", "y", "out", "h0", "hl", "c0", "cl"))}
+    ptr.update(kw)
+    return lib.rglru_prefill_noalloc(ctypes.byref(p), B, T, ptr["x"], ptr["y"], ptr["out"],
+                                     ptr["h0"], ptr["hl"], ptr["c0"], ptr["cl"], None)
+
+
+def test_prefill_noalloc_validation(lib):
+    """The allocation-free prefill checks everything rglru_prefill checks, and rejects calls
+    whose look-back state exceeds its static scratch, before any HIP call."""
+    assert binding.PREFILL_NOALLOC_MAX_BYTES == 64 << 20
+    p = _params()
+    assert lib.rglru_prefill_noalloc(None, 1, 1, X, Y, OUT, None, None, None, None, None) == NULL
+    assert _noalloc(lib, p, 0, 100) == SHAPE
+    assert _noalloc(lib, p, 2, -1) == SHAPE
+    assert _noalloc(lib, p, 2, 100, x=None) == NULL
+    assert _noalloc(lib, p, 2, 100, x=(1 << 36) + 2) == UNSUP
+    assert _noalloc(lib, p, 2, 100, out=(1 << 36) + 64) == ALIAS
+    assert _noalloc(lib, _params(D=512, H=8), 2, 100) == UNSUP
+    big = _params(D=4096, H=16)
+    f = lib.rglru_prefill_workspace_bytes
+    # the 9B long-context shape fits (1023 segments publish words) ...
+    assert f(2, 65536, 4096, 16, 1) <= binding.PREFILL_NOALLOC_MAX_BYTES
+    # ... one more segment does not, and is refused before anything is launched
+    assert f(2, 65537, 4096, 16, 1) > binding.PREFILL_NOALLOC_MAX_BYTES
+    assert _noalloc(lib, big, 2, 65537) == WS
+    assert _noalloc(lib, big, 3, 65536) == WS
