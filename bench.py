@@ -719,6 +719,93 @@ def counter_summary(args):
     print(json.dumps(out))
 
 
+CENSUS_JSON = os.path.join(ROOT, "profiles", "prefill_bf16_kernel-2b-batched-census.json")
+CENSUS_PASSES = [
+    # (derived or base counters of one rocprofv3 --pmc pass; each fits the SQ/GRBM limits)
+    ["VALUBusy", "MfmaUtil", "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_BUSY_CYCLES"],
+    ["SQ_INSTS_VALU", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU",
+     "SQ_INSTS_VMEM", "SQ_WAVES", "SQ_LDS_BANK_CONFLICT"],
+    ["SQ_WAVE_CYCLES", "SQ_ACTIVE_INST_ANY", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS",
+     "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_VALU", "GRBM_GUI_ACTIVE"],
+]
+
+
+def census_summary(args):
+    """Per-launch SQ counters of the prefill kernel (from rocprofv3 --pmc CSVs of the passes in
+    CENSUS_PASSES) turned into per-element instruction counts, unit utilisations and the wave
+    state split; written to profiles/ with the commands that produced the CSVs."""
+    vals = {}
+    for path in args.census:
+        names = {r["Counter_Name"] for r in _rows(path) if "prefill_bf16_kernel" in r["Kernel_Name"]}
+        for n in names:
+            vals[n] = _mean_counter(path, "prefill_bf16_kernel", n)[0]
+    w = synth.WORKLOADS[synth.BATCHED_2B]
+    elems = w.B * w.T * w.D
+    per_elem = lambda n: vals[n] * 64.0 / elems if n in vals else None  # wave instr x 64 lanes
+    ratio = lambda a, b: vals[a] / vals[b] if a in vals and b in vals and vals[b] else None
+    out = {
+        "kernel": PREFILL_KERNEL, "workload": w.name, "kernel_source_hash": kernel_source_hash(),
+        "elements_per_launch": elems,
+        "counters_per_launch": vals,
+        "valu_busy_pct": vals.get("VALUBusy"), "mfma_util_pct": vals.get("MfmaUtil"),
+        "mfma_coexec_over_mfma_busy": ratio("SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES"),
+        "valu_instructions_per_element": per_elem("SQ_INSTS_VALU"),
+        "transcendental_f32_per_element": per_elem("SQ_INSTS_VALU_TRANS_F32"),
+        "mfma_instructions_per_element": per_elem("SQ_INSTS_MFMA"),
+        "lds_instructions_per_element": per_elem("SQ_INSTS_LDS"),
+        "salu_instructions_per_element": per_elem("SQ_INSTS_SALU"),
+        "vmem_instructions_per_element": per_elem("SQ_INSTS_VMEM"),
+        "wave_state": {"issuing": ratio("SQ_ACTIVE_INST_ANY", "SQ_WAVE_CYCLES"),
+                       "waiting_any": ratio("SQ_WAIT_ANY", "SQ_WAVE_CYCLES"),
+                       "waiting_to_issue": ratio("SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES"),
+                       "waiting_lds": ratio("SQ_WAIT_INST_LDS", "SQ_WAVE_CYCLES"),
+                       "valu_active": ratio("SQ_ACTIVE_INST_VALU", "SQ_WAVE_CYCLES")},
+        "lds_bank_conflict_cycles_per_lds_instruction": ratio("SQ_LDS_BANK_CONFLICT", "SQ_INSTS_LDS"),
+        "passes": CENSUS_PASSES, "commands": args.commands,
+        "definitions": "per element = wave instructions x 64 lanes / (B T D); VALUBusy and MfmaUtil "
+                       "are rocprofv3's derived counters; wave_state ratios are over SQ_WAVE_CYCLES",
+    }
+    with open(CENSUS_JSON, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    txt = CENSUS_JSON.replace(".json", ".txt")
+    with open(txt, "w") as f:
+        f.write("rocprofv3 --pmc counter census, %s on %s (bf16)\n" % (PREFILL_KERNEL, w.name))
+        f.write("kernel source hash %s\n\ncommands (from the repository root):\n" %
+                out["kernel_source_hash"])
+        for c in args.commands:
+            f.write("  %s\n" % c)
+        f.write("\nper launch (mean over the profiled dispatches):\n")
+        for k in sorted(vals):
+            f.write("  %-30s %16.1f\n" % (k, vals[k]))
+        f.write("\nderived:\n")
+        for k in ("valu_busy_pct", "mfma_util_pct", "mfma_coexec_over_mfma_busy",
+                  "valu_instructions_per_element", "transcendental_f32_per_element",
+                  "mfma_instructions_per_element", "lds_instructions_per_element",
+                  "salu_instructions_per_element", "vmem_instructions_per_element",
+                  "lds_bank_conflict_cycles_per_lds_instruction"):
+            v = out[k]
+            f.write("  %-46s %s\n" % (k, "n/a" if v is None else "%.4g" % v))
+        for k, v in out["wave_state"].items():
+            f.write("  wave_state.%-36s %s\n" % (k, "n/a" if v is None else "%.3f" % v))
+    print(json.dumps(out))
+
+
+def measured_census():
+    """MFMA and VALU utilisation of the prefill kernel from the committed census, or None when
+    it was taken on other kernel sources."""
+    try:
+        with open(CENSUS_JSON) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return {"valu_busy_pct": c.get("valu_busy_pct"), "mfma_util_pct": c.get("mfma_util_pct"),
+            "valu_instructions_per_element": c.get("valu_instructions_per_element"),
+            "source": "profiles/" + os.path.basename(CENSUS_JSON)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -736,9 +823,15 @@ def main():
     ap.add_argument("--copy-fetch")
     ap.add_argument("--copy-write")
     ap.add_argument("--commands", nargs="*", default=[])
+    ap.add_argument("--census-summary", action="store_true",
+                    help="write the SQ counter census under profiles/ from rocprofv3 CSVs (no GPU)")
+    ap.add_argument("--census", nargs="*", default=[])
     args = ap.parse_args()
     if args.counter_summary:
         counter_summary(args)
+        return
+    if args.census_summary:
+        census_summary(args)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path (--gpus %d "
@@ -767,7 +860,8 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "kernel": PREFILL_KERNEL, "algorithmic_bytes": nbytes,
                      "timed": "whole rglru_prefill calls on the launch stream (HIP events): the "
-                              "look-back reset kernel and the scan kernel"},
+                              "look-back reset kernel and the scan kernel",
+                     "census": measured_census()},
     }
     if not args.no_extras:
         w2 = synth.WORKLOADS[synth.PREFILL_2B]
