@@ -508,9 +508,17 @@ int rglru_local_attention(int32_t B, int32_t T, int32_t n_heads, int32_t window,
 
 size_t rglru_local_attention_decode_workspace_bytes(int32_t N, int32_t n_heads, int32_t window) {
     if (N < 1 || n_heads < 1 || window < 1 || window >= (1 << 22)) return 0;
-    const size_t nsplit = (size_t)attn_dec_nsplit(N, window);
-    return round256((size_t)N * n_heads * kAttnDh * 2) +
-           (size_t)N * nsplit * n_heads * (2 + kAttnDh) * sizeof(float);
+    // the window splits per sequence shrink as the batch grows (attn_dec_tiles_per_wave), so the
+    // size is taken as the largest over all batches up to N: a buffer sized for N fits any
+    // smaller batch.  Within one split regime the size grows with N.
+    size_t best = 0;
+    const int32_t cand[3] = {N, std::min<int32_t>(N, 15), std::min<int32_t>(N, 63)};
+    for (int32_t n : cand) {
+        const size_t nsplit = (size_t)attn_dec_nsplit(n, window);
+        best = std::max(best, round256((size_t)n * n_heads * kAttnDh * 2) +
+                                  (size_t)n * nsplit * n_heads * (2 + kAttnDh) * sizeof(float));
+    }
+    return best;
 }
 
 // the attention decode step: every check runs first; with launch = false nothing else happens
@@ -778,9 +786,16 @@ LayerBufs layer_bufs(void* workspace, size_t block_bytes, size_t M, int Dm) {
     return {base, base + act, base + 2 * act, base + 3 * act, nullptr, 0};
 }
 // the largest split-K partial buffer of a decode layer's GEMMs (M rows; N and K per GEMM)
+// Split-K partial bytes of the decode-time projections, the largest over all row counts up to
+// M (a buffer sized for M then fits any smaller batch): the split count changes only when the
+// number of 256-row tiles does, and within one tile count the bytes grow with the rows, so
+// the largest value is at M or at a multiple of 256 below it.
 size_t decode_part_bytes(int M, const int (*nk)[2], int n) {
     size_t b = 0;
-    for (int i = 0; i < n; ++i) b = std::max(b, proj_gemm_part_bytes(M, nk[i][0], nk[i][1]));
+    for (int m = std::min(M, 256);; m = std::min(m + 256, M)) {
+        for (int i = 0; i < n; ++i) b = std::max(b, proj_gemm_part_bytes(m, nk[i][0], nk[i][1]));
+        if (m >= M) break;
+    }
     return round256(b);
 }
 size_t layer_tail_bytes(size_t M, int Dm, int F) {

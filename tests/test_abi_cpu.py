@@ -273,10 +273,15 @@ def test_attention_cache_and_decode_sizes(lib):
     assert lib.rglru_local_attention_cache_bytes(1, 0) == 0
     f = lib.rglru_local_attention_decode_workspace_bytes
     # q after RoPE, then per split and head: max, normaliser and 256 outputs (fp32); a split is
-    # 512 cache slots for N >= 64, 256 for 16 <= N < 64 and 128 below
-    assert f(256, 10, 2048) == 256 * 10 * 512 + 256 * 4 * 10 * 258 * 4
-    assert f(64, 10, 2048) == 64 * 10 * 512 + 64 * 4 * 10 * 258 * 4
-    assert f(16, 10, 2048) == 16 * 10 * 512 + 16 * 8 * 10 * 258 * 4
+    # 512 cache slots for N >= 64, 256 for 16 <= N < 64 and 128 below; the size is the largest
+    # over batches up to N (so a buffer for N fits any smaller batch)
+    def per(n, Hq=10, W=2048):
+        slots = 512 if n >= 64 else (256 if n >= 16 else 128)
+        return (n * Hq * 512 + 255) // 256 * 256 + n * (-(-W // slots)) * Hq * 258 * 4
+    upto = lambda n: max(per(n), per(min(n, 15)), per(min(n, 63)))
+    assert f(256, 10, 2048) == 256 * 10 * 512 + 256 * 4 * 10 * 258 * 4 == upto(256)
+    assert f(64, 10, 2048) == 63 * 10 * 512 + 63 * 8 * 10 * 258 * 4 == upto(64)
+    assert f(16, 10, 2048) == 15 * 10 * 512 + 15 * 16 * 10 * 258 * 4 == upto(16)
     assert f(1, 10, 2048) == 10 * 512 + 16 * 10 * 258 * 4
     assert f(1, 1, 1) == 512 + 258 * 4
     assert f(0, 1, 64) == 0 and f(1, 0, 64) == 0
@@ -541,3 +546,18 @@ def test_prefill_noalloc_validation(lib):
     assert f(2, 65537, 4096, 16, 1) > binding.PREFILL_NOALLOC_MAX_BYTES
     assert _noalloc(lib, big, 2, 65537) == WS
     assert _noalloc(lib, big, 3, 65536) == WS
+
+
+def test_decode_workspace_sizes_fit_smaller_batches(lib):
+    """A decode workspace sized for N sequences also fits every smaller batch: the sizes never
+    decrease with N, although the attention's window splits and the projections' K splits
+    change with the batch."""
+    fa = lib.rglru_local_attention_decode_workspace_bytes
+    a = _attn_params(Dm=2560, Hq=10, window=2048)
+    fl = lambda n: lib.rglru_attention_layer_decode_workspace_bytes(ctypes.byref(a), n, 7680)
+    fr = lambda n: lib.rglru_recurrent_layer_decode_workspace_bytes(n, 2560, 2560, 7680)
+    for f in (lambda n: fa(n, 10, 2048), lambda n: fa(n, 4, 100), fl, fr):
+        sizes = [f(n) for n in list(range(1, 300)) + [511, 512, 513, 1000, 1024, 1025, 4096]]
+        assert all(b >= a_ for a_, b in zip(sizes, sizes[1:])), sizes
+    # the batches that used to shrink it: 63 -> 64 and 15 -> 16 sequences
+    assert fa(64, 10, 2048) >= fa(63, 10, 2048) and fa(16, 10, 2048) >= fa(15, 10, 2048)
