@@ -813,6 +813,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="prefill headline only")
+    ap.add_argument("--legs", default="all",
+                    help="comma-separated extras to run (default all): prefill_2b_single, "
+                         "prefill_9b_long, prefill_tiny_fp32, decode, conv1d_state_update, "
+                         "block_prefill, local_attention, residual_layers, backward")
     ap.add_argument("--copy-probe", action="store_true",
                     help="time a plain 1 GiB device-to-device copy instead (counter calibration)")
     ap.add_argument("--counter-summary", action="store_true",
@@ -863,7 +867,9 @@ def main():
                               "look-back reset kernel and the scan kernel",
                      "census": measured_census()},
     }
-    if not args.no_extras:
+    legs = None if args.legs == "all" else set(args.legs.split(","))
+    want = lambda leg: not args.no_extras and (legs is None or leg in legs)
+    if want("prefill_2b_single"):
         w2 = synth.WORKLOADS[synth.PREFILL_2B]
         ms2 = time_prefill(w2, w2.B, w2.T, max(args.steps, 50), args.warmup, torch, binding)
         ms2f = time_prefill(w2, w2.B, w2.T, 25, args.warmup, torch, binding, flush=True)
@@ -874,12 +880,11 @@ def main():
             "ms_flushed": ms2f, "hbm_frac_flushed": b2 / (ms2f * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "note": "34 MB working set fits the 256 MB Infinity Cache: 'ms' is back-to-back "
                     "launches, 'ms_flushed' the median single launch after a 512 MB write"}
-        # the 9B-scale long-context prefill (B=2, T=65536, D=4096, 16 heads) and the tiny fp32
-        # block (B=1, T=256, D=256): same call, same roofline arithmetic
-        for key, wk, reps in (("prefill_9b_long", synth.WORKLOADS[synth.LONG_9B],
-                               max(args.steps // 2, 5)),
-                              ("prefill_tiny_fp32", synth.WORKLOADS[synth.TINY],
-                               max(args.steps, 50))):
+    # the 9B-scale long-context prefill (B=2, T=65536, D=4096, 16 heads) and the tiny fp32
+    # block (B=1, T=256, D=256): same call, same roofline arithmetic
+    for key, wk, reps in (("prefill_9b_long", synth.WORKLOADS[synth.LONG_9B], max(args.steps // 2, 5)),
+                          ("prefill_tiny_fp32", synth.WORKLOADS[synth.TINY], max(args.steps, 50))):
+        if want(key):
             msk = time_prefill(wk, wk.B, wk.T, reps, args.warmup, torch, binding)
             bk = algorithmic_bytes(wk, wk.B, wk.T)
             gbs = bk / (msk * 1e-3) / 1e9
@@ -890,6 +895,7 @@ def main():
                 "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes": bk,
                              "kernel": "one rglru_prefill call (look-back reset + scan kernel)"}}
+    if want("decode"):
         wd = synth.WORKLOADS[synth.DECODE_2B]
         eager_us, graph_us = time_decode(wd, wd.B, wd.T, torch, binding, split=True)
         f_eager, f_graph = time_decode(wd, wd.B, wd.T, torch, binding, split=False)
@@ -902,16 +908,21 @@ def main():
                           "us_per_step_flushed": flushed_us,
                           "bytes_per_step": db,
                           "hbm_frac": db / (best * 1e-6) / 1e9 / HBM_PEAK_GBS}
+    if want("conv1d_state_update"):
         msc = time_conv_update(w, max(args.steps, 10), torch, binding)
         cb = conv_update_bytes(w, w.B, w.T)
         line["conv1d_state_update"] = {
             "workload": w.name + " (conv outputs for every token, window update)", "ms": msc,
             "algorithmic_bytes": cb, "algorithmic_GBs": cb / (msc * 1e-3) / 1e9,
             "hbm_frac": cb / (msc * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    if want("block_prefill"):
         line["block_prefill"] = time_block(w, max(args.steps // 2, 5), args.warmup, torch, binding)
+    if want("local_attention"):
         line["local_attention"] = time_attention(w, max(args.steps // 2, 5), args.warmup, torch,
                                                  binding)
+    if want("residual_layers"):
         line["residual_layers"] = time_layers(w, args.steps, args.warmup, torch, binding)
+    if want("backward"):
         line["backward"] = time_backward(w, max(args.steps // 4, 3), args.warmup, torch, binding)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
