@@ -5,7 +5,7 @@
 //
 // Intermediates are head-major, [H][B*T][256] (channel k of head h of token m at
 // (h * M + m) * 256 + k), so that the three block-diagonal products are plain GEMMs of the
-// projection kernel, one launch per head:
+// projection kernel, one launch per product with the heads as a batch:
 //   gates:      [Rpre | Ipre]_h = U_h [W_a[h]; W_x[h]]^T + b           (K = 256, two segments)
 //   input grad: dU_h = [dRpre | dIpre]_h [W_a[h]^T | W_x[h]^T]^T       (K = 512)
 //   weights:    [dW_a; dW_x]_h = [dRpre | dIpre]_h^T U_h                (K = B*T, split K, fp32)
@@ -66,7 +66,7 @@ BwdBufs carve(void* ws, int B, int T, int D, int H, size_t* total) {
     b.pbx = reinterpret_cast<float*>(take(nc * 4));
     b.pconv = reinterpret_cast<float*>(take(nc * 5 * 4));
     b.dW = reinterpret_cast<float*>(take((size_t)H * 2 * kBs * kBs * 4));
-    b.part_bytes = proj_gemm_part_bytes(2 * kBs, kBs, (int)M);
+    b.part_bytes = proj_gemm_part_bytes_batched(H, 2 * kBs, kBs, (int)M);
     b.part = reinterpret_cast<float*>(take(b.part_bytes));
     *total = off;
     return b;
@@ -77,13 +77,30 @@ __device__ __forceinline__ float sigm(float z) {
     return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * kLog2e));
 }
 
-// gelu_tanh(y) and its derivative from one tanh
+// gelu_tanh(y) and its derivative from one tanh; tanh(z) = 1 - 2 / (1 + e^(2z)) with the
+// hardware exp2 and reciprocal (saturates to +-1 for large |z|; about 1e-7 absolute error)
 __device__ __forceinline__ float2 gelu_and_grad(float y) {
     const float k = 0.7978845608028654f;
-    const float th = tanhf(k * (y + 0.044715f * y * y * y));
-    return make_float2(0.5f * y * (1.0f + th),
-                       0.5f * (1.0f + th) +
-                           0.5f * y * (1.0f - th * th) * k * (1.0f + 3.0f * 0.044715f * y * y));
+    const float z = k * __builtin_fmaf(0.044715f * y, y * y, y);
+    const float th = __builtin_fmaf(-2.0f, __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(2.0f * kLog2e * z)), 1.0f);
+    const float hp = 0.5f * (1.0f + th);
+    return make_float2(y * hp,
+                       __builtin_fmaf(0.5f * y * __builtin_fmaf(-th, th, 1.0f) * k,
+                                      __builtin_fmaf(3.0f * 0.044715f, y * y, 1.0f), hp));
+}
+
+// 1 - e^x for x <= 0, keeping full relative accuracy as x -> 0: a degree-7 Taylor polynomial
+// above -0.5 (truncation below 1e-7 relative), 1 - 2^(x log2 e) with the hardware exp2 below
+__device__ __forceinline__ float one_minus_exp(float x) {
+    float p = __builtin_fmaf(x, 1.0f / 5040.0f, 1.0f / 720.0f);
+    p = __builtin_fmaf(x, p, 1.0f / 120.0f);
+    p = __builtin_fmaf(x, p, 1.0f / 24.0f);
+    p = __builtin_fmaf(x, p, 1.0f / 6.0f);
+    p = __builtin_fmaf(x, p, 0.5f);
+    p = __builtin_fmaf(x, p, 1.0f);
+    const float small = -x * p;
+    const float large = 1.0f - __builtin_amdgcn_exp2f(x * kLog2e);
+    return x > -0.5f ? small : large;
 }
 
 __device__ __forceinline__ size_t hm(int h, size_t m, int k, size_t M) {
@@ -153,7 +170,7 @@ __device__ __forceinline__ Gate gate_of(float rp, float ip, float lsg) {
     g.i = sigm(ip);
     const float la = 8.0f * g.r * lsg;          // log a
     g.a = __builtin_amdgcn_exp2f(la * kLog2e);
-    g.m = sqrtf(-expm1f(2.0f * la));            // sqrt(1 - a^2), accurate as a -> 1
+    g.m = __builtin_amdgcn_sqrtf(one_minus_exp(2.0f * la));   // sqrt(1 - a^2), accurate as a -> 1
     return g;
 }
 __device__ __forceinline__ float log_sigmoid(float lam) { return -log1pf(expf(-lam)); }
@@ -207,6 +224,25 @@ __global__ void __launch_bounds__(256) bwd_carry_kernel(BwdArgs a, BwdBufs w) {
     a.dh0[idx] = cc;
 }
 
+// precise forms for the gradient pass: library tanh, expm1 and IEEE division (the derivative of
+// sqrt(1 - a^2) divides by it, so it keeps full relative accuracy as a -> 1)
+__device__ __forceinline__ float2 gelu_and_grad_precise(float y) {
+    const float k = 0.7978845608028654f;
+    const float th = tanhf(k * (y + 0.044715f * y * y * y));
+    return make_float2(0.5f * y * (1.0f + th),
+                       0.5f * (1.0f + th) +
+                           0.5f * y * (1.0f - th * th) * k * (1.0f + 3.0f * 0.044715f * y * y));
+}
+__device__ __forceinline__ Gate gate_of_precise(float rp, float ip, float lsg) {
+    Gate g;
+    g.r = sigm(rp);
+    g.i = sigm(ip);
+    const float la = 8.0f * g.r * lsg;
+    g.a = __builtin_amdgcn_exp2f(la * kLog2e);
+    g.m = sqrtf(-expm1f(2.0f * la));
+    return g;
+}
+
 // ---- per-element gradients of one chunk ----------------------------------------------------
 __global__ void __launch_bounds__(256) bwd_grad_kernel(BwdArgs a, BwdBufs w) {
     const int nch = a.T / kChunk;
@@ -229,7 +265,7 @@ __global__ void __launch_bounds__(256) bwd_grad_kernel(BwdArgs a, BwdBufs w) {
         for (int tt = 0; tt < kChunk; ++tt) {
             hp[tt] = hv;
             const size_t e = hm(h, m0 + tt, k, M);
-            const Gate g = gate_of(bf2f(w.R[e]), bf2f(w.I[e]), lsg);
+            const Gate g = gate_of_precise(bf2f(w.R[e]), bf2f(w.I[e]), lsg);
             hv = __builtin_fmaf(g.a, hv, g.m * g.i * bf2f(w.U[e]));
         }
     }
@@ -239,10 +275,10 @@ __global__ void __launch_bounds__(256) bwd_grad_kernel(BwdArgs a, BwdBufs w) {
     for (int tt = kChunk - 1; tt >= 0; --tt) {
         const size_t m = m0 + tt, e = hm(h, m, k, M);
         const float u = bf2f(w.U[e]);
-        const Gate g = gate_of(bf2f(w.R[e]), bf2f(w.I[e]), lsg);
+        const Gate g = gate_of_precise(bf2f(w.R[e]), bf2f(w.I[e]), lsg);
         const float ht = __builtin_fmaf(g.a, hp[tt], g.m * g.i * u);
         const float yv = bf2f(y[m * a.D + d]), dov = bf2f(dout[m * a.D + d]);
-        const float2 gg = gelu_and_grad(yv);
+        const float2 gg = gelu_and_grad_precise(yv);
         const float dh = __builtin_fmaf(dov, gg.x, cc);
         dy[m * a.D + d] = f2bf(dov * ht * gg.y);
         w.duv[e] = dh * g.m * g.i;
@@ -432,39 +468,46 @@ hipError_t launch_prefill_backward(const BwdArgs& a, hipStream_t s) {
                        dim3(256), 0, s, a, w);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     RG_LAUNCH(bwd_wtrans_kernel, (size_t)a.H * kBs * 2 * kBs);
-    for (int h = 0; h < a.H; ++h) {   // gate pre-activations
+    {   // gate pre-activations, all heads in one launch
         ProjGemmArgs g;
         memset(&g, 0, sizeof g);
-        g.A = w.U + (size_t)h * M * kBs;
-        g.W[0] = static_cast<const uint16_t*>(a.wa) + (size_t)h * kBs * kBs;
-        g.W[1] = static_cast<const uint16_t*>(a.wx) + (size_t)h * kBs * kBs;
-        g.b[0] = a.ba ? static_cast<const uint16_t*>(a.ba) + (size_t)h * kBs : nullptr;
-        g.b[1] = a.bx ? static_cast<const uint16_t*>(a.bx) + (size_t)h * kBs : nullptr;
-        g.C[0] = w.R + (size_t)h * M * kBs;
-        g.C[1] = w.I + (size_t)h * M * kBs;
+        g.A = w.U;
+        g.W[0] = a.wa;
+        g.W[1] = a.wx;
+        g.b[0] = a.ba;
+        g.b[1] = a.bx;
+        g.C[0] = w.R;
+        g.C[1] = w.I;
         g.Nw[0] = kBs; g.Nw[1] = kBs; g.nseg = 2; g.M = (int)M; g.K = kBs;
+        g.batch = a.H;
+        g.bsA = (long long)M * kBs; g.bsW = (long long)kBs * kBs; g.bsC = (long long)M * kBs;
+        g.bsb = kBs;
         if ((e = launch_proj_gemm(g, s)) != hipSuccess) return e;
     }
     RG_LAUNCH(bwd_chunk_agg_kernel, nlane);
     RG_LAUNCH(bwd_carry_kernel, (size_t)a.B * a.D);
     RG_LAUNCH(bwd_grad_kernel, nlane);
-    for (int h = 0; h < a.H; ++h) {   // gradient of u through the gates
+    {   // gradient of u through the gates, all heads in one launch
         ProjGemmArgs g;
         memset(&g, 0, sizeof g);
-        g.A = w.dRI + (size_t)h * M * 2 * kBs;
-        g.W[0] = w.Wt + (size_t)h * kBs * 2 * kBs;
-        g.C[0] = w.dUg + (size_t)h * M * kBs;
+        g.A = w.dRI;
+        g.W[0] = w.Wt;
+        g.C[0] = w.dUg;
         g.Nw[0] = kBs; g.nseg = 1; g.M = (int)M; g.K = 2 * kBs;
+        g.batch = a.H;
+        g.bsA = (long long)M * 2 * kBs; g.bsW = (long long)kBs * 2 * kBs; g.bsC = (long long)M * kBs;
         if ((e = launch_proj_gemm(g, s)) != hipSuccess) return e;
     }
-    for (int h = 0; h < a.H; ++h) {   // gate weight gradients (K = B * T, fp32)
+    {   // gate weight gradients (K = B * T, fp32), all heads in one launch
         ProjGemmArgs g;
         memset(&g, 0, sizeof g);
-        g.A = w.dRIt + (size_t)h * 2 * kBs * M;
-        g.W[0] = w.Ut + (size_t)h * kBs * M;
-        g.C[0] = w.dW + (size_t)h * 2 * kBs * kBs;
+        g.A = w.dRIt;
+        g.W[0] = w.Ut;
+        g.C[0] = w.dW;
         g.Nw[0] = kBs; g.nseg = 1; g.M = 2 * kBs; g.K = (int)M;
         g.part = w.part; g.part_bytes = w.part_bytes; g.c_f32 = 1;
+        g.batch = a.H;
+        g.bsA = (long long)2 * kBs * M; g.bsW = (long long)kBs * M; g.bsC = (long long)2 * kBs * kBs;
         if ((e = launch_proj_gemm(g, s)) != hipSuccess) return e;
     }
     RG_LAUNCH(bwd_conv_kernel, nlane / 8);

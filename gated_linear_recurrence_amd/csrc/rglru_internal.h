@@ -88,11 +88,18 @@ struct ProjGemmArgs {
     int gated;                   // two segments of equal width: C[0] = gelu_tanh(gate) * up,
                                  // from the bf16-rounded segment outputs (C[1] unused)
     const void* R;               // one segment: C = R + the rounded output, rounded again
+    // Tile kernel only: `batch` (>= 1; 0 means 1) independent GEMMs of this shape in one launch,
+    // item i at A + i bsA, W[o] + i bsW, C[o] + i bsC, b[o] + i bsb (elements), with its own
+    // split-K partials [ksplit][M][sum Nw] at part + i ksplit M sum Nw.
+    int batch;
+    long long bsA, bsW, bsC, bsb;
 };
 // true when launch_proj_gemm takes the row kernel (which alone supports gated and R)
 bool proj_gemm_rows(int M, int K);
 // fp32 partial-sum bytes the launcher would use for this shape with unlimited part_bytes
 size_t proj_gemm_part_bytes(int M, int Ntot, int K);
+// the same for `batch` GEMMs of this shape in one launch (tile kernel)
+size_t proj_gemm_part_bytes_batched(int batch, int M, int Ntot, int K);
 
 // Local sliding-window multi-query attention (head dim 256).
 struct AttnArgs {

@@ -144,10 +144,14 @@ __global__ void __launch_bounds__(kThreads, 1) proj_gemm_kernel(ProjGemmArgs g) 
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (the copies' LDS base)
     const int wm = wv >> 1, wn = wv & 1;
     int tm, tn;
-    // with K split, blocks tiles * ks .. tiles * (ks + 1) - 1 take split ks of every tile
+    // with K split, blocks tiles * ks .. tiles * (ks + 1) - 1 take split ks of every tile; with
+    // a batch, each item's blocks follow the previous item's
     const int tiles = g.ntm * g.ntn;
-    const int ks = kSplitK ? __builtin_amdgcn_readfirstlane((int)blockIdx.x / tiles) : 0;
-    tile_of((int)blockIdx.x - ks * tiles, g.ntm, g.ntn, tm, tn);
+    const int per_item = tiles * (kSplitK ? g.ksplit : 1);
+    const int bi = g.batch > 1 ? __builtin_amdgcn_readfirstlane((int)blockIdx.x / per_item) : 0;
+    const int bloc = (int)blockIdx.x - bi * per_item;
+    const int ks = kSplitK ? __builtin_amdgcn_readfirstlane(bloc / tiles) : 0;
+    tile_of(bloc - ks * tiles, g.ntm, g.ntn, tm, tn);
     // the divisions above run on the vector unit; the tile is uniform, and the buffer resources
     // built from it must sit in scalar registers
     const int m0 = __builtin_amdgcn_readfirstlane(tm) * kBM;
@@ -159,8 +163,8 @@ __global__ void __launch_bounds__(kThreads, 1) proj_gemm_kernel(ProjGemmArgs g) 
     const int Ks = kSplitK ? K / g.ksplit : K;   // this block's share of K
     const int k0 = ks * Ks;
     const int rows = min(g.M - m0, kBM);
-    const uint16_t* A = static_cast<const uint16_t*>(g.A) + (size_t)m0 * K + k0;
-    const uint16_t* W = static_cast<const uint16_t*>(g.W[seg]) + (size_t)nl0 * K + k0;
+    const uint16_t* A = static_cast<const uint16_t*>(g.A) + (size_t)bi * g.bsA + (size_t)m0 * K + k0;
+    const uint16_t* W = static_cast<const uint16_t*>(g.W[seg]) + (size_t)bi * g.bsW + (size_t)nl0 * K + k0;
     // (the ranges run k0 elements past the last row's share; no access reaches that far)
     const u32x4 ra = rsrc_words(A, (uint32_t)(rows * K * 2));
     const u32x4 rb = rsrc_words(W, (uint32_t)(kBN * K * 2));
@@ -250,7 +254,7 @@ __global__ void __launch_bounds__(kThreads, 1) proj_gemm_kernel(ProjGemmArgs g) 
     if constexpr (kSplitK) {
         // fp32 partial sums of this split, [ks][M][Ntot], four columns per 16-byte store
         const int ntot = g.ntn * kBN;
-        float* P = g.part + ((size_t)ks * g.M + m0) * ntot + n0;
+        float* P = g.part + (size_t)bi * g.ksplit * g.M * ntot + ((size_t)ks * g.M + m0) * ntot + n0;
         const __amdgpu_buffer_rsrc_t rp = make_rsrc_n(P, (uint32_t)(rows * ntot * 4));
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -267,9 +271,9 @@ __global__ void __launch_bounds__(kThreads, 1) proj_gemm_kernel(ProjGemmArgs g) 
         return;
     }
     // bias, round, store
-    const uint16_t* bias = static_cast<const uint16_t*>(g.b[seg]);
+    const uint16_t* bias = g.b[seg] ? static_cast<const uint16_t*>(g.b[seg]) + (size_t)bi * g.bsb : nullptr;
     const int ldc = g.Nw[seg];
-    uint16_t* C = static_cast<uint16_t*>(g.C[seg]) + (size_t)m0 * ldc + nl0;
+    uint16_t* C = static_cast<uint16_t*>(g.C[seg]) + (size_t)bi * g.bsC + (size_t)m0 * ldc + nl0;
     const __amdgpu_buffer_rsrc_t rc = make_rsrc_n(C, (uint32_t)(rows * ldc * 2));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -298,13 +302,16 @@ __global__ void __launch_bounds__(kThreads, 1) proj_gemm_kernel(ProjGemmArgs g) 
 // segment's columns are a multiple of the tile width, so eight never straddle two segments).
 __global__ void __launch_bounds__(256) proj_splitk_reduce_kernel(ProjGemmArgs g) {
     const int ntot = g.ntn * kBN, n8 = ntot / 8;
-    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= (size_t)g.M * n8) return;
+    const size_t i0 = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const int nb = g.batch > 1 ? g.batch : 1;
+    if (i0 >= (size_t)nb * g.M * n8) return;
+    const size_t bi = i0 / ((size_t)g.M * n8), i = i0 - bi * ((size_t)g.M * n8);
     const int m = (int)(i / n8), n = (int)(i % n8) * 8;
     const int seg = n < g.Nw[0] ? 0 : (n < g.Nw[0] + g.Nw[1] ? 1 : 2);
     const int nl = n - (seg > 0 ? g.Nw[0] : 0) - (seg > 1 ? g.Nw[1] : 0);
     float v[8];
-    const uint16_t* bias = static_cast<const uint16_t*>(g.b[seg]);
+    const uint16_t* bias = g.b[seg] ? static_cast<const uint16_t*>(g.b[seg]) + bi * g.bsb : nullptr;
+    const float* part = g.part + bi * g.ksplit * g.M * ntot;
     if (bias) {
         const uint4 b = *reinterpret_cast<const uint4*>(bias + nl);
         const uint32_t w[4] = {b.x, b.y, b.z, b.w};
@@ -320,18 +327,18 @@ __global__ void __launch_bounds__(256) proj_splitk_reduce_kernel(ProjGemmArgs g)
     // the partials are added in split order (as one GEMM adds its k-steps), then the bias
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int s = 0; s < g.ksplit; ++s) {
-        const float4* p = reinterpret_cast<const float4*>(g.part + ((size_t)s * g.M + m) * ntot + n);
+        const float4* p = reinterpret_cast<const float4*>(part + ((size_t)s * g.M + m) * ntot + n);
         const float4 x = p[0], y = p[1];
         acc[0] += x.x; acc[1] += x.y; acc[2] += x.z; acc[3] += x.w;
         acc[4] += y.x; acc[5] += y.y; acc[6] += y.z; acc[7] += y.w;
     }
     if (g.c_f32) {
-        float4* Cf = reinterpret_cast<float4*>(static_cast<float*>(g.C[seg]) + (size_t)m * g.Nw[seg] + nl);
+        float4* Cf = reinterpret_cast<float4*>(static_cast<float*>(g.C[seg]) + bi * g.bsC + (size_t)m * g.Nw[seg] + nl);
         Cf[0] = make_float4(acc[0] + v[0], acc[1] + v[1], acc[2] + v[2], acc[3] + v[3]);
         Cf[1] = make_float4(acc[4] + v[4], acc[5] + v[5], acc[6] + v[6], acc[7] + v[7]);
         return;
     }
-    uint16_t* C = static_cast<uint16_t*>(g.C[seg]) + (size_t)m * g.Nw[seg] + nl;
+    uint16_t* C = static_cast<uint16_t*>(g.C[seg]) + bi * g.bsC + (size_t)m * g.Nw[seg] + nl;
     *reinterpret_cast<uint4*>(C) = make_uint4(pack2bf(acc[0] + v[0], acc[1] + v[1]),
                                               pack2bf(acc[2] + v[2], acc[3] + v[3]),
                                               pack2bf(acc[4] + v[4], acc[5] + v[5]),
@@ -484,8 +491,8 @@ __global__ void __launch_bounds__(64 * kRowsWaves) gemv_rows_kernel(ProjGemmArgs
 
 // K splits for a shape: enough blocks to cover the chip (about 240) when the tiles alone do
 // not, each split a multiple of 128 of K.
-int choose_ksplit(int M, int Ntot, int K) {
-    const long long tiles = (long long)((M + kBM - 1) / kBM) * (Ntot / kBN);
+int choose_ksplit(int M, int Ntot, int K, int batch = 1) {
+    const long long tiles = (long long)((M + kBM - 1) / kBM) * (Ntot / kBN) * (batch > 1 ? batch : 1);
     if (tiles <= 0 || tiles >= 240) return 1;
     const int want = (int)((240 + tiles - 1) / tiles), units = K / 128;
     int best = 1;
@@ -505,6 +512,12 @@ size_t proj_gemm_part_bytes(int M, int Ntot, int K) {
     return s > 1 ? (size_t)s * M * Ntot * sizeof(float) : 0;
 }
 
+size_t proj_gemm_part_bytes_batched(int batch, int M, int Ntot, int K) {
+    if (batch <= 1) return proj_gemm_part_bytes(M, Ntot, K);
+    const int s = choose_ksplit(M, Ntot, K, batch);
+    return s > 1 ? (size_t)batch * s * M * Ntot * sizeof(float) : 0;
+}
+
 hipError_t launch_proj_gemm(const ProjGemmArgs& a_in, hipStream_t s) {
     ProjGemmArgs a = a_in;
     a.ntm = (a.M + kBM - 1) / kBM;
@@ -512,6 +525,27 @@ hipError_t launch_proj_gemm(const ProjGemmArgs& a_in, hipStream_t s) {
     const long long tiles = (long long)a.ntm * a.ntn;
     if (tiles <= 0) return hipSuccess;
     a.ksplit = 1;
+    const int nb = a.batch > 1 ? a.batch : 1;
+    if (nb > 1) {
+        // a batch runs on the tile kernel only
+        if (a.gated || a.R) return hipErrorInvalidValue;
+        if (a.part) {
+            const int ks = choose_ksplit(a.M, a.ntn * kBN, a.K, nb);
+            if (ks > 1 && (size_t)nb * ks * a.M * a.ntn * kBN * sizeof(float) <= a.part_bytes) a.ksplit = ks;
+        }
+        if (a.c_f32 && a.ksplit == 1) return hipErrorInvalidValue;
+        if (a.ksplit > 1)
+            hipLaunchKernelGGL(proj_gemm_kernel<true>, dim3((unsigned)(nb * tiles * a.ksplit)),
+                               dim3(kThreads), 0, s, a);
+        else
+            hipLaunchKernelGGL(proj_gemm_kernel<false>, dim3((unsigned)(nb * tiles)), dim3(kThreads), 0, s, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess || a.ksplit == 1) return e;
+        const size_t n = (size_t)nb * a.M * a.ntn * kBN / 8;
+        hipLaunchKernelGGL(proj_splitk_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                           s, a);
+        return hipGetLastError();
+    }
     const bool rows = !a.c_f32 && proj_gemm_rows(a.M, a.K);
     if (a.gated && !(rows && a.nseg == 2 && a.Nw[0] == a.Nw[1])) return hipErrorInvalidValue;
     if (a.R && !(rows && a.nseg == 1)) return hipErrorInvalidValue;
