@@ -31,10 +31,18 @@ constexpr int kChunk = 32;  // tokens per scan chunk (32: the gradient pass keep
 struct BwdBufs {
     uint16_t *U, *R, *I, *Wt, *dRI, *dRIt, *Ut, *dUg;
     float *aggA, *aggB, *carry, *bQ, *cin, *duv, *plam, *pba, *pbx, *pconv, *dW, *part;
+    float *sA, *sB, *sQ, *sh, *sc;   // chunk-group aggregates and carries (two-level carry scan)
+    float* red;                       // reduction parts [kRedParts][8][D]
     size_t part_bytes;
 };
 
 size_t r256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// the carry scan over a sequence's nch chunks runs in groups of kGroupChunks consecutive chunks
+constexpr int kGroupChunks = 16;
+__host__ __device__ inline int groups_of(int nch) { return (nch + kGroupChunks - 1) / kGroupChunks; }
+// the fixed-order sums of the per-chunk partials run in kRedParts consecutive ranges
+constexpr int kRedParts = 32;
 
 // Carve the workspace (the same order sizes it).
 BwdBufs carve(void* ws, int B, int T, int D, int H, size_t* total) {
@@ -64,7 +72,14 @@ BwdBufs carve(void* ws, int B, int T, int D, int H, size_t* total) {
     b.plam = reinterpret_cast<float*>(take(nc * 4));
     b.pba = reinterpret_cast<float*>(take(nc * 4));
     b.pbx = reinterpret_cast<float*>(take(nc * 4));
-    b.pconv = reinterpret_cast<float*>(take(nc * 5 * 4));
+    b.pconv = reinterpret_cast<float*>(take(nc * 5 * 4));   // [5][B * nch * D]
+    const size_t ng = (size_t)B * groups_of(T / kChunk) * D;
+    b.sA = reinterpret_cast<float*>(take(ng * 4));
+    b.sB = reinterpret_cast<float*>(take(ng * 4));
+    b.sQ = reinterpret_cast<float*>(take(ng * 4));
+    b.sh = reinterpret_cast<float*>(take(ng * 4));
+    b.sc = reinterpret_cast<float*>(take(ng * 4));
+    b.red = reinterpret_cast<float*>(take((size_t)kRedParts * 8 * D * 4));
     b.dW = reinterpret_cast<float*>(take((size_t)H * 2 * kBs * kBs * 4));
     b.part_bytes = proj_gemm_part_bytes_batched(H, 2 * kBs, kBs, (int)M);
     b.part = reinterpret_cast<float*>(take(b.part_bytes));
@@ -117,37 +132,49 @@ __device__ __forceinline__ void unpack8(uint4 v, float* f) {
     }
 }
 
+constexpr int kConvRun = 8;   // tokens per thread in the conv (T % 32 == 0, so runs stay in one sequence)
+
 __global__ void __launch_bounds__(256) bwd_conv_fwd_kernel(BwdArgs a, BwdBufs w) {
-    // grid: (B * T token rows, D / 2048 channel blocks); thread: channels d .. d + 7
+    // grid: (B * T / kConvRun token runs, D / 2048 channel blocks); thread: channels d .. d + 7 of
+    // kConvRun consecutive tokens, each x row loaded once
     const size_t M = (size_t)a.B * a.T;
     const int d = (blockIdx.y * 256 + threadIdx.x) * 8;
     if (d >= a.D) return;
-    const size_t m = blockIdx.x;
-    const int b = (int)(m / a.T), t = (int)(m % a.T);
+    const size_t m0 = (size_t)blockIdx.x * kConvRun;
+    const int b = (int)(m0 / a.T), t0 = (int)(m0 % a.T);
     const uint16_t* x = static_cast<const uint16_t*>(a.x);
     const uint16_t* c0 = static_cast<const uint16_t*>(a.conv0);
     const uint4* cw = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.conv_w) + (size_t)d * 4);
-    float u[8], wt[32];
-    if (a.conv_b) unpack8(*reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.conv_b) + d), u);
+    float bias[8], wt[32];
+    if (a.conv_b) unpack8(*reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.conv_b) + d), bias);
     else
 #pragma unroll
-        for (int q = 0; q < 8; ++q) u[q] = 0.0f;
+        for (int q = 0; q < 8; ++q) bias[q] = 0.0f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) unpack8(cw[q], wt + 8 * q);   // wt[4 c + j]: channel d + c, tap j
+    float xr[kConvRun + 3][8];   // x~ at t0 - 3 .. t0 + kConvRun - 1
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int p = t - 3 + j;
-        float xv[8];
-        if (p >= 0) unpack8(*reinterpret_cast<const uint4*>(x + ((size_t)b * a.T + p) * a.D + d), xv);
-        else if (c0) unpack8(*reinterpret_cast<const uint4*>(c0 + ((size_t)b * 3 + p + 3) * a.D + d), xv);
+    for (int r = 0; r < kConvRun + 3; ++r) {
+        const int p = t0 - 3 + r;
+        if (p >= 0) unpack8(*reinterpret_cast<const uint4*>(x + ((size_t)b * a.T + p) * a.D + d), xr[r]);
+        else if (c0) unpack8(*reinterpret_cast<const uint4*>(c0 + ((size_t)b * 3 + p + 3) * a.D + d), xr[r]);
         else
 #pragma unroll
-            for (int q = 0; q < 8; ++q) xv[q] = 0.0f;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) u[q] = __builtin_fmaf(wt[4 * q + j], xv[q], u[q]);
+            for (int q = 0; q < 8; ++q) xr[r][q] = 0.0f;
     }
-    *reinterpret_cast<uint4*>(w.U + hm(d / kBs, m, d % kBs, M)) =
-        make_uint4(pack2bf(u[0], u[1]), pack2bf(u[2], u[3]), pack2bf(u[4], u[5]), pack2bf(u[6], u[7]));
+#pragma unroll
+    for (int tt = 0; tt < kConvRun; ++tt) {
+        float u[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            float acc = bias[q];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc = __builtin_fmaf(wt[4 * q + j], xr[tt + j][q], acc);
+            u[q] = acc;
+        }
+        *reinterpret_cast<uint4*>(w.U + hm(d / kBs, m0 + tt, d % kBs, M)) =
+            make_uint4(pack2bf(u[0], u[1]), pack2bf(u[2], u[3]), pack2bf(u[4], u[5]), pack2bf(u[6], u[7]));
+    }
 }
 
 // ---- [W_a^T | W_x^T] per head: Wt[h][k][j'] ------------------------------------------------
@@ -202,26 +229,74 @@ __global__ void __launch_bounds__(256) bwd_chunk_agg_kernel(BwdArgs a, BwdBufs w
     w.bQ[idx] = Q;
 }
 
-// ---- sequential carries over the chunks: h entering each chunk (forward) and c entering it
-// from the right (reverse); the reverse carry past the first chunk is dh0 ----------------------
-__global__ void __launch_bounds__(256) bwd_carry_kernel(BwdArgs a, BwdBufs w) {
-    const int nch = a.T / kChunk;
-    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+// ---- carries over the chunks: h entering each chunk (forward) and c entering it from the
+// right (reverse); the reverse carry past the first chunk is dh0.  Two levels: each group of
+// kGroupChunks chunks is composed into one (A, B) and (A, Q) pair, the groups are walked in
+// sequence per (sequence, channel), then each group hands its entry carries to its chunks.
+// Every step is the same fma in the same order as a plain walk over the chunks would take
+// within a group, and composed pairs across groups. -----------------------------------------
+__global__ void __launch_bounds__(256) bwd_carry_group_kernel(BwdArgs a, BwdBufs w) {
+    const int nch = a.T / kChunk, ng = groups_of(nch);
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;   // (b, group, d)
+    if (idx >= (size_t)a.B * ng * a.D) return;
+    const int d = (int)(idx % a.D), gi = (int)((idx / a.D) % ng), b = (int)(idx / ((size_t)ng * a.D));
+    const int c0 = gi * kGroupChunks, c1 = min(nch, c0 + kGroupChunks);
+    // forward: h_out = A h_in + Bf; reverse: c_out (entering the group's first chunk from the
+    // right) = A c_in + Q, with A the product of the chunks' A
+    float A = 1.0f, Bf = 0.0f;
+    for (int c = c0; c < c1; ++c) {
+        const size_t e = ((size_t)b * nch + c) * a.D + d;
+        A *= w.aggA[e];
+        Bf = __builtin_fmaf(w.aggA[e], Bf, w.aggB[e]);
+    }
+    float Q = 0.0f;
+    for (int c = c1 - 1; c >= c0; --c) {
+        const size_t e = ((size_t)b * nch + c) * a.D + d;
+        Q = __builtin_fmaf(w.aggA[e], Q, w.bQ[e]);
+    }
+    w.sA[idx] = A;
+    w.sB[idx] = Bf;
+    w.sQ[idx] = Q;
+}
+
+__global__ void __launch_bounds__(256) bwd_carry_walk_kernel(BwdArgs a, BwdBufs w) {
+    const int nch = a.T / kChunk, ng = groups_of(nch);
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;   // (b, d)
     if (idx >= (size_t)a.B * a.D) return;
     const int d = (int)(idx % a.D), b = (int)(idx / a.D);
     float h = a.h0 ? a.h0[idx] : 0.0f;
-    for (int c = 0; c < nch; ++c) {
+    for (int gi = 0; gi < ng; ++gi) {
+        const size_t e = ((size_t)b * ng + gi) * a.D + d;
+        w.sh[e] = h;
+        h = __builtin_fmaf(w.sA[e], h, w.sB[e]);
+    }
+    float cc = a.dh_last ? a.dh_last[idx] : 0.0f;
+    for (int gi = ng - 1; gi >= 0; --gi) {
+        const size_t e = ((size_t)b * ng + gi) * a.D + d;
+        w.sc[e] = cc;
+        cc = __builtin_fmaf(w.sA[e], cc, w.sQ[e]);
+    }
+    a.dh0[idx] = cc;
+}
+
+__global__ void __launch_bounds__(256) bwd_carry_fill_kernel(BwdArgs a, BwdBufs w) {
+    const int nch = a.T / kChunk, ng = groups_of(nch);
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;   // (b, group, d)
+    if (idx >= (size_t)a.B * ng * a.D) return;
+    const int d = (int)(idx % a.D), gi = (int)((idx / a.D) % ng), b = (int)(idx / ((size_t)ng * a.D));
+    const int c0 = gi * kGroupChunks, c1 = min(nch, c0 + kGroupChunks);
+    float h = w.sh[idx];
+    for (int c = c0; c < c1; ++c) {
         const size_t e = ((size_t)b * nch + c) * a.D + d;
         w.carry[e] = h;
         h = __builtin_fmaf(w.aggA[e], h, w.aggB[e]);
     }
-    float cc = a.dh_last ? a.dh_last[idx] : 0.0f;
-    for (int c = nch - 1; c >= 0; --c) {
+    float cc = w.sc[idx];
+    for (int c = c1 - 1; c >= c0; --c) {
         const size_t e = ((size_t)b * nch + c) * a.D + d;
         w.cin[e] = cc;
         cc = __builtin_fmaf(w.aggA[e], cc, w.bQ[e]);
     }
-    a.dh0[idx] = cc;
 }
 
 // precise forms for the gradient pass: library tanh, expm1 and IEEE division (the derivative of
@@ -387,11 +462,15 @@ __global__ void __launch_bounds__(256) bwd_conv_kernel(BwdArgs a, BwdBufs w) {
         *reinterpret_cast<uint4*>(dx + ((size_t)b * a.T + t) * a.D + d) =
             make_uint4(pack2bf(o[0], o[1]), pack2bf(o[2], o[3]), pack2bf(o[4], o[5]), pack2bf(o[6], o[7]));
     }
-    const size_t pe = ((size_t)b * nch + c) * a.D + d;
+    const size_t pe = ((size_t)b * nch + c) * a.D + d, nc = (size_t)a.B * nch * a.D;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        float* pc = w.pconv + (pe + q) * 5;
-        pc[0] = sw[q][0]; pc[1] = sw[q][1]; pc[2] = sw[q][2]; pc[3] = sw[q][3]; pc[4] = sb[q];
+    for (int j = 0; j < 5; ++j) {   // [5][B * nch * D]: eight consecutive channels per store pair
+        float v8[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v8[q] = j < 4 ? sw[q][j] : sb[q];
+        float4* pc = reinterpret_cast<float4*>(w.pconv + j * nc + pe);
+        pc[0] = make_float4(v8[0], v8[1], v8[2], v8[3]);
+        pc[1] = make_float4(v8[4], v8[5], v8[6], v8[7]);
     }
     if (c == 0) {
         // window slot s (position s - 3) feeds u_t through tap j = s - t for t = 0 .. s
@@ -418,25 +497,35 @@ __global__ void __launch_bounds__(256) bwd_wcopy_kernel(BwdArgs a, BwdBufs w) {
     a.dwx[idx] = w.dW[h * 2 * kBs * kBs + (size_t)kBs * kBs + r];
 }
 
-// One wave per channel: lane l sums partials l, l + 64, ... in order, then a fixed butterfly.
-__global__ void __launch_bounds__(256) bwd_reduce_kernel(BwdArgs a, BwdBufs w) {
+// Fixed-order sums of the per-chunk partials, in two passes with consecutive lanes on
+// consecutive channels (whole-row loads): pass 1 sums each of kRedParts consecutive ranges of
+// the B * nch partials in order, pass 2 adds the ranges in order.
+__global__ void __launch_bounds__(256) bwd_reduce_part_kernel(BwdArgs a, BwdBufs w) {
     const int nch = a.T / kChunk, np = a.B * nch;
-    const int d = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int d = blockIdx.x * 256 + threadIdx.x, r = blockIdx.y;
     if (d >= a.D) return;
+    const int per = (np + kRedParts - 1) / kRedParts, q0 = r * per, q1 = min(np, q0 + per);
+    const size_t nc = (size_t)np * a.D;
     float v[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-    for (int q = lane; q < np; q += 64) {
+    for (int q = q0; q < q1; ++q) {
         const size_t e = (size_t)q * a.D + d;
         v[0] += w.plam[e];
         v[1] += w.pba[e];
         v[2] += w.pbx[e];
 #pragma unroll
-        for (int j = 0; j < 5; ++j) v[3 + j] += w.pconv[e * 5 + j];
+        for (int j = 0; j < 5; ++j) v[3 + j] += w.pconv[j * nc + e];
     }
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1)
+    for (int j = 0; j < 8; ++j) w.red[((size_t)r * 8 + j) * a.D + d] = v[j];
+}
+
+__global__ void __launch_bounds__(256) bwd_reduce_kernel(BwdArgs a, BwdBufs w) {
+    const int d = blockIdx.x * 256 + threadIdx.x;
+    if (d >= a.D) return;
+    float v[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    for (int r = 0; r < kRedParts; ++r)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] += __shfl_xor(v[j], o);
-    if (lane != 0) return;
+        for (int j = 0; j < 8; ++j) v[j] += w.red[((size_t)r * 8 + j) * a.D + d];
     a.dlambda[d] = v[0];
     a.dba[d] = v[1];
     a.dbx[d] = v[2];
@@ -464,7 +553,7 @@ hipError_t launch_prefill_backward(const BwdArgs& a, hipStream_t s) {
 #define RG_LAUNCH(kern, n)                                                              \
     hipLaunchKernelGGL(kern, dim3(blocks_for(n)), dim3(256), 0, s, a, w);               \
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_conv_fwd_kernel, dim3((unsigned)M, (unsigned)((a.D / 8 + 255) / 256)),
+    hipLaunchKernelGGL(bwd_conv_fwd_kernel, dim3((unsigned)(M / kConvRun), (unsigned)((a.D / 8 + 255) / 256)),
                        dim3(256), 0, s, a, w);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     RG_LAUNCH(bwd_wtrans_kernel, (size_t)a.H * kBs * 2 * kBs);
@@ -485,7 +574,12 @@ hipError_t launch_prefill_backward(const BwdArgs& a, hipStream_t s) {
         if ((e = launch_proj_gemm(g, s)) != hipSuccess) return e;
     }
     RG_LAUNCH(bwd_chunk_agg_kernel, nlane);
-    RG_LAUNCH(bwd_carry_kernel, (size_t)a.B * a.D);
+    {
+        const size_t ngl = (size_t)a.B * groups_of((int)nch) * a.D;
+        RG_LAUNCH(bwd_carry_group_kernel, ngl);
+        RG_LAUNCH(bwd_carry_walk_kernel, (size_t)a.B * a.D);
+        RG_LAUNCH(bwd_carry_fill_kernel, ngl);
+    }
     RG_LAUNCH(bwd_grad_kernel, nlane);
     {   // gradient of u through the gates, all heads in one launch
         ProjGemmArgs g;
@@ -512,7 +606,10 @@ hipError_t launch_prefill_backward(const BwdArgs& a, hipStream_t s) {
     }
     RG_LAUNCH(bwd_conv_kernel, nlane / 8);
     RG_LAUNCH(bwd_wcopy_kernel, (size_t)a.H * kBs * kBs);
-    hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((a.D + 3) / 4)), dim3(256), 0, s, a, w);
+    hipLaunchKernelGGL(bwd_reduce_part_kernel, dim3((unsigned)((a.D + 255) / 256), kRedParts),
+                       dim3(256), 0, s, a, w);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((a.D + 255) / 256)), dim3(256), 0, s, a, w);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 #undef RG_LAUNCH
     return hipSuccess;
