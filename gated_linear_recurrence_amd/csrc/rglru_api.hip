@@ -785,14 +785,14 @@ LayerBufs layer_bufs(void* workspace, size_t block_bytes, size_t M, int Dm) {
     char* base = static_cast<char*>(workspace) + round256(block_bytes);
     return {base, base + act, base + 2 * act, base + 3 * act, nullptr, 0};
 }
-// the largest split-K partial buffer of a decode layer's GEMMs (M rows; N and K per GEMM)
-// Split-K partial bytes of the decode-time projections, the largest over all row counts up to
-// M (a buffer sized for M then fits any smaller batch): the split count changes only when the
-// number of 256-row tiles does, and within one tile count the bytes grow with the rows, so
-// the largest value is at M or at a multiple of 256 below it.
+// Split-K partial bytes of the decode-time projections (M rows; N and K per GEMM), the
+// largest over all row counts up to M (a buffer sized for M then fits any smaller batch): the
+// split count changes only when the number of row tiles (128 or 256 rows) does, and within one
+// tile count the bytes grow with the rows, so the largest value is at M or at a multiple of 128
+// below it.
 size_t decode_part_bytes(int M, const int (*nk)[2], int n) {
     size_t b = 0;
-    for (int m = std::min(M, 256);; m = std::min(m + 256, M)) {
+    for (int m = std::min(M, 128);; m = std::min(m + 128, M)) {
         for (int i = 0; i < n; ++i) b = std::max(b, proj_gemm_part_bytes(m, nk[i][0], nk[i][1]));
         if (m >= M) break;
     }

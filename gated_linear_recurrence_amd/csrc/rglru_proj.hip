@@ -18,6 +18,7 @@
 // filled by buffer loads with the LDS bit (16 bytes per lane, straight into LDS), one k-step
 // ahead of the MFMAs.  A k-step reads whole 128-byte lines of its 512 tile rows; with 32-byte
 // k-steps each line was fetched twice (the L1 cannot keep 512 lines between the halves).
+#include <algorithm>
 #include <type_traits>
 
 #include "rglru_device.h"
@@ -345,6 +346,165 @@ __global__ void __launch_bounds__(256) proj_splitk_reduce_kernel(ProjGemmArgs g)
                                               pack2bf(acc[6] + v[6], acc[7] + v[7]));
 }
 
+// Mid-size row counts (decode of a few hundred sequences): 128 x 128 output tiles, four waves
+// of 64 x 64 (2 x 2 tiles of v_mfma_f32_32x32x16_bf16).  At such M the 256 x 256 tiles leave
+// 10..60 tiles per projection, and filling the chip then takes K splits whose fp32 partial sums
+// outweigh the weights several times over (M Ntot 4 bytes per split against N K 2 for the
+// weights); quarter-size tiles need a quarter of the splits or none.  K advances through a ring
+// of four LDS stages (64 k per stage, the swizzled 128-byte rows of the large kernel), three
+// k-steps of copies in flight ahead of the MFMAs: a split of K may be only a few k-steps long,
+// so the ring is filled once and streamed without a refill bubble per step.
+constexpr int kMidM = 128, kMidN = 128;
+constexpr int kMidStages = 4;
+constexpr int kMidMaxRows = 1024;   // 64 < M <= this, one GEMM (no batch), bf16 output
+
+// One operand's copies of k-step kt into an LDS stage of a 128-row tile: 16 copies of 1 KB,
+// four per wave (copy 4 w + j fills LDS chunks 64 (4 w + j) .. + 63).  Rows past `rows` repeat
+// the last row (results never stored).
+__device__ __forceinline__ void copy_mid(const u32x4& rs, uint16_t* lds, int wv, int lane, int K,
+                                         int rows, int kt) {
+    int off[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int p = (4 * wv + j) * 64 + lane;
+        const int r = p / kChunks;
+        const int c = chunk_pos(r, p % kChunks);
+        off[j] = min(r, rows - 1) * K * 2 + kt * kRowBytes + 16 * c;
+    }
+    copy4(rs, lds_address(lds + 4 * wv * 512), off);
+}
+
+// K splits of the mid kernel: enough workgroups to cover the chip once (one workgroup per CU:
+// the ring takes 128 KB of LDS), at least two k-steps per split.  Split s takes k-steps
+// [s KT / S, (s + 1) KT / S).
+int mid_ksplit(int M, int Ntot, int K) {
+    const long long tiles = (long long)((M + kMidM - 1) / kMidM) * (Ntot / kMidN);
+    if (tiles <= 0) return 1;
+    long long s = 256 / tiles;
+    s = std::min<long long>(s, K / kBK / 2);
+    return (int)std::max<long long>(s, 1);
+}
+
+template <bool kSplitK>
+__global__ void __launch_bounds__(kThreads, 1) proj_gemm_mid_kernel(ProjGemmArgs g) {
+    __shared__ __attribute__((aligned(16))) uint16_t sa[kMidStages][kMidM * kBK];
+    __shared__ __attribute__((aligned(16))) uint16_t sb[kMidStages][kMidN * kBK];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wv >> 1, wn = wv & 1;
+    const int ntot = g.Nw[0] + g.Nw[1] + g.Nw[2];
+    const int ntm = (g.M + kMidM - 1) / kMidM, ntn = ntot / kMidN;
+    const int S = kSplitK ? g.ksplit : 1;
+    // workgroups go to the 8 XCDs round-robin: each XCD gets a contiguous range of the order
+    // (M tiles fastest, then N tiles, then splits), so the tiles of one weight block share an L2
+    const int total = ntm * ntn * S, bid = (int)blockIdx.x;
+    const int L = (total & 7) == 0 ? (bid & 7) * (total >> 3) + (bid >> 3) : bid;
+    const int m0 = __builtin_amdgcn_readfirstlane(L % ntm) * kMidM;
+    const int n0 = __builtin_amdgcn_readfirstlane((L / ntm) % ntn) * kMidN;
+    const int ks = kSplitK ? __builtin_amdgcn_readfirstlane(L / (ntm * ntn)) : 0;
+    const int seg = n0 < g.Nw[0] ? 0 : (n0 < g.Nw[0] + g.Nw[1] ? 1 : 2);
+    const int nl0 = n0 - (seg > 0 ? g.Nw[0] : 0) - (seg > 1 ? g.Nw[1] : 0);
+    const int K = g.K, KT = K / kBK;
+    const int kt0 = ks * KT / S, nk = (ks + 1) * KT / S - kt0;
+    const int rows = min(g.M - m0, kMidM);
+    const uint16_t* A = static_cast<const uint16_t*>(g.A) + (size_t)m0 * K + (size_t)kt0 * kBK;
+    const uint16_t* W = static_cast<const uint16_t*>(g.W[seg]) + (size_t)nl0 * K + (size_t)kt0 * kBK;
+    // (the ranges run kt0 k-steps past the last row's share; no access reaches that far)
+    const u32x4 ra = rsrc_words(A, (uint32_t)(rows * K * 2));
+    const u32x4 rb = rsrc_words(W, (uint32_t)(kMidN * K * 2));
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    guard_vmem_sgprs(ra, rb);
+#pragma unroll
+    for (int q = 0; q < kMidStages - 1; ++q)
+        if (q < nk) {
+            copy_mid(ra, sa[q], wv, lane, K, rows, q);
+            copy_mid(rb, sb[q], wv, lane, K, kMidN, q);
+        }
+    for (int kt = 0; kt < nk; ++kt) {
+        // this wave's copies of k-step kt have landed once at most those of the later k-steps
+        // already issued (eight loads each) are outstanding; the barrier then publishes the
+        // stage, and every wave is past its reads of the stage refilled next (k-step kt - 1)
+        const int ahead = min(kMidStages - 2, nk - 1 - kt);
+        static_assert(kMidStages == 4, "the waits below cover two later k-steps");
+        if (ahead >= 2) wait_vmcnt<16>();
+        else if (ahead == 1) wait_vmcnt<8>();
+        else wait_vmcnt<0>();
+        lds_sync();
+        if (kt + kMidStages - 1 < nk) {
+            const int st = (kt + kMidStages - 1) % kMidStages;
+            copy_mid(ra, sa[st], wv, lane, K, rows, kt + kMidStages - 1);
+            copy_mid(rb, sb[st], wv, lane, K, kMidN, kt + kMidStages - 1);
+        }
+        const uint16_t* ca = sa[kt % kMidStages];
+        const uint16_t* cb = sb[kt % kMidStages];
+#pragma unroll
+        for (int s = 0; s < kBK / 16; ++s) {
+            bf16x8 fa[2], fb[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) fa[i] = frag(ca, 64 * wm + 32 * i, lane, s);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) fb[j] = frag(cb, 64 * wn + 32 * j, lane, s);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+        }
+    }
+
+    // acc[i][j] is the transposed 32 x 32 tile: lane l holds output row 32 i + l % 32 and, in
+    // registers 4 q .. 4 q + 3, output columns 32 j + 8 q + 4 (l / 32) + 0..3 (wave offsets added)
+    const int ncol = 64 * wn + 4 * (lane >> 5);
+    const int mrow = 64 * wm + (lane & 31);
+    if constexpr (kSplitK) {
+        float* P = g.part + ((size_t)ks * g.M + m0) * ntot + n0;
+        const __amdgpu_buffer_rsrc_t rp = make_rsrc_n(P, (uint32_t)(rows * ntot * 4));
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const f32x16& t = acc[i][j];
+                    const f32x4 v = {t[4 * q], t[4 * q + 1], t[4 * q + 2], t[4 * q + 3]};
+                    const int off = ((mrow + 32 * i) * ntot + ncol + 32 * j + 8 * q) * 4;
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rp, off,
+                                                           0, 0);
+                }
+        return;
+    }
+    const uint16_t* bias = static_cast<const uint16_t*>(g.b[seg]);
+    const int ldc = g.Nw[seg];
+    uint16_t* C = static_cast<uint16_t*>(g.C[seg]) + (size_t)m0 * ldc + nl0;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc_n(C, (uint32_t)(rows * ldc * 2));
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int n = ncol + 32 * j + 8 * q;
+            const uint2 bw = bias ? *reinterpret_cast<const uint2*>(bias + nl0 + n) : make_uint2(0u, 0u);
+            const float bv[4] = {bf_lo(bw.x), bf_hi(bw.x), bf_lo(bw.y), bf_hi(bw.y)};
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const f32x16& t = acc[i][j];
+                const u32x2 v = {pack2bf(t[4 * q] + bv[0], t[4 * q + 1] + bv[1]),
+                                 pack2bf(t[4 * q + 2] + bv[2], t[4 * q + 3] + bv[3])};
+                const int off = ((mrow + 32 * i) * ldc + n) * 2;
+                __builtin_amdgcn_raw_buffer_store_b64(v, rc, off, 0, 0);
+            }
+        }
+    }
+}
+
 // Few rows (decode: one row per sequence), up to 64, where the row kernel below does not
 // apply.  One workgroup per 16 output features: the weight rows are the A operand of
 // v_mfma_f32_16x16x32_bf16 (16 features x 32 k, each lane 16 bytes of one row) and up to 64
@@ -508,7 +668,7 @@ bool proj_gemm_rows(int M, int K) { return M >= 1 && M <= kRowsMax && K % 512 ==
 size_t proj_gemm_part_bytes(int M, int Ntot, int K) {
     if (proj_gemm_rows(M, K)) return 0;
     if (M <= kSkinnyRows && K % (32 * kSkinnyWaves) == 0) return 0;
-    const int s = choose_ksplit(M, Ntot, K);
+    const int s = M <= kMidMaxRows ? mid_ksplit(M, Ntot, K) : choose_ksplit(M, Ntot, K);
     return s > 1 ? (size_t)s * M * Ntot * sizeof(float) : 0;
 }
 
@@ -576,6 +736,24 @@ hipError_t launch_proj_gemm(const ProjGemmArgs& a_in, hipStream_t s) {
             case 3: hipLaunchKernelGGL(skinny_gemm_kernel<3>, dim3(blocks), dim3(512), 0, s, a); break;
             default: hipLaunchKernelGGL(skinny_gemm_kernel<4>, dim3(blocks), dim3(512), 0, s, a);
         }
+        return hipGetLastError();
+    }
+    if (!a.c_f32 && a.M <= kMidMaxRows) {
+        const int ntot = a.ntn * kBN;
+        if (a.part) {
+            const int ks = mid_ksplit(a.M, ntot, a.K);
+            if (ks > 1 && (size_t)ks * a.M * ntot * sizeof(float) <= a.part_bytes) a.ksplit = ks;
+        }
+        const unsigned blocks = (unsigned)(((a.M + kMidM - 1) / kMidM) * (ntot / kMidN) * a.ksplit);
+        if (a.ksplit > 1)
+            hipLaunchKernelGGL(proj_gemm_mid_kernel<true>, dim3(blocks), dim3(kThreads), 0, s, a);
+        else
+            hipLaunchKernelGGL(proj_gemm_mid_kernel<false>, dim3(blocks), dim3(kThreads), 0, s, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess || a.ksplit == 1) return e;
+        const size_t n = (size_t)a.M * ntot / 8;
+        hipLaunchKernelGGL(proj_splitk_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256),
+                           0, s, a);
         return hipGetLastError();
     }
     if (a.part) {

@@ -245,6 +245,7 @@ def test_layers_2b_batched_full_size_sampled():
     (2560, 10, 2560, 7680, 2, 20, 3),     # the 2B widths
     (2560, 10, 2560, 7680, 1, 20, 3),     # one row: the row GEMV with the residual epilogue
     (2560, 10, 2560, 7680, 4, 20, 3),     # four rows: the row GEMV's widest case
+    (512, 2, 768, 1536, 130, 6, 2),       # 128-row tiles with split K (gate|up: 12 k-steps in 5)
 ])
 def test_recurrent_layer_decode_continues_prefill(D, nh, Dm, F, N, T0, steps):
     from gated_linear_recurrence_amd import binding
@@ -276,6 +277,7 @@ def test_recurrent_layer_decode_continues_prefill(D, nh, Dm, F, N, T0, steps):
     (2560, 10, 7680, 2, 2048, 20, 3),     # the 2B widths and window
     (2560, 10, 7680, 1, 2048, 20, 3),     # one row
     (2560, 10, 7680, 4, 2048, 20, 3),     # four rows
+    (512, 2, 768, 130, 32, 40, 2),        # 128-row tiles with split K
 ])
 def test_attention_layer_decode_continues_prefill(Dm, Hq, F, N, W, T0, steps):
     from gated_linear_recurrence_amd import binding

@@ -51,9 +51,12 @@ def _check_linear(got_bits, ref, x_bits, w_bits, label):
 
 @pytest.mark.parametrize("M,K,N,bias", [
     (1, 128, 256, True),          # one row
-    (300, 256, 512, True),        # ragged M: a full tile and a partial one
-    (257, 2560, 2560, False),     # the 2B widths, one row past a tile
-    (513, 384, 768, True),        # K = 384: a loop trip and a half over the stage ring
+    (300, 256, 512, True),        # ragged M on the 128-row tiles: two full tiles and a partial one
+    (257, 2560, 2560, False),     # the 2B widths, one row past a 128-row tile pair
+    (256, 2560, 5120, True),      # decode of 256 sequences, the branch projections' shape
+    (65, 7680, 256, False),       # the fewest rows of the 128-row tiles, a long K
+    (513, 384, 768, True),        # K = 384: six k-steps through the four-stage ring
+    (1025, 384, 768, True),       # past 1024 rows: the 256 x 256 tiles, a ragged last row tile
     (1, 2560, 2560, True),        # decode of one sequence: the row kernel (M <= 4, K % 512 == 0)
     (2, 7680, 512, False),        # row kernel, two rows, the MLP down projection's K
     (3, 1024, 768, True),         # row kernel, a ragged row count (held as four)
