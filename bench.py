@@ -719,6 +719,63 @@ def counter_summary(args):
     print(json.dumps(out))
 
 
+BACKWARD_TXT = os.path.join(ROOT, "profiles", "prefill_backward-2b-batched-kernel-trace.txt")
+
+
+def backward_summary(args):
+    """Per-kernel time and HBM traffic of the path's backward (rglru_prefill_backward) from
+    rocprofv3 CSVs of the `--legs backward` run: a kernel trace and one FETCH_SIZE and one
+    WRITE_SIZE pass, scaled by the copy-probe calibration; written to profiles/."""
+    stats = _rows(args.kernel_stats)
+    cf_kib, _ = _mean_counter(args.copy_fetch, "copyBuffer", "FETCH_SIZE", 1e5)
+    cw_kib, _ = _mean_counter(args.copy_write, "copyBuffer", "WRITE_SIZE", 1e5)
+    fs, ws = float(1 << 20) / cf_kib, float(1 << 20) / cw_kib
+    per = {}
+    for path, ctr in ((args.fetch, "FETCH_SIZE"), (args.write, "WRITE_SIZE")):
+        acc = {}
+        for r in _rows(path):
+            if r["Counter_Name"] == ctr:
+                acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        for name, v in acc.items():
+            per.setdefault(name, {})[ctr] = sum(v) / len(v)
+    w = synth.WORKLOADS[synth.BATCHED_2B]
+    alg = 10 * w.B * w.T * w.D
+    # kernels of the backward: everything but the forward prefill and torch's own set-up kernels
+    keep = lambda n: ("bwd_" in n or "proj_" in n) and "prefill_bf16" not in n
+    rows, tot_ns, tot_b = [], 0.0, 0.0
+    for r in stats:
+        n = r["Name"]
+        if not keep(n):
+            continue
+        c = per.get(n, {})
+        b = (c.get("FETCH_SIZE", 0.0) * fs + c.get("WRITE_SIZE", 0.0) * ws) * 1024.0
+        calls = int(r["Calls"])
+        short = n.replace("(anonymous namespace)", "").split("(")[0].split("::")[-1]
+        rows.append((short, calls, float(r["AverageNs"]), b))
+    # calls per backward: the bwd_ kernels run once per call
+    n_bwd = max(c for name, c, _, _ in rows if name == "bwd_grad_kernel")
+    with open(BACKWARD_TXT, "w") as f:
+        f.write("rocprofv3 kernel trace and HBM traffic, the path's backward pass "
+                "(rglru_prefill_backward) on\n%s (bf16, 10 heads of 256)\n\n" % w.name)
+        f.write("commands (from the repository root):\n")
+        for c in args.commands:
+            f.write("  %s\n" % c)
+        f.write("\n%-28s %6s %12s %14s %10s\n" % ("kernel", "calls", "avg us", "MB per call",
+                                                  "GB/s"))
+        for short, calls, ns, b in sorted(rows, key=lambda t: -t[1] * t[2]):
+            k = calls / n_bwd   # launches per backward
+            tot_ns += ns * k
+            tot_b += b * k
+            f.write("%-28s %6d %12.1f %14.1f %10.0f\n" % (short, calls, ns / 1e3, b / 1e6,
+                                                          b / ns if ns else 0.0))
+        f.write("\nper backward (launches per call weighted): %.0f us of kernels, %.2f GB of HBM "
+                "traffic = %.2f x the algorithmic %.2f GB (x, y, dout read; dx, dy written)\n"
+                % (tot_ns / 1e3, tot_b / 1e9, tot_b / alg, alg / 1e9))
+        f.write("traffic = FETCH_SIZE x %.3f + WRITE_SIZE x %.3f (KiB per dispatch, scaled by a "
+                "plain 1 GiB copy)\n" % (fs, ws))
+    print(open(BACKWARD_TXT).read())
+
+
 CENSUS_JSON = os.path.join(ROOT, "profiles", "prefill_bf16_kernel-2b-batched-census.json")
 CENSUS_PASSES = [
     # (derived or base counters of one rocprofv3 --pmc pass; each fits the SQ/GRBM limits)
@@ -830,7 +887,14 @@ def main():
     ap.add_argument("--census-summary", action="store_true",
                     help="write the SQ counter census under profiles/ from rocprofv3 CSVs (no GPU)")
     ap.add_argument("--census", nargs="*", default=[])
+    ap.add_argument("--backward-summary", action="store_true",
+                    help="write the backward's kernel-trace and traffic summary under profiles/ "
+                         "from rocprofv3 CSVs (no GPU; --kernel-stats, --fetch, --write, "
+                         "--copy-fetch, --copy-write)")
     args = ap.parse_args()
+    if args.backward_summary:
+        backward_summary(args)
+        return
     if args.counter_summary:
         counter_summary(args)
         return

@@ -296,6 +296,41 @@ def test_decode_split_matches_fused(D, nh, N):
     assert float((a != b).float().mean()) < 0.01
 
 
+def test_decode_workspace_reused_across_batch_sizes():
+    """One workspace, never initialised (random bytes), serves split steps of several batch
+    sizes in turn (the gate pass's waves per workgroup, and so its blocks of u, change with
+    the batch).  Every step must match the fused kernel (no workspace) on the same state:
+    windows bit-identical, h to fp32 rounding, outputs within one bf16 step."""
+    from gated_linear_recurrence_amd import binding
+    D, nh, Nmax = 2560, 10, 300
+    w = synth.Workload("dec-reuse", Nmax, 4, D, nh, synth.BF16, 0.9, 0.999, 0.0, 31)
+    p = synth.make_params(w, biases=True)
+    x, y = synth.make_act(w, "x"), synth.make_act(w, "y")
+    P = H.dev_params(p, w.H)
+    xd, yd = H.to_dev(x), H.to_dev(y)
+    need = binding.rglru_decode_workspace_bytes(Nmax, D, torch.bfloat16)
+    g = torch.Generator(device="cuda").manual_seed(5)
+    ws = torch.randint(0, 256, (need,), generator=g, dtype=torch.uint8, device="cuda")
+    h0 = H.to_dev(np.random.default_rng(8).normal(0, 0.5, (Nmax, D)).astype(np.float32))
+    c0 = H.to_dev(synth.make_conv0(w, Nmax))
+    state = {k: (h0.clone(), c0.clone()) for k in ("fused", "ws")}
+    for t, N in enumerate((300, 40, 300, 1, 129)):
+        outs = {}
+        for k, workspace in (("fused", None), ("ws", ws)):
+            h, cs = state[k]
+            o = torch.empty((N, D), dtype=torch.bfloat16, device="cuda")
+            binding.rglru_decode_step(P, xd[:N, t % 4], yd[:N, t % 4], h[:N], cs[:N], out_t=o,
+                                      workspace=workspace)
+            outs[k] = o
+        torch.cuda.synchronize()
+        assert torch.equal(state["fused"][1], state["ws"][1]), "window, step %d N=%d" % (t, N)
+        torch.testing.assert_close(state["ws"][0], state["fused"][0], rtol=1e-5, atol=1e-5)
+        a, b = outs["fused"].float(), outs["ws"].float()
+        assert bool(((a - b).abs() <= a.abs() * 2.0 ** -7 + 1e-6).all()), "out, step %d N=%d" % (t, N)
+        # keep both paths on the same state (their h differ by fp32 rounding)
+        state["ws"] = (state["fused"][0].clone(), state["fused"][1].clone())
+
+
 # ------------------------------------------------------------------------------------------
 # conv-state update
 # ------------------------------------------------------------------------------------------
