@@ -750,7 +750,8 @@ int check_norms(const rglru_norm_params* n, int Dm) {
 // (*res_added tells the caller which happened).
 hipError_t run_mlp(const rglru_mlp_params* m, int M, const void* x, void* out, void* ws,
                    float* part, size_t part_bytes, hipStream_t s,
-                   const void* residual = nullptr, bool* res_added = nullptr) {
+                   const void* residual = nullptr, bool* res_added = nullptr,
+                   bool rows_epilogue = false) {
     const size_t nf = (size_t)M * m->F;
     void* G = ws;
     void* U = static_cast<char*>(ws) + round256(nf * 2);
@@ -763,12 +764,16 @@ hipError_t run_mlp(const rglru_mlp_params* m, int M, const void* x, void* out, v
     hipError_t e = launch_proj_gemm(g, s);
     if (e == hipSuccess && !gated) e = launch_geglu(G, U, nf, s);
     if (e != hipSuccess) return e;
-    const bool add = residual && proj_gemm_rows(M, m->F);
+    // the final residual addition rides on the down projection: in the row kernel's epilogue,
+    // or in the row-wise sum of its partials
+    const bool fuse = residual && rows_epilogue && part;
+    const bool add = residual && (proj_gemm_rows(M, m->F) || fuse);
     if (res_added) *res_added = add;
     memset(&g, 0, sizeof g);
     g.A = G; g.W[0] = m->down_w; g.b[0] = m->down_b; g.C[0] = out;
     g.M = M; g.K = m->F; g.Nw[0] = m->D_model; g.nseg = 1;
     g.part = part; g.part_bytes = part_bytes; g.R = add ? residual : nullptr;
+    g.rows_epilogue = fuse;
     return launch_proj_gemm(g, s);
 }
 
@@ -790,10 +795,14 @@ LayerBufs layer_bufs(void* workspace, size_t block_bytes, size_t M, int Dm) {
 // split count changes only when the number of row tiles (128 or 256 rows) does, and within one
 // tile count the bytes grow with the rows, so the largest value is at M or at a multiple of 128
 // below it.
-size_t decode_part_bytes(int M, const int (*nk)[2], int n) {
+size_t decode_part_bytes(int M, const int (*nk)[2], int n, const int (*nk_rows)[2] = nullptr,
+                         int n_rows = 0) {
     size_t b = 0;
     for (int m = std::min(M, 128);; m = std::min(m + 128, M)) {
         for (int i = 0; i < n; ++i) b = std::max(b, proj_gemm_part_bytes(m, nk[i][0], nk[i][1]));
+        // the GEMMs whose sums carry the layer's add-and-norm (partials even without a split)
+        for (int i = 0; i < n_rows; ++i)
+            b = std::max(b, proj_gemm_part_bytes_rows_epilogue(m, nk_rows[i][0], nk_rows[i][1]));
         if (m >= M) break;
     }
     return round256(b);
@@ -805,9 +814,14 @@ size_t layer_tail_bytes(size_t M, int Dm, int F) {
 // Launches of the layer after validation: norm 1, the block (through `block`), h and norm 2,
 // the MLP into out, the final residual addition in place (done by the MLP's last launch when
 // that takes the row kernel).
+// With fuse (decode layers of more than 64 rows, which have partial-sum space), the block's
+// output projection is expected to write h = x_in + its output and the second norm itself
+// (rows_epilogue; see fuse_out_proj), and the final residual addition rides on the down
+// projection's sum.
 template <class Block>
 int run_layer(const rglru_norm_params* nrm, const rglru_mlp_params* m, size_t M, int Dm,
-              const void* x_in, void* out, const LayerBufs& L, hipStream_t s, Block block) {
+              const void* x_in, void* out, const LayerBufs& L, hipStream_t s, Block block,
+              bool fuse = false) {
     NormArgs na;
     na.x = x_in; na.y = nullptr; na.g = nrm->temporal_scale; na.h = nullptr; na.n = L.a;
     na.M = (int)M; na.D = Dm; na.eps = nrm->eps;
@@ -815,16 +829,30 @@ int run_layer(const rglru_norm_params* nrm, const rglru_mlp_params* m, size_t M,
     if (e != hipSuccess) return hip_fail(e);
     int st = block();
     if (st != RGLRU_OK) return st;
-    na.x = x_in; na.y = L.b; na.g = nrm->channel_scale; na.h = L.h; na.n = L.a;
-    e = launch_add_rmsnorm(na, s);
+    if (!fuse) {
+        na.x = x_in; na.y = L.b; na.g = nrm->channel_scale; na.h = L.h; na.n = L.a;
+        e = launch_add_rmsnorm(na, s);
+    }
     bool added = false;
     if (e == hipSuccess)
-        e = run_mlp(m, (int)M, L.a, out, L.mlp, L.part, L.part_bytes, s, L.h, &added);
+        e = run_mlp(m, (int)M, L.a, out, L.mlp, L.part, L.part_bytes, s, L.h, &added, fuse);
     if (e != hipSuccess) return hip_fail(e);
     if (added) return RGLRU_OK;
     na.x = L.h; na.y = out; na.g = nullptr; na.h = out; na.n = nullptr;
     e = launch_add_rmsnorm(na, s);
     return e == hipSuccess ? RGLRU_OK : hip_fail(e);
+}
+
+// The block's output projection in a fused decode layer: C = h = x_in + the projection, and
+// the second norm of h into L.a, from the row-wise sum of its partials.
+void fuse_out_proj(ProjGemmArgs& g, const rglru_norm_params* nrm, const void* x_in,
+                   const LayerBufs& L) {
+    g.rows_epilogue = 1;
+    g.R = x_in;
+    g.C[0] = L.h;
+    g.norm_g = nrm->channel_scale;
+    g.norm_out = L.a;
+    g.norm_eps = nrm->eps;
 }
 
 // out and the workspace against everything else the layer reads or writes
@@ -980,7 +1008,8 @@ static size_t rec_dec_block_bytes(size_t N, int D) {
 
 static size_t rec_dec_part_bytes(int N, int D, int Dm, int F) {
     const int nk[4][2] = {{2 * D, Dm}, {Dm, D}, {2 * F, Dm}, {Dm, F}};
-    return decode_part_bytes(N, nk, 4);
+    const int nk_rows[2][2] = {{Dm, D}, {Dm, F}};   // output and down projections
+    return decode_part_bytes(N, nk, 4, nk_rows, 2);
 }
 
 size_t rglru_recurrent_layer_decode_workspace_bytes(int32_t N, int32_t D, int32_t D_model,
@@ -1030,6 +1059,7 @@ int rglru_recurrent_layer_decode(const rglru_params* p, const rglru_proj_params*
     L.part_bytes = rec_dec_part_bytes(N, D, Dm, m->F);
     L.part = L.part_bytes ? reinterpret_cast<float*>(ws + need - L.part_bytes) : nullptr;
     const hipStream_t s = (hipStream_t)stream;
+    const bool fuse = L.part && proj_gemm_rows_epilogue_ok(N);
     return run_layer(nrm, m, N, Dm, x_t, out_t, L, s, [&]() {
         ProjGemmArgs g;
         memset(&g, 0, sizeof g);
@@ -1044,9 +1074,10 @@ int rglru_recurrent_layer_decode(const rglru_params* p, const rglru_proj_params*
         memset(&g, 0, sizeof g);
         g.A = mg; g.W[0] = q->lin_out_w; g.b[0] = q->lin_out_b; g.C[0] = L.b;
         g.M = N; g.K = D; g.Nw[0] = Dm; g.nseg = 1; g.part = L.part; g.part_bytes = L.part_bytes;
+        if (fuse) fuse_out_proj(g, nrm, x_t, L);
         e = launch_proj_gemm(g, s);
         return e == hipSuccess ? RGLRU_OK : hip_fail(e);
-    });
+    }, fuse);
 }
 
 // block part of the attention decode workspace: q, k, v, the attention output, the attention
@@ -1059,7 +1090,8 @@ static size_t attn_dec_block_bytes(size_t N, int Hq, int W) {
 static size_t attn_dec_part_bytes(int N, int Hq, int Dm, int F) {
     const int HD = Hq * kAttnDh;
     const int nk[4][2] = {{HD + 2 * kAttnDh, Dm}, {Dm, HD}, {2 * F, Dm}, {Dm, F}};
-    return decode_part_bytes(N, nk, 4);
+    const int nk_rows[2][2] = {{Dm, HD}, {Dm, F}};  // output and down projections
+    return decode_part_bytes(N, nk, 4, nk_rows, 2);
 }
 
 size_t rglru_attention_layer_decode_workspace_bytes(const rglru_attn_params* a, int32_t N,
@@ -1112,6 +1144,7 @@ int rglru_attention_layer_decode(const rglru_attn_params* a, const rglru_norm_pa
     L.part_bytes = attn_dec_part_bytes(N, Hq, Dm, m->F);
     L.part = L.part_bytes ? reinterpret_cast<float*>(ws + need - L.part_bytes) : nullptr;
     const hipStream_t s = (hipStream_t)stream;
+    const bool fuse = L.part && proj_gemm_rows_epilogue_ok(N);
     return run_layer(nrm, m, N, Dm, x_t, out_t, L, s, [&]() {
         ProjGemmArgs g;
         memset(&g, 0, sizeof g);
@@ -1128,9 +1161,10 @@ int rglru_attention_layer_decode(const rglru_attn_params* a, const rglru_norm_pa
         g.A = ob; g.W[0] = a->o_w; g.b[0] = a->o_b; g.C[0] = L.b;
         g.M = N; g.K = (int)HD; g.Nw[0] = Dm; g.nseg = 1;
         g.part = L.part; g.part_bytes = L.part_bytes;
+        if (fuse) fuse_out_proj(g, nrm, x_t, L);
         e = launch_proj_gemm(g, s);
         return e == hipSuccess ? RGLRU_OK : hip_fail(e);
-    });
+    }, fuse);
 }
 
 // ------------------------------------------------------------------------------------------

@@ -84,10 +84,19 @@ struct ProjGemmArgs {
     int ksplit;                  // set by the launcher
     int c_f32;                   // split-K only: C[0] is fp32 (no rounding); the call fails
                                  // unless the launcher splits K
-    // Row kernel only (proj_gemm_rows(M, K)); the call fails otherwise.
+    // Row kernel (proj_gemm_rows(M, K)), or any shape with rows_epilogue; the call fails
+    // otherwise.
     int gated;                   // two segments of equal width: C[0] = gelu_tanh(gate) * up,
                                  // from the bf16-rounded segment outputs (C[1] unused)
     const void* R;               // one segment: C = R + the rounded output, rounded again
+    // rows_epilogue (one segment of at most 8192 columns, M > 64, part given): the tile
+    // kernels write fp32 partials even without a K split, and one workgroup per row adds them
+    // with the bias and R, and, with norm_out, also writes RMSNorm(C) * norm_g (the
+    // add-and-norm step of the residual layer)
+    int rows_epilogue;
+    const void* norm_g;
+    void* norm_out;
+    float norm_eps;
     // Tile kernel only: `batch` (>= 1; 0 means 1) independent GEMMs of this shape in one launch,
     // item i at A + i bsA, W[o] + i bsW, C[o] + i bsC, b[o] + i bsb (elements), with its own
     // split-K partials [ksplit][M][sum Nw] at part + i ksplit M sum Nw.
@@ -98,6 +107,10 @@ struct ProjGemmArgs {
 bool proj_gemm_rows(int M, int K);
 // fp32 partial-sum bytes the launcher would use for this shape with unlimited part_bytes
 size_t proj_gemm_part_bytes(int M, int Ntot, int K);
+// true when a GEMM of M rows can take rows_epilogue (the tile kernels: M > 64)
+bool proj_gemm_rows_epilogue_ok(int M);
+// the partial-sum bytes of that form (at least one split's worth)
+size_t proj_gemm_part_bytes_rows_epilogue(int M, int Ntot, int K);
 // the same for `batch` GEMMs of this shape in one launch (tile kernel)
 size_t proj_gemm_part_bytes_batched(int batch, int M, int Ntot, int K);
 

@@ -346,6 +346,89 @@ __global__ void __launch_bounds__(256) proj_splitk_reduce_kernel(ProjGemmArgs g)
                                               pack2bf(acc[6] + v[6], acc[7] + v[7]));
 }
 
+// The residual layer's add-and-norm fused into the split-K sum (rows_epilogue): one workgroup
+// of 256 threads per row of at most 8192 columns, eight columns per thread and step.
+// C = R + (bias + the split partials in split order), each rounding as the separate GEMM, sum
+// and add_rmsnorm steps make it; with norm_out also the row's RMSNorm(C) * norm_g from the
+// rounded C in fp32 (sum of squares per thread, then per wave, then the four waves in order).
+constexpr int kRowsMaxChunks = 4;    // 8-column chunks per thread
+__device__ __forceinline__ float row_wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+__global__ void __launch_bounds__(256) proj_splitk_rows_kernel(ProjGemmArgs g) {
+    __shared__ float wsum[4];
+    const int tid = threadIdx.x;
+    const int row = blockIdx.x;
+    const int ntot = g.Nw[0], nch = ntot / 8;
+    const uint16_t* bias = static_cast<const uint16_t*>(g.b[0]);
+    const uint16_t* R = static_cast<const uint16_t*>(g.R);
+    uint16_t* C = static_cast<uint16_t*>(g.C[0]) + (size_t)row * ntot;
+    uint4 hv[kRowsMaxChunks];
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kRowsMaxChunks; ++i) {
+        const int c = tid + 256 * i;
+        if (c >= nch) continue;
+        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int s = 0; s < g.ksplit; ++s) {
+            const float4* p = reinterpret_cast<const float4*>(g.part + ((size_t)s * g.M + row) * ntot + 8 * c);
+            const float4 x = p[0], y = p[1];
+            acc[0] += x.x; acc[1] += x.y; acc[2] += x.z; acc[3] += x.w;
+            acc[4] += y.x; acc[5] += y.y; acc[6] += y.z; acc[7] += y.w;
+        }
+        float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (bias) {
+            const uint4 b = *reinterpret_cast<const uint4*>(bias + 8 * c);
+            const uint32_t w[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                v[2 * k] = bf_lo(w[k]);
+                v[2 * k + 1] = bf_hi(w[k]);
+            }
+        }
+        uint4 h = make_uint4(pack2bf(acc[0] + v[0], acc[1] + v[1]), pack2bf(acc[2] + v[2], acc[3] + v[3]),
+                             pack2bf(acc[4] + v[4], acc[5] + v[5]), pack2bf(acc[6] + v[6], acc[7] + v[7]));
+        if (R) {
+            const uint4 x = *reinterpret_cast<const uint4*>(R + (size_t)row * ntot + 8 * c);
+            h.x = pack2bf(bf_lo(x.x) + bf_lo(h.x), bf_hi(x.x) + bf_hi(h.x));
+            h.y = pack2bf(bf_lo(x.y) + bf_lo(h.y), bf_hi(x.y) + bf_hi(h.y));
+            h.z = pack2bf(bf_lo(x.z) + bf_lo(h.z), bf_hi(x.z) + bf_hi(h.z));
+            h.w = pack2bf(bf_lo(x.w) + bf_lo(h.w), bf_hi(x.w) + bf_hi(h.w));
+        }
+        hv[i] = h;
+        *reinterpret_cast<uint4*>(C + 8 * c) = h;
+        const uint32_t e[4] = {h.x, h.y, h.z, h.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float lo = bf_lo(e[k]), hi = bf_hi(e[k]);
+            ss = __builtin_fmaf(lo, lo, ss);
+            ss = __builtin_fmaf(hi, hi, ss);
+        }
+    }
+    if (!g.norm_out) return;
+    ss = row_wave_sum(ss);
+    if ((tid & 63) == 0) wsum[tid >> 6] = ss;
+    __syncthreads();
+    const float tot = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+    const float inv = 1.0f / sqrtf(tot / (float)ntot + g.norm_eps);
+    const uint16_t* gs = static_cast<const uint16_t*>(g.norm_g);
+    uint16_t* n = static_cast<uint16_t*>(g.norm_out) + (size_t)row * ntot;
+#pragma unroll
+    for (int i = 0; i < kRowsMaxChunks; ++i) {
+        const int c = tid + 256 * i;
+        if (c >= nch) continue;
+        const uint4 v = hv[i], sc = *reinterpret_cast<const uint4*>(gs + 8 * c);
+        uint4 o;
+        o.x = pack2bf(bf_lo(v.x) * inv * bf_lo(sc.x), bf_hi(v.x) * inv * bf_hi(sc.x));
+        o.y = pack2bf(bf_lo(v.y) * inv * bf_lo(sc.y), bf_hi(v.y) * inv * bf_hi(sc.y));
+        o.z = pack2bf(bf_lo(v.z) * inv * bf_lo(sc.z), bf_hi(v.z) * inv * bf_hi(sc.z));
+        o.w = pack2bf(bf_lo(v.w) * inv * bf_lo(sc.w), bf_hi(v.w) * inv * bf_hi(sc.w));
+        *reinterpret_cast<uint4*>(n + 8 * c) = o;
+    }
+}
+
 // Mid-size row counts (decode of a few hundred sequences): 128 x 128 output tiles, four waves
 // of 64 x 64 (2 x 2 tiles of v_mfma_f32_32x32x16_bf16).  At such M the 256 x 256 tiles leave
 // 10..60 tiles per projection, and filling the chip then takes K splits whose fp32 partial sums
@@ -672,6 +755,14 @@ size_t proj_gemm_part_bytes(int M, int Ntot, int K) {
     return s > 1 ? (size_t)s * M * Ntot * sizeof(float) : 0;
 }
 
+bool proj_gemm_rows_epilogue_ok(int M) { return M > kSkinnyRows; }
+
+size_t proj_gemm_part_bytes_rows_epilogue(int M, int Ntot, int K) {
+    if (!proj_gemm_rows_epilogue_ok(M)) return 0;
+    const int s = M <= kMidMaxRows ? mid_ksplit(M, Ntot, K) : choose_ksplit(M, Ntot, K);
+    return (size_t)std::max(s, 1) * M * Ntot * sizeof(float);
+}
+
 size_t proj_gemm_part_bytes_batched(int batch, int M, int Ntot, int K) {
     if (batch <= 1) return proj_gemm_part_bytes(M, Ntot, K);
     const int s = choose_ksplit(M, Ntot, K, batch);
@@ -688,7 +779,7 @@ hipError_t launch_proj_gemm(const ProjGemmArgs& a_in, hipStream_t s) {
     const int nb = a.batch > 1 ? a.batch : 1;
     if (nb > 1) {
         // a batch runs on the tile kernel only
-        if (a.gated || a.R) return hipErrorInvalidValue;
+        if (a.gated || a.R || a.rows_epilogue) return hipErrorInvalidValue;
         if (a.part) {
             const int ks = choose_ksplit(a.M, a.ntn * kBN, a.K, nb);
             if (ks > 1 && (size_t)nb * ks * a.M * a.ntn * kBN * sizeof(float) <= a.part_bytes) a.ksplit = ks;
@@ -704,6 +795,29 @@ hipError_t launch_proj_gemm(const ProjGemmArgs& a_in, hipStream_t s) {
         const size_t n = (size_t)nb * a.M * a.ntn * kBN / 8;
         hipLaunchKernelGGL(proj_splitk_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
                            s, a);
+        return hipGetLastError();
+    }
+    if (a.rows_epilogue) {
+        // partials (even unsplit) on a tile kernel, then one wave per row adds them with the
+        // bias, R and the norm
+        const int ntot = a.ntn * kBN;
+        if (a.nseg != 1 || a.gated || a.c_f32 || !proj_gemm_rows_epilogue_ok(a.M) || !a.part ||
+            ntot > 8 * 256 * kRowsMaxChunks || (a.norm_out && !a.norm_g))
+            return hipErrorInvalidValue;
+        const bool mid = a.M <= kMidMaxRows;
+        int ks = std::max(mid ? mid_ksplit(a.M, ntot, a.K) : choose_ksplit(a.M, ntot, a.K), 1);
+        while (ks > 1 && (size_t)ks * a.M * ntot * sizeof(float) > a.part_bytes) --ks;
+        if ((size_t)ks * a.M * ntot * sizeof(float) > a.part_bytes) return hipErrorInvalidValue;
+        a.ksplit = ks;
+        if (mid)
+            hipLaunchKernelGGL(proj_gemm_mid_kernel<true>,
+                               dim3((unsigned)(((a.M + kMidM - 1) / kMidM) * (ntot / kMidN) * ks)),
+                               dim3(kThreads), 0, s, a);
+        else
+            hipLaunchKernelGGL(proj_gemm_kernel<true>, dim3((unsigned)(tiles * ks)), dim3(kThreads), 0, s, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(proj_splitk_rows_kernel, dim3((unsigned)a.M), dim3(256), 0, s, a);
         return hipGetLastError();
     }
     const bool rows = !a.c_f32 && proj_gemm_rows(a.M, a.K);

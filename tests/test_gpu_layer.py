@@ -246,6 +246,7 @@ def test_layers_2b_batched_full_size_sampled():
     (2560, 10, 2560, 7680, 1, 20, 3),     # one row: the row GEMV with the residual epilogue
     (2560, 10, 2560, 7680, 4, 20, 3),     # four rows: the row GEMV's widest case
     (512, 2, 768, 1536, 130, 6, 2),       # 128-row tiles with split K (gate|up: 12 k-steps in 5)
+    (512, 2, 512, 768, 1100, 2, 1),       # past 1024 rows: 256-row tiles; add-and-norm in their sums
 ])
 def test_recurrent_layer_decode_continues_prefill(D, nh, Dm, F, N, T0, steps):
     from gated_linear_recurrence_amd import binding
