@@ -745,9 +745,10 @@ int check_norms(const rglru_norm_params* n, int Dm) {
     return RGLRU_OK;
 }
 
-// The MLP on M rows.  With the row kernel (one to four rows) the gating runs in the gate|up
-// launch's epilogue, and a residual, when given, is added in the down launch's epilogue
-// (*res_added tells the caller which happened).
+// The MLP on M rows.  With the row kernel (one to four rows) and the mid-size tiles (65 to
+// 1024 rows) the gating runs in the gate|up launch's epilogue or split reduction; a residual,
+// when given, is added in the down launch's epilogue (row kernel) or row-wise sum
+// (rows_epilogue) (*res_added tells the caller which happened).
 hipError_t run_mlp(const rglru_mlp_params* m, int M, const void* x, void* out, void* ws,
                    float* part, size_t part_bytes, hipStream_t s,
                    const void* residual = nullptr, bool* res_added = nullptr,
@@ -755,7 +756,7 @@ hipError_t run_mlp(const rglru_mlp_params* m, int M, const void* x, void* out, v
     const size_t nf = (size_t)M * m->F;
     void* G = ws;
     void* U = static_cast<char*>(ws) + round256(nf * 2);
-    const bool gated = proj_gemm_rows(M, m->D_model);
+    const bool gated = proj_gemm_gated_ok(M, m->D_model);
     ProjGemmArgs g;
     memset(&g, 0, sizeof g);
     g.A = x; g.W[0] = m->gate_w; g.W[1] = m->up_w; g.b[0] = m->gate_b; g.b[1] = m->up_b;

@@ -84,8 +84,8 @@ struct ProjGemmArgs {
     int ksplit;                  // set by the launcher
     int c_f32;                   // split-K only: C[0] is fp32 (no rounding); the call fails
                                  // unless the launcher splits K
-    // Row kernel (proj_gemm_rows(M, K)), or any shape with rows_epilogue; the call fails
-    // otherwise.
+    // gated: proj_gemm_gated_ok(M, K); R: the row kernel, or any shape with rows_epilogue; the
+    // call fails otherwise.
     int gated;                   // two segments of equal width: C[0] = gelu_tanh(gate) * up,
                                  // from the bf16-rounded segment outputs (C[1] unused)
     const void* R;               // one segment: C = R + the rounded output, rounded again
@@ -103,8 +103,10 @@ struct ProjGemmArgs {
     int batch;
     long long bsA, bsW, bsC, bsb;
 };
-// true when launch_proj_gemm takes the row kernel (which alone supports gated and R)
+// true when launch_proj_gemm takes the row kernel (which supports gated and R)
 bool proj_gemm_rows(int M, int K);
+// true when a GEMM of M rows may be gated: the row kernel, or the mid-size tiles (65..1024 rows)
+bool proj_gemm_gated_ok(int M, int K);
 // fp32 partial-sum bytes the launcher would use for this shape with unlimited part_bytes
 size_t proj_gemm_part_bytes(int M, int Ntot, int K);
 // true when a GEMM of M rows can take rows_epilogue (the tile kernels: M > 64)

@@ -301,13 +301,59 @@ __global__ void __launch_bounds__(kThreads, 1) proj_gemm_kernel(ProjGemmArgs g) 
 
 // C = bias + the sum of the K splits' partials, in split order; eight columns per thread (a
 // segment's columns are a multiple of the tile width, so eight never straddle two segments).
+// Sum of eight columns' partials in split order (as one GEMM adds its k-steps).
+__device__ __forceinline__ void sum_splits(const ProjGemmArgs& g, const float* part, int m, int ntot,
+                                           int n, float (&acc)[8]) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = 0.0f;
+    for (int s = 0; s < g.ksplit; ++s) {
+        const float4* p = reinterpret_cast<const float4*>(part + ((size_t)s * g.M + m) * ntot + n);
+        const float4 x = p[0], y = p[1];
+        acc[0] += x.x; acc[1] += x.y; acc[2] += x.z; acc[3] += x.w;
+        acc[4] += y.x; acc[5] += y.y; acc[6] += y.z; acc[7] += y.w;
+    }
+}
+__device__ __forceinline__ void bias8(const uint16_t* bias, int n, float (&v)[8]) {
+    if (bias) {
+        const uint4 b = *reinterpret_cast<const uint4*>(bias + n);
+        const uint32_t w[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[2 * k] = bf_lo(w[k]);
+            v[2 * k + 1] = bf_hi(w[k]);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = 0.0f;
+    }
+}
+
 __global__ void __launch_bounds__(256) proj_splitk_reduce_kernel(ProjGemmArgs g) {
-    const int ntot = g.ntn * kBN, n8 = ntot / 8;
+    const int ntot = g.ntn * kBN, n8 = (g.gated ? g.Nw[0] : ntot) / 8;
     const size_t i0 = (size_t)blockIdx.x * 256 + threadIdx.x;
     const int nb = g.batch > 1 ? g.batch : 1;
     if (i0 >= (size_t)nb * g.M * n8) return;
     const size_t bi = i0 / ((size_t)g.M * n8), i = i0 - bi * ((size_t)g.M * n8);
     const int m = (int)(i / n8), n = (int)(i % n8) * 8;
+    if (g.gated) {
+        // gate columns n.., up columns Nw[0] + n..: each rounded with its bias, then the gating
+        // step's gelu_tanh(gate) * up, rounded
+        float ag[8], au[8], vg[8], vu[8];
+        sum_splits(g, g.part, m, ntot, n, ag);
+        sum_splits(g, g.part, m, ntot, g.Nw[0] + n, au);
+        bias8(static_cast<const uint16_t*>(g.b[0]), n, vg);
+        bias8(static_cast<const uint16_t*>(g.b[1]), n, vu);
+        uint32_t o[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t gw = pack2bf(ag[2 * k] + vg[2 * k], ag[2 * k + 1] + vg[2 * k + 1]);
+            const uint32_t uw = pack2bf(au[2 * k] + vu[2 * k], au[2 * k + 1] + vu[2 * k + 1]);
+            o[k] = pack2bf(gelu_fast(bf_lo(gw)) * bf_lo(uw), gelu_fast(bf_hi(gw)) * bf_hi(uw));
+        }
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(g.C[0]) + (size_t)m * g.Nw[0] + n) =
+            make_uint4(o[0], o[1], o[2], o[3]);
+        return;
+    }
     const int seg = n < g.Nw[0] ? 0 : (n < g.Nw[0] + g.Nw[1] ? 1 : 2);
     const int nl = n - (seg > 0 ? g.Nw[0] : 0) - (seg > 1 ? g.Nw[1] : 0);
     float v[8];
@@ -445,14 +491,14 @@ constexpr int kMidMaxRows = 1024;   // 64 < M <= this, one GEMM (no batch), bf16
 // four per wave (copy 4 w + j fills LDS chunks 64 (4 w + j) .. + 63).  Rows past `rows` repeat
 // the last row (results never stored).
 __device__ __forceinline__ void copy_mid(const u32x4& rs, uint16_t* lds, int wv, int lane, int K,
-                                         int rows, int kt) {
+                                         int rows, int kt, int row_off = 0) {
     int off[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int p = (4 * wv + j) * 64 + lane;
         const int r = p / kChunks;
         const int c = chunk_pos(r, p % kChunks);
-        off[j] = min(r, rows - 1) * K * 2 + kt * kRowBytes + 16 * c;
+        off[j] = (min(r, rows - 1) - row_off) * K * 2 + kt * kRowBytes + 16 * c;
     }
     copy4(rs, lds_address(lds + 4 * wv * 512), off);
 }
@@ -468,8 +514,18 @@ int mid_ksplit(int M, int Ntot, int K) {
     return (int)std::max<long long>(s, 1);
 }
 
-template <bool kSplitK>
+// kGated (no K split; two segments of equal width, gate and up): a tile takes 64 features of
+// both, the gate rows in tile columns 0..63 and the up rows of the same features in 64..127, so
+// waves (wm, 0) and (wm, 1) hold gate and up of the same outputs in the same registers; the up
+// half hands its rounded values over through LDS and the gate half writes
+// gelu_tanh(gate) * up, rounded as the separate gating step rounds it.
+// the mid kernel takes the gating (in its epilogue, or in the split reduction) above the
+// skinny kernel's rows
+__host__ __device__ inline bool proj_gemm_mid_gated(int M) { return M > kSkinnyRows && M <= kMidMaxRows; }
+
+template <bool kSplitK, bool kGated = false>
 __global__ void __launch_bounds__(kThreads, 1) proj_gemm_mid_kernel(ProjGemmArgs g) {
+    static_assert(!(kSplitK && kGated), "the gating of split sums runs in the reduction");
     __shared__ __attribute__((aligned(16))) uint16_t sa[kMidStages][kMidM * kBK];
     __shared__ __attribute__((aligned(16))) uint16_t sb[kMidStages][kMidN * kBK];
 
@@ -477,14 +533,14 @@ __global__ void __launch_bounds__(kThreads, 1) proj_gemm_mid_kernel(ProjGemmArgs
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wv >> 1, wn = wv & 1;
     const int ntot = g.Nw[0] + g.Nw[1] + g.Nw[2];
-    const int ntm = (g.M + kMidM - 1) / kMidM, ntn = ntot / kMidN;
+    const int ntm = (g.M + kMidM - 1) / kMidM, ntn = kGated ? g.Nw[0] / 64 : ntot / kMidN;
     const int S = kSplitK ? g.ksplit : 1;
     // workgroups go to the 8 XCDs round-robin: each XCD gets a contiguous range of the order
     // (M tiles fastest, then N tiles, then splits), so the tiles of one weight block share an L2
     const int total = ntm * ntn * S, bid = (int)blockIdx.x;
     const int L = (total & 7) == 0 ? (bid & 7) * (total >> 3) + (bid >> 3) : bid;
     const int m0 = __builtin_amdgcn_readfirstlane(L % ntm) * kMidM;
-    const int n0 = __builtin_amdgcn_readfirstlane((L / ntm) % ntn) * kMidN;
+    const int n0 = __builtin_amdgcn_readfirstlane((L / ntm) % ntn) * (kGated ? 64 : kMidN);
     const int ks = kSplitK ? __builtin_amdgcn_readfirstlane(L / (ntm * ntn)) : 0;
     const int seg = n0 < g.Nw[0] ? 0 : (n0 < g.Nw[0] + g.Nw[1] ? 1 : 2);
     const int nl0 = n0 - (seg > 0 ? g.Nw[0] : 0) - (seg > 1 ? g.Nw[1] : 0);
@@ -492,7 +548,9 @@ __global__ void __launch_bounds__(kThreads, 1) proj_gemm_mid_kernel(ProjGemmArgs
     const int kt0 = ks * KT / S, nk = (ks + 1) * KT / S - kt0;
     const int rows = min(g.M - m0, kMidM);
     const uint16_t* A = static_cast<const uint16_t*>(g.A) + (size_t)m0 * K + (size_t)kt0 * kBK;
-    const uint16_t* W = static_cast<const uint16_t*>(g.W[seg]) + (size_t)nl0 * K + (size_t)kt0 * kBK;
+    // gated: waves 2 and 3 copy tile rows 64..127, the up rows of the same features
+    const int wseg = kGated && wv >= 2 ? 1 : seg, wrow_off = kGated && wv >= 2 ? 64 : 0;
+    const uint16_t* W = static_cast<const uint16_t*>(g.W[wseg]) + (size_t)nl0 * K + (size_t)kt0 * kBK;
     // (the ranges run kt0 k-steps past the last row's share; no access reaches that far)
     const u32x4 ra = rsrc_words(A, (uint32_t)(rows * K * 2));
     const u32x4 rb = rsrc_words(W, (uint32_t)(kMidN * K * 2));
@@ -510,7 +568,7 @@ __global__ void __launch_bounds__(kThreads, 1) proj_gemm_mid_kernel(ProjGemmArgs
     for (int q = 0; q < kMidStages - 1; ++q)
         if (q < nk) {
             copy_mid(ra, sa[q], wv, lane, K, rows, q);
-            copy_mid(rb, sb[q], wv, lane, K, kMidN, q);
+            copy_mid(rb, sb[q], wv, lane, K, kMidN, q, wrow_off);
         }
     for (int kt = 0; kt < nk; ++kt) {
         // this wave's copies of k-step kt have landed once at most those of the later k-steps
@@ -525,7 +583,7 @@ __global__ void __launch_bounds__(kThreads, 1) proj_gemm_mid_kernel(ProjGemmArgs
         if (kt + kMidStages - 1 < nk) {
             const int st = (kt + kMidStages - 1) % kMidStages;
             copy_mid(ra, sa[st], wv, lane, K, rows, kt + kMidStages - 1);
-            copy_mid(rb, sb[st], wv, lane, K, kMidN, kt + kMidStages - 1);
+            copy_mid(rb, sb[st], wv, lane, K, kMidN, kt + kMidStages - 1, wrow_off);
         }
         const uint16_t* ca = sa[kt % kMidStages];
         const uint16_t* cb = sb[kt % kMidStages];
@@ -548,6 +606,55 @@ __global__ void __launch_bounds__(kThreads, 1) proj_gemm_mid_kernel(ProjGemmArgs
     // registers 4 q .. 4 q + 3, output columns 32 j + 8 q + 4 (l / 32) + 0..3 (wave offsets added)
     const int ncol = 64 * wn + 4 * (lane >> 5);
     const int mrow = 64 * wm + (lane & 31);
+    if constexpr (kGated) {
+        // gate (wn = 0) and up (wn = 1) of features n0 + 32 j + 8 q + 4 (l / 32) + 0..3, rounded
+        // with their biases; up through LDS (stage memory, free once every wave is past its
+        // last MFMA operands)
+        const uint16_t* bias = static_cast<const uint16_t*>(g.b[wn]);
+        u32x2 gv[2][2][4];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int f = n0 + 4 * (lane >> 5) + 32 * j + 8 * q;
+                const uint2 bw = bias ? *reinterpret_cast<const uint2*>(bias + f) : make_uint2(0u, 0u);
+                const float bv[4] = {bf_lo(bw.x), bf_hi(bw.x), bf_lo(bw.y), bf_hi(bw.y)};
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const f32x16& t = acc[i][j];
+                    gv[i][j][q] = u32x2{pack2bf(t[4 * q] + bv[0], t[4 * q + 1] + bv[1]),
+                                        pack2bf(t[4 * q + 2] + bv[2], t[4 * q + 3] + bv[3])};
+                }
+            }
+        u32x2* const xb = reinterpret_cast<u32x2*>(&sa[0][0]) + wm * (2 * 2 * 4 * 64);
+        __syncthreads();
+        if (wn == 1) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) xb[((i * 2 + j) * 4 + q) * 64 + lane] = gv[i][j][q];
+        }
+        __syncthreads();
+        if (wn == 1) return;
+        const int ldc = g.Nw[0];
+        uint16_t* C = static_cast<uint16_t*>(g.C[0]) + (size_t)m0 * ldc + n0;
+        const __amdgpu_buffer_rsrc_t rc = make_rsrc_n(C, (uint32_t)(rows * ldc * 2));
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const u32x2 gt = gv[i][j][q], up = xb[((i * 2 + j) * 4 + q) * 64 + lane];
+                    const u32x2 v = {pack2bf(gelu_fast(bf_lo(gt[0])) * bf_lo(up[0]), gelu_fast(bf_hi(gt[0])) * bf_hi(up[0])),
+                                     pack2bf(gelu_fast(bf_lo(gt[1])) * bf_lo(up[1]), gelu_fast(bf_hi(gt[1])) * bf_hi(up[1]))};
+                    const int off = ((mrow + 32 * i) * ldc + 4 * (lane >> 5) + 32 * j + 8 * q) * 2;
+                    __builtin_amdgcn_raw_buffer_store_b64(v, rc, off, 0, 0);
+                }
+        return;
+    }
     if constexpr (kSplitK) {
         float* P = g.part + ((size_t)ks * g.M + m0) * ntot + n0;
         const __amdgpu_buffer_rsrc_t rp = make_rsrc_n(P, (uint32_t)(rows * ntot * 4));
@@ -748,6 +855,8 @@ int choose_ksplit(int M, int Ntot, int K, int batch = 1) {
 
 bool proj_gemm_rows(int M, int K) { return M >= 1 && M <= kRowsMax && K % 512 == 0; }
 
+bool proj_gemm_gated_ok(int M, int K) { return proj_gemm_rows(M, K) || proj_gemm_mid_gated(M); }
+
 size_t proj_gemm_part_bytes(int M, int Ntot, int K) {
     if (proj_gemm_rows(M, K)) return 0;
     if (M <= kSkinnyRows && K % (32 * kSkinnyWaves) == 0) return 0;
@@ -821,7 +930,9 @@ hipError_t launch_proj_gemm(const ProjGemmArgs& a_in, hipStream_t s) {
         return hipGetLastError();
     }
     const bool rows = !a.c_f32 && proj_gemm_rows(a.M, a.K);
-    if (a.gated && !(rows && a.nseg == 2 && a.Nw[0] == a.Nw[1])) return hipErrorInvalidValue;
+    if (a.gated && !((rows || (!a.c_f32 && proj_gemm_mid_gated(a.M))) && a.nseg == 2 &&
+                     a.Nw[0] == a.Nw[1]))
+        return hipErrorInvalidValue;
     if (a.R && !(rows && a.nseg == 1)) return hipErrorInvalidValue;
     if (rows) {
         const unsigned blocks = (unsigned)((a.gated ? a.Nw[0] : a.ntn * kBN) / kRowsWaves);
@@ -858,14 +969,18 @@ hipError_t launch_proj_gemm(const ProjGemmArgs& a_in, hipStream_t s) {
             const int ks = mid_ksplit(a.M, ntot, a.K);
             if (ks > 1 && (size_t)ks * a.M * ntot * sizeof(float) <= a.part_bytes) a.ksplit = ks;
         }
-        const unsigned blocks = (unsigned)(((a.M + kMidM - 1) / kMidM) * (ntot / kMidN) * a.ksplit);
+        const unsigned ntm = (unsigned)((a.M + kMidM - 1) / kMidM);
+        const unsigned blocks = ntm * (unsigned)(ntot / kMidN) * (unsigned)a.ksplit;
         if (a.ksplit > 1)
-            hipLaunchKernelGGL(proj_gemm_mid_kernel<true>, dim3(blocks), dim3(kThreads), 0, s, a);
+            hipLaunchKernelGGL((proj_gemm_mid_kernel<true, false>), dim3(blocks), dim3(kThreads), 0, s, a);
+        else if (a.gated)
+            hipLaunchKernelGGL((proj_gemm_mid_kernel<false, true>), dim3(ntm * (unsigned)(a.Nw[0] / 64)),
+                               dim3(kThreads), 0, s, a);
         else
-            hipLaunchKernelGGL(proj_gemm_mid_kernel<false>, dim3(blocks), dim3(kThreads), 0, s, a);
+            hipLaunchKernelGGL((proj_gemm_mid_kernel<false, false>), dim3(blocks), dim3(kThreads), 0, s, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || a.ksplit == 1) return e;
-        const size_t n = (size_t)a.M * ntot / 8;
+        const size_t n = (size_t)a.M * (a.gated ? a.Nw[0] : ntot) / 8;
         hipLaunchKernelGGL(proj_splitk_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256),
                            0, s, a);
         return hipGetLastError();
