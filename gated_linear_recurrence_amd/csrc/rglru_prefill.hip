@@ -783,7 +783,9 @@ prefill_bf16_kernel(PrefillArgs a) {
                 for (int j = 0; j < 16; j += 2) {
                     const float o0 = __builtin_fmaf(accP[mt][j], state_in, accB[mt][j]);
                     const float o1 = __builtin_fmaf(accP[mt][j + 1], state_in, accB[mt][j + 1]);
-                    const uint32_t o01 = pack2bf(o0, o1);
+                    // opaque: otherwise the compiler converts o1 a second time for the high half
+                    // instead of storing that half with ds_write_b16_d16_hi
+                    const uint32_t o01 = (uint32_t)opaque((int)pack2bf(o0, o1));
                     y_lds[iy + (16 * mt + j) * 32] = (uint16_t)o01;
                     y_lds[iy + (16 * mt + j + 1) * 32] = (uint16_t)(o01 >> 16);
                 }
