@@ -202,27 +202,66 @@ __device__ __forceinline__ Gate gate_of(float rp, float ip, float lsg) {
 }
 __device__ __forceinline__ float log_sigmoid(float lam) { return -log1pf(expf(-lam)); }
 
+// Per-token accesses of the scan kernels go through buffer resources based at the block's first
+// token (the block's sequence, chunk and head are uniform): a lane's channel is its 32-bit
+// offset and a token's stride a scalar offset, so no 64-bit address is formed per access.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_at(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0xffffffffu, 0x00020000);
+}
+__device__ __forceinline__ float ld_bf(__amdgpu_buffer_rsrc_t r, int vo, int so) {
+    return bf2f((uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, vo, so, 0));
+}
+__device__ __forceinline__ uint16_t ld_u16(__amdgpu_buffer_rsrc_t r, int vo, int so) {
+    return (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, vo, so, 0);
+}
+__device__ __forceinline__ void st_u16(__amdgpu_buffer_rsrc_t r, int vo, int so, uint16_t v) {
+    __builtin_amdgcn_raw_buffer_store_b16(v, r, vo, so, 0);
+}
+__device__ __forceinline__ void st_f32(__amdgpu_buffer_rsrc_t r, int vo, int so, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, vo, so, 0);
+}
+
+// Block decomposition of the scan kernels: one block of kBs lanes per (sequence, chunk, head),
+// lane = channel of the head; blockIdx = (b * nch + c) * H + h.
+struct ScanBlock {
+    int b, c, h;
+    size_t m0;   // first token of the chunk
+};
+__device__ __forceinline__ ScanBlock scan_block(const BwdArgs& a) {
+    const int nch = a.T / kChunk;
+    ScanBlock s;
+    s.h = (int)(blockIdx.x % (unsigned)a.H);
+    const unsigned bc = blockIdx.x / (unsigned)a.H;
+    s.c = (int)(bc % (unsigned)nch);
+    s.b = (int)(bc / (unsigned)nch);
+    s.m0 = (size_t)s.b * a.T + (size_t)s.c * kChunk;
+    return s;
+}
+
+
 // ---- chunk aggregates, both directions in one forward pass over the chunk -----------------
 // forward: h_end = A h_start + Bh with A = prod a, Bh the local state from 0;
 // reverse: c_start = A c_in + Q with c_t = a_t dh_t, dh_t = dout_t gelu(y_t) + c_{t+1}, i.e.
 // Q = sum_t (a_start ... a_t) dout_t gelu(y_t).
 __global__ void __launch_bounds__(256) bwd_chunk_agg_kernel(BwdArgs a, BwdBufs w) {
-    const int nch = a.T / kChunk;
-    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= (size_t)a.B * nch * a.D) return;
-    const int d = (int)(idx % a.D), c = (int)((idx / a.D) % nch), b = (int)(idx / ((size_t)nch * a.D));
+    const ScanBlock sb = scan_block(a);
+    const int k = threadIdx.x, d = sb.h * kBs + k;
+    const size_t idx = (size_t)blockIdx.x * kBs + k;   // ((b * nch + c) * D + d)
     const size_t M = (size_t)a.B * a.T;
-    const int h = d / kBs, k = d % kBs;
     const float lsg = log_sigmoid(a.lambda[d]);
-    const uint16_t* dout = static_cast<const uint16_t*>(a.dout);
-    const uint16_t* y = static_cast<const uint16_t*>(a.y);
+    const size_t hmo = ((size_t)sb.h * M + sb.m0) * kBs;   // head-major element of token m0
+    const auto rR = rsrc_at(w.R + hmo), rI = rsrc_at(w.I + hmo), rU = rsrc_at(w.U + hmo);
+    const size_t tmo = sb.m0 * a.D + (size_t)sb.h * kBs;   // token-major element of token m0
+    const auto rY = rsrc_at(static_cast<const uint16_t*>(a.y) + tmo);
+    const auto rDo = rsrc_at(static_cast<const uint16_t*>(a.dout) + tmo);
+    const int vo = 2 * k, sD = 2 * a.D;
     float A = 1.0f, Bh = 0.0f, Q = 0.0f;
+#pragma unroll 8
     for (int tt = 0; tt < kChunk; ++tt) {
-        const size_t m = (size_t)b * a.T + c * kChunk + tt, e = hm(h, m, k, M);
-        const Gate g = gate_of(bf2f(w.R[e]), bf2f(w.I[e]), lsg);
+        const Gate g = gate_of(ld_bf(rR, vo, tt * 2 * kBs), ld_bf(rI, vo, tt * 2 * kBs), lsg);
         A *= g.a;
-        Bh = __builtin_fmaf(g.a, Bh, g.m * g.i * bf2f(w.U[e]));
-        Q = __builtin_fmaf(A, bf2f(dout[m * a.D + d]) * gelu_and_grad(bf2f(y[m * a.D + d])).x, Q);
+        Bh = __builtin_fmaf(g.a, Bh, g.m * g.i * ld_bf(rU, vo, tt * 2 * kBs));
+        Q = __builtin_fmaf(A, ld_bf(rDo, vo, tt * sD) * gelu_and_grad(ld_bf(rY, vo, tt * sD)).x, Q);
     }
     w.aggA[idx] = A;
     w.aggB[idx] = Bh;
