@@ -205,17 +205,12 @@ __device__ __forceinline__ float log_sigmoid(float lam) { return -log1pf(expf(-l
 // Per-token accesses of the scan kernels go through buffer resources based at the block's first
 // token (the block's sequence, chunk and head are uniform): a lane's channel is its 32-bit
 // offset and a token's stride a scalar offset, so no 64-bit address is formed per access.
+// The gradient pass also copies whole tiles into LDS through them.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_at(const void* base) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0xffffffffu, 0x00020000);
 }
 __device__ __forceinline__ float ld_bf(__amdgpu_buffer_rsrc_t r, int vo, int so) {
     return bf2f((uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, vo, so, 0));
-}
-__device__ __forceinline__ uint16_t ld_u16(__amdgpu_buffer_rsrc_t r, int vo, int so) {
-    return (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, vo, so, 0);
-}
-__device__ __forceinline__ void st_u16(__amdgpu_buffer_rsrc_t r, int vo, int so, uint16_t v) {
-    __builtin_amdgcn_raw_buffer_store_b16(v, r, vo, so, 0);
 }
 __device__ __forceinline__ void st_f32(__amdgpu_buffer_rsrc_t r, int vo, int so, float v) {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, vo, so, 0);
@@ -338,99 +333,128 @@ __global__ void __launch_bounds__(256) bwd_carry_fill_kernel(BwdArgs a, BwdBufs 
     }
 }
 
-// precise forms for the gradient pass: library tanh, expm1 and IEEE division (the derivative of
-// sqrt(1 - a^2) divides by it, so it keeps full relative accuracy as a -> 1)
-__device__ __forceinline__ float2 gelu_and_grad_precise(float y) {
-    const float k = 0.7978845608028654f;
-    const float th = tanhf(k * (y + 0.044715f * y * y * y));
-    return make_float2(0.5f * y * (1.0f + th),
-                       0.5f * (1.0f + th) +
-                           0.5f * y * (1.0f - th * th) * k * (1.0f + 3.0f * 0.044715f * y * y));
-}
-__device__ __forceinline__ Gate gate_of_precise(float rp, float ip, float lsg) {
-    Gate g;
-    g.r = sigm(rp);
-    g.i = sigm(ip);
-    const float la = 8.0f * g.r * lsg;
-    g.a = __builtin_amdgcn_exp2f(la * kLog2e);
-    g.m = sqrtf(-expm1f(2.0f * la));
-    return g;
-}
-
 // ---- per-element gradients of one chunk ----------------------------------------------------
-__global__ void __launch_bounds__(256) bwd_grad_kernel(BwdArgs a, BwdBufs w) {
+// The block's inputs (32 tokens x 256 channels of R, I, U, y and dout: 80 KB) come into LDS by
+// bulk global -> LDS copies, 1 KB per instruction, all in flight at once; each lane then walks
+// its channel out of LDS (with per-token global loads the pass waited on memory latency).  The
+// gradients of the gate pre-activations and of y replace R, I and y in LDS as the backward walk
+// consumes them, and leave as whole rows at the end: dRI head-major and dy token-major in
+// coalesced 16-byte chunks, and the token-contiguous rows of dR, dI and U for the weight-gradient
+// GEMM, 64 bytes per lane.
+__global__ void __launch_bounds__(128, 2) bwd_grad_kernel(BwdArgs a, BwdBufs w) {
+    constexpr int kHalf = kBs / 2;   // channels per block: half a head
+    __shared__ __attribute__((aligned(16))) uint16_t tR[kChunk * kHalf], tI[kChunk * kHalf],
+        tU[kChunk * kHalf], tY[kChunk * kHalf], tD[kChunk * kHalf];
+    // blockIdx = ((b * nch + c) * H + h) * 2 + half
     const int nch = a.T / kChunk;
-    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= (size_t)a.B * nch * a.D) return;
-    const int d = (int)(idx % a.D), c = (int)((idx / a.D) % nch), b = (int)(idx / ((size_t)nch * a.D));
+    const int half = (int)(blockIdx.x & 1u);
+    const unsigned bh = blockIdx.x >> 1;
+    const int h = (int)(bh % (unsigned)a.H);
+    const unsigned bc = bh / (unsigned)a.H;
+    const int c_ = (int)(bc % (unsigned)nch), b_ = (int)(bc / (unsigned)nch);
+    const size_t m0 = (size_t)b_ * a.T + (size_t)c_ * kChunk;
+    const int t = threadIdx.x, k = half * kHalf + t, d = h * kBs + k;
+    const int wv = t >> 6, lane = t & 63;
+    const size_t idx = (size_t)blockIdx.x * kHalf + t;   // ((b * nch + c) * D + d)
     const size_t M = (size_t)a.B * a.T;
-    const int h = d / kBs, k = d % kBs;
-    const float lsg = log_sigmoid(a.lambda[d]);
-    const float sg = expf(lsg);
-    const uint16_t* dout = static_cast<const uint16_t*>(a.dout);
-    const uint16_t* y = static_cast<const uint16_t*>(a.y);
-    uint16_t* dy = static_cast<uint16_t*>(a.dy);
-    const size_t m0 = (size_t)b * a.T + (size_t)c * kChunk;
-    // forward within the chunk: h_{t-1} of every token
-    float hp[kChunk];
+    const size_t hmo = ((size_t)h * M + m0) * kBs;   // head-major element of token m0
+    const size_t tmo = m0 * a.D + (size_t)h * kBs;   // token-major element of token m0
     {
-        float hv = w.carry[idx];
+        const auto rR = rsrc_at(w.R + hmo), rI = rsrc_at(w.I + hmo), rU = rsrc_at(w.U + hmo);
+        const auto rY = rsrc_at(static_cast<const uint16_t*>(a.y) + tmo);
+        const auto rDo = rsrc_at(static_cast<const uint16_t*>(a.dout) + tmo);
+        const int sD = 2 * a.D;
+        // 1 KB chunk c of a tile is its rows 4c .. 4c+3 (256 bytes each: this half's channels)
 #pragma unroll
-        for (int tt = 0; tt < kChunk; ++tt) {
-            hp[tt] = hv;
-            const size_t e = hm(h, m0 + tt, k, M);
-            const Gate g = gate_of_precise(bf2f(w.R[e]), bf2f(w.I[e]), lsg);
-            hv = __builtin_fmaf(g.a, hv, g.m * g.i * bf2f(w.U[e]));
+        for (int j = 0; j < 4; ++j) {
+            const int c = 4 * wv + j, row = 4 * c + (lane >> 4), col = half * 256 + (lane & 15) * 16;
+            const int ho = row * (2 * kBs) + col, to = row * sD + col;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rR, tR + c * 512, 16, ho, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rI, tI + c * 512, 16, ho, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rU, tU + c * 512, 16, ho, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rY, tY + c * 512, 16, to, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rDo, tD + c * 512, 16, to, 0, 0, 0);
         }
     }
-    uint32_t tr[kChunk / 2], ti[kChunk / 2], tu[kChunk / 2];   // transposed rows, bf16 pairs
-    float cc = w.cin[idx], slam = 0.0f, sba = 0.0f, sbx = 0.0f;
+    const float lsg = log_sigmoid(a.lambda[d]);
+    const float sg = expf(lsg);
+    float hv = w.carry[idx];
+    float cc = w.cin[idx];
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's copies have landed
+    __syncthreads();                      // and the other wave's
+    float hp[kChunk];
+#pragma unroll
+    for (int tt = 0; tt < kChunk; ++tt) {
+        hp[tt] = hv;
+        const int e = tt * kHalf + t;
+        const Gate g = gate_of(bf2f(tR[e]), bf2f(tI[e]), lsg);
+        hv = __builtin_fmaf(g.a, hv, g.m * g.i * bf2f(tU[e]));
+    }
+    const auto rDuv = rsrc_at(w.duv + hmo);
+    float slam = 0.0f, sba = 0.0f, sbx = 0.0f;
 #pragma unroll
     for (int tt = kChunk - 1; tt >= 0; --tt) {
-        const size_t m = m0 + tt, e = hm(h, m, k, M);
-        const float u = bf2f(w.U[e]);
-        const Gate g = gate_of_precise(bf2f(w.R[e]), bf2f(w.I[e]), lsg);
+        const int e = tt * kHalf + t;
+        const float u = bf2f(tU[e]);
+        const Gate g = gate_of(bf2f(tR[e]), bf2f(tI[e]), lsg);
         const float ht = __builtin_fmaf(g.a, hp[tt], g.m * g.i * u);
-        const float yv = bf2f(y[m * a.D + d]), dov = bf2f(dout[m * a.D + d]);
-        const float2 gg = gelu_and_grad_precise(yv);
+        const float yv = bf2f(tY[e]), dov = bf2f(tD[e]);
+        const float2 gg = gelu_and_grad(yv);
         const float dh = __builtin_fmaf(dov, gg.x, cc);
-        dy[m * a.D + d] = f2bf(dov * ht * gg.y);
-        w.duv[e] = dh * g.m * g.i;
+        tY[e] = f2bf(dov * ht * gg.y);
+        st_f32(rDuv, 4 * k, tt * 4 * kBs, dh * g.m * g.i);
         const float dm = dh * g.i * u, di = dh * g.m * u;
-        const float da = dh * hp[tt] - dm * g.a / g.m;
+        const float da = dh * hp[tt] - dm * g.a * __builtin_amdgcn_rcpf(g.m);
         slam += da * g.a * 8.0f * g.r * (1.0f - sg);
         const float dr = da * g.a * 8.0f * lsg;
         const float dRp = dr * g.r * (1.0f - g.r), dIp = di * g.i * (1.0f - g.i);
         sba += dRp;
         sbx += dIp;
-        const uint16_t rb = f2bf(dRp), ib = f2bf(dIp);
-        w.dRI[((size_t)h * M + m) * (2 * kBs) + k] = rb;
-        w.dRI[((size_t)h * M + m) * (2 * kBs) + kBs + k] = ib;
-        const uint32_t ub = w.U[e];
-        if (tt & 1) {
-            tr[tt / 2] = (uint32_t)rb << 16;
-            ti[tt / 2] = (uint32_t)ib << 16;
-            tu[tt / 2] = ub << 16;
-        } else {
-            tr[tt / 2] |= rb;
-            ti[tt / 2] |= ib;
-            tu[tt / 2] |= ub;
-        }
+        tR[e] = f2bf(dRp);
+        tI[e] = f2bf(dIp);
         cc = dh * g.a;
-    }
-    // token-contiguous rows for the weight-gradient GEMM: 64 bytes per lane and array
-    uint4* dr_t = reinterpret_cast<uint4*>(w.dRIt + ((size_t)h * 2 * kBs + k) * M + m0);
-    uint4* di_t = reinterpret_cast<uint4*>(w.dRIt + ((size_t)h * 2 * kBs + kBs + k) * M + m0);
-    uint4* u_t = reinterpret_cast<uint4*>(w.Ut + ((size_t)h * kBs + k) * M + m0);
-#pragma unroll
-    for (int q = 0; q < kChunk / 8; ++q) {
-        dr_t[q] = make_uint4(tr[4 * q], tr[4 * q + 1], tr[4 * q + 2], tr[4 * q + 3]);
-        di_t[q] = make_uint4(ti[4 * q], ti[4 * q + 1], ti[4 * q + 2], ti[4 * q + 3]);
-        u_t[q] = make_uint4(tu[4 * q], tu[4 * q + 1], tu[4 * q + 2], tu[4 * q + 3]);
     }
     w.plam[idx] = slam;
     w.pba[idx] = sba;
     w.pbx[idx] = sbx;
+    __syncthreads();   // every lane's column of dR, dI and dy is in LDS
+    {
+        // dRI, head-major: token tt's row is [dR (256) | dI (256)]; this block's part of it is
+        // bytes half * 256 .. + 255 of each half.  16-byte chunk c: token c / 32, then dR or dI
+        // ((c / 16) & 1) and chunk c % 16 of this half.
+        uint16_t* const dri = w.dRI + 2 * hmo;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int c = t + 128 * i, tt = c >> 5, which = (c >> 4) & 1, q = c & 15;
+            const uint16_t* src = (which ? tI : tR) + tt * kHalf + 8 * q;
+            *reinterpret_cast<uint4*>(dri + (size_t)tt * 2 * kBs + which * kBs + half * kHalf + 8 * q) =
+                *reinterpret_cast<const uint4*>(src);
+        }
+        // dy, token-major: 16-byte chunk c is token c / 16, chunk c % 16 of this half
+        uint16_t* const dyb = static_cast<uint16_t*>(a.dy) + tmo + half * kHalf;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = t + 128 * i, tt = c >> 4, q = c & 15;
+            *reinterpret_cast<uint4*>(dyb + (size_t)tt * a.D + 8 * q) =
+                *reinterpret_cast<const uint4*>(tY + tt * kHalf + 8 * q);
+        }
+    }
+    {
+        // token-contiguous rows for the weight-gradient GEMM: 64 bytes per lane and array
+        uint4* const dr_t = reinterpret_cast<uint4*>(w.dRIt + ((size_t)h * 2 * kBs + k) * M + m0);
+        uint4* const di_t = reinterpret_cast<uint4*>(w.dRIt + ((size_t)h * 2 * kBs + kBs + k) * M + m0);
+        uint4* const u_t = reinterpret_cast<uint4*>(w.Ut + ((size_t)h * kBs + k) * M + m0);
+        auto pair = [&](const uint16_t* tl, int t0) {
+            return (uint32_t)tl[t0 * kHalf + t] | ((uint32_t)tl[(t0 + 1) * kHalf + t] << 16);
+        };
+#pragma unroll
+        for (int q = 0; q < kChunk / 8; ++q) {
+            const int t0 = 8 * q;
+            dr_t[q] = make_uint4(pair(tR, t0), pair(tR, t0 + 2), pair(tR, t0 + 4), pair(tR, t0 + 6));
+            di_t[q] = make_uint4(pair(tI, t0), pair(tI, t0 + 2), pair(tI, t0 + 4), pair(tI, t0 + 6));
+            u_t[q] = make_uint4(pair(tU, t0), pair(tU, t0 + 2), pair(tU, t0 + 4), pair(tU, t0 + 6));
+        }
+    }
 }
 
 // ---- conv backward: dx, the conv0 window, per-chunk partial sums of the conv weights -------
@@ -619,7 +643,8 @@ hipError_t launch_prefill_backward(const BwdArgs& a, hipStream_t s) {
         RG_LAUNCH(bwd_carry_walk_kernel, (size_t)a.B * a.D);
         RG_LAUNCH(bwd_carry_fill_kernel, ngl);
     }
-    RG_LAUNCH(bwd_grad_kernel, nlane);
+    hipLaunchKernelGGL(bwd_grad_kernel, dim3((unsigned)(nlane / (kBs / 2))), dim3(kBs / 2), 0, s, a, w);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     {   // gradient of u through the gates, all heads in one launch
         ProjGemmArgs g;
         memset(&g, 0, sizeof g);
