@@ -748,11 +748,13 @@ int check_norms(const rglru_norm_params* n, int Dm) {
 // The MLP on M rows.  With the row kernel (one to four rows) and the mid-size tiles (65 to
 // 1024 rows) the gating runs in the gate|up launch's epilogue or split reduction; a residual,
 // when given, is added in the down launch's epilogue (row kernel) or row-wise sum
-// (rows_epilogue) (*res_added tells the caller which happened).
+// (rows_epilogue) (*res_added tells the caller which happened).  With in_norm_g (row kernel
+// only) x is the residual stream and the gate|up launch applies the RMSNorm before the MLP.
 hipError_t run_mlp(const rglru_mlp_params* m, int M, const void* x, void* out, void* ws,
                    float* part, size_t part_bytes, hipStream_t s,
                    const void* residual = nullptr, bool* res_added = nullptr,
-                   bool rows_epilogue = false) {
+                   bool rows_epilogue = false, const void* in_norm_g = nullptr,
+                   float in_norm_eps = 0.0f) {
     const size_t nf = (size_t)M * m->F;
     void* G = ws;
     void* U = static_cast<char*>(ws) + round256(nf * 2);
@@ -762,6 +764,7 @@ hipError_t run_mlp(const rglru_mlp_params* m, int M, const void* x, void* out, v
     g.A = x; g.W[0] = m->gate_w; g.W[1] = m->up_w; g.b[0] = m->gate_b; g.b[1] = m->up_b;
     g.C[0] = G; g.C[1] = U; g.M = M; g.K = m->D_model; g.Nw[0] = m->F; g.Nw[1] = m->F; g.nseg = 2;
     g.part = part; g.part_bytes = part_bytes; g.gated = gated;
+    g.in_norm_g = in_norm_g; g.in_norm_eps = in_norm_eps;
     hipError_t e = launch_proj_gemm(g, s);
     if (e == hipSuccess && !gated) e = launch_geglu(G, U, nf, s);
     if (e != hipSuccess) return e;
@@ -819,23 +822,31 @@ size_t layer_tail_bytes(size_t M, int Dm, int F) {
 // output projection is expected to write h = x_in + its output and the second norm itself
 // (rows_epilogue; see fuse_out_proj), and the final residual addition rides on the down
 // projection's sum.
+// With fold (decode layers of one sequence whose projections all take the row kernel), no
+// norm runs on its own: the block's first projection is expected to normalise x_in on the way
+// in (in_norm_g = the temporal scale), its output projection to write h = x_in + its output
+// into L.h (R), and the MLP's gate|up projection normalises h on the way in.
 template <class Block>
 int run_layer(const rglru_norm_params* nrm, const rglru_mlp_params* m, size_t M, int Dm,
               const void* x_in, void* out, const LayerBufs& L, hipStream_t s, Block block,
-              bool fuse = false) {
+              bool fuse = false, bool fold = false) {
     NormArgs na;
     na.x = x_in; na.y = nullptr; na.g = nrm->temporal_scale; na.h = nullptr; na.n = L.a;
     na.M = (int)M; na.D = Dm; na.eps = nrm->eps;
-    hipError_t e = launch_add_rmsnorm(na, s);
+    hipError_t e = hipSuccess;
+    if (!fold) e = launch_add_rmsnorm(na, s);
     if (e != hipSuccess) return hip_fail(e);
     int st = block();
     if (st != RGLRU_OK) return st;
-    if (!fuse) {
+    if (!fuse && !fold) {
         na.x = x_in; na.y = L.b; na.g = nrm->channel_scale; na.h = L.h; na.n = L.a;
         e = launch_add_rmsnorm(na, s);
     }
     bool added = false;
-    if (e == hipSuccess)
+    if (e == hipSuccess && fold)
+        e = run_mlp(m, (int)M, L.h, out, L.mlp, L.part, L.part_bytes, s, L.h, &added, false,
+                    nrm->channel_scale, nrm->eps);
+    else if (e == hipSuccess)
         e = run_mlp(m, (int)M, L.a, out, L.mlp, L.part, L.part_bytes, s, L.h, &added, fuse);
     if (e != hipSuccess) return hip_fail(e);
     if (added) return RGLRU_OK;
@@ -854,6 +865,15 @@ void fuse_out_proj(ProjGemmArgs& g, const rglru_norm_params* nrm, const void* x_
     g.norm_g = nrm->channel_scale;
     g.norm_out = L.a;
     g.norm_eps = nrm->eps;
+}
+
+// A decode layer of one sequence folds both norms into its projections when every projection
+// takes the row kernel: the block's first and output projections (K = Dm and K = Kout), the
+// MLP's gate|up (K = Dm) and down (K = F) projections.  (Every wave of a normalising launch
+// forms the normalised row itself: for one row that costs less than a launch of the norm
+// kernel; for two or four rows it costs more.)
+bool fold_norms(int N, int Dm, int Kout, int F) {
+    return N == 1 && proj_gemm_rows(N, Dm) && proj_gemm_rows(N, Kout) && proj_gemm_rows(N, F);
 }
 
 // out and the workspace against everything else the layer reads or writes
@@ -1061,12 +1081,14 @@ int rglru_recurrent_layer_decode(const rglru_params* p, const rglru_proj_params*
     L.part = L.part_bytes ? reinterpret_cast<float*>(ws + need - L.part_bytes) : nullptr;
     const hipStream_t s = (hipStream_t)stream;
     const bool fuse = L.part && proj_gemm_rows_epilogue_ok(N);
+    const bool fold = !fuse && fold_norms(N, Dm, D, m->F);
     return run_layer(nrm, m, N, Dm, x_t, out_t, L, s, [&]() {
         ProjGemmArgs g;
         memset(&g, 0, sizeof g);
-        g.A = L.a; g.W[0] = q->lin_x_w; g.W[1] = q->lin_y_w; g.b[0] = q->lin_x_b;
+        g.A = fold ? x_t : L.a; g.W[0] = q->lin_x_w; g.W[1] = q->lin_y_w; g.b[0] = q->lin_x_b;
         g.b[1] = q->lin_y_b; g.C[0] = xb; g.C[1] = yb; g.M = N; g.K = Dm; g.Nw[0] = D;
         g.Nw[1] = D; g.nseg = 2; g.part = L.part; g.part_bytes = L.part_bytes;
+        if (fold) { g.in_norm_g = nrm->temporal_scale; g.in_norm_eps = nrm->eps; }
         hipError_t e = launch_proj_gemm(g, s);
         if (e != hipSuccess) return hip_fail(e);
         int r = decode_step_impl(p, N, xb, D, yb, D, mg, D, h, conv_state, dws, dws_bytes, stream,
@@ -1076,9 +1098,10 @@ int rglru_recurrent_layer_decode(const rglru_params* p, const rglru_proj_params*
         g.A = mg; g.W[0] = q->lin_out_w; g.b[0] = q->lin_out_b; g.C[0] = L.b;
         g.M = N; g.K = D; g.Nw[0] = Dm; g.nseg = 1; g.part = L.part; g.part_bytes = L.part_bytes;
         if (fuse) fuse_out_proj(g, nrm, x_t, L);
+        if (fold) { g.R = x_t; g.C[0] = L.h; }
         e = launch_proj_gemm(g, s);
         return e == hipSuccess ? RGLRU_OK : hip_fail(e);
-    }, fuse);
+    }, fuse, fold);
 }
 
 // block part of the attention decode workspace: q, k, v, the attention output, the attention
@@ -1146,13 +1169,15 @@ int rglru_attention_layer_decode(const rglru_attn_params* a, const rglru_norm_pa
     L.part = L.part_bytes ? reinterpret_cast<float*>(ws + need - L.part_bytes) : nullptr;
     const hipStream_t s = (hipStream_t)stream;
     const bool fuse = L.part && proj_gemm_rows_epilogue_ok(N);
+    const bool fold = !fuse && fold_norms(N, Dm, (int)HD, m->F);
     return run_layer(nrm, m, N, Dm, x_t, out_t, L, s, [&]() {
         ProjGemmArgs g;
         memset(&g, 0, sizeof g);
-        g.A = L.a; g.W[0] = a->q_w; g.W[1] = a->k_w; g.W[2] = a->v_w;
+        g.A = fold ? x_t : L.a; g.W[0] = a->q_w; g.W[1] = a->k_w; g.W[2] = a->v_w;
         g.C[0] = qb; g.C[1] = kb; g.C[2] = vb;
         g.M = N; g.K = Dm; g.Nw[0] = (int)HD; g.Nw[1] = kAttnDh; g.Nw[2] = kAttnDh; g.nseg = 3;
         g.part = L.part; g.part_bytes = L.part_bytes;
+        if (fold) { g.in_norm_g = nrm->temporal_scale; g.in_norm_eps = nrm->eps; }
         hipError_t e = launch_proj_gemm(g, s);
         if (e != hipSuccess) return hip_fail(e);
         int r = attn_decode_impl(N, Hq, a->window, a->rope_base, pos, qb, kb, vb, kcache, vcache,
@@ -1163,9 +1188,10 @@ int rglru_attention_layer_decode(const rglru_attn_params* a, const rglru_norm_pa
         g.M = N; g.K = (int)HD; g.Nw[0] = Dm; g.nseg = 1;
         g.part = L.part; g.part_bytes = L.part_bytes;
         if (fuse) fuse_out_proj(g, nrm, x_t, L);
+        if (fold) { g.R = x_t; g.C[0] = L.h; }
         e = launch_proj_gemm(g, s);
         return e == hipSuccess ? RGLRU_OK : hip_fail(e);
-    }, fuse);
+    }, fuse, fold);
 }
 
 // ------------------------------------------------------------------------------------------

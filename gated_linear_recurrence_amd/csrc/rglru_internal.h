@@ -97,6 +97,11 @@ struct ProjGemmArgs {
     const void* norm_g;
     void* norm_out;
     float norm_eps;
+    // in_norm_g (the row kernel only; the call fails otherwise): A holds the rows before an
+    // RMSNorm of scale in_norm_g [K] and the kernel multiplies by RMSNorm(A row) * in_norm_g,
+    // each element rounded to bf16 as the norm kernel would write it
+    const void* in_norm_g;
+    float in_norm_eps;
     // Tile kernel only: `batch` (>= 1; 0 means 1) independent GEMMs of this shape in one launch,
     // item i at A + i bsA, W[o] + i bsW, C[o] + i bsC, b[o] + i bsb (elements), with its own
     // split-K partials [ksplit][M][sum Nw] at part + i ksplit M sum Nw.

@@ -788,7 +788,12 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 constexpr int kRowsMax = 4;        // at most this many rows: gemv_rows_kernel
 constexpr int kRowsWaves = 4;      // features (waves) per workgroup
-template <int NB, bool kGated>   // input rows held per lane: M <= NB
+// kNorm: the input rows are normalised on the way in (in_norm_g).  Each wave first forms every
+// row's sum of squares over the same 8-element chunks per lane (chunk lane + 64 i), in the same
+// order and with the same butterfly as the norm kernel, so each normalised input is bitwise
+// what that kernel would have written; the row is 2 * K bytes, read again from the cache by the
+// main loop.
+template <int NB, bool kGated, bool kNorm>   // input rows held per lane: M <= NB
 __global__ void __launch_bounds__(64 * kRowsWaves) gemv_rows_kernel(ProjGemmArgs g) {
     constexpr int NS = kGated ? 2 : 1;   // weight rows per wave
     const int lane = threadIdx.x & 63;
@@ -804,6 +809,31 @@ __global__ void __launch_bounds__(64 * kRowsWaves) gemv_rows_kernel(ProjGemmArgs
     size_t xo[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) xo[b] = (size_t)min(b, g.M - 1) * K;   // rows past M repeat
+    float inv[NB];
+    const uint16_t* gs = static_cast<const uint16_t*>(g.in_norm_g) + 8 * lane;
+    if constexpr (kNorm) {
+        float ss[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) ss[b] = 0.0f;
+#pragma unroll 4
+        for (int k = 0; k < K; k += 512) {
+            uint4 v[NB];   // every row's chunk in flight together
+#pragma unroll
+            for (int b = 0; b < NB; ++b) v[b] = *reinterpret_cast<const uint4*>(x + xo[b] + k);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const uint32_t e[4] = {v[b].x, v[b].y, v[b].z, v[b].w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float lo = bf_lo(e[q]), hi = bf_hi(e[q]);
+                    ss[b] = __builtin_fmaf(lo, lo, ss[b]);
+                    ss[b] = __builtin_fmaf(hi, hi, ss[b]);
+                }
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) inv[b] = 1.0f / sqrtf(wave_sum(ss[b]) / (float)K + g.in_norm_eps);
+    }
     float acc[NS][NB];
 #pragma unroll
     for (int j = 0; j < NS; ++j)
@@ -814,9 +844,18 @@ __global__ void __launch_bounds__(64 * kRowsWaves) gemv_rows_kernel(ProjGemmArgs
         uint4 wv[NS];
 #pragma unroll
         for (int j = 0; j < NS; ++j) wv[j] = *reinterpret_cast<const uint4*>(w[j] + k);
+        uint4 sv;
+        if constexpr (kNorm) sv = *reinterpret_cast<const uint4*>(gs + k);
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            const uint4 xv = *reinterpret_cast<const uint4*>(x + xo[b] + k);
+            uint4 xv = *reinterpret_cast<const uint4*>(x + xo[b] + k);
+            if constexpr (kNorm) {
+                const float t = inv[b];
+                xv.x = pack2bf(bf_lo(xv.x) * t * bf_lo(sv.x), bf_hi(xv.x) * t * bf_hi(sv.x));
+                xv.y = pack2bf(bf_lo(xv.y) * t * bf_lo(sv.y), bf_hi(xv.y) * t * bf_hi(sv.y));
+                xv.z = pack2bf(bf_lo(xv.z) * t * bf_lo(sv.z), bf_hi(xv.z) * t * bf_hi(sv.z));
+                xv.w = pack2bf(bf_lo(xv.w) * t * bf_lo(sv.w), bf_hi(xv.w) * t * bf_hi(sv.w));
+            }
 #pragma unroll
             for (int j = 0; j < NS; ++j) dot8(wv[j], xv, acc[j][b]);
         }
@@ -888,7 +927,7 @@ hipError_t launch_proj_gemm(const ProjGemmArgs& a_in, hipStream_t s) {
     const int nb = a.batch > 1 ? a.batch : 1;
     if (nb > 1) {
         // a batch runs on the tile kernel only
-        if (a.gated || a.R || a.rows_epilogue) return hipErrorInvalidValue;
+        if (a.gated || a.R || a.rows_epilogue || a.in_norm_g) return hipErrorInvalidValue;
         if (a.part) {
             const int ks = choose_ksplit(a.M, a.ntn * kBN, a.K, nb);
             if (ks > 1 && (size_t)nb * ks * a.M * a.ntn * kBN * sizeof(float) <= a.part_bytes) a.ksplit = ks;
@@ -910,7 +949,7 @@ hipError_t launch_proj_gemm(const ProjGemmArgs& a_in, hipStream_t s) {
         // partials (even unsplit) on a tile kernel, then one wave per row adds them with the
         // bias, R and the norm
         const int ntot = a.ntn * kBN;
-        if (a.nseg != 1 || a.gated || a.c_f32 || !proj_gemm_rows_epilogue_ok(a.M) || !a.part ||
+        if (a.nseg != 1 || a.gated || a.c_f32 || a.in_norm_g || !proj_gemm_rows_epilogue_ok(a.M) || !a.part ||
             ntot > 8 * 256 * kRowsMaxChunks || (a.norm_out && !a.norm_g))
             return hipErrorInvalidValue;
         const bool mid = a.M <= kMidMaxRows;
@@ -934,22 +973,23 @@ hipError_t launch_proj_gemm(const ProjGemmArgs& a_in, hipStream_t s) {
                      a.Nw[0] == a.Nw[1]))
         return hipErrorInvalidValue;
     if (a.R && !(rows && a.nseg == 1)) return hipErrorInvalidValue;
+    if (a.in_norm_g && !rows) return hipErrorInvalidValue;
     if (rows) {
         const unsigned blocks = (unsigned)((a.gated ? a.Nw[0] : a.ntn * kBN) / kRowsWaves);
         const dim3 grid(blocks), blk(64 * kRowsWaves);
-        if (a.gated) {
-            switch (a.M) {
-                case 1: hipLaunchKernelGGL((gemv_rows_kernel<1, true>), grid, blk, 0, s, a); break;
-                case 2: hipLaunchKernelGGL((gemv_rows_kernel<2, true>), grid, blk, 0, s, a); break;
-                default: hipLaunchKernelGGL((gemv_rows_kernel<4, true>), grid, blk, 0, s, a);
-            }
-        } else {
-            switch (a.M) {
-                case 1: hipLaunchKernelGGL((gemv_rows_kernel<1, false>), grid, blk, 0, s, a); break;
-                case 2: hipLaunchKernelGGL((gemv_rows_kernel<2, false>), grid, blk, 0, s, a); break;
-                default: hipLaunchKernelGGL((gemv_rows_kernel<4, false>), grid, blk, 0, s, a);
-            }
+        const int nb = a.M == 1 ? 1 : (a.M == 2 ? 2 : 4);
+#define RG_ROWS(G, NORM)                                                                      \
+        switch (nb) {                                                                         \
+            case 1: hipLaunchKernelGGL((gemv_rows_kernel<1, G, NORM>), grid, blk, 0, s, a); break; \
+            case 2: hipLaunchKernelGGL((gemv_rows_kernel<2, G, NORM>), grid, blk, 0, s, a); break; \
+            default: hipLaunchKernelGGL((gemv_rows_kernel<4, G, NORM>), grid, blk, 0, s, a);  \
         }
+        if (a.gated) {
+            if (a.in_norm_g) { RG_ROWS(true, true) } else { RG_ROWS(true, false) }
+        } else {
+            if (a.in_norm_g) { RG_ROWS(false, true) } else { RG_ROWS(false, false) }
+        }
+#undef RG_ROWS
         return hipGetLastError();
     }
     // the skinny kernel's waves each take whole 32-wide steps of K: K % (32 * waves) == 0

@@ -306,6 +306,51 @@ def test_attention_layer_decode_continues_prefill(Dm, Hq, F, N, W, T0, steps):
     assert e <= H.TOL[synth.BF16]
 
 
+def test_one_row_decode_folds_the_norms_bitwise():
+    """One sequence takes the layers' folded path (each RMSNorm formed inside the projection
+    that consumes it); two copies of the same sequence take the separate norm kernel.  The
+    folded norm repeats the norm kernel's arithmetic in its order, so the outputs and the
+    updated states of the one sequence must equal those of either copy bit for bit."""
+    from gated_linear_recurrence_amd import binding
+    D, Dm, F, Hq, W = 2560, 2560, 7680, 10, 64
+    w = dataclasses.replace(synth.small(synth.WORKLOADS[synth.PREFILL_2B], B=2, T=8), D=D, H=10)
+    p, q = synth.make_params(w, biases=True), synth.make_proj(w, Dm=Dm, biases=True)
+    L = synth.make_layer(w, Dm=Dm, F=F, biases=True)
+    a = synth.make_attn(w, Dm=Dm, n_heads=Hq, bias=True)
+    P = H.dev_params(p, w.H)
+    Q = binding.ProjParams(*[H.to_dev(q[k]) for k in ("lx_w", "lx_b", "ly_w", "ly_b",
+                                                      "lo_w", "lo_b")])
+    A = binding.AttnParams(H.to_dev(a["q_w"]), H.to_dev(a["k_w"]), H.to_dev(a["v_w"]),
+                           H.to_dev(a["o_w"]), H.to_dev(a["o_b"]), Hq, W)
+    Nd, Md = _norms_dev(L), _mlp_dev(L)
+    g = torch.Generator(device="cuda").manual_seed(11)
+    x1 = torch.randn((1, Dm), generator=g, device="cuda").to(torch.bfloat16)
+    h1 = torch.randn((1, D), generator=g, device="cuda") * 0.3
+    c1 = torch.randn((1, 3, D), generator=g, device="cuda").to(torch.bfloat16)
+    x2, h2, c2 = x1.repeat(2, 1), h1.repeat(2, 1), c1.repeat(2, 1, 1)
+    o1 = binding.rglru_recurrent_layer_decode(P, Q, Nd, Md, x1, h1, c1)
+    o2 = binding.rglru_recurrent_layer_decode(P, Q, Nd, Md, x2, h2, c2)
+    torch.cuda.synchronize()
+    for r in range(2):
+        assert torch.equal(o1[0], o2[r]) and torch.equal(h1[0], h2[r]) and torch.equal(c1[0], c2[r]), r
+    k1, k2 = binding.AttnCache(1, W, "cuda"), binding.AttnCache(2, W, "cuda")
+    per = k1.k.numel()                       # the cache is sequence-major
+    assert k2.k.numel() == 2 * per
+    k1.k.normal_(generator=g)
+    k1.v.normal_(generator=g)
+    for r in range(2):
+        k2.k.view(2, per)[r].copy_(k1.k)
+        k2.v.view(2, per)[r].copy_(k1.v)
+    pos1 = torch.full((1,), 40, dtype=torch.int32, device="cuda")
+    pos2 = torch.full((2,), 40, dtype=torch.int32, device="cuda")
+    y1 = binding.rglru_attention_layer_decode(A, Nd, Md, pos1, o1, k1)
+    y2 = binding.rglru_attention_layer_decode(A, Nd, Md, pos2, o2, k2)
+    torch.cuda.synchronize()
+    for r in range(2):
+        assert torch.equal(y1[0], y2[r]), r
+        assert torch.equal(k1.k, k2.k.view(2, per)[r]) and torch.equal(k1.v, k2.v.view(2, per)[r]), r
+
+
 def test_layer_decode_steps_replay_from_a_graph():
     """Decode steps of both layers captured in one HIP graph and replayed three times (eager
     work in between) give bitwise the eager steps' outputs and states."""
