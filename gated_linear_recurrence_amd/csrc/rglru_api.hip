@@ -818,7 +818,7 @@ size_t layer_tail_bytes(size_t M, int Dm, int F) {
 // Launches of the layer after validation: norm 1, the block (through `block`), h and norm 2,
 // the MLP into out, the final residual addition in place (done by the MLP's last launch when
 // that takes the row kernel).
-// With fuse (decode layers of more than 64 rows, which have partial-sum space), the block's
+// With fuse (decode layers of more than four rows, which have partial-sum space), the block's
 // output projection is expected to write h = x_in + its output and the second norm itself
 // (rows_epilogue; see fuse_out_proj), and the final residual addition rides on the down
 // projection's sum.

@@ -89,7 +89,7 @@ struct ProjGemmArgs {
     int gated;                   // two segments of equal width: C[0] = gelu_tanh(gate) * up,
                                  // from the bf16-rounded segment outputs (C[1] unused)
     const void* R;               // one segment: C = R + the rounded output, rounded again
-    // rows_epilogue (one segment of at most 8192 columns, M > 64, part given): the tile
+    // rows_epilogue (one segment of at most 8192 columns, M > 4, part given): the tile
     // kernels write fp32 partials even without a K split, and one workgroup per row adds them
     // with the bias and R, and, with norm_out, also writes RMSNorm(C) * norm_g (the
     // add-and-norm step of the residual layer)
@@ -110,11 +110,11 @@ struct ProjGemmArgs {
 };
 // true when launch_proj_gemm takes the row kernel (which supports gated and R)
 bool proj_gemm_rows(int M, int K);
-// true when a GEMM of M rows may be gated: the row kernel, or the mid-size tiles (65..1024 rows)
+// true when a GEMM of M rows may be gated: the row kernel, or the mid-size tiles (5..1024 rows)
 bool proj_gemm_gated_ok(int M, int K);
 // fp32 partial-sum bytes the launcher would use for this shape with unlimited part_bytes
 size_t proj_gemm_part_bytes(int M, int Ntot, int K);
-// true when a GEMM of M rows can take rows_epilogue (the tile kernels: M > 64)
+// true when a GEMM of M rows can take rows_epilogue (the tile kernels: M > 4)
 bool proj_gemm_rows_epilogue_ok(int M);
 // the partial-sum bytes of that form (at least one split's worth)
 size_t proj_gemm_part_bytes_rows_epilogue(int M, int Ntot, int K);

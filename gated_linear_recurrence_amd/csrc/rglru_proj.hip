@@ -33,7 +33,9 @@ typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
 constexpr int kBM = 256;                    // tile rows (M)
 constexpr int kBN = 256;                    // tile columns (N)
 constexpr int kBK = 64;                     // K per stage
-constexpr int kSkinnyRows = 64;             // at most this many rows: skinny_gemm_kernel
+constexpr int kSkinnyRows = 64;             // at most this many rows: skinny_gemm_kernel (taken
+                                            // when the caller gives no partial-sum space)
+constexpr int kRowsMax = 4;                 // at most this many rows: gemv_rows_kernel
 constexpr int kThreads = 256;               // 4 waves, 2 x 2 over the tile
 constexpr int kChunks = kBK / 8;            // 16-byte chunks per tile row
 constexpr int kRowBytes = kBK * 2;
@@ -519,9 +521,9 @@ int mid_ksplit(int M, int Ntot, int K) {
 // waves (wm, 0) and (wm, 1) hold gate and up of the same outputs in the same registers; the up
 // half hands its rounded values over through LDS and the gate half writes
 // gelu_tanh(gate) * up, rounded as the separate gating step rounds it.
-// the mid kernel takes the gating (in its epilogue, or in the split reduction) above the
-// skinny kernel's rows
-__host__ __device__ inline bool proj_gemm_mid_gated(int M) { return M > kSkinnyRows && M <= kMidMaxRows; }
+// the mid kernel takes the gating (in its epilogue, or in the split reduction) above the row
+// kernel's rows
+__host__ __device__ inline bool proj_gemm_mid_gated(int M) { return M > kRowsMax && M <= kMidMaxRows; }
 
 template <bool kSplitK, bool kGated = false>
 __global__ void __launch_bounds__(kThreads, 1) proj_gemm_mid_kernel(ProjGemmArgs g) {
@@ -695,8 +697,8 @@ __global__ void __launch_bounds__(kThreads, 1) proj_gemm_mid_kernel(ProjGemmArgs
     }
 }
 
-// Few rows (decode: one row per sequence), up to 64, where the row kernel below does not
-// apply.  One workgroup per 16 output features: the weight rows are the A operand of
+// Few rows, up to 64, where the row kernel below does not apply and the caller gives no
+// partial-sum space (a Linear without a workspace).  One workgroup per 16 output features: the weight rows are the A operand of
 // v_mfma_f32_16x16x32_bf16 (16 features x 32 k, each lane 16 bytes of one row) and up to 64
 // input rows the B operand in blocks of 16 columns, so each weight byte is read once and no
 // MFMA work is spent on rows that do not exist.  The eight waves take an eighth of K each, with
@@ -786,7 +788,6 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-constexpr int kRowsMax = 4;        // at most this many rows: gemv_rows_kernel
 constexpr int kRowsWaves = 4;      // features (waves) per workgroup
 // kNorm: the input rows are normalised on the way in (in_norm_g).  Each wave first forms every
 // row's sum of squares over the same 8-element chunks per lane (chunk lane + 64 i), in the same
@@ -898,12 +899,11 @@ bool proj_gemm_gated_ok(int M, int K) { return proj_gemm_rows(M, K) || proj_gemm
 
 size_t proj_gemm_part_bytes(int M, int Ntot, int K) {
     if (proj_gemm_rows(M, K)) return 0;
-    if (M <= kSkinnyRows && K % (32 * kSkinnyWaves) == 0) return 0;
     const int s = M <= kMidMaxRows ? mid_ksplit(M, Ntot, K) : choose_ksplit(M, Ntot, K);
     return s > 1 ? (size_t)s * M * Ntot * sizeof(float) : 0;
 }
 
-bool proj_gemm_rows_epilogue_ok(int M) { return M > kSkinnyRows; }
+bool proj_gemm_rows_epilogue_ok(int M) { return M > kRowsMax; }
 
 size_t proj_gemm_part_bytes_rows_epilogue(int M, int Ntot, int K) {
     if (!proj_gemm_rows_epilogue_ok(M)) return 0;
@@ -992,8 +992,11 @@ hipError_t launch_proj_gemm(const ProjGemmArgs& a_in, hipStream_t s) {
 #undef RG_ROWS
         return hipGetLastError();
     }
-    // the skinny kernel's waves each take whole 32-wide steps of K: K % (32 * waves) == 0
-    if (!a.c_f32 && a.M <= kSkinnyRows && a.K % (32 * kSkinnyWaves) == 0) {
+    // the skinny kernel's waves each take whole 32-wide steps of K: K % (32 * waves) == 0.  With
+    // partial-sum space the mid-size tiles and their K splits serve these rows instead: a 128-row
+    // tile reads each weight byte once too, and the splits cover the chip (at 64 rows the
+    // 26-layer decode step took 2.84 ms that way against 4.76 ms with this kernel).
+    if (!a.c_f32 && !a.part && !a.gated && a.M <= kSkinnyRows && a.K % (32 * kSkinnyWaves) == 0) {
         const unsigned blocks = (unsigned)(a.ntn * kBN / 16);
         switch ((a.M + 15) / 16) {
             case 1: hipLaunchKernelGGL(skinny_gemm_kernel<1>, dim3(blocks), dim3(512), 0, s, a); break;

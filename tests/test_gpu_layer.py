@@ -90,6 +90,7 @@ def _mlp_oracle(L):
     (130, 2560, 7680, False),  # the 2B widths
     (1, 2560, 7680, True),     # one row: gating in the gate|up row kernel's epilogue
     (3, 512, 768, True),       # gated row kernel, then the down projection on the MFMA kernel
+    (40, 512, 768, True),      # no workspace for partial sums: gated mid-size tiles, skinny down
 ])
 def test_mlp_matches_oracle(M, Dm, F, biases):
     from gated_linear_recurrence_amd import binding
@@ -245,6 +246,8 @@ def test_layers_2b_batched_full_size_sampled():
     (2560, 10, 2560, 7680, 2, 20, 3),     # the 2B widths
     (2560, 10, 2560, 7680, 1, 20, 3),     # one row: the row GEMV with the residual epilogue
     (2560, 10, 2560, 7680, 4, 20, 3),     # four rows: the row GEMV's widest case
+    (512, 2, 512, 768, 40, 6, 2),         # 5..64 rows: mid-size tiles with split K, add-and-norm in their sums
+    (2560, 10, 2560, 7680, 16, 4, 2),     # the same at the 2B widths
     (512, 2, 768, 1536, 130, 6, 2),       # 128-row tiles with split K (gate|up: 12 k-steps in 5)
     (512, 2, 512, 768, 1100, 2, 1),       # past 1024 rows: 256-row tiles; add-and-norm in their sums
 ])
@@ -278,6 +281,7 @@ def test_recurrent_layer_decode_continues_prefill(D, nh, Dm, F, N, T0, steps):
     (2560, 10, 7680, 2, 2048, 20, 3),     # the 2B widths and window
     (2560, 10, 7680, 1, 2048, 20, 3),     # one row
     (2560, 10, 7680, 4, 2048, 20, 3),     # four rows
+    (512, 2, 768, 40, 32, 20, 2),         # 5..64 rows: mid-size tiles with split K
     (512, 2, 768, 130, 32, 40, 2),        # 128-row tiles with split K
 ])
 def test_attention_layer_decode_continues_prefill(Dm, Hq, F, N, W, T0, steps):
