@@ -57,14 +57,14 @@ __device__ __forceinline__ int chunk_pos(int r, int c) { return c ^ ((r ^ (r >> 
 // inverse).  Tile row r is global row min(r, rows - 1) relative to the resource base: rows past
 // a ragged M repeat the last row and their results are never stored.
 __device__ __forceinline__ void copy_half(const u32x4& rs, uint16_t* lds, int h, int wv,
-                                          int lane, int K, int rows, int kt) {
+                                          int lane, int K, int rows, int kt, int row_off = 0) {
     int off[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int p = (wv * kCopiesPerWave + 4 * h + j) * 64 + lane;
         const int r = p / kChunks;
         const int c = chunk_pos(r, p % kChunks);
-        off[j] = min(r, rows - 1) * K * 2 + kt * kRowBytes + 16 * c;
+        off[j] = (min(r, rows - 1) - row_off) * K * 2 + kt * kRowBytes + 16 * c;
     }
     copy4(rs, lds_address(lds + (wv * kCopiesPerWave + 4 * h) * 512), off);
 }
@@ -138,8 +138,15 @@ __device__ __forceinline__ void tile_of(int bid, int ntm, int ntn, int& tm, int&
     tn = r / gm;
 }
 
-template <bool kSplitK>
+// kGated (no K split; two segments of equal width, gate and up): a tile takes 128 features of
+// both, the gate rows in tile columns 0..127 and the up rows of the same features in 128..255
+// (waves 0 and 1 copy the gate rows, waves 2 and 3 the up rows), so waves (wm, 0) and (wm, 1)
+// hold gate and up of the same outputs in the same registers; the up half hands its rounded
+// values over through LDS and the gate half writes gelu_tanh(gate) * up, rounded as the
+// separate gating step rounds it.
+template <bool kSplitK, bool kGated = false>
 __global__ void __launch_bounds__(kThreads, 1) proj_gemm_kernel(ProjGemmArgs g) {
+    static_assert(!(kSplitK && kGated), "the gating of split sums runs in the reduction");
     __shared__ __attribute__((aligned(16))) uint16_t a0[kBM * kBK], a1[kBM * kBK];
     __shared__ __attribute__((aligned(16))) uint16_t b0[kBN * kBK], b1[kBN * kBK];
 
@@ -158,16 +165,19 @@ __global__ void __launch_bounds__(kThreads, 1) proj_gemm_kernel(ProjGemmArgs g) 
     // the divisions above run on the vector unit; the tile is uniform, and the buffer resources
     // built from it must sit in scalar registers
     const int m0 = __builtin_amdgcn_readfirstlane(tm) * kBM;
-    const int n0 = __builtin_amdgcn_readfirstlane(tn) * kBN;
+    // gated: the tile's features are n0 .. n0 + 127 of both segments
+    const int n0 = __builtin_amdgcn_readfirstlane(tn) * (kGated ? kBN / 2 : kBN);
     // output segment of this tile (segment widths are multiples of the tile width)
-    const int seg = n0 < g.Nw[0] ? 0 : (n0 < g.Nw[0] + g.Nw[1] ? 1 : 2);
-    const int nl0 = n0 - (seg > 0 ? g.Nw[0] : 0) - (seg > 1 ? g.Nw[1] : 0);
+    const int seg = kGated ? 0 : (n0 < g.Nw[0] ? 0 : (n0 < g.Nw[0] + g.Nw[1] ? 1 : 2));
+    const int nl0 = kGated ? n0 : n0 - (seg > 0 ? g.Nw[0] : 0) - (seg > 1 ? g.Nw[1] : 0);
+    // gated: waves 2 and 3 copy tile rows 128..255, the up rows of the same features
+    const int wseg = kGated && wv >= 2 ? 1 : seg, wrow_off = kGated && wv >= 2 ? kBN / 2 : 0;
     const int K = g.K;                            // row pitch of A and W
     const int Ks = kSplitK ? K / g.ksplit : K;   // this block's share of K
     const int k0 = ks * Ks;
     const int rows = min(g.M - m0, kBM);
     const uint16_t* A = static_cast<const uint16_t*>(g.A) + (size_t)bi * g.bsA + (size_t)m0 * K + k0;
-    const uint16_t* W = static_cast<const uint16_t*>(g.W[seg]) + (size_t)bi * g.bsW + (size_t)nl0 * K + k0;
+    const uint16_t* W = static_cast<const uint16_t*>(g.W[wseg]) + (size_t)bi * g.bsW + (size_t)nl0 * K + k0;
     // (the ranges run k0 elements past the last row's share; no access reaches that far)
     const u32x4 ra = rsrc_words(A, (uint32_t)(rows * K * 2));
     const u32x4 rb = rsrc_words(W, (uint32_t)(kBN * K * 2));
@@ -185,12 +195,12 @@ __global__ void __launch_bounds__(kThreads, 1) proj_gemm_kernel(ProjGemmArgs g) 
     guard_vmem_sgprs(ra, rb);
     copy_half(ra, a0, 0, wv, lane, K, rows, 0);
     copy_half(ra, a0, 1, wv, lane, K, rows, 0);
-    copy_half(rb, b0, 0, wv, lane, K, kBN, 0);
-    copy_half(rb, b0, 1, wv, lane, K, kBN, 0);
+    copy_half(rb, b0, 0, wv, lane, K, kBN, 0, wrow_off);
+    copy_half(rb, b0, 1, wv, lane, K, kBN, 0, wrow_off);
     copy_half(ra, a1, 0, wv, lane, K, rows, 1);
     copy_half(ra, a1, 1, wv, lane, K, rows, 1);
-    copy_half(rb, b1, 0, wv, lane, K, kBN, 1);
-    copy_half(rb, b1, 1, wv, lane, K, kBN, 1);
+    copy_half(rb, b1, 0, wv, lane, K, kBN, 1, wrow_off);
+    copy_half(rb, b1, 1, wv, lane, K, kBN, 1, wrow_off);
     wait_vmcnt<kPerStep>();
     lds_sync();
     bf16x8 fa[4], fb[4];                           // fragments of the current k-step's sub-step 0
@@ -220,7 +230,7 @@ __global__ void __launch_bounds__(kThreads, 1) proj_gemm_kernel(ProjGemmArgs g) 
             auto refill = [&](int h) {
                 if constexpr ((F & kRefill) != 0) {
                     if (h < 2) copy_half(ra, ca, h, wv, lane, K, rows, kt + 2);
-                    else copy_half(rb, cb, h - 2, wv, lane, K, kBN, kt + 2);
+                    else copy_half(rb, cb, h - 2, wv, lane, K, kBN, kt + 2, wrow_off);
                 }
             };
             mma_pipe(ga, gb, acc, xa, xb, 0, wm, wn, lane, fa, fb, refill);
@@ -270,6 +280,50 @@ __global__ void __launch_bounds__(kThreads, 1) proj_gemm_kernel(ProjGemmArgs g) 
                     const int off = ((mrow + 32 * i) * ntot + ncol + 32 * j + 8 * q) * 4;
                     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rp, off,
                                                            0, 0);
+                }
+        return;
+    }
+    if constexpr (kGated) {
+        // gate (wn = 0) and up (wn = 1) of features n0 + 32 j + 8 q + 4 (l / 32) + 0..3, rounded
+        // with their biases; up through LDS (stage memory, free once every wave is past its last
+        // MFMA operands: 32 KB per up wave)
+        const uint16_t* bias = static_cast<const uint16_t*>(g.b[wn]);
+        u32x2* const xb = reinterpret_cast<u32x2*>(wm ? a1 : a0);
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int f = n0 + 4 * (lane >> 5) + 32 * j + 8 * q;
+                const uint2 bw = bias ? *reinterpret_cast<const uint2*>(bias + f) : make_uint2(0u, 0u);
+                const float bv[4] = {bf_lo(bw.x), bf_hi(bw.x), bf_lo(bw.y), bf_hi(bw.y)};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const f32x16& t = acc[i][j];
+                    const u32x2 v = {pack2bf(t[4 * q] + bv[0], t[4 * q + 1] + bv[1]),
+                                     pack2bf(t[4 * q + 2] + bv[2], t[4 * q + 3] + bv[3])};
+                    const int slot = ((i * 4 + j) * 4 + q) * 64 + lane;
+                    if (wn == 1) xb[slot] = v;
+                    else acc[i][j][4 * q] = __uint_as_float(v[0]), acc[i][j][4 * q + 1] = __uint_as_float(v[1]);
+                }
+            }
+        __syncthreads();
+        if (wn == 1) return;
+        const int ldc = g.Nw[0];
+        uint16_t* C = static_cast<uint16_t*>(g.C[0]) + (size_t)m0 * ldc + n0;
+        const __amdgpu_buffer_rsrc_t rc = make_rsrc_n(C, (uint32_t)(rows * ldc * 2));
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const u32x2 gt = {__float_as_uint(acc[i][j][4 * q]), __float_as_uint(acc[i][j][4 * q + 1])};
+                    const u32x2 up = xb[((i * 4 + j) * 4 + q) * 64 + lane];
+                    const u32x2 v = {pack2bf(gelu_fast(bf_lo(gt[0])) * bf_lo(up[0]), gelu_fast(bf_hi(gt[0])) * bf_hi(up[0])),
+                                     pack2bf(gelu_fast(bf_lo(gt[1])) * bf_lo(up[1]), gelu_fast(bf_hi(gt[1])) * bf_hi(up[1]))};
+                    const int off = ((mrow + 32 * i) * ldc + 4 * (lane >> 5) + 32 * j + 8 * q) * 2;
+                    __builtin_amdgcn_raw_buffer_store_b64(v, rc, off, 0, 0);
                 }
         return;
     }
@@ -895,7 +949,7 @@ int choose_ksplit(int M, int Ntot, int K, int batch = 1) {
 
 bool proj_gemm_rows(int M, int K) { return M >= 1 && M <= kRowsMax && K % 512 == 0; }
 
-bool proj_gemm_gated_ok(int M, int K) { return proj_gemm_rows(M, K) || proj_gemm_mid_gated(M); }
+bool proj_gemm_gated_ok(int M, int K) { return proj_gemm_rows(M, K) || M > kRowsMax; }
 
 size_t proj_gemm_part_bytes(int M, int Ntot, int K) {
     if (proj_gemm_rows(M, K)) return 0;
@@ -969,8 +1023,7 @@ hipError_t launch_proj_gemm(const ProjGemmArgs& a_in, hipStream_t s) {
         return hipGetLastError();
     }
     const bool rows = !a.c_f32 && proj_gemm_rows(a.M, a.K);
-    if (a.gated && !((rows || (!a.c_f32 && proj_gemm_mid_gated(a.M))) && a.nseg == 2 &&
-                     a.Nw[0] == a.Nw[1]))
+    if (a.gated && !((rows || (!a.c_f32 && a.M > kRowsMax)) && a.nseg == 2 && a.Nw[0] == a.Nw[1]))
         return hipErrorInvalidValue;
     if (a.R && !(rows && a.nseg == 1)) return hipErrorInvalidValue;
     if (a.in_norm_g && !rows) return hipErrorInvalidValue;
@@ -1036,11 +1089,13 @@ hipError_t launch_proj_gemm(const ProjGemmArgs& a_in, hipStream_t s) {
     if (a.ksplit > 1)
         hipLaunchKernelGGL(proj_gemm_kernel<true>, dim3((unsigned)(tiles * a.ksplit)),
                            dim3(kThreads), 0, s, a);
+    else if (a.gated)
+        hipLaunchKernelGGL((proj_gemm_kernel<false, true>), dim3((unsigned)tiles), dim3(kThreads), 0, s, a);
     else
-        hipLaunchKernelGGL(proj_gemm_kernel<false>, dim3((unsigned)tiles), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((proj_gemm_kernel<false, false>), dim3((unsigned)tiles), dim3(kThreads), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.ksplit == 1) return e;
-    const size_t n = (size_t)a.M * a.ntn * kBN / 8;
+    const size_t n = (size_t)a.M * (a.gated ? a.Nw[0] : a.ntn * kBN) / 8;
     hipLaunchKernelGGL(proj_splitk_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
                        s, a);
     return hipGetLastError();

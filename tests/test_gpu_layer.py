@@ -91,6 +91,7 @@ def _mlp_oracle(L):
     (1, 2560, 7680, True),     # one row: gating in the gate|up row kernel's epilogue
     (3, 512, 768, True),       # gated row kernel, then the down projection on the MFMA kernel
     (40, 512, 768, True),      # no workspace for partial sums: gated mid-size tiles, skinny down
+    (2048, 512, 768, True),    # past 1024 rows: gating in the 256 x 256 tiles' epilogue
 ])
 def test_mlp_matches_oracle(M, Dm, F, biases):
     from gated_linear_recurrence_amd import binding
