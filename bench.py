@@ -795,6 +795,147 @@ def backward_summary(args):
     print(open(BACKWARD_TXT).read())
 
 
+LAYERS_TXT = os.path.join(ROOT, "profiles", "residual-layers-2b-batched-kernel-trace.txt")
+PROJ_TXT = os.path.join(ROOT, "profiles", "proj_gemm_kernel-2b-batched-kernel-trace.txt")
+
+
+def _kernel_short(name):
+    """'void rglru::(anonymous namespace)::proj_gemm_kernel<false, true>(rglru::ProjGemmArgs)'
+    -> 'proj_gemm_kernel<false, true>'."""
+    n = name.replace("(anonymous namespace)::", "")
+    if n.startswith("void "):
+        n = n[5:]
+    depth, end = 0, len(n)
+    for i, ch in enumerate(n):          # the argument list starts at the first '(' outside <>
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            end = i
+            break
+    return n[:end].replace("rglru::", "").replace("unsigned short", "uint16_t")
+
+
+def _trace_dispatches(path):
+    """(start ns, duration ns, kernel short name, workgroups) of this library's dispatches."""
+    out = []
+    for r in _rows(path):
+        if "rglru::" not in r["Kernel_Name"]:
+            continue
+        wg = int(r["Workgroup_Size_X"]) * int(r["Workgroup_Size_Y"]) * int(r["Workgroup_Size_Z"])
+        grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+        t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+        out.append((t0, t1 - t0, _kernel_short(r["Kernel_Name"]), grid // max(wg, 1)))
+    out.sort()
+    return out
+
+
+def _stack_decode_steps(disp, anchor_groups):
+    """Per-kernel time per decode step of the 26-layer stack: the dispatches between the first
+    and the last-but-one step's first attention decode (anchor: attn_dec_kernel with
+    `anchor_groups` workgroups, eight per step) span whole steps."""
+    idx = [i for i, d in enumerate(disp) if d[2] == "attn_dec_kernel" and d[3] == anchor_groups]
+    per_step = sum(1 for i in range(STACK_LAYERS) if i % 3 == 2)   # attention layers per step
+    steps = len(idx) // per_step
+    if steps < 2:
+        return 0, {}
+    lo, hi = idx[0], idx[(steps - 1) * per_step]
+    acc = {}
+    for _, ns, k, g in disp[lo:hi]:
+        e = acc.setdefault((k, g), [0, 0.0])
+        e[0] += 1
+        e[1] += ns
+    return steps - 1, acc
+
+
+def trace_summary(args):
+    """Kernel-trace summaries of the residual layers and the projection GEMMs from a rocprofv3
+    --kernel-trace CSV of `bench.py --legs residual_layers` (no GPU): every kernel of this
+    library grouped by name and grid, and the per-step kernel time of the stack's decode steps
+    for 256 and for 1 sequences; written to profiles/."""
+    disp = _trace_dispatches(args.kernel_trace)
+    groups = {}
+    for _, ns, k, g in disp:
+        groups.setdefault((k, g), []).append(ns)
+    w = synth.WORKLOADS[synth.BATCHED_2B]
+    M, Dm = w.B * w.T, w.D
+    F = synth.MLP_EXPANSION * Dm
+    # large-M projections: 256 x 256 tiles over M = B T rows; the gated gate|up tiles take 128
+    # features of both halves
+    big = {("proj_gemm_kernel<false, false>", (M // 256) * (2 * w.D // 256)): ("x | y", 2 * w.D, Dm),
+           ("proj_gemm_kernel<false, false>", (M // 256) * ((Dm + 512) // 256)): ("q | k | v", Dm + 512, Dm),
+           ("proj_gemm_kernel<false, true>", (M // 256) * (F // 128)): ("MLP gate | up, gated", 2 * F, Dm)}
+
+    def table(f, keep):
+        f.write("%-44s %8s %7s %11s %11s %11s %10s\n" % ("kernel", "groups", "calls", "avg us",
+                                                          "min us", "max us", "total ms"))
+        for (k, g), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+            if keep(k):
+                f.write("%-44s %8d %7d %11.1f %11.1f %11.1f %10.2f\n" % (
+                    k, g, len(v), sum(v) / len(v) / 1e3, min(v) / 1e3, max(v) / 1e3, sum(v) / 1e6))
+
+    def steps_table(f, n_seq, anchor):
+        steps, acc = _stack_decode_steps(disp, anchor)
+        if not steps:
+            f.write("(no decode steps for %d sequences in this trace)\n" % n_seq)
+            return
+        tot = sum(v[1] for v in acc.values()) / steps
+        f.write("\n26-layer stack, one decode step for %d sequences: kernel time per step over %d "
+                "whole steps = %.0f us\n" % (n_seq, steps, tot / 1e3))
+        f.write("%-44s %8s %10s %12s %12s\n" % ("kernel", "groups", "per step", "avg us",
+                                                 "us per step"))
+        for (k, g), (c, ns) in sorted(acc.items(), key=lambda kv: -kv[1][1]):
+            f.write("%-44s %8d %10.2f %12.1f %12.1f\n" % (k, g, c / steps, ns / c / 1e3,
+                                                          ns / steps / 1e3))
+
+    def hdr(f):
+        f.write("commands (from the repository root):\n")
+        for c in args.commands:
+            f.write("  %s\n" % c)
+    with open(LAYERS_TXT, "w") as f:
+        f.write("rocprofv3 kernel trace, the residual layers at the 2B widths (bf16, width %d, MLP "
+                "%d)\non the %s shape (prefill of %d rows) and decode steps of the 26-layer stack\n\n"
+                % (Dm, F, w.name, M))
+        hdr(f)
+        f.write("\nkernel_trace.csv, End - Start, every kernel of this library grouped by kernel and "
+                "grid (the\nprefill leg's own rglru_prefill calls included):\n")
+        table(f, lambda k: True)
+        steps_table(f, 256, 256 * attn_nsplit(256))
+        steps_table(f, 1, attn_nsplit(1))
+        f.write("\nadd_rmsnorm_kernel (four rows per workgroup) serves a layer's first norm, the residual "
+                "add fused\nwith the second norm, and the final residual add; for one decode row the "
+                "norms ride in the\nrow kernel's input (gemv_rows_kernel<1, *, true>).  "
+                "proj_splitk_rows_kernel (one workgroup per\nrow) adds a decode projection's split "
+                "partials with the bias and the residual and writes the\nsecond norm.  The MLP's "
+                "gating runs in the gate|up launch at every row count (the <*, true>\nkernels).\n")
+    with open(PROJ_TXT, "w") as f:
+        f.write("rocprofv3 kernel trace, the projection GEMMs at the 2B widths (bf16)\n\n")
+        hdr(f)
+        f.write("\nLarge M (M = %d rows): 256 x 256 tiles, proj_gemm_kernel<split K, gated>\n" % M)
+        f.write("%-28s %6s %6s %7s %11s %9s\n" % ("launch", "K", "N", "calls", "avg us", "TFLOP/s"))
+        for (k, g), (label, N, K) in big.items():
+            v = groups.get((k, g))
+            if v:
+                avg = sum(v) / len(v)
+                f.write("%-28s %6d %6d %7d %11.1f %9.0f\n" % (label, K, N, len(v), avg / 1e3,
+                                                            2.0 * M * N * K / avg / 1e3))
+        f.write("(the out-projection, o_proj and the MLP's down projection share the N = %d grid; "
+                "down has\nthree times the K, so that grid's average is not one shape's)\n\n" % Dm)
+        f.write("Every projection kernel (large M above; decode rows: the row kernel for one to "
+                "four rows,\nthe mid-size 128 x 128 tiles for 5 to 1024, their split-K reductions):\n")
+        table(f, lambda k: k.startswith("proj_") or k.startswith("gemv_rows"))
+    print(open(LAYERS_TXT).read())
+    print(open(PROJ_TXT).read())
+
+
+def attn_nsplit(N, window=None):
+    """Window splits per sequence of the attention decode (one workgroup each)."""
+    W = synth.ATTN_WINDOW if window is None else window
+    slots = 128 * (4 if N >= 64 else (2 if N >= 16 else 1))
+    return (W + slots - 1) // slots
+
+
 CENSUS_JSON = os.path.join(ROOT, "profiles", "prefill_bf16_kernel-2b-batched-census.json")
 CENSUS_PASSES = [
     # (derived or base counters of one rocprofv3 --pmc pass; each fits the SQ/GRBM limits)
@@ -913,7 +1054,14 @@ def main():
                     help="write the backward's kernel-trace and traffic summary under profiles/ "
                          "from rocprofv3 CSVs (no GPU; --kernel-stats, --fetch, --write, "
                          "--copy-fetch, --copy-write)")
+    ap.add_argument("--trace-summary", action="store_true",
+                    help="write the residual-layer and projection kernel-trace summaries under "
+                         "profiles/ from a rocprofv3 kernel trace CSV (--kernel-trace) of "
+                         "`--legs residual_layers` (no GPU)")
     args = ap.parse_args()
+    if args.trace_summary:
+        trace_summary(args)
+        return
     if args.backward_summary:
         backward_summary(args)
         return
