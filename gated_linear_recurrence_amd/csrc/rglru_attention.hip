@@ -356,13 +356,14 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// One workgroup per (sequence, 128 tpw cache slots): each wave takes tpw (1, 2 or 4) 32-slot tiles
-// (tile 4 tpw sp + 4 i + wave, i < tpw), heads as the 16 columns of S^T = K Q^T and O^T = V^T P^T, and a softmax
+// One workgroup per (sequence, 128 TPW cache slots): each wave takes TPW (1, 2 or 4) 32-slot tiles
+// (tile 4 TPW sp + 4 i + wave, i < TPW), heads as the 16 columns of S^T = K Q^T and O^T = V^T P^T, and a softmax
 // per head over its tiles; the four waves are merged through LDS into one partial result
 // (reference maximum M, normaliser L, unnormalised output O) per head.  Only slots below
 // min(pos + 1, W) hold positions of the window; the others are masked, and their V entries
 // zeroed (a slot never written may hold any bits).
 constexpr int kDecPad = 260;   // LDS row pitch (floats) of the per-wave outputs
+template <int TPW>
 __global__ void __launch_bounds__(256, 2) attn_dec_kernel(AttnDecodeArgs a) {
     __shared__ __attribute__((aligned(16))) float ow[4][16][kDecPad];
     __shared__ float wm[4][16], wl[4][16];
@@ -390,43 +391,58 @@ __global__ void __launch_bounds__(256, 2) attn_dec_kernel(AttnDecodeArgs a) {
     const uint16_t* kseq = static_cast<const uint16_t*>(a.kc) + (size_t)n * (a.Wc / 32) * kTileElems;
     const uint16_t* vseq = static_cast<const uint16_t*>(a.vc) + (size_t)n * (a.Wc / 32) * kTileElems;
 
-    int ntile = 0;   // this wave's tiles holding a slot of the window (a prefix of its tpw)
+    int ntile = 0;   // this wave's tiles holding a slot of the window (a prefix of its TPW)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ntile += (i < a.tpw && (sp * 4 * a.tpw + 4 * i + wv) * 32 < nvalid) ? 1 : 0;
+    for (int i = 0; i < TPW; ++i) ntile += ((sp * 4 * TPW + 4 * i + wv) * 32 < nvalid) ? 1 : 0;
 
     // Pass 1: scores of the wave's tiles, kept in registers, and their exact maximum per head
-    // (no running rescale: branches stay around loads and scores, never around accumulation).
+    // (no running rescale; no branch surrounds the accumulating MFMAs).
     // xs[i][m]: tile i, slot 4 g + m (m < 4) or 16 + 4 g + m - 4, the order of the P^T operand.
-    float xs[4][8];
+    // A tile's 16 fragments (16 KB per wave) are loaded together, the next tile's before this
+    // tile's MFMAs (two register buffers), and the first value tile's during the last key tile
+    // (one buffer for the values: the output accumulators take the registers); the scheduling
+    // barriers keep the compiler from sinking each load next to its use, which left
+    // only two to four fragments of a wave in flight.  The loads are unconditional (a branch
+    // around them makes the compiler's wait counts fall back to waiting for all): a tile past
+    // the wave's live ones re-reads its first tile, clamped to the last tile holding a slot of
+    // the window (cache hits; its scores and values are discarded below).
+    const int last_tile = (nvalid > 0 ? nvalid - 1 : 0) / 32;
+    auto load_tile = [&](bf16x8* f16, const uint16_t* base, int i) {
+        const int tile = min(sp * 4 * TPW + 4 * (i < ntile ? i : 0) + wv, last_tile);
+        const uint16_t* tp = base + (size_t)tile * kTileElems;
+#pragma unroll
+        for (int f = 0; f < 16; ++f)
+            f16[f] = *reinterpret_cast<const bf16x8*>(tp + (f * 64 + lane) * 8);
+    };
+    float xs[TPW][8];
     float mx = -INFINITY;
+    bf16x8 kf[2][16], vf[16];
+    load_tile(kf[0], kseq, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int tile = sp * 4 * a.tpw + 4 * i + wv, s0 = tile * 32;
-        if (i < ntile) {
-            const uint16_t* kt = kseq + (size_t)tile * kTileElems;
-            bf16x8 kf[16];
-#pragma unroll
-            for (int f = 0; f < 16; ++f)
-                kf[f] = *reinterpret_cast<const bf16x8*>(kt + (f * 64 + lane) * 8);
+    for (int i = 0; i < TPW; ++i) {
+        const int tile = sp * 4 * TPW + 4 * i + wv, s0 = tile * 32;
+        if (i + 1 < TPW) load_tile(kf[(i + 1) & 1], kseq, i + 1);
+        else load_tile(vf, vseq, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        {
+            const bf16x8* kc = kf[i & 1];
             f32x4 sa = {0.0f, 0.0f, 0.0f, 0.0f}, sb = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) {
-                sa = mfma16(kf[kk], qf[kk], sa);
-                sb = mfma16(kf[8 + kk], qf[kk], sb);
+                sa = mfma16(kc[kk], qf[kk], sa);
+                sb = mfma16(kc[8 + kk], qf[kk], sb);
             }
+            const bool live = i < ntile;
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                xs[i][m] = sa[m] * sc;
-                xs[i][4 + m] = sb[m] * sc;
+                xs[i][m] = live ? sa[m] * sc : -INFINITY;
+                xs[i][4 + m] = live ? sb[m] * sc : -INFINITY;
             }
-            if (s0 + 32 > nvalid) {
+            if (live && s0 + 32 > nvalid) {
 #pragma unroll
                 for (int m = 0; m < 8; ++m)
                     if (s0 + (m < 4 ? 4 * g + m : 16 + 4 * g + m - 4) >= nvalid) xs[i][m] = -INFINITY;
             }
-        } else {
-#pragma unroll
-            for (int m = 0; m < 8; ++m) xs[i][m] = -INFINITY;
         }
 #pragma unroll
         for (int m = 0; m < 8; ++m) mx = fmaxf(mx, xs[i][m]);
@@ -438,25 +454,23 @@ __global__ void __launch_bounds__(256, 2) attn_dec_kernel(AttnDecodeArgs a) {
 
     // Pass 2: O^T += V^T P^T over the same tiles; a tile past the window contributes zeros
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int tile = sp * 4 * a.tpw + 4 * i + wv, s0 = tile * 32;
-        bf16x8 vf[16];
+    for (int i = 0; i < TPW; ++i) {
+        const int tile = sp * 4 * TPW + 4 * i + wv, s0 = tile * 32;
+        if (i > 0) load_tile(vf, vseq, i);
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8* vc = vf;
         if (i < ntile) {
-            const uint16_t* vt = vseq + (size_t)tile * kTileElems;
-#pragma unroll
-            for (int f = 0; f < 16; ++f)
-                vf[f] = *reinterpret_cast<const bf16x8*>(vt + (f * 64 + lane) * 8);
             if (s0 + 32 > nvalid) {
 #pragma unroll
                 for (int m = 0; m < 8; ++m) {
                     const bool dead = s0 + (m < 4 ? 4 * g + m : 16 + 4 * g + m - 4) >= nvalid;
 #pragma unroll
-                    for (int f = 0; f < 16; ++f) vf[f][m] = dead ? (__bf16)0.0f : vf[f][m];
+                    for (int f = 0; f < 16; ++f) vc[f][m] = dead ? (__bf16)0.0f : vc[f][m];
                 }
             }
         } else {
 #pragma unroll
-            for (int f = 0; f < 16; ++f) vf[f] = bf16x8{};
+            for (int f = 0; f < 16; ++f) vc[f] = bf16x8{};
         }
         bf16x8 pf;
 #pragma unroll
@@ -466,7 +480,7 @@ __global__ void __launch_bounds__(256, 2) attn_dec_kernel(AttnDecodeArgs a) {
             pf[m] = (__bf16)p;
         }
 #pragma unroll
-        for (int j = 0; j < 16; ++j) oacc[j] = mfma16(vf[j], pf, oacc[j]);
+        for (int j = 0; j < 16; ++j) oacc[j] = mfma16(vc[j], pf, oacc[j]);
     }
     lsum += __shfl_xor(lsum, 16);
     lsum += __shfl_xor(lsum, 32);
@@ -526,7 +540,12 @@ hipError_t launch_attention_decode(const AttnDecodeArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(attn_dec_prep_kernel, dim3((unsigned)a.N), dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_dec_kernel, dim3((unsigned)(a.N * a.nsplit)), dim3(256), 0, s, a);
+    const dim3 grid((unsigned)(a.N * a.nsplit));
+    switch (a.tpw) {
+        case 1: hipLaunchKernelGGL(attn_dec_kernel<1>, grid, dim3(256), 0, s, a); break;
+        case 2: hipLaunchKernelGGL(attn_dec_kernel<2>, grid, dim3(256), 0, s, a); break;
+        default: hipLaunchKernelGGL(attn_dec_kernel<4>, grid, dim3(256), 0, s, a);
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attn_dec_combine_kernel, dim3((unsigned)(a.N * a.Hq)), dim3(256), 0, s, a);
