@@ -365,21 +365,25 @@ __device__ __forceinline__ size_t u_frag_offset(size_t n, size_t c0, int bs, int
     return ((((n / 16) * (size_t)H + head) * (size_t)(bs / 32) + s) * 64 + g * 16 + n % 16) * 8;
 }
 
-// Pass 1 of the split step: u = conv([window, x_t]) for one 8-channel chunk of NS sequences
-// per thread (the chunk's taps and bias are loaded once and applied to all NS), written to the
-// workspace in the storage dtype (nearest-even, as the fused step rounds it) in the order above,
-// and the window shifted in place (elementwise: no thread reads what another writes).
-// Consecutive threads take consecutive chunks, so each load instruction covers whole rows.
-template <typename ST, int NS>
+// Pass 1 of the split step: u = conv([window, x_t]) for 8 channels of one sequence per thread,
+// written to the workspace in the storage dtype (nearest-even, as the fused step rounds it) in
+// the order above, and the window shifted in place (elementwise: no thread reads what another
+// writes).  A wave covers one 1 KB block of that order (16 sequences x 32 channels of one head:
+// lane = 16 * (8-channel group) + sequence), so each of its u stores writes one whole block
+// instead of sixteen-byte pieces of blocks that other workgroups complete; the four waves of a
+// workgroup take neighbouring 32-channel slices, so the window and x rows they read and write
+// come in whole 256-byte pieces per sequence.
+template <typename ST>
 __global__ void __launch_bounds__(256) decode_conv_kernel(DecodeArgs a) {
     using S = Store<ST>;
-    const unsigned D8 = (unsigned)a.D >> 3;
-    const unsigned groups = (unsigned)((a.N + NS - 1) / NS);
     const unsigned i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= groups * D8) return;
-    const size_t D = (size_t)a.D;
-    const unsigned ng = i / D8;
-    const size_t c0 = (size_t)(i - ng * D8) * 8;
+    const unsigned blk = i >> 6, lane = i & 63u;
+    const unsigned nslice = (unsigned)a.D >> 5;   // 32-channel slices of all heads
+    const unsigned g16 = blk / nslice;            // group of 16 sequences
+    const int n_ = (int)(g16 * 16u + (lane & 15u));
+    if (n_ >= a.N) return;
+    const size_t D = (size_t)a.D, n = (size_t)n_;
+    const size_t c0 = (size_t)(blk - g16 * nslice) * 32 + (size_t)(lane >> 4) * 8;
     float w[32], cb[8];
     const ST* cw = static_cast<const ST*>(a.conv_w) + c0 * 4;  // [channel][tap]
 #pragma unroll
@@ -394,38 +398,27 @@ __global__ void __launch_bounds__(256) decode_conv_kernel(DecodeArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) cb[e] = 0.0f;
     }
-    // rows past N repeat row N-1 and are not stored
-    float s0[NS][8], s1[NS][8], s2[NS][8], xt[NS][8];
+    float s0[8], s1[8], s2[8], xt[8];
+    ST* cs = static_cast<ST*>(a.conv_state) + n * 3 * D + c0;
+    S::load8(cs, s0);
+    S::load8(cs + D, s1);
+    S::load8(cs + 2 * D, s2);
+    S::load8(static_cast<const ST*>(a.x) + n * (size_t)a.ld_x + c0, xt);
+    float u[8];
 #pragma unroll
-    for (int k = 0; k < NS; ++k) {
-        const size_t n = (size_t)min((int)(ng * NS) + k, a.N - 1);
-        const ST* cs = static_cast<const ST*>(a.conv_state) + n * 3 * D + c0;
-        S::load8(cs, s0[k]);
-        S::load8(cs + D, s1[k]);
-        S::load8(cs + 2 * D, s2[k]);
-        S::load8(static_cast<const ST*>(a.x) + n * (size_t)a.ld_x + c0, xt[k]);
+    for (int e = 0; e < 8; ++e) {
+        // tap j multiplies x_{t-3+j}: the window holds x_{t-3}, x_{t-2}, x_{t-1}
+        float acc = __builtin_fmaf(w[4 * e + 0], s0[e], cb[e]);
+        acc = __builtin_fmaf(w[4 * e + 1], s1[e], acc);
+        acc = __builtin_fmaf(w[4 * e + 2], s2[e], acc);
+        u[e] = __builtin_fmaf(w[4 * e + 3], xt[e], acc);
     }
-#pragma unroll
-    for (int k = 0; k < NS; ++k) {
-        const int nk = (int)(ng * NS) + k;
-        if (nk >= a.N) break;
-        const size_t n = (size_t)nk;
-        float u[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            // tap j multiplies x_{t-3+j}: the window holds x_{t-3}, x_{t-2}, x_{t-1}
-            float acc = __builtin_fmaf(w[4 * e + 0], s0[k][e], cb[e]);
-            acc = __builtin_fmaf(w[4 * e + 1], s1[k][e], acc);
-            acc = __builtin_fmaf(w[4 * e + 2], s2[k][e], acc);
-            u[e] = __builtin_fmaf(w[4 * e + 3], xt[k][e], acc);
-        }
-        S::store8(static_cast<ST*>(a.u_ws) + u_frag_offset(n, c0, a.D / a.H, a.H), u);
-        // the stored values round-trip exactly (bf16 -> fp32 -> bf16)
-        ST* cs = static_cast<ST*>(a.conv_state) + n * 3 * D + c0;
-        S::store8(cs, s1[k]);
-        S::store8(cs + D, s2[k]);
-        S::store8(cs + 2 * D, xt[k]);
-    }
+    // (blk, lane) is exactly this thread's place in the fragment order: u_frag_offset(n, c0)
+    S::store8(static_cast<ST*>(a.u_ws) + ((size_t)blk * 64 + lane) * 8, u);
+    // the stored values round-trip exactly (bf16 -> fp32 -> bf16)
+    S::store8(cs, s1);
+    S::store8(cs + D, s2);
+    S::store8(cs + 2 * D, xt);
 }
 
 // Global -> LDS copy of 16 bytes per lane (buffer load with the LDS bit).
@@ -744,18 +737,16 @@ static int gate_waves(int N, int H, int bs, int ncu) {
     return best;
 }
 
-constexpr int kConvSeqs = 1;     // sequences per thread in the split step's conv pass
 constexpr int kConvBlock = 256;  // threads per workgroup of the conv pass
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int bs, hipStream_t s) {
     const dim3 grid((a.N + 31) / 32, a.H);
-    // the split form's conv pass indexes (sequence, 8-channel chunk) pairs in 32 bits; beyond
-    // that (N * D / 8 >= 2^31, some 6.7 million sequences at D = 2560) the fused kernel runs
-    const size_t pairs = (size_t)((a.N + kConvSeqs - 1) / kConvSeqs) * (size_t)(a.D / 8);
-    if (dtype == 1 && a.u_ws != nullptr && pairs < ((size_t)1 << 31)) {
+    // the split form's conv pass indexes its threads (16-sequence group, 32-channel slice,
+    // lane) in 32 bits; beyond that (some 6.7 million sequences at D = 2560) the fused kernel runs
+    const size_t nc = (size_t)((a.N + 15) / 16) * (size_t)(a.D / 32) * 64;
+    if (dtype == 1 && a.u_ws != nullptr && nc < ((size_t)1 << 31)) {
         // split: conv pass over (sequence, 8-channel chunk), then the gate pass
-        const size_t nc = pairs;
-        hipLaunchKernelGGL((decode_conv_kernel<uint16_t, kConvSeqs>),
+        hipLaunchKernelGGL((decode_conv_kernel<uint16_t>),
                            dim3((unsigned)((nc + kConvBlock - 1) / kConvBlock)), dim3(kConvBlock), 0, s, a);
         const int nw = gate_waves(a.N, a.H, bs, device_cu_count());
         const unsigned g2 = (unsigned)(((a.N + 16 * nw - 1) / (16 * nw)) * a.H * (bs / 32));
