@@ -4,13 +4,15 @@
 //   L = sum_t dout_t . out_t + dh_last . h_{T-1}.
 //
 // Intermediates are head-major, [H][B*T][256] (channel k of head h of token m at
-// (h * M + m) * 256 + k), so that the three block-diagonal products are plain GEMMs of the
-// projection kernel, one launch per product with the heads as a batch:
-//   gates:      [Rpre | Ipre]_h = U_h [W_a[h]; W_x[h]]^T + b           (K = 256, two segments)
+// (h * M + m) * 256 + k).  The three block-diagonal products:
+//   gates:      [Rpre | Ipre]_h = U_h [W_a[h]; W_x[h]]^T + b           (K = 256)
 //   input grad: dU_h = [dRpre | dIpre]_h [W_a[h]^T | W_x[h]^T]^T       (K = 512)
 //   weights:    [dW_a; dW_x]_h = [dRpre | dIpre]_h^T U_h                (K = B*T, split K, fp32)
-// The scans run per channel over chunks of 32 tokens: local aggregates of both directions in one
-// pass, sequential carries over the chunks, then a pass that uses the carries (forward for h; the backward recurrence
+// The first runs inside the front pass (conv, gates on MFMA with the weights held in registers,
+// chunk aggregates); the other two are plain GEMMs of the projection kernel, one launch each
+// with the heads as a batch.  The scans run per channel over chunks of 32 tokens: local
+// aggregates of both directions (front pass), sequential carries over the chunks, then a pass
+// that uses the carries (forward for h; the backward recurrence
 //   dh_t = dout_t gelu(y_t) + a_{t+1} dh_{t+1}
 // in reverse, re-running the chunk's forward in registers to have h_{t-1}).
 #include <math.h>
@@ -132,50 +134,6 @@ __device__ __forceinline__ void unpack8(uint4 v, float* f) {
     }
 }
 
-constexpr int kConvRun = 8;   // tokens per thread in the conv (T % 32 == 0, so runs stay in one sequence)
-
-__global__ void __launch_bounds__(256) bwd_conv_fwd_kernel(BwdArgs a, BwdBufs w) {
-    // grid: (B * T / kConvRun token runs, D / 2048 channel blocks); thread: channels d .. d + 7 of
-    // kConvRun consecutive tokens, each x row loaded once
-    const size_t M = (size_t)a.B * a.T;
-    const int d = (blockIdx.y * 256 + threadIdx.x) * 8;
-    if (d >= a.D) return;
-    const size_t m0 = (size_t)blockIdx.x * kConvRun;
-    const int b = (int)(m0 / a.T), t0 = (int)(m0 % a.T);
-    const uint16_t* x = static_cast<const uint16_t*>(a.x);
-    const uint16_t* c0 = static_cast<const uint16_t*>(a.conv0);
-    const uint4* cw = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.conv_w) + (size_t)d * 4);
-    float bias[8], wt[32];
-    if (a.conv_b) unpack8(*reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.conv_b) + d), bias);
-    else
-#pragma unroll
-        for (int q = 0; q < 8; ++q) bias[q] = 0.0f;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) unpack8(cw[q], wt + 8 * q);   // wt[4 c + j]: channel d + c, tap j
-    float xr[kConvRun + 3][8];   // x~ at t0 - 3 .. t0 + kConvRun - 1
-#pragma unroll
-    for (int r = 0; r < kConvRun + 3; ++r) {
-        const int p = t0 - 3 + r;
-        if (p >= 0) unpack8(*reinterpret_cast<const uint4*>(x + ((size_t)b * a.T + p) * a.D + d), xr[r]);
-        else if (c0) unpack8(*reinterpret_cast<const uint4*>(c0 + ((size_t)b * 3 + p + 3) * a.D + d), xr[r]);
-        else
-#pragma unroll
-            for (int q = 0; q < 8; ++q) xr[r][q] = 0.0f;
-    }
-#pragma unroll
-    for (int tt = 0; tt < kConvRun; ++tt) {
-        float u[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            float acc = bias[q];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc = __builtin_fmaf(wt[4 * q + j], xr[tt + j][q], acc);
-            u[q] = acc;
-        }
-        *reinterpret_cast<uint4*>(w.U + hm(d / kBs, m0 + tt, d % kBs, M)) =
-            make_uint4(pack2bf(u[0], u[1]), pack2bf(u[2], u[3]), pack2bf(u[4], u[5]), pack2bf(u[6], u[7]));
-    }
-}
 
 // ---- [W_a^T | W_x^T] per head: Wt[h][k][j'] ------------------------------------------------
 __global__ void __launch_bounds__(256) bwd_wtrans_kernel(BwdArgs a, BwdBufs w) {
@@ -234,33 +192,242 @@ __device__ __forceinline__ ScanBlock scan_block(const BwdArgs& a) {
 }
 
 
-// ---- chunk aggregates, both directions in one forward pass over the chunk -----------------
-// forward: h_end = A h_start + Bh with A = prod a, Bh the local state from 0;
-// reverse: c_start = A c_in + Q with c_t = a_t dh_t, dh_t = dout_t gelu(y_t) + c_{t+1}, i.e.
-// Q = sum_t (a_start ... a_t) dout_t gelu(y_t).
-__global__ void __launch_bounds__(256) bwd_chunk_agg_kernel(BwdArgs a, BwdBufs w) {
-    const ScanBlock sb = scan_block(a);
-    const int k = threadIdx.x, d = sb.h * kBs + k;
-    const size_t idx = (size_t)blockIdx.x * kBs + k;   // ((b * nch + c) * D + d)
-    const size_t M = (size_t)a.B * a.T;
-    const float lsg = log_sigmoid(a.lambda[d]);
-    const size_t hmo = ((size_t)sb.h * M + sb.m0) * kBs;   // head-major element of token m0
-    const auto rR = rsrc_at(w.R + hmo), rI = rsrc_at(w.I + hmo), rU = rsrc_at(w.U + hmo);
-    const size_t tmo = sb.m0 * a.D + (size_t)sb.h * kBs;   // token-major element of token m0
-    const auto rY = rsrc_at(static_cast<const uint16_t*>(a.y) + tmo);
-    const auto rDo = rsrc_at(static_cast<const uint16_t*>(a.dout) + tmo);
-    const int vo = 2 * k, sD = 2 * a.D;
-    float A = 1.0f, Bh = 0.0f, Q = 0.0f;
-#pragma unroll 8
-    for (int tt = 0; tt < kChunk; ++tt) {
-        const Gate g = gate_of(ld_bf(rR, vo, tt * 2 * kBs), ld_bf(rI, vo, tt * 2 * kBs), lsg);
-        A *= g.a;
-        Bh = __builtin_fmaf(g.a, Bh, g.m * g.i * ld_bf(rU, vo, tt * 2 * kBs));
-        Q = __builtin_fmaf(A, ld_bf(rDo, vo, tt * sD) * gelu_and_grad(ld_bf(rY, vo, tt * sD)).x, Q);
+// ---- front pass: conv, gate pre-activations and chunk aggregates in one persistent kernel ----
+// One workgroup of eight waves per CU, pinned to a gate head: wave w keeps the MFMA B fragments
+// of output channels [32w, 32w + 32) of both gate blocks in VGPRs for the kernel's lifetime, so
+// the head's 256 KB of gate weights are read once per workgroup instead of once per output
+// tile.  The workgroup walks units of 64 tokens of one sequence (two scan chunks):
+//   1. global -> LDS copies of the unit's x rows (with the 3-token halo from the previous tokens,
+//      the conv0 window or zeros), and of y and dout rows of each wave's 32 channels;
+//   2. conv (fp32, taps in order from the bias, as the per-token definition adds them), u rounded
+//      to bf16 into an LDS tile and out to U;
+//   3. both gates' pre-activations on MFMA (v_mfma_f32_32x32x16_bf16, K in natural order), tile
+//      rows permuted so that each lane holds 32 consecutive tokens of one channel: the low
+//      half-wave chunk 0 of the unit, the high half-wave chunk 1;
+//   4. per lane: R and I = bias + product rounded to bf16 (as stored), then the chunk's forward
+//      aggregate (prod a, local state from 0) and reverse aggregate Q from the rounded values,
+//      in token order.
+// Outputs: U, R, I head-major and the aggregates, exactly as the separate conv, GEMM and
+// aggregate passes would produce them.
+constexpr int kFSeg = 64;                  // tokens per unit
+constexpr int kFWaves = 8;
+constexpr int kFThreads = 64 * kFWaves;
+constexpr int kFRow = kBs + 8;             // u row stride (elements)
+constexpr int kFXRows = 20;                // x rows of a wave: tokens 16 tg - 3 .. 16 tg + 16
+constexpr int kFXElems = kFXRows * 128;
+constexpr int kFYElems = kFSeg * 32 + 32;  // y (or dout) rows of a wave's 32 channels
+
+// u row of token t (0..63): tokens 32..63 have row bits 2..3 flipped, so the A-fragment reads of
+// tokens t and t + 32 in one pass fall in different bank groups
+__device__ __forceinline__ int f_urow(int t) { return t ^ (((t >> 5) & 1) * 12); }
+// y / dout row r of a wave's region: rows 32..63 start 64 bytes later (the two half-waves'
+// 2-byte reads of rows r and r + 32 then fall in different banks)
+__device__ __forceinline__ int f_yrow(int r) { return r * 32 + ((r >> 5) << 5); }
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_len(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+// A copy the compiler cannot see through: addresses derived from it inside the unit loop are
+// formed there (one base plus constant offsets) instead of being hoisted out of the loop for
+// every token, which would not fit beside the gate weights held in registers.
+__device__ __forceinline__ int f_opaque(int v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+__device__ __forceinline__ void f_wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
+__device__ __forceinline__ void f_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__global__ void __launch_bounds__(kFThreads) bwd_front_kernel(BwdArgs a, BwdBufs w, int wph) {
+    __shared__ __attribute__((aligned(16))) uint16_t u_lds[kFSeg * kFRow];
+    __shared__ __attribute__((aligned(16))) uint16_t x_lds[kFWaves * kFXElems];
+    __shared__ __attribute__((aligned(16))) uint16_t y_lds[kFWaves * kFYElems];
+    __shared__ __attribute__((aligned(16))) uint16_t d_lds[kFWaves * kFYElems];
+    __shared__ __attribute__((aligned(16))) float4 ctap[kBs];   // conv taps of a channel, fp32
+    __shared__ float cbias[kBs], gba[kBs], gbx[kBs], glsg[kBs];
+    const uint32_t* const x_lds32 = reinterpret_cast<const uint32_t*>(x_lds);
+    uint32_t* const u_lds32 = reinterpret_cast<uint32_t*>(u_lds);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // placement: workgroups are dealt to the 8 XCDs round-robin; consecutive slots of one XCD
+    // serve one head, so each XCD's L2 holds few heads' inputs
+    const unsigned G = gridDim.x, bid = blockIdx.x;
+    const unsigned xcd = bid & 7u, jx = bid >> 3, per = G >> 3, rem = G & 7u;
+    const unsigned slot = xcd * per + min(xcd, rem) + jx;
+    const int head = (int)(slot / (unsigned)wph), jw = (int)(slot % (unsigned)wph);
+    if (head >= a.H) return;
+    const int B = a.B, T = a.T, D = a.D;
+    const size_t M = (size_t)B * T;
+    const int nseg = (T + kFSeg - 1) / kFSeg, nch = T / kChunk;
+    const int units = B * nseg;
+
+    for (int i = tid; i < kBs; i += kFThreads) {
+        const int d = head * kBs + i;
+        float t4[4];
+        const uint16_t* cw = static_cast<const uint16_t*>(a.conv_w) + (size_t)d * 4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) t4[j] = bf2f(cw[j]);
+        ctap[i] = make_float4(t4[0], t4[1], t4[2], t4[3]);
+        cbias[i] = a.conv_b ? bf2f(static_cast<const uint16_t*>(a.conv_b)[d]) : 0.0f;
+        gba[i] = a.ba ? bf2f(static_cast<const uint16_t*>(a.ba)[d]) : 0.0f;
+        gbx[i] = a.bx ? bf2f(static_cast<const uint16_t*>(a.bx)[d]) : 0.0f;
+        glsg[i] = log_sigmoid(a.lambda[d]);
     }
-    w.aggA[idx] = A;
-    w.aggB[idx] = Bh;
-    w.bQ[idx] = Q;
+    // gate weights of this wave's 32 channels: B fragments of the 16 K steps (lane half kh
+    // supplies inputs 16 s + 8 kh .. + 7 of step s)
+    const int ln = lane & 31, kh = lane >> 5;
+    bf16x8 wA[kBs / 16], wX[kBs / 16];
+    {
+        const size_t chn = (size_t)head * kBs + 32 * wv + ln;
+        const uint16_t* war = static_cast<const uint16_t*>(a.wa) + chn * kBs;
+        const uint16_t* wxr = static_cast<const uint16_t*>(a.wx) + chn * kBs;
+#pragma unroll
+        for (int s = 0; s < kBs / 16; ++s) {
+            wA[s] = *reinterpret_cast<const bf16x8*>(war + 16 * s + 8 * kh);
+            wX[s] = *reinterpret_cast<const bf16x8*>(wxr + 16 * s + 8 * kh);
+        }
+    }
+    __syncthreads();  // tables
+
+    const int pw = wv & 1, tg = wv >> 1;      // conv tile: channels 128 pw .., tokens 16 tg ..
+    const int xw0 = wv * kFXElems, yw0 = wv * kFYElems;
+    const int cw0 = 32 * wv;                  // output channels of this wave
+    // A-fragment row -> token: lane ln supplies token 32 ((ln >> 2) & 1) + 4 (ln >> 3) + (ln & 3)
+    // (+ 16 for tile 1), so result register j of lane (kh, ln) is token 32 kh + j (+ 16)
+    const int atok = 32 * ((ln >> 2) & 1) + 4 * (ln >> 3) + (ln & 3);
+    const int rowb = D * 2;
+
+    for (int un = jw; un < units; un += wph) {
+        const int b = un / nseg, seg = un % nseg;
+        const int t0 = seg * kFSeg, nt = min(kFSeg, T - t0);
+        const size_t m0 = (size_t)b * T + t0;
+
+        // ---- 1. copies into this wave's LDS regions (no earlier read of them is pending) ----
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        {
+            const __amdgpu_buffer_rsrc_t rx = rsrc_at(static_cast<const uint16_t*>(a.x) + (size_t)b * T * D);
+            const int coff = (head * kBs + 128 * pw + 8 * (lane & 15)) * 2;
+            const int tok0 = t0 + 16 * tg - 3 + (lane >> 4);
+            if (t0 == 0 && tg == 0) {
+                // rows 0..2 of the first copy are tokens -3..-1: the conv0 window (a resource of
+                // length 0 reads zeros when there is none); built from a wave-uniform pointer
+                const uint64_t cp = reinterpret_cast<uint64_t>(a.conv0 ? a.conv0 : a.x);
+                const uint32_t c_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(cp >> 32));
+                const uint32_t c_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)cp);
+                const __amdgpu_buffer_rsrc_t rc = rsrc_len(
+                    reinterpret_cast<void*>(((uint64_t)c_hi << 32) | (uint64_t)c_lo), a.conv0 ? 0xffffffffu : 0u);
+                if ((lane >> 4) == 3) __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, x_lds + xw0, 16, coff, 0, 0, 0);
+                else __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, x_lds + xw0, 16, ((b * 3 + (lane >> 4)) * D) * 2 + coff, 0, 0, 0);
+            } else {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, x_lds + xw0, 16, min(tok0, T - 1) * rowb + coff, 0, 0, 0);
+            }
+#pragma unroll
+            for (int q = 1; q < 5; ++q)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, x_lds + xw0 + q * 512, 16,
+                                                         min(tok0 + 4 * q, T - 1) * rowb + coff, 0, 0, 0);
+            const size_t tmo = (size_t)b * T * D + (size_t)head * kBs + cw0;
+            const __amdgpu_buffer_rsrc_t ry = rsrc_at(static_cast<const uint16_t*>(a.y) + tmo);
+            const __amdgpu_buffer_rsrc_t rd = rsrc_at(static_cast<const uint16_t*>(a.dout) + tmo);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int off = min(t0 + 16 * q + (lane >> 2), T - 1) * rowb + 16 * (lane & 3);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, y_lds + yw0 + f_yrow(16 * q), 16, off, 0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, d_lds + yw0 + f_yrow(16 * q), 16, off, 0, 0, 0);
+            }
+        }
+        f_wait_vmem();     // this wave's copies have landed (and its stores of the last unit)
+        f_lds_barrier();   // every wave's reads of the last unit's u tile are complete
+
+        // ---- 2. conv: lane = channel pair 128 pw + 2 lane, tokens 16 tg .. 16 tg + 15 ----
+        {
+            const int c = 128 * pw + 2 * lane;
+            const float4 tl = ctap[c], th = ctap[c + 1];
+            const float bl = cbias[c], bh = cbias[c + 1];
+            const int ixr = f_opaque(xw0 / 2 + lane);
+            const int iuw = f_opaque(c / 2), iug = f_opaque(2 * c);
+            uint32_t xr[19];
+#pragma unroll
+            for (int r = 0; r < 19; ++r) xr[r] = x_lds32[ixr + r * 64];
+            const __amdgpu_buffer_rsrc_t ru = rsrc_len(w.U + ((size_t)head * M + m0) * kBs, (uint32_t)nt * kBs * 2);
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                float lo = __builtin_fmaf(tl.x, bf_lo(xr[k]), bl);
+                lo = __builtin_fmaf(tl.y, bf_lo(xr[k + 1]), lo);
+                lo = __builtin_fmaf(tl.z, bf_lo(xr[k + 2]), lo);
+                lo = __builtin_fmaf(tl.w, bf_lo(xr[k + 3]), lo);
+                float hi = __builtin_fmaf(th.x, bf_hi(xr[k]), bh);
+                hi = __builtin_fmaf(th.y, bf_hi(xr[k + 1]), hi);
+                hi = __builtin_fmaf(th.z, bf_hi(xr[k + 2]), hi);
+                hi = __builtin_fmaf(th.w, bf_hi(xr[k + 3]), hi);
+                const uint32_t pk = pack2bf(lo, hi);
+                const int tt = 16 * tg + k;   // wave-uniform
+                u_lds32[iuw + f_urow(tt) * (kFRow / 2)] = pk;
+                __builtin_amdgcn_raw_buffer_store_b32(pk, ru, iug, tt * kBs * 2, 0);
+            }
+        }
+        f_lds_barrier();   // u tile complete
+
+        // ---- 3. gate pre-activations ----
+        f32x16 accA[2], accX[2];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) { accA[0][e] = 0.0f; accX[0][e] = 0.0f; accA[1][e] = 0.0f; accX[1][e] = 0.0f; }
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            const int ia = f_opaque(f_urow(atok + 16 * mt) * kFRow + 8 * kh);
+#pragma unroll
+            for (int s = 0; s < kBs / 16; ++s) {
+                const bf16x8 A = *reinterpret_cast<const bf16x8*>(u_lds + ia + 16 * s);
+                accA[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, wA[s], accA[mt], 0, 0, 0);
+                accX[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, wX[s], accX[mt], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);  // one fragment in flight: the weights hold half the registers
+            }
+        }
+
+        // ---- 4. R, I out; chunk aggregates of chunk 2 seg + kh over its 32 tokens ----
+        {
+            const int c = cw0 + ln;
+            const float bA = gba[c], bX = gbx[c], lsg = glsg[c];
+            const size_t hb = ((size_t)head * M + m0) * kBs;
+            const __amdgpu_buffer_rsrc_t rr = rsrc_len(w.R + hb, (uint32_t)nt * kBs * 2);
+            const __amdgpu_buffer_rsrc_t ri = rsrc_len(w.I + hb, (uint32_t)nt * kBs * 2);
+            // token tt = 32 kh + 16 mt + j: stores at byte vst + (16 mt + j) * 512; u at row
+            // f_urow(tt) = 32 kh + 16 mt + j + kh (12 - 8 (j / 4)) (bits 2..3 of j flipped for kh = 1);
+            // y and dout at yb + (16 mt + j) * 32
+            const int vst = f_opaque((32 * kh * kBs + c) * 2);
+            int iub[4];
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) iub[g4] = f_opaque((32 * kh + kh * (12 - 8 * g4)) * kFRow + c);
+            const int yb = f_opaque(yw0 + f_yrow(32 * kh) + ln);
+            float A = 1.0f, Bh = 0.0f, Q = 0.0f;
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int tj = 16 * mt + j;
+                    const uint16_t r16 = f2bf(accA[mt][j] + bA), i16 = f2bf(accX[mt][j] + bX);
+                    __builtin_amdgcn_raw_buffer_store_b16(r16, rr, vst, tj * kBs * 2, 0);
+                    __builtin_amdgcn_raw_buffer_store_b16(i16, ri, vst, tj * kBs * 2, 0);
+                    const Gate g = gate_of(bf2f(r16), bf2f(i16), lsg);
+                    const float u = bf2f(u_lds[iub[j >> 2] + tj * kFRow]);
+                    A *= g.a;
+                    Bh = __builtin_fmaf(g.a, Bh, g.m * g.i * u);
+                    const float yv = bf2f(y_lds[yb + tj * 32]);
+                    const float dov = bf2f(d_lds[yb + tj * 32]);
+                    Q = __builtin_fmaf(A, dov * gelu_and_grad(yv).x, Q);
+                    __builtin_amdgcn_sched_barrier(0);  // bound the loads hoisted ahead
+                }
+            }
+            // [B * nch][D] rows of this unit's chunks; a unit of 32 tokens has no second chunk,
+            // and the resource's range drops its stores (unconditional stores: a branch here
+            // would let the compiler sink the whole gate computation below all the R/I stores)
+            const size_t row0 = ((size_t)b * nch + t0 / kChunk) * D;
+            const uint32_t nb = (uint32_t)(nt / kChunk) * (uint32_t)D * 4;
+            const int vo = f_opaque((kh * D + head * kBs + c) * 4);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(A), rsrc_len(w.aggA + row0, nb), vo, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(Bh), rsrc_len(w.aggB + row0, nb), vo, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(Q), rsrc_len(w.bQ + row0, nb), vo, 0, 0);
+        }
+    }
+    f_wait_vmem();
 }
 
 // ---- carries over the chunks: h entering each chunk (forward) and c entering it from the
@@ -616,27 +783,12 @@ hipError_t launch_prefill_backward(const BwdArgs& a, hipStream_t s) {
 #define RG_LAUNCH(kern, n)                                                              \
     hipLaunchKernelGGL(kern, dim3(blocks_for(n)), dim3(256), 0, s, a, w);               \
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_conv_fwd_kernel, dim3((unsigned)(M / kConvRun), (unsigned)((a.D / 8 + 255) / 256)),
-                       dim3(256), 0, s, a, w);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
     RG_LAUNCH(bwd_wtrans_kernel, (size_t)a.H * kBs * 2 * kBs);
-    {   // gate pre-activations, all heads in one launch
-        ProjGemmArgs g;
-        memset(&g, 0, sizeof g);
-        g.A = w.U;
-        g.W[0] = a.wa;
-        g.W[1] = a.wx;
-        g.b[0] = a.ba;
-        g.b[1] = a.bx;
-        g.C[0] = w.R;
-        g.C[1] = w.I;
-        g.Nw[0] = kBs; g.Nw[1] = kBs; g.nseg = 2; g.M = (int)M; g.K = kBs;
-        g.batch = a.H;
-        g.bsA = (long long)M * kBs; g.bsW = (long long)kBs * kBs; g.bsC = (long long)M * kBs;
-        g.bsb = kBs;
-        if ((e = launch_proj_gemm(g, s)) != hipSuccess) return e;
+    {   // U, the gate pre-activations R and I, and the chunk aggregates: one persistent launch
+        const int wph = std::max(1, device_cu_count() / a.H);
+        hipLaunchKernelGGL(bwd_front_kernel, dim3((unsigned)(wph * a.H)), dim3(kFThreads), 0, s, a, w, wph);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    RG_LAUNCH(bwd_chunk_agg_kernel, nlane);
     {
         const size_t ngl = (size_t)a.B * groups_of((int)nch) * a.D;
         RG_LAUNCH(bwd_carry_group_kernel, ngl);

@@ -46,6 +46,8 @@ def _compare(g, ref, label):
     (512, 2, 2, 128, True),      # two heads, with h0, conv0 and dh_last
     (256, 1, 4, 64, False),      # one chunk per sequence
     (2560, 10, 1, 256, True),    # the 2B widths
+    (256, 1, 8, 96, True),       # T = 96: the front pass's last unit of each sequence has 32 tokens
+    (256, 1, 8, 32, False),      # one 32-token unit per sequence
 ])
 def test_backward_matches_oracle(D, nh, B, T, state):
     from gated_linear_recurrence_amd import binding
