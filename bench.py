@@ -833,9 +833,10 @@ def _trace_dispatches(path):
 
 def _stack_decode_steps(disp, anchor_groups):
     """Per-kernel time per decode step of the 26-layer stack: the dispatches between the first
-    and the last-but-one step's first attention decode (anchor: attn_dec_kernel with
-    `anchor_groups` workgroups, eight per step) span whole steps."""
-    idx = [i for i, d in enumerate(disp) if d[2] == "attn_dec_kernel" and d[3] == anchor_groups]
+    and the last-but-one step's first attention decode (anchor: attn_dec_kernel, any tile
+    count, with `anchor_groups` workgroups, eight per step) span whole steps."""
+    idx = [i for i, d in enumerate(disp)
+           if d[2].startswith("attn_dec_kernel") and d[3] == anchor_groups]
     per_step = sum(1 for i in range(STACK_LAYERS) if i % 3 == 2)   # attention layers per step
     steps = len(idx) // per_step
     if steps < 2:
