@@ -512,17 +512,37 @@ __global__ void __launch_bounds__(128, 2) bwd_grad_kernel(BwdArgs a, BwdBufs w) 
     constexpr int kHalf = kBs / 2;   // channels per block: half a head
     __shared__ __attribute__((aligned(16))) uint16_t tR[kChunk * kHalf], tI[kChunk * kHalf],
         tU[kChunk * kHalf], tY[kChunk * kHalf], tD[kChunk * kHalf];
-    // blockIdx = ((b * nch + c) * H + h) * 2 + half
+    // Block -> (sequence b, chunk c, head h, half).  The token-contiguous rows this block writes
+    // are 64-byte halves of 128-byte lines whose other halves come from chunk c ^ 1 of the same
+    // (b, h, half).  Workgroups are dealt to the 8 XCDs round-robin, so the two blocks of such a
+    // pair are placed 8 indices apart (same XCD, same L2): unit u = ((b * nch / 2 + c / 2) * H +
+    // h) * 2 + half, block = (u / 8) * 16 + (c & 1) * 8 + u % 8.  This needs an even chunk count
+    // and a multiple of 8 units; otherwise blockIdx = ((b * nch + c) * H + h) * 2 + half.
     const int nch = a.T / kChunk;
-    const int half = (int)(blockIdx.x & 1u);
-    const unsigned bh = blockIdx.x >> 1;
-    const int h = (int)(bh % (unsigned)a.H);
-    const unsigned bc = bh / (unsigned)a.H;
-    const int c_ = (int)(bc % (unsigned)nch), b_ = (int)(bc / (unsigned)nch);
+    const unsigned bid = blockIdx.x;
+    const bool paired = (nch & 1) == 0 && ((unsigned)a.B * (unsigned)nch * (unsigned)a.H) % 8u == 0;
+    int half, h, c_, b_;
+    if (paired) {
+        const unsigned u = (bid >> 4) * 8u + (bid & 7u), par = (bid >> 3) & 1u;
+        half = (int)(u & 1u);
+        const unsigned uh = u >> 1;
+        h = (int)(uh % (unsigned)a.H);
+        const unsigned bp = uh / (unsigned)a.H, np = (unsigned)nch / 2u;
+        c_ = (int)(2u * (bp % np) + par);
+        b_ = (int)(bp / np);
+    } else {
+        half = (int)(bid & 1u);
+        const unsigned bh = bid >> 1;
+        h = (int)(bh % (unsigned)a.H);
+        const unsigned bc = bh / (unsigned)a.H;
+        c_ = (int)(bc % (unsigned)nch);
+        b_ = (int)(bc / (unsigned)nch);
+    }
     const size_t m0 = (size_t)b_ * a.T + (size_t)c_ * kChunk;
     const int t = threadIdx.x, k = half * kHalf + t, d = h * kBs + k;
     const int wv = t >> 6, lane = t & 63;
-    const size_t idx = (size_t)blockIdx.x * kHalf + t;   // ((b * nch + c) * D + d)
+    // ((b * nch + c) * D + d)
+    const size_t idx = ((((size_t)b_ * nch + c_) * a.H + h) * 2 + half) * kHalf + t;
     const size_t M = (size_t)a.B * a.T;
     const size_t hmo = ((size_t)h * M + m0) * kBs;   // head-major element of token m0
     const size_t tmo = m0 * a.D + (size_t)h * kBs;   // token-major element of token m0
