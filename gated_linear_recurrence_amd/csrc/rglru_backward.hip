@@ -9,8 +9,9 @@
 //   input grad: dU_h = [dRpre | dIpre]_h [W_a[h]^T | W_x[h]^T]^T       (K = 512)
 //   weights:    [dW_a; dW_x]_h = [dRpre | dIpre]_h^T U_h                (K = B*T, split K, fp32)
 // The first runs inside the front pass (conv, gates on MFMA with the weights held in registers,
-// chunk aggregates); the other two are plain GEMMs of the projection kernel, one launch each
-// with the heads as a batch.  The scans run per channel over chunks of 32 tokens: local
+// chunk aggregates); the input gradient is a plain GEMM of the projection kernel (one launch,
+// the heads as a batch); the weight gradients have a kernel of their own that reads dRI and U
+// in their head-major layout (K runs over tokens).  The scans run per channel over chunks of 32 tokens: local
 // aggregates of both directions (front pass), sequential carries over the chunks, then a pass
 // that uses the carries (forward for h; the backward recurrence
 //   dh_t = dout_t gelu(y_t) + a_{t+1} dh_{t+1}
@@ -31,11 +32,11 @@ constexpr int kBs = 256;    // block size (channels per gate head)
 constexpr int kChunk = 32;  // tokens per scan chunk (32: the gradient pass keeps a chunk in registers)
 
 struct BwdBufs {
-    uint16_t *U, *R, *I, *Wt, *dRI, *dRIt, *Ut, *dUg;
-    float *aggA, *aggB, *carry, *bQ, *cin, *duv, *plam, *pba, *pbx, *pconv, *dW, *part;
+    uint16_t *U, *R, *I, *Wt, *dRI, *dUg;
+    float *aggA, *aggB, *carry, *bQ, *cin, *duv, *plam, *pba, *pbx, *pconv, *wpart;
     float *sA, *sB, *sQ, *sh, *sc;   // chunk-group aggregates and carries (two-level carry scan)
     float* red;                       // reduction parts [kRedParts][8][D]
-    size_t part_bytes;
+    int wsplits;                      // token splits of the weight-gradient product
 };
 
 size_t r256(size_t n) { return (n + 255) & ~(size_t)255; }
@@ -45,6 +46,15 @@ constexpr int kGroupChunks = 16;
 __host__ __device__ inline int groups_of(int nch) { return (nch + kGroupChunks - 1) / kGroupChunks; }
 // the fixed-order sums of the per-chunk partials run in kRedParts consecutive ranges
 constexpr int kRedParts = 32;
+
+// The weight-gradient product splits the B*T tokens into this many ranges (about one
+// workgroup per CU over the 2 H output tiles; each range one 32-token step at least); its
+// fp32 partials are summed in range order.
+constexpr int kWgSplitMax = 16;
+inline int wgrad_splits(int B, int T, int H) {
+    const int ksteps = (int)((long long)B * T / 32);
+    return std::max(1, std::min(std::min(ksteps, kWgSplitMax), 256 / (2 * H)));
+}
 
 // Carve the workspace (the same order sizes it).
 BwdBufs carve(void* ws, int B, int T, int D, int H, size_t* total) {
@@ -62,8 +72,6 @@ BwdBufs carve(void* ws, int B, int T, int D, int H, size_t* total) {
     b.I = reinterpret_cast<uint16_t*>(take(MD * 2));
     b.Wt = reinterpret_cast<uint16_t*>(take((size_t)H * kBs * 2 * kBs * 2));
     b.dRI = reinterpret_cast<uint16_t*>(take(MD * 2 * 2));
-    b.dRIt = reinterpret_cast<uint16_t*>(take(MD * 2 * 2));
-    b.Ut = reinterpret_cast<uint16_t*>(take(MD * 2));
     b.dUg = reinterpret_cast<uint16_t*>(take(MD * 2));
     b.aggA = reinterpret_cast<float*>(take(nc * 4));
     b.aggB = reinterpret_cast<float*>(take(nc * 4));
@@ -82,9 +90,8 @@ BwdBufs carve(void* ws, int B, int T, int D, int H, size_t* total) {
     b.sh = reinterpret_cast<float*>(take(ng * 4));
     b.sc = reinterpret_cast<float*>(take(ng * 4));
     b.red = reinterpret_cast<float*>(take((size_t)kRedParts * 8 * D * 4));
-    b.dW = reinterpret_cast<float*>(take((size_t)H * 2 * kBs * kBs * 4));
-    b.part_bytes = proj_gemm_part_bytes_batched(H, 2 * kBs, kBs, (int)M);
-    b.part = reinterpret_cast<float*>(take(b.part_bytes));
+    b.wsplits = wgrad_splits(B, T, H);
+    b.wpart = reinterpret_cast<float*>(take((size_t)b.wsplits * H * 2 * kBs * kBs * 4));
     *total = off;
     return b;
 }
@@ -506,43 +513,22 @@ __global__ void __launch_bounds__(256) bwd_carry_fill_kernel(BwdArgs a, BwdBufs 
 // its channel out of LDS (with per-token global loads the pass waited on memory latency).  The
 // gradients of the gate pre-activations and of y replace R, I and y in LDS as the backward walk
 // consumes them, and leave as whole rows at the end: dRI head-major and dy token-major in
-// coalesced 16-byte chunks, and the token-contiguous rows of dR, dI and U for the weight-gradient
-// GEMM, 64 bytes per lane.
+// coalesced 16-byte chunks.
 __global__ void __launch_bounds__(128, 2) bwd_grad_kernel(BwdArgs a, BwdBufs w) {
     constexpr int kHalf = kBs / 2;   // channels per block: half a head
     __shared__ __attribute__((aligned(16))) uint16_t tR[kChunk * kHalf], tI[kChunk * kHalf],
         tU[kChunk * kHalf], tY[kChunk * kHalf], tD[kChunk * kHalf];
-    // Block -> (sequence b, chunk c, head h, half).  The token-contiguous rows this block writes
-    // are 64-byte halves of 128-byte lines whose other halves come from chunk c ^ 1 of the same
-    // (b, h, half).  Workgroups are dealt to the 8 XCDs round-robin, so the two blocks of such a
-    // pair are placed 8 indices apart (same XCD, same L2): unit u = ((b * nch / 2 + c / 2) * H +
-    // h) * 2 + half, block = (u / 8) * 16 + (c & 1) * 8 + u % 8.  This needs an even chunk count
-    // and a multiple of 8 units; otherwise blockIdx = ((b * nch + c) * H + h) * 2 + half.
+    // blockIdx = ((b * nch + c) * H + h) * 2 + half
     const int nch = a.T / kChunk;
-    const unsigned bid = blockIdx.x;
-    const bool paired = (nch & 1) == 0 && ((unsigned)a.B * (unsigned)nch * (unsigned)a.H) % 8u == 0;
-    int half, h, c_, b_;
-    if (paired) {
-        const unsigned u = (bid >> 4) * 8u + (bid & 7u), par = (bid >> 3) & 1u;
-        half = (int)(u & 1u);
-        const unsigned uh = u >> 1;
-        h = (int)(uh % (unsigned)a.H);
-        const unsigned bp = uh / (unsigned)a.H, np = (unsigned)nch / 2u;
-        c_ = (int)(2u * (bp % np) + par);
-        b_ = (int)(bp / np);
-    } else {
-        half = (int)(bid & 1u);
-        const unsigned bh = bid >> 1;
-        h = (int)(bh % (unsigned)a.H);
-        const unsigned bc = bh / (unsigned)a.H;
-        c_ = (int)(bc % (unsigned)nch);
-        b_ = (int)(bc / (unsigned)nch);
-    }
+    const int half = (int)(blockIdx.x & 1u);
+    const unsigned bh = blockIdx.x >> 1;
+    const int h = (int)(bh % (unsigned)a.H);
+    const unsigned bc = bh / (unsigned)a.H;
+    const int c_ = (int)(bc % (unsigned)nch), b_ = (int)(bc / (unsigned)nch);
     const size_t m0 = (size_t)b_ * a.T + (size_t)c_ * kChunk;
     const int t = threadIdx.x, k = half * kHalf + t, d = h * kBs + k;
     const int wv = t >> 6, lane = t & 63;
-    // ((b * nch + c) * D + d)
-    const size_t idx = ((((size_t)b_ * nch + c_) * a.H + h) * 2 + half) * kHalf + t;
+    const size_t idx = (size_t)blockIdx.x * kHalf + t;   // ((b * nch + c) * D + d)
     const size_t M = (size_t)a.B * a.T;
     const size_t hmo = ((size_t)h * M + m0) * kBs;   // head-major element of token m0
     const size_t tmo = m0 * a.D + (size_t)h * kBs;   // token-major element of token m0
@@ -624,22 +610,6 @@ __global__ void __launch_bounds__(128, 2) bwd_grad_kernel(BwdArgs a, BwdBufs w) 
             const int c = t + 128 * i, tt = c >> 4, q = c & 15;
             *reinterpret_cast<uint4*>(dyb + (size_t)tt * a.D + 8 * q) =
                 *reinterpret_cast<const uint4*>(tY + tt * kHalf + 8 * q);
-        }
-    }
-    {
-        // token-contiguous rows for the weight-gradient GEMM: 64 bytes per lane and array
-        uint4* const dr_t = reinterpret_cast<uint4*>(w.dRIt + ((size_t)h * 2 * kBs + k) * M + m0);
-        uint4* const di_t = reinterpret_cast<uint4*>(w.dRIt + ((size_t)h * 2 * kBs + kBs + k) * M + m0);
-        uint4* const u_t = reinterpret_cast<uint4*>(w.Ut + ((size_t)h * kBs + k) * M + m0);
-        auto pair = [&](const uint16_t* tl, int t0) {
-            return (uint32_t)tl[t0 * kHalf + t] | ((uint32_t)tl[(t0 + 1) * kHalf + t] << 16);
-        };
-#pragma unroll
-        for (int q = 0; q < kChunk / 8; ++q) {
-            const int t0 = 8 * q;
-            dr_t[q] = make_uint4(pair(tR, t0), pair(tR, t0 + 2), pair(tR, t0 + 4), pair(tR, t0 + 6));
-            di_t[q] = make_uint4(pair(tI, t0), pair(tI, t0 + 2), pair(tI, t0 + 4), pair(tI, t0 + 6));
-            u_t[q] = make_uint4(pair(tU, t0), pair(tU, t0 + 2), pair(tU, t0 + 4), pair(tU, t0 + 6));
         }
     }
 }
@@ -738,13 +708,115 @@ __global__ void __launch_bounds__(256) bwd_conv_kernel(BwdArgs a, BwdBufs w) {
     }
 }
 
-// ---- fixed-order sums of the partials; dW from the GEMM's fp32 output ----------------------
-__global__ void __launch_bounds__(256) bwd_wcopy_kernel(BwdArgs a, BwdBufs w) {
-    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= (size_t)a.H * kBs * kBs) return;   // [H][2 bs][bs] -> dwa, dwx
-    const size_t h = idx / ((size_t)kBs * kBs), r = idx % ((size_t)kBs * kBs);
-    a.dwa[idx] = w.dW[h * 2 * kBs * kBs + r];
-    a.dwx[idx] = w.dW[h * 2 * kBs * kBs + (size_t)kBs * kBs + r];
+// ---- gate weight gradients from the head-major dRI and U: [dW_a; dW_x]_h = [dR | dI]_h^T U_h ----
+// K runs over tokens, which are the rows (not the contiguous dimension) of both operands, so the
+// MFMA fragments (eight consecutive K per lane) are gathered from LDS with 2-byte reads.  One
+// workgroup (four waves of 128 x 128) per 256 x 256 output tile (head h, dR or dI rows) and
+// token range; 32-token steps through two LDS stages filled by buffer loads (1 KB = two 512-byte
+// rows per copy; 16 bytes of padding after every two rows put the two half-waves' reads, eight
+// rows apart, on different banks).  The fp32 tile of each range goes to wpart and the ranges are
+// summed in order by bwd_wgrad_sum_kernel (bitwise repeatable).
+constexpr int kWgRowB = 2 * kBs;             // bytes of one staged row (256 bf16)
+constexpr int kWgBlk = 2 * kWgRowB + 16;     // one copy: two rows and the padding
+constexpr int kWgTile = 16 * kWgBlk;         // 32 rows
+constexpr int kWgStage = 2 * kWgTile;        // dRI and U rows of one step
+
+__device__ __forceinline__ bf16x8 wg_frag(const unsigned char* tile, int r0, int col) {
+    typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+    u16x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int r = r0 + e;
+        v[e] = *reinterpret_cast<const unsigned short*>(tile + (r >> 1) * kWgBlk + (r & 1) * kWgRowB + 2 * col);
+    }
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+__global__ void __launch_bounds__(256, 1) bwd_wgrad_kernel(BwdArgs a, BwdBufs w) {
+    __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kWgStage];
+    const int H = a.H, S = w.wsplits;
+    const unsigned bid = blockIdx.x;     // (s * H + h) * 2 + ohalf
+    const int ohalf = (int)(bid & 1u), h = (int)((bid >> 1) % (unsigned)H), s = (int)((bid >> 1) / (unsigned)H);
+    const size_t M = (size_t)a.B * a.T;
+    const int KS = (int)(M / 32);
+    const int k0 = (int)((long long)KS * s / S), k1 = (int)((long long)KS * (s + 1) / S);
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int wm = wv >> 1, wn = wv & 1;
+    const uint16_t* const abase = w.dRI + (size_t)h * M * 2 * kBs + ohalf * kBs;   // row m at + m * 512
+    const uint16_t* const bbase = w.U + (size_t)h * M * kBs;                       // row m at + m * 256
+    // copies of step ks into stage st: this wave's blocks 4 wv .. 4 wv + 3 of each tile
+    auto issue = [&](int ks, int st) {
+        const size_t m0 = (size_t)ks * 32;
+        const __amdgpu_buffer_rsrc_t ra = rsrc_at(abase + m0 * 2 * kBs), rb = rsrc_at(bbase + m0 * kBs);
+        unsigned char* const sa = lds + st * kWgStage;
+        const int row = lane >> 5, colb = (lane & 31) * 16;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int blk = 4 * wv + q;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, sa + blk * kWgBlk, 16, (2 * blk + row) * (4 * kBs) + colb, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, sa + kWgTile + blk * kWgBlk, 16, (2 * blk + row) * (2 * kBs) + colb, 0, 0, 0);
+        }
+    };
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+    if (k0 < k1) issue(k0, 0);
+    for (int ks = k0; ks < k1; ++ks) {
+        const int st = (ks - k0) & 1;
+        if (ks + 1 < k1) {
+            issue(ks + 1, st ^ 1);   // that stage's reads ended at the last step's final barrier
+            __builtin_amdgcn_s_waitcnt(0x0f78);   // vmcnt(8): this step's eight copies have landed
+        } else {
+            __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+        }
+        f_lds_barrier();   // every wave's copies of this step (each waited for its own above)
+        const unsigned char* const sa = lds + st * kWgStage;
+        const unsigned char* const sb = sa + kWgTile;
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+            const int r0 = 16 * sub + 8 * (lane >> 5);   // K slice of this lane: tokens r0 .. r0 + 7
+            bf16x8 af[4], bfr[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) af[i] = wg_frag(sa, r0, 128 * wm + 32 * i + (lane & 31));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bfr[j] = wg_frag(sb, r0, 128 * wn + 32 * j + (lane & 31));
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
+        f_lds_barrier();   // this stage is no longer read (the next step refills it)
+    }
+    // tile element (o, c): block (i, j) register e holds o = 128 wm + 32 i + 8 (e / 4) + 4 (lane / 32)
+    // + e % 4 and c = 128 wn + 32 j + lane % 32
+    float* const out = w.wpart + (((size_t)s * H + h) * 2 * kBs + (size_t)ohalf * kBs) * kBs;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int o = 128 * wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                const int c = 128 * wn + 32 * j + (lane & 31);
+                out[(size_t)o * kBs + c] = acc[i][j][e];
+            }
+}
+
+// dW_a, dW_x = the token ranges' partial tiles added in range order
+__global__ void __launch_bounds__(256) bwd_wgrad_sum_kernel(BwdArgs a, BwdBufs w) {
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;   // (h, o in 0..511, c)
+    const size_t per = (size_t)2 * kBs * kBs;
+    if (idx >= (size_t)a.H * per) return;
+    const size_t h = idx / per, r = idx % per;
+    float v = 0.0f;
+    for (int s = 0; s < w.wsplits; ++s) v += w.wpart[((size_t)s * a.H + h) * per + r];
+    if (r < (size_t)kBs * kBs) a.dwa[h * kBs * kBs + r] = v;
+    else a.dwx[h * kBs * kBs + (r - (size_t)kBs * kBs)] = v;
 }
 
 // Fixed-order sums of the per-chunk partials, in two passes with consecutive lanes on
@@ -828,20 +900,11 @@ hipError_t launch_prefill_backward(const BwdArgs& a, hipStream_t s) {
         g.bsA = (long long)M * 2 * kBs; g.bsW = (long long)kBs * 2 * kBs; g.bsC = (long long)M * kBs;
         if ((e = launch_proj_gemm(g, s)) != hipSuccess) return e;
     }
-    {   // gate weight gradients (K = B * T, fp32), all heads in one launch
-        ProjGemmArgs g;
-        memset(&g, 0, sizeof g);
-        g.A = w.dRIt;
-        g.W[0] = w.Ut;
-        g.C[0] = w.dW;
-        g.Nw[0] = kBs; g.nseg = 1; g.M = 2 * kBs; g.K = (int)M;
-        g.part = w.part; g.part_bytes = w.part_bytes; g.c_f32 = 1;
-        g.batch = a.H;
-        g.bsA = (long long)2 * kBs * M; g.bsW = (long long)kBs * M; g.bsC = (long long)2 * kBs * kBs;
-        if ((e = launch_proj_gemm(g, s)) != hipSuccess) return e;
-    }
+    // gate weight gradients (K = B * T), all heads in one launch, then the ranges' sum
+    hipLaunchKernelGGL(bwd_wgrad_kernel, dim3((unsigned)(w.wsplits * a.H * 2)), dim3(256), 0, s, a, w);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    RG_LAUNCH(bwd_wgrad_sum_kernel, (size_t)a.H * 2 * kBs * kBs);
     RG_LAUNCH(bwd_conv_kernel, nlane / 8);
-    RG_LAUNCH(bwd_wcopy_kernel, (size_t)a.H * kBs * kBs);
     hipLaunchKernelGGL(bwd_reduce_part_kernel, dim3((unsigned)((a.D + 255) / 256), kRedParts),
                        dim3(256), 0, s, a, w);
     if ((e = hipGetLastError()) != hipSuccess) return e;
