@@ -303,52 +303,70 @@ __global__ void __launch_bounds__(kFThreads) bwd_front_kernel(BwdArgs a, BwdBufs
     const int atok = 32 * ((ln >> 2) & 1) + 4 * (ln >> 3) + (ln & 3);
     const int rowb = D * 2;
 
+    // copies of unit un into this wave's LDS regions: x rows (with the 3-token halo: the
+    // previous tokens, the conv0 window or zeros), and y and dout rows of its 32 channels
+    auto copy_x = [&](int un) {
+        const int b = un / nseg, t0 = (un % nseg) * kFSeg;
+        const __amdgpu_buffer_rsrc_t rx = rsrc_at(static_cast<const uint16_t*>(a.x) + (size_t)b * T * D);
+        const int coff = (head * kBs + 128 * pw + 8 * (lane & 15)) * 2;
+        const int tok0 = t0 + 16 * tg - 3 + (lane >> 4);
+        if (t0 == 0 && tg == 0) {
+            // rows 0..2 of the first copy are tokens -3..-1: the conv0 window (a resource of
+            // length 0 reads zeros when there is none); built from a wave-uniform pointer
+            const uint64_t cp = reinterpret_cast<uint64_t>(a.conv0 ? a.conv0 : a.x);
+            const uint32_t c_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(cp >> 32));
+            const uint32_t c_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)cp);
+            const __amdgpu_buffer_rsrc_t rc = rsrc_len(
+                reinterpret_cast<void*>(((uint64_t)c_hi << 32) | (uint64_t)c_lo), a.conv0 ? 0xffffffffu : 0u);
+            if ((lane >> 4) == 3) __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, x_lds + xw0, 16, coff, 0, 0, 0);
+            else __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, x_lds + xw0, 16, ((b * 3 + (lane >> 4)) * D) * 2 + coff, 0, 0, 0);
+        } else {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, x_lds + xw0, 16, min(tok0, T - 1) * rowb + coff, 0, 0, 0);
+        }
+#pragma unroll
+        for (int q = 1; q < 5; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, x_lds + xw0 + q * 512, 16,
+                                                     min(tok0 + 4 * q, T - 1) * rowb + coff, 0, 0, 0);
+    };
+    // eight copies (wait counts below rely on that number)
+    auto copy_yd = [&](int un) {
+        const int b = un / nseg, t0 = (un % nseg) * kFSeg;
+        const size_t tmo = (size_t)b * T * D + (size_t)head * kBs + cw0;
+        const __amdgpu_buffer_rsrc_t ry = rsrc_at(static_cast<const uint16_t*>(a.y) + tmo);
+        const __amdgpu_buffer_rsrc_t rd = rsrc_at(static_cast<const uint16_t*>(a.dout) + tmo);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int off = min(t0 + 16 * q + (lane >> 2), T - 1) * rowb + 16 * (lane & 3);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, y_lds + yw0 + f_yrow(16 * q), 16, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, d_lds + yw0 + f_yrow(16 * q), 16, off, 0, 0, 0);
+        }
+    };
+    // this lane's conv taps and biases (channels 128 pw + 2 lane, + 1), the same for every unit
+    const float4 tl = ctap[128 * pw + 2 * lane], th = ctap[128 * pw + 2 * lane + 1];
+    const float bl = cbias[128 * pw + 2 * lane], bh = cbias[128 * pw + 2 * lane + 1];
+    if (jw < units) {
+        copy_x(jw);
+        copy_yd(jw);
+    }
+
+    // A unit's copies go out a unit ahead: x right after the last unit's conv has read the x
+    // rows, y and dout right after the last unit's aggregate walk has read those.  The wait at
+    // the top of a unit needs only x: the eight y/dout copies are the youngest memory operations
+    // in flight and loads complete in order, so vmcnt(8) leaves exactly them outstanding (and
+    // waits for the last unit's stores).  y and dout are waited for before the walk, a conv and
+    // an MFMA phase after they were issued.
     for (int un = jw; un < units; un += wph) {
         const int b = un / nseg, seg = un % nseg;
         const int t0 = seg * kFSeg, nt = min(kFSeg, T - t0);
         const size_t m0 = (size_t)b * T + t0;
+        const bool more = un + wph < units;
 
-        // ---- 1. copies into this wave's LDS regions (no earlier read of them is pending) ----
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        {
-            const __amdgpu_buffer_rsrc_t rx = rsrc_at(static_cast<const uint16_t*>(a.x) + (size_t)b * T * D);
-            const int coff = (head * kBs + 128 * pw + 8 * (lane & 15)) * 2;
-            const int tok0 = t0 + 16 * tg - 3 + (lane >> 4);
-            if (t0 == 0 && tg == 0) {
-                // rows 0..2 of the first copy are tokens -3..-1: the conv0 window (a resource of
-                // length 0 reads zeros when there is none); built from a wave-uniform pointer
-                const uint64_t cp = reinterpret_cast<uint64_t>(a.conv0 ? a.conv0 : a.x);
-                const uint32_t c_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(cp >> 32));
-                const uint32_t c_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)cp);
-                const __amdgpu_buffer_rsrc_t rc = rsrc_len(
-                    reinterpret_cast<void*>(((uint64_t)c_hi << 32) | (uint64_t)c_lo), a.conv0 ? 0xffffffffu : 0u);
-                if ((lane >> 4) == 3) __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, x_lds + xw0, 16, coff, 0, 0, 0);
-                else __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, x_lds + xw0, 16, ((b * 3 + (lane >> 4)) * D) * 2 + coff, 0, 0, 0);
-            } else {
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, x_lds + xw0, 16, min(tok0, T - 1) * rowb + coff, 0, 0, 0);
-            }
-#pragma unroll
-            for (int q = 1; q < 5; ++q)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, x_lds + xw0 + q * 512, 16,
-                                                         min(tok0 + 4 * q, T - 1) * rowb + coff, 0, 0, 0);
-            const size_t tmo = (size_t)b * T * D + (size_t)head * kBs + cw0;
-            const __amdgpu_buffer_rsrc_t ry = rsrc_at(static_cast<const uint16_t*>(a.y) + tmo);
-            const __amdgpu_buffer_rsrc_t rd = rsrc_at(static_cast<const uint16_t*>(a.dout) + tmo);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int off = min(t0 + 16 * q + (lane >> 2), T - 1) * rowb + 16 * (lane & 3);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, y_lds + yw0 + f_yrow(16 * q), 16, off, 0, 0, 0);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, d_lds + yw0 + f_yrow(16 * q), 16, off, 0, 0, 0);
-            }
-        }
-        f_wait_vmem();     // this wave's copies have landed (and its stores of the last unit)
-        f_lds_barrier();   // every wave's reads of the last unit's u tile are complete
+        __builtin_amdgcn_s_waitcnt(0x0f78);   // vmcnt(8): this wave's x rows of this unit have landed
+        f_lds_barrier();   // every wave's x rows; every wave's reads of the last unit's u tile done
 
         // ---- 2. conv: lane = channel pair 128 pw + 2 lane, tokens 16 tg .. 16 tg + 15 ----
         {
             const int c = 128 * pw + 2 * lane;
-            const float4 tl = ctap[c], th = ctap[c + 1];
-            const float bl = cbias[c], bh = cbias[c + 1];
             const int ixr = f_opaque(xw0 / 2 + lane);
             const int iuw = f_opaque(c / 2), iug = f_opaque(2 * c);
             uint32_t xr[19];
@@ -371,7 +389,8 @@ __global__ void __launch_bounds__(kFThreads) bwd_front_kernel(BwdArgs a, BwdBufs
                 __builtin_amdgcn_raw_buffer_store_b32(pk, ru, iug, tt * kBs * 2, 0);
             }
         }
-        f_lds_barrier();   // u tile complete
+        f_lds_barrier();   // u tile complete; this wave's x rows are read
+        if (more) copy_x(un + wph);
 
         // ---- 3. gate pre-activations ----
         f32x16 accA[2], accX[2];
@@ -390,6 +409,11 @@ __global__ void __launch_bounds__(kFThreads) bwd_front_kernel(BwdArgs a, BwdBufs
         }
 
         // ---- 4. R, I out; chunk aggregates of chunk 2 seg + kh over its 32 tokens ----
+        // this wave's y and dout rows of this unit: younger than them are this unit's U stores
+        // and, when there is a next unit, its five or six x copies, which cannot land before
+        // them; vmcnt(5) therefore implies they have landed (and leaves the x copies in flight)
+        if (more) __builtin_amdgcn_s_waitcnt(0x0f75);   // vmcnt(5)
+        else f_wait_vmem();
         {
             const int c = cw0 + ln;
             const float bA = gba[c], bX = gbx[c], lsg = glsg[c];
@@ -433,6 +457,8 @@ __global__ void __launch_bounds__(kFThreads) bwd_front_kernel(BwdArgs a, BwdBufs
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(Bh), rsrc_len(w.aggB + row0, nb), vo, 0, 0);
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(Q), rsrc_len(w.bQ + row0, nb), vo, 0, 0);
         }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's y and dout reads are done
+        if (more) copy_yd(un + wph);
     }
     f_wait_vmem();
 }
