@@ -226,6 +226,8 @@ constexpr int kFYElems = kFSeg * 32 + 32;  // y (or dout) rows of a wave's 32 ch
 
 // u row of token t (0..63): tokens 32..63 have row bits 2..3 flipped, so the A-fragment reads of
 // tokens t and t + 32 in one pass fall in different bank groups
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ int f_urow(int t) { return t ^ (((t >> 5) & 1) * 12); }
 // y / dout row r of a wave's region: rows 32..63 start 64 bytes later (the two half-waves'
 // 2-byte reads of rows r and r + 32 then fall in different banks)
@@ -368,11 +370,10 @@ __global__ void __launch_bounds__(kFThreads) bwd_front_kernel(BwdArgs a, BwdBufs
         {
             const int c = 128 * pw + 2 * lane;
             const int ixr = f_opaque(xw0 / 2 + lane);
-            const int iuw = f_opaque(c / 2), iug = f_opaque(2 * c);
+            const int iuw = f_opaque(c / 2);
             uint32_t xr[19];
 #pragma unroll
             for (int r = 0; r < 19; ++r) xr[r] = x_lds32[ixr + r * 64];
-            const __amdgpu_buffer_rsrc_t ru = rsrc_len(w.U + ((size_t)head * M + m0) * kBs, (uint32_t)nt * kBs * 2);
 #pragma unroll
             for (int k = 0; k < 16; ++k) {
                 float lo = __builtin_fmaf(tl.x, bf_lo(xr[k]), bl);
@@ -386,10 +387,20 @@ __global__ void __launch_bounds__(kFThreads) bwd_front_kernel(BwdArgs a, BwdBufs
                 const uint32_t pk = pack2bf(lo, hi);
                 const int tt = 16 * tg + k;   // wave-uniform
                 u_lds32[iuw + f_urow(tt) * (kFRow / 2)] = pk;
-                __builtin_amdgcn_raw_buffer_store_b32(pk, ru, iug, tt * kBs * 2, 0);
             }
         }
         f_lds_barrier();   // u tile complete; this wave's x rows are read
+        {
+            // U out of the tile: 64 rows of 512 bytes as 16-byte stores, four per thread
+            // (rows past the unit's tokens fall outside the resource and are dropped)
+            const __amdgpu_buffer_rsrc_t ru = rsrc_len(w.U + ((size_t)head * M + m0) * kBs, (uint32_t)nt * kBs * 2);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int id = q * kFThreads + tid, row = id >> 5, ch = id & 31;
+                const uint4 v = *reinterpret_cast<const uint4*>(u_lds + f_urow(row) * kFRow + 8 * ch);
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), ru, (row * kBs + 8 * ch) * 2, 0, 0);
+            }
+        }
         if (more) copy_x(un + wph);
 
         // ---- 3. gate pre-activations ----
@@ -420,10 +431,9 @@ __global__ void __launch_bounds__(kFThreads) bwd_front_kernel(BwdArgs a, BwdBufs
             const size_t hb = ((size_t)head * M + m0) * kBs;
             const __amdgpu_buffer_rsrc_t rr = rsrc_len(w.R + hb, (uint32_t)nt * kBs * 2);
             const __amdgpu_buffer_rsrc_t ri = rsrc_len(w.I + hb, (uint32_t)nt * kBs * 2);
-            // token tt = 32 kh + 16 mt + j: stores at byte vst + (16 mt + j) * 512; u at row
+            // token tt = 32 kh + 16 mt + j: u at row
             // f_urow(tt) = 32 kh + 16 mt + j + kh (12 - 8 (j / 4)) (bits 2..3 of j flipped for kh = 1);
             // y and dout at yb + (16 mt + j) * 32
-            const int vst = f_opaque((32 * kh * kBs + c) * 2);
             int iub[4];
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) iub[g4] = f_opaque((32 * kh + kh * (12 - 8 * g4)) * kFRow + c);
@@ -435,8 +445,6 @@ __global__ void __launch_bounds__(kFThreads) bwd_front_kernel(BwdArgs a, BwdBufs
                 for (int j = 0; j < 16; ++j) {
                     const int tj = 16 * mt + j;
                     const uint16_t r16 = f2bf(accA[mt][j] + bA), i16 = f2bf(accX[mt][j] + bX);
-                    __builtin_amdgcn_raw_buffer_store_b16(r16, rr, vst, tj * kBs * 2, 0);
-                    __builtin_amdgcn_raw_buffer_store_b16(i16, ri, vst, tj * kBs * 2, 0);
                     const Gate g = gate_of(bf2f(r16), bf2f(i16), lsg);
                     const float u = bf2f(u_lds[iub[j >> 2] + tj * kFRow]);
                     A *= g.a;
@@ -444,6 +452,9 @@ __global__ void __launch_bounds__(kFThreads) bwd_front_kernel(BwdArgs a, BwdBufs
                     const float yv = bf2f(y_lds[yb + tj * 32]);
                     const float dov = bf2f(d_lds[yb + tj * 32]);
                     Q = __builtin_fmaf(A, dov * gelu_and_grad(yv).x, Q);
+                    // R and I of this token take the places of its y and dout, just read
+                    y_lds[yb + tj * 32] = r16;
+                    d_lds[yb + tj * 32] = i16;
                     __builtin_amdgcn_sched_barrier(0);  // bound the loads hoisted ahead
                 }
             }
@@ -456,8 +467,20 @@ __global__ void __launch_bounds__(kFThreads) bwd_front_kernel(BwdArgs a, BwdBufs
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(A), rsrc_len(w.aggA + row0, nb), vo, 0, 0);
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(Bh), rsrc_len(w.aggB + row0, nb), vo, 0, 0);
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(Q), rsrc_len(w.bQ + row0, nb), vo, 0, 0);
+            // R and I out of the y and dout regions: 64 rows of this wave's 32 channels, four
+            // lanes per 64-byte row, 16-byte stores (rows past the unit's tokens are dropped)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int row = 16 * q + (lane >> 2), ch = lane & 3;
+                const int li = yw0 + f_yrow(16 * q) + (lane >> 2) * 32 + 8 * ch;
+                const uint4 vr = *reinterpret_cast<const uint4*>(y_lds + li);
+                const uint4 vi = *reinterpret_cast<const uint4*>(d_lds + li);
+                const int off = (row * kBs + cw0 + 8 * ch) * 2;
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, vr), rr, off, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, vi), ri, off, 0, 0);
+            }
         }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's y and dout reads are done
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's reads of its y and dout regions are done
         if (more) copy_yd(un + wph);
     }
     f_wait_vmem();
