@@ -407,14 +407,13 @@ __global__ void __launch_bounds__(kFThreads) bwd_front_kernel(BwdArgs a, BwdBufs
         f32x16 accA[2], accX[2];
 #pragma unroll
         for (int e = 0; e < 16; ++e) { accA[0][e] = 0.0f; accX[0][e] = 0.0f; accA[1][e] = 0.0f; accX[1][e] = 0.0f; }
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            const int ia = f_opaque(f_urow(atok + 16 * mt) * kFRow + 8 * kh);
+        {   // tile 0 here; tile 1's MFMAs run beside tile 0's walk below
+            const int ia = f_opaque(f_urow(atok) * kFRow + 8 * kh);
 #pragma unroll
             for (int s = 0; s < kBs / 16; ++s) {
                 const bf16x8 A = *reinterpret_cast<const bf16x8*>(u_lds + ia + 16 * s);
-                accA[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, wA[s], accA[mt], 0, 0, 0);
-                accX[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, wX[s], accX[mt], 0, 0, 0);
+                accA[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, wA[s], accA[0], 0, 0, 0);
+                accX[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, wX[s], accX[0], 0, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);  // one fragment in flight: the weights hold half the registers
             }
         }
@@ -438,11 +437,17 @@ __global__ void __launch_bounds__(kFThreads) bwd_front_kernel(BwdArgs a, BwdBufs
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) iub[g4] = f_opaque((32 * kh + kh * (12 - 8 * g4)) * kFRow + c);
             const int yb = f_opaque(yw0 + f_yrow(32 * kh) + ln);
+            const int ia1 = f_opaque(f_urow(atok + 16) * kFRow + 8 * kh);
             float A = 1.0f, Bh = 0.0f, Q = 0.0f;
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
+                    if (mt == 0) {   // K step j of tile 1
+                        const bf16x8 Af = *reinterpret_cast<const bf16x8*>(u_lds + ia1 + 16 * j);
+                        accA[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Af, wA[j], accA[1], 0, 0, 0);
+                        accX[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Af, wX[j], accX[1], 0, 0, 0);
+                    }
                     const int tj = 16 * mt + j;
                     const uint16_t r16 = f2bf(accA[mt][j] + bA), i16 = f2bf(accX[mt][j] + bX);
                     const Gate g = gate_of(bf2f(r16), bf2f(i16), lsg);
