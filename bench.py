@@ -1009,6 +1009,57 @@ def census_summary(args):
     print(json.dumps(out))
 
 
+BACKWARD_CENSUS_TXT = os.path.join(ROOT, "profiles", "prefill_backward-2b-batched-census.txt")
+BACKWARD_CENSUS_KERNELS = ("bwd_grad_kernel", "bwd_front_kernel", "bwd_conv_kernel", "bwd_wgrad_kernel")
+
+
+def backward_census(args):
+    """Per-launch SQ counters of the backward's largest kernels (from rocprofv3 --pmc CSVs of the
+    passes in CENSUS_PASSES over `bench.py --legs backward`): per-element instruction counts, unit
+    utilisations and the wave-state split of each; written to profiles/ with the commands."""
+    w = synth.WORKLOADS[synth.BATCHED_2B]
+    elems = w.B * w.T * w.D
+    rows = []
+    for kern in BACKWARD_CENSUS_KERNELS:
+        vals = {}
+        for path in args.census:
+            names = {r["Counter_Name"] for r in _rows(path) if kern in r["Kernel_Name"]}
+            for n in names:
+                vals[n] = _mean_counter(path, kern, n)[0]
+        per_elem = lambda n: vals[n] * 64.0 / elems if n in vals else None
+        ratio = lambda a, b: vals[a] / vals[b] if a in vals and b in vals and vals[b] else None
+        rows.append((kern, [
+            ("VALUBusy %", vals.get("VALUBusy")), ("MfmaUtil %", vals.get("MfmaUtil")),
+            ("VALU instructions per element", per_elem("SQ_INSTS_VALU")),
+            ("  of them transcendental f32", per_elem("SQ_INSTS_VALU_TRANS_F32")),
+            ("LDS instructions per element", per_elem("SQ_INSTS_LDS")),
+            ("VMEM instructions per element", per_elem("SQ_INSTS_VMEM")),
+            ("SALU instructions per element", per_elem("SQ_INSTS_SALU")),
+            ("waves per launch", vals.get("SQ_WAVES")),
+            ("wave state: issuing", ratio("SQ_ACTIVE_INST_ANY", "SQ_WAVE_CYCLES")),
+            ("wave state: waiting at s_waitcnt", ratio("SQ_WAIT_ANY", "SQ_WAVE_CYCLES")),
+            ("wave state: ready, not issued", ratio("SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES")),
+            ("wave state: VALU active", ratio("SQ_ACTIVE_INST_VALU", "SQ_WAVE_CYCLES")),
+            ("LDS bank-conflict cycles per LDS instruction", ratio("SQ_LDS_BANK_CONFLICT", "SQ_INSTS_LDS")),
+        ]))
+    with open(BACKWARD_CENSUS_TXT, "w") as f:
+        f.write("rocprofv3 --pmc counter census, the path's backward kernels on %s (bf16)\n\n" % w.name)
+        f.write("commands (from the repository root):\n")
+        for c in args.commands:
+            f.write("  %s\n" % c)
+        f.write("\nper launch, mean over the profiled dispatches; per element = wave instructions x 64 "
+                "lanes / (B T D) = %d elements;\nwave-state ratios over SQ_WAVE_CYCLES\n\n" % elems)
+        f.write("%-46s" % "" + "".join("%18s" % k for k, _ in rows) + "\n")
+        for i in range(len(rows[0][1])):
+            label = rows[0][1][i][0]
+            f.write("%-46s" % label)
+            for _, r in rows:
+                v = r[i][1]
+                f.write("%18s" % ("n/a" if v is None else "%.3g" % v))
+            f.write("\n")
+    print(open(BACKWARD_CENSUS_TXT).read())
+
+
 def measured_census():
     """MFMA and VALU utilisation of the prefill kernel from the committed census, or None when
     it was taken on other kernel sources."""
@@ -1051,6 +1102,8 @@ def main():
     ap.add_argument("--census-summary", action="store_true",
                     help="write the SQ counter census under profiles/ from rocprofv3 CSVs (no GPU)")
     ap.add_argument("--census", nargs="*", default=[])
+    ap.add_argument("--backward-census", action="store_true",
+                    help="write the backward kernels' counter census from --census CSVs (no GPU)")
     ap.add_argument("--backward-summary", action="store_true",
                     help="write the backward's kernel-trace and traffic summary under profiles/ "
                          "from rocprofv3 CSVs (no GPU; --kernel-stats, --fetch, --write, "
@@ -1065,6 +1118,9 @@ def main():
         return
     if args.backward_summary:
         backward_summary(args)
+        return
+    if args.backward_census:
+        backward_census(args)
         return
     if args.counter_summary:
         counter_summary(args)
