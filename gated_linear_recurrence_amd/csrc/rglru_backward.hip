@@ -609,12 +609,17 @@ __global__ void __launch_bounds__(128, 2) bwd_grad_kernel(BwdArgs a, BwdBufs w) 
     float cc = w.cin[idx];
     __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's copies have landed
     __syncthreads();                      // and the other wave's
-    float hp[kChunk];
+    // the forward re-run keeps h_{t-1}, a and sqrt(1 - a^2) of each token for the walk (the
+    // registers are free: LDS allows two waves per SIMD); the walk re-forms only r and i, and
+    // h_t is the re-run's next h_{t-1}
+    float hp[kChunk], ca[kChunk], cm[kChunk];
 #pragma unroll
     for (int tt = 0; tt < kChunk; ++tt) {
         hp[tt] = hv;
         const int e = tt * kHalf + t;
         const Gate g = gate_of(bf2f(tR[e]), bf2f(tI[e]), lsg);
+        ca[tt] = g.a;
+        cm[tt] = g.m;
         hv = __builtin_fmaf(g.a, hv, g.m * g.i * bf2f(tU[e]));
     }
     const auto rDuv = rsrc_at(w.duv + hmo);
@@ -623,8 +628,12 @@ __global__ void __launch_bounds__(128, 2) bwd_grad_kernel(BwdArgs a, BwdBufs w) 
     for (int tt = kChunk - 1; tt >= 0; --tt) {
         const int e = tt * kHalf + t;
         const float u = bf2f(tU[e]);
-        const Gate g = gate_of(bf2f(tR[e]), bf2f(tI[e]), lsg);
-        const float ht = __builtin_fmaf(g.a, hp[tt], g.m * g.i * u);
+        Gate g;
+        g.r = sigm(bf2f(tR[e]));
+        g.i = sigm(bf2f(tI[e]));
+        g.a = ca[tt];
+        g.m = cm[tt];
+        const float ht = tt + 1 < kChunk ? hp[tt + 1] : hv;
         const float yv = bf2f(tY[e]), dov = bf2f(tD[e]);
         const float2 gg = gelu_and_grad(yv);
         const float dh = __builtin_fmaf(dov, gg.x, cc);
