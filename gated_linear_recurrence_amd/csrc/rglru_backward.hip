@@ -9,9 +9,9 @@
 //   input grad: dU_h = [dRpre | dIpre]_h [W_a[h]^T | W_x[h]^T]^T       (K = 512)
 //   weights:    [dW_a; dW_x]_h = [dRpre | dIpre]_h^T U_h                (K = B*T, split K, fp32)
 // The first runs inside the front pass (conv, gates on MFMA with the weights held in registers,
-// chunk aggregates); the input gradient is a plain GEMM of the projection kernel (one launch,
-// the heads as a batch); the weight gradients have a kernel of their own that reads dRI and U
-// in their head-major layout (K runs over tokens).  The scans run per channel over chunks of 32 tokens: local
+// chunk aggregates); the input gradient is a persistent kernel of the same kind (the transposed
+// weights held in registers); the weight gradients have a kernel of their own that reads dRI and
+// U in their head-major layout (K runs over tokens).  The scans run per channel over chunks of 32 tokens: local
 // aggregates of both directions (front pass), sequential carries over the chunks, then a pass
 // that uses the carries (forward for h; the backward recurrence
 //   dh_t = dout_t gelu(y_t) + a_{t+1} dh_{t+1}
@@ -771,6 +771,109 @@ __global__ void __launch_bounds__(256) bwd_conv_kernel(BwdArgs a, BwdBufs w) {
     }
 }
 
+// ---- gradient of u through both gates: dU_h = [dR | dI]_h [W_a[h]^T | W_x[h]^T]^T, K = 512 ----
+// One workgroup of eight waves per CU pinned to a head: wave w keeps the B fragments of
+// [W_a^T | W_x^T] for u channels 32w .. 32w + 31 (all 512 K) in VGPRs, and the workgroup walks
+// 64-token units of dRI rows, double-buffered in LDS (one 1 KB row per copy, 16 bytes of padding
+// per row so that an A fragment's 32 rows fall on different banks).  K runs in natural order in
+// steps of 16 and the result is rounded as the projection GEMM's epilogue rounds it, so dU is
+// the same as that GEMM's.  The bf16 tile is staged in the unit's stage and leaves as 16-byte
+// stores one unit later (held in registers), so the wait for the next copies never includes
+// stores issued just before it.
+constexpr int kDgRow = 4 * kBs + 16;            // bytes of one staged dRI row (512 bf16 + padding)
+constexpr int kDgStage = kFSeg * kDgRow;
+__device__ __forceinline__ int dg_orow(int r) { return r * 2 * kBs + ((r >> 5) << 6); }  // output row, bytes
+
+__global__ void __launch_bounds__(kFThreads) bwd_dgate_kernel(BwdArgs a, BwdBufs w, int wph) {
+    __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kDgStage];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const unsigned G = gridDim.x, bid = blockIdx.x;
+    const unsigned xcd = bid & 7u, jx = bid >> 3, per = G >> 3, rem = G & 7u;
+    const unsigned slot = xcd * per + min(xcd, rem) + jx;
+    const int head = (int)(slot / (unsigned)wph), jw = (int)(slot % (unsigned)wph);
+    if (head >= a.H) return;
+    const int B = a.B, T = a.T;
+    const size_t M = (size_t)B * T;
+    const int nseg = (T + kFSeg - 1) / kFSeg, units = B * nseg;
+    const int ln = lane & 31, kh = lane >> 5;
+    bf16x8 wB[2 * kBs / 16];
+    {
+        const uint16_t* wr = w.Wt + ((size_t)head * kBs + 32 * wv + ln) * 2 * kBs;
+#pragma unroll
+        for (int s2 = 0; s2 < 2 * kBs / 16; ++s2) wB[s2] = *reinterpret_cast<const bf16x8*>(wr + 16 * s2 + 8 * kh);
+    }
+    const int atok = 32 * ((ln >> 2) & 1) + 4 * (ln >> 3) + (ln & 3);
+    // rows 8 wv .. 8 wv + 7 of unit un into stage st (rows past the unit repeat its last row)
+    auto copy_rows = [&](int un, int st) {
+        const int b = un / nseg, t0 = (un % nseg) * kFSeg, nt = min(kFSeg, T - t0);
+        const __amdgpu_buffer_rsrc_t rs = rsrc_at(w.dRI + ((size_t)head * M + (size_t)b * T + t0) * 2 * kBs);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int r = 8 * wv + q;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds + st * kDgStage + r * kDgRow, 16,
+                                                     min(r, nt - 1) * 4 * kBs + 16 * lane, 0, 0, 0);
+        }
+    };
+    uint4 sv[4];                 // the last unit's staged output, stored one unit late
+    size_t pm0 = 0;
+    int pnt = 0;
+    bool pending = false;
+    auto store_prev = [&]() {
+        const __amdgpu_buffer_rsrc_t ro = rsrc_len(w.dUg + ((size_t)head * M + pm0) * kBs, (uint32_t)pnt * kBs * 2);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int id = q * kFThreads + tid, row = id >> 5, ch = id & 31;
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, sv[q]), ro, (row * kBs + 8 * ch) * 2, 0, 0);
+        }
+    };
+    if (jw < units) copy_rows(jw, 0);
+    int st = 0;
+    for (int un = jw; un < units; un += wph, st ^= 1) {
+        const int b = un / nseg, t0 = (un % nseg) * kFSeg;
+        f_wait_vmem();     // this wave's rows of this unit (and the stores issued a unit ago)
+        f_lds_barrier();   // every wave's rows; every wave's reads of the other stage are done
+        if (un + wph < units) copy_rows(un + wph, st ^ 1);
+        if (pending) store_prev();
+        const unsigned char* const sa = lds + st * kDgStage;
+        f32x16 acc0, acc1;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) { acc0[e] = 0.0f; acc1[e] = 0.0f; }
+        const int ia0 = f_opaque(atok * kDgRow + 16 * kh), ia1 = f_opaque((atok + 16) * kDgRow + 16 * kh);
+#pragma unroll
+        for (int s2 = 0; s2 < 2 * kBs / 16; ++s2) {
+            const bf16x8 A0 = *reinterpret_cast<const bf16x8*>(sa + ia0 + 32 * s2);
+            const bf16x8 A1 = *reinterpret_cast<const bf16x8*>(sa + ia1 + 32 * s2);
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0, wB[s2], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, wB[s2], acc1, 0, 0, 0);
+        }
+        f_lds_barrier();   // every wave's reads of this stage are done: it takes the output now
+        unsigned char* const so = lds + st * kDgStage;
+        {
+            // token 32 kh + 16 mt + j, channel 32 wv + ln; + 0.0f as the GEMM's epilogue adds a
+            // zero bias (a -0 sum leaves as +0)
+            const int ob = f_opaque(dg_orow(32 * kh) + 2 * (32 * wv + ln));
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                *reinterpret_cast<uint16_t*>(so + ob + j * 2 * kBs) = f2bf(acc0[j] + 0.0f);
+                *reinterpret_cast<uint16_t*>(so + ob + (16 + j) * 2 * kBs) = f2bf(acc1[j] + 0.0f);
+            }
+        }
+        f_lds_barrier();   // the output tile is complete
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int id = q * kFThreads + tid, row = id >> 5, ch = id & 31;
+            sv[q] = *reinterpret_cast<const uint4*>(so + dg_orow(row) + 16 * ch);
+        }
+        pm0 = (size_t)b * T + t0;
+        pnt = min(kFSeg, T - t0);
+        pending = true;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (pending) store_prev();
+    f_wait_vmem();
+}
+
 // ---- gate weight gradients from the head-major dRI and U: [dW_a; dW_x]_h = [dR | dI]_h^T U_h ----
 // K runs over tokens, which are the rows (not the contiguous dimension) of both operands, so the
 // MFMA fragments (eight consecutive K per lane) are gathered from LDS with 2-byte reads.  One
@@ -952,16 +1055,10 @@ hipError_t launch_prefill_backward(const BwdArgs& a, hipStream_t s) {
     }
     hipLaunchKernelGGL(bwd_grad_kernel, dim3((unsigned)(nlane / (kBs / 2))), dim3(kBs / 2), 0, s, a, w);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    {   // gradient of u through the gates, all heads in one launch
-        ProjGemmArgs g;
-        memset(&g, 0, sizeof g);
-        g.A = w.dRI;
-        g.W[0] = w.Wt;
-        g.C[0] = w.dUg;
-        g.Nw[0] = kBs; g.nseg = 1; g.M = (int)M; g.K = 2 * kBs;
-        g.batch = a.H;
-        g.bsA = (long long)M * 2 * kBs; g.bsW = (long long)kBs * 2 * kBs; g.bsC = (long long)M * kBs;
-        if ((e = launch_proj_gemm(g, s)) != hipSuccess) return e;
+    {   // gradient of u through the gates: one persistent launch, the weights held in registers
+        const int wph = std::max(1, device_cu_count() / a.H);
+        hipLaunchKernelGGL(bwd_dgate_kernel, dim3((unsigned)(wph * a.H)), dim3(kFThreads), 0, s, a, w, wph);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     // gate weight gradients (K = B * T), all heads in one launch, then the ranges' sum
     hipLaunchKernelGGL(bwd_wgrad_kernel, dim3((unsigned)(w.wsplits * a.H * 2)), dim3(256), 0, s, a, w);
