@@ -101,16 +101,17 @@ __device__ __forceinline__ float sigm(float z) {
     return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * kLog2e));
 }
 
-// gelu_tanh(y) and its derivative from one tanh; tanh(z) = 1 - 2 / (1 + e^(2z)) with the
-// hardware exp2 and reciprocal (saturates to +-1 for large |z|; about 1e-7 absolute error)
+// gelu_tanh(y) and its derivative from one exponential: with z = k (y + c y^3),
+// 0.5 (1 + tanh z) = s = 1 / (1 + e^(-2z)), so gelu = y s and
+// gelu' = s + y s (1 - s) 2k (1 + 3c y^2); hardware exp2 and reciprocal (about 1 ulp each;
+// s saturates to 0 or 1 for large |z|)
 __device__ __forceinline__ float2 gelu_and_grad(float y) {
-    const float k = 0.7978845608028654f;
-    const float z = k * __builtin_fmaf(0.044715f * y, y * y, y);
-    const float th = __builtin_fmaf(-2.0f, __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(2.0f * kLog2e * z)), 1.0f);
-    const float hp = 0.5f * (1.0f + th);
-    return make_float2(y * hp,
-                       __builtin_fmaf(0.5f * y * __builtin_fmaf(-th, th, 1.0f) * k,
-                                      __builtin_fmaf(3.0f * 0.044715f, y * y, 1.0f), hp));
+    constexpr float k = 0.7978845608028654f, c = 0.044715f;
+    const float y2 = y * y;
+    const float e = __builtin_amdgcn_exp2f(y * __builtin_fmaf(y2, -2.0f * k * c * kLog2e, -2.0f * k * kLog2e));
+    const float sv = __builtin_amdgcn_rcpf(1.0f + e);
+    const float gx = y * sv;
+    return make_float2(gx, __builtin_fmaf(gx * (1.0f - sv), __builtin_fmaf(y2, 6.0f * k * c, 2.0f * k), sv));
 }
 
 // 1 - e^x for x <= 0, keeping full relative accuracy as x -> 0: a degree-7 Taylor polynomial
@@ -605,6 +606,8 @@ __global__ void __launch_bounds__(128, 2) bwd_grad_kernel(BwdArgs a, BwdBufs w) 
     }
     const float lsg = log_sigmoid(a.lambda[d]);
     const float sg = expf(lsg);
+    // per channel: log a = c2 r; log2 a = c2l r; d/dLambda log a = c1 r
+    const float c2 = 8.0f * lsg, c2l = c2 * kLog2e, c2x2 = 2.0f * c2, c1 = 8.0f * (1.0f - sg);
     float hv = w.carry[idx];
     float cc = w.cin[idx];
     __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's copies have landed
@@ -617,10 +620,21 @@ __global__ void __launch_bounds__(128, 2) bwd_grad_kernel(BwdArgs a, BwdBufs w) 
     for (int tt = 0; tt < kChunk; ++tt) {
         hp[tt] = hv;
         const int e = tt * kHalf + t;
-        const Gate g = gate_of(bf2f(tR[e]), bf2f(tI[e]), lsg);
-        ca[tt] = g.a;
-        cm[tt] = g.m;
-        hv = __builtin_fmaf(g.a, hv, g.m * g.i * bf2f(tU[e]));
+        const float r = sigm(bf2f(tR[e])), i = sigm(bf2f(tI[e]));
+        const float av = __builtin_amdgcn_exp2f(r * c2l);
+        // sqrt(1 - a^2): 1 - e^(2 log a) by its Taylor polynomial while a^2 > e^-0.5 (full
+        // relative accuracy as a -> 1), else 1 - a^2 directly (no cancellation there)
+        const float x = r * c2x2;
+        float p = __builtin_fmaf(x, 1.0f / 5040.0f, 1.0f / 720.0f);
+        p = __builtin_fmaf(x, p, 1.0f / 120.0f);
+        p = __builtin_fmaf(x, p, 1.0f / 24.0f);
+        p = __builtin_fmaf(x, p, 1.0f / 6.0f);
+        p = __builtin_fmaf(x, p, 0.5f);
+        p = __builtin_fmaf(x, p, 1.0f);
+        const float m = __builtin_amdgcn_sqrtf(x > -0.5f ? -x * p : __builtin_fmaf(-av, av, 1.0f));
+        ca[tt] = av;
+        cm[tt] = m;
+        hv = __builtin_fmaf(av, hv, m * i * bf2f(tU[e]));
     }
     const auto rDuv = rsrc_at(w.duv + hmo);
     float slam = 0.0f, sba = 0.0f, sbx = 0.0f;
@@ -628,27 +642,26 @@ __global__ void __launch_bounds__(128, 2) bwd_grad_kernel(BwdArgs a, BwdBufs w) 
     for (int tt = kChunk - 1; tt >= 0; --tt) {
         const int e = tt * kHalf + t;
         const float u = bf2f(tU[e]);
-        Gate g;
-        g.r = sigm(bf2f(tR[e]));
-        g.i = sigm(bf2f(tI[e]));
-        g.a = ca[tt];
-        g.m = cm[tt];
+        const float r = sigm(bf2f(tR[e])), i = sigm(bf2f(tI[e]));
+        const float av = ca[tt], m = cm[tt];
         const float ht = tt + 1 < kChunk ? hp[tt + 1] : hv;
         const float yv = bf2f(tY[e]), dov = bf2f(tD[e]);
         const float2 gg = gelu_and_grad(yv);
         const float dh = __builtin_fmaf(dov, gg.x, cc);
         tY[e] = f2bf(dov * ht * gg.y);
-        st_f32(rDuv, 4 * k, tt * 4 * kBs, dh * g.m * g.i);
-        const float dm = dh * g.i * u, di = dh * g.m * u;
-        const float da = dh * hp[tt] - dm * g.a * __builtin_amdgcn_rcpf(g.m);
-        slam += da * g.a * 8.0f * g.r * (1.0f - sg);
-        const float dr = da * g.a * 8.0f * lsg;
-        const float dRp = dr * g.r * (1.0f - g.r), dIp = di * g.i * (1.0f - g.i);
+        const float dv = dh * (m * i);
+        st_f32(rDuv, 4 * k, tt * 4 * kBs, dv);
+        // q = a dL/da with m = sqrt(1 - a^2): a (h_{t-1} dh - dh i u a / m), and since
+        // a h_{t-1} = h_t - m i u and a^2 / m = 1 / m - m, q = dh (h_t - i u / m)
+        const float q = dh * (ht - (i * u) * __builtin_amdgcn_rcpf(m));
+        const float qr = q * r;
+        slam = __builtin_fmaf(qr, c1, slam);
+        const float dRp = (qr * c2) * (1.0f - r), dIp = (dv * u) * (1.0f - i);
         sba += dRp;
         sbx += dIp;
         tR[e] = f2bf(dRp);
         tI[e] = f2bf(dIp);
-        cc = dh * g.a;
+        cc = dh * av;
     }
     w.plam[idx] = slam;
     w.pba[idx] = sba;
