@@ -615,7 +615,7 @@ __global__ void __launch_bounds__(128, 2) bwd_grad_kernel(BwdArgs a, BwdBufs w) 
     // the forward re-run keeps h_{t-1}, a and sqrt(1 - a^2) of each token for the walk (the
     // registers are free: LDS allows two waves per SIMD); the walk re-forms only r and i, and
     // h_t is the re-run's next h_{t-1}
-    float hp[kChunk], ca[kChunk], cm[kChunk];
+    float hp[kChunk], ca[kChunk], cm[kChunk], cr[kChunk], ci[kChunk];
 #pragma unroll
     for (int tt = 0; tt < kChunk; ++tt) {
         hp[tt] = hv;
@@ -634,6 +634,8 @@ __global__ void __launch_bounds__(128, 2) bwd_grad_kernel(BwdArgs a, BwdBufs w) 
         const float m = __builtin_amdgcn_sqrtf(x > -0.5f ? -x * p : __builtin_fmaf(-av, av, 1.0f));
         ca[tt] = av;
         cm[tt] = m;
+        cr[tt] = r;
+        ci[tt] = i;
         hv = __builtin_fmaf(av, hv, m * i * bf2f(tU[e]));
     }
     const auto rDuv = rsrc_at(w.duv + hmo);
@@ -642,7 +644,7 @@ __global__ void __launch_bounds__(128, 2) bwd_grad_kernel(BwdArgs a, BwdBufs w) 
     for (int tt = kChunk - 1; tt >= 0; --tt) {
         const int e = tt * kHalf + t;
         const float u = bf2f(tU[e]);
-        const float r = sigm(bf2f(tR[e])), i = sigm(bf2f(tI[e]));
+        const float r = cr[tt], i = ci[tt];
         const float av = ca[tt], m = cm[tt];
         const float ht = tt + 1 < kChunk ? hp[tt + 1] : hv;
         const float yv = bf2f(tY[e]), dov = bf2f(tD[e]);
