@@ -114,18 +114,17 @@ __device__ __forceinline__ float2 gelu_and_grad(float y) {
     return make_float2(gx, __builtin_fmaf(gx * (1.0f - sv), __builtin_fmaf(y2, 6.0f * k * c, 2.0f * k), sv));
 }
 
-// 1 - e^x for x <= 0, keeping full relative accuracy as x -> 0: a degree-7 Taylor polynomial
-// above -0.5 (truncation below 1e-7 relative), 1 - 2^(x log2 e) with the hardware exp2 below
-__device__ __forceinline__ float one_minus_exp(float x) {
+// sqrt(1 - a^2) from x = 2 log a <= 0 and a = e^(x/2): 1 - e^x by its degree-7 Taylor
+// polynomial above x = -0.5 (full relative accuracy as a -> 1; truncation below 1e-7
+// relative), 1 - a a below it (no cancellation there)
+__device__ __forceinline__ float sqrt_one_minus_a2(float x, float av) {
     float p = __builtin_fmaf(x, 1.0f / 5040.0f, 1.0f / 720.0f);
     p = __builtin_fmaf(x, p, 1.0f / 120.0f);
     p = __builtin_fmaf(x, p, 1.0f / 24.0f);
     p = __builtin_fmaf(x, p, 1.0f / 6.0f);
     p = __builtin_fmaf(x, p, 0.5f);
     p = __builtin_fmaf(x, p, 1.0f);
-    const float small = -x * p;
-    const float large = 1.0f - __builtin_amdgcn_exp2f(x * kLog2e);
-    return x > -0.5f ? small : large;
+    return __builtin_amdgcn_sqrtf(x > -0.5f ? -x * p : __builtin_fmaf(-av, av, 1.0f));
 }
 
 __device__ __forceinline__ size_t hm(int h, size_t m, int k, size_t M) {
@@ -153,7 +152,10 @@ __global__ void __launch_bounds__(256) bwd_wtrans_kernel(BwdArgs a, BwdBufs w) {
     w.Wt[idx] = W[((size_t)h * kBs + (jp % kBs)) * kBs + k];
 }
 
-// gate values of one element from the pre-activations; lsg = log sigma(Lambda) of the channel
+// gate values of one element from the pre-activations; lsg = log sigma(Lambda) of the channel.
+// (The front pass's form: sqrt(1 - a^2) as sqrt(1 - e^(2 log a)) throughout, its large-x side
+// with a second exponential; 1 - a a there, as in the gradient pass, costs the front pass
+// register spills.)
 struct Gate {
     float r, i, a, m;
 };
@@ -163,7 +165,16 @@ __device__ __forceinline__ Gate gate_of(float rp, float ip, float lsg) {
     g.i = sigm(ip);
     const float la = 8.0f * g.r * lsg;          // log a
     g.a = __builtin_amdgcn_exp2f(la * kLog2e);
-    g.m = __builtin_amdgcn_sqrtf(one_minus_exp(2.0f * la));   // sqrt(1 - a^2), accurate as a -> 1
+    const float x = 2.0f * la;
+    float p = __builtin_fmaf(x, 1.0f / 5040.0f, 1.0f / 720.0f);
+    p = __builtin_fmaf(x, p, 1.0f / 120.0f);
+    p = __builtin_fmaf(x, p, 1.0f / 24.0f);
+    p = __builtin_fmaf(x, p, 1.0f / 6.0f);
+    p = __builtin_fmaf(x, p, 0.5f);
+    p = __builtin_fmaf(x, p, 1.0f);
+    const float small = -x * p;
+    const float large = 1.0f - __builtin_amdgcn_exp2f(x * kLog2e);
+    g.m = __builtin_amdgcn_sqrtf(x > -0.5f ? small : large);
     return g;
 }
 __device__ __forceinline__ float log_sigmoid(float lam) { return -log1pf(expf(-lam)); }
@@ -622,16 +633,7 @@ __global__ void __launch_bounds__(128, 2) bwd_grad_kernel(BwdArgs a, BwdBufs w) 
         const int e = tt * kHalf + t;
         const float r = sigm(bf2f(tR[e])), i = sigm(bf2f(tI[e]));
         const float av = __builtin_amdgcn_exp2f(r * c2l);
-        // sqrt(1 - a^2): 1 - e^(2 log a) by its Taylor polynomial while a^2 > e^-0.5 (full
-        // relative accuracy as a -> 1), else 1 - a^2 directly (no cancellation there)
-        const float x = r * c2x2;
-        float p = __builtin_fmaf(x, 1.0f / 5040.0f, 1.0f / 720.0f);
-        p = __builtin_fmaf(x, p, 1.0f / 120.0f);
-        p = __builtin_fmaf(x, p, 1.0f / 24.0f);
-        p = __builtin_fmaf(x, p, 1.0f / 6.0f);
-        p = __builtin_fmaf(x, p, 0.5f);
-        p = __builtin_fmaf(x, p, 1.0f);
-        const float m = __builtin_amdgcn_sqrtf(x > -0.5f ? -x * p : __builtin_fmaf(-av, av, 1.0f));
+        const float m = sqrt_one_minus_a2(r * c2x2, av);
         ca[tt] = av;
         cm[tt] = m;
         cr[tt] = r;
