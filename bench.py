@@ -1010,7 +1010,8 @@ def census_summary(args):
 
 
 BACKWARD_CENSUS_TXT = os.path.join(ROOT, "profiles", "prefill_backward-2b-batched-census.txt")
-BACKWARD_CENSUS_KERNELS = ("bwd_grad_kernel", "bwd_front_kernel", "bwd_conv_kernel", "bwd_wgrad_kernel")
+BACKWARD_CENSUS_KERNELS = ("bwd_grad_kernel", "bwd_front_kernel", "bwd_conv_kernel", "bwd_wgrad_kernel",
+                           "bwd_dgate_kernel")
 
 
 def backward_census(args):
